@@ -1,0 +1,107 @@
+"""CPU oracle for the Mamba-3 SSM scan -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The HIP library never imports, links or
+calls it, and it shares no code with the HIP library.
+
+Contents
+  * ``scan``          -- ctypes front end of ``m3_oracle.c``: the sequential
+                         fp64 loop over t (the definition written out).
+  * ``m3_oracle_np``  -- two independent numpy formulations used to pin it:
+                         complex modes (``scan_complex``) and the dense
+                         semiseparable matrix (``scan_dense``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "m3_oracle.c")
+_LIB = os.path.join(_HERE, "libm3_oracle.so")
+_lib = None
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ("batch", "seqlen", "nheads", "ngroups", "headdim", "dstate", "rank")]
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the C oracle with gcc (-O2, IEEE fp64: no fast-math)."""
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                        "-fno-fast-math", "-Wall", "-o", tmp, src, "-lm"], check=True)
+        os.replace(tmp, out)
+    return out
+
+
+def load(path: str = _LIB):
+    global _lib
+    if path == _LIB and _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        build(force=False, out=path)
+    lib = ctypes.CDLL(path)
+    f = lib.m3o_scan
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.POINTER(_Dims)] + [ctypes.c_void_p] * 13 + [ctypes.c_int]
+    lib.m3o_max_threads.restype = ctypes.c_int
+    if path == _LIB:
+        _lib = lib
+    return lib
+
+
+def max_threads() -> int:
+    return int(load().m3o_max_threads())
+
+
+def _f64(a):
+    """Inputs are widened to fp64 (exact for fp32 and bf16 values)."""
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def scan(x, dt, A, lam, theta, B, C, D, state_in=None, nthreads: int = 0, lib_path: str = _LIB):
+    """Sequential fp64 scan.
+
+    Shapes: x (b,L,H,R,P), dt/lam (b,L,H), A/D (H,), theta (b,L,G,N/2),
+    B/C (b,L,G,R,N).  ``state_in`` is None or a tuple (h0 (b,H,N,P),
+    b_last (b,G,R,N), x_last (b,H,R,P)); b_last/x_last may be None.
+    Returns (y (b,L,H,R,P) float64, h_out (b,H,N,P) float64).
+    """
+    x, dt, A, lam, theta, B, C, D = map(_f64, (x, dt, A, lam, theta, B, C, D))
+    b, L, H, R, P = x.shape
+    G, N = B.shape[2], B.shape[4]
+    assert dt.shape == (b, L, H) and lam.shape == (b, L, H)
+    assert A.shape == (H,) and D.shape == (H,)
+    assert theta.shape == (b, L, G, N // 2)
+    assert B.shape == (b, L, G, R, N) and C.shape == (b, L, G, R, N)
+    h0 = bl = xl = None
+    if state_in is not None:
+        h0, bl, xl = state_in
+        if h0 is not None:
+            h0 = _f64(h0)
+            assert h0.shape == (b, H, N, P)
+        if bl is not None:
+            bl = _f64(bl)
+            assert bl.shape == (b, G, R, N)
+        if xl is not None:
+            xl = _f64(xl)
+            assert xl.shape == (b, H, R, P)
+    y = np.empty((b, L, H, R, P), dtype=np.float64)
+    h_out = np.empty((b, H, N, P), dtype=np.float64)
+    d = _Dims(b, L, H, G, P, N, R)
+    rc = load(lib_path).m3o_scan(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(lam),
+                                 _ptr(theta), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(bl),
+                                 _ptr(xl), _ptr(y), _ptr(h_out), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"m3o_scan failed with code {rc}")
+    return y, h_out

@@ -1,0 +1,185 @@
+/*
+ * m3_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, sequential fp64 CPU implementation of the Mamba-3 SSM scan.
+ * Only tests/, the smoke check and the benchmark's cpu_baseline leg may load
+ * it.  It shares no code, header or constant with the HIP library.
+ *
+ * What it computes (per batch b and head h, group g = h / (H/G), tokens t = 1..L):
+ *
+ *   U_t   = B_t X_t                       B_t in R^{N x R}, X_t in R^{R x P}
+ *           -- MIMO rank-R input: "Mamba-3 paper note" (docsaid.org),
+ *              section "Solution 3: MIMO" (R input/output branches, rank-R write).
+ *   alpha_t = exp(dt_t * A_h)
+ *   beta_t  = (1 - lambda_t) * dt_t * alpha_t
+ *   gamma_t = lambda_t * dt_t
+ *           -- same note, section "Solution 1: a more expressive discretisation",
+ *              exponential-trapezoidal recurrence and its alpha/beta/gamma.
+ *   M_t   = block-diagonal of 2x2 counter-clockwise rotations by theta_{t,k}
+ *           acting on the pair of state rows (2k, 2k+1)
+ *           -- same note, section "Solution 2: a complex state that rotates"
+ *              (complex SSM == real SSM of twice the size whose transition is the
+ *              decay times a block-diagonal of 2x2 rotations; the rotation matrix
+ *              of the parity example fixes the direction).
+ *   h_t   = alpha_t M_t h_{t-1} + beta_t M_t U_{t-1} + gamma_t U_t
+ *           (the complex transition multiplies the beta term as well: beta_t
+ *            carries exp(dt_t * A_t) with complex A_t, so the rotation rides along)
+ *   Y_t   = C_t^T h_t + D_h X_t           (R x P outputs)
+ *           -- output equation y = C h + D x: IBM "What is a Mamba model?",
+ *              section on the state and output equations.
+ *
+ * Start of a scan: h_0 and the previous input (B_0, X_0) come from the optional
+ * state_in; absent, both are zero.  state_out is (h_L, B_L, X_L).
+ *
+ * All inputs and outputs are fp64 arrays (fp32 and bf16 values are exact in
+ * fp64, so the kernels' inputs pass through unchanged).
+ *
+ * Layouts (contiguous, row-major, last index fastest):
+ *   x, y  (batch, L, H, R, P)      dt, lambda (batch, L, H)      A, D (H)
+ *   theta (batch, L, G, N/2)       B, C (batch, L, G, R, N)
+ *   h0, h_out (batch, H, N, P)     b_last (batch, G, R, N)       x_last (batch, H, R, P)
+ *
+ * Pins: every function here is checked by tests/test_oracle_pins.py against
+ * special cases, a brute-force matrix form, an independent complex-number
+ * formulation, an ODE convergence order and the worked parity example printed
+ * on the Mamba-3 note; no function is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+typedef struct {
+    int64_t batch, seqlen, nheads, ngroups, headdim, dstate, rank;
+} m3o_dims;
+
+#define IDX5(a, b, c, d, e, B_, C_, D_, E_) ((((((a) * (B_) + (b)) * (C_) + (c)) * (D_) + (d)) * (E_)) + (e))
+
+/* Scan one (batch b, head h) slice through all L tokens. */
+static void scan_slice(const m3o_dims* dm, int64_t b, int64_t h,
+                       const double* x, const double* dt, const double* A,
+                       const double* lam, const double* theta, const double* B,
+                       const double* C, const double* D,
+                       const double* h0, const double* b_last, const double* x_last,
+                       double* y, double* h_out, double* hs, double* U, double* Uprev) {
+    const int64_t L = dm->seqlen, H = dm->nheads, G = dm->ngroups;
+    const int64_t P = dm->headdim, N = dm->dstate, R = dm->rank, K = N / 2;
+    const int64_t g = h / (H / G);
+
+    /* h_0 */
+    for (int64_t i = 0; i < N * P; ++i) hs[i] = h0 ? h0[(b * H + h) * N * P + i] : 0.0;
+    /* U_0 = B_0 X_0 (the previous token's input term) */
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t p = 0; p < P; ++p) {
+            double u = 0.0;
+            if (b_last && x_last)
+                for (int64_t r = 0; r < R; ++r)
+                    u += b_last[((b * G + g) * R + r) * N + n] *
+                         x_last[((b * H + h) * R + r) * P + p];
+            Uprev[n * P + p] = u;
+        }
+
+    for (int64_t t = 0; t < L; ++t) {
+        const double dtv = dt[(b * L + t) * H + h];
+        const double lv = lam[(b * L + t) * H + h];
+        const double alpha = exp(dtv * A[h]);
+        const double beta = (1.0 - lv) * dtv * alpha;
+        const double gamma = lv * dtv;
+
+        /* U_t = B_t X_t : U[n][p] = sum_r B[n][r] X[r][p] */
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t p = 0; p < P; ++p) {
+                double u = 0.0;
+                for (int64_t r = 0; r < R; ++r)
+                    u += B[IDX5(b, t, g, r, n, L, G, R, N)] *
+                         x[IDX5(b, t, h, r, p, L, H, R, P)];
+                U[n * P + p] = u;
+            }
+
+        /* h_t = alpha M h + beta M U_{t-1} + gamma U_t, M rotating pairs (2k, 2k+1) */
+        for (int64_t k = 0; k < K; ++k) {
+            const double th = theta[((b * L + t) * G + g) * K + k];
+            const double c = cos(th), s = sin(th);
+            double* h0r = hs + (2 * k) * P;
+            double* h1r = hs + (2 * k + 1) * P;
+            const double* u0p = Uprev + (2 * k) * P;
+            const double* u1p = Uprev + (2 * k + 1) * P;
+            const double* u0 = U + (2 * k) * P;
+            const double* u1 = U + (2 * k + 1) * P;
+            for (int64_t p = 0; p < P; ++p) {
+                const double mh0 = c * h0r[p] - s * h1r[p];   /* M h     */
+                const double mh1 = s * h0r[p] + c * h1r[p];
+                const double mu0 = c * u0p[p] - s * u1p[p];   /* M U_{t-1} */
+                const double mu1 = s * u0p[p] + c * u1p[p];
+                h0r[p] = alpha * mh0 + beta * mu0 + gamma * u0[p];
+                h1r[p] = alpha * mh1 + beta * mu1 + gamma * u1[p];
+            }
+        }
+
+        /* Y_t = C_t^T h_t + D X_t */
+        for (int64_t r = 0; r < R; ++r)
+            for (int64_t p = 0; p < P; ++p) {
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n)
+                    acc += C[IDX5(b, t, g, r, n, L, G, R, N)] * hs[n * P + p];
+                const int64_t xi = IDX5(b, t, h, r, p, L, H, R, P);
+                y[xi] = acc + D[h] * x[xi];
+            }
+
+        memcpy(Uprev, U, sizeof(double) * N * P);
+    }
+    if (h_out) memcpy(h_out + (b * H + h) * N * P, hs, sizeof(double) * N * P);
+}
+
+/*
+ * Full scan.  Returns 0 on success, -1 on a shape error (N odd, H % G != 0,
+ * non-positive sizes, y NULL), -2 if scratch memory cannot be allocated.
+ * nthreads <= 0 uses the OpenMP default.  h_out may be NULL.
+ * (b_last, x_last) are used only when both are non-NULL.
+ */
+int m3o_scan(const m3o_dims* dm, const double* x, const double* dt, const double* A,
+             const double* lam, const double* theta, const double* B, const double* C,
+             const double* D, const double* h0, const double* b_last, const double* x_last,
+             double* y, double* h_out, int nthreads) {
+    if (!dm || !y || dm->batch < 0 || dm->seqlen < 0 || dm->nheads <= 0 || dm->ngroups <= 0 ||
+        dm->headdim <= 0 || dm->dstate <= 0 || dm->rank <= 0)
+        return -1;
+    if (dm->dstate % 2 != 0 || dm->nheads % dm->ngroups != 0) return -1;
+    const int64_t NP = dm->dstate * dm->headdim;
+    const int64_t nslices = dm->batch * dm->nheads;
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double* scratch = (double*)malloc(sizeof(double) * 3 * (size_t)NP);
+        if (!scratch) {
+#pragma omp atomic write
+            err = -2;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t s = 0; s < nslices; ++s) {
+            if (!scratch) continue;
+            const int64_t b = s / dm->nheads, h = s % dm->nheads;
+            scan_slice(dm, b, h, x, dt, A, lam, theta, B, C, D, h0, b_last, x_last, y, h_out,
+                       scratch, scratch + NP, scratch + 2 * NP);
+        }
+        free(scratch);
+    }
+    return err;
+}
+
+/* Number of OpenMP threads a parallel region would use (for reporting). */
+int m3o_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,66 @@
+"""The workloads the scan is measured and parity-tested on.
+
+Shapes are those of the models the Mamba-3 pages describe: the 113M pure
+Mamba-3 "nanomamba3" LM (d_model 768, 12 layers, MIMO rank 2, chunk 32:
+the nanomamba3 article's model table) and 1.5B-scale layers with state size
+128 (the Mamba-3 paper note, sections "Solution 3: MIMO" (R = 4) and
+"Speed" (Table 6, state 128)).  d_model / d_inner are not consumed by the
+scan (d_inner = H * P) and are kept only as labels.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+
+@dataclasses.dataclass(frozen=True)
+class ScanConfig:
+    name: str
+    batch: int
+    seqlen: int          # prefill length L
+    nheads: int          # H
+    headdim: int         # P
+    dstate: int          # N
+    rank: int            # R (1 = SISO)
+    chunk: int           # Q
+    ngroups: int = 1     # G (B, C, theta shared by H/G heads)
+    io_dtype: str = "bf16"          # dtype of x, B, C, y ("fp32" or "bf16")
+    theta_scale: float = 1.0
+    decode_steps: int = 0
+    seed: int = 1000
+    label: str = ""
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.seqlen
+
+
+CONFIGS = {
+    "c0": ScanConfig("c0", batch=1, seqlen=256, nheads=4, headdim=16, dstate=16, rank=1,
+                     chunk=32, io_dtype="fp32", seed=1000,
+                     label="single SISO layer, fp32, L=256, H=4, P=16, N=16, chunk 32"),
+    "c1": ScanConfig("c1", batch=4, seqlen=2048, nheads=24, headdim=64, dstate=128, rank=2,
+                     chunk=32, seed=1001,
+                     label="nanomamba3-shaped layer (d_model 768, d_inner 1536): 24 heads x P=64, "
+                           "N=128, MIMO R=2, chunk 32, batch 4, L=2048"),
+    "c2": ScanConfig("c2", batch=8, seqlen=8192, nheads=64, headdim=64, dstate=128, rank=1,
+                     chunk=64, seed=1002,
+                     label="1.5B-scale SISO layer (d_model 2048): 64 heads x P=64, N=128, R=1, "
+                           "chunk 64, batch 8, L=8192"),
+    "c3": ScanConfig("c3", batch=2, seqlen=16384, nheads=64, headdim=64, dstate=128, rank=4,
+                     chunk=64, theta_scale=4.0, seed=1003,
+                     label="1.5B-scale MIMO layer: 64 heads x P=64, N=128, R=4, chunk 64, batch 2, "
+                           "L=16384, theta x4"),
+    "c4": ScanConfig("c4", batch=256, seqlen=1024, nheads=64, headdim=64, dstate=128, rank=4,
+                     chunk=64, decode_steps=512, seed=1004,
+                     label="1.5B-scale MIMO R=4 layer, batch 256: 1024-token chunked prefill, "
+                           "then 512 single-token decode steps from its fp32 state"),
+}
+
+
+def scaled(cfg: ScanConfig, **kw) -> ScanConfig:
+    """A copy with some fields replaced (smaller parity-test variants)."""
+    return dataclasses.replace(cfg, **kw)
+
+
+THETA_RANGE = math.pi
