@@ -1,0 +1,144 @@
+/*
+ * m3scan.h -- C ABI of the Mamba-3 selective SSM scan for MI355X (gfx950).
+ *
+ * The operation (per batch b, head h with group g = h / (H/G), token t):
+ *
+ *   U_t     = B_t X_t                                  B_t: N x R, X_t: R x P
+ *   h_t     = alpha_t M_t h_{t-1} + beta_t M_t U_{t-1} + gamma_t U_t
+ *   Y_t     = C_t^T h_t + D_h X_t                       R x P outputs
+ *   alpha_t = exp(dt_t A_h),  beta_t = (1 - lambda_t) dt_t alpha_t,
+ *   gamma_t = lambda_t dt_t,  M_t = 2x2 rotations by theta_{t,k} on state rows (2k, 2k+1)
+ *
+ * Sources: the exponential-trapezoidal recurrence and its alpha/beta/gamma are
+ * the "Mamba-3 paper note" (docsaid.org), section "Solution 1: a more expressive
+ * discretisation"; the rotation (complex state == real state of twice the size
+ * with a block-diagonal of 2x2 rotations; absorbed into B and C it is a
+ * data-dependent RoPE) is section "Solution 2: a complex state that rotates";
+ * the rank-R MIMO update with R read-outs is section "Solution 3: MIMO"; the
+ * output equation y = C h + D x is IBM's "What is a Mamba model?" (state and
+ * output equations).  The chunked prefill is the hardware-aware parallel scan
+ * (same IBM page, selective scan section): chunks of `chunk` tokens computed in
+ * parallel, states passed between them.
+ *
+ * Conventions fixed by this library where the pages leave a choice open:
+ *   - rotation pairs are adjacent state rows (2k, 2k+1), counter-clockwise;
+ *     pair k is (real, imaginary) of complex mode k;
+ *   - the rotation multiplies the beta term as well (beta carries exp(dt A)
+ *     of the complex A);
+ *   - theta is the per-step angle already scaled by the caller;
+ *   - B, C and theta are shared by the H/G heads of a group;
+ *   - the previous input (B_0, X_0) at the start of a scan is zero unless a
+ *     state is passed in.
+ *
+ * Layouts: contiguous, row-major, last index fastest.
+ *   x, y   (batch, L, H, R, P)   io dtype       dt, lambda (batch, L, H) fp32
+ *   A, D   (H)                   fp32           theta      (batch, L, G, N/2) fp32
+ *   B, C   (batch, L, G, R, N)   io dtype       B[b,t,g,r,n] = (B_t)_{n,r}
+ *   state h (batch, H, N, P) fp32 (true frame)
+ *   carry  b_last (batch, G, R, N), x_last (batch, H, R, P) io dtype
+ *   Decode drops the L axis of every per-token tensor.
+ *
+ * Ownership and execution: every pointer is device memory owned by the caller.
+ * The library never allocates, frees or synchronises; all work is enqueued on
+ * `stream` (a hipStream_t; NULL = the null stream) and the call returns at once.
+ * There is no global mutable state: calls on different streams may run from
+ * different threads.  Outputs must not alias inputs unless stated.
+ *
+ * Errors: argument and shape errors are returned before anything is launched.
+ * Launch failures return M3_ERR_HIP.  Faults inside a kernel surface at the
+ * caller's next synchronisation.  No C++ exception crosses this interface.
+ * Value ranges (dt > 0, 0 <= lambda <= 1, A <= 0) are not checked: the
+ * arithmetic is carried out on whatever is passed.
+ */
+#ifndef M3SCAN_H
+#define M3SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    M3_OK = 0,
+    M3_ERR_INVALID_ARG = -1,   /* null pointer, non-positive size, N odd, H % G != 0 */
+    M3_ERR_UNSUPPORTED = -2,   /* a shape/dtype combination no kernel here handles   */
+    M3_ERR_WORKSPACE = -3,     /* workspace_bytes smaller than the size asked for     */
+    M3_ERR_HIP = -4            /* a HIP launch or runtime call failed                 */
+} m3_status;
+
+typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype;   /* dtype of x, B, C, y and the carry */
+
+typedef struct {
+    int64_t batch;     /* b                                   >= 1 */
+    int64_t seqlen;    /* L (prefill); ignored by decode      >= 0 */
+    int64_t nheads;    /* H                                   >= 1 */
+    int64_t ngroups;   /* G, divides H                        >= 1 */
+    int64_t headdim;   /* P                                   >= 1 */
+    int64_t dstate;    /* N, even                             >= 2 */
+    int64_t rank;      /* R (1 = SISO)                        >= 1 */
+    int64_t chunk;     /* Q, tokens per chunk; ignored by decode >= 1 */
+    int32_t io_dtype;  /* m3_dtype                                 */
+} m3_dims;
+
+typedef struct {
+    float* h;          /* (batch, H, N, P) fp32: the state after the last token        */
+    void* b_last;      /* (batch, G, R, N) io dtype: B of the last token (the carry)    */
+    void* x_last;      /* (batch, H, R, P) io dtype: X of the last token (the carry)    */
+} m3_state;
+
+/* Bytes of device workspace m3_prefill_chunked needs for these dims (may be 0).
+ * Errors: M3_ERR_INVALID_ARG for bad dims or a NULL `bytes`. */
+m3_status m3_prefill_workspace_size(const m3_dims* dims, size_t* bytes);
+
+/*
+ * Chunked prefill: the whole sequence of `seqlen` tokens for every (b, h).
+ * Computes y (batch, L, H, R, P) in the io dtype, rounded to nearest even from
+ * fp32, and optionally the final state.
+ *
+ * state_in:  NULL, or the state to continue from; its h must be non-NULL and
+ *            its carry (b_last, x_last) may be NULL (zero previous input).
+ *            May alias state_out (read before written).
+ * state_out: NULL, or where to write the final state; each of its fields may
+ *            be NULL to skip it.  The carry written is a copy of B and X of
+ *            the last token (the caller may equally keep those slices).
+ * workspace: device memory of at least m3_prefill_workspace_size bytes
+ *            (NULL allowed when that size is 0); contents on entry ignored.
+ * Partial last chunks (L not a multiple of `chunk`) and L = 0 are allowed.
+ */
+m3_status m3_prefill_chunked(const m3_dims* dims, const void* x, const float* dt,
+                             const float* A, const float* lambda, const float* theta,
+                             const void* B, const void* C, const float* D,
+                             const m3_state* state_in, m3_state* state_out, void* y,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step for every (b, h): reads the fp32 state h in place, applies
+ * one token and writes the new state back to h, and writes y_t (batch, H, R, P).
+ *
+ * b_last, x_last: B and X of the previous token (the trapezoid carry), in the
+ *            io dtype; both NULL means a zero previous input.  They are only
+ *            read, so the caller passes this call's B_t and x_t as the next
+ *            call's b_last and x_last -- no copy, and no race between heads of
+ *            a group that share b_last.
+ * Per-token inputs: x_t (b,H,R,P), dt_t, lambda_t (b,H), theta_t (b,G,N/2),
+ *            B_t, C_t (b,G,R,N).  dims->seqlen and dims->chunk are ignored.
+ */
+m3_status m3_decode_step(const m3_dims* dims, float* h, const void* b_last,
+                         const void* x_last, const void* x_t, const float* dt_t,
+                         const float* A, const float* lambda_t, const float* theta_t,
+                         const void* B_t, const void* C_t, const float* D, void* y_t,
+                         void* stream);
+
+/* Static text for a status code. */
+const char* m3_status_string(m3_status status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t m3_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* M3SCAN_H */

@@ -1,0 +1,172 @@
+// m3_api.cpp -- the C ABI declared in include/m3scan.h: argument checks,
+// kernel selection, workspace sizing and launches on the caller's stream.
+#include "m3scan.h"
+
+#include <hip/hip_runtime.h>
+
+#include "m3_internal.h"
+
+namespace {
+
+constexpr int32_t kVersion = 100;  // 0.1.0
+constexpr size_t kMaxLds = 160 * 1024;
+
+bool dims_ok(const m3_dims* d, bool prefill) {
+    if (!d) return false;
+    if (d->batch < 1 || d->nheads < 1 || d->ngroups < 1 || d->headdim < 1 || d->dstate < 2 ||
+        d->rank < 1)
+        return false;
+    if (prefill && (d->seqlen < 0 || d->chunk < 1)) return false;
+    if (d->dstate % 2 != 0 || d->nheads % d->ngroups != 0) return false;
+    if (d->io_dtype != M3_F32 && d->io_dtype != M3_BF16) return false;
+    // Index arithmetic inside the kernels is 32-bit for per-slice sizes.
+    if (d->headdim > 4096 || d->dstate > 4096 || d->rank > 64 || d->nheads > (1 << 20)) return false;
+    if (prefill && d->chunk > 4096) return false;
+    return true;
+}
+
+m3::PrefillArgs make_prefill_args(const m3_dims* d) {
+    m3::PrefillArgs a{};
+    a.batch = d->batch;
+    a.L = d->seqlen;
+    a.H = static_cast<int>(d->nheads);
+    a.G = static_cast<int>(d->ngroups);
+    a.N = static_cast<int>(d->dstate);
+    a.P = static_cast<int>(d->headdim);
+    a.R = static_cast<int>(d->rank);
+    a.Q = static_cast<int>(d->chunk);
+    a.bf16 = d->io_dtype == M3_BF16;
+    return a;
+}
+
+}  // namespace
+
+namespace m3 {
+
+PrefillPlan plan_prefill(const PrefillArgs& a) {
+    PrefillPlan p{PrefillPath::Unsupported, 1, 0, 0};
+    if (a.R > kMaxRankGeneric) return p;
+    const size_t lds = generic_lds_bytes(a);
+    if (lds <= kMaxLds) {
+        p.path = PrefillPath::Generic;
+        p.lds = lds;
+    }
+    return p;
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStream_t st) {
+    hipError_t e = hipSuccess;
+    if (plan.path == PrefillPath::Generic) {
+        if (a.batch * a.H > 0) e = launch_prefill_generic(a, st);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    if (a.bl_out || a.xl_out) e = launch_carry_out(a, st);
+    return e;
+}
+
+}  // namespace m3
+
+extern "C" {
+
+const char* m3_status_string(m3_status s) {
+    switch (s) {
+        case M3_OK: return "ok";
+        case M3_ERR_INVALID_ARG: return "invalid argument";
+        case M3_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case M3_ERR_WORKSPACE: return "workspace too small";
+        case M3_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int32_t m3_version(void) { return kVersion; }
+
+m3_status m3_prefill_workspace_size(const m3_dims* dims, size_t* bytes) {
+    if (!bytes || !dims_ok(dims, true)) return M3_ERR_INVALID_ARG;
+    const m3::PrefillArgs a = make_prefill_args(dims);
+    const m3::PrefillPlan plan = m3::plan_prefill(a);
+    if (plan.path == m3::PrefillPath::Unsupported) return M3_ERR_UNSUPPORTED;
+    *bytes = plan.workspace;
+    return M3_OK;
+}
+
+m3_status m3_prefill_chunked(const m3_dims* dims, const void* x, const float* dt,
+                             const float* A, const float* lambda, const float* theta,
+                             const void* B, const void* C, const float* D,
+                             const m3_state* state_in, m3_state* state_out, void* y,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (!dims_ok(dims, true)) return M3_ERR_INVALID_ARG;
+    if (!A || !D) return M3_ERR_INVALID_ARG;
+    if (dims->seqlen > 0 && (!x || !dt || !lambda || !theta || !B || !C || !y))
+        return M3_ERR_INVALID_ARG;
+    if (state_in) {
+        if (!state_in->h) return M3_ERR_INVALID_ARG;
+        if ((state_in->b_last == nullptr) != (state_in->x_last == nullptr)) return M3_ERR_INVALID_ARG;
+    }
+    m3::PrefillArgs a = make_prefill_args(dims);
+    a.x = x;
+    a.dt = dt;
+    a.A = A;
+    a.lam = lambda;
+    a.theta = theta;
+    a.B = B;
+    a.C = C;
+    a.D = D;
+    a.y = y;
+    if (state_in) {
+        a.h_in = state_in->h;
+        a.bl_in = state_in->b_last;
+        a.xl_in = state_in->x_last;
+    }
+    if (state_out) {
+        a.h_out = state_out->h;
+        a.bl_out = state_out->b_last;
+        a.xl_out = state_out->x_last;
+    }
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+    const m3::PrefillPlan plan = m3::plan_prefill(a);
+    if (plan.path == m3::PrefillPath::Unsupported) return M3_ERR_UNSUPPORTED;
+    if (plan.workspace > 0 && (!workspace || workspace_bytes < plan.workspace)) return M3_ERR_WORKSPACE;
+    const hipError_t e = m3::launch_prefill(a, plan, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
+m3_status m3_decode_step(const m3_dims* dims, float* h, const void* b_last, const void* x_last,
+                         const void* x_t, const float* dt_t, const float* A,
+                         const float* lambda_t, const float* theta_t, const void* B_t,
+                         const void* C_t, const float* D, void* y_t, void* stream) {
+    if (!dims_ok(dims, false)) return M3_ERR_INVALID_ARG;
+    if (!h || !x_t || !dt_t || !A || !lambda_t || !theta_t || !B_t || !C_t || !D || !y_t)
+        return M3_ERR_INVALID_ARG;
+    if ((b_last == nullptr) != (x_last == nullptr)) return M3_ERR_INVALID_ARG;
+    m3::DecodeArgs a{};
+    a.h = h;
+    a.b_last = b_last;
+    a.x_last = x_last;
+    a.x_t = x_t;
+    a.dt_t = dt_t;
+    a.A = A;
+    a.lam_t = lambda_t;
+    a.theta_t = theta_t;
+    a.B_t = B_t;
+    a.C_t = C_t;
+    a.D = D;
+    a.y_t = y_t;
+    a.batch = static_cast<int>(dims->batch);
+    a.H = static_cast<int>(dims->nheads);
+    a.G = static_cast<int>(dims->ngroups);
+    a.N = static_cast<int>(dims->dstate);
+    a.P = static_cast<int>(dims->headdim);
+    a.R = static_cast<int>(dims->rank);
+    a.has_carry = b_last != nullptr;
+    a.bf16 = dims->io_dtype == M3_BF16;
+    if (dims->batch * dims->nheads > 0x7fffffffLL) return M3_ERR_UNSUPPORTED;
+    if (!m3::decode_supported(a)) return M3_ERR_UNSUPPORTED;
+    const hipError_t e = m3::launch_decode(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
+}  // extern "C"

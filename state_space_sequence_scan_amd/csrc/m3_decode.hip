@@ -1,0 +1,254 @@
+// m3_decode.hip -- one decode step of the Mamba-3 scan (gfx950).
+//
+// Per (b, h), with the trapezoid carry U_prev = B_prev X_prev:
+//   h <- alpha M (h + (1 - lambda) dt U_prev) + lambda dt U,   U = B_t X_t
+//   y  = C_t^T h + D X_t
+// (alpha M h + beta M U_prev + gamma U with beta = (1 - lambda) dt alpha, the
+// exponential-trapezoidal step of the Mamba-3 paper note, "Solution 1", with the
+// rotation of "Solution 2" and the rank-R input/read-out of "Solution 3").
+//
+// The step reads and writes the whole fp32 state and does little arithmetic per
+// byte: it is bound by HBM bandwidth.  The fast kernel streams each (b, h) state
+// slice once with 16-byte non-temporal loads and stores, keeps every rotation
+// pair (2k, 2k+1) inside one thread, and reduces the R x P read-out across the
+// threads that share a column block with cross-lane shuffles and one LDS pass.
+#include "m3_common.h"
+#include "m3_internal.h"
+
+namespace m3 {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Fast path.  One workgroup of NT threads per (b, h).  Thread tid owns the
+// 4-column block c = tid % PC (PC = P/4) and the rotation pairs
+// k = kk + TPG * j (kk = tid / PC, j < PPT), i.e. 2 * PPT state rows x 4 columns.
+template <typename T, int N, int P, int R, int NT>
+__global__ __launch_bounds__(NT) void decode_fast(
+    float* __restrict__ h, const T* __restrict__ b_last, const T* __restrict__ x_last,
+    const T* __restrict__ x_t, const float* __restrict__ dt_t, const float* __restrict__ A,
+    const float* __restrict__ lam_t, const float* __restrict__ theta_t,
+    const T* __restrict__ B_t, const T* __restrict__ C_t, const float* __restrict__ D,
+    T* __restrict__ y_t, int H, int G, int has_carry) {
+    constexpr int KP = N / 2;
+    constexpr int PC = P / 4;
+    constexpr int TPG = NT / PC;
+    constexpr int PPT = KP / TPG;
+    constexpr int NW = (NT + 63) / 64;
+    static_assert(P % 4 == 0 && NT % PC == 0 && KP % TPG == 0 && PPT >= 1, "decode tiling");
+
+    const int bh = blockIdx.x;
+    const int b = bh / H, hh = bh - b * H;
+    const int g = hh / (H / G);
+    const int tid = threadIdx.x;
+    const int c = tid % PC;
+    const int kk = tid / PC;
+
+    float* hp = h + static_cast<size_t>(bh) * N * P;
+
+    // Issue the state loads first: they are the only HBM-sized traffic.
+    f32x4 s0[PPT], s1[PPT];
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+        const int k = kk + TPG * j;
+        s0[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(hp + (2 * k) * P) + c);
+        s1[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(hp + (2 * k + 1) * P) + c);
+    }
+
+    __shared__ float sB[R][N], sC[R][N], sBp[R][N];
+    __shared__ __align__(16) float sX[R][P];
+    __shared__ __align__(16) float sXp[R][P];
+    __shared__ float sCs[KP], sSn[KP];
+
+    const size_t gofs = (static_cast<size_t>(b) * G + g) * R * N;
+    const size_t hofs = static_cast<size_t>(bh) * R * P;
+    for (int i = tid; i < R * N; i += NT) {
+        (&sB[0][0])[i] = io<T>::load(B_t + gofs + i);
+        (&sC[0][0])[i] = io<T>::load(C_t + gofs + i);
+        (&sBp[0][0])[i] = has_carry ? io<T>::load(b_last + gofs + i) : 0.f;
+    }
+    for (int i = tid; i < R * P; i += NT) {
+        (&sX[0][0])[i] = io<T>::load(x_t + hofs + i);
+        (&sXp[0][0])[i] = has_carry ? io<T>::load(x_last + hofs + i) : 0.f;
+    }
+    for (int k = tid; k < KP; k += NT) {
+        float sn, cs;
+        sincos_acc(theta_t[(static_cast<size_t>(b) * G + g) * KP + k], &sn, &cs);
+        sCs[k] = cs;
+        sSn[k] = sn;
+    }
+    const float dtv = dt_t[bh];
+    const float lv = lam_t[bh];
+    const float alpha = __expf(dtv * A[hh]);
+    const float c1 = (1.f - lv) * dtv;   // (1 - lambda) dt : weight of the carry before the decay
+    const float c2 = lv * dtv;           // gamma
+    __syncthreads();
+
+    f32x4 xv[R], xpv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        xv[r] = reinterpret_cast<const f32x4*>(sX[r])[c];
+        xpv[r] = reinterpret_cast<const f32x4*>(sXp[r])[c];
+    }
+    f32x4 yacc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) yacc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+        const int k = kk + TPG * j;
+        const float cs = sCs[k], sn = sSn[k];
+        f32x4 up0 = {0.f, 0.f, 0.f, 0.f}, up1 = up0, u0 = up0, u1 = up0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            up0 += sBp[r][2 * k] * xpv[r];
+            up1 += sBp[r][2 * k + 1] * xpv[r];
+            u0 += sB[r][2 * k] * xv[r];
+            u1 += sB[r][2 * k + 1] * xv[r];
+        }
+        const f32x4 v0 = s0[j] + c1 * up0;
+        const f32x4 v1 = s1[j] + c1 * up1;
+        const f32x4 n0 = alpha * (cs * v0 - sn * v1) + c2 * u0;
+        const f32x4 n1 = alpha * (sn * v0 + cs * v1) + c2 * u1;
+        __builtin_nontemporal_store(n0, reinterpret_cast<f32x4*>(hp + (2 * k) * P) + c);
+        __builtin_nontemporal_store(n1, reinterpret_cast<f32x4*>(hp + (2 * k + 1) * P) + c);
+#pragma unroll
+        for (int r = 0; r < R; ++r) yacc[r] += sC[r][2 * k] * n0 + sC[r][2 * k + 1] * n1;
+    }
+
+    // Sum the read-out over the threads that share column block c: first the
+    // lanes of one wave (stride PC), then the waves through LDS.
+#pragma unroll
+    for (int off = PC; off < 64 && off < NT; off <<= 1) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) yacc[r][q] += __shfl_xor(yacc[r][q], off);
+    }
+    __shared__ __align__(16) float sY[NW][R][P];
+    const int lane = tid & 63, wave = tid >> 6;
+    if (lane < PC) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) reinterpret_cast<f32x4*>(sY[wave][r])[c] = yacc[r];
+    }
+    __syncthreads();
+    const float dv = D[hh];
+    for (int i = tid; i < R * P; i += NT) {
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) acc += (&sY[w][0][0])[i];
+        io<T>::store(y_t + hofs + i, acc + dv * (&sX[0][0])[i]);
+    }
+}
+
+// Any shape: one workgroup per (b, h); each thread owns whole state columns p and
+// walks the N/2 rotation pairs of that column.  R <= kMaxRankGeneric.
+template <typename T>
+__global__ __launch_bounds__(64) void decode_generic(
+    float* __restrict__ h, const T* __restrict__ b_last, const T* __restrict__ x_last,
+    const T* __restrict__ x_t, const float* __restrict__ dt_t, const float* __restrict__ A,
+    const float* __restrict__ lam_t, const float* __restrict__ theta_t,
+    const T* __restrict__ B_t, const T* __restrict__ C_t, const float* __restrict__ D,
+    T* __restrict__ y_t, int H, int G, int N, int P, int R, int has_carry) {
+    extern __shared__ float smem[];
+    const int KP = N / 2;
+    float* sB = smem;               // R*N
+    float* sC = sB + R * N;         // R*N
+    float* sBp = sC + R * N;        // R*N
+    float* sX = sBp + R * N;        // R*P
+    float* sXp = sX + R * P;        // R*P
+    float* sCs = sXp + R * P;       // KP
+    float* sSn = sCs + KP;          // KP
+
+    const int bh = blockIdx.x;
+    const int b = bh / H, hh = bh - b * H;
+    const int g = hh / (H / G);
+    const int tid = threadIdx.x;
+    const size_t gofs = (static_cast<size_t>(b) * G + g) * R * N;
+    const size_t hofs = static_cast<size_t>(bh) * R * P;
+    for (int i = tid; i < R * N; i += blockDim.x) {
+        sB[i] = io<T>::load(B_t + gofs + i);
+        sC[i] = io<T>::load(C_t + gofs + i);
+        sBp[i] = has_carry ? io<T>::load(b_last + gofs + i) : 0.f;
+    }
+    for (int i = tid; i < R * P; i += blockDim.x) {
+        sX[i] = io<T>::load(x_t + hofs + i);
+        sXp[i] = has_carry ? io<T>::load(x_last + hofs + i) : 0.f;
+    }
+    for (int k = tid; k < KP; k += blockDim.x) {
+        float sn, cs;
+        sincos_acc(theta_t[(static_cast<size_t>(b) * G + g) * KP + k], &sn, &cs);
+        sCs[k] = cs;
+        sSn[k] = sn;
+    }
+    __syncthreads();
+    const float dtv = dt_t[bh], lv = lam_t[bh];
+    const float alpha = __expf(dtv * A[hh]);
+    const float c1 = (1.f - lv) * dtv, c2 = lv * dtv;
+    float* hp = h + static_cast<size_t>(bh) * N * P;
+    for (int p = tid; p < P; p += blockDim.x) {
+        float yacc[kMaxRankGeneric];
+        for (int r = 0; r < R; ++r) yacc[r] = 0.f;
+        for (int k = 0; k < KP; ++k) {
+            float up0 = 0.f, up1 = 0.f, u0 = 0.f, u1 = 0.f;
+            for (int r = 0; r < R; ++r) {
+                up0 += sBp[r * N + 2 * k] * sXp[r * P + p];
+                up1 += sBp[r * N + 2 * k + 1] * sXp[r * P + p];
+                u0 += sB[r * N + 2 * k] * sX[r * P + p];
+                u1 += sB[r * N + 2 * k + 1] * sX[r * P + p];
+            }
+            const float v0 = hp[(2 * k) * P + p] + c1 * up0;
+            const float v1 = hp[(2 * k + 1) * P + p] + c1 * up1;
+            const float n0 = alpha * (sCs[k] * v0 - sSn[k] * v1) + c2 * u0;
+            const float n1 = alpha * (sSn[k] * v0 + sCs[k] * v1) + c2 * u1;
+            hp[(2 * k) * P + p] = n0;
+            hp[(2 * k + 1) * P + p] = n1;
+            for (int r = 0; r < R; ++r) yacc[r] += sC[r * N + 2 * k] * n0 + sC[r * N + 2 * k + 1] * n1;
+        }
+        for (int r = 0; r < R; ++r)
+            io<T>::store(y_t + hofs + r * P + p, yacc[r] + D[hh] * sX[r * P + p]);
+    }
+}
+
+template <typename T, int N, int P, int R, int NT>
+static hipError_t launch_fast(const DecodeArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL((decode_fast<T, N, P, R, NT>), dim3(static_cast<unsigned>(a.batch * a.H)),
+                       dim3(NT), 0, st, a.h, static_cast<const T*>(a.b_last),
+                       static_cast<const T*>(a.x_last), static_cast<const T*>(a.x_t), a.dt_t, a.A,
+                       a.lam_t, a.theta_t, static_cast<const T*>(a.B_t),
+                       static_cast<const T*>(a.C_t), a.D, static_cast<T*>(a.y_t), a.H, a.G,
+                       a.has_carry);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
+    if (a.N == 128 && a.P == 64) {
+        switch (a.R) {
+            case 1: return launch_fast<T, 128, 64, 1, 256>(a, st);
+            case 2: return launch_fast<T, 128, 64, 2, 256>(a, st);
+            case 4: return launch_fast<T, 128, 64, 4, 256>(a, st);
+            default: break;
+        }
+    }
+    if (a.N == 16 && a.P == 16 && a.R == 1) return launch_fast<T, 16, 16, 1, 32>(a, st);
+    const size_t shm = sizeof(float) * (3 * a.R * a.N + 2 * a.R * a.P + a.N);
+    hipLaunchKernelGGL(decode_generic<T>, dim3(static_cast<unsigned>(a.batch * a.H)), dim3(64),
+                       shm, st, a.h, static_cast<const T*>(a.b_last),
+                       static_cast<const T*>(a.x_last), static_cast<const T*>(a.x_t), a.dt_t, a.A,
+                       a.lam_t, a.theta_t, static_cast<const T*>(a.B_t),
+                       static_cast<const T*>(a.C_t), a.D, static_cast<T*>(a.y_t), a.H, a.G,
+                       a.N, a.P, a.R, a.has_carry);
+    return hipGetLastError();
+}
+
+bool decode_supported(const DecodeArgs& a) {
+    if (a.R > kMaxRankGeneric) return false;
+    const size_t shm = sizeof(float) * (3 * a.R * a.N + 2 * a.R * a.P + a.N);
+    return shm <= 64 * 1024;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+    return a.bf16 ? launch_decode_t<bf16_t>(a, st) : launch_decode_t<float>(a, st);
+}
+
+}  // namespace m3

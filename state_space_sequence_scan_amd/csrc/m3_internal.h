@@ -1,0 +1,74 @@
+// m3_internal.h -- launch descriptors shared by the C-ABI host code and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace m3 {
+
+constexpr int kMaxRankGeneric = 8;
+
+struct DecodeArgs {
+    float* h;
+    const void* b_last;
+    const void* x_last;
+    const void* x_t;
+    const float* dt_t;
+    const float* A;
+    const float* lam_t;
+    const float* theta_t;
+    const void* B_t;
+    const void* C_t;
+    const float* D;
+    void* y_t;
+    int batch, H, G, N, P, R;
+    int has_carry;
+    bool bf16;
+};
+
+bool decode_supported(const DecodeArgs& a);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+
+struct PrefillArgs {
+    const void* x;
+    const float* dt;
+    const float* A;
+    const float* lam;
+    const float* theta;
+    const void* B;
+    const void* C;
+    const float* D;
+    const float* h_in;       // may be null (zero state)
+    const void* bl_in;       // carry in, may be null (with xl_in)
+    const void* xl_in;
+    void* y;
+    float* h_out;            // may be null
+    void* bl_out;            // may be null
+    void* xl_out;            // may be null
+    void* workspace;
+    size_t workspace_bytes;
+    int64_t batch, L;
+    int H, G, N, P, R, Q;
+    bool bf16;
+};
+
+// Which kernel family runs a prefill, and the workspace it needs.
+enum class PrefillPath { Generic, Mfma, Unsupported };
+struct PrefillPlan {
+    PrefillPath path;
+    int nseg;                // segments per sequence (1 = one sweep per (b, h))
+    size_t workspace;        // bytes
+    size_t lds;              // dynamic LDS bytes of the main kernel
+};
+PrefillPlan plan_prefill(const PrefillArgs& a);
+hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStream_t st);
+
+// Generic family (any shape whose chunk fits in LDS), in m3_prefill_generic.hip.
+size_t generic_lds_bytes(const PrefillArgs& a);
+hipError_t launch_prefill_generic(const PrefillArgs& a, hipStream_t st);
+
+// Carry-out copy (B and X of the last token), in m3_prefill_generic.hip.
+hipError_t launch_carry_out(const PrefillArgs& a, hipStream_t st);
+
+}  // namespace m3

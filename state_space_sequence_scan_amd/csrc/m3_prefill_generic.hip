@@ -1,0 +1,259 @@
+// m3_prefill_generic.hip -- chunked prefill of the Mamba-3 scan in fp32 vector
+// arithmetic, for any shape whose chunk fits in LDS (gfx950).
+//
+// The chunked form (per (b, h), chunk of Q tokens, all sums chunk-local):
+//   cum_i = sum_{j<=i} dt_j A                     (decay exponent)
+//   phi_i = sum_{j<=i} theta_j                    (angle per pair k)
+//   Bt_i  = R(-phi_i) B_i,   Ct_i = R(-phi_i) C_i (data-dependent RoPE: the
+//           cumulative rotation absorbed into B and C, Mamba-3 paper note,
+//           "Solution 2: a complex state that rotates")
+//   w_j   = lambda_j dt_j + (1 - lambda_{j+1}) dt_{j+1}   (gamma_j plus the beta
+//           weight the next step gives the same input: the implicit width-2
+//           convolution of the exponential-trapezoidal rule, "Solution 1";
+//           w = gamma at the last token of the sequence)
+//   Y_i   = D X_i + e^{cum_i} Ct_i^T S  +  sum_{j<=i} m_ij (Ct_i^T Bt_j) X_j
+//           m_ij = e^{cum_i - cum_j} w_j (j < i),   gamma_i (j = i)
+//   S    <- R(phi_end) [ e^{cum_end} S + sum_j e^{cum_end - cum_j} w_j Bt_j X_j ]
+// S is the state entering the chunk in the true frame, with the beta term of
+// the chunk's first token already folded in (h + (1 - lambda) dt U_prev); after
+// the last chunk it is exactly h_L.  The chunks are walked in order by one
+// workgroup per (b, h) (the state passing of the chunked scan, IBM "What is a
+// Mamba model?", hardware-aware parallel scan).
+#include "m3_common.h"
+#include "m3_internal.h"
+
+namespace m3 {
+
+template <typename T>
+__global__ __launch_bounds__(256) void prefill_generic(
+    const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
+    const float* __restrict__ lam, const float* __restrict__ theta, const T* __restrict__ B,
+    const T* __restrict__ C, const float* __restrict__ Dv, const float* __restrict__ h_in,
+    const T* __restrict__ bl_in, const T* __restrict__ xl_in, T* __restrict__ y,
+    float* __restrict__ h_out, int64_t L, int H, int G, int N, int P, int R, int Q) {
+    extern __shared__ float smem[];
+    const int KP = N / 2, QR = Q * R;
+    float* S = smem;                       // N*P
+    float* Ct = S + N * P;                 // QR*N
+    float* Bt = Ct + QR * N;               // QR*N
+    float* X = Bt + QR * N;                // QR*P
+    float* Gm = X + QR * P;                // QR*QR
+    float* phi = Gm + QR * QR;             // Q*KP
+    float* cum = phi + Q * KP;             // Q
+    float* wv = cum + Q;                   // Q
+    float* gam = wv + Q;                   // Q
+    float* sv = gam + Q;                   // Q
+
+    const int bh = blockIdx.x;
+    const int b = bh / H, h = bh - b * H;
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, NT = blockDim.x;
+    const float Ah = A[h], Dh = Dv[h];
+
+    // Incoming state: h_in plus the beta term of the first token for the carry.
+    const bool carry = (bl_in != nullptr) && (xl_in != nullptr) && L > 0;
+    const float c1_first = carry ? (1.f - lam[(static_cast<int64_t>(b) * L) * H + h]) *
+                                       dt[(static_cast<int64_t>(b) * L) * H + h]
+                                 : 0.f;
+    for (int idx = tid; idx < N * P; idx += NT) {
+        const int n = idx / P, p = idx - n * P;
+        float s = h_in ? h_in[static_cast<size_t>(bh) * N * P + idx] : 0.f;
+        if (carry) {
+            float u = 0.f;
+            for (int r = 0; r < R; ++r)
+                u += io<T>::load(bl_in + ((static_cast<size_t>(b) * G + g) * R + r) * N + n) *
+                     io<T>::load(xl_in + (static_cast<size_t>(bh) * R + r) * P + p);
+            s += c1_first * u;
+        }
+        S[idx] = s;
+    }
+
+    const int64_t nchunks = (L + Q - 1) / Q;
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const int64_t t0 = c * Q;
+        const int nq = static_cast<int>(L - t0 < Q ? L - t0 : Q);
+        __syncthreads();   // previous chunk done with every LDS array
+
+        // Per-token scalars (a_t in cum before the prefix sum).
+        for (int i = tid; i < Q; i += NT) {
+            float a = 0.f, gm = 0.f, w = 0.f;
+            if (i < nq) {
+                const int64_t t = t0 + i;
+                const float dtv = dt[(b * L + t) * H + h], lv = lam[(b * L + t) * H + h];
+                a = dtv * Ah;
+                gm = lv * dtv;
+                w = gm;
+                if (t + 1 < L) w += (1.f - lam[(b * L + t + 1) * H + h]) * dt[(b * L + t + 1) * H + h];
+            }
+            cum[i] = a;
+            gam[i] = gm;
+            wv[i] = w;
+        }
+        // Chunk-local angle prefix sums, one pair per thread.
+        for (int k = tid; k < KP; k += NT) {
+            float acc = 0.f;
+            for (int i = 0; i < Q; ++i) {
+                if (i < nq) acc += theta[((b * L + t0 + i) * G + g) * KP + k];
+                phi[i * KP + k] = acc;
+            }
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float acc = 0.f;
+            for (int i = 0; i < Q; ++i) {
+                acc += cum[i];
+                cum[i] = acc;
+            }
+        }
+        // Rotated B, C (R(-phi_i) on pairs) and X, as fp32 in LDS.
+        for (int idx = tid; idx < Q * R * KP; idx += NT) {
+            const int i = idx / (R * KP), rem = idx - i * R * KP, r = rem / KP, k = rem - r * KP;
+            float b0 = 0.f, b1 = 0.f, c0 = 0.f, c1 = 0.f;
+            if (i < nq) {
+                const size_t o = (((b * L + t0 + i) * G + g) * R + r) * static_cast<size_t>(N) + 2 * k;
+                float sn, cs;
+                sincos_acc(phi[i * KP + k], &sn, &cs);
+                const float bb0 = io<T>::load(B + o), bb1 = io<T>::load(B + o + 1);
+                const float cc0 = io<T>::load(C + o), cc1 = io<T>::load(C + o + 1);
+                b0 = cs * bb0 + sn * bb1;
+                b1 = -sn * bb0 + cs * bb1;
+                c0 = cs * cc0 + sn * cc1;
+                c1 = -sn * cc0 + cs * cc1;
+            }
+            Bt[(i * R + r) * N + 2 * k] = b0;
+            Bt[(i * R + r) * N + 2 * k + 1] = b1;
+            Ct[(i * R + r) * N + 2 * k] = c0;
+            Ct[(i * R + r) * N + 2 * k + 1] = c1;
+        }
+        for (int idx = tid; idx < QR * P; idx += NT) {
+            const int i = idx / (R * P);
+            X[idx] = (i < nq) ? io<T>::load(x + ((b * L + t0 + i) * H + h) * static_cast<size_t>(R * P) +
+                                            (idx - i * R * P))
+                              : 0.f;
+        }
+        __syncthreads();
+        const float cend = cum[Q - 1];
+        for (int j = tid; j < Q; j += NT) sv[j] = __expf(cend - cum[j]) * wv[j];
+        // Masked intra-chunk block m_ij (Ct_i . Bt_j).
+        for (int idx = tid; idx < QR * QR; idx += NT) {
+            const int ir = idx / QR, js = idx - ir * QR;
+            const int i = ir / R, j = js / R;
+            float v = 0.f;
+            if (j <= i) {
+                float dot = 0.f;
+                for (int n = 0; n < N; ++n) dot += Ct[ir * N + n] * Bt[js * N + n];
+                const float m = (j < i) ? __expf(cum[i] - cum[j]) * wv[j] : gam[i];
+                v = m * dot;
+            }
+            Gm[idx] = v;
+        }
+        __syncthreads();
+        // Outputs.
+        for (int idx = tid; idx < QR * P; idx += NT) {
+            const int ir = idx / P, p = idx - ir * P;
+            const int i = ir / R;
+            if (i >= nq) continue;
+            float st = 0.f;
+            for (int n = 0; n < N; ++n) st += Ct[ir * N + n] * S[n * P + p];
+            float acc = __expf(cum[i]) * st;
+            for (int js = 0; js < (i + 1) * R; ++js) acc += Gm[ir * QR + js] * X[js * P + p];
+            acc += Dh * X[ir * P + p];
+            io<T>::store(y + ((b * L + t0 + i) * H + h) * static_cast<size_t>(R * P) + (ir - i * R) * P + p,
+                         acc);
+        }
+        __syncthreads();
+        // State update, one rotation pair x column per thread.
+        const float decay = __expf(cend);
+        for (int idx = tid; idx < KP * P; idx += NT) {
+            const int k = idx / P, p = idx - k * P;
+            float s0 = decay * S[(2 * k) * P + p], s1 = decay * S[(2 * k + 1) * P + p];
+            for (int js = 0; js < QR; ++js) {
+                const float xs = sv[js / R] * X[js * P + p];
+                s0 += Bt[js * N + 2 * k] * xs;
+                s1 += Bt[js * N + 2 * k + 1] * xs;
+            }
+            float sn, cs;
+            sincos_acc(phi[(Q - 1) * KP + k], &sn, &cs);
+            S[(2 * k) * P + p] = cs * s0 - sn * s1;
+            S[(2 * k + 1) * P + p] = sn * s0 + cs * s1;
+        }
+    }
+    __syncthreads();
+    if (h_out)
+        for (int idx = tid; idx < N * P; idx += NT) h_out[static_cast<size_t>(bh) * N * P + idx] = S[idx];
+}
+
+// state_out carry: B and X of the last token (or the incoming carry when L == 0).
+template <typename T>
+__global__ void carry_out(const T* __restrict__ x, const T* __restrict__ B,
+                          const T* __restrict__ bl_in, const T* __restrict__ xl_in,
+                          T* __restrict__ bl_out, T* __restrict__ xl_out, int64_t batch,
+                          int64_t L, int H, int G, int N, int P, int R) {
+    const int64_t nb = batch * G * R * N, nx = batch * H * R * P;
+    for (int64_t idx = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; idx < nb + nx;
+         idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        if (idx < nb) {
+            if (!bl_out) continue;
+            const int64_t bb = idx / (G * R * N), rem = idx - bb * G * R * N;
+            T v{};
+            if (L > 0) v = B[(bb * L + (L - 1)) * G * R * N + rem];
+            else if (bl_in && xl_in) v = bl_in[idx];
+            bl_out[idx] = v;
+        } else {
+            if (!xl_out) continue;
+            const int64_t i2 = idx - nb;
+            const int64_t bb = i2 / (H * R * P), rem = i2 - bb * H * R * P;
+            T v{};
+            if (L > 0) v = x[(bb * L + (L - 1)) * H * R * P + rem];
+            else if (bl_in && xl_in) v = xl_in[i2];
+            xl_out[i2] = v;
+        }
+    }
+}
+
+size_t generic_lds_bytes(const PrefillArgs& a) {
+    const size_t QR = static_cast<size_t>(a.Q) * a.R;
+    return sizeof(float) * (static_cast<size_t>(a.N) * a.P + 2 * QR * a.N + QR * a.P + QR * QR +
+                            static_cast<size_t>(a.Q) * (a.N / 2) + 4 * static_cast<size_t>(a.Q));
+}
+
+template <typename T>
+static hipError_t launch_generic_t(const PrefillArgs& a, hipStream_t st) {
+    const size_t shm = generic_lds_bytes(a);
+    if (shm > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_generic<T>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(shm));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(prefill_generic<T>, dim3(static_cast<unsigned>(a.batch * a.H)), dim3(256), shm,
+                       st, static_cast<const T*>(a.x), a.dt, a.A, a.lam, a.theta,
+                       static_cast<const T*>(a.B), static_cast<const T*>(a.C), a.D, a.h_in,
+                       static_cast<const T*>(a.bl_in), static_cast<const T*>(a.xl_in),
+                       static_cast<T*>(a.y), a.h_out, a.L, a.H, a.G, a.N, a.P, a.R, a.Q);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_generic(const PrefillArgs& a, hipStream_t st) {
+    return a.bf16 ? launch_generic_t<bf16_t>(a, st) : launch_generic_t<float>(a, st);
+}
+
+template <typename T>
+static hipError_t launch_carry_t(const PrefillArgs& a, hipStream_t st) {
+    const int64_t n = a.batch * (static_cast<int64_t>(a.G) * a.R * a.N + static_cast<int64_t>(a.H) * a.R * a.P);
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(carry_out<T>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                       static_cast<const T*>(a.x), static_cast<const T*>(a.B),
+                       static_cast<const T*>(a.bl_in), static_cast<const T*>(a.xl_in),
+                       static_cast<T*>(a.bl_out), static_cast<T*>(a.xl_out), a.batch, a.L, a.H,
+                       a.G, a.N, a.P, a.R);
+    return hipGetLastError();
+}
+
+hipError_t launch_carry_out(const PrefillArgs& a, hipStream_t st) {
+    return a.bf16 ? launch_carry_t<bf16_t>(a, st) : launch_carry_t<float>(a, st);
+}
+
+}  // namespace m3

@@ -1,0 +1,197 @@
+"""Python binding of libm3scan.so: argument marshalling only.
+
+Every step of the scan runs in the library's HIP kernels; PyTorch supplies the
+device memory and the current HIP stream.  There is no fallback: if the library
+is missing or a call fails, these functions raise.
+
+Layouts are those of include/m3scan.h (contiguous, last index fastest):
+  x, y (b, L, H, R, P)   dt, lam (b, L, H)   A, D (H,)   theta (b, L, G, N/2)
+  B, C (b, L, G, R, N)   state h (b, H, N, P) fp32
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libm3scan.so")
+
+M3_F32, M3_BF16 = 0, 1
+_IO = {torch.float32: M3_F32, torch.bfloat16: M3_BF16}
+STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape or dtype",
+          -3: "workspace too small", -4: "HIP runtime error"}
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("ngroups", ctypes.c_int64), ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+                ("rank", ctypes.c_int64), ("chunk", ctypes.c_int64), ("io_dtype", ctypes.c_int32)]
+
+
+class State(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_void_p), ("b_last", ctypes.c_void_p), ("x_last", ctypes.c_void_p)]
+
+
+class M3Error(RuntimeError):
+    def __init__(self, where: str, code: int):
+        super().__init__(f"{where}: {STATUS.get(code, code)} ({code})")
+        self.code = code
+
+
+_lib = None
+
+
+def lib(path: str = LIB_PATH):
+    """Load libm3scan.so once and declare its C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m state_space_sequence_scan_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    L.m3_status_string.restype = ctypes.c_char_p
+    L.m3_status_string.argtypes = [ctypes.c_int]
+    L.m3_version.restype = ctypes.c_int32
+    L.m3_version.argtypes = []
+    L.m3_prefill_workspace_size.restype = ctypes.c_int
+    L.m3_prefill_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(sz)]
+    L.m3_prefill_chunked.restype = ctypes.c_int
+    L.m3_prefill_chunked.argtypes = ([ctypes.POINTER(Dims)] + [vp] * 8 +
+                                     [ctypes.POINTER(State), ctypes.POINTER(State), vp, vp, sz, vp])
+    L.m3_decode_step.restype = ctypes.c_int
+    L.m3_decode_step.argtypes = [ctypes.POINTER(Dims)] + [vp] * 13
+    _lib = L
+    return L
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+@dataclasses.dataclass
+class DecodeState:
+    """Scan state: h (b,H,N,P) fp32, and the previous token's B (b,G,R,N) and
+    X (b,H,R,P) in the io dtype (the trapezoid carry; None = zero)."""
+    h: torch.Tensor
+    b_last: Optional[torch.Tensor] = None
+    x_last: Optional[torch.Tensor] = None
+
+
+def make_dims(batch, seqlen, nheads, ngroups, headdim, dstate, rank, chunk, io_dtype) -> Dims:
+    return Dims(batch, seqlen, nheads, ngroups, headdim, dstate, rank, chunk, io_dtype)
+
+
+def workspace_size(dims: Dims) -> int:
+    n = ctypes.c_size_t(0)
+    rc = lib().m3_prefill_workspace_size(ctypes.byref(dims), ctypes.byref(n))
+    if rc != 0:
+        raise M3Error("m3_prefill_workspace_size", rc)
+    return int(n.value)
+
+
+def prefill(x, dt, A, lam, theta, B, C, D, chunk: int, state_in: Optional[DecodeState] = None,
+            out_state: bool = True, y: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None):
+    """Chunked prefill.  Returns (y, DecodeState or None)."""
+    b, L, H, R, P = x.shape
+    G, N = B.shape[2], B.shape[4]
+    dev = x.device
+    io = x.dtype
+    if io not in _IO:
+        raise ValueError(f"x dtype {io} not supported (fp32 or bf16)")
+    _check(x, "x", (b, L, H, R, P), io, dev)
+    _check(dt, "dt", (b, L, H), torch.float32, dev)
+    _check(lam, "lam", (b, L, H), torch.float32, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(theta, "theta", (b, L, G, N // 2), torch.float32, dev)
+    _check(B, "B", (b, L, G, R, N), io, dev)
+    _check(C, "C", (b, L, G, R, N), io, dev)
+    dims = make_dims(b, L, H, G, P, N, R, chunk, _IO[io])
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _check(y, "y", x.shape, io, dev)
+    sin = None
+    if state_in is not None:
+        _check(state_in.h, "state_in.h", (b, H, N, P), torch.float32, dev)
+        if state_in.b_last is not None:
+            _check(state_in.b_last, "state_in.b_last", (b, G, R, N), io, dev)
+            _check(state_in.x_last, "state_in.x_last", (b, H, R, P), io, dev)
+        sin = State(state_in.h.data_ptr(),
+                    None if state_in.b_last is None else state_in.b_last.data_ptr(),
+                    None if state_in.x_last is None else state_in.x_last.data_ptr())
+    sout = st = None
+    if out_state:
+        st = DecodeState(torch.empty((b, H, N, P), dtype=torch.float32, device=dev),
+                         torch.empty((b, G, R, N), dtype=io, device=dev),
+                         torch.empty((b, H, R, P), dtype=io, device=dev))
+        sout = State(st.h.data_ptr(), st.b_last.data_ptr(), st.x_last.data_ptr())
+    ws = workspace_size(dims)
+    if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
+        workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+    rc = lib().m3_prefill_chunked(ctypes.byref(dims), _p(x), _p(dt), _p(A), _p(lam), _p(theta),
+                                  _p(B), _p(C), _p(D),
+                                  None if sin is None else ctypes.byref(sin),
+                                  None if sout is None else ctypes.byref(sout), _p(y),
+                                  _p(workspace) if ws > 0 else None,
+                                  ws, _stream(dev))
+    if rc != 0:
+        raise M3Error("m3_prefill_chunked", rc)
+    return y, st
+
+
+def decode_step(state: DecodeState, x_t, dt_t, A, lam_t, theta_t, B_t, C_t, D,
+                y_t: Optional[torch.Tensor] = None, advance: bool = True):
+    """One decode step: updates state.h in place and returns y_t (b,H,R,P).
+
+    With advance=True the state's carry becomes (B_t, x_t) -- references to the
+    caller's tensors, no copy."""
+    b, H, R, P = x_t.shape
+    G, N = B_t.shape[1], B_t.shape[3]
+    dev, io = x_t.device, x_t.dtype
+    if io not in _IO:
+        raise ValueError(f"x_t dtype {io} not supported (fp32 or bf16)")
+    _check(state.h, "state.h", (b, H, N, P), torch.float32, dev)
+    _check(x_t, "x_t", (b, H, R, P), io, dev)
+    _check(dt_t, "dt_t", (b, H), torch.float32, dev)
+    _check(lam_t, "lam_t", (b, H), torch.float32, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(theta_t, "theta_t", (b, G, N // 2), torch.float32, dev)
+    _check(B_t, "B_t", (b, G, R, N), io, dev)
+    _check(C_t, "C_t", (b, G, R, N), io, dev)
+    if state.b_last is not None:
+        _check(state.b_last, "state.b_last", (b, G, R, N), io, dev)
+        _check(state.x_last, "state.x_last", (b, H, R, P), io, dev)
+    if y_t is None:
+        y_t = torch.empty_like(x_t)
+    dims = make_dims(b, 1, H, G, P, N, R, 1, _IO[io])
+    rc = lib().m3_decode_step(ctypes.byref(dims), _p(state.h), _p(state.b_last), _p(state.x_last),
+                              _p(x_t), _p(dt_t), _p(A), _p(lam_t), _p(theta_t), _p(B_t), _p(C_t),
+                              _p(D), _p(y_t), _stream(dev))
+    if rc != 0:
+        raise M3Error("m3_decode_step", rc)
+    if advance:
+        state.b_last, state.x_last = B_t, x_t
+    return y_t

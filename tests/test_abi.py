@@ -1,0 +1,131 @@
+"""The C-ABI library loads and exports what include/m3scan.h declares; argument
+errors come back as status codes before anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from state_space_sequence_scan_amd import m3scan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "m3scan.h")
+
+
+def declared_symbols():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[\w\s\*]*?\b(m3_\w+)\s*\(", txt, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(m3scan.LIB_PATH):
+        from state_space_sequence_scan_amd import build
+        build.build()
+    return m3scan.lib()
+
+
+def test_header_declares_the_entry_points():
+    assert declared_symbols() == ["m3_decode_step", "m3_prefill_chunked", "m3_prefill_workspace_size",
+                                  "m3_status_string", "m3_version"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", m3scan.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (m3_\w+)$", out, re.M))
+    for s in declared_symbols():
+        assert s in exported, s
+        assert hasattr(lib, s)
+
+
+def test_status_strings_and_version(lib):
+    for code, text in m3scan.STATUS.items():
+        assert lib.m3_status_string(code).decode() == text
+    assert lib.m3_status_string(99).decode() == "unknown status"
+    assert lib.m3_version() >= 100
+
+
+def _dims(**kw):
+    base = dict(batch=2, seqlen=64, nheads=4, ngroups=2, headdim=16, dstate=16, rank=2, chunk=16,
+                io_dtype=m3scan.M3_F32)
+    base.update(kw)
+    return m3scan.Dims(**base)
+
+
+BAD_DIMS = [dict(batch=0), dict(seqlen=-1), dict(nheads=0), dict(ngroups=3), dict(dstate=15),
+            dict(headdim=0), dict(rank=0), dict(chunk=0), dict(io_dtype=7)]
+
+
+@pytest.mark.parametrize("kw", BAD_DIMS, ids=lambda k: next(iter(k)))
+def test_workspace_size_rejects_bad_dims(lib, kw):
+    n = ctypes.c_size_t(123)
+    assert lib.m3_prefill_workspace_size(ctypes.byref(_dims(**kw)), ctypes.byref(n)) == -1
+    assert lib.m3_prefill_workspace_size(None, ctypes.byref(n)) == -1
+    assert lib.m3_prefill_workspace_size(ctypes.byref(_dims()), None) == -1
+
+
+def test_workspace_size_ok(lib):
+    n = ctypes.c_size_t(123)
+    assert lib.m3_prefill_workspace_size(ctypes.byref(_dims()), ctypes.byref(n)) == 0
+    assert n.value >= 0
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails its checks first
+
+
+@pytest.mark.parametrize("kw", BAD_DIMS, ids=lambda k: next(iter(k)))
+def test_prefill_rejects_bad_dims(lib, kw):
+    d = _dims(**kw)
+    rc = lib.m3_prefill_chunked(ctypes.byref(d), *[FAKE] * 8, None, None, FAKE, None, 0, None)
+    assert rc == -1
+
+
+def test_prefill_rejects_null_inputs(lib):
+    d = _dims()
+    for i in range(8):
+        args = [FAKE] * 8
+        args[i] = None
+        assert lib.m3_prefill_chunked(ctypes.byref(d), *args, None, None, FAKE, None, 0, None) == -1
+    # y missing
+    assert lib.m3_prefill_chunked(ctypes.byref(d), *[FAKE] * 8, None, None, None, None, 0, None) == -1
+    # state_in without h, or with half a carry
+    s = m3scan.State(None, None, None)
+    assert lib.m3_prefill_chunked(ctypes.byref(d), *[FAKE] * 8, ctypes.byref(s), None, FAKE, None, 0,
+                                  None) == -1
+    s = m3scan.State(0x1000, 0x1000, None)
+    assert lib.m3_prefill_chunked(ctypes.byref(d), *[FAKE] * 8, ctypes.byref(s), None, FAKE, None, 0,
+                                  None) == -1
+
+
+def test_prefill_rejects_unsupported(lib):
+    d = _dims(rank=9, dstate=512, headdim=512, chunk=256)
+    n = ctypes.c_size_t(0)
+    assert lib.m3_prefill_workspace_size(ctypes.byref(d), ctypes.byref(n)) == -2
+    assert lib.m3_prefill_chunked(ctypes.byref(d), *[FAKE] * 8, None, None, FAKE, None, 0, None) == -2
+
+
+@pytest.mark.parametrize("kw", [k for k in BAD_DIMS if "seqlen" not in k and "chunk" not in k],
+                         ids=lambda k: next(iter(k)))
+def test_decode_rejects_bad_dims(lib, kw):
+    d = _dims(**kw)
+    assert lib.m3_decode_step(ctypes.byref(d), *[FAKE] * 13) == -1
+
+
+def test_decode_rejects_null_and_half_carry(lib):
+    d = _dims()
+    for i in [0, 3, 4, 5, 6, 7, 8, 9, 10, 11]:
+        args = [FAKE] * 13
+        args[i] = None
+        assert lib.m3_decode_step(ctypes.byref(d), *args) == -1, i
+    args = [FAKE] * 13
+    args[1] = None          # b_last without x_last
+    assert lib.m3_decode_step(ctypes.byref(d), *args) == -1
+
+
+def test_binding_raises_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(m3scan, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        m3scan.lib(str(tmp_path / "missing.so"))
