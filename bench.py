@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark of the Mamba-3 scan on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+the chunked prefill of every sequence, then the single-token decode steps that
+continue from its state (default workload: the 1.5B-scale MIMO R=4 layer at
+batch 256, 1024-token prefill + 512 decode steps).  Inputs are generated on the
+GPU and resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is whole-step token throughput (prefill tokens +
+decode tokens, all sequences) per second; the line also carries the prefill
+tokens/s, the decode state bandwidth, the roofline of the dominant kernel and
+the CPU oracle timed on this host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill scan tokens/s + decode state GB/s (% roofline), 1.5B-shape layer, 1 GPU"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2516.6        # dense bf16 MFMA: 4096 flop/clk/CU x 256 CU x 2.4 GHz
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="c4", help="c1, c2, c3 (prefill only) or c4 (prefill + decode)")
+    ap.add_argument("--decode-steps", type=int, default=None, help="override the decode steps per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--check-slices", type=int, default=2, help="(b,h) slices checked against the oracle")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(cfg, L, steps):
+    """Bytes the method must move (see the workload formulas in the design notes)."""
+    s = 2 if cfg.io_dtype == "bf16" else 4
+    b, H, G, P, N, R = cfg.batch, cfg.nheads, cfg.ngroups, cfg.headdim, cfg.dstate, cfg.rank
+    pre = 0
+    if L > 0:
+        pre += b * L * H * (2 * R * P * s + 8)              # x read, y write, dt, lambda
+        pre += b * L * G * (2 * N * R * s + 4 * (N // 2))   # B, C, theta
+        pre += b * H * N * P * 4                            # state out
+        pre += b * (G * R * N + H * R * P) * s              # carry out
+        pre += 8 * H
+    dec = 0
+    if steps > 0:
+        dec += 2 * b * H * N * P * 4                        # state read + write
+        dec += b * H * (3 * R * P * s + 8)                  # x_t, x_last read, y_t write, dt, lambda
+        dec += b * G * (3 * R * N * s + 4 * (N // 2))       # B_t, C_t, b_last, theta
+        dec += 8 * H
+    return pre, dec
+
+
+def prefill_flops(cfg, L):
+    """Useful MFMA-shaped flops of the chunked prefill (causal half of each chunk block)."""
+    b, H, G, P, N, R, Q = cfg.batch, cfg.nheads, cfg.ngroups, cfg.headdim, cfg.dstate, cfg.rank, cfg.chunk
+    tok = b * L
+    return 2 * (tok * G * R * R * N * (Q + 1) / 2 + tok * H * (R * R * P * (Q + 1) / 2 + 2 * R * N * P))
+
+
+def source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "state_space_sequence_scan_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(kernel_file, src_names, per_launch_alg):
+    """HBM bytes per launch from a committed counter summary, if it was taken on the
+    current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", kernel_file)
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        if rec.get("source_sha") != source_sha(*src_names):
+            return None
+        return float(rec["hbm_bytes_per_dispatch"])
+    except Exception:
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the scan on a single MI355X "
+              "(multi-GPU sharding is a design note, not implemented); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from state_space_sequence_scan_amd import CONFIGS, inputs, m3scan
+
+    cfg = CONFIGS[args.workload]
+    steps_dec = cfg.decode_steps if args.decode_steps is None else args.decode_steps
+    L = cfg.seqlen
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    m3scan.lib()
+    stream = torch.cuda.current_stream(dev)
+
+    t_gen = time.time()
+    d = inputs.draw_config(cfg, device=dev)
+    dd = inputs.draw_decode(cfg, steps_dec, device=dev) if steps_dec > 0 else None
+    y = torch.empty_like(d["x"])
+    ydec = torch.empty((max(steps_dec, 1),) + tuple(d["x"][:, 0].shape), dtype=d["x"].dtype, device=dev)
+    torch.cuda.synchronize()
+    t_gen = time.time() - t_gen
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def one_step(record=None):
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record(stream)
+        _, st = m3scan.prefill(d["x"], d["dt"], d["A"], d["lam"], d["theta"], d["B"], d["C"], d["D"],
+                               cfg.chunk, y=y)
+        e1.record(stream)
+        for t in range(steps_dec):
+            m3scan.decode_step(st, dd["x"][t], dd["dt"][t], d["A"], dd["lam"][t], dd["theta"][t],
+                               dd["B"][t], dd["C"][t], d["D"], y_t=ydec[t])
+        e2.record(stream)
+        if record is not None:
+            record.append((e0, e1, e2))
+        return st
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        st = one_step(recs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [a.elapsed_time(b) for a, b, _ in recs]
+    dec_ms = [b.elapsed_time(c) for _, b, c in recs]
+    step_ms = wall * 1e3 / args.steps
+    pre_avg, dec_avg = float(np.mean(pre_ms)), float(np.mean(dec_ms))
+
+    tokens_pre = cfg.batch * L
+    tokens_dec = cfg.batch * steps_dec
+    value = (tokens_pre + tokens_dec) / (step_ms / 1e3)
+    pre_bytes, dec_bytes = algorithmic_bytes(cfg, L, steps_dec)
+    pre_tps = tokens_pre / (pre_avg / 1e3)
+    pre_gbs = pre_bytes / (pre_avg / 1e3) / 1e9
+    dec_launch_ms = dec_avg / max(steps_dec, 1)
+    dec_gbs = dec_bytes / (dec_launch_ms / 1e3) / 1e9 if steps_dec else 0.0
+    state_gbs = (2 * cfg.batch * cfg.nheads * cfg.dstate * cfg.headdim * 4) / (dec_launch_ms / 1e3) / 1e9 \
+        if steps_dec else 0.0
+    flops = prefill_flops(cfg, L)
+
+    # Dominant kernel: the one with the larger share of the step.
+    if steps_dec and dec_avg >= pre_avg:
+        traffic = pmc_traffic("decode_c4_hbm_counters.json", ["m3_decode.hip"], dec_bytes)
+        roof = {"kernel": "decode_fast<bf16,128,64,4>", "bound": "hbm",
+                "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "alg_bytes_per_launch": dec_bytes, "avg_launch_us": round(dec_launch_ms * 1e3, 2)}
+    else:
+        traffic = pmc_traffic(f"prefill_{args.workload}_hbm_counters.json",
+                              ["m3_prefill_mfma.hip"], pre_bytes)
+        roof = {"kernel": "prefill (chunked scan)", "bound": "hbm",
+                "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(pre_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "alg_bytes_per_launch": pre_bytes, "avg_launch_us": round(pre_avg * 1e3, 2)}
+
+    # Sampled parity of this very run against the oracle, and the CPU baseline.
+    check = None
+    cpu = None
+    if args.check_slices > 0 or not args.no_cpu_baseline:
+        import oracle
+
+        def slice_inputs(bi, h, with_decode=True):
+            g = h // (cfg.nheads // cfg.ngroups)
+            f = lambda t: t.detach().double().cpu().numpy()
+            parts = {
+                "x": [f(d["x"][bi:bi + 1, :, h:h + 1])], "dt": [f(d["dt"][bi:bi + 1, :, h:h + 1])],
+                "lam": [f(d["lam"][bi:bi + 1, :, h:h + 1])],
+                "theta": [f(d["theta"][bi:bi + 1, :, g:g + 1])],
+                "B": [f(d["B"][bi:bi + 1, :, g:g + 1])], "C": [f(d["C"][bi:bi + 1, :, g:g + 1])]}
+            if with_decode and steps_dec:
+                parts["x"].append(f(dd["x"][:, bi:bi + 1, h:h + 1].transpose(0, 1)))
+                parts["dt"].append(f(dd["dt"][:, bi:bi + 1, h:h + 1].transpose(0, 1)))
+                parts["lam"].append(f(dd["lam"][:, bi:bi + 1, h:h + 1].transpose(0, 1)))
+                parts["theta"].append(f(dd["theta"][:, bi:bi + 1, g:g + 1].transpose(0, 1)))
+                parts["B"].append(f(dd["B"][:, bi:bi + 1, g:g + 1].transpose(0, 1)))
+                parts["C"].append(f(dd["C"][:, bi:bi + 1, g:g + 1].transpose(0, 1)))
+            out = {k: np.concatenate(v, axis=1) for k, v in parts.items()}
+            out["A"] = f(d["A"][h:h + 1])
+            out["D"] = f(d["D"][h:h + 1])
+            return out
+
+        order = ("x", "dt", "A", "lam", "theta", "B", "C", "D")
+        if args.check_slices > 0:
+            rng = np.random.default_rng(cfg.seed)
+            errs = []
+            for _ in range(args.check_slices):
+                bi, h = int(rng.integers(cfg.batch)), int(rng.integers(cfg.nheads))
+                si = slice_inputs(bi, h)
+                yr, hr = oracle.scan(*[si[k] for k in order])
+                yg = [y[bi:bi + 1, :, h:h + 1].double().cpu().numpy()]
+                if steps_dec:
+                    yg.append(ydec[:steps_dec, bi:bi + 1, h:h + 1].transpose(0, 1).double().cpu().numpy())
+                yg = np.concatenate(yg, axis=1)
+                e = float(np.max(np.abs(yg - yr)) / np.max(np.abs(yr)))
+                eh = float(np.max(np.abs(st.h[bi, h].double().cpu().numpy() - hr[0, 0])) / np.max(np.abs(hr)))
+                errs.append(max(e, eh))
+            check = {"slices": args.check_slices, "max_rel_err": float(max(errs)),
+                     "tolerance": 2e-2 if cfg.io_dtype == "bf16" else 1e-4}
+        if not args.no_cpu_baseline:
+            threads = oracle.max_threads()
+            si = slice_inputs(0, 0)
+            t1 = time.perf_counter()
+            oracle.scan(*[si[k] for k in order], nthreads=1)
+            one = time.perf_counter() - t1
+            n = int(max(threads, min(cfg.batch * cfg.nheads, args.cpu_seconds * threads / max(one, 1e-6))))
+            n = max(threads, (n // threads) * threads)
+            hs = list(range(n))
+            batch_in = [slice_inputs(i // cfg.nheads % cfg.batch, i % cfg.nheads) for i in hs]
+            # each sampled slice becomes its own head (and group) of one oracle call
+            stack = {k: np.concatenate([s[k] for s in batch_in], axis=2)
+                     for k in ("x", "dt", "lam", "theta", "B", "C")}
+            stack["A"] = np.concatenate([s["A"] for s in batch_in])
+            stack["D"] = np.concatenate([s["D"] for s in batch_in])
+            t1 = time.perf_counter()
+            oracle.scan(*[stack[k] for k in order], nthreads=threads)
+            sec = time.perf_counter() - t1
+            tok_per_slice = L + steps_dec
+            # tokens of the full workload carry all H heads: (slice-tokens / H) per second
+            cpu = {"value": round(n * tok_per_slice / cfg.nheads / sec, 2), "unit": "tokens/s",
+                   "cores": threads, "kind": "oracle",
+                   "sample": f"{n} (batch, head) slices of the workload, {tok_per_slice} tokens each "
+                             f"({L} prefill + {steps_dec} decode), fp64 sequential loop, "
+                             f"{sec:.1f} s; scaled to whole-workload tokens (1/{cfg.nheads} per slice-token)"}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded torch generators on the GPU; distributions of the workload)",
+        "config": {"workload": cfg.label, "name": cfg.name, "batch": cfg.batch, "prefill_len": L,
+                   "decode_steps": steps_dec, "heads": cfg.nheads, "groups": cfg.ngroups,
+                   "headdim": cfg.headdim, "dstate": cfg.dstate, "rank": cfg.rank, "chunk": cfg.chunk,
+                   "io_dtype": cfg.io_dtype, "state_dtype": "fp32"},
+        "prefill": {"ms": round(pre_avg, 4), "tokens_per_s": round(pre_tps, 1),
+                    "alg_GB_per_s": round(pre_gbs, 1), "hbm_frac": round(pre_gbs / HBM_PEAK_GBS, 4),
+                    "mfma_tflops": round(flops / (pre_avg / 1e3) / 1e12, 2),
+                    "mfma_frac": round(flops / (pre_avg / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "decode": ({"ms_total": round(dec_avg, 4), "us_per_step": round(dec_launch_ms * 1e3, 2),
+                    "steps_per_s": round(1e3 / dec_launch_ms, 1), "state_GB_per_s": round(state_gbs, 1),
+                    "alg_GB_per_s": round(dec_gbs, 1), "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4)}
+                   if steps_dec else None),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity_check": check,
+        "input_gen_s": round(t_gen, 2),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -45,6 +45,10 @@ namespace m3 {
 
 PrefillPlan plan_prefill(const PrefillArgs& a) {
     PrefillPlan p{PrefillPath::Unsupported, 1, 0, 0};
+    if (mfma_supported(a)) {
+        plan_mfma(a, &p);
+        return p;
+    }
     if (a.R > kMaxRankGeneric) return p;
     const size_t lds = generic_lds_bytes(a);
     if (lds <= kMaxLds) {
@@ -57,7 +61,13 @@ PrefillPlan plan_prefill(const PrefillArgs& a) {
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStream_t st) {
     hipError_t e = hipSuccess;
     if (plan.path == PrefillPath::Generic) {
-        if (a.batch * a.H > 0) e = launch_prefill_generic(a, st);
+        e = launch_prefill_generic(a, st);
+    } else if (plan.path == PrefillPath::Mfma) {
+        if (a.L == 0) {
+            e = launch_prefill_generic(a, st);   // no chunks: passes the state through
+        } else {
+            e = launch_prefill_mfma(a, plan, st);
+        }
     } else {
         return hipErrorInvalidValue;
     }

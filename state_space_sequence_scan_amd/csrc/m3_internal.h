@@ -68,6 +68,12 @@ hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStre
 size_t generic_lds_bytes(const PrefillArgs& a);
 hipError_t launch_prefill_generic(const PrefillArgs& a, hipStream_t st);
 
+// Matrix-core family (bf16, N = 128, P = 64, R in {1, 2, 4}, Q in {32, 64}),
+// in m3_prefill_mfma.hip.
+bool mfma_supported(const PrefillArgs& a);
+void plan_mfma(const PrefillArgs& a, PrefillPlan* plan);
+hipError_t launch_prefill_mfma(const PrefillArgs& a, const PrefillPlan& plan, hipStream_t st);
+
 // Carry-out copy (B and X of the last token), in m3_prefill_generic.hip.
 hipError_t launch_carry_out(const PrefillArgs& a, hipStream_t st);
 
