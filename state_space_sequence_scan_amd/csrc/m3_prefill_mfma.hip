@@ -66,6 +66,12 @@ struct PrepLayout {
 // ------------------------------------------------------------------------------------
 // rope_prep
 // ------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 v = {to_bf(a), to_bf(b)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 template <int R, int Q>
 __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
                                                 const uint16_t* __restrict__ C,
@@ -73,7 +79,7 @@ __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
                                                 int nchunks, uint8_t* __restrict__ prep) {
     constexpr int QR = Q * R;
     __shared__ float sCos[Q][KP], sSin[Q][KP];
-    __shared__ __align__(16) uint16_t sB[QR][N + 8];
+    __shared__ float sPart[4][KP];
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     const int64_t t0 = static_cast<int64_t>(c) * Q;
@@ -94,11 +100,9 @@ __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
 #pragma unroll
         for (int e = 0; e < QP; ++e) {
             const int i = part * QP + e;
-            th[e] = (i < nq) ? theta[((b * L + t0 + i) * G + g) * KP + k] : 0.f;
-            run += th[e];
+            run += (i < nq) ? theta[((b * L + t0 + i) * G + g) * KP + k] : 0.f;
             th[e] = run;
         }
-        __shared__ float sPart[4][KP];
         sPart[part][k] = run;
         __syncthreads();
         float off = 0.f;
@@ -110,8 +114,7 @@ __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
             sCos[part * QP + e][k] = cn;
             sSin[part * QP + e][k] = sn;
         }
-        if (part == 3) {
-            // total angle of the chunk (tokens past the end add nothing)
+        if (part == 3) {   // total angle of the chunk (tokens past the end add nothing)
             float sn, cn;
             sincos_acc(th[QP - 1] + off, &sn, &cn);
             cs[2 * k] = cn;
@@ -119,42 +122,42 @@ __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
         }
     }
     __syncthreads();
-    // Rotate pairs: R(-phi) (x0, x1) = (c x0 + s x1, -s x0 + c x1).
-    for (int idx = tid; idx < QR * KP; idx += NT) {
-        const int row = idx / KP, k = idx - row * KP;
-        const int i = row / R, r = row - i * R;
-        float b0 = 0.f, b1 = 0.f, c0 = 0.f, c1 = 0.f;
-        if (i < nq) {
-            const size_t o = (((b * L + t0 + i) * G + g) * R + r) * static_cast<size_t>(N) + 2 * k;
-            const uint32_t bb = *reinterpret_cast<const uint32_t*>(B + o);
-            const uint32_t cc = *reinterpret_cast<const uint32_t*>(C + o);
-            const float cn = sCos[i][k], sn = sSin[i][k];
-            const float x0 = bits_to_f(bb & 0xffff), x1 = bits_to_f(bb >> 16);
-            const float y0 = bits_to_f(cc & 0xffff), y1 = bits_to_f(cc >> 16);
-            b0 = cn * x0 + sn * x1;
-            b1 = -sn * x0 + cn * x1;
-            c0 = cn * y0 + sn * y1;
-            c1 = -sn * y0 + cn * y1;
-        }
-        const uint32_t pb = f32_to_bf16(b0) | (static_cast<uint32_t>(f32_to_bf16(b1)) << 16);
-        const uint32_t pc = f32_to_bf16(c0) | (static_cast<uint32_t>(f32_to_bf16(c1)) << 16);
-        *reinterpret_cast<uint32_t*>(Bt + static_cast<size_t>(row) * N + 2 * k) = pb;
-        *reinterpret_cast<uint32_t*>(Ct + static_cast<size_t>(row) * N + 2 * k) = pc;
-        *reinterpret_cast<uint32_t*>(&sB[row][2 * k]) = pb;
-    }
-    __syncthreads();
-    // n-major copy: BtT[n][row], 8 rows per 16-byte store.
-    for (int idx = tid; idx < N * (QR / 8); idx += NT) {
-        const int n = idx / (QR / 8), r8 = idx - n * (QR / 8);
-        uint16_t v[8];
+    // One unit = 8 consecutive rows (token, rank) x one rotation pair k:
+    // R(-phi) (x0, x1) = (c x0 + s x1, -s x0 + c x1).  Token-major stores are
+    // 4 bytes per row; the n-major copy is two 16-byte stores (rows 2k, 2k+1).
+    for (int u = tid; u < (QR / 8) * KP; u += NT) {
+        const int r8 = u / KP, k = u - r8 * KP;
+        uint32_t lo[4] = {0u, 0u, 0u, 0u}, hi[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = sB[8 * r8 + e][n];
-        uint4 w;
-        w.x = v[0] | (static_cast<uint32_t>(v[1]) << 16);
-        w.y = v[2] | (static_cast<uint32_t>(v[3]) << 16);
-        w.z = v[4] | (static_cast<uint32_t>(v[5]) << 16);
-        w.w = v[6] | (static_cast<uint32_t>(v[7]) << 16);
-        *reinterpret_cast<uint4*>(BtT + static_cast<size_t>(n) * QR + 8 * r8) = w;
+        for (int e = 0; e < 8; ++e) {
+            const int row = 8 * r8 + e;
+            const int i = row / R, r = row - i * R;
+            float b0 = 0.f, b1 = 0.f, c0 = 0.f, c1 = 0.f;
+            if (i < nq) {
+                const size_t o = (((b * L + t0 + i) * G + g) * R + r) * static_cast<size_t>(N) + 2 * k;
+                const uint32_t bb = *reinterpret_cast<const uint32_t*>(B + o);
+                const uint32_t cc = *reinterpret_cast<const uint32_t*>(C + o);
+                const float cn = sCos[i][k], sn = sSin[i][k];
+                const float x0 = bits_to_f(bb & 0xffff), x1 = bits_to_f(bb >> 16);
+                const float y0 = bits_to_f(cc & 0xffff), y1 = bits_to_f(cc >> 16);
+                b0 = cn * x0 + sn * x1;
+                b1 = -sn * x0 + cn * x1;
+                c0 = cn * y0 + sn * y1;
+                c1 = -sn * y0 + cn * y1;
+            }
+            const uint32_t pb = pack_bf16x2(b0, b1);
+            *reinterpret_cast<uint32_t*>(Bt + static_cast<size_t>(row) * N + 2 * k) = pb;
+            *reinterpret_cast<uint32_t*>(Ct + static_cast<size_t>(row) * N + 2 * k) = pack_bf16x2(c0, c1);
+            if (e & 1) {
+                lo[e >> 1] |= (pb & 0xffffu) << 16;
+                hi[e >> 1] |= pb & 0xffff0000u;
+            } else {
+                lo[e >> 1] = pb & 0xffffu;
+                hi[e >> 1] = pb >> 16;
+            }
+        }
+        *reinterpret_cast<uint4*>(BtT + static_cast<size_t>(2 * k) * QR + 8 * r8) = uint4{lo[0], lo[1], lo[2], lo[3]};
+        *reinterpret_cast<uint4*>(BtT + static_cast<size_t>(2 * k + 1) * QR + 8 * r8) = uint4{hi[0], hi[1], hi[2], hi[3]};
     }
 }
 
@@ -197,240 +200,384 @@ __device__ float initial_state(const ScanParams& p, int b, int h, int g, int n, 
     return s;
 }
 
-template <int R, int Q, bool FULL>
-__global__ __launch_bounds__(NT) void scan_mfma(ScanParams p) {
+// Swap a value with the neighbouring lane (lane ^ 1) through a DPP quad permutation.
+__device__ __forceinline__ float swap_adjacent(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+
+// Prefetched data is carried in vector-typed values (never addressable arrays)
+// so that it stays in registers while the loads are in flight.
+template <int K> using u32v = uint32_t __attribute__((ext_vector_type(K)));
+template <int K> using bfv = __bf16 __attribute__((ext_vector_type(K)));
+
+template <int K>
+__device__ __forceinline__ uint4 quad(const u32v<K>& v, int i) {   // i: constant after unrolling
+    return uint4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+}
+template <int K>
+__device__ __forceinline__ void set_quad(u32v<K>& v, int i, uint4 q) {
+    v[4 * i] = q.x;
+    v[4 * i + 1] = q.y;
+    v[4 * i + 2] = q.z;
+    v[4 * i + 3] = q.w;
+}
+template <int K>
+__device__ __forceinline__ bf16x8 oct(const bfv<K>& v, int i) {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = v[8 * i + e];
+    return o;
+}
+template <int K>
+__device__ __forceinline__ void set_oct(bfv<K>& v, int i, bf16x8 o) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[8 * i + e] = o[e];
+}
+
+template <int R, int Q, int NW, bool FULL>
+__global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
+    constexpr int NTH = 64 * NW;
     constexpr int QR = Q * R;
     constexpr int NB = QR / 16;          // 16-row blocks of the chunk
-    constexpr int XS = QR + 8;           // row stride (elements) of sXT
+    constexpr int XS = QR + 8;           // row stride (elements) of sXT / sXsT
     constexpr int BS = N + 8;            // row stride of sBt and sST
-    static_assert(QR % 32 == 0 && Q <= 64, "tiling");
+    constexpr int RT = N / (16 * NW);    // 16-row state tiles per wave
+    constexpr int KS = QR / 32;          // k-steps of the state contraction
+    constexpr int BPT = (QR * (N / 8)) / NTH;              // 16-byte units of Bt per thread
+    constexpr int RB = (QR * 8 / NTH) < 1 ? 1 : (QR * 8 / NTH);   // X staging unit: RB rows x 8 columns
+    constexpr int XU = (QR / RB) * 8;    // X staging units per chunk (<= NTH)
+    constexpr int MB = (NB + NW - 1) / NW;                 // row blocks per wave
+    constexpr bool AF_EARLY = (QR <= 128);                 // prefetch Bt^T fragments a chunk ahead
+    static_assert(RT >= 1 && QR % 32 == 0 && Q <= 64 && XU <= NTH && (QR * (N / 8)) % NTH == 0 && BPT >= 1 &&
+                      (RB == 1 || RB == 2 || RB == 4),
+                  "tiling");
 
-    __shared__ __align__(16) uint16_t sXT[P * XS];                 // X^T: [p][token*R + r]
+    __shared__ __align__(16) uint16_t sXsT[P * XS];                // (s_j X_j)^T: [p][token*R + r]
+    __shared__ __align__(16) uint16_t sXT[FULL ? P * XS : 8];      // X^T
     __shared__ __align__(16) uint16_t sBt[FULL ? QR * BS : 8];     // Bt token-major
     __shared__ __align__(16) uint16_t sST[FULL ? P * BS : 8];      // S^T (bf16): [p][n]
-    __shared__ float sCum[Q], sEc[Q], sSc[Q], sW[Q], sGam[Q];
-    __shared__ float sCs[KP * 2];
-    __shared__ float sDec[1];
+    __shared__ float sCum[2][Q], sEc[2][Q], sSc[2][Q], sW[2][Q], sGam[2][Q];   // by chunk parity
+    __shared__ float sCs[2][KP * 2];
+    __shared__ float sDec[2];
 
     const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int g = h / (p.H / p.G);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
+    const int n0 = 16 * RT * w;                  // first state row owned by this wave
     const PrepLayout lay{QR};
     const float Ah = p.A[h], Dh = p.D[h];
     const int c_begin = seg * p.chunks_per_seg;
     const int c_end = min(p.nchunks, c_begin + p.chunks_per_seg);
     const bool last_seg = (seg == p.nseg - 1);
+    const size_t gbase = (static_cast<size_t>(b) * p.G + g) * p.nchunks;
+    const int xrb = tid % (QR / RB), xpo = tid / (QR / RB);   // X unit: rows RB*xrb.., columns 8*xpo..
 
-    // ---- state accumulators: wave w, row tiles rt (n = 32w + 16rt + 4lg + i), col tiles ct (p = 16ct + l16)
-    f32x4 sacc[2][4];
+    // ---- state accumulators: rows n = n0 + 16rt + 4lg + i, columns p = 16ct + l16
+    f32x4 sacc[RT][4];
     if (FULL) {
         const float c1 = (p.L > 0 && p.bl_in && p.xl_in)
                              ? (1.f - p.lam[(static_cast<int64_t>(b) * p.L) * p.H + h]) *
                                    p.dt[(static_cast<int64_t>(b) * p.L) * p.H + h]
                              : 0.f;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int n = 32 * w + 16 * rt + 4 * lg + i, col = 16 * ct + l16;
-                    float v;
-                    if (p.s_init)
-                        v = p.s_init[((static_cast<size_t>(b) * p.H + h) * p.nseg + seg) * N * P + n * P + col];
-                    else
-                        v = initial_state<R>(p, b, h, g, n, col, c1);
-                    sacc[rt][ct][i] = v;
+                    const int n = n0 + 16 * rt + 4 * lg + i, col = 16 * ct + l16;
+                    sacc[rt][ct][i] =
+                        p.s_init ? p.s_init[((static_cast<size_t>(b) * p.H + h) * p.nseg + seg) * N * P + n * P + col]
+                                 : initial_state<R>(p, b, h, g, n, col, c1);
                 }
     } else {
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) sacc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    if (FULL) {
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-                bf16x4 v = {to_bf(sacc[rt][ct][0]), to_bf(sacc[rt][ct][1]), to_bf(sacc[rt][ct][2]),
-                            to_bf(sacc[rt][ct][3])};
-                *reinterpret_cast<bf16x4*>(&sST[(16 * ct + l16) * BS + 32 * w + 16 * rt + 4 * lg]) = v;
-            }
+
+    // ---- registers holding the next chunk's inputs (raw loads; validity applied by the consumer)
+    u32v<4 * RB> xr;            // X rows RB*xrb + e, columns 8*xpo .. +7
+    u32v<4 * BPT> br;           // Bt units tid + NTH*e
+    float pd0 = 0.f, pl0 = 0.f, pd1 = 0.f, pl1 = 0.f, pcs = 0.f;
+    int pnq = 0;                // valid tokens of the prefetched chunk
+    bfv<32> cf;                 // Ct fragments (4 k-steps) of the wave's current row block
+    bfv<8 * KS * RT> af;        // Bt^T fragments of this wave's state rows
+
+#define M3_FETCH(c_)                                                                                          \
+    do {                                                                                                      \
+        const int64_t t0f = static_cast<int64_t>(c_) * Q;                                                     \
+        const int nqf = static_cast<int>(p.L - t0f < Q ? p.L - t0f : Q);                                      \
+        pnq = nqf;                                                                                            \
+        if (XU == NTH || tid < XU) {                                                                          \
+            _Pragma("unroll") for (int e = 0; e < RB; ++e) {                                                  \
+                const int row = RB * xrb + e;                                                                 \
+                const int i = row / R, r = row - i * R;                                                       \
+                const int ic = i < nqf ? i : nqf - 1;                                                         \
+                set_quad(xr, e,                                                                               \
+                         *reinterpret_cast<const uint4*>(p.x + (((b * p.L + t0f + ic) * p.H + h) * R + r) *   \
+                                                                   static_cast<size_t>(P) + 8 * xpo));        \
+            }                                                                                                 \
+        }                                                                                                     \
+        if (FULL) {                                                                                           \
+            const uint16_t* gBt = reinterpret_cast<const uint16_t*>(p.prep + (gbase + (c_)) * lay.bytes() +   \
+                                                                    lay.bt());                                \
+            _Pragma("unroll") for (int e = 0; e < BPT; ++e)                                                   \
+                set_quad(br, e, *reinterpret_cast<const uint4*>(gBt + static_cast<size_t>(tid + NTH * e) * 8)); \
+        }                                                                                                     \
+        if (w == 0) {                                                                                         \
+            const int64_t tf = t0f + (lane < nqf ? lane : nqf - 1);                                           \
+            const int64_t tf1 = (tf + 1 < p.L) ? tf + 1 : tf;                                                 \
+            pd0 = p.dt[(b * p.L + tf) * p.H + h];                                                             \
+            pl0 = p.lam[(b * p.L + tf) * p.H + h];                                                            \
+            pd1 = p.dt[(b * p.L + tf1) * p.H + h];                                                            \
+            pl1 = p.lam[(b * p.L + tf1) * p.H + h];                                                           \
+        }                                                                                                     \
+        if (tid < 2 * KP) pcs = reinterpret_cast<const float*>(p.prep + (gbase + (c_)) * lay.bytes() + lay.cs())[tid]; \
+    } while (0)
+
+#define M3_LOAD_CF(c_, a_)                                                                                    \
+    do {                                                                                                      \
+        const uint16_t* gCt = reinterpret_cast<const uint16_t*>(p.prep + (gbase + (c_)) * lay.bytes() + lay.ct()); \
+        _Pragma("unroll") for (int ks = 0; ks < 4; ++ks)                                                      \
+            set_oct(cf, ks, *reinterpret_cast<const bf16x8*>(gCt + static_cast<size_t>(16 * (a_) + l16) * N + 32 * ks + 8 * lg)); \
+    } while (0)
+
+#define M3_LOAD_AF(c_)                                                                                        \
+    do {                                                                                                      \
+        const uint16_t* gBtT = reinterpret_cast<const uint16_t*>(p.prep + (gbase + (c_)) * lay.bytes() + lay.btT()); \
+        _Pragma("unroll") for (int ks = 0; ks < KS; ++ks)                                                     \
+            _Pragma("unroll") for (int rt = 0; rt < RT; ++rt)                                                 \
+                set_oct(af, ks * RT + rt,                                                                     \
+                        *reinterpret_cast<const bf16x8*>(gBtT + static_cast<size_t>(n0 + 16 * rt + l16) * QR + 32 * ks + 8 * lg)); \
+    } while (0)
+
+    // Per-token scalars (wave 0, lane = token) of the prefetched chunk into parity slot q_.
+#define M3_STAGE_SCALARS(q_)                                                                                  \
+    do {                                                                                                      \
+        if (w == 0) {                                                                                         \
+            const bool valid = lane < pnq;                                                                    \
+            const int64_t tl = static_cast<int64_t>(0);                                                       \
+            (void)tl;                                                                                         \
+            const float dtv = valid ? pd0 : 0.f, lv = valid ? pl0 : 0.f;                                      \
+            const bool has1 = valid && (nextpos + lane + 1 < p.L);                                            \
+            const float a = dtv * Ah;                                                                         \
+            const float gm = lv * dtv;                                                                        \
+            const float wv = gm + (has1 ? (1.f - pl1) * pd1 : 0.f);                                           \
+            float cum = a;                                                                                    \
+            _Pragma("unroll") for (int off = 1; off < 64; off <<= 1) {                                        \
+                const float o = __shfl_up(cum, off);                                                          \
+                if (lane >= off) cum += o;                                                                    \
+            }                                                                                                 \
+            const float cend = __shfl(cum, Q - 1);                                                            \
+            if (lane < Q) {                                                                                   \
+                sCum[q_][lane] = cum;                                                                         \
+                sEc[q_][lane] = __expf(cum);                                                                  \
+                sSc[q_][lane] = __expf(cend - cum) * wv;                                                      \
+                sW[q_][lane] = wv;                                                                            \
+                sGam[q_][lane] = gm;                                                                          \
+            }                                                                                                 \
+            if (lane == 0) sDec[q_] = cend;                                                                   \
+        }                                                                                                     \
+        if (tid < 2 * KP) sCs[q_][tid] = pcs;                                                                 \
+    } while (0)
+
+    // X^T and (s X)^T (small transposes in registers) and Bt into LDS.
+#define M3_STAGE_TILES(q_)                                                                                    \
+    do {                                                                                                      \
+        if (XU == NTH || tid < XU) {                                                                          \
+            float sc[RB];                                                                                     \
+            uint4 xq[RB];                                                                                     \
+            _Pragma("unroll") for (int e = 0; e < RB; ++e) {                                                  \
+                const int tok = (RB * xrb + e) / R;                                                           \
+                sc[e] = sSc[q_][tok];                                                                         \
+                xq[e] = (tok < pnq) ? quad(xr, e) : uint4{0u, 0u, 0u, 0u};                                    \
+            }                                                                                                 \
+            _Pragma("unroll") for (int pp = 0; pp < 8; ++pp) {                                                \
+                uint16_t v[RB];                                                                               \
+                _Pragma("unroll") for (int e = 0; e < RB; ++e) {                                              \
+                    const uint32_t wv = (pp < 2) ? xq[e].x : (pp < 4) ? xq[e].y : (pp < 6) ? xq[e].z : xq[e].w; \
+                    v[e] = (pp & 1) ? static_cast<uint16_t>(wv >> 16) : static_cast<uint16_t>(wv & 0xffff);   \
+                }                                                                                             \
+                const int off = (8 * xpo + pp) * XS + RB * xrb;                                               \
+                if constexpr (RB == 1) {                                                                      \
+                    if (FULL) sXT[off] = v[0];                                                                \
+                    sXsT[off] = static_cast<uint16_t>(pack_bf16x2(bits_to_f(v[0]) * sc[0], 0.f) & 0xffff);    \
+                } else {                                                                                      \
+                    uint32_t raw[RB / 2], scl[RB / 2];                                                        \
+                    _Pragma("unroll") for (int e = 0; e < RB / 2; ++e) {                                      \
+                        raw[e] = v[2 * e] | (static_cast<uint32_t>(v[2 * e + 1]) << 16);                      \
+                        scl[e] = pack_bf16x2(bits_to_f(v[2 * e]) * sc[2 * e], bits_to_f(v[2 * e + 1]) * sc[2 * e + 1]); \
+                    }                                                                                         \
+                    if constexpr (RB == 2) {                                                                  \
+                        if (FULL) *reinterpret_cast<uint32_t*>(&sXT[off]) = raw[0];                           \
+                        *reinterpret_cast<uint32_t*>(&sXsT[off]) = scl[0];                                    \
+                    } else {                                                                                  \
+                        if (FULL) *reinterpret_cast<uint2*>(&sXT[off]) = uint2{raw[0], raw[1]};               \
+                        *reinterpret_cast<uint2*>(&sXsT[off]) = uint2{scl[0], scl[1]};                        \
+                    }                                                                                         \
+                }                                                                                             \
+            }                                                                                                 \
+        }                                                                                                     \
+        if (FULL) {                                                                                           \
+            _Pragma("unroll") for (int e = 0; e < BPT; ++e) {                                                 \
+                const int u = tid + NTH * e;                                                                  \
+                *reinterpret_cast<uint4*>(&sBt[(u >> 4) * BS + 8 * (u & 15)]) = quad(br, e);                  \
+            }                                                                                                 \
+        }                                                                                                     \
+    } while (0)
+
+#define M3_WRITE_SST()                                                                                        \
+    do {                                                                                                      \
+        _Pragma("unroll") for (int rt = 0; rt < RT; ++rt)                                                     \
+            _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) {                                                \
+                const uint2 v = {pack_bf16x2(sacc[rt][ct][0], sacc[rt][ct][1]),                               \
+                                 pack_bf16x2(sacc[rt][ct][2], sacc[rt][ct][3])};                              \
+                *reinterpret_cast<uint2*>(&sST[(16 * ct + l16) * BS + n0 + 16 * rt + 4 * lg]) = v;            \
+            }                                                                                                 \
+    } while (0)
+
+    auto row_block = [&](int m) { return (m & 1) ? ((m + 1) * NW - 1 - w) : (m * NW + w); };  // snake order
+    int64_t nextpos = 0;          // first token of the prefetched chunk
+
+    // ---- prologue: chunk c_begin into LDS, chunk c_begin+1 into registers
+    if (c_begin < c_end) {
+        M3_FETCH(c_begin);
+        nextpos = static_cast<int64_t>(c_begin) * Q;
+        M3_STAGE_SCALARS(c_begin & 1);
+        __syncthreads();
+        M3_STAGE_TILES(c_begin & 1);
+        if (FULL && row_block(0) < NB) M3_LOAD_CF(c_begin, row_block(0));
+        if (!FULL || AF_EARLY) M3_LOAD_AF(c_begin);
+        if (c_begin + 1 < c_end) {
+            M3_FETCH(c_begin + 1);
+            nextpos = static_cast<int64_t>(c_begin + 1) * Q;
+        }
     }
+    if (FULL) M3_WRITE_SST();
+    __syncthreads();
+
     float dec_total = 0.f;                 // state-only: sum of chunk log-decays
     float rot_c = 1.f, rot_s = 0.f;        // state-only: total rotation of pair tid (tid < KP)
 
     for (int c = c_begin; c < c_end; ++c) {
+        const int q = c & 1;
         const int64_t t0 = static_cast<int64_t>(c) * Q;
         const int nq = static_cast<int>(p.L - t0 < Q ? p.L - t0 : Q);
-        const uint8_t* pbase = p.prep + ((static_cast<size_t>(b) * p.G + g) * p.nchunks + c) * lay.bytes();
-        const uint16_t* gBt = reinterpret_cast<const uint16_t*>(pbase + lay.bt());
-        const uint16_t* gCt = reinterpret_cast<const uint16_t*>(pbase + lay.ct());
-        const uint16_t* gBtT = reinterpret_cast<const uint16_t*>(pbase + lay.btT());
-        const float* gCs = reinterpret_cast<const float*>(pbase + lay.cs());
+        const bool has_next = c + 1 < c_end;
 
-        // (1) per-token scalars, one wave, lane = token
-        if (w == 0) {
-            const int i = lane;
-            float a = 0.f, gm = 0.f, wv = 0.f;
-            if (i < nq) {
-                const int64_t t = t0 + i;
-                const float dtv = p.dt[(b * p.L + t) * p.H + h], lv = p.lam[(b * p.L + t) * p.H + h];
-                a = dtv * Ah;
-                gm = lv * dtv;
-                wv = gm;
-                if (t + 1 < p.L)
-                    wv += (1.f - p.lam[(b * p.L + t + 1) * p.H + h]) * p.dt[(b * p.L + t + 1) * p.H + h];
-            }
-            float cum = a;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_up(cum, off);
-                if (lane >= off) cum += o;
-            }
-            const float cend = __shfl(cum, Q - 1);
-            if (i < Q) {
-                sCum[i] = cum;
-                sEc[i] = __expf(cum);
-                sSc[i] = __expf(cend - cum) * wv;
-                sW[i] = wv;
-                sGam[i] = gm;
-            }
-            if (lane == 0) sDec[0] = cend;
-        }
-        if (tid < 2 * KP) sCs[tid] = gCs[tid];
-
-        // (2) X^T into LDS: 8x8 blocks (8 token-rank rows x 8 columns), transposed in registers
-        for (int blk = tid; blk < QR; blk += NT) {
-            const int rb = blk >> 3, po = blk & 7;
-            uint16_t v[8][8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int row = 8 * rb + e;
-                const int i = row / R, r = row - i * R;
-                uint4 q = {0u, 0u, 0u, 0u};
-                if (i < nq)
-                    q = *reinterpret_cast<const uint4*>(
-                        p.x + (((b * p.L + t0 + i) * p.H + h) * R + r) * static_cast<size_t>(P) + 8 * po);
-                v[e][0] = q.x & 0xffff; v[e][1] = q.x >> 16;
-                v[e][2] = q.y & 0xffff; v[e][3] = q.y >> 16;
-                v[e][4] = q.z & 0xffff; v[e][5] = q.z >> 16;
-                v[e][6] = q.w & 0xffff; v[e][7] = q.w >> 16;
-            }
-#pragma unroll
-            for (int pp = 0; pp < 8; ++pp) {
-                uint4 o;
-                o.x = v[0][pp] | (static_cast<uint32_t>(v[1][pp]) << 16);
-                o.y = v[2][pp] | (static_cast<uint32_t>(v[3][pp]) << 16);
-                o.z = v[4][pp] | (static_cast<uint32_t>(v[5][pp]) << 16);
-                o.w = v[6][pp] | (static_cast<uint32_t>(v[7][pp]) << 16);
-                *reinterpret_cast<uint4*>(&sXT[(8 * po + pp) * XS + 8 * rb]) = o;
-            }
-        }
-        // (3) Bt token-major into LDS
         if (FULL) {
-            for (int idx = tid; idx < QR * (N / 8); idx += NT) {
-                const int row = idx / (N / 8), c8 = idx - row * (N / 8);
-                *reinterpret_cast<uint4*>(&sBt[row * BS + 8 * c8]) =
-                    *reinterpret_cast<const uint4*>(gBt + static_cast<size_t>(row) * N + 8 * c8);
-            }
-        }
-        __syncthreads();
-
-        // (4) outputs
-        if (FULL) {
-            for (int a = w; a < NB; a += 4) {
-                bf16x8 cf[4];
+            // (4) outputs, row blocks in snake order across the waves (balances the causal work)
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    cf[ks] = *reinterpret_cast<const bf16x8*>(gCt + static_cast<size_t>(16 * a + l16) * N + 32 * ks + 8 * lg);
+            for (int m = 0; m < MB; ++m) {
+                const int a = row_block(m);
+                if (a >= NB) continue;
+                if (m > 0) M3_LOAD_CF(c, a);
                 f32x4 yacc[4];
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
                     yacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks)
-                        yacc[ct] = mfma_k32(cf[ks], *reinterpret_cast<const bf16x8*>(&sST[(16 * ct + l16) * BS + 32 * ks + 8 * lg]),
+                        yacc[ct] = mfma_k32(oct(cf, ks), *reinterpret_cast<const bf16x8*>(&sST[(16 * ct + l16) * BS + 32 * ks + 8 * lg]),
                                             yacc[ct]);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float ec = sEc[(16 * a + 4 * lg + i) / R];
+                    const float ec = sEc[q][(16 * a + 4 * lg + i) / R];
 #pragma unroll
                     for (int ct = 0; ct < 4; ++ct) yacc[ct][i] *= ec;
                 }
                 const int ti = (16 * a + l16) / R;
-                const float cum_i = sCum[ti], gam_i = sGam[ti];
+                const float cum_i = sCum[q][ti], gam_i = sGam[q][ti];
+                auto mask = [&](int tj) {        // branch-free: every lane evaluates the exp
+                    const float ex = __expf(fminf(cum_i - sCum[q][tj], 0.f)) * sW[q][tj];
+                    return (tj < ti) ? ex : ((tj == ti) ? gam_i : 0.f);
+                };
                 for (int bb = 0; bb <= a; ++bb) {
                     f32x4 gt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks)
-                        gt = mfma_k32(*reinterpret_cast<const bf16x8*>(&sBt[(16 * bb + l16) * BS + 32 * ks + 8 * lg]), cf[ks], gt);
+                        gt = mfma_k32(*reinterpret_cast<const bf16x8*>(&sBt[(16 * bb + l16) * BS + 32 * ks + 8 * lg]), oct(cf, ks), gt);
                     // gt[e] = (Ct Bt^T)[i = 16a + l16][j = 16bb + 4lg + e]
-                    s16x4 mf;
+                    float mv[4];
+                    if (R == 4) {
+                        const float m0 = mask(4 * bb + lg);
+                        mv[0] = mv[1] = mv[2] = mv[3] = m0;
+                    } else if (R == 2) {
+                        const float m0 = mask(8 * bb + 2 * lg), m1 = mask(8 * bb + 2 * lg + 1);
+                        mv[0] = mv[1] = m0;
+                        mv[2] = mv[3] = m1;
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int tj = (16 * bb + 4 * lg + e) / R;
-                        const float m = (tj < ti) ? __expf(cum_i - sCum[tj]) * sW[tj] : ((tj == ti) ? gam_i : 0.f);
-                        mf[e] = static_cast<short>(f32_to_bf16(m * gt[e]));
+                        for (int e = 0; e < 4; ++e) mv[e] = mask((16 * bb + 4 * lg + e) / R);
                     }
+                    const uint2 mp = {pack_bf16x2(mv[0] * gt[0], mv[1] * gt[1]), pack_bf16x2(mv[2] * gt[2], mv[3] * gt[3])};
+                    const s16x4 mf = __builtin_bit_cast(s16x4, mp);
 #pragma unroll
                     for (int ct = 0; ct < 4; ++ct)
                         yacc[ct] = mfma_k16(mf, *reinterpret_cast<const s16x4*>(&sXT[(16 * ct + l16) * XS + 16 * bb + 4 * lg]),
                                             yacc[ct]);
                 }
-                // skip term and store (rows 16a + 4lg + i, column 16ct + l16)
+                // next chunk's Ct for the first row block: cf is dead once the last block is done
+                if (m == MB - 1 || row_block(m + 1) >= NB) {
+                    if (has_next && row_block(0) < NB) M3_LOAD_CF(c + 1, row_block(0));
+                }
+                // skip term, then store column pairs: lanes 2j and 2j+1 swap halves so
+                // each writes two rows of two adjacent columns as 4-byte words
+                const bool odd = l16 & 1;
+                const int rbase = 16 * a + 4 * lg + (odd ? 2 : 0);
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
                     const s16x4 xv = *reinterpret_cast<const s16x4*>(&sXT[(16 * ct + l16) * XS + 16 * a + 4 * lg]);
+                    float v[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int row = 16 * a + 4 * lg + i;
-                        const int ti2 = row / R, r = row - ti2 * R;
-                        if (ti2 < nq) {
-                            const float yv = yacc[ct][i] + Dh * bits_to_f(static_cast<uint16_t>(xv[i]));
-                            p.y[(((b * p.L + t0 + ti2) * p.H + h) * R + r) * static_cast<size_t>(P) + 16 * ct + l16] =
-                                f32_to_bf16(yv);
-                        }
+                    for (int i = 0; i < 4; ++i) v[i] = yacc[ct][i] + Dh * bits_to_f(static_cast<uint16_t>(xv[i]));
+                    const float r0 = swap_adjacent(odd ? v[0] : v[2]);
+                    const float r1 = swap_adjacent(odd ? v[1] : v[3]);
+                    const uint32_t w0 = odd ? pack_bf16x2(r0, v[2]) : pack_bf16x2(v[0], r0);
+                    const uint32_t w1 = odd ? pack_bf16x2(r1, v[3]) : pack_bf16x2(v[1], r1);
+                    const int col = 16 * ct + (l16 & ~1);
+#pragma unroll
+                    for (int qq = 0; qq < 2; ++qq) {
+                        const int row = rbase + qq;
+                        const int tk = row / R, r = row - tk * R;
+                        if (tk < nq)
+                            *reinterpret_cast<uint32_t*>(
+                                p.y + (((b * p.L + t0 + tk) * p.H + h) * R + r) * static_cast<size_t>(P) + col) = qq ? w1 : w0;
                     }
                 }
             }
-            __syncthreads();   // every wave is done reading sST (S_{c-1})
+            if (!AF_EARLY) M3_LOAD_AF(c);
         }
+        if (has_next) M3_STAGE_SCALARS(q ^ 1);   // the other parity slot: nobody reads it now
+        __syncthreads();   // S_{c-1} no longer read; next chunk's scalars visible
 
-        // (5) state update: S <- R(phi_end) [e^{cum_end} S + Bt^T diag(s) X]
+        // (5) state update: S <- R(phi_end) [e^{cum_end} S + Bt^T (s X)]
         {
-            const float cend = sDec[0];
+            const float cend = sDec[q];
             const float decay = __expf(cend);
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) sacc[rt][ct] *= decay;
 #pragma unroll
-            for (int ks = 0; ks < QR / 32; ++ks) {
-                bf16x8 af[2];
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    const bf16x8 raw = *reinterpret_cast<const bf16x8*>(
-                        gBtT + static_cast<size_t>(32 * w + 16 * rt + l16) * QR + 32 * ks + 8 * lg);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) af[rt][e] = to_bf(from_bf(raw[e]) * sSc[(32 * ks + 8 * lg + e) / R]);
-                }
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
-                    const bf16x8 bx = *reinterpret_cast<const bf16x8*>(&sXT[(16 * ct + l16) * XS + 32 * ks + 8 * lg]);
+                    const bf16x8 bx = *reinterpret_cast<const bf16x8*>(&sXsT[(16 * ct + l16) * XS + 32 * ks + 8 * lg]);
 #pragma unroll
-                    for (int rt = 0; rt < 2; ++rt) sacc[rt][ct] = mfma_k32(af[rt], bx, sacc[rt][ct]);
+                    for (int rt = 0; rt < RT; ++rt) sacc[rt][ct] = mfma_k32(oct(af, ks * RT + rt), bx, sacc[rt][ct]);
                 }
-            }
+            if ((!FULL || AF_EARLY) && has_next) M3_LOAD_AF(c + 1);
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int i = 0; i < 4; i += 2) {
-                    const int k = (32 * w + 16 * rt + 4 * lg + i) >> 1;
-                    const float cn = sCs[2 * k], sn = sCs[2 * k + 1];
+                    const int k = (n0 + 16 * rt + 4 * lg + i) >> 1;
+                    const float cn = sCs[q][2 * k], sn = sCs[q][2 * k + 1];
 #pragma unroll
                     for (int ct = 0; ct < 4; ++ct) {
                         const float s0 = sacc[rt][ct][i], s1 = sacc[rt][ct][i + 1];
@@ -439,49 +586,56 @@ __global__ __launch_bounds__(NT) void scan_mfma(ScanParams p) {
                     }
                 }
             if (FULL) {
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                    for (int ct = 0; ct < 4; ++ct) {
-                        bf16x4 v = {to_bf(sacc[rt][ct][0]), to_bf(sacc[rt][ct][1]), to_bf(sacc[rt][ct][2]),
-                                    to_bf(sacc[rt][ct][3])};
-                        *reinterpret_cast<bf16x4*>(&sST[(16 * ct + l16) * BS + 32 * w + 16 * rt + 4 * lg]) = v;
-                    }
+                M3_WRITE_SST();
             } else {
                 dec_total += cend;
                 if (tid < KP) {
-                    const float cn = sCs[2 * tid], sn = sCs[2 * tid + 1];
+                    const float cn = sCs[q][2 * tid], sn = sCs[q][2 * tid + 1];
                     const float nc = cn * rot_c - sn * rot_s, ns = sn * rot_c + cn * rot_s;
                     rot_c = nc;
                     rot_s = ns;
                 }
             }
         }
-        __syncthreads();   // sXT / sST / scalars free for the next chunk
+        if (has_next) {
+            __syncthreads();   // the chunk's X / Bt tiles are no longer read
+            M3_STAGE_TILES(q ^ 1);
+            if (c + 2 < c_end) {
+                M3_FETCH(c + 2);
+                nextpos = static_cast<int64_t>(c + 2) * Q;
+            }
+        }
+        __syncthreads();
     }
+#undef M3_FETCH
+#undef M3_LOAD_CF
+#undef M3_LOAD_AF
+#undef M3_STAGE_SCALARS
+#undef M3_STAGE_TILES
+#undef M3_WRITE_SST
 
     // epilogue
     if (FULL) {
         if (last_seg && p.h_out) {
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int n = 32 * w + 16 * rt + 4 * lg + i, col = 16 * ct + l16;
+                        const int n = n0 + 16 * rt + 4 * lg + i, col = 16 * ct + l16;
                         p.h_out[(static_cast<size_t>(b) * p.H + h) * N * P + n * P + col] = sacc[rt][ct][i];
                     }
         }
     } else {
         const size_t sidx = (static_cast<size_t>(b) * p.H + h) * (p.nseg - 1) + seg;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int n = 32 * w + 16 * rt + 4 * lg + i, col = 16 * ct + l16;
+                    const int n = n0 + 16 * rt + 4 * lg + i, col = 16 * ct + l16;
                     p.seg_state[sidx * N * P + n * P + col] = sacc[rt][ct][i];
                 }
         if (tid == 0) p.seg_decay[sidx] = dec_total;
@@ -585,6 +739,7 @@ void plan_mfma(const PrefillArgs& a, PrefillPlan* plan) {
 
 template <int R, int Q>
 static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, hipStream_t st) {
+    constexpr int NW = (Q * R >= 128) ? 8 : 4;   // waves per workgroup
     const int nchunks = static_cast<int>((a.L + a.Q - 1) / a.Q);
     if (nchunks == 0) return hipSuccess;
     const int nseg = plan.nseg;
@@ -620,8 +775,8 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
         p.seg_state = reinterpret_cast<float*>(base + ws.seg_state);
         p.seg_decay = reinterpret_cast<float*>(base + ws.seg_decay);
         p.seg_rot = reinterpret_cast<float*>(base + ws.seg_rot);
-        hipLaunchKernelGGL((mf::scan_mfma<R, Q, false>), dim3(nseg - 1, a.H, static_cast<unsigned>(a.batch)),
-                           dim3(mf::NT), 0, st, p);
+        hipLaunchKernelGGL((mf::scan_mfma<R, Q, NW, false>), dim3(nseg - 1, a.H, static_cast<unsigned>(a.batch)),
+                           dim3(64 * NW), 0, st, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         float* s_init = reinterpret_cast<float*>(base + ws.s_init);
         hipLaunchKernelGGL((mf::seg_pass<R>), dim3(static_cast<unsigned>(a.batch * a.H)), dim3(mf::NT), 0, st, p,
@@ -629,8 +784,8 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
         if ((e = hipGetLastError()) != hipSuccess) return e;
         p.s_init = s_init;
     }
-    hipLaunchKernelGGL((mf::scan_mfma<R, Q, true>), dim3(nseg, a.H, static_cast<unsigned>(a.batch)), dim3(mf::NT),
-                       0, st, p);
+    hipLaunchKernelGGL((mf::scan_mfma<R, Q, NW, true>), dim3(nseg, a.H, static_cast<unsigned>(a.batch)),
+                       dim3(64 * NW), 0, st, p);
     return hipGetLastError();
 }
 
