@@ -8,10 +8,11 @@
 // rotation of "Solution 2" and the rank-R input/read-out of "Solution 3").
 //
 // The step reads and writes the whole fp32 state and does little arithmetic per
-// byte: it is bound by HBM bandwidth.  The fast kernel streams each (b, h) state
-// slice once with 16-byte non-temporal loads and stores, keeps every rotation
-// pair (2k, 2k+1) inside one thread, and reduces the R x P read-out across the
-// threads that share a column block with cross-lane shuffles and one LDS pass.
+// byte: it is bound by HBM bandwidth.  The kernels stream each (b, h) state slice
+// once with 16-byte non-temporal loads and stores and keep every rotation pair
+// (2k, 2k+1) inside one thread.  decode_stream (N = 128, P = 64) keeps the R x P
+// read-out reduction inside each wave; decode_fast (small N) reduces across
+// waves through LDS; decode_generic handles any other shape.
 #include "m3_common.h"
 #include "m3_internal.h"
 
@@ -43,9 +44,46 @@ __global__ __launch_bounds__(NT) void decode_fast(
     const int c = tid % PC;
     const int kk = tid / PC;
 
-    float* hp = h + static_cast<size_t>(bh) * N * P;
+    __shared__ float sB[R][N], sC[R][N], sBp[R][N];
+    __shared__ __align__(16) float sX[R][P];
+    __shared__ __align__(16) float sXp[R][P];
+    __shared__ float sCs[KP], sSn[KP];
 
-    // Issue the state loads first: they are the only HBM-sized traffic.
+    // The small per-token operands are loaded into registers first and written to
+    // LDS after the state loads have been issued: their staging then overlaps the
+    // state stream instead of delaying it.
+    constexpr int SPT = (R * N + NT - 1) / NT;
+    constexpr int XPT = (R * P + NT - 1) / NT;
+    constexpr int KPT = (KP + NT - 1) / NT;
+    const size_t gofs = (static_cast<size_t>(b) * G + g) * R * N;
+    const size_t hofs = static_cast<size_t>(bh) * R * P;
+    float vb[SPT], vc[SPT], vbp[SPT], vx[XPT], vxp[XPT], vth[KPT];
+#pragma unroll
+    for (int e = 0; e < SPT; ++e) {
+        const int i = tid + NT * e;
+        vb[e] = vc[e] = vbp[e] = 0.f;
+        if (i < R * N) {
+            vb[e] = io<T>::load(B_t + gofs + i);
+            vc[e] = io<T>::load(C_t + gofs + i);
+            if (has_carry) vbp[e] = io<T>::load(b_last + gofs + i);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < XPT; ++e) {
+        const int i = tid + NT * e;
+        vx[e] = vxp[e] = 0.f;
+        if (i < R * P) {
+            vx[e] = io<T>::load(x_t + hofs + i);
+            if (has_carry) vxp[e] = io<T>::load(x_last + hofs + i);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        const int k = tid + NT * e;
+        vth[e] = (k < KP) ? theta_t[(static_cast<size_t>(b) * G + g) * KP + k] : 0.f;
+    }
+
+    float* hp = h + static_cast<size_t>(bh) * N * P;
     f32x4 s0[PPT], s1[PPT];
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
@@ -54,27 +92,32 @@ __global__ __launch_bounds__(NT) void decode_fast(
         s1[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(hp + (2 * k + 1) * P) + c);
     }
 
-    __shared__ float sB[R][N], sC[R][N], sBp[R][N];
-    __shared__ __align__(16) float sX[R][P];
-    __shared__ __align__(16) float sXp[R][P];
-    __shared__ float sCs[KP], sSn[KP];
-
-    const size_t gofs = (static_cast<size_t>(b) * G + g) * R * N;
-    const size_t hofs = static_cast<size_t>(bh) * R * P;
-    for (int i = tid; i < R * N; i += NT) {
-        (&sB[0][0])[i] = io<T>::load(B_t + gofs + i);
-        (&sC[0][0])[i] = io<T>::load(C_t + gofs + i);
-        (&sBp[0][0])[i] = has_carry ? io<T>::load(b_last + gofs + i) : 0.f;
+#pragma unroll
+    for (int e = 0; e < SPT; ++e) {
+        const int i = tid + NT * e;
+        if (i < R * N) {
+            (&sB[0][0])[i] = vb[e];
+            (&sC[0][0])[i] = vc[e];
+            (&sBp[0][0])[i] = vbp[e];
+        }
     }
-    for (int i = tid; i < R * P; i += NT) {
-        (&sX[0][0])[i] = io<T>::load(x_t + hofs + i);
-        (&sXp[0][0])[i] = has_carry ? io<T>::load(x_last + hofs + i) : 0.f;
+#pragma unroll
+    for (int e = 0; e < XPT; ++e) {
+        const int i = tid + NT * e;
+        if (i < R * P) {
+            (&sX[0][0])[i] = vx[e];
+            (&sXp[0][0])[i] = vxp[e];
+        }
     }
-    for (int k = tid; k < KP; k += NT) {
-        float sn, cs;
-        sincos_acc(theta_t[(static_cast<size_t>(b) * G + g) * KP + k], &sn, &cs);
-        sCs[k] = cs;
-        sSn[k] = sn;
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        const int k = tid + NT * e;
+        if (k < KP) {
+            float sn, cs;
+            sincos_acc(vth[e], &sn, &cs);
+            sCs[k] = cs;
+            sSn[k] = sn;
+        }
     }
     const float dtv = dt_t[bh];
     const float lv = lam_t[bh];
