@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--check-slices", type=int, default=2, help="(b,h) slices checked against the oracle")
+    ap.add_argument("--probe-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy (known bytes) to calibrate HBM counters")
     return ap.parse_args()
 
 
@@ -112,6 +114,13 @@ def main():
     torch.cuda.set_device(dev)
     m3scan.lib()
     stream = torch.cuda.current_stream(dev)
+
+    if args.probe_copy:
+        src = torch.empty(2**28, dtype=torch.float32, device=dev)   # 1 GiB read + 1 GiB written
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     t_gen = time.time()
     d = inputs.draw_config(cfg, device=dev)
