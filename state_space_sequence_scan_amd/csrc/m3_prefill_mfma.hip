@@ -205,6 +205,23 @@ __device__ __forceinline__ float swap_adjacent(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
 }
 
+// Workgroups are dispatched to the 8 XCDs round-robin by linear id, and each
+// XCD has its own L2.  The heads of one (batch, segment) group read the same
+// prepared Bt/Ct, so the linear id is permuted to place a group's heads on one
+// XCD, one after another: the prepared operands are then fetched into one L2
+// instead of eight.  Any id permutation is correct; this one only helps speed.
+__device__ __forceinline__ void xcd_decode(int id, int total, int H, int nseg, int* b, int* h, int* seg) {
+    int v = id;
+    if ((total & 7) == 0) {
+        const int per = total >> 3;
+        v = (id & 7) * per + (id >> 3);
+    }
+    const int grp = v / H;
+    *h = v - grp * H;
+    *b = grp / nseg;
+    *seg = grp - *b * nseg;
+}
+
 // Prefetched data is carried in vector-typed values (never addressable arrays)
 // so that it stays in registers while the loads are in flight.
 template <int K> using u32v = uint32_t __attribute__((ext_vector_type(K)));
@@ -260,7 +277,8 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
     __shared__ float sCs[2][KP * 2];
     __shared__ float sDec[2];
 
-    const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    int seg, h, b;
+    xcd_decode(blockIdx.x, gridDim.x, p.H, FULL ? p.nseg : p.nseg - 1, &b, &h, &seg);
     const int g = h / (p.H / p.G);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
@@ -744,6 +762,7 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
     if (nchunks == 0) return hipSuccess;
     const int nseg = plan.nseg;
     const int cps = (nchunks + nseg - 1) / nseg;
+    if (static_cast<int64_t>(nseg) * a.H * a.batch > 0x7fffffffLL) return hipErrorInvalidValue;
     const MfmaWs ws = mfma_ws(a, nchunks, nseg);
     uint8_t* base = static_cast<uint8_t*>(a.workspace);
 
@@ -775,7 +794,7 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
         p.seg_state = reinterpret_cast<float*>(base + ws.seg_state);
         p.seg_decay = reinterpret_cast<float*>(base + ws.seg_decay);
         p.seg_rot = reinterpret_cast<float*>(base + ws.seg_rot);
-        hipLaunchKernelGGL((mf::scan_mfma<R, Q, NW, false>), dim3(nseg - 1, a.H, static_cast<unsigned>(a.batch)),
+        hipLaunchKernelGGL((mf::scan_mfma<R, Q, NW, false>), dim3(static_cast<unsigned>((nseg - 1) * a.H * a.batch)),
                            dim3(64 * NW), 0, st, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         float* s_init = reinterpret_cast<float*>(base + ws.s_init);
@@ -784,7 +803,7 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
         if ((e = hipGetLastError()) != hipSuccess) return e;
         p.s_init = s_init;
     }
-    hipLaunchKernelGGL((mf::scan_mfma<R, Q, NW, true>), dim3(nseg, a.H, static_cast<unsigned>(a.batch)),
+    hipLaunchKernelGGL((mf::scan_mfma<R, Q, NW, true>), dim3(static_cast<unsigned>(nseg * a.H * a.batch)),
                        dim3(64 * NW), 0, st, p);
     return hipGetLastError();
 }
