@@ -26,6 +26,9 @@ FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
          "-Wall", "-Wno-unused-function",
          # no packed-fp32 instructions in device code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA accumulators in ordinary VGPRs: the scan scales and rotates its
+         # accumulators with vector ALU ops, which cannot read AGPRs directly
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", INCLUDE, "-I", CSRC]
 
 

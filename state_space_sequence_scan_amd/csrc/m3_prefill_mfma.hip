@@ -10,20 +10,27 @@
 //
 //  rope_prep   one workgroup per (b, g, chunk): chunk-local angle prefix sums,
 //              the rotated operands Bt = R(-phi) B and Ct = R(-phi) C in bf16,
-//              token-major ([Q*R][N]) and, for Bt, also n-major ([N][Q*R]), plus
-//              cos/sin of the chunk's total angle.  B, C and theta are shared by
-//              the H/G heads of a group, so this work is done once per group, not
-//              once per head.
-//  scan_mfma   one workgroup (4 waves) per (b, h, segment of chunks).  The N x P
-//              state lives in MFMA accumulators (wave w owns state rows
-//              32w .. 32w+31).  Per chunk:
+//              token-major ([Q*R][N]), and cos/sin of the chunk's total angle
+//              phi_end.  B, C and theta are shared by the H/G heads of a group, so
+//              this work is done once per group, not once per head.
+//  scan_mfma   one workgroup per (b, h, segment of chunks), one wave per 16-row
+//              block of the chunk (at least 4).  The N x P state lives in MFMA
+//              accumulators, split over the waves in 16 x 16 tiles.  Per chunk:
 //                Y      = diag(e^cum) Ct S  +  (M o Ct Bt^T) X  +  D X
-//                S     <- R(phi_end) [ e^{cum_end} S + Bt^T diag(s) X ]
+//                S     <- R(phi_end) [ e^{cum_end} S  +  Bt^T diag(s) X ]
 //              with M the decay/trapezoid mask and s_j = e^{cum_end - cum_j} w_j.
+//              Y is computed transposed (Y^T = S^T Ct^T + X^T (M o G)^T), so a
+//              lane ends up holding four consecutive columns of one output row.
 //              The mask is applied to G^T = Bt Ct^T tiles in registers: the 16x16
 //              accumulator layout of a 16x16x32 MFMA (4 consecutive rows per lane)
-//              is exactly the A-operand layout of a 16x16x16 MFMA, so the masked
+//              is exactly the B-operand layout of a 16x16x16 MFMA, so the masked
 //              tile feeds the next contraction without leaving the registers.
+//              Off the diagonal the decay factors into a row part and a column
+//              part, each at most 1 (see scan_mfma), so those tiles need no
+//              exponentials; D X is two more small contractions (D split into a
+//              bf16 high and low part) so that it is not rounded to bf16.  The
+//              state contraction reads Bt^T straight from the token-major Bt tile
+//              in LDS with the transposing 64-bit LDS read of gfx950.
 //              In state-only mode (segment summaries) only the S update runs.
 //  seg_pass    one workgroup per (b, h): combines the segment summaries into the
 //              state entering each segment (sequential over segments).
@@ -43,6 +50,44 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposing 64-bit LDS read (gfx950): within each group of 16 lanes, lane j
+// receives element (j mod 4) of the 4-element segments addressed by lanes
+// 4e + j/4, e = 0..3.  If lane s of a group addresses row r0 + s/4, columns
+// c0 + 4(s mod 4) .. +3 of a row-major tile, lane j receives column c0 + j of
+// rows r0 .. r0+3: a 4-row slice of the tile, transposed.
+__device__ __forceinline__ s16x4 lds_read_tr4(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)(p)));
+}
+
+// Per-lane LDS byte address held opaque to the optimizer.  The tiles live above
+// 64 KB of LDS, beyond the 16-bit immediate offset of LDS instructions; with the
+// array's absolute address folded into every access the compiler keeps one
+// address register per access pattern (and spills them).  From an opaque base,
+// every access of a tile is base + immediate.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)(p)));
+    asm volatile("" : "+v"(a));
+    return a;
+}
+template <typename T>
+__device__ __forceinline__ T lds_ld(uint32_t a) {
+    return *(__attribute__((address_space(3))) const T*)(static_cast<uintptr_t>(a));
+}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void lds_st(uint32_t a, uint4 v) {
+    *(__attribute__((address_space(3))) u32x4*)(static_cast<uintptr_t>(a)) = u32x4{v.x, v.y, v.z, v.w};
+}
+__device__ __forceinline__ void lds_st(uint32_t a, uint2 v) {
+    *(__attribute__((address_space(3))) u32x2*)(static_cast<uintptr_t>(a)) = u32x2{v.x, v.y};
+}
+__device__ __forceinline__ s16x4 lds_tr4(uint32_t a) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(static_cast<uintptr_t>(a)));
+}
+
 __device__ __forceinline__ f32x4 mfma_k32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -58,8 +103,7 @@ struct PrepLayout {
     int QR;
     __host__ __device__ size_t bt() const { return 0; }                                    // [QR][N] bf16
     __host__ __device__ size_t ct() const { return static_cast<size_t>(QR) * N * 2; }      // [QR][N] bf16
-    __host__ __device__ size_t btT() const { return static_cast<size_t>(QR) * N * 4; }     // [N][QR] bf16
-    __host__ __device__ size_t cs() const { return static_cast<size_t>(QR) * N * 6; }      // [KP][2] fp32
+    __host__ __device__ size_t cs() const { return static_cast<size_t>(QR) * N * 4; }      // [KP][2] fp32
     __host__ __device__ size_t bytes() const { return cs() + KP * 2 * sizeof(float); }
 };
 
@@ -88,7 +132,6 @@ __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
     uint8_t* base = prep + ((static_cast<size_t>(b) * G + g) * nchunks + c) * lay.bytes();
     uint16_t* Bt = reinterpret_cast<uint16_t*>(base + lay.bt());
     uint16_t* Ct = reinterpret_cast<uint16_t*>(base + lay.ct());
-    uint16_t* BtT = reinterpret_cast<uint16_t*>(base + lay.btT());
     float* cs = reinterpret_cast<float*>(base + lay.cs());
 
     // Chunk-local inclusive angle sums: 4 threads per pair, Q/4 tokens each.
@@ -123,11 +166,9 @@ __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
     }
     __syncthreads();
     // One unit = 8 consecutive rows (token, rank) x one rotation pair k:
-    // R(-phi) (x0, x1) = (c x0 + s x1, -s x0 + c x1).  Token-major stores are
-    // 4 bytes per row; the n-major copy is two 16-byte stores (rows 2k, 2k+1).
+    // R(-phi) (x0, x1) = (c x0 + s x1, -s x0 + c x1), stored as 4 bytes per row.
     for (int u = tid; u < (QR / 8) * KP; u += NT) {
         const int r8 = u / KP, k = u - r8 * KP;
-        uint32_t lo[4] = {0u, 0u, 0u, 0u}, hi[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int row = 8 * r8 + e;
@@ -145,19 +186,9 @@ __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
                 c0 = cn * y0 + sn * y1;
                 c1 = -sn * y0 + cn * y1;
             }
-            const uint32_t pb = pack_bf16x2(b0, b1);
-            *reinterpret_cast<uint32_t*>(Bt + static_cast<size_t>(row) * N + 2 * k) = pb;
+            *reinterpret_cast<uint32_t*>(Bt + static_cast<size_t>(row) * N + 2 * k) = pack_bf16x2(b0, b1);
             *reinterpret_cast<uint32_t*>(Ct + static_cast<size_t>(row) * N + 2 * k) = pack_bf16x2(c0, c1);
-            if (e & 1) {
-                lo[e >> 1] |= (pb & 0xffffu) << 16;
-                hi[e >> 1] |= pb & 0xffff0000u;
-            } else {
-                lo[e >> 1] = pb & 0xffffu;
-                hi[e >> 1] = pb >> 16;
-            }
         }
-        *reinterpret_cast<uint4*>(BtT + static_cast<size_t>(2 * k) * QR + 8 * r8) = uint4{lo[0], lo[1], lo[2], lo[3]};
-        *reinterpret_cast<uint4*>(BtT + static_cast<size_t>(2 * k + 1) * QR + 8 * r8) = uint4{hi[0], hi[1], hi[2], hi[3]};
     }
 }
 
@@ -172,6 +203,7 @@ struct ScanParams {
     const float* D;         // (H)
     const uint8_t* prep;    // prepared operands, per (b, g, chunk)
     uint16_t* y;            // (b, L, H, R, P) bf16
+    uint16_t* y_sink;       // 64 x 64 bf16 scratch: stores of rows past the sequence end land here
     const float* s_init;    // state entering segment s: (b, H, nseg, N, P) fp32, or null
     const float* h_in;      // used when s_init is null (nseg == 1): (b, H, N, P), may be null
     const uint16_t* bl_in;  // carry in (b, G, R, N), may be null
@@ -198,6 +230,14 @@ __device__ float initial_state(const ScanParams& p, int b, int h, int g, int n, 
         s += c1 * u;
     }
     return s;
+}
+
+// Element offset of (row, col) in a row-major [rows][P] bf16 LDS tile whose 16-byte
+// chunks are swapped in pairs on odd rows, so that the 4 rows x 32 bytes of a
+// transposing read spread over twice as many banks.  The swap keeps the offset of
+// a 16-column tile linear in the tile index (an immediate in the LDS instruction).
+__device__ __forceinline__ int xoff(int row, int col) {
+    return row * P + (((col >> 3) ^ (row & 1)) << 3) + (col & 7);
 }
 
 // Swap a value with the neighbouring lane (lane ^ 1) through a DPP quad permutation.
@@ -256,43 +296,78 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
     constexpr int NTH = 64 * NW;
     constexpr int QR = Q * R;
     constexpr int NB = QR / 16;          // 16-row blocks of the chunk
-    constexpr int XS = QR + 8;           // row stride (elements) of sXT / sXsT
     constexpr int BS = N + 8;            // row stride of sBt and sST
-    constexpr int RT = N / (16 * NW);    // 16-row state tiles per wave
+    constexpr int MB = NB > NW ? 2 : 1;  // output row blocks per wave
+    constexpr int CT = NW > 8 ? 2 : 4;   // 16-column state tiles per wave
+    constexpr int RT = 32 / (NW * CT);   // 16-row state tiles per wave
+    constexpr int RW = 8 / RT;           // waves covering the N rows of one column range
     constexpr int KS = QR / 32;          // k-steps of the state contraction
     constexpr int BPT = (QR * (N / 8)) / NTH;              // 16-byte units of Bt per thread
-    constexpr int RB = (QR * 8 / NTH) < 1 ? 1 : (QR * 8 / NTH);   // X staging unit: RB rows x 8 columns
-    constexpr int XU = (QR / RB) * 8;    // X staging units per chunk (<= NTH)
-    constexpr int MB = (NB + NW - 1) / NW;                 // row blocks per wave
-    constexpr bool AF_EARLY = (QR <= 128);                 // prefetch Bt^T fragments a chunk ahead
-    static_assert(RT >= 1 && QR % 32 == 0 && Q <= 64 && XU <= NTH && (QR * (N / 8)) % NTH == 0 && BPT >= 1 &&
-                      (RB == 1 || RB == 2 || RB == 4),
+    constexpr int XPT = (QR * (P / 8)) / NTH;              // 16-byte units of X per thread
+    constexpr int VN = (NB * Q + NTH - 1) / NTH;           // column-factor entries per thread
+    static_assert(RT >= 1 && RT * CT * NW == 32 && QR % 32 == 0 && Q <= 64 && (QR * (N / 8)) % NTH == 0 &&
+                      BPT >= 1 && (QR * (P / 8)) % NTH == 0 && XPT >= 1 && (NB <= NW || NB == 2 * NW) &&
+                      NW % 4 == 0,
                   "tiling");
 
-    __shared__ __align__(16) uint16_t sXsT[P * XS];                // (s_j X_j)^T: [p][token*R + r]
-    __shared__ __align__(16) uint16_t sXT[FULL ? P * XS : 8];      // X^T
-    __shared__ __align__(16) uint16_t sBt[FULL ? QR * BS : 8];     // Bt token-major
+    __shared__ __align__(16) uint16_t sXs[QR * P];                 // s_j X_j, row-major, swizzled
+    __shared__ __align__(16) uint16_t sX[FULL ? QR * P : 8];       // X, row-major, swizzled
+    __shared__ __align__(16) uint16_t sBt[QR * BS];                // Bt token-major
     __shared__ __align__(16) uint16_t sST[FULL ? P * BS : 8];      // S^T (bf16): [p][n]
-    __shared__ float sCum[2][Q], sEc[2][Q], sSc[2][Q], sW[2][Q], sGam[2][Q];   // by chunk parity
+    __shared__ __align__(16) float sV[FULL ? NB * Q : 4];          // column factors [row block][token]
+    __shared__ float sCum[2][Q], sSc[2][Q], sW[2][Q], sGam[2][Q];  // by chunk parity
     __shared__ float sCs[2][KP * 2];
     __shared__ float sDec[2];
 
     int seg, h, b;
     xcd_decode(blockIdx.x, gridDim.x, p.H, FULL ? p.nseg : p.nseg - 1, &b, &h, &seg);
     const int g = h / (p.H / p.G);
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
     const int l16 = lane & 15, lg = lane >> 4;
-    const int n0 = 16 * RT * w;                  // first state row owned by this wave
+    const int n0 = 16 * RT * (w % RW);           // first state row owned by this wave
+    const int p0 = 16 * CT * (w / RW);           // first state column owned by this wave
     const PrepLayout lay{QR};
-    const float Ah = p.A[h], Dh = p.D[h];
+    const float Ah = p.A[h];
     const int c_begin = seg * p.chunks_per_seg;
     const int c_end = min(p.nchunks, c_begin + p.chunks_per_seg);
     const bool last_seg = (seg == p.nseg - 1);
     const size_t gbase = (static_cast<size_t>(b) * p.G + g) * p.nchunks;
-    const int xrb = tid % (QR / RB), xpo = tid / (QR / RB);   // X unit: rows RB*xrb.., columns 8*xpo..
+    const uint32_t HRP = static_cast<uint32_t>(p.H) * R * P;   // elements between tokens of x and y
+    // Output row block(s) of this wave (uniform).  Waves w, w+4, .. share a SIMD.  With
+    // one block per wave the order 0..3, 7..4, 8..11, 15..12 gives every SIMD the same
+    // number of causal tiles (block a has a+1); with two, wave w takes blocks w and
+    // 2NW-1-w (a_lo < a_hi), and the B tiles they share are read from LDS once.
+    const int a_lo = (MB == 2) ? w : 4 * (w >> 2) + (((w >> 2) & 1) ? 3 - (w & 3) : (w & 3));
+    const int a_hi = (MB == 2) ? 2 * NW - 1 - w : a_lo;
+    const bool has_rows = a_lo < NB;
+    // per-lane LDS bases (byte addresses); tile accesses add compile-time offsets
+    const uint32_t aBtRow = lds_addr(&sBt[l16 * BS + 8 * lg]);                          // Bt tiles, A operand
+    const uint32_t aBtTr = lds_addr(&sBt[(8 * lg + (l16 >> 2)) * BS + n0 + 4 * (l16 & 3)]);   // Bt^T, transposed
+    const uint32_t aBtW = lds_addr(&sBt[(tid >> 4) * BS + 8 * (tid & 15)]);             // Bt staging
+    const uint32_t aXTr = FULL ? lds_addr(&sX[xoff(4 * lg + (l16 >> 2), 4 * (l16 & 3))]) : 0u;   // X^T, transposed
+    const uint32_t aXsTr = lds_addr(&sXs[xoff(8 * lg + (l16 >> 2), p0 + 4 * (l16 & 3))]);     // (sX)^T, transposed
+    const uint32_t aXW = FULL ? lds_addr(&sX[xoff(tid >> 3, 8 * (tid & 7))]) : 0u;      // X staging
+    const uint32_t aXsW = lds_addr(&sXs[xoff(tid >> 3, 8 * (tid & 7))]);               // sX staging
+    const uint32_t aST = FULL ? lds_addr(&sST[l16 * BS + 8 * lg]) : 0u;                 // S^T, A operand
+    const uint32_t aSTW = FULL ? lds_addr(&sST[(p0 + l16) * BS + n0 + 4 * lg]) : 0u;    // S^T writes
 
-    // ---- state accumulators: rows n = n0 + 16rt + 4lg + i, columns p = 16ct + l16
-    f32x4 sacc[RT][4];
+    // D X as two exact bf16 contractions with diagonal operands D_hi I and D_lo I
+    // (B operand of a 16x16x16 MFMA: lane holds rows k = 4lg + e of column l16).
+    s16x4 dI_hi, dI_lo;
+    {
+        const float Dh = p.D[h];
+        const __bf16 dh = to_bf(Dh);
+        const __bf16 dl = to_bf(Dh - from_bf(dh));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            dI_hi[e] = (4 * lg + e == l16) ? __builtin_bit_cast(short, dh) : short(0);
+            dI_lo[e] = (4 * lg + e == l16) ? __builtin_bit_cast(short, dl) : short(0);
+        }
+    }
+
+    // ---- state accumulators: rows n = n0 + 16rt + 4lg + i, columns p = p0 + 16ct + l16
+    f32x4 sacc[RT][CT];
     if (FULL) {
         const float c1 = (p.L > 0 && p.bl_in && p.xl_in)
                              ? (1.f - p.lam[(static_cast<int64_t>(b) * p.L) * p.H + h]) *
@@ -301,10 +376,10 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int n = n0 + 16 * rt + 4 * lg + i, col = 16 * ct + l16;
+                    const int n = n0 + 16 * rt + 4 * lg + i, col = p0 + 16 * ct + l16;
                     sacc[rt][ct][i] =
                         p.s_init ? p.s_init[((static_cast<size_t>(b) * p.H + h) * p.nseg + seg) * N * P + n * P + col]
                                  : initial_state<R>(p, b, h, g, n, col, c1);
@@ -313,63 +388,74 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) sacc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int ct = 0; ct < CT; ++ct) sacc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     // ---- registers holding the next chunk's inputs (raw loads; validity applied by the consumer)
-    u32v<4 * RB> xr;            // X rows RB*xrb + e, columns 8*xpo .. +7
+    u32v<4 * XPT> xr;           // X units tid + NTH*e: row u / 8, columns 8 (u % 8) .. +7
     u32v<4 * BPT> br;           // Bt units tid + NTH*e
     float pd0 = 0.f, pl0 = 0.f, pd1 = 0.f, pl1 = 0.f, pcs = 0.f;
     int pnq = 0;                // valid tokens of the prefetched chunk
-    bfv<32> cf;                 // Ct fragments (4 k-steps) of the wave's current row block
-    bfv<8 * KS * RT> af;        // Bt^T fragments of this wave's state rows
+    bfv<32> cf0, cf1;           // Ct fragments (4 k-steps) of the wave's output row blocks a_lo, a_hi
 
-#define M3_FETCH(c_)                                                                                          \
+    // Per-workgroup base pointers are uniform (scalar registers); per-lane offsets
+    // within one chunk are 32-bit.
+    //
+    // Every path through the chunk loop issues the same sequence of global loads
+    // and stores (chunk indices of prefetches are clamped, rows past the sequence
+    // end are stored to a sink).  The vector-memory counter retires in issue order
+    // and the compiler places its waits for the fewest operations any path issues
+    // after a load; with equal sequences the wait for this chunk's operands never
+    // drains the prefetch of the chunk after next.
+#define M3_PREP(c_) (p.prep + (gbase + (c_)) * lay.bytes())
+
+#define M3_FETCH_X(c_)                                                                                        \
     do {                                                                                                      \
         const int64_t t0f = static_cast<int64_t>(c_) * Q;                                                     \
         const int nqf = static_cast<int>(p.L - t0f < Q ? p.L - t0f : Q);                                      \
         pnq = nqf;                                                                                            \
-        if (XU == NTH || tid < XU) {                                                                          \
-            _Pragma("unroll") for (int e = 0; e < RB; ++e) {                                                  \
-                const int row = RB * xrb + e;                                                                 \
+        {                                                                                                     \
+            const uint16_t* xch = p.x + ((b * p.L + t0f) * p.H + h) * static_cast<int64_t>(R * P);            \
+            _Pragma("unroll") for (int e = 0; e < XPT; ++e) {                                                 \
+                const int u = tid + NTH * e, row = u >> 3;                                                    \
                 const int i = row / R, r = row - i * R;                                                       \
                 const int ic = i < nqf ? i : nqf - 1;                                                         \
-                set_quad(xr, e,                                                                               \
-                         *reinterpret_cast<const uint4*>(p.x + (((b * p.L + t0f + ic) * p.H + h) * R + r) *   \
-                                                                   static_cast<size_t>(P) + 8 * xpo));        \
+                set_quad(xr, e, *reinterpret_cast<const uint4*>(                                              \
+                                    xch + (static_cast<uint32_t>(ic) * HRP + static_cast<uint32_t>(r * P + 8 * (u & 7))))); \
             }                                                                                                 \
         }                                                                                                     \
-        if (FULL) {                                                                                           \
-            const uint16_t* gBt = reinterpret_cast<const uint16_t*>(p.prep + (gbase + (c_)) * lay.bytes() +   \
-                                                                    lay.bt());                                \
-            _Pragma("unroll") for (int e = 0; e < BPT; ++e)                                                   \
-                set_quad(br, e, *reinterpret_cast<const uint4*>(gBt + static_cast<size_t>(tid + NTH * e) * 8)); \
+        {   /* wave 0 uses these; the other waves read one broadcast address */                               \
+            const float* dtc = p.dt + (b * p.L + t0f) * p.H + h;                                              \
+            const float* lmc = p.lam + (b * p.L + t0f) * p.H + h;                                             \
+            const int i0 = (w == 0 && lane < nqf) ? lane : 0;                                                 \
+            const int i1 = (w == 0 && t0f + i0 + 1 < p.L) ? i0 + 1 : i0;                                      \
+            pd0 = dtc[static_cast<uint32_t>(i0 * p.H)];                                                       \
+            pl0 = lmc[static_cast<uint32_t>(i0 * p.H)];                                                       \
+            pd1 = dtc[static_cast<uint32_t>(i1 * p.H)];                                                       \
+            pl1 = lmc[static_cast<uint32_t>(i1 * p.H)];                                                       \
         }                                                                                                     \
-        if (w == 0) {                                                                                         \
-            const int64_t tf = t0f + (lane < nqf ? lane : nqf - 1);                                           \
-            const int64_t tf1 = (tf + 1 < p.L) ? tf + 1 : tf;                                                 \
-            pd0 = p.dt[(b * p.L + tf) * p.H + h];                                                             \
-            pl0 = p.lam[(b * p.L + tf) * p.H + h];                                                            \
-            pd1 = p.dt[(b * p.L + tf1) * p.H + h];                                                            \
-            pl1 = p.lam[(b * p.L + tf1) * p.H + h];                                                           \
-        }                                                                                                     \
-        if (tid < 2 * KP) pcs = reinterpret_cast<const float*>(p.prep + (gbase + (c_)) * lay.bytes() + lay.cs())[tid]; \
     } while (0)
 
-#define M3_LOAD_CF(c_, a_)                                                                                    \
+#define M3_FETCH_B(c_)                                                                                        \
     do {                                                                                                      \
-        const uint16_t* gCt = reinterpret_cast<const uint16_t*>(p.prep + (gbase + (c_)) * lay.bytes() + lay.ct()); \
+        const uint16_t* gBt = reinterpret_cast<const uint16_t*>(M3_PREP(c_) + lay.bt());                      \
+        _Pragma("unroll") for (int e = 0; e < BPT; ++e)                                                       \
+            set_quad(br, e, *reinterpret_cast<const uint4*>(gBt + static_cast<uint32_t>(tid + NTH * e) * 8u)); \
+        pcs = reinterpret_cast<const float*>(M3_PREP(c_) + lay.cs())[tid & (2 * KP - 1)];                     \
+    } while (0)
+
+#define M3_FETCH(c_)                                                                                          \
+    do {                                                                                                      \
+        M3_FETCH_X(c_);                                                                                       \
+        M3_FETCH_B(c_);                                                                                       \
+    } while (0)
+
+#define M3_LOAD_CF(dst_, c_, a_)                                                                              \
+    do {                                                                                                      \
+        const uint16_t* gCt = reinterpret_cast<const uint16_t*>(M3_PREP(c_) + lay.ct());                      \
         _Pragma("unroll") for (int ks = 0; ks < 4; ++ks)                                                      \
-            set_oct(cf, ks, *reinterpret_cast<const bf16x8*>(gCt + static_cast<size_t>(16 * (a_) + l16) * N + 32 * ks + 8 * lg)); \
-    } while (0)
-
-#define M3_LOAD_AF(c_)                                                                                        \
-    do {                                                                                                      \
-        const uint16_t* gBtT = reinterpret_cast<const uint16_t*>(p.prep + (gbase + (c_)) * lay.bytes() + lay.btT()); \
-        _Pragma("unroll") for (int ks = 0; ks < KS; ++ks)                                                     \
-            _Pragma("unroll") for (int rt = 0; rt < RT; ++rt)                                                 \
-                set_oct(af, ks * RT + rt,                                                                     \
-                        *reinterpret_cast<const bf16x8*>(gBtT + static_cast<size_t>(n0 + 16 * rt + l16) * QR + 32 * ks + 8 * lg)); \
+            set_oct(dst_, ks, *reinterpret_cast<const bf16x8*>(                                               \
+                                  gCt + static_cast<uint32_t>((16 * (a_) + l16) * N + 32 * ks + 8 * lg)));    \
     } while (0)
 
     // Per-token scalars (wave 0, lane = token) of the prefetched chunk into parity slot q_.
@@ -377,14 +463,11 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
     do {                                                                                                      \
         if (w == 0) {                                                                                         \
             const bool valid = lane < pnq;                                                                    \
-            const int64_t tl = static_cast<int64_t>(0);                                                       \
-            (void)tl;                                                                                         \
             const float dtv = valid ? pd0 : 0.f, lv = valid ? pl0 : 0.f;                                      \
             const bool has1 = valid && (nextpos + lane + 1 < p.L);                                            \
-            const float a = dtv * Ah;                                                                         \
             const float gm = lv * dtv;                                                                        \
             const float wv = gm + (has1 ? (1.f - pl1) * pd1 : 0.f);                                           \
-            float cum = a;                                                                                    \
+            float cum = dtv * Ah;                                                                             \
             _Pragma("unroll") for (int off = 1; off < 64; off <<= 1) {                                        \
                 const float o = __shfl_up(cum, off);                                                          \
                 if (lane >= off) cum += o;                                                                    \
@@ -392,7 +475,6 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
             const float cend = __shfl(cum, Q - 1);                                                            \
             if (lane < Q) {                                                                                   \
                 sCum[q_][lane] = cum;                                                                         \
-                sEc[q_][lane] = __expf(cum);                                                                  \
                 sSc[q_][lane] = __expf(cend - cum) * wv;                                                      \
                 sW[q_][lane] = wv;                                                                            \
                 sGam[q_][lane] = gm;                                                                          \
@@ -402,47 +484,29 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
         if (tid < 2 * KP) sCs[q_][tid] = pcs;                                                                 \
     } while (0)
 
-    // X^T and (s X)^T (small transposes in registers) and Bt into LDS.
+    // X and s X (row-major, 16-byte chunks swizzled by row), Bt, and the column
+    // factors of the off-diagonal mask tiles, into LDS.
 #define M3_STAGE_TILES(q_)                                                                                    \
     do {                                                                                                      \
-        if (XU == NTH || tid < XU) {                                                                          \
-            float sc[RB];                                                                                     \
-            uint4 xq[RB];                                                                                     \
-            _Pragma("unroll") for (int e = 0; e < RB; ++e) {                                                  \
-                const int tok = (RB * xrb + e) / R;                                                           \
-                sc[e] = sSc[q_][tok];                                                                         \
-                xq[e] = (tok < pnq) ? quad(xr, e) : uint4{0u, 0u, 0u, 0u};                                    \
-            }                                                                                                 \
-            _Pragma("unroll") for (int pp = 0; pp < 8; ++pp) {                                                \
-                uint16_t v[RB];                                                                               \
-                _Pragma("unroll") for (int e = 0; e < RB; ++e) {                                              \
-                    const uint32_t wv = (pp < 2) ? xq[e].x : (pp < 4) ? xq[e].y : (pp < 6) ? xq[e].z : xq[e].w; \
-                    v[e] = (pp & 1) ? static_cast<uint16_t>(wv >> 16) : static_cast<uint16_t>(wv & 0xffff);   \
-                }                                                                                             \
-                const int off = (8 * xpo + pp) * XS + RB * xrb;                                               \
-                if constexpr (RB == 1) {                                                                      \
-                    if (FULL) sXT[off] = v[0];                                                                \
-                    sXsT[off] = static_cast<uint16_t>(pack_bf16x2(bits_to_f(v[0]) * sc[0], 0.f) & 0xffff);    \
-                } else {                                                                                      \
-                    uint32_t raw[RB / 2], scl[RB / 2];                                                        \
-                    _Pragma("unroll") for (int e = 0; e < RB / 2; ++e) {                                      \
-                        raw[e] = v[2 * e] | (static_cast<uint32_t>(v[2 * e + 1]) << 16);                      \
-                        scl[e] = pack_bf16x2(bits_to_f(v[2 * e]) * sc[2 * e], bits_to_f(v[2 * e + 1]) * sc[2 * e + 1]); \
-                    }                                                                                         \
-                    if constexpr (RB == 2) {                                                                  \
-                        if (FULL) *reinterpret_cast<uint32_t*>(&sXT[off]) = raw[0];                           \
-                        *reinterpret_cast<uint32_t*>(&sXsT[off]) = scl[0];                                    \
-                    } else {                                                                                  \
-                        if (FULL) *reinterpret_cast<uint2*>(&sXT[off]) = uint2{raw[0], raw[1]};               \
-                        *reinterpret_cast<uint2*>(&sXsT[off]) = uint2{scl[0], scl[1]};                        \
-                    }                                                                                         \
-                }                                                                                             \
-            }                                                                                                 \
+        _Pragma("unroll") for (int e = 0; e < XPT; ++e) {                                                     \
+            const int u = tid + NTH * e, row = u >> 3;                                                        \
+            const int tok = row / R;                                                                          \
+            const float sc = sSc[q_][tok];                                                                    \
+            const uint4 xq = (tok < pnq) ? quad(xr, e) : uint4{0u, 0u, 0u, 0u};                               \
+            if (FULL) lds_st(aXW + e * (NTH / 8) * P * 2, xq);                                         \
+            const uint32_t wq[4] = {xq.x, xq.y, xq.z, xq.w};                                                  \
+            uint32_t sq[4];                                                                                   \
+            _Pragma("unroll") for (int k = 0; k < 4; ++k)                                                     \
+                sq[k] = pack_bf16x2(bits_to_f(wq[k] & 0xffff) * sc, bits_to_f(wq[k] >> 16) * sc);             \
+            lds_st(aXsW + e * (NTH / 8) * P * 2, uint4{sq[0], sq[1], sq[2], sq[3]});                   \
         }                                                                                                     \
+        _Pragma("unroll") for (int e = 0; e < BPT; ++e) lds_st(aBtW + e * (NTH / 16) * BS * 2, quad(br, e)); \
         if (FULL) {                                                                                           \
-            _Pragma("unroll") for (int e = 0; e < BPT; ++e) {                                                 \
-                const int u = tid + NTH * e;                                                                  \
-                *reinterpret_cast<uint4*>(&sBt[(u >> 4) * BS + 8 * (u & 15)]) = quad(br, e);                  \
+            _Pragma("unroll") for (int e = 0; e < VN; ++e) {                                                  \
+                const int idx = tid + NTH * e;                                                                \
+                const int ab = idx / Q, j = idx - ab * Q, ta = (16 * ab) / R;                                 \
+                if (idx < NB * Q && j < ta)                                                                   \
+                    sV[idx] = __expf(sCum[q_][ta - 1] - sCum[q_][j]) * sW[q_][j];                             \
             }                                                                                                 \
         }                                                                                                     \
     } while (0)
@@ -450,14 +514,107 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
 #define M3_WRITE_SST()                                                                                        \
     do {                                                                                                      \
         _Pragma("unroll") for (int rt = 0; rt < RT; ++rt)                                                     \
-            _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) {                                                \
+            _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) {                                               \
                 const uint2 v = {pack_bf16x2(sacc[rt][ct][0], sacc[rt][ct][1]),                               \
                                  pack_bf16x2(sacc[rt][ct][2], sacc[rt][ct][3])};                              \
-                *reinterpret_cast<uint2*>(&sST[(16 * ct + l16) * BS + n0 + 16 * rt + 4 * lg]) = v;            \
+                lds_st(aSTW + (16 * ct * BS + 16 * rt) * 2, v);                                        \
             }                                                                                                 \
     } while (0)
 
-    auto row_block = [&](int m) { return (m & 1) ? ((m + 1) * NW - 1 - w) : (m * NW + w); };  // snake order
+    // ---- output tiles.  yv[ct] (lane (l16, lg), element e) holds Y^T[p][i] for
+    // p = 16ct + 4lg + e and output row i = 16a + l16.
+    //
+    // Decay of token j < i seen from token i is e^{cum_i - cum_j}.  For a column
+    // block before row block a it factors through ref_a = cum at the token just
+    // before the block: e^{cum_i - ref_a} (row part E_i) times e^{ref_a - cum_j}
+    // (column part, stored with w_j in sV[a][j]).  Both parts are at most 1, so
+    // neither overflows, and either one underflows only where the exact product
+    // is at least as small.  The row part and e^{ref_a} of the inter-chunk term
+    // are applied to the accumulators; only the diagonal tile evaluates the full
+    // mask per element.
+
+    // Bt tile bb (A operand) and X^T tile bb (A operand of the 16x16x16 steps).
+#define M3_LOAD_COLS(bb_)                                                                                     \
+    do {                                                                                                      \
+        _Pragma("unroll") for (int ks = 0; ks < 4; ++ks)                                                      \
+            btf[ks] = lds_ld<bf16x8>(aBtRow + (16 * (bb_) * BS + 32 * ks) * 2);                               \
+        _Pragma("unroll") for (int ct = 0; ct < 4; ++ct)                                                      \
+            xf[ct] = lds_tr4(aXTr + (16 * (bb_) * P + 16 * ct) * 2);                                          \
+    } while (0)
+
+    // gt_[e] = G[i = 16a + l16][j = 16bb + 4lg + e],  G = Ct Bt^T
+#define M3_GTILE(gt_, cfv_)                                                                                   \
+    do {                                                                                                      \
+        gt_ = f32x4{0.f, 0.f, 0.f, 0.f};                                                                      \
+        _Pragma("unroll") for (int ks = 0; ks < 4; ++ks) gt_ = mfma_k32(btf[ks], oct(cfv_, ks), gt_);         \
+    } while (0)
+
+#define M3_OFFDIAG(yv_, cfv_, a_, bb_)                                                                        \
+    do {                                                                                                      \
+        f32x4 gt;                                                                                             \
+        M3_GTILE(gt, cfv_);                                                                                   \
+        const float* vrow = &sV[(a_) * Q];                                                                    \
+        float4 vv;                                                                                            \
+        if constexpr (R == 1) {                                                                               \
+            vv = *reinterpret_cast<const float4*>(vrow + 16 * (bb_) + 4 * lg);                                \
+        } else if constexpr (R == 2) {                                                                        \
+            const float2 v2 = *reinterpret_cast<const float2*>(vrow + 8 * (bb_) + 2 * lg);                    \
+            vv = float4{v2.x, v2.x, v2.y, v2.y};                                                              \
+        } else {                                                                                              \
+            const float v1 = vrow[4 * (bb_) + lg];                                                            \
+            vv = float4{v1, v1, v1, v1};                                                                      \
+        }                                                                                                     \
+        const uint2 mp = {pack_bf16x2(gt[0] * vv.x, gt[1] * vv.y), pack_bf16x2(gt[2] * vv.z, gt[3] * vv.w)};  \
+        const s16x4 mf = __builtin_bit_cast(s16x4, mp);                                                       \
+        _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) yv_[ct] = mfma_k16(xf[ct], mf, yv_[ct]);             \
+    } while (0)
+
+    // Diagonal tile: row part of the off-diagonal sum, the full mask, and D X.
+#define M3_DIAG(yv_, cfv_, a_)                                                                                \
+    do {                                                                                                      \
+        f32x4 gt;                                                                                             \
+        M3_GTILE(gt, cfv_);                                                                                   \
+        const int ta = (16 * (a_)) / R;                                                                       \
+        const float ref = ta > 0 ? sCum[q][ta - 1] : 0.f;                                                     \
+        const int ti = (16 * (a_) + l16) / R;                                                                 \
+        const float cum_i = sCum[q][ti], gam_i = sGam[q][ti];                                                 \
+        const float ei = __expf(cum_i - ref);                                                                 \
+        _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) yv_[ct] *= ei;                                       \
+        float mv[4];                                                                                          \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                                       \
+            const int tj = (16 * (a_) + 4 * lg + e) / R;                                                      \
+            const float ex = __expf(cum_i - sCum[q][tj]) * sW[q][tj];                                         \
+            mv[e] = (tj < ti) ? ex : ((tj == ti) ? gam_i : 0.f);                                              \
+        }                                                                                                     \
+        const uint2 mp = {pack_bf16x2(gt[0] * mv[0], gt[1] * mv[1]), pack_bf16x2(gt[2] * mv[2], gt[3] * mv[3])}; \
+        const s16x4 mf = __builtin_bit_cast(s16x4, mp);                                                       \
+        _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) {                                                    \
+            yv_[ct] = mfma_k16(xf[ct], mf, yv_[ct]);                                                          \
+            yv_[ct] = mfma_k16(xf[ct], dI_hi, yv_[ct]);                                                       \
+            yv_[ct] = mfma_k16(xf[ct], dI_lo, yv_[ct]);                                                       \
+        }                                                                                                     \
+    } while (0)
+
+    // Lane (l16, lg) writes columns 16ct + 4lg .. +3 of output row 16a + l16: 8 bytes per tile.
+#define M3_STORE_Y(yv_, a_)                                                                                   \
+    do {                                                                                                      \
+        const int i = 16 * (a_) + l16;                                                                        \
+        const int tk = i / R, r = i - tk * R;                                                                 \
+        uint16_t* yrow = (tk < nq) ? ych + (static_cast<uint32_t>(tk) * HRP + static_cast<uint32_t>(r * P + 4 * lg)) \
+                                   : p.y_sink + lane * 64;                                                    \
+        _Pragma("unroll") for (int ct = 0; ct < 4; ++ct)                                                      \
+            *reinterpret_cast<uint2*>(yrow + 16 * ct) =                                                       \
+                uint2{pack_bf16x2(yv_[ct][0], yv_[ct][1]), pack_bf16x2(yv_[ct][2], yv_[ct][3])};              \
+    } while (0)
+
+    // Inter-chunk term for row block(s), scaled by e^{ref_a}: yv[ct] = e^{ref_a} S^T Ct^T.
+#define M3_INTER_SCALE(yv_, a_)                                                                               \
+    do {                                                                                                      \
+        const int ta = (16 * (a_)) / R;                                                                       \
+        const float er = ta > 0 ? __expf(sCum[q][ta - 1]) : 1.f;                                              \
+        _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) yv_[ct] *= er;                                       \
+    } while (0)
+
     int64_t nextpos = 0;          // first token of the prefetched chunk
 
     // ---- prologue: chunk c_begin into LDS, chunk c_begin+1 into registers
@@ -466,12 +623,15 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
         nextpos = static_cast<int64_t>(c_begin) * Q;
         M3_STAGE_SCALARS(c_begin & 1);
         __syncthreads();
-        M3_STAGE_TILES(c_begin & 1);
-        if (FULL && row_block(0) < NB) M3_LOAD_CF(c_begin, row_block(0));
-        if (!FULL || AF_EARLY) M3_LOAD_AF(c_begin);
-        if (c_begin + 1 < c_end) {
-            M3_FETCH(c_begin + 1);
-            nextpos = static_cast<int64_t>(c_begin + 1) * Q;
+        const int q = c_begin & 1;
+        M3_STAGE_TILES(q);
+        if (FULL) {
+            M3_LOAD_CF(cf0, c_begin, has_rows ? a_lo : 0);
+            if (MB == 2) M3_LOAD_CF(cf1, c_begin, a_hi);
+        } else {
+            const int cf = c_begin + 1 < c_end ? c_begin + 1 : c_begin;
+            M3_FETCH(cf);
+            nextpos = static_cast<int64_t>(cf) * Q;
         }
     }
     if (FULL) M3_WRITE_SST();
@@ -485,111 +645,96 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
         const int64_t t0 = static_cast<int64_t>(c) * Q;
         const int nq = static_cast<int>(p.L - t0 < Q ? p.L - t0 : Q);
         const bool has_next = c + 1 < c_end;
-
+        const int cn = has_next ? c + 1 : c;    // chunk of the register prefetches (clamped)
         if (FULL) {
-            // (4) outputs, row blocks in snake order across the waves (balances the causal work)
+            // next chunk's X and scalars, issued before this chunk's output contractions
+            // so that the loads are in flight while the matrix cores work
+            M3_FETCH_X(cn);
+            nextpos = static_cast<int64_t>(cn) * Q;
+        }
+
+        if (FULL && !has_rows) {
+            // a wave without output rows still issues the stores and loads of one
+            uint16_t* yrow = p.y_sink + lane * 64;
 #pragma unroll
-            for (int m = 0; m < MB; ++m) {
-                const int a = row_block(m);
-                if (a >= NB) continue;
-                if (m > 0) M3_LOAD_CF(c, a);
-                f32x4 yacc[4];
+            for (int ct = 0; ct < 4; ++ct) *reinterpret_cast<uint2*>(yrow + 16 * ct) = uint2{0u, 0u};
+            M3_LOAD_CF(cf0, cn, 0);
+        }
+        if (FULL && has_rows) {
+            uint16_t* ych = p.y + ((b * p.L + t0) * p.H + h) * static_cast<int64_t>(R * P);
+            bf16x8 btf[4];
+            s16x4 xf[4];
+            f32x4 y0[4], y1[4];
+            // (4a) inter-chunk term; with two row blocks the S^T fragments serve both
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) {
-                    yacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int ct = 0; ct < 4; ++ct) {
+                y0[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                y1[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks)
-                        yacc[ct] = mfma_k32(oct(cf, ks), *reinterpret_cast<const bf16x8*>(&sST[(16 * ct + l16) * BS + 32 * ks + 8 * lg]),
-                                            yacc[ct]);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float ec = sEc[q][(16 * a + 4 * lg + i) / R];
-#pragma unroll
-                    for (int ct = 0; ct < 4; ++ct) yacc[ct][i] *= ec;
-                }
-                const int ti = (16 * a + l16) / R;
-                const float cum_i = sCum[q][ti], gam_i = sGam[q][ti];
-                auto mask = [&](int tj) {        // branch-free: every lane evaluates the exp
-                    const float ex = __expf(fminf(cum_i - sCum[q][tj], 0.f)) * sW[q][tj];
-                    return (tj < ti) ? ex : ((tj == ti) ? gam_i : 0.f);
-                };
-                for (int bb = 0; bb <= a; ++bb) {
-                    f32x4 gt = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks)
-                        gt = mfma_k32(*reinterpret_cast<const bf16x8*>(&sBt[(16 * bb + l16) * BS + 32 * ks + 8 * lg]), oct(cf, ks), gt);
-                    // gt[e] = (Ct Bt^T)[i = 16a + l16][j = 16bb + 4lg + e]
-                    float mv[4];
-                    if (R == 4) {
-                        const float m0 = mask(4 * bb + lg);
-                        mv[0] = mv[1] = mv[2] = mv[3] = m0;
-                    } else if (R == 2) {
-                        const float m0 = mask(8 * bb + 2 * lg), m1 = mask(8 * bb + 2 * lg + 1);
-                        mv[0] = mv[1] = m0;
-                        mv[2] = mv[3] = m1;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) mv[e] = mask((16 * bb + 4 * lg + e) / R);
-                    }
-                    const uint2 mp = {pack_bf16x2(mv[0] * gt[0], mv[1] * gt[1]), pack_bf16x2(mv[2] * gt[2], mv[3] * gt[3])};
-                    const s16x4 mf = __builtin_bit_cast(s16x4, mp);
-#pragma unroll
-                    for (int ct = 0; ct < 4; ++ct)
-                        yacc[ct] = mfma_k16(mf, *reinterpret_cast<const s16x4*>(&sXT[(16 * ct + l16) * XS + 16 * bb + 4 * lg]),
-                                            yacc[ct]);
-                }
-                // next chunk's Ct for the first row block: cf is dead once the last block is done
-                if (m == MB - 1 || row_block(m + 1) >= NB) {
-                    if (has_next && row_block(0) < NB) M3_LOAD_CF(c + 1, row_block(0));
-                }
-                // skip term, then store column pairs: lanes 2j and 2j+1 swap halves so
-                // each writes two rows of two adjacent columns as 4-byte words
-                const bool odd = l16 & 1;
-                const int rbase = 16 * a + 4 * lg + (odd ? 2 : 0);
-#pragma unroll
-                for (int ct = 0; ct < 4; ++ct) {
-                    const s16x4 xv = *reinterpret_cast<const s16x4*>(&sXT[(16 * ct + l16) * XS + 16 * a + 4 * lg]);
-                    float v[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = yacc[ct][i] + Dh * bits_to_f(static_cast<uint16_t>(xv[i]));
-                    const float r0 = swap_adjacent(odd ? v[0] : v[2]);
-                    const float r1 = swap_adjacent(odd ? v[1] : v[3]);
-                    const uint32_t w0 = odd ? pack_bf16x2(r0, v[2]) : pack_bf16x2(v[0], r0);
-                    const uint32_t w1 = odd ? pack_bf16x2(r1, v[3]) : pack_bf16x2(v[1], r1);
-                    const int col = 16 * ct + (l16 & ~1);
-#pragma unroll
-                    for (int qq = 0; qq < 2; ++qq) {
-                        const int row = rbase + qq;
-                        const int tk = row / R, r = row - tk * R;
-                        if (tk < nq)
-                            *reinterpret_cast<uint32_t*>(
-                                p.y + (((b * p.L + t0 + tk) * p.H + h) * R + r) * static_cast<size_t>(P) + col) = qq ? w1 : w0;
-                    }
+                for (int ks = 0; ks < 4; ++ks) {
+                    const bf16x8 sf = lds_ld<bf16x8>(aST + (16 * ct * BS + 32 * ks) * 2);
+                    y0[ct] = mfma_k32(sf, oct(cf0, ks), y0[ct]);
+                    if (MB == 2) y1[ct] = mfma_k32(sf, oct(cf1, ks), y1[ct]);
                 }
             }
-            if (!AF_EARLY) M3_LOAD_AF(c);
+            M3_INTER_SCALE(y0, a_lo);
+            if (MB == 2) M3_INTER_SCALE(y1, a_hi);
+            // (4b) intra-chunk tiles, column blocks in order; the diagonal tile closes a row block
+            for (int bb = 0; bb < a_lo; ++bb) {
+                M3_LOAD_COLS(bb);
+                M3_OFFDIAG(y0, cf0, a_lo, bb);
+                if (MB == 2) M3_OFFDIAG(y1, cf1, a_hi, bb);
+            }
+            M3_LOAD_COLS(a_lo);
+            M3_DIAG(y0, cf0, a_lo);
+            if (MB == 2) M3_OFFDIAG(y1, cf1, a_hi, a_lo);
+            M3_STORE_Y(y0, a_lo);
+            M3_LOAD_CF(cf0, cn, a_lo);
+            if constexpr (MB == 2) {
+                for (int bb = a_lo + 1; bb < a_hi; ++bb) {
+                    M3_LOAD_COLS(bb);
+                    M3_OFFDIAG(y1, cf1, a_hi, bb);
+                }
+                M3_LOAD_COLS(a_hi);
+                M3_DIAG(y1, cf1, a_hi);
+                M3_STORE_Y(y1, a_hi);
+                M3_LOAD_CF(cf1, cn, a_hi);
+            }
         }
-        if (has_next) M3_STAGE_SCALARS(q ^ 1);   // the other parity slot: nobody reads it now
-        __syncthreads();   // S_{c-1} no longer read; next chunk's scalars visible
-
-        // (5) state update: S <- R(phi_end) [e^{cum_end} S + Bt^T (s X)]
+        if (FULL) M3_FETCH_B(cn);   // next chunk's Bt: registers held only across the state update
+        // (5) state update: S <- R(phi_end) [e^{cum_end} S + Bt^T (s X)].  It reads only this
+        // chunk's tiles and its own accumulators, so a wave starts it as soon as its outputs
+        // are done, overlapping the output work of the other waves.
         {
             const float cend = sDec[q];
             const float decay = __expf(cend);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) sacc[rt][ct] *= decay;
+                for (int ct = 0; ct < CT; ++ct) sacc[rt][ct] *= decay;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KS; ++ks) {
+                // A operand: Bt^T rows n0 + 16rt + l16, k = 32ks + 8lg .. +7, read transposed
+                bf16x8 bta[RT];
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) {
-                    const bf16x8 bx = *reinterpret_cast<const bf16x8*>(&sXsT[(16 * ct + l16) * XS + 32 * ks + 8 * lg]);
-#pragma unroll
-                    for (int rt = 0; rt < RT; ++rt) sacc[rt][ct] = mfma_k32(oct(af, ks * RT + rt), bx, sacc[rt][ct]);
+                for (int rt = 0; rt < RT; ++rt) {
+                    const uint32_t src = aBtTr + (32 * ks * BS + 16 * rt) * 2;
+                    const s16x4 lo = lds_tr4(src), hi = lds_tr4(src + 4 * BS * 2);
+                    bta[rt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
-            if ((!FULL || AF_EARLY) && has_next) M3_LOAD_AF(c + 1);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    // B operand: (s X)^T column p = p0 + 16ct + l16, k = 32ks + 8lg .. +7, read transposed
+                    const uint32_t xa = aXsTr + (32 * ks * P + 16 * ct) * 2;
+                    const s16x4 xlo = lds_tr4(xa), xhi = lds_tr4(xa + 4 * P * 2);
+                    const bf16x8 bx = __builtin_bit_cast(bf16x8, __builtin_shufflevector(xlo, xhi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) sacc[rt][ct] = mfma_k32(bta[rt], bx, sacc[rt][ct]);
+                }
+                // one k-step of operands in flight at a time (the reads of the next step
+                // still overlap this step's matrix ops); hoisting them all costs registers
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -597,15 +742,13 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
                     const int k = (n0 + 16 * rt + 4 * lg + i) >> 1;
                     const float cn = sCs[q][2 * k], sn = sCs[q][2 * k + 1];
 #pragma unroll
-                    for (int ct = 0; ct < 4; ++ct) {
+                    for (int ct = 0; ct < CT; ++ct) {
                         const float s0 = sacc[rt][ct][i], s1 = sacc[rt][ct][i + 1];
                         sacc[rt][ct][i] = cn * s0 - sn * s1;
                         sacc[rt][ct][i + 1] = sn * s0 + cn * s1;
                     }
                 }
-            if (FULL) {
-                M3_WRITE_SST();
-            } else {
+            if (!FULL) {
                 dec_total += cend;
                 if (tid < KP) {
                     const float cn = sCs[q][2 * tid], sn = sCs[q][2 * tid + 1];
@@ -615,46 +758,58 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
                 }
             }
         }
-        if (has_next) {
-            __syncthreads();   // the chunk's X / Bt tiles are no longer read
-            M3_STAGE_TILES(q ^ 1);
-            if (c + 2 < c_end) {
-                M3_FETCH(c + 2);
-                nextpos = static_cast<int64_t>(c + 2) * Q;
-            }
+        if (has_next) M3_STAGE_SCALARS(q ^ 1);   // the other parity slot: nobody reads it now
+        __syncthreads();   // this chunk's tiles, S_{c-1} and the column factors no longer read;
+                           // next chunk's scalars visible
+        if (FULL) M3_WRITE_SST();
+        if (has_next) M3_STAGE_TILES(q ^ 1);
+        if (!FULL) {   // state-only mode has no output phase to hide the loads behind: a chunk further ahead
+            const int cf = c + 2 < c_end ? c + 2 : c_end - 1;
+            M3_FETCH(cf);
+            nextpos = static_cast<int64_t>(cf) * Q;
         }
         __syncthreads();
     }
+#undef M3_PREP
 #undef M3_FETCH
+#undef M3_FETCH_X
+#undef M3_FETCH_B
 #undef M3_LOAD_CF
-#undef M3_LOAD_AF
 #undef M3_STAGE_SCALARS
 #undef M3_STAGE_TILES
 #undef M3_WRITE_SST
+#undef M3_LOAD_COLS
+#undef M3_GTILE
+#undef M3_OFFDIAG
+#undef M3_DIAG
+#undef M3_STORE_Y
+#undef M3_INTER_SCALE
 
     // epilogue
     if (FULL) {
         if (last_seg && p.h_out) {
+            float* ho = p.h_out + (static_cast<size_t>(b) * p.H + h) * N * P;
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct)
+                for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int n = n0 + 16 * rt + 4 * lg + i, col = 16 * ct + l16;
-                        p.h_out[(static_cast<size_t>(b) * p.H + h) * N * P + n * P + col] = sacc[rt][ct][i];
+                        const int n = n0 + 16 * rt + 4 * lg + i, col = p0 + 16 * ct + l16;
+                        ho[n * P + col] = sacc[rt][ct][i];
                     }
         }
     } else {
         const size_t sidx = (static_cast<size_t>(b) * p.H + h) * (p.nseg - 1) + seg;
+        float* so = p.seg_state + sidx * N * P;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int n = n0 + 16 * rt + 4 * lg + i, col = 16 * ct + l16;
-                    p.seg_state[sidx * N * P + n * P + col] = sacc[rt][ct][i];
+                    const int n = n0 + 16 * rt + 4 * lg + i, col = p0 + 16 * ct + l16;
+                    so[n * P + col] = sacc[rt][ct][i];
                 }
         if (tid == 0) p.seg_decay[sidx] = dec_total;
         if (tid < KP) {
@@ -702,8 +857,10 @@ __global__ __launch_bounds__(NT) void seg_pass(ScanParams p, float* __restrict__
 // host side
 // ------------------------------------------------------------------------------------
 bool mfma_supported(const PrefillArgs& a) {
+    // per-lane offsets within one chunk of x and y are 32-bit
+    const bool offsets_fit = static_cast<int64_t>(a.H) * a.R * a.P * a.Q < (int64_t{1} << 31);
     return a.bf16 && a.N == mf::N && a.P == mf::P && (a.R == 1 || a.R == 2 || a.R == 4) &&
-           (a.Q == 32 || a.Q == 64);
+           (a.Q == 32 || a.Q == 64) && offsets_fit;
 }
 
 static int choose_nseg(const PrefillArgs& a, int nchunks) {
@@ -717,7 +874,7 @@ static int choose_nseg(const PrefillArgs& a, int nchunks) {
 }
 
 struct MfmaWs {
-    size_t prep, seg_state, seg_decay, seg_rot, s_init, total;
+    size_t prep, sink, seg_state, seg_decay, seg_rot, s_init, total;
 };
 
 static MfmaWs mfma_ws(const PrefillArgs& a, int nchunks, int nseg) {
@@ -727,6 +884,8 @@ static MfmaWs mfma_ws(const PrefillArgs& a, int nchunks, int nseg) {
     size_t off = 0;
     w.prep = off;
     off += al(static_cast<size_t>(a.batch) * a.G * nchunks * lay.bytes());
+    w.sink = off;
+    off += al(64 * 64 * sizeof(uint16_t));
     const size_t bh = static_cast<size_t>(a.batch) * a.H;
     if (nseg > 1) {
         w.seg_state = off;
@@ -757,7 +916,10 @@ void plan_mfma(const PrefillArgs& a, PrefillPlan* plan) {
 
 template <int R, int Q>
 static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, hipStream_t st) {
-    constexpr int NW = (Q * R >= 128) ? 8 : 4;   // waves per workgroup
+    // waves per workgroup: one per 16-row block of the chunk, at least 4; 16 blocks
+    // go two to a wave (8 waves), which shares their Bt and X tile reads
+    constexpr int NB = Q * R / 16;
+    constexpr int NW = NB > 8 ? NB / 2 : (NB > 4 ? NB : 4);
     const int nchunks = static_cast<int>((a.L + a.Q - 1) / a.Q);
     if (nchunks == 0) return hipSuccess;
     const int nseg = plan.nseg;
@@ -780,6 +942,7 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
     p.D = a.D;
     p.prep = base + ws.prep;
     p.y = static_cast<uint16_t*>(a.y);
+    p.y_sink = reinterpret_cast<uint16_t*>(base + ws.sink);
     p.h_in = a.h_in;
     p.bl_in = static_cast<const uint16_t*>(a.bl_in);
     p.xl_in = static_cast<const uint16_t*>(a.xl_in);
