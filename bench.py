@@ -259,7 +259,8 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.io_dtype == "bf16" else "fp32",
         "data": "synthetic (seeded torch generators on the GPU; distributions of the workload)",
         "config": {"workload": cfg.label, "name": cfg.name, "batch": cfg.batch, "prefill_len": L,
                    "decode_steps": steps_dec, "heads": cfg.nheads, "groups": cfg.ngroups,

@@ -74,8 +74,9 @@ __global__ __launch_bounds__(256) void prefill_generic(
         const int nq = static_cast<int>(L - t0 < Q ? L - t0 : Q);
         __syncthreads();   // previous chunk done with every LDS array
 
-        // Per-token scalars (a_t in cum before the prefix sum).
-        for (int i = tid; i < Q; i += NT) {
+        // Per-token scalars; the decay exponents a_t = dt_t A are prefix-summed in
+        // registers across the lanes of wave 0 when the chunk fits in one wave.
+        for (int i = tid; i < (Q <= 64 ? 64 : Q); i += NT) {
             float a = 0.f, gm = 0.f, w = 0.f;
             if (i < nq) {
                 const int64_t t = t0 + i;
@@ -85,26 +86,40 @@ __global__ __launch_bounds__(256) void prefill_generic(
                 w = gm;
                 if (t + 1 < L) w += (1.f - lam[(b * L + t + 1) * H + h]) * dt[(b * L + t + 1) * H + h];
             }
-            cum[i] = a;
-            gam[i] = gm;
-            wv[i] = w;
+            if (Q <= 64) {   // i == lane of wave 0
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float o = __shfl_up(a, off);
+                    if (i >= off) a += o;
+                }
+            }
+            if (i < Q) {
+                cum[i] = a;
+                gam[i] = gm;
+                wv[i] = w;
+            }
         }
-        // Chunk-local angle prefix sums, one pair per thread.
+        // Angles into LDS, one element per thread (loads in parallel).
+        for (int idx = tid; idx < Q * KP; idx += NT) {
+            const int i = idx / KP, k = idx - i * KP;
+            phi[idx] = (i < nq) ? theta[((b * L + t0 + i) * G + g) * KP + k] : 0.f;
+        }
+        __syncthreads();
+        // Chunk-local angle prefix sums, one pair per thread, within LDS.
         for (int k = tid; k < KP; k += NT) {
             float acc = 0.f;
             for (int i = 0; i < Q; ++i) {
-                if (i < nq) acc += theta[((b * L + t0 + i) * G + g) * KP + k];
+                acc += phi[i * KP + k];
                 phi[i * KP + k] = acc;
             }
         }
-        __syncthreads();
-        if (tid == 0) {
+        if (Q > 64 && tid == 0) {
             float acc = 0.f;
             for (int i = 0; i < Q; ++i) {
                 acc += cum[i];
                 cum[i] = acc;
             }
         }
+        __syncthreads();
         // Rotated B, C (R(-phi_i) on pairs) and X, as fp32 in LDS.
         for (int idx = tid; idx < Q * R * KP; idx += NT) {
             const int i = idx / (R * KP), rem = idx - i * R * KP, r = rem / KP, k = rem - r * KP;
