@@ -50,6 +50,11 @@ def load(path: str = _LIB):
     f = lib.m3o_scan
     f.restype = ctypes.c_int
     f.argtypes = [ctypes.POINTER(_Dims)] + [ctypes.c_void_p] * 13 + [ctypes.c_int]
+    f = lib.m3o_scan_rounded
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.POINTER(_Dims)] + [ctypes.c_void_p] * 14 + [ctypes.c_int]
+    lib.m3o_round_bf16.restype = ctypes.c_double
+    lib.m3o_round_bf16.argtypes = [ctypes.c_double]
     lib.m3o_max_threads.restype = ctypes.c_int
     if path == _LIB:
         _lib = lib
@@ -69,12 +74,21 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def scan(x, dt, A, lam, theta, B, C, D, state_in=None, nthreads: int = 0, lib_path: str = _LIB):
+def round_bf16(v: float) -> float:
+    """Nearest bf16 value of a float (ties to even), as the oracle rounds a state."""
+    return float(load().m3o_round_bf16(float(v)))
+
+
+def scan(x, dt, A, lam, theta, B, C, D, state_in=None, nthreads: int = 0, lib_path: str = _LIB,
+         round_after=None):
     """Sequential fp64 scan.
 
     Shapes: x (b,L,H,R,P), dt/lam (b,L,H), A/D (H,), theta (b,L,G,N/2),
     B/C (b,L,G,R,N).  ``state_in`` is None or a tuple (h0 (b,H,N,P),
     b_last (b,G,R,N), x_last (b,H,R,P)); b_last/x_last may be None.
+    ``round_after``: None (full-precision state) or L booleans; after each
+    flagged token the state is replaced by its nearest bf16 value (the output
+    of that token still reads the unrounded state).
     Returns (y (b,L,H,R,P) float64, h_out (b,H,N,P) float64).
     """
     x, dt, A, lam, theta, B, C, D = map(_f64, (x, dt, A, lam, theta, B, C, D))
@@ -99,9 +113,17 @@ def scan(x, dt, A, lam, theta, B, C, D, state_in=None, nthreads: int = 0, lib_pa
     y = np.empty((b, L, H, R, P), dtype=np.float64)
     h_out = np.empty((b, H, N, P), dtype=np.float64)
     d = _Dims(b, L, H, G, P, N, R)
-    rc = load(lib_path).m3o_scan(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(lam),
-                                 _ptr(theta), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(bl),
-                                 _ptr(xl), _ptr(y), _ptr(h_out), int(nthreads))
+    if round_after is None:
+        rc = load(lib_path).m3o_scan(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(lam),
+                                     _ptr(theta), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(bl),
+                                     _ptr(xl), _ptr(y), _ptr(h_out), int(nthreads))
+    else:
+        ra = np.ascontiguousarray(np.asarray(round_after, dtype=bool), dtype=np.uint8)
+        assert ra.shape == (L,)
+        rc = load(lib_path).m3o_scan_rounded(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A),
+                                             _ptr(lam), _ptr(theta), _ptr(B), _ptr(C), _ptr(D),
+                                             _ptr(h0), _ptr(bl), _ptr(xl), _ptr(ra), _ptr(y),
+                                             _ptr(h_out), int(nthreads))
     if rc != 0:
         raise ValueError(f"m3o_scan failed with code {rc}")
     return y, h_out

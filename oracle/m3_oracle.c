@@ -31,6 +31,13 @@
  * Start of a scan: h_0 and the previous input (B_0, X_0) come from the optional
  * state_in; absent, both are zero.  state_out is (h_L, B_L, X_L).
  *
+ * Reduced-precision state (m3o_scan_rounded): a state kept in bf16 between
+ * steps is the same recurrence with h_t replaced by its nearest bf16 value
+ * (round to nearest, ties to even) after every token t flagged in round_after,
+ * once Y_t has been formed from the unrounded h_t.  A decode step that reads
+ * and writes a bf16 state rounds after every token; a prefill that only writes
+ * its final state in bf16 rounds after its last token.
+ *
  * All inputs and outputs are fp64 arrays (fp32 and bf16 values are exact in
  * fp64, so the kernels' inputs pass through unchanged).
  *
@@ -58,12 +65,26 @@ typedef struct {
 
 #define IDX5(a, b, c, d, e, B_, C_, D_, E_) ((((((a) * (B_) + (b)) * (C_) + (c)) * (D_) + (d)) * (E_)) + (e))
 
+/* Nearest bf16 value (8 significant bits, fp32's exponent range), ties to even.
+ * v = m 2^e with 0.5 <= |m| < 1; keep 8 bits of m with the default rounding
+ * mode of nearbyint (to nearest, ties to even).  Values below fp32's smallest
+ * normal number keep fp32's absolute spacing there, 2^-133 at bf16 precision. */
+double m3o_round_bf16(double v) {
+    if (v == 0.0 || isnan(v) || isinf(v)) return v;
+    int e;
+    const double m = frexp(v, &e);
+    if (e < -125) return ldexp(nearbyint(ldexp(v, 133)), -133);
+    const double r = ldexp(nearbyint(ldexp(m, 8)), e - 8);
+    return fabs(r) > 3.3895313892515355e38 ? copysign(INFINITY, v) : r;
+}
+
 /* Scan one (batch b, head h) slice through all L tokens. */
 static void scan_slice(const m3o_dims* dm, int64_t b, int64_t h,
                        const double* x, const double* dt, const double* A,
                        const double* lam, const double* theta, const double* B,
                        const double* C, const double* D,
                        const double* h0, const double* b_last, const double* x_last,
+                       const unsigned char* round_after,
                        double* y, double* h_out, double* hs, double* U, double* Uprev) {
     const int64_t L = dm->seqlen, H = dm->nheads, G = dm->ngroups;
     const int64_t P = dm->headdim, N = dm->dstate, R = dm->rank, K = N / 2;
@@ -129,6 +150,9 @@ static void scan_slice(const m3o_dims* dm, int64_t b, int64_t h,
                 y[xi] = acc + D[h] * x[xi];
             }
 
+        if (round_after && round_after[t])
+            for (int64_t i = 0; i < N * P; ++i) hs[i] = m3o_round_bf16(hs[i]);
+
         memcpy(Uprev, U, sizeof(double) * N * P);
     }
     if (h_out) memcpy(h_out + (b * H + h) * N * P, hs, sizeof(double) * N * P);
@@ -138,12 +162,14 @@ static void scan_slice(const m3o_dims* dm, int64_t b, int64_t h,
  * Full scan.  Returns 0 on success, -1 on a shape error (N odd, H % G != 0,
  * non-positive sizes, y NULL), -2 if scratch memory cannot be allocated.
  * nthreads <= 0 uses the OpenMP default.  h_out may be NULL.
- * (b_last, x_last) are used only when both are non-NULL.
+ * (b_last, x_last) are used only when both are non-NULL.  round_after is NULL
+ * (full-precision state) or one flag per token (length L, shared by all slices).
  */
-int m3o_scan(const m3o_dims* dm, const double* x, const double* dt, const double* A,
-             const double* lam, const double* theta, const double* B, const double* C,
-             const double* D, const double* h0, const double* b_last, const double* x_last,
-             double* y, double* h_out, int nthreads) {
+int m3o_scan_rounded(const m3o_dims* dm, const double* x, const double* dt, const double* A,
+                     const double* lam, const double* theta, const double* B, const double* C,
+                     const double* D, const double* h0, const double* b_last,
+                     const double* x_last, const unsigned char* round_after, double* y,
+                     double* h_out, int nthreads) {
     if (!dm || !y || dm->batch < 0 || dm->seqlen < 0 || dm->nheads <= 0 || dm->ngroups <= 0 ||
         dm->headdim <= 0 || dm->dstate <= 0 || dm->rank <= 0)
         return -1;
@@ -167,12 +193,21 @@ int m3o_scan(const m3o_dims* dm, const double* x, const double* dt, const double
         for (int64_t s = 0; s < nslices; ++s) {
             if (!scratch) continue;
             const int64_t b = s / dm->nheads, h = s % dm->nheads;
-            scan_slice(dm, b, h, x, dt, A, lam, theta, B, C, D, h0, b_last, x_last, y, h_out,
-                       scratch, scratch + NP, scratch + 2 * NP);
+            scan_slice(dm, b, h, x, dt, A, lam, theta, B, C, D, h0, b_last, x_last, round_after,
+                       y, h_out, scratch, scratch + NP, scratch + 2 * NP);
         }
         free(scratch);
     }
     return err;
+}
+
+/* The scan with a full-precision state (no rounding). */
+int m3o_scan(const m3o_dims* dm, const double* x, const double* dt, const double* A,
+             const double* lam, const double* theta, const double* B, const double* C,
+             const double* D, const double* h0, const double* b_last, const double* x_last,
+             double* y, double* h_out, int nthreads) {
+    return m3o_scan_rounded(dm, x, dt, A, lam, theta, B, C, D, h0, b_last, x_last, NULL, y,
+                            h_out, nthreads);
 }
 
 /* Number of OpenMP threads a parallel region would use (for reporting). */
