@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="c4", help="c1, c2, c3 (prefill only) or c4 (prefill + decode)")
     ap.add_argument("--decode-steps", type=int, default=None, help="override the decode steps per step")
+    ap.add_argument("--state-dtype", default="fp32", choices=("fp32", "bf16"),
+                    help="dtype of the state in HBM (bf16: reduced-precision state, fp32 math)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--check-slices", type=int, default=2, help="(b,h) slices checked against the oracle")
@@ -44,20 +46,21 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_bytes(cfg, L, steps):
-    """Bytes the method must move (see the workload formulas in the design notes)."""
+def algorithmic_bytes(cfg, L, steps, state_bytes=4):
+    """Bytes the method must move (see the workload formulas in the design notes);
+    state_bytes is 4 for an fp32 state, 2 for a bf16 state."""
     s = 2 if cfg.io_dtype == "bf16" else 4
     b, H, G, P, N, R = cfg.batch, cfg.nheads, cfg.ngroups, cfg.headdim, cfg.dstate, cfg.rank
     pre = 0
     if L > 0:
         pre += b * L * H * (2 * R * P * s + 8)              # x read, y write, dt, lambda
         pre += b * L * G * (2 * N * R * s + 4 * (N // 2))   # B, C, theta
-        pre += b * H * N * P * 4                            # state out
+        pre += b * H * N * P * state_bytes                  # state out
         pre += b * (G * R * N + H * R * P) * s              # carry out
         pre += 8 * H
     dec = 0
     if steps > 0:
-        dec += 2 * b * H * N * P * 4                        # state read + write
+        dec += 2 * b * H * N * P * state_bytes              # state read + write
         dec += b * H * (3 * R * P * s + 8)                  # x_t, x_last read, y_t write, dt, lambda
         dec += b * G * (3 * R * N * s + 4 * (N // 2))       # B_t, C_t, b_last, theta
         dec += 8 * H
@@ -108,6 +111,8 @@ def main():
     from state_space_sequence_scan_amd import CONFIGS, inputs, m3scan
 
     cfg = CONFIGS[args.workload]
+    state_dtype = torch.bfloat16 if args.state_dtype == "bf16" else torch.float32
+    state_bytes = 2 if args.state_dtype == "bf16" else 4
     steps_dec = cfg.decode_steps if args.decode_steps is None else args.decode_steps
     L = cfg.seqlen
     dev = torch.device("cuda:0")
@@ -136,7 +141,7 @@ def main():
         e0, e1, e2 = ev(), ev(), ev()
         e0.record(stream)
         _, st = m3scan.prefill(d["x"], d["dt"], d["A"], d["lam"], d["theta"], d["B"], d["C"], d["D"],
-                               cfg.chunk, y=y)
+                               cfg.chunk, y=y, state_dtype=state_dtype)
         e1.record(stream)
         for t in range(steps_dec):
             m3scan.decode_step(st, dd["x"][t], dd["dt"][t], d["A"], dd["lam"][t], dd["theta"][t],
@@ -163,25 +168,27 @@ def main():
     tokens_pre = cfg.batch * L
     tokens_dec = cfg.batch * steps_dec
     value = (tokens_pre + tokens_dec) / (step_ms / 1e3)
-    pre_bytes, dec_bytes = algorithmic_bytes(cfg, L, steps_dec)
+    pre_bytes, dec_bytes = algorithmic_bytes(cfg, L, steps_dec, state_bytes)
     pre_tps = tokens_pre / (pre_avg / 1e3)
     pre_gbs = pre_bytes / (pre_avg / 1e3) / 1e9
     dec_launch_ms = dec_avg / max(steps_dec, 1)
     dec_gbs = dec_bytes / (dec_launch_ms / 1e3) / 1e9 if steps_dec else 0.0
-    state_gbs = (2 * cfg.batch * cfg.nheads * cfg.dstate * cfg.headdim * 4) / (dec_launch_ms / 1e3) / 1e9 \
+    state_gbs = (2 * cfg.batch * cfg.nheads * cfg.dstate * cfg.headdim * state_bytes) / (dec_launch_ms / 1e3) / 1e9 \
         if steps_dec else 0.0
     flops = prefill_flops(cfg, L)
 
     # Dominant kernel: the one with the larger share of the step.
     if steps_dec and dec_avg >= pre_avg:
-        traffic = pmc_traffic("decode_c4_hbm_counters.json", ["m3_decode.hip"], dec_bytes)
-        roof = {"kernel": "decode_fast<bf16,128,64,4>", "bound": "hbm",
+        sfx = "" if args.state_dtype == "fp32" else "_bf16state"
+        traffic = pmc_traffic(f"decode_{args.workload}{sfx}_hbm_counters.json",
+                              ["m3_decode.hip", "m3_common.h"], dec_bytes)
+        roof = {"kernel": f"decode_fast<io bf16, state {args.state_dtype}, N128, P64, R4>", "bound": "hbm",
                 "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "alg_bytes_per_launch": dec_bytes, "avg_launch_us": round(dec_launch_ms * 1e3, 2)}
     else:
         traffic = pmc_traffic(f"prefill_{args.workload}_hbm_counters.json",
-                              ["m3_prefill_mfma.hip"], pre_bytes)
+                              ["m3_prefill_mfma.hip", "m3_common.h"], pre_bytes)
         roof = {"kernel": "prefill (chunked scan)", "bound": "hbm",
                 "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(pre_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -220,7 +227,11 @@ def main():
             for _ in range(args.check_slices):
                 bi, h = int(rng.integers(cfg.batch)), int(rng.integers(cfg.nheads))
                 si = slice_inputs(bi, h)
-                yr, hr = oracle.scan(*[si[k] for k in order])
+                flags = None
+                if args.state_dtype == "bf16":   # state rounded after the prefill and every decode token
+                    flags = np.zeros(L + steps_dec, bool)
+                    flags[L - 1:] = True
+                yr, hr = oracle.scan(*[si[k] for k in order], round_after=flags)
                 yg = [y[bi:bi + 1, :, h:h + 1].double().cpu().numpy()]
                 if steps_dec:
                     yg.append(ydec[:steps_dec, bi:bi + 1, h:h + 1].transpose(0, 1).double().cpu().numpy())
@@ -265,7 +276,7 @@ def main():
         "config": {"workload": cfg.label, "name": cfg.name, "batch": cfg.batch, "prefill_len": L,
                    "decode_steps": steps_dec, "heads": cfg.nheads, "groups": cfg.ngroups,
                    "headdim": cfg.headdim, "dstate": cfg.dstate, "rank": cfg.rank, "chunk": cfg.chunk,
-                   "io_dtype": cfg.io_dtype, "state_dtype": "fp32"},
+                   "io_dtype": cfg.io_dtype, "state_dtype": args.state_dtype},
         "prefill": {"ms": round(pre_avg, 4), "tokens_per_s": round(pre_tps, 1),
                     "alg_GB_per_s": round(pre_gbs, 1), "hbm_frac": round(pre_gbs / HBM_PEAK_GBS, 4),
                     "mfma_tflops": round(flops / (pre_avg / 1e3) / 1e12, 2),

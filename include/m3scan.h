@@ -34,7 +34,7 @@
  *   x, y   (batch, L, H, R, P)   io dtype       dt, lambda (batch, L, H) fp32
  *   A, D   (H)                   fp32           theta      (batch, L, G, N/2) fp32
  *   B, C   (batch, L, G, R, N)   io dtype       B[b,t,g,r,n] = (B_t)_{n,r}
- *   state h (batch, H, N, P) fp32 (true frame)
+ *   state h (batch, H, N, P) state dtype (fp32 by default; true frame)
  *   carry  b_last (batch, G, R, N), x_last (batch, H, R, P) io dtype
  *   Decode drops the L axis of every per-token tensor.
  *
@@ -68,7 +68,7 @@ typedef enum {
     M3_ERR_HIP = -4            /* a HIP launch or runtime call failed                 */
 } m3_status;
 
-typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype;   /* dtype of x, B, C, y and the carry */
+typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype;
 
 typedef struct {
     int64_t batch;     /* b                                   >= 1 */
@@ -79,11 +79,18 @@ typedef struct {
     int64_t dstate;    /* N, even                             >= 2 */
     int64_t rank;      /* R (1 = SISO)                        >= 1 */
     int64_t chunk;     /* Q, tokens per chunk; ignored by decode >= 1 */
-    int32_t io_dtype;  /* m3_dtype                                 */
+    int32_t io_dtype;     /* m3_dtype of x, B, C, y and the carry                   */
+    int32_t state_dtype;  /* m3_dtype of the state h; 0 = M3_F32.  With M3_BF16 the
+                             state is stored in bf16 (rounded to nearest even) and
+                             all arithmetic stays fp32: a decode step reads the bf16
+                             state, updates it in fp32 and writes it back rounded
+                             (half the state bytes of fp32); a prefill reads
+                             state_in and writes state_out in bf16.              */
 } m3_dims;
 
 typedef struct {
-    float* h;          /* (batch, H, N, P) fp32: the state after the last token        */
+    void* h;           /* (batch, H, N, P) in dims->state_dtype: the state after the
+                          last token                                                  */
     void* b_last;      /* (batch, G, R, N) io dtype: B of the last token (the carry)    */
     void* x_last;      /* (batch, H, R, P) io dtype: X of the last token (the carry)    */
 } m3_state;
@@ -114,8 +121,10 @@ m3_status m3_prefill_chunked(const m3_dims* dims, const void* x, const float* dt
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * One decode step for every (b, h): reads the fp32 state h in place, applies
- * one token and writes the new state back to h, and writes y_t (batch, H, R, P).
+ * One decode step for every (b, h): reads the state h (dims->state_dtype) in
+ * place, applies one token in fp32 and writes the new state back to h, and
+ * writes y_t (batch, H, R, P).  y_t reads the new state before it is rounded to
+ * a bf16 state.
  *
  * b_last, x_last: B and X of the previous token (the trapezoid carry), in the
  *            io dtype; both NULL means a zero previous input.  They are only
@@ -125,7 +134,7 @@ m3_status m3_prefill_chunked(const m3_dims* dims, const void* x, const float* dt
  * Per-token inputs: x_t (b,H,R,P), dt_t, lambda_t (b,H), theta_t (b,G,N/2),
  *            B_t, C_t (b,G,R,N).  dims->seqlen and dims->chunk are ignored.
  */
-m3_status m3_decode_step(const m3_dims* dims, float* h, const void* b_last,
+m3_status m3_decode_step(const m3_dims* dims, void* h, const void* b_last,
                          const void* x_last, const void* x_t, const float* dt_t,
                          const float* A, const float* lambda_t, const float* theta_t,
                          const void* B_t, const void* C_t, const float* D, void* y_t,

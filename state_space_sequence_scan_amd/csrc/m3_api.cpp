@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int32_t kVersion = 100;  // 0.1.0
+constexpr int32_t kVersion = 101;  // 0.1.1: state dtype
 constexpr size_t kMaxLds = 160 * 1024;
 
 bool dims_ok(const m3_dims* d, bool prefill) {
@@ -19,6 +19,7 @@ bool dims_ok(const m3_dims* d, bool prefill) {
     if (prefill && (d->seqlen < 0 || d->chunk < 1)) return false;
     if (d->dstate % 2 != 0 || d->nheads % d->ngroups != 0) return false;
     if (d->io_dtype != M3_F32 && d->io_dtype != M3_BF16) return false;
+    if (d->state_dtype != M3_F32 && d->state_dtype != M3_BF16) return false;
     // Index arithmetic inside the kernels is 32-bit for per-slice sizes.
     if (d->headdim > 4096 || d->dstate > 4096 || d->rank > 64 || d->nheads > (1 << 20)) return false;
     if (prefill && d->chunk > 4096) return false;
@@ -36,6 +37,7 @@ m3::PrefillArgs make_prefill_args(const m3_dims* d) {
     a.R = static_cast<int>(d->rank);
     a.Q = static_cast<int>(d->chunk);
     a.bf16 = d->io_dtype == M3_BF16;
+    a.state_bf16 = d->state_dtype == M3_BF16;
     return a;
 }
 
@@ -144,7 +146,7 @@ m3_status m3_prefill_chunked(const m3_dims* dims, const void* x, const float* dt
     return e == hipSuccess ? M3_OK : M3_ERR_HIP;
 }
 
-m3_status m3_decode_step(const m3_dims* dims, float* h, const void* b_last, const void* x_last,
+m3_status m3_decode_step(const m3_dims* dims, void* h, const void* b_last, const void* x_last,
                          const void* x_t, const float* dt_t, const float* A,
                          const float* lambda_t, const float* theta_t, const void* B_t,
                          const void* C_t, const float* D, void* y_t, void* stream) {
@@ -173,6 +175,7 @@ m3_status m3_decode_step(const m3_dims* dims, float* h, const void* b_last, cons
     a.R = static_cast<int>(dims->rank);
     a.has_carry = b_last != nullptr;
     a.bf16 = dims->io_dtype == M3_BF16;
+    a.state_bf16 = dims->state_dtype == M3_BF16;
     if (dims->batch * dims->nheads > 0x7fffffffLL) return M3_ERR_UNSUPPORTED;
     if (!m3::decode_supported(a)) return M3_ERR_UNSUPPORTED;
     const hipError_t e = m3::launch_decode(a, static_cast<hipStream_t>(stream));

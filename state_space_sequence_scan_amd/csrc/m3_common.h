@@ -34,6 +34,45 @@ template <> struct io<bf16_t> {
     __device__ __forceinline__ static void store(bf16_t* p, float v) { p->bits = f32_to_bf16(v); }
 };
 
+// One state element of a state stored in fp32 or bf16 (chosen at run time).
+__device__ __forceinline__ float state_load(const void* p, size_t i, bool bf16) {
+    return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
+}
+__device__ __forceinline__ void state_store(void* p, size_t i, float v, bool bf16) {
+    if (bf16)
+        static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
+    else
+        static_cast<float*>(p)[i] = v;
+}
+
+// Four consecutive state values: fp32 (16 bytes) or bf16 (8 bytes, rounded to
+// nearest even on store), streamed with non-temporal accesses.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+template <typename S> struct state4;
+template <> struct state4<float> {
+    __device__ __forceinline__ static f32x4_t load(const float* p) {
+        return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    }
+    __device__ __forceinline__ static void store(float* p, f32x4_t v) {
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
+    }
+};
+template <> struct state4<bf16_t> {
+    __device__ __forceinline__ static f32x4_t load(const bf16_t* p) {
+        const u32x2_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+        return f32x4_t{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+    }
+    __device__ __forceinline__ static void store(bf16_t* p, f32x4_t v) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 lo = {static_cast<__bf16>(v.x), static_cast<__bf16>(v.y)};
+        const bf16x2 hi = {static_cast<__bf16>(v.z), static_cast<__bf16>(v.w)};
+        const u32x2_t w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(p));
+    }
+};
+
 // Accurate sin/cos of an angle of any size (chunk-local angle sums can reach
 // hundreds of radians); the HIP library routine does the range reduction.
 __device__ __forceinline__ void sincos_acc(float a, float* s, float* c) { sincosf(a, s, c); }

@@ -20,22 +20,58 @@ namespace m3 {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// CW consecutive state values of one row: 16 bytes for CW = 4 fp32 or CW = 8 bf16
+// (8 bytes for CW = 4 bf16), streamed with non-temporal accesses.
+template <typename S, int CW> struct state_vec;
+template <> struct state_vec<float, 4> {
+    typedef float V __attribute__((ext_vector_type(4)));
+    __device__ __forceinline__ static V load(const float* p) { return state4<float>::load(p); }
+    __device__ __forceinline__ static void store(float* p, V v) { state4<float>::store(p, v); }
+};
+template <> struct state_vec<bf16_t, 4> {
+    typedef float V __attribute__((ext_vector_type(4)));
+    __device__ __forceinline__ static V load(const bf16_t* p) { return state4<bf16_t>::load(p); }
+    __device__ __forceinline__ static void store(bf16_t* p, V v) { state4<bf16_t>::store(p, v); }
+};
+template <> struct state_vec<bf16_t, 8> {
+    typedef float V __attribute__((ext_vector_type(8)));
+    typedef uint32_t W __attribute__((ext_vector_type(4)));
+    __device__ __forceinline__ static V load(const bf16_t* p) {
+        const W w = __builtin_nontemporal_load(reinterpret_cast<const W*>(p));
+        return V{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                 __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u),
+                 __uint_as_float(w.z << 16), __uint_as_float(w.z & 0xffff0000u),
+                 __uint_as_float(w.w << 16), __uint_as_float(w.w & 0xffff0000u)};
+    }
+    __device__ __forceinline__ static void store(bf16_t* p, V v) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 a = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1])};
+        const bf16x2 b = {static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])};
+        const bf16x2 c = {static_cast<__bf16>(v[4]), static_cast<__bf16>(v[5])};
+        const bf16x2 d = {static_cast<__bf16>(v[6]), static_cast<__bf16>(v[7])};
+        const W w = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                     __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
+        __builtin_nontemporal_store(w, reinterpret_cast<W*>(p));
+    }
+};
+
 // Fast path.  One workgroup of NT threads per (b, h).  Thread tid owns the
-// 4-column block c = tid % PC (PC = P/4) and the rotation pairs
-// k = kk + TPG * j (kk = tid / PC, j < PPT), i.e. 2 * PPT state rows x 4 columns.
-template <typename T, int N, int P, int R, int NT>
+// CW-column block c = tid % PC (PC = P/CW) and the rotation pairs
+// k = kk + TPG * j (kk = tid / PC, j < PPT), i.e. 2 * PPT state rows x CW columns.
+template <typename T, typename S, int N, int P, int R, int NT, int CW>
 __global__ __launch_bounds__(NT) void decode_fast(
-    float* __restrict__ h, const T* __restrict__ b_last, const T* __restrict__ x_last,
+    S* __restrict__ h, const T* __restrict__ b_last, const T* __restrict__ x_last,
     const T* __restrict__ x_t, const float* __restrict__ dt_t, const float* __restrict__ A,
     const float* __restrict__ lam_t, const float* __restrict__ theta_t,
     const T* __restrict__ B_t, const T* __restrict__ C_t, const float* __restrict__ D,
     T* __restrict__ y_t, int H, int G, int has_carry) {
     constexpr int KP = N / 2;
-    constexpr int PC = P / 4;
+    constexpr int PC = P / CW;
     constexpr int TPG = NT / PC;
     constexpr int PPT = KP / TPG;
     constexpr int NW = (NT + 63) / 64;
-    static_assert(P % 4 == 0 && NT % PC == 0 && KP % TPG == 0 && PPT >= 1, "decode tiling");
+    static_assert(P % CW == 0 && NT % PC == 0 && KP % TPG == 0 && PPT >= 1, "decode tiling");
+    typedef typename state_vec<S, CW>::V fvec;
 
     const int bh = blockIdx.x;
     const int b = bh / H, hh = bh - b * H;
@@ -45,8 +81,8 @@ __global__ __launch_bounds__(NT) void decode_fast(
     const int kk = tid / PC;
 
     __shared__ float sB[R][N], sC[R][N], sBp[R][N];
-    __shared__ __align__(16) float sX[R][P];
-    __shared__ __align__(16) float sXp[R][P];
+    __shared__ __align__(32) float sX[R][P];
+    __shared__ __align__(32) float sXp[R][P];
     __shared__ float sCs[KP], sSn[KP];
 
     // The small per-token operands are loaded into registers first and written to
@@ -83,13 +119,13 @@ __global__ __launch_bounds__(NT) void decode_fast(
         vth[e] = (k < KP) ? theta_t[(static_cast<size_t>(b) * G + g) * KP + k] : 0.f;
     }
 
-    float* hp = h + static_cast<size_t>(bh) * N * P;
-    f32x4 s0[PPT], s1[PPT];
+    S* hp = h + static_cast<size_t>(bh) * N * P;
+    fvec s0[PPT], s1[PPT];
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
         const int k = kk + TPG * j;
-        s0[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(hp + (2 * k) * P) + c);
-        s1[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(hp + (2 * k + 1) * P) + c);
+        s0[j] = state_vec<S, CW>::load(hp + (2 * k) * P + CW * c);
+        s1[j] = state_vec<S, CW>::load(hp + (2 * k + 1) * P + CW * c);
     }
 
 #pragma unroll
@@ -126,21 +162,21 @@ __global__ __launch_bounds__(NT) void decode_fast(
     const float c2 = lv * dtv;           // gamma
     __syncthreads();
 
-    f32x4 xv[R], xpv[R];
+    fvec xv[R], xpv[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        xv[r] = reinterpret_cast<const f32x4*>(sX[r])[c];
-        xpv[r] = reinterpret_cast<const f32x4*>(sXp[r])[c];
+        xv[r] = reinterpret_cast<const fvec*>(sX[r])[c];
+        xpv[r] = reinterpret_cast<const fvec*>(sXp[r])[c];
     }
-    f32x4 yacc[R];
+    fvec yacc[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) yacc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < R; ++r) yacc[r] = fvec(0.f);
 
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
         const int k = kk + TPG * j;
         const float cs = sCs[k], sn = sSn[k];
-        f32x4 up0 = {0.f, 0.f, 0.f, 0.f}, up1 = up0, u0 = up0, u1 = up0;
+        fvec up0 = fvec(0.f), up1 = up0, u0 = up0, u1 = up0;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             up0 += sBp[r][2 * k] * xpv[r];
@@ -148,12 +184,12 @@ __global__ __launch_bounds__(NT) void decode_fast(
             u0 += sB[r][2 * k] * xv[r];
             u1 += sB[r][2 * k + 1] * xv[r];
         }
-        const f32x4 v0 = s0[j] + c1 * up0;
-        const f32x4 v1 = s1[j] + c1 * up1;
-        const f32x4 n0 = alpha * (cs * v0 - sn * v1) + c2 * u0;
-        const f32x4 n1 = alpha * (sn * v0 + cs * v1) + c2 * u1;
-        __builtin_nontemporal_store(n0, reinterpret_cast<f32x4*>(hp + (2 * k) * P) + c);
-        __builtin_nontemporal_store(n1, reinterpret_cast<f32x4*>(hp + (2 * k + 1) * P) + c);
+        const fvec v0 = s0[j] + c1 * up0;
+        const fvec v1 = s1[j] + c1 * up1;
+        const fvec n0 = alpha * (cs * v0 - sn * v1) + c2 * u0;
+        const fvec n1 = alpha * (sn * v0 + cs * v1) + c2 * u1;
+        state_vec<S, CW>::store(hp + (2 * k) * P + CW * c, n0);
+        state_vec<S, CW>::store(hp + (2 * k + 1) * P + CW * c, n1);
 #pragma unroll
         for (int r = 0; r < R; ++r) yacc[r] += sC[r][2 * k] * n0 + sC[r][2 * k + 1] * n1;
     }
@@ -165,13 +201,13 @@ __global__ __launch_bounds__(NT) void decode_fast(
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) yacc[r][q] += __shfl_xor(yacc[r][q], off);
+            for (int q = 0; q < CW; ++q) yacc[r][q] += __shfl_xor(yacc[r][q], off);
     }
-    __shared__ __align__(16) float sY[NW][R][P];
+    __shared__ __align__(32) float sY[NW][R][P];
     const int lane = tid & 63, wave = tid >> 6;
     if (lane < PC) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) reinterpret_cast<f32x4*>(sY[wave][r])[c] = yacc[r];
+        for (int r = 0; r < R; ++r) reinterpret_cast<fvec*>(sY[wave][r])[c] = yacc[r];
     }
     __syncthreads();
     const float dv = D[hh];
@@ -185,9 +221,9 @@ __global__ __launch_bounds__(NT) void decode_fast(
 
 // Any shape: one workgroup per (b, h); each thread owns whole state columns p and
 // walks the N/2 rotation pairs of that column.  R <= kMaxRankGeneric.
-template <typename T>
+template <typename T, typename S>
 __global__ __launch_bounds__(64) void decode_generic(
-    float* __restrict__ h, const T* __restrict__ b_last, const T* __restrict__ x_last,
+    S* __restrict__ h, const T* __restrict__ b_last, const T* __restrict__ x_last,
     const T* __restrict__ x_t, const float* __restrict__ dt_t, const float* __restrict__ A,
     const float* __restrict__ lam_t, const float* __restrict__ theta_t,
     const T* __restrict__ B_t, const T* __restrict__ C_t, const float* __restrict__ D,
@@ -227,7 +263,7 @@ __global__ __launch_bounds__(64) void decode_generic(
     const float dtv = dt_t[bh], lv = lam_t[bh];
     const float alpha = __expf(dtv * A[hh]);
     const float c1 = (1.f - lv) * dtv, c2 = lv * dtv;
-    float* hp = h + static_cast<size_t>(bh) * N * P;
+    S* hp = h + static_cast<size_t>(bh) * N * P;
     for (int p = tid; p < P; p += blockDim.x) {
         float yacc[kMaxRankGeneric];
         for (int r = 0; r < R; ++r) yacc[r] = 0.f;
@@ -239,12 +275,12 @@ __global__ __launch_bounds__(64) void decode_generic(
                 u0 += sB[r * N + 2 * k] * sX[r * P + p];
                 u1 += sB[r * N + 2 * k + 1] * sX[r * P + p];
             }
-            const float v0 = hp[(2 * k) * P + p] + c1 * up0;
-            const float v1 = hp[(2 * k + 1) * P + p] + c1 * up1;
+            const float v0 = io<S>::load(hp + (2 * k) * P + p) + c1 * up0;
+            const float v1 = io<S>::load(hp + (2 * k + 1) * P + p) + c1 * up1;
             const float n0 = alpha * (sCs[k] * v0 - sSn[k] * v1) + c2 * u0;
             const float n1 = alpha * (sSn[k] * v0 + sCs[k] * v1) + c2 * u1;
-            hp[(2 * k) * P + p] = n0;
-            hp[(2 * k + 1) * P + p] = n1;
+            io<S>::store(hp + (2 * k) * P + p, n0);
+            io<S>::store(hp + (2 * k + 1) * P + p, n1);
             for (int r = 0; r < R; ++r) yacc[r] += sC[r * N + 2 * k] * n0 + sC[r * N + 2 * k + 1] * n1;
         }
         for (int r = 0; r < R; ++r)
@@ -252,10 +288,13 @@ __global__ __launch_bounds__(64) void decode_generic(
     }
 }
 
-template <typename T, int N, int P, int R, int NT>
+// Four columns per thread for either state dtype.  (Eight bf16 columns, for 16-byte
+// accesses, measured slower at N = 128, P = 64, R = 4: with half the state bytes the
+// step is limited by its fp32 arithmetic, and fewer rows per thread are in flight.)
+template <typename T, typename S, int N, int P, int R, int NT, int CW = 4>
 static hipError_t launch_fast(const DecodeArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((decode_fast<T, N, P, R, NT>), dim3(static_cast<unsigned>(a.batch * a.H)),
-                       dim3(NT), 0, st, a.h, static_cast<const T*>(a.b_last),
+    hipLaunchKernelGGL((decode_fast<T, S, N, P, R, NT, CW>), dim3(static_cast<unsigned>(a.batch * a.H)),
+                       dim3(NT), 0, st, static_cast<S*>(a.h), static_cast<const T*>(a.b_last),
                        static_cast<const T*>(a.x_last), static_cast<const T*>(a.x_t), a.dt_t, a.A,
                        a.lam_t, a.theta_t, static_cast<const T*>(a.B_t),
                        static_cast<const T*>(a.C_t), a.D, static_cast<T*>(a.y_t), a.H, a.G,
@@ -263,20 +302,20 @@ static hipError_t launch_fast(const DecodeArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, typename S>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
     if (a.N == 128 && a.P == 64) {
         switch (a.R) {
-            case 1: return launch_fast<T, 128, 64, 1, 256>(a, st);
-            case 2: return launch_fast<T, 128, 64, 2, 256>(a, st);
-            case 4: return launch_fast<T, 128, 64, 4, 256>(a, st);
+            case 1: return launch_fast<T, S, 128, 64, 1, 256>(a, st);
+            case 2: return launch_fast<T, S, 128, 64, 2, 256>(a, st);
+            case 4: return launch_fast<T, S, 128, 64, 4, 256>(a, st);
             default: break;
         }
     }
-    if (a.N == 16 && a.P == 16 && a.R == 1) return launch_fast<T, 16, 16, 1, 32>(a, st);
+    if (a.N == 16 && a.P == 16 && a.R == 1) return launch_fast<T, S, 16, 16, 1, 32>(a, st);
     const size_t shm = sizeof(float) * (3 * a.R * a.N + 2 * a.R * a.P + a.N);
-    hipLaunchKernelGGL(decode_generic<T>, dim3(static_cast<unsigned>(a.batch * a.H)), dim3(64),
-                       shm, st, a.h, static_cast<const T*>(a.b_last),
+    hipLaunchKernelGGL((decode_generic<T, S>), dim3(static_cast<unsigned>(a.batch * a.H)), dim3(64),
+                       shm, st, static_cast<S*>(a.h), static_cast<const T*>(a.b_last),
                        static_cast<const T*>(a.x_last), static_cast<const T*>(a.x_t), a.dt_t, a.A,
                        a.lam_t, a.theta_t, static_cast<const T*>(a.B_t),
                        static_cast<const T*>(a.C_t), a.D, static_cast<T*>(a.y_t), a.H, a.G,
@@ -291,7 +330,9 @@ bool decode_supported(const DecodeArgs& a) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-    return a.bf16 ? launch_decode_t<bf16_t>(a, st) : launch_decode_t<float>(a, st);
+    if (a.state_bf16)
+        return a.bf16 ? launch_decode_t<bf16_t, bf16_t>(a, st) : launch_decode_t<float, bf16_t>(a, st);
+    return a.bf16 ? launch_decode_t<bf16_t, float>(a, st) : launch_decode_t<float, float>(a, st);
 }
 
 }  // namespace m3

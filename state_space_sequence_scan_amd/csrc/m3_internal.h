@@ -10,7 +10,7 @@ namespace m3 {
 constexpr int kMaxRankGeneric = 8;
 
 struct DecodeArgs {
-    float* h;
+    void* h;                 // state, fp32 or bf16 (state_bf16)
     const void* b_last;
     const void* x_last;
     const void* x_t;
@@ -24,7 +24,8 @@ struct DecodeArgs {
     void* y_t;
     int batch, H, G, N, P, R;
     int has_carry;
-    bool bf16;
+    bool bf16;               // io dtype
+    bool state_bf16;         // state dtype
 };
 
 bool decode_supported(const DecodeArgs& a);
@@ -39,18 +40,19 @@ struct PrefillArgs {
     const void* B;
     const void* C;
     const float* D;
-    const float* h_in;       // may be null (zero state)
+    const void* h_in;        // may be null (zero state); fp32 or bf16 (state_bf16)
     const void* bl_in;       // carry in, may be null (with xl_in)
     const void* xl_in;
     void* y;
-    float* h_out;            // may be null
+    void* h_out;             // may be null; fp32 or bf16 (state_bf16)
     void* bl_out;            // may be null
     void* xl_out;            // may be null
     void* workspace;
     size_t workspace_bytes;
     int64_t batch, L;
     int H, G, N, P, R, Q;
-    bool bf16;
+    bool bf16;               // io dtype
+    bool state_bf16;         // state dtype
 };
 
 // Which kernel family runs a prefill, and the workspace it needs.

@@ -28,9 +28,9 @@ template <typename T>
 __global__ __launch_bounds__(256) void prefill_generic(
     const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
     const float* __restrict__ lam, const float* __restrict__ theta, const T* __restrict__ B,
-    const T* __restrict__ C, const float* __restrict__ Dv, const float* __restrict__ h_in,
+    const T* __restrict__ C, const float* __restrict__ Dv, const void* __restrict__ h_in,
     const T* __restrict__ bl_in, const T* __restrict__ xl_in, T* __restrict__ y,
-    float* __restrict__ h_out, int64_t L, int H, int G, int N, int P, int R, int Q) {
+    void* __restrict__ h_out, int64_t L, int H, int G, int N, int P, int R, int Q, int state_bf16) {
     extern __shared__ float smem[];
     const int KP = N / 2, QR = Q * R;
     float* S = smem;                       // N*P
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void prefill_generic(
                                  : 0.f;
     for (int idx = tid; idx < N * P; idx += NT) {
         const int n = idx / P, p = idx - n * P;
-        float s = h_in ? h_in[static_cast<size_t>(bh) * N * P + idx] : 0.f;
+        float s = h_in ? state_load(h_in, static_cast<size_t>(bh) * N * P + idx, state_bf16) : 0.f;
         if (carry) {
             float u = 0.f;
             for (int r = 0; r < R; ++r)
@@ -195,7 +195,8 @@ __global__ __launch_bounds__(256) void prefill_generic(
     }
     __syncthreads();
     if (h_out)
-        for (int idx = tid; idx < N * P; idx += NT) h_out[static_cast<size_t>(bh) * N * P + idx] = S[idx];
+        for (int idx = tid; idx < N * P; idx += NT)
+            state_store(h_out, static_cast<size_t>(bh) * N * P + idx, S[idx], state_bf16);
 }
 
 // state_out carry: B and X of the last token (or the incoming carry when L == 0).
@@ -245,7 +246,8 @@ static hipError_t launch_generic_t(const PrefillArgs& a, hipStream_t st) {
                        st, static_cast<const T*>(a.x), a.dt, a.A, a.lam, a.theta,
                        static_cast<const T*>(a.B), static_cast<const T*>(a.C), a.D, a.h_in,
                        static_cast<const T*>(a.bl_in), static_cast<const T*>(a.xl_in),
-                       static_cast<T*>(a.y), a.h_out, a.L, a.H, a.G, a.N, a.P, a.R, a.Q);
+                       static_cast<T*>(a.y), a.h_out, a.L, a.H, a.G, a.N, a.P, a.R, a.Q,
+                       a.state_bf16 ? 1 : 0);
     return hipGetLastError();
 }
 

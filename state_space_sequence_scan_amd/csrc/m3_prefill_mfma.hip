@@ -205,22 +205,24 @@ struct ScanParams {
     uint16_t* y;            // (b, L, H, R, P) bf16
     uint16_t* y_sink;       // 64 x 64 bf16 scratch: stores of rows past the sequence end land here
     const float* s_init;    // state entering segment s: (b, H, nseg, N, P) fp32, or null
-    const float* h_in;      // used when s_init is null (nseg == 1): (b, H, N, P), may be null
+    const void* h_in;       // used when s_init is null (nseg == 1): (b, H, N, P), may be null
     const uint16_t* bl_in;  // carry in (b, G, R, N), may be null
     const uint16_t* xl_in;  // carry in (b, H, R, P), may be null
-    float* h_out;           // final state (b, H, N, P), may be null
+    void* h_out;            // final state (b, H, N, P), may be null
     float* seg_state;       // state-only mode: (b, H, nseg-1, N, P)
     float* seg_decay;       // state-only mode: (b, H, nseg-1)
     float* seg_rot;         // state-only mode: (b, H, nseg-1, KP, 2)
     int64_t L;
     int H, G, nchunks, nseg, chunks_per_seg;
+    int state_bf16;         // h_in and h_out hold bf16 (else fp32)
 };
 
 // Initial state of segment 0 when no segment pass ran: h_in plus the beta term
 // the first token gives the carried previous input.
 template <int R>
 __device__ float initial_state(const ScanParams& p, int b, int h, int g, int n, int col, float c1) {
-    float s = p.h_in ? p.h_in[(static_cast<size_t>(b) * p.H + h) * N * P + n * P + col] : 0.f;
+    float s = p.h_in ? state_load(p.h_in, (static_cast<size_t>(b) * p.H + h) * N * P + n * P + col, p.state_bf16)
+                     : 0.f;
     if (p.bl_in && p.xl_in) {
         float u = 0.f;
 #pragma unroll
@@ -788,7 +790,7 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
     // epilogue
     if (FULL) {
         if (last_seg && p.h_out) {
-            float* ho = p.h_out + (static_cast<size_t>(b) * p.H + h) * N * P;
+            const size_t ho = (static_cast<size_t>(b) * p.H + h) * N * P;
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -796,7 +798,7 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int n = n0 + 16 * rt + 4 * lg + i, col = p0 + 16 * ct + l16;
-                        ho[n * P + col] = sacc[rt][ct][i];
+                        state_store(p.h_out, ho + n * P + col, sacc[rt][ct][i], p.state_bf16);
                     }
         }
     } else {
@@ -944,6 +946,7 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
     p.y = static_cast<uint16_t*>(a.y);
     p.y_sink = reinterpret_cast<uint16_t*>(base + ws.sink);
     p.h_in = a.h_in;
+    p.state_bf16 = a.state_bf16 ? 1 : 0;
     p.bl_in = static_cast<const uint16_t*>(a.bl_in);
     p.xl_in = static_cast<const uint16_t*>(a.xl_in);
     p.h_out = a.h_out;

@@ -6,7 +6,7 @@ is missing or a call fails, these functions raise.
 
 Layouts are those of include/m3scan.h (contiguous, last index fastest):
   x, y (b, L, H, R, P)   dt, lam (b, L, H)   A, D (H,)   theta (b, L, G, N/2)
-  B, C (b, L, G, R, N)   state h (b, H, N, P) fp32
+  B, C (b, L, G, R, N)   state h (b, H, N, P) fp32 or bf16 (the state dtype)
 """
 from __future__ import annotations
 
@@ -29,7 +29,8 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape or dtype",
 class Dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
                 ("ngroups", ctypes.c_int64), ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64),
-                ("rank", ctypes.c_int64), ("chunk", ctypes.c_int64), ("io_dtype", ctypes.c_int32)]
+                ("rank", ctypes.c_int64), ("chunk", ctypes.c_int64), ("io_dtype", ctypes.c_int32),
+                ("state_dtype", ctypes.c_int32)]
 
 
 class State(ctypes.Structure):
@@ -90,15 +91,17 @@ def _stream(device) -> ctypes.c_void_p:
 
 @dataclasses.dataclass
 class DecodeState:
-    """Scan state: h (b,H,N,P) fp32, and the previous token's B (b,G,R,N) and
+    """Scan state: h (b,H,N,P) in fp32 or bf16 (its dtype is the state dtype of
+    every call that reads or writes it), and the previous token's B (b,G,R,N) and
     X (b,H,R,P) in the io dtype (the trapezoid carry; None = zero)."""
     h: torch.Tensor
     b_last: Optional[torch.Tensor] = None
     x_last: Optional[torch.Tensor] = None
 
 
-def make_dims(batch, seqlen, nheads, ngroups, headdim, dstate, rank, chunk, io_dtype) -> Dims:
-    return Dims(batch, seqlen, nheads, ngroups, headdim, dstate, rank, chunk, io_dtype)
+def make_dims(batch, seqlen, nheads, ngroups, headdim, dstate, rank, chunk, io_dtype,
+              state_dtype: int = M3_F32) -> Dims:
+    return Dims(batch, seqlen, nheads, ngroups, headdim, dstate, rank, chunk, io_dtype, state_dtype)
 
 
 def workspace_size(dims: Dims) -> int:
@@ -111,8 +114,11 @@ def workspace_size(dims: Dims) -> int:
 
 def prefill(x, dt, A, lam, theta, B, C, D, chunk: int, state_in: Optional[DecodeState] = None,
             out_state: bool = True, y: Optional[torch.Tensor] = None,
-            workspace: Optional[torch.Tensor] = None):
-    """Chunked prefill.  Returns (y, DecodeState or None)."""
+            workspace: Optional[torch.Tensor] = None, state_dtype: Optional[torch.dtype] = None):
+    """Chunked prefill.  Returns (y, DecodeState or None).
+
+    state_dtype: dtype of the state read (state_in.h) and written (the returned
+    h): torch.float32 or torch.bfloat16; default that of state_in.h, else fp32."""
     b, L, H, R, P = x.shape
     G, N = B.shape[2], B.shape[4]
     dev = x.device
@@ -127,14 +133,18 @@ def prefill(x, dt, A, lam, theta, B, C, D, chunk: int, state_in: Optional[Decode
     _check(theta, "theta", (b, L, G, N // 2), torch.float32, dev)
     _check(B, "B", (b, L, G, R, N), io, dev)
     _check(C, "C", (b, L, G, R, N), io, dev)
-    dims = make_dims(b, L, H, G, P, N, R, chunk, _IO[io])
+    if state_dtype is None:
+        state_dtype = state_in.h.dtype if state_in is not None else torch.float32
+    if state_dtype not in _IO:
+        raise ValueError(f"state dtype {state_dtype} not supported (fp32 or bf16)")
+    dims = make_dims(b, L, H, G, P, N, R, chunk, _IO[io], _IO[state_dtype])
     if y is None:
         y = torch.empty_like(x)
     else:
         _check(y, "y", x.shape, io, dev)
     sin = None
     if state_in is not None:
-        _check(state_in.h, "state_in.h", (b, H, N, P), torch.float32, dev)
+        _check(state_in.h, "state_in.h", (b, H, N, P), state_dtype, dev)
         if state_in.b_last is not None:
             _check(state_in.b_last, "state_in.b_last", (b, G, R, N), io, dev)
             _check(state_in.x_last, "state_in.x_last", (b, H, R, P), io, dev)
@@ -143,7 +153,7 @@ def prefill(x, dt, A, lam, theta, B, C, D, chunk: int, state_in: Optional[Decode
                     None if state_in.x_last is None else state_in.x_last.data_ptr())
     sout = st = None
     if out_state:
-        st = DecodeState(torch.empty((b, H, N, P), dtype=torch.float32, device=dev),
+        st = DecodeState(torch.empty((b, H, N, P), dtype=state_dtype, device=dev),
                          torch.empty((b, G, R, N), dtype=io, device=dev),
                          torch.empty((b, H, R, P), dtype=io, device=dev))
         sout = State(st.h.data_ptr(), st.b_last.data_ptr(), st.x_last.data_ptr())
@@ -172,7 +182,9 @@ def decode_step(state: DecodeState, x_t, dt_t, A, lam_t, theta_t, B_t, C_t, D,
     dev, io = x_t.device, x_t.dtype
     if io not in _IO:
         raise ValueError(f"x_t dtype {io} not supported (fp32 or bf16)")
-    _check(state.h, "state.h", (b, H, N, P), torch.float32, dev)
+    if state.h.dtype not in _IO:
+        raise ValueError(f"state.h dtype {state.h.dtype} not supported (fp32 or bf16)")
+    _check(state.h, "state.h", (b, H, N, P), state.h.dtype, dev)
     _check(x_t, "x_t", (b, H, R, P), io, dev)
     _check(dt_t, "dt_t", (b, H), torch.float32, dev)
     _check(lam_t, "lam_t", (b, H), torch.float32, dev)
@@ -186,7 +198,7 @@ def decode_step(state: DecodeState, x_t, dt_t, A, lam_t, theta_t, B_t, C_t, D,
         _check(state.x_last, "state.x_last", (b, H, R, P), io, dev)
     if y_t is None:
         y_t = torch.empty_like(x_t)
-    dims = make_dims(b, 1, H, G, P, N, R, 1, _IO[io])
+    dims = make_dims(b, 1, H, G, P, N, R, 1, _IO[io], _IO[state.h.dtype])
     rc = lib().m3_decode_step(ctypes.byref(dims), _p(state.h), _p(state.b_last), _p(state.x_last),
                               _p(x_t), _p(dt_t), _p(A), _p(lam_t), _p(theta_t), _p(B_t), _p(C_t),
                               _p(D), _p(y_t), _stream(dev))

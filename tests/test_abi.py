@@ -56,7 +56,7 @@ def _dims(**kw):
 
 
 BAD_DIMS = [dict(batch=0), dict(seqlen=-1), dict(nheads=0), dict(ngroups=3), dict(dstate=15),
-            dict(headdim=0), dict(rank=0), dict(chunk=0), dict(io_dtype=7)]
+            dict(headdim=0), dict(rank=0), dict(chunk=0), dict(io_dtype=7), dict(state_dtype=5)]
 
 
 @pytest.mark.parametrize("kw", BAD_DIMS, ids=lambda k: next(iter(k)))
@@ -71,6 +71,10 @@ def test_workspace_size_ok(lib):
     n = ctypes.c_size_t(123)
     assert lib.m3_prefill_workspace_size(ctypes.byref(_dims()), ctypes.byref(n)) == 0
     assert n.value >= 0
+    d = _dims(state_dtype=m3scan.M3_BF16)       # bf16 state: accepted, same workspace
+    m = ctypes.c_size_t(123)
+    assert lib.m3_prefill_workspace_size(ctypes.byref(d), ctypes.byref(m)) == 0
+    assert m.value == n.value
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails its checks first
