@@ -121,6 +121,35 @@ m3_status m3_prefill_chunked(const m3_dims* dims, const void* x, const float* dt
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Chunked prefill of a packed batch of variable-length sequences.  Sequence s
+ * is tokens cu_seqlens[s] .. cu_seqlens[s+1]-1 of one token axis of
+ * total_tokens tokens; its scan starts afresh there (from state_in's slice s,
+ * else from a zero state and a zero previous input), exactly as if it were run
+ * alone through m3_prefill_chunked with batch 1.  The chunks of a sequence start
+ * at its first token.
+ *
+ * dims:       batch = number of sequences; seqlen = an upper bound on every
+ *             sequence's length (it sizes the launch and the workspace:
+ *             m3_prefill_workspace_size(dims) covers this call too); the other
+ *             fields as for m3_prefill_chunked.
+ * cu_seqlens: device array of batch + 1 int64 offsets, non-decreasing, from 0
+ *             to total_tokens.  It is read only by the kernels, so it is not
+ *             checked here: offsets outside [0, total_tokens], decreasing ones
+ *             or lengths above seqlen are clamped to those bounds (wrong results
+ *             for such a sequence, never an access outside the arrays).
+ * Layouts:    x, y (total_tokens, H, R, P); dt, lambda (total_tokens, H);
+ *             theta (total_tokens, G, N/2); B, C (total_tokens, G, R, N);
+ *             state_in / state_out per sequence, as for m3_prefill_chunked.
+ * Errors:     as m3_prefill_chunked; also M3_ERR_INVALID_ARG for a NULL
+ *             cu_seqlens or total_tokens < 0.
+ */
+m3_status m3_prefill_varlen(const m3_dims* dims, const int64_t* cu_seqlens, int64_t total_tokens,
+                            const void* x, const float* dt, const float* A, const float* lambda,
+                            const float* theta, const void* B, const void* C, const float* D,
+                            const m3_state* state_in, m3_state* state_out, void* y,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One decode step for every (b, h): reads the state h (dims->state_dtype) in
  * place, applies one token in fp32 and writes the new state back to h, and
  * writes y_t (batch, H, R, P).  y_t reads the new state before it is rounded to

@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int32_t kVersion = 101;  // 0.1.1: state dtype
+constexpr int32_t kVersion = 102;  // 0.1.2: state dtype, packed variable-length prefill
 constexpr size_t kMaxLds = 160 * 1024;
 
 bool dims_ok(const m3_dims* d, bool prefill) {
@@ -38,6 +38,8 @@ m3::PrefillArgs make_prefill_args(const m3_dims* d) {
     a.Q = static_cast<int>(d->chunk);
     a.bf16 = d->io_dtype == M3_BF16;
     a.state_bf16 = d->state_dtype == M3_BF16;
+    a.cu = nullptr;
+    a.T = d->batch * d->seqlen;
     return a;
 }
 
@@ -104,20 +106,28 @@ m3_status m3_prefill_workspace_size(const m3_dims* dims, size_t* bytes) {
     return M3_OK;
 }
 
-m3_status m3_prefill_chunked(const m3_dims* dims, const void* x, const float* dt,
-                             const float* A, const float* lambda, const float* theta,
-                             const void* B, const void* C, const float* D,
-                             const m3_state* state_in, m3_state* state_out, void* y,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+m3_status prefill_common(const m3_dims* dims, const int64_t* cu, int64_t total_tokens, const void* x,
+                         const float* dt, const float* A, const float* lambda, const float* theta,
+                         const void* B, const void* C, const float* D, const m3_state* state_in,
+                         m3_state* state_out, void* y, void* workspace, size_t workspace_bytes,
+                         void* stream) {
     if (!dims_ok(dims, true)) return M3_ERR_INVALID_ARG;
     if (!A || !D) return M3_ERR_INVALID_ARG;
-    if (dims->seqlen > 0 && (!x || !dt || !lambda || !theta || !B || !C || !y))
-        return M3_ERR_INVALID_ARG;
+    const int64_t tokens = cu ? total_tokens : dims->batch * dims->seqlen;
+    if (tokens > 0 && (!x || !dt || !lambda || !theta || !B || !C || !y)) return M3_ERR_INVALID_ARG;
     if (state_in) {
         if (!state_in->h) return M3_ERR_INVALID_ARG;
         if ((state_in->b_last == nullptr) != (state_in->x_last == nullptr)) return M3_ERR_INVALID_ARG;
     }
     m3::PrefillArgs a = make_prefill_args(dims);
+    if (cu) {
+        a.cu = cu;
+        a.T = total_tokens;
+    }
     a.x = x;
     a.dt = dt;
     a.A = A;
@@ -144,6 +154,29 @@ m3_status m3_prefill_chunked(const m3_dims* dims, const void* x, const float* dt
     if (plan.workspace > 0 && (!workspace || workspace_bytes < plan.workspace)) return M3_ERR_WORKSPACE;
     const hipError_t e = m3::launch_prefill(a, plan, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+m3_status m3_prefill_chunked(const m3_dims* dims, const void* x, const float* dt,
+                             const float* A, const float* lambda, const float* theta,
+                             const void* B, const void* C, const float* D,
+                             const m3_state* state_in, m3_state* state_out, void* y,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_common(dims, nullptr, 0, x, dt, A, lambda, theta, B, C, D, state_in, state_out, y,
+                          workspace, workspace_bytes, stream);
+}
+
+m3_status m3_prefill_varlen(const m3_dims* dims, const int64_t* cu_seqlens, int64_t total_tokens,
+                            const void* x, const float* dt, const float* A, const float* lambda,
+                            const float* theta, const void* B, const void* C, const float* D,
+                            const m3_state* state_in, m3_state* state_out, void* y, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    if (!cu_seqlens || total_tokens < 0) return M3_ERR_INVALID_ARG;
+    return prefill_common(dims, cu_seqlens, total_tokens, x, dt, A, lambda, theta, B, C, D, state_in,
+                          state_out, y, workspace, workspace_bytes, stream);
 }
 
 m3_status m3_decode_step(const m3_dims* dims, void* h, const void* b_last, const void* x_last,

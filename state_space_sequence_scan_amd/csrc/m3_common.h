@@ -34,6 +34,22 @@ template <> struct io<bf16_t> {
     __device__ __forceinline__ static void store(bf16_t* p, float v) { p->bits = f32_to_bf16(v); }
 };
 
+// Token span of sequence b.  A packed variable-length batch gives the starts
+// (cu[b] .. cu[b+1]) in device memory; they are clamped to the T tokens present
+// and to at most L tokens (the maximum length the launch was sized for), so
+// that inconsistent offsets give wrong results but never an access out of
+// bounds.  Without offsets every sequence is L tokens starting at b * L.
+struct SeqSpan {
+    int64_t start, len;
+};
+__device__ __forceinline__ SeqSpan seq_span(const int64_t* cu, int64_t b, int64_t L, int64_t T) {
+    if (!cu) return SeqSpan{b * L, L};
+    int64_t s = cu[b], e = cu[b + 1];
+    s = s < 0 ? 0 : (s > T ? T : s);
+    e = e < s ? s : (e > T ? T : e);
+    return SeqSpan{s, e - s < L ? e - s : L};
+}
+
 // One state element of a state stored in fp32 or bf16 (chosen at run time).
 __device__ __forceinline__ float state_load(const void* p, size_t i, bool bf16) {
     return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];

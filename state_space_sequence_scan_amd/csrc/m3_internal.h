@@ -49,10 +49,12 @@ struct PrefillArgs {
     void* xl_out;            // may be null
     void* workspace;
     size_t workspace_bytes;
-    int64_t batch, L;
+    int64_t batch, L;        // sequences; their (maximum) length
     int H, G, N, P, R, Q;
     bool bf16;               // io dtype
     bool state_bf16;         // state dtype
+    const int64_t* cu;       // packed variable-length batch: sequence starts (batch + 1), device; else null
+    int64_t T;               // tokens in the packed batch (batch * L without cu)
 };
 
 // Which kernel family runs a prefill, and the workspace it needs.

@@ -30,7 +30,8 @@ __global__ __launch_bounds__(256) void prefill_generic(
     const float* __restrict__ lam, const float* __restrict__ theta, const T* __restrict__ B,
     const T* __restrict__ C, const float* __restrict__ Dv, const void* __restrict__ h_in,
     const T* __restrict__ bl_in, const T* __restrict__ xl_in, T* __restrict__ y,
-    void* __restrict__ h_out, int64_t L, int H, int G, int N, int P, int R, int Q, int state_bf16) {
+    void* __restrict__ h_out, int64_t Lmax, int H, int G, int N, int P, int R, int Q, int state_bf16,
+    const int64_t* __restrict__ cu, int64_t Tt) {
     extern __shared__ float smem[];
     const int KP = N / 2, QR = Q * R;
     float* S = smem;                       // N*P
@@ -47,14 +48,15 @@ __global__ __launch_bounds__(256) void prefill_generic(
     const int bh = blockIdx.x;
     const int b = bh / H, h = bh - b * H;
     const int g = h / (H / G);
+    // this sequence: tokens tb .. tb + L - 1 of the (possibly packed) token axis
+    const SeqSpan sp = seq_span(cu, b, Lmax, Tt);
+    const int64_t tb = sp.start, L = sp.len;
     const int tid = threadIdx.x, NT = blockDim.x;
     const float Ah = A[h], Dh = Dv[h];
 
     // Incoming state: h_in plus the beta term of the first token for the carry.
     const bool carry = (bl_in != nullptr) && (xl_in != nullptr) && L > 0;
-    const float c1_first = carry ? (1.f - lam[(static_cast<int64_t>(b) * L) * H + h]) *
-                                       dt[(static_cast<int64_t>(b) * L) * H + h]
-                                 : 0.f;
+    const float c1_first = carry ? (1.f - lam[tb * H + h]) * dt[tb * H + h] : 0.f;
     for (int idx = tid; idx < N * P; idx += NT) {
         const int n = idx / P, p = idx - n * P;
         float s = h_in ? state_load(h_in, static_cast<size_t>(bh) * N * P + idx, state_bf16) : 0.f;
@@ -80,11 +82,11 @@ __global__ __launch_bounds__(256) void prefill_generic(
             float a = 0.f, gm = 0.f, w = 0.f;
             if (i < nq) {
                 const int64_t t = t0 + i;
-                const float dtv = dt[(b * L + t) * H + h], lv = lam[(b * L + t) * H + h];
+                const float dtv = dt[(tb + t) * H + h], lv = lam[(tb + t) * H + h];
                 a = dtv * Ah;
                 gm = lv * dtv;
                 w = gm;
-                if (t + 1 < L) w += (1.f - lam[(b * L + t + 1) * H + h]) * dt[(b * L + t + 1) * H + h];
+                if (t + 1 < L) w += (1.f - lam[(tb + t + 1) * H + h]) * dt[(tb + t + 1) * H + h];
             }
             if (Q <= 64) {   // i == lane of wave 0
                 for (int off = 1; off < 64; off <<= 1) {
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(256) void prefill_generic(
         // Angles into LDS, one element per thread (loads in parallel).
         for (int idx = tid; idx < Q * KP; idx += NT) {
             const int i = idx / KP, k = idx - i * KP;
-            phi[idx] = (i < nq) ? theta[((b * L + t0 + i) * G + g) * KP + k] : 0.f;
+            phi[idx] = (i < nq) ? theta[((tb + t0 + i) * G + g) * KP + k] : 0.f;
         }
         __syncthreads();
         // Chunk-local angle prefix sums, one pair per thread, within LDS.
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(256) void prefill_generic(
             const int i = idx / (R * KP), rem = idx - i * R * KP, r = rem / KP, k = rem - r * KP;
             float b0 = 0.f, b1 = 0.f, c0 = 0.f, c1 = 0.f;
             if (i < nq) {
-                const size_t o = (((b * L + t0 + i) * G + g) * R + r) * static_cast<size_t>(N) + 2 * k;
+                const size_t o = (((tb + t0 + i) * G + g) * R + r) * static_cast<size_t>(N) + 2 * k;
                 float sn, cs;
                 sincos_acc(phi[i * KP + k], &sn, &cs);
                 const float bb0 = io<T>::load(B + o), bb1 = io<T>::load(B + o + 1);
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(256) void prefill_generic(
         }
         for (int idx = tid; idx < QR * P; idx += NT) {
             const int i = idx / (R * P);
-            X[idx] = (i < nq) ? io<T>::load(x + ((b * L + t0 + i) * H + h) * static_cast<size_t>(R * P) +
+            X[idx] = (i < nq) ? io<T>::load(x + ((tb + t0 + i) * H + h) * static_cast<size_t>(R * P) +
                                             (idx - i * R * P))
                               : 0.f;
         }
@@ -173,7 +175,7 @@ __global__ __launch_bounds__(256) void prefill_generic(
             float acc = __expf(cum[i]) * st;
             for (int js = 0; js < (i + 1) * R; ++js) acc += Gm[ir * QR + js] * X[js * P + p];
             acc += Dh * X[ir * P + p];
-            io<T>::store(y + ((b * L + t0 + i) * H + h) * static_cast<size_t>(R * P) + (ir - i * R) * P + p,
+            io<T>::store(y + ((tb + t0 + i) * H + h) * static_cast<size_t>(R * P) + (ir - i * R) * P + p,
                          acc);
         }
         __syncthreads();
@@ -204,23 +206,26 @@ template <typename T>
 __global__ void carry_out(const T* __restrict__ x, const T* __restrict__ B,
                           const T* __restrict__ bl_in, const T* __restrict__ xl_in,
                           T* __restrict__ bl_out, T* __restrict__ xl_out, int64_t batch,
-                          int64_t L, int H, int G, int N, int P, int R) {
+                          int64_t Lmax, int H, int G, int N, int P, int R, const int64_t* __restrict__ cu,
+                          int64_t Tt) {
     const int64_t nb = batch * G * R * N, nx = batch * H * R * P;
     for (int64_t idx = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; idx < nb + nx;
          idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
         if (idx < nb) {
             if (!bl_out) continue;
             const int64_t bb = idx / (G * R * N), rem = idx - bb * G * R * N;
+            const SeqSpan sp = seq_span(cu, bb, Lmax, Tt);
             T v{};
-            if (L > 0) v = B[(bb * L + (L - 1)) * G * R * N + rem];
+            if (sp.len > 0) v = B[(sp.start + sp.len - 1) * G * R * N + rem];
             else if (bl_in && xl_in) v = bl_in[idx];
             bl_out[idx] = v;
         } else {
             if (!xl_out) continue;
             const int64_t i2 = idx - nb;
             const int64_t bb = i2 / (H * R * P), rem = i2 - bb * H * R * P;
+            const SeqSpan sp = seq_span(cu, bb, Lmax, Tt);
             T v{};
-            if (L > 0) v = x[(bb * L + (L - 1)) * H * R * P + rem];
+            if (sp.len > 0) v = x[(sp.start + sp.len - 1) * H * R * P + rem];
             else if (bl_in && xl_in) v = xl_in[i2];
             xl_out[i2] = v;
         }
@@ -247,7 +252,7 @@ static hipError_t launch_generic_t(const PrefillArgs& a, hipStream_t st) {
                        static_cast<const T*>(a.B), static_cast<const T*>(a.C), a.D, a.h_in,
                        static_cast<const T*>(a.bl_in), static_cast<const T*>(a.xl_in),
                        static_cast<T*>(a.y), a.h_out, a.L, a.H, a.G, a.N, a.P, a.R, a.Q,
-                       a.state_bf16 ? 1 : 0);
+                       a.state_bf16 ? 1 : 0, a.cu, a.T);
     return hipGetLastError();
 }
 
@@ -265,7 +270,7 @@ static hipError_t launch_carry_t(const PrefillArgs& a, hipStream_t st) {
                        static_cast<const T*>(a.x), static_cast<const T*>(a.B),
                        static_cast<const T*>(a.bl_in), static_cast<const T*>(a.xl_in),
                        static_cast<T*>(a.bl_out), static_cast<T*>(a.xl_out), a.batch, a.L, a.H,
-                       a.G, a.N, a.P, a.R);
+                       a.G, a.N, a.P, a.R, a.cu, a.T);
     return hipGetLastError();
 }
 

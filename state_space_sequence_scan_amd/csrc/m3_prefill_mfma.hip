@@ -120,14 +120,18 @@ template <int R, int Q>
 __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
                                                 const uint16_t* __restrict__ C,
                                                 const float* __restrict__ theta, int64_t L, int G,
-                                                int nchunks, uint8_t* __restrict__ prep) {
+                                                int nchunks, uint8_t* __restrict__ prep,
+                                                const int64_t* __restrict__ cu, int64_t T) {
     constexpr int QR = Q * R;
     __shared__ float sCos[Q][KP], sSin[Q][KP];
     __shared__ float sPart[4][KP];
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
+    const SeqSpan sp = seq_span(cu, b, L, T);
     const int64_t t0 = static_cast<int64_t>(c) * Q;
-    const int nq = static_cast<int>(L - t0 < Q ? L - t0 : Q);
+    if (t0 >= sp.len) return;                 // no such chunk in this sequence: nothing reads it
+    const int nq = static_cast<int>(sp.len - t0 < Q ? sp.len - t0 : Q);
+    const int64_t tg = sp.start + t0;         // first token of the chunk in the packed arrays
     const PrepLayout lay{QR};
     uint8_t* base = prep + ((static_cast<size_t>(b) * G + g) * nchunks + c) * lay.bytes();
     uint16_t* Bt = reinterpret_cast<uint16_t*>(base + lay.bt());
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
 #pragma unroll
         for (int e = 0; e < QP; ++e) {
             const int i = part * QP + e;
-            run += (i < nq) ? theta[((b * L + t0 + i) * G + g) * KP + k] : 0.f;
+            run += (i < nq) ? theta[((tg + i) * G + g) * KP + k] : 0.f;
             th[e] = run;
         }
         sPart[part][k] = run;
@@ -175,7 +179,7 @@ __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
             const int i = row / R, r = row - i * R;
             float b0 = 0.f, b1 = 0.f, c0 = 0.f, c1 = 0.f;
             if (i < nq) {
-                const size_t o = (((b * L + t0 + i) * G + g) * R + r) * static_cast<size_t>(N) + 2 * k;
+                const size_t o = (((tg + i) * G + g) * R + r) * static_cast<size_t>(N) + 2 * k;
                 const uint32_t bb = *reinterpret_cast<const uint32_t*>(B + o);
                 const uint32_t cc = *reinterpret_cast<const uint32_t*>(C + o);
                 const float cn = sCos[i][k], sn = sSin[i][k];
@@ -212,9 +216,11 @@ struct ScanParams {
     float* seg_state;       // state-only mode: (b, H, nseg-1, N, P)
     float* seg_decay;       // state-only mode: (b, H, nseg-1)
     float* seg_rot;         // state-only mode: (b, H, nseg-1, KP, 2)
-    int64_t L;
+    int64_t L;              // sequence length (the maximum one with cu)
     int H, G, nchunks, nseg, chunks_per_seg;
     int state_bf16;         // h_in and h_out hold bf16 (else fp32)
+    const int64_t* cu;      // packed variable-length batch: sequence starts, or null
+    int64_t T;              // tokens in the packed arrays
 };
 
 // Initial state of segment 0 when no segment pass ran: h_in plus the beta term
@@ -331,8 +337,11 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
     const int p0 = 16 * CT * (w / RW);           // first state column owned by this wave
     const PrepLayout lay{QR};
     const float Ah = p.A[h];
+    const SeqSpan sp = seq_span(p.cu, b, p.L, p.T);
+    const int64_t tb = sp.start, Lb = sp.len;    // this sequence's first token and length
+    const int nchunks_b = static_cast<int>((Lb + Q - 1) / Q);
     const int c_begin = seg * p.chunks_per_seg;
-    const int c_end = min(p.nchunks, c_begin + p.chunks_per_seg);
+    const int c_end = min(nchunks_b, c_begin + p.chunks_per_seg);
     const bool last_seg = (seg == p.nseg - 1);
     const size_t gbase = (static_cast<size_t>(b) * p.G + g) * p.nchunks;
     const uint32_t HRP = static_cast<uint32_t>(p.H) * R * P;   // elements between tokens of x and y
@@ -371,9 +380,8 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
     // ---- state accumulators: rows n = n0 + 16rt + 4lg + i, columns p = p0 + 16ct + l16
     f32x4 sacc[RT][CT];
     if (FULL) {
-        const float c1 = (p.L > 0 && p.bl_in && p.xl_in)
-                             ? (1.f - p.lam[(static_cast<int64_t>(b) * p.L) * p.H + h]) *
-                                   p.dt[(static_cast<int64_t>(b) * p.L) * p.H + h]
+        const float c1 = (Lb > 0 && p.bl_in && p.xl_in)
+                             ? (1.f - p.lam[tb * p.H + h]) * p.dt[tb * p.H + h]
                              : 0.f;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -414,10 +422,10 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
 #define M3_FETCH_X(c_)                                                                                        \
     do {                                                                                                      \
         const int64_t t0f = static_cast<int64_t>(c_) * Q;                                                     \
-        const int nqf = static_cast<int>(p.L - t0f < Q ? p.L - t0f : Q);                                      \
+        const int nqf = static_cast<int>(Lb - t0f < Q ? Lb - t0f : Q);                                        \
         pnq = nqf;                                                                                            \
         {                                                                                                     \
-            const uint16_t* xch = p.x + ((b * p.L + t0f) * p.H + h) * static_cast<int64_t>(R * P);            \
+            const uint16_t* xch = p.x + ((tb + t0f) * p.H + h) * static_cast<int64_t>(R * P);                 \
             _Pragma("unroll") for (int e = 0; e < XPT; ++e) {                                                 \
                 const int u = tid + NTH * e, row = u >> 3;                                                    \
                 const int i = row / R, r = row - i * R;                                                       \
@@ -427,10 +435,10 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
             }                                                                                                 \
         }                                                                                                     \
         {   /* wave 0 uses these; the other waves read one broadcast address */                               \
-            const float* dtc = p.dt + (b * p.L + t0f) * p.H + h;                                              \
-            const float* lmc = p.lam + (b * p.L + t0f) * p.H + h;                                             \
+            const float* dtc = p.dt + (tb + t0f) * p.H + h;                                                   \
+            const float* lmc = p.lam + (tb + t0f) * p.H + h;                                                  \
             const int i0 = (w == 0 && lane < nqf) ? lane : 0;                                                 \
-            const int i1 = (w == 0 && t0f + i0 + 1 < p.L) ? i0 + 1 : i0;                                      \
+            const int i1 = (w == 0 && t0f + i0 + 1 < Lb) ? i0 + 1 : i0;                                       \
             pd0 = dtc[static_cast<uint32_t>(i0 * p.H)];                                                       \
             pl0 = lmc[static_cast<uint32_t>(i0 * p.H)];                                                       \
             pd1 = dtc[static_cast<uint32_t>(i1 * p.H)];                                                       \
@@ -466,7 +474,7 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
         if (w == 0) {                                                                                         \
             const bool valid = lane < pnq;                                                                    \
             const float dtv = valid ? pd0 : 0.f, lv = valid ? pl0 : 0.f;                                      \
-            const bool has1 = valid && (nextpos + lane + 1 < p.L);                                            \
+            const bool has1 = valid && (nextpos + lane + 1 < Lb);                                             \
             const float gm = lv * dtv;                                                                        \
             const float wv = gm + (has1 ? (1.f - pl1) * pd1 : 0.f);                                           \
             float cum = dtv * Ah;                                                                             \
@@ -645,7 +653,7 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
     for (int c = c_begin; c < c_end; ++c) {
         const int q = c & 1;
         const int64_t t0 = static_cast<int64_t>(c) * Q;
-        const int nq = static_cast<int>(p.L - t0 < Q ? p.L - t0 : Q);
+        const int nq = static_cast<int>(Lb - t0 < Q ? Lb - t0 : Q);
         const bool has_next = c + 1 < c_end;
         const int cn = has_next ? c + 1 : c;    // chunk of the register prefetches (clamped)
         if (FULL) {
@@ -663,7 +671,7 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
             M3_LOAD_CF(cf0, cn, 0);
         }
         if (FULL && has_rows) {
-            uint16_t* ych = p.y + ((b * p.L + t0) * p.H + h) * static_cast<int64_t>(R * P);
+            uint16_t* ych = p.y + ((tb + t0) * p.H + h) * static_cast<int64_t>(R * P);
             bf16x8 btf[4];
             s16x4 xf[4];
             f32x4 y0[4], y1[4];
@@ -828,9 +836,9 @@ template <int R>
 __global__ __launch_bounds__(NT) void seg_pass(ScanParams p, float* __restrict__ s_init) {
     const int bh = blockIdx.x;
     const int b = bh / p.H, h = bh - b * p.H, g = h / (p.H / p.G);
-    const float c1 = (p.L > 0 && p.bl_in && p.xl_in)
-                         ? (1.f - p.lam[(static_cast<int64_t>(b) * p.L) * p.H + h]) *
-                               p.dt[(static_cast<int64_t>(b) * p.L) * p.H + h]
+    const SeqSpan sp = seq_span(p.cu, b, p.L, p.T);
+    const float c1 = (sp.len > 0 && p.bl_in && p.xl_in)
+                         ? (1.f - p.lam[sp.start * p.H + h]) * p.dt[sp.start * p.H + h]
                          : 0.f;
     for (int idx = threadIdx.x; idx < KP * P; idx += NT) {
         const int k = idx / P, col = idx - k * P;
@@ -905,7 +913,8 @@ static MfmaWs mfma_ws(const PrefillArgs& a, int nchunks, int nseg) {
 
 void plan_mfma(const PrefillArgs& a, PrefillPlan* plan) {
     const int nchunks = static_cast<int>((a.L + a.Q - 1) / a.Q);
-    int nseg = nchunks > 0 ? choose_nseg(a, nchunks) : 1;
+    // packed variable-length batches run each sequence in one sweep
+    int nseg = (nchunks > 0 && !a.cu) ? choose_nseg(a, nchunks) : 1;
     if (nchunks > 0) {                       // no empty trailing segment
         const int cps = (nchunks + nseg - 1) / nseg;
         nseg = (nchunks + cps - 1) / cps;
@@ -932,7 +941,7 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
 
     hipLaunchKernelGGL((mf::rope_prep<R, Q>), dim3(nchunks, a.G, static_cast<unsigned>(a.batch)), dim3(mf::NT), 0,
                        st, static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.theta, a.L,
-                       a.G, nchunks, base + ws.prep);
+                       a.G, nchunks, base + ws.prep, a.cu, a.T);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
@@ -951,6 +960,8 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
     p.xl_in = static_cast<const uint16_t*>(a.xl_in);
     p.h_out = a.h_out;
     p.L = a.L;
+    p.cu = a.cu;
+    p.T = a.T;
     p.H = a.H;
     p.G = a.G;
     p.nchunks = nchunks;

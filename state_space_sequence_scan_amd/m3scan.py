@@ -64,6 +64,9 @@ def lib(path: str = LIB_PATH):
     L.m3_prefill_chunked.restype = ctypes.c_int
     L.m3_prefill_chunked.argtypes = ([ctypes.POINTER(Dims)] + [vp] * 8 +
                                      [ctypes.POINTER(State), ctypes.POINTER(State), vp, vp, sz, vp])
+    L.m3_prefill_varlen.restype = ctypes.c_int
+    L.m3_prefill_varlen.argtypes = ([ctypes.POINTER(Dims), vp, ctypes.c_int64] + [vp] * 8 +
+                                    [ctypes.POINTER(State), ctypes.POINTER(State), vp, vp, sz, vp])
     L.m3_decode_step.restype = ctypes.c_int
     L.m3_decode_step.argtypes = [ctypes.POINTER(Dims)] + [vp] * 13
     _lib = L
@@ -207,3 +210,68 @@ def decode_step(state: DecodeState, x_t, dt_t, A, lam_t, theta_t, B_t, C_t, D,
     if advance:
         state.b_last, state.x_last = B_t, x_t
     return y_t
+
+
+def prefill_varlen(x, dt, A, lam, theta, B, C, D, cu_seqlens, max_seqlen: int, chunk: int,
+                   state_in: Optional[DecodeState] = None, out_state: bool = True,
+                   y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                   state_dtype: Optional[torch.dtype] = None):
+    """Chunked prefill of a packed batch of variable-length sequences.
+
+    x (T,H,R,P), dt/lam (T,H), theta (T,G,N/2), B/C (T,G,R,N) hold the sequences
+    one after another; cu_seqlens (nseq+1,) int64 on the device gives their starts
+    (cu_seqlens[0] = 0, cu_seqlens[-1] = T); max_seqlen bounds every length.
+    Each sequence is scanned from its own state_in slice (else from zero).
+    Returns (y (T,H,R,P), DecodeState with (nseq, ...) tensors or None)."""
+    T, H, R, P = x.shape
+    G, N = B.shape[1], B.shape[3]
+    nseq = cu_seqlens.shape[0] - 1
+    dev, io = x.device, x.dtype
+    if io not in _IO:
+        raise ValueError(f"x dtype {io} not supported (fp32 or bf16)")
+    if nseq < 1:
+        raise ValueError("cu_seqlens needs at least two entries")
+    _check(cu_seqlens, "cu_seqlens", (nseq + 1,), torch.int64, dev)
+    _check(x, "x", (T, H, R, P), io, dev)
+    _check(dt, "dt", (T, H), torch.float32, dev)
+    _check(lam, "lam", (T, H), torch.float32, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(theta, "theta", (T, G, N // 2), torch.float32, dev)
+    _check(B, "B", (T, G, R, N), io, dev)
+    _check(C, "C", (T, G, R, N), io, dev)
+    if state_dtype is None:
+        state_dtype = state_in.h.dtype if state_in is not None else torch.float32
+    if state_dtype not in _IO:
+        raise ValueError(f"state dtype {state_dtype} not supported (fp32 or bf16)")
+    dims = make_dims(nseq, max_seqlen, H, G, P, N, R, chunk, _IO[io], _IO[state_dtype])
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _check(y, "y", x.shape, io, dev)
+    sin = None
+    if state_in is not None:
+        _check(state_in.h, "state_in.h", (nseq, H, N, P), state_dtype, dev)
+        if state_in.b_last is not None:
+            _check(state_in.b_last, "state_in.b_last", (nseq, G, R, N), io, dev)
+            _check(state_in.x_last, "state_in.x_last", (nseq, H, R, P), io, dev)
+        sin = State(state_in.h.data_ptr(),
+                    None if state_in.b_last is None else state_in.b_last.data_ptr(),
+                    None if state_in.x_last is None else state_in.x_last.data_ptr())
+    sout = st = None
+    if out_state:
+        st = DecodeState(torch.empty((nseq, H, N, P), dtype=state_dtype, device=dev),
+                         torch.empty((nseq, G, R, N), dtype=io, device=dev),
+                         torch.empty((nseq, H, R, P), dtype=io, device=dev))
+        sout = State(st.h.data_ptr(), st.b_last.data_ptr(), st.x_last.data_ptr())
+    ws = workspace_size(dims)
+    if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
+        workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+    rc = lib().m3_prefill_varlen(ctypes.byref(dims), _p(cu_seqlens), ctypes.c_int64(T), _p(x), _p(dt),
+                                 _p(A), _p(lam), _p(theta), _p(B), _p(C), _p(D),
+                                 None if sin is None else ctypes.byref(sin),
+                                 None if sout is None else ctypes.byref(sout), _p(y),
+                                 _p(workspace) if ws > 0 else None, ws, _stream(dev))
+    if rc != 0:
+        raise M3Error("m3_prefill_varlen", rc)
+    return y, st

@@ -28,8 +28,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_symbols() == ["m3_decode_step", "m3_prefill_chunked", "m3_prefill_workspace_size",
-                                  "m3_status_string", "m3_version"]
+    assert declared_symbols() == ["m3_decode_step", "m3_prefill_chunked", "m3_prefill_varlen",
+                                  "m3_prefill_workspace_size", "m3_status_string", "m3_version"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -133,3 +133,29 @@ def test_binding_raises_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(m3scan, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         m3scan.lib(str(tmp_path / "missing.so"))
+
+
+def test_varlen_rejects_bad_arguments(lib):
+    d = _dims()
+    T = ctypes.c_int64(100)
+    # no offsets, negative token count
+    assert lib.m3_prefill_varlen(ctypes.byref(d), None, T, *[FAKE] * 8, None, None, FAKE, None, 0,
+                                 None) == -1
+    assert lib.m3_prefill_varlen(ctypes.byref(d), FAKE, ctypes.c_int64(-1), *[FAKE] * 8, None, None,
+                                 FAKE, None, 0, None) == -1
+    # bad dims and missing per-token inputs fail like the uniform prefill
+    for kw in BAD_DIMS:
+        bd = _dims(**kw)
+        assert lib.m3_prefill_varlen(ctypes.byref(bd), FAKE, T, *[FAKE] * 8, None, None, FAKE, None, 0,
+                                     None) == -1, kw
+    for i in range(8):
+        args = [FAKE] * 8
+        args[i] = None
+        assert lib.m3_prefill_varlen(ctypes.byref(d), FAKE, T, *args, None, None, FAKE, None, 0,
+                                     None) == -1
+    # workspace too small (the MFMA path needs one)
+    big = _dims(headdim=64, dstate=128, rank=2, chunk=32, io_dtype=m3scan.M3_BF16)
+    n = ctypes.c_size_t(0)
+    assert lib.m3_prefill_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0 and n.value > 0
+    assert lib.m3_prefill_varlen(ctypes.byref(big), FAKE, T, *[FAKE] * 8, None, None, FAKE, FAKE, 16,
+                                 None) == -3
