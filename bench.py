@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="c4", help="c1, c2, c3 (prefill only) or c4 (prefill + decode)")
     ap.add_argument("--decode-steps", type=int, default=None, help="override the decode steps per step")
+    ap.add_argument("--varlen", action="store_true",
+                    help="pack the batch's sequences with seeded lengths uniform in [L/4, L] "
+                         "(m3_prefill_varlen) instead of equal lengths L")
     ap.add_argument("--state-dtype", default="fp32", choices=("fp32", "bf16"),
                     help="dtype of the state in HBM (bf16: reduced-precision state, fp32 math)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -46,15 +49,17 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_bytes(cfg, L, steps, state_bytes=4):
+def algorithmic_bytes(cfg, L, steps, state_bytes=4, tokens=None):
     """Bytes the method must move (see the workload formulas in the design notes);
-    state_bytes is 4 for an fp32 state, 2 for a bf16 state."""
+    state_bytes is 4 for an fp32 state, 2 for a bf16 state; tokens is the number of
+    prefill tokens over all sequences (batch * L unless the lengths vary)."""
     s = 2 if cfg.io_dtype == "bf16" else 4
     b, H, G, P, N, R = cfg.batch, cfg.nheads, cfg.ngroups, cfg.headdim, cfg.dstate, cfg.rank
+    tok = b * L if tokens is None else tokens
     pre = 0
-    if L > 0:
-        pre += b * L * H * (2 * R * P * s + 8)              # x read, y write, dt, lambda
-        pre += b * L * G * (2 * N * R * s + 4 * (N // 2))   # B, C, theta
+    if tok > 0:
+        pre += tok * H * (2 * R * P * s + 8)                # x read, y write, dt, lambda
+        pre += tok * G * (2 * N * R * s + 4 * (N // 2))     # B, C, theta
         pre += b * H * N * P * state_bytes                  # state out
         pre += b * (G * R * N + H * R * P) * s              # carry out
         pre += 8 * H
@@ -67,10 +72,10 @@ def algorithmic_bytes(cfg, L, steps, state_bytes=4):
     return pre, dec
 
 
-def prefill_flops(cfg, L):
+def prefill_flops(cfg, L, tokens=None):
     """Useful MFMA-shaped flops of the chunked prefill (causal half of each chunk block)."""
     b, H, G, P, N, R, Q = cfg.batch, cfg.nheads, cfg.ngroups, cfg.headdim, cfg.dstate, cfg.rank, cfg.chunk
-    tok = b * L
+    tok = b * L if tokens is None else tokens
     return 2 * (tok * G * R * R * N * (Q + 1) / 2 + tok * H * (R * R * P * (Q + 1) / 2 + 2 * R * N * P))
 
 
@@ -130,7 +135,16 @@ def main():
     t_gen = time.time()
     d = inputs.draw_config(cfg, device=dev)
     dd = inputs.draw_decode(cfg, steps_dec, device=dev) if steps_dec > 0 else None
-    y = torch.empty_like(d["x"])
+    lens = np.full(cfg.batch, L, dtype=np.int64)
+    if args.varlen:   # seeded length mix; the packed arrays hold each sequence's first lens[i] tokens
+        lens = np.random.default_rng(cfg.seed + 7).integers(max(L // 4, 1), L + 1, cfg.batch)
+        starts = np.concatenate([[0], np.cumsum(lens)])
+        cu = torch.tensor(starts, dtype=torch.int64, device=dev)
+        dp = {k: torch.cat([d[k][i, :int(lens[i])] for i in range(cfg.batch)]).contiguous()
+              for k in ("x", "dt", "lam", "theta", "B", "C")}
+        y = torch.empty_like(dp["x"])
+    else:
+        y = torch.empty_like(d["x"])
     ydec = torch.empty((max(steps_dec, 1),) + tuple(d["x"][:, 0].shape), dtype=d["x"].dtype, device=dev)
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
@@ -140,8 +154,12 @@ def main():
     def one_step(record=None):
         e0, e1, e2 = ev(), ev(), ev()
         e0.record(stream)
-        _, st = m3scan.prefill(d["x"], d["dt"], d["A"], d["lam"], d["theta"], d["B"], d["C"], d["D"],
-                               cfg.chunk, y=y, state_dtype=state_dtype)
+        if args.varlen:
+            _, st = m3scan.prefill_varlen(dp["x"], dp["dt"], d["A"], dp["lam"], dp["theta"], dp["B"],
+                                          dp["C"], d["D"], cu, L, cfg.chunk, y=y, state_dtype=state_dtype)
+        else:
+            _, st = m3scan.prefill(d["x"], d["dt"], d["A"], d["lam"], d["theta"], d["B"], d["C"], d["D"],
+                                   cfg.chunk, y=y, state_dtype=state_dtype)
         e1.record(stream)
         for t in range(steps_dec):
             m3scan.decode_step(st, dd["x"][t], dd["dt"][t], d["A"], dd["lam"][t], dd["theta"][t],
@@ -165,17 +183,17 @@ def main():
     step_ms = wall * 1e3 / args.steps
     pre_avg, dec_avg = float(np.mean(pre_ms)), float(np.mean(dec_ms))
 
-    tokens_pre = cfg.batch * L
+    tokens_pre = int(lens.sum())
     tokens_dec = cfg.batch * steps_dec
     value = (tokens_pre + tokens_dec) / (step_ms / 1e3)
-    pre_bytes, dec_bytes = algorithmic_bytes(cfg, L, steps_dec, state_bytes)
+    pre_bytes, dec_bytes = algorithmic_bytes(cfg, L, steps_dec, state_bytes, tokens=tokens_pre)
     pre_tps = tokens_pre / (pre_avg / 1e3)
     pre_gbs = pre_bytes / (pre_avg / 1e3) / 1e9
     dec_launch_ms = dec_avg / max(steps_dec, 1)
     dec_gbs = dec_bytes / (dec_launch_ms / 1e3) / 1e9 if steps_dec else 0.0
     state_gbs = (2 * cfg.batch * cfg.nheads * cfg.dstate * cfg.headdim * state_bytes) / (dec_launch_ms / 1e3) / 1e9 \
         if steps_dec else 0.0
-    flops = prefill_flops(cfg, L)
+    flops = prefill_flops(cfg, L, tokens=tokens_pre)
 
     # Dominant kernel: the one with the larger share of the step.
     if steps_dec and dec_avg >= pre_avg:
@@ -187,7 +205,7 @@ def main():
                 "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "alg_bytes_per_launch": dec_bytes, "avg_launch_us": round(dec_launch_ms * 1e3, 2)}
     else:
-        traffic = pmc_traffic(f"prefill_{args.workload}_hbm_counters.json",
+        traffic = pmc_traffic(f"prefill_{args.workload}{'_varlen' if args.varlen else ''}_hbm_counters.json",
                               ["m3_prefill_mfma.hip", "m3_common.h"], pre_bytes)
         roof = {"kernel": "prefill (chunked scan)", "bound": "hbm",
                 "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -200,14 +218,16 @@ def main():
     if args.check_slices > 0 or not args.no_cpu_baseline:
         import oracle
 
-        def slice_inputs(bi, h, with_decode=True):
+        def slice_inputs(bi, h, with_decode=True, n=None):
+            """(bi, h) slice: its first n prefill tokens (all L by default), then the decode tokens."""
             g = h // (cfg.nheads // cfg.ngroups)
             f = lambda t: t.detach().double().cpu().numpy()
+            n = L if n is None else n
             parts = {
-                "x": [f(d["x"][bi:bi + 1, :, h:h + 1])], "dt": [f(d["dt"][bi:bi + 1, :, h:h + 1])],
-                "lam": [f(d["lam"][bi:bi + 1, :, h:h + 1])],
-                "theta": [f(d["theta"][bi:bi + 1, :, g:g + 1])],
-                "B": [f(d["B"][bi:bi + 1, :, g:g + 1])], "C": [f(d["C"][bi:bi + 1, :, g:g + 1])]}
+                "x": [f(d["x"][bi:bi + 1, :n, h:h + 1])], "dt": [f(d["dt"][bi:bi + 1, :n, h:h + 1])],
+                "lam": [f(d["lam"][bi:bi + 1, :n, h:h + 1])],
+                "theta": [f(d["theta"][bi:bi + 1, :n, g:g + 1])],
+                "B": [f(d["B"][bi:bi + 1, :n, g:g + 1])], "C": [f(d["C"][bi:bi + 1, :n, g:g + 1])]}
             if with_decode and steps_dec:
                 parts["x"].append(f(dd["x"][:, bi:bi + 1, h:h + 1].transpose(0, 1)))
                 parts["dt"].append(f(dd["dt"][:, bi:bi + 1, h:h + 1].transpose(0, 1)))
@@ -226,13 +246,17 @@ def main():
             errs = []
             for _ in range(args.check_slices):
                 bi, h = int(rng.integers(cfg.batch)), int(rng.integers(cfg.nheads))
-                si = slice_inputs(bi, h)
+                n = int(lens[bi])
+                si = slice_inputs(bi, h, n=n)
                 flags = None
                 if args.state_dtype == "bf16":   # state rounded after the prefill and every decode token
-                    flags = np.zeros(L + steps_dec, bool)
-                    flags[L - 1:] = True
+                    flags = np.zeros(n + steps_dec, bool)
+                    flags[n - 1:] = True
                 yr, hr = oracle.scan(*[si[k] for k in order], round_after=flags)
-                yg = [y[bi:bi + 1, :, h:h + 1].double().cpu().numpy()]
+                if args.varlen:
+                    yg = [y[int(starts[bi]):int(starts[bi + 1]), h:h + 1][None].double().cpu().numpy()]
+                else:
+                    yg = [y[bi:bi + 1, :, h:h + 1].double().cpu().numpy()]
                 if steps_dec:
                     yg.append(ydec[:steps_dec, bi:bi + 1, h:h + 1].transpose(0, 1).double().cpu().numpy())
                 yg = np.concatenate(yg, axis=1)
@@ -273,7 +297,9 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if cfg.io_dtype == "bf16" else "fp32",
         "data": "synthetic (seeded torch generators on the GPU; distributions of the workload)",
-        "config": {"workload": cfg.label, "name": cfg.name, "batch": cfg.batch, "prefill_len": L,
+        "config": {"workload": cfg.label + (f"; packed lengths uniform in [{max(L // 4, 1)}, {L}], "
+                                            f"{tokens_pre} tokens" if args.varlen else ""),
+                   "name": cfg.name, "batch": cfg.batch, "prefill_len": L,
                    "decode_steps": steps_dec, "heads": cfg.nheads, "groups": cfg.ngroups,
                    "headdim": cfg.headdim, "dstate": cfg.dstate, "rank": cfg.rank, "chunk": cfg.chunk,
                    "io_dtype": cfg.io_dtype, "state_dtype": args.state_dtype},
