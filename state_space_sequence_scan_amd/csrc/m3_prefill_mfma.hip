@@ -240,12 +240,14 @@ __device__ float initial_state(const ScanParams& p, int b, int h, int g, int n, 
     return s;
 }
 
-// Element offset of (row, col) in a row-major [rows][P] bf16 LDS tile whose 16-byte
-// chunks are swapped in pairs on odd rows, so that the 4 rows x 32 bytes of a
-// transposing read spread over twice as many banks.  The swap keeps the offset of
-// a 16-column tile linear in the tile index (an immediate in the LDS instruction).
+// Element offset of (row, col) in a row-major [rows][P] bf16 LDS tile (P = 64: four
+// 32-byte column groups per 128-byte row) whose groups are permuted by row: group g of
+// row r is stored at position g ^ (r & 3).  A transposing read covers 4 consecutive
+// rows x one 32-byte group; rows 128 bytes apart would put all four on the same 8 of
+// the 32 banks, the permutation puts them on 4 different sets of 8.  Rows 4 apart
+// share the permutation, so moving by a multiple of 4 rows is a constant offset.
 __device__ __forceinline__ int xoff(int row, int col) {
-    return row * P + (((col >> 3) ^ (row & 1)) << 3) + (col & 7);
+    return row * P + ((((col >> 4) ^ row) & 3) << 4) + (col & 15);
 }
 
 // Swap a value with the neighbouring lane (lane ^ 1) through a DPP quad permutation.
@@ -323,7 +325,7 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
     __shared__ __align__(16) uint16_t sBt[QR * BS];                // Bt token-major
     __shared__ __align__(16) uint16_t sST[FULL ? P * BS : 8];      // S^T (bf16): [p][n]
     __shared__ __align__(16) float sV[FULL ? NB * Q : 4];          // column factors [row block][token]
-    __shared__ float sCum[2][Q], sSc[2][Q], sW[2][Q], sGam[2][Q];  // by chunk parity
+    __shared__ __align__(16) float sCum[2][Q], sSc[2][Q], sW[2][Q], sGam[2][Q];  // by chunk parity
     __shared__ float sCs[2][KP * 2];
     __shared__ float sDec[2];
 
@@ -351,13 +353,18 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
     // 2NW-1-w (a_lo < a_hi), and the B tiles they share are read from LDS once.
     const int a_lo = (MB == 2) ? w : 4 * (w >> 2) + (((w >> 2) & 1) ? 3 - (w & 3) : (w & 3));
     const int a_hi = (MB == 2) ? 2 * NW - 1 - w : a_lo;
-    const bool has_rows = a_lo < NB;
+    const bool has_rows = NB >= NW || a_lo < NB;   // every wave has rows unless the chunk has fewer blocks
     // per-lane LDS bases (byte addresses); tile accesses add compile-time offsets
     const uint32_t aBtRow = lds_addr(&sBt[l16 * BS + 8 * lg]);                          // Bt tiles, A operand
     const uint32_t aBtTr = lds_addr(&sBt[(8 * lg + (l16 >> 2)) * BS + n0 + 4 * (l16 & 3)]);   // Bt^T, transposed
     const uint32_t aBtW = lds_addr(&sBt[(tid >> 4) * BS + 8 * (tid & 15)]);             // Bt staging
-    const uint32_t aXTr = FULL ? lds_addr(&sX[xoff(4 * lg + (l16 >> 2), 4 * (l16 & 3))]) : 0u;   // X^T, transposed
-    const uint32_t aXsTr = lds_addr(&sXs[xoff(8 * lg + (l16 >> 2), p0 + 4 * (l16 & 3))]);     // (sX)^T, transposed
+    uint32_t aXTr[4], aXsTr[CT];   // X^T and (sX)^T, transposed: one base per 16-column tile
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+        aXTr[ct] = FULL ? lds_addr(&sX[xoff(4 * lg + (l16 >> 2), 16 * ct + 4 * (l16 & 3))]) : 0u;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+        aXsTr[ct] = lds_addr(&sXs[xoff(8 * lg + (l16 >> 2), p0 + 16 * ct + 4 * (l16 & 3))]);
     const uint32_t aXW = FULL ? lds_addr(&sX[xoff(tid >> 3, 8 * (tid & 7))]) : 0u;      // X staging
     const uint32_t aXsW = lds_addr(&sXs[xoff(tid >> 3, 8 * (tid & 7))]);               // sX staging
     const uint32_t aST = FULL ? lds_addr(&sST[l16 * BS + 8 * lg]) : 0u;                 // S^T, A operand
@@ -543,65 +550,94 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
     // are applied to the accumulators; only the diagonal tile evaluates the full
     // mask per element.
 
-    // Bt tile bb (A operand) and X^T tile bb (A operand of the 16x16x16 steps).
-#define M3_LOAD_COLS(bb_)                                                                                     \
+    // Operands of column block bb_ into register set S_ (A or B): the Bt tile (A operand
+    // of G^T), the X^T tile (A operand of the 16x16x16 steps), and the column factors of
+    // row block(s) a_lo / a_hi (v0 / v1).  The tile loops load set B for the next column
+    // block before working on set A, so the LDS latency is covered by the work on A.
+#define M3_LOAD_COLS(S_, bb_)                                                                                 \
     do {                                                                                                      \
         _Pragma("unroll") for (int ks = 0; ks < 4; ++ks)                                                      \
-            btf[ks] = lds_ld<bf16x8>(aBtRow + (16 * (bb_) * BS + 32 * ks) * 2);                               \
+            btf##S_[ks] = lds_ld<bf16x8>(aBtRow + (16 * (bb_) * BS + 32 * ks) * 2);                           \
         _Pragma("unroll") for (int ct = 0; ct < 4; ++ct)                                                      \
-            xf[ct] = lds_tr4(aXTr + (16 * (bb_) * P + 16 * ct) * 2);                                          \
+            xf##S_[ct] = lds_tr4(aXTr[ct] + 16 * (bb_) * P * 2);                                              \
     } while (0)
 
-    // gt_[e] = G[i = 16a + l16][j = 16bb + 4lg + e],  G = Ct Bt^T
-#define M3_GTILE(gt_, cfv_)                                                                                   \
-    do {                                                                                                      \
-        gt_ = f32x4{0.f, 0.f, 0.f, 0.f};                                                                      \
-        _Pragma("unroll") for (int ks = 0; ks < 4; ++ks) gt_ = mfma_k32(btf[ks], oct(cfv_, ks), gt_);         \
-    } while (0)
+    // Keeps the prefetches above the work on the other register set (the scheduler would
+    // otherwise sink them next to their uses).
+#define M3_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-#define M3_OFFDIAG(yv_, cfv_, a_, bb_)                                                                        \
+#define M3_LOAD_V(vv_, a_, bb_)                                                                               \
     do {                                                                                                      \
-        f32x4 gt;                                                                                             \
-        M3_GTILE(gt, cfv_);                                                                                   \
         const float* vrow = &sV[(a_) * Q];                                                                    \
-        float4 vv;                                                                                            \
         if constexpr (R == 1) {                                                                               \
-            vv = *reinterpret_cast<const float4*>(vrow + 16 * (bb_) + 4 * lg);                                \
+            vv_ = *reinterpret_cast<const float4*>(vrow + 16 * (bb_) + 4 * lg);                               \
         } else if constexpr (R == 2) {                                                                        \
             const float2 v2 = *reinterpret_cast<const float2*>(vrow + 8 * (bb_) + 2 * lg);                    \
-            vv = float4{v2.x, v2.x, v2.y, v2.y};                                                              \
+            vv_ = float4{v2.x, v2.x, v2.y, v2.y};                                                             \
         } else {                                                                                              \
             const float v1 = vrow[4 * (bb_) + lg];                                                            \
-            vv = float4{v1, v1, v1, v1};                                                                      \
+            vv_ = float4{v1, v1, v1, v1};                                                                     \
         }                                                                                                     \
-        const uint2 mp = {pack_bf16x2(gt[0] * vv.x, gt[1] * vv.y), pack_bf16x2(gt[2] * vv.z, gt[3] * vv.w)};  \
+    } while (0)
+
+    // gt_[e] = G[i = 16a + l16][j = 16bb + 4lg + e],  G = Ct Bt^T, from the Bt tile of set S_
+#define M3_GTILE(gt_, cfv_, S_)                                                                               \
+    do {                                                                                                      \
+        gt_ = f32x4{0.f, 0.f, 0.f, 0.f};                                                                      \
+        _Pragma("unroll") for (int ks = 0; ks < 4; ++ks) gt_ = mfma_k32(btf##S_[ks], oct(cfv_, ks), gt_);     \
+    } while (0)
+
+    // Off-diagonal tile with column factors vv_ (loaded by M3_LOAD_V).
+#define M3_OFFDIAG(yv_, cfv_, S_, vv_)                                                                        \
+    do {                                                                                                      \
+        f32x4 gt;                                                                                             \
+        M3_GTILE(gt, cfv_, S_);                                                                               \
+        const uint2 mp = {pack_bf16x2(gt[0] * vv_.x, gt[1] * vv_.y), pack_bf16x2(gt[2] * vv_.z, gt[3] * vv_.w)}; \
         const s16x4 mf = __builtin_bit_cast(s16x4, mp);                                                       \
-        _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) yv_[ct] = mfma_k16(xf[ct], mf, yv_[ct]);             \
+        _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) yv_[ct] = mfma_k16(xf##S_[ct], mf, yv_[ct]);         \
     } while (0)
 
     // Diagonal tile: row part of the off-diagonal sum, the full mask, and D X.
-#define M3_DIAG(yv_, cfv_, a_)                                                                                \
+#define M3_DIAG(yv_, cfv_, a_, S_)                                                                            \
     do {                                                                                                      \
         f32x4 gt;                                                                                             \
-        M3_GTILE(gt, cfv_);                                                                                   \
+        M3_GTILE(gt, cfv_, S_);                                                                               \
+        /* every value is loaded unconditionally (vector loads where R < 4) and selected after */            \
         const int ta = (16 * (a_)) / R;                                                                       \
-        const float ref = ta > 0 ? sCum[q][ta - 1] : 0.f;                                                     \
+        const float ref_raw = sCum[q][ta > 0 ? ta - 1 : 0];                                                   \
+        const float ref = ta > 0 ? ref_raw : 0.f;                                                             \
         const int ti = (16 * (a_) + l16) / R;                                                                 \
         const float cum_i = sCum[q][ti], gam_i = sGam[q][ti];                                                 \
+        const int j0 = (16 * (a_) + 4 * lg) / R;                                                              \
+        float cj[4], wj[4];                                                                                   \
+        if constexpr (R == 1) {                                                                               \
+            const float4 c4 = *reinterpret_cast<const float4*>(&sCum[q][j0]);                                 \
+            const float4 w4 = *reinterpret_cast<const float4*>(&sW[q][j0]);                                   \
+            cj[0] = c4.x; cj[1] = c4.y; cj[2] = c4.z; cj[3] = c4.w;                                           \
+            wj[0] = w4.x; wj[1] = w4.y; wj[2] = w4.z; wj[3] = w4.w;                                           \
+        } else if constexpr (R == 2) {                                                                        \
+            const float2 c2 = *reinterpret_cast<const float2*>(&sCum[q][j0]);                                 \
+            const float2 w2 = *reinterpret_cast<const float2*>(&sW[q][j0]);                                   \
+            cj[0] = cj[1] = c2.x; cj[2] = cj[3] = c2.y;                                                       \
+            wj[0] = wj[1] = w2.x; wj[2] = wj[3] = w2.y;                                                       \
+        } else {                                                                                              \
+            cj[0] = cj[1] = cj[2] = cj[3] = sCum[q][j0];                                                      \
+            wj[0] = wj[1] = wj[2] = wj[3] = sW[q][j0];                                                        \
+        }                                                                                                     \
         const float ei = __expf(cum_i - ref);                                                                 \
         _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) yv_[ct] *= ei;                                       \
         float mv[4];                                                                                          \
         _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                                       \
             const int tj = (16 * (a_) + 4 * lg + e) / R;                                                      \
-            const float ex = __expf(cum_i - sCum[q][tj]) * sW[q][tj];                                         \
+            const float ex = __expf(cum_i - cj[e]) * wj[e];                                                   \
             mv[e] = (tj < ti) ? ex : ((tj == ti) ? gam_i : 0.f);                                              \
         }                                                                                                     \
         const uint2 mp = {pack_bf16x2(gt[0] * mv[0], gt[1] * mv[1]), pack_bf16x2(gt[2] * mv[2], gt[3] * mv[3])}; \
         const s16x4 mf = __builtin_bit_cast(s16x4, mp);                                                       \
         _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) {                                                    \
-            yv_[ct] = mfma_k16(xf[ct], mf, yv_[ct]);                                                          \
-            yv_[ct] = mfma_k16(xf[ct], dI_hi, yv_[ct]);                                                       \
-            yv_[ct] = mfma_k16(xf[ct], dI_lo, yv_[ct]);                                                       \
+            yv_[ct] = mfma_k16(xf##S_[ct], mf, yv_[ct]);                                                      \
+            yv_[ct] = mfma_k16(xf##S_[ct], dI_hi, yv_[ct]);                                                   \
+            yv_[ct] = mfma_k16(xf##S_[ct], dI_lo, yv_[ct]);                                                   \
         }                                                                                                     \
     } while (0)
 
@@ -663,17 +699,11 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
             nextpos = static_cast<int64_t>(cn) * Q;
         }
 
-        if (FULL && !has_rows) {
-            // a wave without output rows still issues the stores and loads of one
-            uint16_t* yrow = p.y_sink + lane * 64;
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) *reinterpret_cast<uint2*>(yrow + 16 * ct) = uint2{0u, 0u};
-            M3_LOAD_CF(cf0, cn, 0);
-        }
         if (FULL && has_rows) {
             uint16_t* ych = p.y + ((tb + t0) * p.H + h) * static_cast<int64_t>(R * P);
-            bf16x8 btf[4];
-            s16x4 xf[4];
+            bf16x8 btfA[4], btfB[4];
+            s16x4 xfA[4], xfB[4];
+            float4 v0A, v1A, v0B, v1B;
             f32x4 y0[4], y1[4];
             // (4a) inter-chunk term; with two row blocks the S^T fragments serve both
 #pragma unroll
@@ -689,27 +719,87 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
             }
             M3_INTER_SCALE(y0, a_lo);
             if (MB == 2) M3_INTER_SCALE(y1, a_hi);
-            // (4b) intra-chunk tiles, column blocks in order; the diagonal tile closes a row block
-            for (int bb = 0; bb < a_lo; ++bb) {
-                M3_LOAD_COLS(bb);
-                M3_OFFDIAG(y0, cf0, a_lo, bb);
-                if (MB == 2) M3_OFFDIAG(y1, cf1, a_hi, bb);
+            // (4b) intra-chunk tiles, column blocks in order; the diagonal tile closes a row block.
+            // Two register sets: the operands of the next column block are read from LDS
+            // while the current block is multiplied.
+            M3_LOAD_COLS(A, 0);
+            M3_LOAD_V(v0A, a_lo, 0);
+            if (MB == 2) M3_LOAD_V(v1A, a_hi, 0);
+            int bb = 0;
+            for (; bb + 1 < a_lo; bb += 2) {   // column blocks bb (set A) and bb + 1 (set B)
+                M3_LOAD_COLS(B, bb + 1);
+                M3_LOAD_V(v0B, a_lo, bb + 1);
+                if (MB == 2) M3_LOAD_V(v1B, a_hi, bb + 1);
+                M3_FENCE();
+                M3_OFFDIAG(y0, cf0, A, v0A);
+                if (MB == 2) M3_OFFDIAG(y1, cf1, A, v1A);
+                M3_LOAD_COLS(A, bb + 2);
+                M3_LOAD_V(v0A, a_lo, bb + 2);
+                if (MB == 2) M3_LOAD_V(v1A, a_hi, bb + 2);
+                M3_FENCE();
+                M3_OFFDIAG(y0, cf0, B, v0B);
+                if (MB == 2) M3_OFFDIAG(y1, cf1, B, v1B);
             }
-            M3_LOAD_COLS(a_lo);
-            M3_DIAG(y0, cf0, a_lo);
-            if (MB == 2) M3_OFFDIAG(y1, cf1, a_hi, a_lo);
+            if (bb < a_lo) {                   // one block left (bb = a_lo - 1): set A, then set A <- block a_lo
+                M3_LOAD_COLS(B, a_lo);
+                if (MB == 2) M3_LOAD_V(v1B, a_hi, a_lo);
+                M3_FENCE();
+                M3_OFFDIAG(y0, cf0, A, v0A);
+                if (MB == 2) M3_OFFDIAG(y1, cf1, A, v1A);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    btfA[k] = btfB[k];
+                    xfA[k] = xfB[k];
+                }
+                v1A = v1B;
+            }
+            // set A holds block a_lo
+            if constexpr (MB == 2) {
+                if (a_lo + 1 < a_hi) {
+                    M3_LOAD_COLS(B, a_lo + 1);
+                    M3_LOAD_V(v1B, a_hi, a_lo + 1);
+                } else {
+                    M3_LOAD_COLS(B, a_hi);
+                }
+                M3_FENCE();
+            }
+            M3_DIAG(y0, cf0, a_lo, A);
+            if (MB == 2) M3_OFFDIAG(y1, cf1, A, v1A);
             M3_STORE_Y(y0, a_lo);
             M3_LOAD_CF(cf0, cn, a_lo);
             if constexpr (MB == 2) {
-                for (int bb = a_lo + 1; bb < a_hi; ++bb) {
-                    M3_LOAD_COLS(bb);
-                    M3_OFFDIAG(y1, cf1, a_hi, bb);
+                // set B holds block a_lo + 1 (or a_hi when that is the next one)
+                bb = a_lo + 1;
+                for (; bb + 1 < a_hi; bb += 2) {   // blocks bb (set B) and bb + 1 (set A)
+                    M3_LOAD_COLS(A, bb + 1);
+                    M3_LOAD_V(v1A, a_hi, bb + 1);
+                    M3_FENCE();
+                    M3_OFFDIAG(y1, cf1, B, v1B);
+                    M3_LOAD_COLS(B, bb + 2);
+                    if (bb + 2 < a_hi) M3_LOAD_V(v1B, a_hi, bb + 2);
+                    M3_FENCE();
+                    M3_OFFDIAG(y1, cf1, A, v1A);
                 }
-                M3_LOAD_COLS(a_hi);
-                M3_DIAG(y1, cf1, a_hi);
+                if (bb < a_hi) {                   // bb = a_hi - 1 in set B; then set B <- block a_hi
+                    M3_LOAD_COLS(A, a_hi);
+                    M3_FENCE();
+                    M3_OFFDIAG(y1, cf1, B, v1B);
+                    M3_DIAG(y1, cf1, a_hi, A);
+                } else {                           // set B holds block a_hi
+                    M3_DIAG(y1, cf1, a_hi, B);
+                }
                 M3_STORE_Y(y1, a_hi);
                 M3_LOAD_CF(cf1, cn, a_hi);
             }
+        } else if (FULL) {
+            // A wave without output rows still issues the stores and loads of one.  (An
+            // else branch: a separate if after the output work would merge this path's
+            // fresh Ct load into the output path's view of the counters, and the output
+            // path would then wait for every load in flight before its first product.)
+            uint16_t* yrow = p.y_sink + lane * 64;
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) *reinterpret_cast<uint2*>(yrow + 16 * ct) = uint2{0u, 0u};
+            M3_LOAD_CF(cf0, cn, 0);
         }
         if (FULL) M3_FETCH_B(cn);   // next chunk's Bt: registers held only across the state update
         // (5) state update: S <- R(phi_end) [e^{cum_end} S + Bt^T (s X)].  It reads only this
@@ -722,28 +812,35 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) sacc[rt][ct] *= decay;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                // A operand: Bt^T rows n0 + 16rt + l16, k = 32ks + 8lg .. +7, read transposed
-                bf16x8 bta[RT];
+            // Operands of k-step ks into slot ks & 1: the reads of step ks + 1 are issued
+            // before the products of step ks (the fence keeps them there), so each step's
+            // LDS latency is covered by the previous step's matrix work.
+            //   A operand: Bt^T rows n0 + 16rt + l16, k = 32ks + 8lg .. +7, read transposed
+            //   B operand: (s X)^T column p = p0 + 16ct + l16, k = 32ks + 8lg .. +7, read transposed
+            bf16x8 bta[2][RT], bxs[2][CT];
+            auto load_step = [&](int ks, int slot) __attribute__((always_inline)) {
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
                     const uint32_t src = aBtTr + (32 * ks * BS + 16 * rt) * 2;
                     const s16x4 lo = lds_tr4(src), hi = lds_tr4(src + 4 * BS * 2);
-                    bta[rt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    bta[slot][rt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
-                    // B operand: (s X)^T column p = p0 + 16ct + l16, k = 32ks + 8lg .. +7, read transposed
-                    const uint32_t xa = aXsTr + (32 * ks * P + 16 * ct) * 2;
+                    const uint32_t xa = aXsTr[ct] + 32 * ks * P * 2;
                     const s16x4 xlo = lds_tr4(xa), xhi = lds_tr4(xa + 4 * P * 2);
-                    const bf16x8 bx = __builtin_bit_cast(bf16x8, __builtin_shufflevector(xlo, xhi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-                    for (int rt = 0; rt < RT; ++rt) sacc[rt][ct] = mfma_k32(bta[rt], bx, sacc[rt][ct]);
+                    bxs[slot][ct] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(xlo, xhi, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
-                // one k-step of operands in flight at a time (the reads of the next step
-                // still overlap this step's matrix ops); hoisting them all costs registers
+            };
+            load_step(0, 0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + 1 < KS) load_step(ks + 1, (ks + 1) & 1);
                 __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) sacc[rt][ct] = mfma_k32(bta[ks & 1][rt], bxs[ks & 1][ct], sacc[rt][ct]);
             }
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
@@ -789,6 +886,8 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
 #undef M3_STAGE_TILES
 #undef M3_WRITE_SST
 #undef M3_LOAD_COLS
+#undef M3_LOAD_V
+#undef M3_FENCE
 #undef M3_GTILE
 #undef M3_OFFDIAG
 #undef M3_DIAG
