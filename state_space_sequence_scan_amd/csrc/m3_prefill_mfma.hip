@@ -242,12 +242,14 @@ __device__ float initial_state(const ScanParams& p, int b, int h, int g, int n, 
 
 // Element offset of (row, col) in a row-major [rows][P] bf16 LDS tile (P = 64: four
 // 32-byte column groups per 128-byte row) whose groups are permuted by row: group g of
-// row r is stored at position g ^ (r & 3).  A transposing read covers 4 consecutive
-// rows x one 32-byte group; rows 128 bytes apart would put all four on the same 8 of
-// the 32 banks, the permutation puts them on 4 different sets of 8.  Rows 4 apart
-// share the permutation, so moving by a multiple of 4 rows is a constant offset.
+// row r is stored at position g ^ f(r), f(r) = (r ^ (r >> 2)) & 3.  LDS has 64 banks of
+// 4 bytes and serves 32 lanes of a 64-bit read per clock; the transposing reads of these
+// tiles cover 8 rows x one 32-byte group per 32 lanes, and rows 128 bytes apart repeat
+// every other row on the same 32 banks.  With f the 8 rows land on 8 different sets of
+// 8 banks.  f depends only on bits 0-3 of the row, so moving by a multiple of 16 rows is a
+// constant offset.
 __device__ __forceinline__ int xoff(int row, int col) {
-    return row * P + ((((col >> 4) ^ row) & 3) << 4) + (col & 15);
+    return row * P + ((((col >> 4) ^ row ^ (row >> 2)) & 3) << 4) + (col & 15);
 }
 
 // Swap a value with the neighbouring lane (lane ^ 1) through a DPP quad permutation.
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
     const bool has_rows = NB >= NW || a_lo < NB;   // every wave has rows unless the chunk has fewer blocks
     // per-lane LDS bases (byte addresses); tile accesses add compile-time offsets
     const uint32_t aBtRow = lds_addr(&sBt[l16 * BS + 8 * lg]);                          // Bt tiles, A operand
-    const uint32_t aBtTr = lds_addr(&sBt[(8 * lg + (l16 >> 2)) * BS + n0 + 4 * (l16 & 3)]);   // Bt^T, transposed
+    const uint32_t aBtTr = lds_addr(&sBt[(4 * lg + (l16 >> 2)) * BS + n0 + 4 * (l16 & 3)]);   // Bt^T, transposed
     const uint32_t aBtW = lds_addr(&sBt[(tid >> 4) * BS + 8 * (tid & 15)]);             // Bt staging
     uint32_t aXTr[4], aXsTr[CT];   // X^T and (sX)^T, transposed: one base per 16-column tile
 #pragma unroll
@@ -364,7 +366,7 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
         aXTr[ct] = FULL ? lds_addr(&sX[xoff(4 * lg + (l16 >> 2), 16 * ct + 4 * (l16 & 3))]) : 0u;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
-        aXsTr[ct] = lds_addr(&sXs[xoff(8 * lg + (l16 >> 2), p0 + 16 * ct + 4 * (l16 & 3))]);
+        aXsTr[ct] = lds_addr(&sXs[xoff(4 * lg + (l16 >> 2), p0 + 16 * ct + 4 * (l16 & 3))]);
     const uint32_t aXW = FULL ? lds_addr(&sX[xoff(tid >> 3, 8 * (tid & 7))]) : 0u;      // X staging
     const uint32_t aXsW = lds_addr(&sXs[xoff(tid >> 3, 8 * (tid & 7))]);               // sX staging
     const uint32_t aST = FULL ? lds_addr(&sST[l16 * BS + 8 * lg]) : 0u;                 // S^T, A operand
@@ -705,16 +707,27 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
             s16x4 xfA[4], xfB[4];
             float4 v0A, v1A, v0B, v1B;
             f32x4 y0[4], y1[4];
-            // (4a) inter-chunk term; with two row blocks the S^T fragments serve both
+            // (4a) inter-chunk term; with two row blocks the S^T fragments serve both.  The
+            // fragments of column tile ct + 1 are read while tile ct is multiplied.
+            {
+                bf16x8 sf[2][4];
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-                y0[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-                y1[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int ks = 0; ks < 4; ++ks) sf[0][ks] = lds_ld<bf16x8>(aST + (32 * ks) * 2);
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const bf16x8 sf = lds_ld<bf16x8>(aST + (16 * ct * BS + 32 * ks) * 2);
-                    y0[ct] = mfma_k32(sf, oct(cf0, ks), y0[ct]);
-                    if (MB == 2) y1[ct] = mfma_k32(sf, oct(cf1, ks), y1[ct]);
+                for (int ct = 0; ct < 4; ++ct) {
+                    if (ct + 1 < 4) {
+#pragma unroll
+                        for (int ks = 0; ks < 4; ++ks)
+                            sf[(ct + 1) & 1][ks] = lds_ld<bf16x8>(aST + (16 * (ct + 1) * BS + 32 * ks) * 2);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    y0[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    y1[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        y0[ct] = mfma_k32(sf[ct & 1][ks], oct(cf0, ks), y0[ct]);
+                        if (MB == 2) y1[ct] = mfma_k32(sf[ct & 1][ks], oct(cf1, ks), y1[ct]);
+                    }
                 }
             }
             M3_INTER_SCALE(y0, a_lo);
@@ -814,21 +827,24 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
                 for (int ct = 0; ct < CT; ++ct) sacc[rt][ct] *= decay;
             // Operands of k-step ks into slot ks & 1: the reads of step ks + 1 are issued
             // before the products of step ks (the fence keeps them there), so each step's
-            // LDS latency is covered by the previous step's matrix work.
-            //   A operand: Bt^T rows n0 + 16rt + l16, k = 32ks + 8lg .. +7, read transposed
-            //   B operand: (s X)^T column p = p0 + 16ct + l16, k = 32ks + 8lg .. +7, read transposed
+            // LDS latency is covered by the previous step's matrix work.  Lane (l16, lg)
+            // supplies contraction rows 32ks + 4lg + (0..3) and 32ks + 16 + 4lg + (0..3)
+            // (the same assignment in both operands; 16 rows apart keeps the X tile reads
+            // on the bank-conflict-free permutation).
+            //   A operand: Bt^T rows n0 + 16rt + l16, read transposed
+            //   B operand: (s X)^T column p = p0 + 16ct + l16, read transposed
             bf16x8 bta[2][RT], bxs[2][CT];
             auto load_step = [&](int ks, int slot) __attribute__((always_inline)) {
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
                     const uint32_t src = aBtTr + (32 * ks * BS + 16 * rt) * 2;
-                    const s16x4 lo = lds_tr4(src), hi = lds_tr4(src + 4 * BS * 2);
+                    const s16x4 lo = lds_tr4(src), hi = lds_tr4(src + 16 * BS * 2);
                     bta[slot][rt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
                     const uint32_t xa = aXsTr[ct] + 32 * ks * P * 2;
-                    const s16x4 xlo = lds_tr4(xa), xhi = lds_tr4(xa + 4 * P * 2);
+                    const s16x4 xlo = lds_tr4(xa), xhi = lds_tr4(xa + 16 * P * 2);
                     bxs[slot][ct] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(xlo, xhi, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
             };
