@@ -7,6 +7,8 @@ calls it, and it shares no code with the HIP library.
 Contents
   * ``scan``          -- ctypes front end of ``m3_oracle.c``: the sequential
                          fp64 loop over t (the definition written out).
+  * ``scan_backward`` -- its reverse-mode derivative (the adjoint loop of
+                         ``m3_oracle.c``), pinned by finite differences of ``scan``.
   * ``m3_oracle_np``  -- two independent numpy formulations used to pin it:
                          complex modes (``scan_complex``) and the dense
                          semiseparable matrix (``scan_dense``).
@@ -53,6 +55,9 @@ def load(path: str = _LIB):
     f = lib.m3o_scan_rounded
     f.restype = ctypes.c_int
     f.argtypes = [ctypes.POINTER(_Dims)] + [ctypes.c_void_p] * 14 + [ctypes.c_int]
+    f = lib.m3o_scan_backward
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.POINTER(_Dims)] + [ctypes.c_void_p] * 24 + [ctypes.c_int]
     lib.m3o_round_bf16.restype = ctypes.c_double
     lib.m3o_round_bf16.argtypes = [ctypes.c_double]
     lib.m3o_max_threads.restype = ctypes.c_int
@@ -127,3 +132,45 @@ def scan(x, dt, A, lam, theta, B, C, D, state_in=None, nthreads: int = 0, lib_pa
     if rc != 0:
         raise ValueError(f"m3o_scan failed with code {rc}")
     return y, h_out
+
+
+def scan_backward(x, dt, A, lam, theta, B, C, D, dy, dh_out=None, state_in=None, nthreads: int = 0,
+                  lib_path: str = _LIB):
+    """Gradient of sum_t <dy_t, y_t> + <dh_out, h_L> with respect to every input of ``scan``.
+
+    Same shapes and ``state_in`` as ``scan``; ``dy`` has the shape of y and ``dh_out``
+    (optional) that of the final state.  Returns a dict with dx, ddt, dA, dlam, dtheta,
+    dB, dC, dD (shapes of the inputs; dB, dC and dtheta summed over the heads of a
+    group, dA and dD over batch and tokens), dh0 (b,H,N,P) and, when the state carries
+    a previous input, db_last (b,G,R,N) and dx_last (b,H,R,P).
+    """
+    x, dt, A, lam, theta, B, C, D, dy = map(_f64, (x, dt, A, lam, theta, B, C, D, dy))
+    b, L, H, R, P = x.shape
+    G, N = B.shape[2], B.shape[4]
+    assert dy.shape == x.shape
+    h0 = bl = xl = None
+    if state_in is not None:
+        h0, bl, xl = state_in
+        h0 = None if h0 is None else _f64(h0)
+        bl = None if bl is None else _f64(bl)
+        xl = None if xl is None else _f64(xl)
+    dho = None if dh_out is None else _f64(dh_out)
+    if dho is not None:
+        assert dho.shape == (b, H, N, P)
+    carry = bl is not None and xl is not None
+    out = {"dx": np.empty_like(x), "ddt": np.empty_like(dt), "dA": np.empty((H,)),
+           "dlam": np.empty_like(lam), "dtheta": np.empty_like(theta), "dB": np.empty_like(B),
+           "dC": np.empty_like(C), "dD": np.empty((H,)), "dh0": np.empty((b, H, N, P))}
+    if carry:
+        out["db_last"] = np.empty((b, G, R, N))
+        out["dx_last"] = np.empty((b, H, R, P))
+    d = _Dims(b, L, H, G, P, N, R)
+    rc = load(lib_path).m3o_scan_backward(
+        ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(lam), _ptr(theta), _ptr(B), _ptr(C),
+        _ptr(D), _ptr(h0), _ptr(bl), _ptr(xl), _ptr(dy), _ptr(dho), _ptr(out["dx"]),
+        _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dlam"]), _ptr(out["dtheta"]), _ptr(out["dB"]),
+        _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dh0"]), _ptr(out.get("db_last")),
+        _ptr(out.get("dx_last")), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"m3o_scan_backward failed with code {rc}")
+    return out

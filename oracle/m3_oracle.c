@@ -218,3 +218,261 @@ int m3o_max_threads(void) {
     return 1;
 #endif
 }
+
+/*
+ * Backward pass (reverse-mode derivative) of the scan, for training.
+ *
+ * Given output cotangents dy (batch, L, H, R, P) and, optionally, a cotangent
+ * dh_out (batch, H, N, P) of the final state, returns the gradient of
+ *     Lsum = sum_t <dy_t, Y_t> + <dh_out, h_L>
+ * with respect to every input of m3o_scan: dx, ddt, dlambda (shapes of their
+ * inputs), dA and dD (H), dtheta (batch, L, G, N/2), dB and dC (batch, L, G, R, N)
+ * (summed over the heads of a group, which share B, C and theta), dh0, and the
+ * carried previous input db_last / dx_last when a carry is given.
+ *
+ * It is the same recurrence run backwards (adjoint method), written from the
+ * forward definition above: with g_t = dLsum/dh_t and q_t = M_t^T g_t,
+ *   g_t     = sum_r C_t[:,r] dy_t[r,:]^T + alpha_{t+1} q_{t+1}
+ *   dU_t    = gamma_t g_t + beta_{t+1} q_{t+1}                 (U_t feeds h_t and h_{t+1})
+ *   dalpha_t = <q_t, h_{t-1}>,  dbeta_t = <q_t, U_{t-1}>,  dgamma_t = <g_t, U_t>
+ *   dtheta_{t,k} = sum_p ( q_t[2k+1,p] v_t[2k,p] - q_t[2k,p] v_t[2k+1,p] ),
+ *                  v_t = alpha_t h_{t-1} + beta_t U_{t-1}     (derivative of the 2x2 rotation)
+ *   dC_t[:,r] = h_t dy_t[r,:],  dB_t[:,r] = dU_t X_t[r,:],  dX_t[r,:] = D dy_t[r,:] + B_t[:,r]^T dU_t
+ *   dD = sum_t <dy_t, X_t>,  dh0 = alpha_1 q_1,  dU_0 = beta_1 q_1 (the carried input)
+ * and the chain rule through alpha = exp(dt A), beta = (1 - lambda) dt alpha,
+ * gamma = lambda dt for ddt, dlambda and dA.
+ *
+ * The forward states are recomputed and kept for the whole slice (fp64, L + 1
+ * states of N x P), which suits the small sizes it is used at.
+ * Returns 0, -1 on a shape error, -2 if memory cannot be allocated.
+ */
+static int backward_batch(const m3o_dims* dm, int64_t b,
+                          const double* x, const double* dt, const double* A, const double* lam,
+                          const double* theta, const double* B, const double* C, const double* D,
+                          const double* h0, const double* b_last, const double* x_last,
+                          const double* dy, const double* dh_out,
+                          double* dx, double* ddt, double* dA_b, double* dlam, double* dtheta,
+                          double* dB, double* dC, double* dD_b, double* dh0, double* db_last,
+                          double* dx_last) {
+    const int64_t L = dm->seqlen, H = dm->nheads, G = dm->ngroups;
+    const int64_t P = dm->headdim, N = dm->dstate, R = dm->rank, K = N / 2, NP = N * P;
+    const int carry = (b_last && x_last);
+    double* hall = (double*)malloc(sizeof(double) * (size_t)(L + 1) * NP);
+    double* work = (double*)malloc(sizeof(double) * 6 * (size_t)NP);
+    if (!hall || !work) {
+        free(hall);
+        free(work);
+        return -2;
+    }
+    double *U = work, *Up = work + NP, *g = work + 2 * NP, *q = work + 3 * NP, *qn = work + 4 * NP,
+           *dU = work + 5 * NP;
+
+    for (int64_t h = 0; h < H; ++h) {
+        const int64_t gi = h / (H / G);
+        /* forward states h_0 .. h_L of this slice (index t + 1 holds h after token t) */
+        for (int64_t i = 0; i < NP; ++i) hall[i] = h0 ? h0[(b * H + h) * NP + i] : 0.0;
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t p = 0; p < P; ++p) {
+                double u = 0.0;
+                if (carry)
+                    for (int64_t r = 0; r < R; ++r)
+                        u += b_last[((b * G + gi) * R + r) * N + n] * x_last[((b * H + h) * R + r) * P + p];
+                Up[n * P + p] = u;
+            }
+        for (int64_t t = 0; t < L; ++t) {
+            const double dtv = dt[(b * L + t) * H + h], lv = lam[(b * L + t) * H + h];
+            const double alpha = exp(dtv * A[h]), beta = (1.0 - lv) * dtv * alpha, gamma = lv * dtv;
+            for (int64_t n = 0; n < N; ++n)
+                for (int64_t p = 0; p < P; ++p) {
+                    double u = 0.0;
+                    for (int64_t r = 0; r < R; ++r)
+                        u += B[IDX5(b, t, gi, r, n, L, G, R, N)] * x[IDX5(b, t, h, r, p, L, H, R, P)];
+                    U[n * P + p] = u;
+                }
+            const double* hp = hall + t * NP;
+            double* hn = hall + (t + 1) * NP;
+            for (int64_t k = 0; k < K; ++k) {
+                const double th = theta[((b * L + t) * G + gi) * K + k], c = cos(th), s = sin(th);
+                for (int64_t p = 0; p < P; ++p) {
+                    const double v0 = alpha * hp[(2 * k) * P + p] + beta * Up[(2 * k) * P + p];
+                    const double v1 = alpha * hp[(2 * k + 1) * P + p] + beta * Up[(2 * k + 1) * P + p];
+                    hn[(2 * k) * P + p] = c * v0 - s * v1 + gamma * U[(2 * k) * P + p];
+                    hn[(2 * k + 1) * P + p] = s * v0 + c * v1 + gamma * U[(2 * k + 1) * P + p];
+                }
+            }
+            memcpy(Up, U, sizeof(double) * NP);
+        }
+
+        /* reverse sweep; the final-state cotangent enters as a token after the last one
+           with alpha = 1, beta = 0 and no rotation */
+        for (int64_t i = 0; i < NP; ++i) qn[i] = dh_out ? dh_out[(b * H + h) * NP + i] : 0.0;
+        double beta_next = 0.0, alpha_next = 1.0;
+        double dA_h = 0.0, dD_h = 0.0;
+        for (int64_t t = L - 1; t >= 0; --t) {
+            const double dtv = dt[(b * L + t) * H + h], lv = lam[(b * L + t) * H + h];
+            const double alpha = exp(dtv * A[h]), beta = (1.0 - lv) * dtv * alpha, gamma = lv * dtv;
+            const double* ht = hall + (t + 1) * NP;
+            const double* hp = hall + t * NP;
+            /* g_t = alpha_{t+1} q_{t+1} + C_t dy_t^T */
+            for (int64_t n = 0; n < N; ++n)
+                for (int64_t p = 0; p < P; ++p) {
+                    double a = alpha_next * qn[n * P + p];
+                    for (int64_t r = 0; r < R; ++r)
+                        a += C[IDX5(b, t, gi, r, n, L, G, R, N)] * dy[IDX5(b, t, h, r, p, L, H, R, P)];
+                    g[n * P + p] = a;
+                }
+            /* output side: dC, dD, the skip part of dX */
+            for (int64_t r = 0; r < R; ++r) {
+                for (int64_t n = 0; n < N; ++n) {
+                    double a = 0.0;
+                    for (int64_t p = 0; p < P; ++p) a += ht[n * P + p] * dy[IDX5(b, t, h, r, p, L, H, R, P)];
+                    dC[IDX5(b, t, gi, r, n, L, G, R, N)] += a;
+                }
+                for (int64_t p = 0; p < P; ++p) {
+                    const int64_t xi = IDX5(b, t, h, r, p, L, H, R, P);
+                    dD_h += dy[xi] * x[xi];
+                    dx[xi] = D[h] * dy[xi];
+                }
+            }
+            /* U_t, U_{t-1} */
+            for (int64_t n = 0; n < N; ++n)
+                for (int64_t p = 0; p < P; ++p) {
+                    double u = 0.0, up = 0.0;
+                    for (int64_t r = 0; r < R; ++r) {
+                        u += B[IDX5(b, t, gi, r, n, L, G, R, N)] * x[IDX5(b, t, h, r, p, L, H, R, P)];
+                        if (t > 0)
+                            up += B[IDX5(b, t - 1, gi, r, n, L, G, R, N)] * x[IDX5(b, t - 1, h, r, p, L, H, R, P)];
+                        else if (carry)
+                            up += b_last[((b * G + gi) * R + r) * N + n] * x_last[((b * H + h) * R + r) * P + p];
+                    }
+                    U[n * P + p] = u;
+                    Up[n * P + p] = up;
+                }
+            /* dU_t = gamma_t g_t + beta_{t+1} q_{t+1};  dgamma_t = <g_t, U_t> */
+            double dgam = 0.0;
+            for (int64_t i = 0; i < NP; ++i) {
+                dU[i] = gamma * g[i] + beta_next * qn[i];
+                dgam += g[i] * U[i];
+            }
+            /* q_t = M_t^T g_t; dalpha, dbeta, dtheta */
+            double dal = 0.0, dbe = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double th = theta[((b * L + t) * G + gi) * K + k], c = cos(th), s = sin(th);
+                double dth = 0.0;
+                for (int64_t p = 0; p < P; ++p) {
+                    const double g0 = g[(2 * k) * P + p], g1 = g[(2 * k + 1) * P + p];
+                    const double q0 = c * g0 + s * g1, q1 = -s * g0 + c * g1;
+                    q[(2 * k) * P + p] = q0;
+                    q[(2 * k + 1) * P + p] = q1;
+                    const double h0v = hp[(2 * k) * P + p], h1v = hp[(2 * k + 1) * P + p];
+                    const double u0 = Up[(2 * k) * P + p], u1 = Up[(2 * k + 1) * P + p];
+                    dal += q0 * h0v + q1 * h1v;
+                    dbe += q0 * u0 + q1 * u1;
+                    const double v0 = alpha * h0v + beta * u0, v1 = alpha * h1v + beta * u1;
+                    dth += q1 * v0 - q0 * v1;
+                }
+                dtheta[((b * L + t) * G + gi) * K + k] += dth;
+            }
+            /* dB_t, dX_t from dU_t */
+            for (int64_t r = 0; r < R; ++r) {
+                for (int64_t n = 0; n < N; ++n) {
+                    double a = 0.0;
+                    for (int64_t p = 0; p < P; ++p) a += dU[n * P + p] * x[IDX5(b, t, h, r, p, L, H, R, P)];
+                    dB[IDX5(b, t, gi, r, n, L, G, R, N)] += a;
+                }
+                for (int64_t p = 0; p < P; ++p) {
+                    double a = 0.0;
+                    for (int64_t n = 0; n < N; ++n) a += B[IDX5(b, t, gi, r, n, L, G, R, N)] * dU[n * P + p];
+                    dx[IDX5(b, t, h, r, p, L, H, R, P)] += a;
+                }
+            }
+            /* scalars through alpha = exp(dt A), beta = (1 - lambda) dt alpha, gamma = lambda dt */
+            ddt[(b * L + t) * H + h] = dal * A[h] * alpha + dbe * (1.0 - lv) * (alpha + dtv * A[h] * alpha) + dgam * lv;
+            dlam[(b * L + t) * H + h] = -dbe * dtv * alpha + dgam * dtv;
+            dA_h += dal * dtv * alpha + dbe * (1.0 - lv) * dtv * dtv * alpha;
+            memcpy(qn, q, sizeof(double) * NP);
+            alpha_next = alpha;
+            beta_next = beta;
+        }
+        /* h_0 and the carried previous input (with no token, h_L is h_0 itself and the
+           final-state cotangent passes through) */
+        if (dh0)
+            for (int64_t i = 0; i < NP; ++i) dh0[(b * H + h) * NP + i] = alpha_next * qn[i];
+        if (carry && (db_last || dx_last)) {
+            for (int64_t i = 0; i < NP; ++i) dU[i] = beta_next * qn[i];
+            for (int64_t r = 0; r < R; ++r) {
+                if (db_last)
+                    for (int64_t n = 0; n < N; ++n) {
+                        double a = 0.0;
+                        for (int64_t p = 0; p < P; ++p) a += dU[n * P + p] * x_last[((b * H + h) * R + r) * P + p];
+                        db_last[((b * G + gi) * R + r) * N + n] += a;
+                    }
+                if (dx_last)
+                    for (int64_t p = 0; p < P; ++p) {
+                        double a = 0.0;
+                        for (int64_t n = 0; n < N; ++n) a += b_last[((b * G + gi) * R + r) * N + n] * dU[n * P + p];
+                        dx_last[((b * H + h) * R + r) * P + p] = a;
+                    }
+            }
+        } else if (dx_last) {
+            for (int64_t r = 0; r < R; ++r)
+                for (int64_t p = 0; p < P; ++p) dx_last[((b * H + h) * R + r) * P + p] = 0.0;
+        }
+        dA_b[h] += dA_h;
+        dD_b[h] += dD_h;
+    }
+    free(hall);
+    free(work);
+    return 0;
+}
+
+/* Backward of m3o_scan (see backward_batch).  Group-shared gradients (dtheta,
+ * dB, dC, db_last) and the per-head sums dA, dD are accumulated, so each batch
+ * element is handled by one thread; the outputs are overwritten, not added to.
+ * dh_out, dh0, db_last and dx_last may be NULL. */
+int m3o_scan_backward(const m3o_dims* dm, const double* x, const double* dt, const double* A,
+                      const double* lam, const double* theta, const double* B, const double* C,
+                      const double* D, const double* h0, const double* b_last, const double* x_last,
+                      const double* dy, const double* dh_out, double* dx, double* ddt, double* dA,
+                      double* dlam, double* dtheta, double* dB, double* dC, double* dD, double* dh0,
+                      double* db_last, double* dx_last, int nthreads) {
+    if (!dm || !dy || !dx || !ddt || !dA || !dlam || !dtheta || !dB || !dC || !dD || dm->batch < 0 ||
+        dm->seqlen < 0 || dm->nheads <= 0 || dm->ngroups <= 0 || dm->headdim <= 0 || dm->dstate <= 0 ||
+        dm->rank <= 0 || dm->dstate % 2 != 0 || dm->nheads % dm->ngroups != 0)
+        return -1;
+    const int64_t b_ = dm->batch, L = dm->seqlen, H = dm->nheads, G = dm->ngroups;
+    const int64_t N = dm->dstate, R = dm->rank;
+    memset(dtheta, 0, sizeof(double) * (size_t)(b_ * L * G * (N / 2)));
+    memset(dB, 0, sizeof(double) * (size_t)(b_ * L * G * R * N));
+    memset(dC, 0, sizeof(double) * (size_t)(b_ * L * G * R * N));
+    if (db_last) memset(db_last, 0, sizeof(double) * (size_t)(b_ * G * R * N));
+    double* partial = (double*)calloc((size_t)(2 * b_ * H + 1), sizeof(double));   /* dA, dD per batch */
+    if (!partial) return -2;
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t b = 0; b < b_; ++b) {
+        const int rc = backward_batch(dm, b, x, dt, A, lam, theta, B, C, D, h0, b_last, x_last, dy,
+                                      dh_out, dx, ddt, partial + b * H, dlam, dtheta, dB, dC,
+                                      partial + (b_ + b) * H, dh0, db_last, dx_last);
+        if (rc) {
+#pragma omp atomic write
+            err = rc;
+        }
+    }
+    for (int64_t h = 0; h < H; ++h) {
+        double a = 0.0, d = 0.0;
+        for (int64_t b = 0; b < b_; ++b) {   /* fixed order: the result does not depend on threads */
+            a += partial[b * H + h];
+            d += partial[(b_ + b) * H + h];
+        }
+        dA[h] = a;
+        dD[h] = d;
+    }
+    free(partial);
+    return err;
+}
