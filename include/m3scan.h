@@ -169,6 +169,56 @@ m3_status m3_decode_step(const m3_dims* dims, void* h, const void* b_last,
                          const void* B_t, const void* C_t, const float* D, void* y_t,
                          void* stream);
 
+/* Gradients written by m3_backward; every array is fp32, in the layout of the
+ * input it belongs to.  dh0, db_last and dx_last may be NULL (not wanted). */
+typedef struct {
+    float* dx;       /* (batch, L, H, R, P)                                        */
+    float* ddt;      /* (batch, L, H)                                              */
+    float* dA;       /* (H): summed over batch and tokens                         */
+    float* dlambda;  /* (batch, L, H)                                              */
+    float* dtheta;   /* (batch, L, G, N/2): summed over the heads of each group    */
+    float* dB;       /* (batch, L, G, R, N): summed over the heads of each group   */
+    float* dC;       /* (batch, L, G, R, N): summed over the heads of each group   */
+    float* dD;       /* (H): summed over batch and tokens                         */
+    float* dh0;      /* (batch, H, N, P): gradient of state_in->h                  */
+    float* db_last;  /* (batch, G, R, N): of state_in->b_last (zero without a carry) */
+    float* dx_last;  /* (batch, H, R, P): of state_in->x_last (zero without a carry) */
+} m3_grads;
+
+/* Bytes of device workspace m3_backward needs for these dims (may be large: the
+ * state of every (b, h) after every third token, N * P * 4 bytes each, plus,
+ * when H > G, per-head copies of the group-shared gradients).
+ * Errors: M3_ERR_INVALID_ARG for bad dims or a NULL `bytes`;
+ * M3_ERR_UNSUPPORTED for shapes m3_backward does not handle. */
+m3_status m3_backward_workspace_size(const m3_dims* dims, size_t* bytes);
+
+/*
+ * Backward pass of the scan for training: the derivative of
+ *     Loss = sum_t <dy_t, y_t> + <dh_out, h_L>
+ * (y and h_L as m3_prefill_chunked computes them from the same inputs and
+ * state_in) with respect to every input, by the adjoint method on the
+ * recurrence of the Mamba-3 paper note ("Solution 1" update, "Solution 2"
+ * rotation, "Solution 3" rank-R input/output).  The forward states are
+ * recomputed from checkpoints in the workspace; nothing from a previous
+ * prefill call is needed.
+ *
+ * Supported: dstate 128, headdim 64, rank 1, 2 or 4; io dtype fp32 or bf16;
+ * state_in->h in dims->state_dtype.  dims->chunk is ignored.  All arithmetic
+ * is fp32.  Results do not depend on scheduling (no atomics).
+ * state_in:  NULL or as for m3_prefill_chunked (h non-NULL; carry optional).
+ * dy:        (batch, L, H, R, P) in the io dtype.
+ * dh_out:    NULL (zero) or (batch, H, N, P) fp32.
+ * grads:     every pointer of m3_grads except dh0, db_last, dx_last non-NULL.
+ * workspace: at least m3_backward_workspace_size bytes; contents ignored.
+ * Errors:    M3_ERR_INVALID_ARG (NULL pointers, bad dims), M3_ERR_UNSUPPORTED,
+ *            M3_ERR_WORKSPACE, M3_ERR_HIP -- all before any launch except the last.
+ */
+m3_status m3_backward(const m3_dims* dims, const void* x, const float* dt, const float* A,
+                      const float* lambda, const float* theta, const void* B, const void* C,
+                      const float* D, const m3_state* state_in, const void* dy,
+                      const float* dh_out, const m3_grads* grads, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* m3_status_string(m3_status status);
 

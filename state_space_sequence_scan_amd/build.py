@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libm3scan.so")
 ARCH = "gfx950"
 
-SOURCES = ["m3_api.cpp", "m3_decode.hip", "m3_prefill_generic.hip", "m3_prefill_mfma.hip"]
+SOURCES = ["m3_api.cpp", "m3_decode.hip", "m3_prefill_generic.hip", "m3_prefill_mfma.hip", "m3_backward.hip"]
 
 FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
          "-Wall", "-Wno-unused-function",

@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int32_t kVersion = 102;  // 0.1.2: state dtype, packed variable-length prefill
+constexpr int32_t kVersion = 103;  // 0.1.3: backward pass
 constexpr size_t kMaxLds = 160 * 1024;
 
 bool dims_ok(const m3_dims* d, bool prefill) {
@@ -212,6 +212,82 @@ m3_status m3_decode_step(const m3_dims* dims, void* h, const void* b_last, const
     if (dims->batch * dims->nheads > 0x7fffffffLL) return M3_ERR_UNSUPPORTED;
     if (!m3::decode_supported(a)) return M3_ERR_UNSUPPORTED;
     const hipError_t e = m3::launch_decode(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
+}  // extern "C"
+
+namespace {
+
+m3::BwdShape bwd_shape(const m3_dims* d) {
+    return m3::BwdShape{d->batch, d->seqlen, static_cast<int>(d->nheads), static_cast<int>(d->ngroups),
+                        static_cast<int>(d->dstate), static_cast<int>(d->headdim), static_cast<int>(d->rank)};
+}
+
+}  // namespace
+
+extern "C" {
+
+m3_status m3_backward_workspace_size(const m3_dims* dims, size_t* bytes) {
+    if (!bytes || !dims_ok(dims, true)) return M3_ERR_INVALID_ARG;
+    const m3::BwdShape s = bwd_shape(dims);
+    if (!m3::backward_supported(s)) return M3_ERR_UNSUPPORTED;
+    *bytes = m3::backward_layout(s).bytes;
+    return M3_OK;
+}
+
+m3_status m3_backward(const m3_dims* dims, const void* x, const float* dt, const float* A,
+                      const float* lambda, const float* theta, const void* B, const void* C,
+                      const float* D, const m3_state* state_in, const void* dy,
+                      const float* dh_out, const m3_grads* grads, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    if (!dims_ok(dims, true) || !grads) return M3_ERR_INVALID_ARG;
+    if (!A || !D || !grads->dA || !grads->dD) return M3_ERR_INVALID_ARG;
+    const bool any_tokens = dims->seqlen > 0;
+    if (any_tokens && (!x || !dt || !lambda || !theta || !B || !C || !dy || !grads->dx || !grads->ddt ||
+                       !grads->dlambda || !grads->dtheta || !grads->dB || !grads->dC))
+        return M3_ERR_INVALID_ARG;
+    if (state_in && !state_in->h) return M3_ERR_INVALID_ARG;
+    const m3::BwdShape s = bwd_shape(dims);
+    if (!m3::backward_supported(s)) return M3_ERR_UNSUPPORTED;
+    const m3::BwdLayout lay = m3::backward_layout(s);
+    if (lay.bytes > 0 && (!workspace || workspace_bytes < lay.bytes)) return M3_ERR_WORKSPACE;
+    m3::BwdArgs a{};
+    a.x = x;
+    a.dt = dt;
+    a.A = A;
+    a.lam = lambda;
+    a.theta = theta;
+    a.B = B;
+    a.C = C;
+    a.D = D;
+    a.h0 = state_in ? state_in->h : nullptr;
+    a.bl = (state_in && state_in->b_last && state_in->x_last) ? state_in->b_last : nullptr;
+    a.xl = (state_in && state_in->b_last && state_in->x_last) ? state_in->x_last : nullptr;
+    a.dy = dy;
+    a.dh_out = dh_out;
+    a.dx = grads->dx;
+    a.ddt = grads->ddt;
+    a.dA = grads->dA;
+    a.dlam = grads->dlambda;
+    a.dtheta = grads->dtheta;
+    a.dB = grads->dB;
+    a.dC = grads->dC;
+    a.dD = grads->dD;
+    a.dh0 = grads->dh0;
+    a.dbl = grads->db_last;
+    a.dxl = grads->dx_last;
+    a.workspace = workspace;
+    a.batch = s.batch;
+    a.L = s.L;
+    a.H = s.H;
+    a.G = s.G;
+    a.N = s.N;
+    a.P = s.P;
+    a.R = s.R;
+    a.bf16 = dims->io_dtype == M3_BF16;
+    a.state_bf16 = dims->state_dtype == M3_BF16;
+    const hipError_t e = m3::launch_backward(a, lay, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? M3_OK : M3_ERR_HIP;
 }
 

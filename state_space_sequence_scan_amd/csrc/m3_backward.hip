@@ -1,0 +1,565 @@
+// m3_backward.hip -- backward pass (reverse-mode derivative) of the Mamba-3 scan
+// on gfx950, for training.
+//
+// The forward recurrence is the one of the prefill kernels (Mamba-3 paper note,
+// "Solution 1" exponential-trapezoidal update, "Solution 2" rotation of state
+// pairs, "Solution 3" rank-R input and output).  Its derivative is taken by the
+// adjoint method: with g_t = dLoss/dh_t and q_t = M_t^T g_t (M_t the rotation),
+//   g_t  = C_t dy_t^T + alpha_{t+1} q_{t+1}           (the adjoint runs backwards)
+//   dU_t = gamma_t g_t + beta_{t+1} q_{t+1}           (U_t = B_t X_t feeds h_t and h_{t+1})
+// and every input gradient is a contraction of g_t, q_t, dU_t with the forward
+// quantities (see m3_backward below).  The adjoint needs h_{t-1} and h_t at
+// every step; they are not stored per token.  A forward sweep keeps h after
+// every KS-th token in a workspace (checkpoints); the reverse sweep takes the
+// segments of KS tokens last to first, recomputes the segment's states into LDS
+// from the previous checkpoint, and walks them backwards.
+//
+// One workgroup per (batch, head), 512 threads; thread t owns state rows
+// 4 (t >> 4) .. +3 (two rotation pairs) and columns 4 (t & 15) .. +3, of h and of
+// the adjoint, in registers.  Sums over columns (dB, dC, dtheta) are taken
+// within the 16 lanes that share rows, by DPP lane exchanges; sums over rows
+// (dX) and over the whole state (dalpha, dbeta, dgamma) go through LDS, one
+// barrier per token.  Gradients of inputs shared by the heads of a group (B, C,
+// theta, the carried B) are written per head and summed by a second kernel in a
+// fixed order, so results do not depend on scheduling.  All gradients are fp32.
+#include "m3_common.h"
+#include "m3_internal.h"
+
+namespace m3 {
+namespace bw {
+
+constexpr int N = 128;
+constexpr int P = 64;
+constexpr int NT = 512;
+constexpr int KS = 3;           // tokens per recompute segment
+constexpr int PS = P;           // row of a state in LDS (a 16-lane group reads or writes one row)
+
+template <typename T> struct ld;
+template <> struct ld<float> {
+    __device__ __forceinline__ static void v4(const float* p, float* o) {
+        const float4 v = *reinterpret_cast<const float4*>(p);
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    }
+};
+template <> struct ld<bf16_t> {
+    __device__ __forceinline__ static void v4(const bf16_t* p, float* o) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+        o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+    }
+};
+
+// Sum over the 16 lanes of a DPP row (the lanes that share state rows); every lane gets it.
+__device__ __forceinline__ float sum16(float v) {
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));   // lane ^ 1
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));   // lane ^ 2
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));  // half-row mirror
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true));  // row rotate by 8
+    return v;
+}
+// Sum over the 64 lanes of a wave; valid in lane 63.
+__device__ __forceinline__ float sum64(float v) {
+    v = sum16(v);
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));  // row_bcast:15
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));  // row_bcast:31
+    return v;
+}
+// Sum over the 4 DPP rows of a wave (lanes 16 and 32 apart); every lane gets it.
+__device__ __forceinline__ float sum_rows(float v) {
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+template <typename T, int R>
+__global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
+    const int bh = blockIdx.x;
+    const int b = bh / a.H, h = bh - b * a.H, g = h / (a.H / a.G);
+    const int tid = threadIdx.x, cb = tid & 15, pb = tid >> 4, lane = tid & 63, wv = tid >> 6;
+    const int r0 = 4 * pb, c0 = 4 * cb;   // state rows r0 .. r0+3 (two rotation pairs), columns c0 .. c0+3
+    const int64_t L = a.L;
+    const int H = a.H, G = a.G;
+    const float Ah = a.A[h], Dh = a.D[h];
+    const int64_t nseg = (L + KS - 1) / KS;
+    float* ck = a.ckpt + static_cast<size_t>(bh) * nseg * N * P;
+    const bool carry = a.bl && a.xl;
+    const T* x = static_cast<const T*>(a.x);
+    const T* dy = static_cast<const T*>(a.dy);
+    const T* Bm = static_cast<const T*>(a.B);
+    const T* Cm = static_cast<const T*>(a.C);
+    // group-shared gradients go to per-head rows when heads share a group
+    const int gh = a.per_head ? h : g, GH = a.per_head ? H : G;
+
+    __shared__ __align__(16) float sH[KS][N * PS];              // states h_{t0-1} .. h_{t0+len-2}
+    __shared__ __align__(16) float sDX[2][NT / 64][R * P];       // per-wave dX sums, by token parity
+    __shared__ float sSc[2][NT / 64][4];                         // per-wave dalpha, dbeta, dgamma, dD
+
+    auto xoff = [&](int64_t t, int r) { return ((static_cast<int64_t>(b) * L + t) * H + h) * (R * P) + r * P + c0; };
+    auto boff = [&](int64_t t, int r) { return ((static_cast<int64_t>(b) * L + t) * G + g) * (R * N) + r * N + r0; };
+    auto toff = [&](int64_t t) { return ((static_cast<int64_t>(b) * L + t) * G + g) * (N / 2) + 2 * pb; };
+    auto soff = [&](int64_t t) { return (static_cast<int64_t>(b) * L + t) * H + h; };
+
+    // B rows and X columns of token t (t = -1: the carried previous input, or zero)
+    auto load_bx = [&](int64_t t, float (&Bv)[R][4], float (&Xv)[R][4]) {
+        if (t >= 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                ld<T>::v4(Bm + boff(t, r), Bv[r]);
+                ld<T>::v4(x + xoff(t, r), Xv[r]);
+            }
+        } else if (carry) {
+            const T* bl = static_cast<const T*>(a.bl);
+            const T* xl = static_cast<const T*>(a.xl);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                ld<T>::v4(bl + ((static_cast<int64_t>(b) * G + g) * R + r) * N + r0, Bv[r]);
+                ld<T>::v4(xl + ((static_cast<int64_t>(b) * H + h) * R + r) * P + c0, Xv[r]);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Bv[r][i] = Xv[r][i] = 0.f;
+        }
+    };
+    auto uval = [&](const float (&Bv)[R][4], const float (&Xv)[R][4], int i, int j) {
+        float u = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) u += Bv[r][i] * Xv[r][j];
+        return u;
+    };
+    auto coeffs = [&](int64_t t, float* al, float* be, float* ga, float* sn, float* cs) {
+        const float dtv = a.dt[soff(t)], lv = a.lam[soff(t)];
+        *al = __expf(dtv * Ah);
+        *be = (1.f - lv) * dtv * *al;
+        *ga = lv * dtv;
+        const float2 th = *reinterpret_cast<const float2*>(a.theta + toff(t));
+        sincos_acc(th.x, &sn[0], &cs[0]);
+        sincos_acc(th.y, &sn[1], &cs[1]);
+    };
+    // one forward step on hs: h <- M (alpha h + beta U_{t-1}) + gamma U_t
+    auto fwd_step = [&](int64_t t, float (&hs)[4][4], const float (&Bp)[R][4], const float (&Xp)[R][4],
+                        const float (&Bv)[R][4], const float (&Xv)[R][4]) {
+        float al, be, ga, sn[2], cs[2];
+        coeffs(t, &al, &be, &ga, sn, cs);
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float v0 = al * hs[2 * k][j] + be * uval(Bp, Xp, 2 * k, j);
+                const float v1 = al * hs[2 * k + 1][j] + be * uval(Bp, Xp, 2 * k + 1, j);
+                hs[2 * k][j] = cs[k] * v0 - sn[k] * v1 + ga * uval(Bv, Xv, 2 * k, j);
+                hs[2 * k + 1][j] = sn[k] * v0 + cs[k] * v1 + ga * uval(Bv, Xv, 2 * k + 1, j);
+            }
+    };
+    auto load_state = [&](float (&hs)[4][4], const float* src, int stride) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 u = *reinterpret_cast<const float4*>(src + (r0 + i) * stride + c0);
+            hs[i][0] = u.x; hs[i][1] = u.y; hs[i][2] = u.z; hs[i][3] = u.w;
+        }
+    };
+    auto store_state = [&](const float (&hs)[4][4], float* dst, int stride) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<float4*>(dst + (r0 + i) * stride + c0) = float4{hs[i][0], hs[i][1], hs[i][2], hs[i][3]};
+    };
+    auto initial_state = [&](float (&hs)[4][4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                hs[i][j] = a.h0 ? state_load(a.h0, (static_cast<size_t>(bh) * N + r0 + i) * P + c0 + j, a.state_bf16)
+                                : 0.f;
+    };
+
+    // ---- forward sweep: checkpoint after the last token of every segment
+    float hc[4][4];
+    initial_state(hc);
+    {
+        float Bp[R][4], Xp[R][4], Bv[R][4], Xv[R][4];
+        load_bx(-1, Bp, Xp);
+        for (int64_t t = 0; t < L; ++t) {
+            load_bx(t, Bv, Xv);
+            fwd_step(t, hc, Bp, Xp, Bv, Xv);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    Bp[r][i] = Bv[r][i];
+                    Xp[r][i] = Xv[r][i];
+                }
+            if ((t + 1) % KS == 0 || t == L - 1) store_state(hc, ck + (t / KS) * N * P, P);
+        }
+    }
+
+    // ---- reverse sweep.  q_{t+1}, alpha_{t+1}, beta_{t+1} belong to the token after; the
+    // final-state cotangent enters as a token after the last one with alpha = 1, beta = 0 and
+    // no rotation.
+    float qn[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            qn[i][j] = a.dh_out ? a.dh_out[(static_cast<size_t>(bh) * N + r0 + i) * P + c0 + j] : 0.f;
+    float an = 1.f, bn = 0.f;
+    float dA_acc = 0.f, dD_acc = 0.f;   // thread 0
+
+    for (int64_t s = nseg - 1; s >= 0; --s) {
+        const int64_t t0 = s * KS;
+        const int len = static_cast<int>(L - t0 < KS ? L - t0 : KS);
+        __syncthreads();   // the previous segment's readers are done with sH
+        {   // recompute h_{t0-1} .. h_{t0+len-2} into LDS
+            float hr[4][4], Bp[R][4], Xp[R][4], Bv[R][4], Xv[R][4];
+            if (s == 0) initial_state(hr); else load_state(hr, ck + (s - 1) * N * P, P);
+            store_state(hr, sH[0], PS);
+            load_bx(t0 - 1, Bp, Xp);
+            for (int j = 1; j < len; ++j) {
+                const int64_t t = t0 + j - 1;
+                load_bx(t, Bv, Xv);
+                fwd_step(t, hr, Bp, Xp, Bv, Xv);
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        Bp[r][i] = Bv[r][i];
+                        Xp[r][i] = Xv[r][i];
+                    }
+                store_state(hr, sH[j], PS);
+            }
+        }
+        __syncthreads();
+
+        for (int j = len - 1; j >= 0; --j) {
+            const int64_t t = t0 + j;
+            const int par = static_cast<int>(t & 1);
+            float al, be, ga, sn[2], cs[2];
+            coeffs(t, &al, &be, &ga, sn, cs);
+            float Bv[R][4], Xv[R][4];
+            load_bx(t, Bv, Xv);
+
+            // (1) g_t = alpha_{t+1} q_{t+1} + C_t dy_t^T; dU_t; dgamma; dC_t = h_t dy_t; dD
+            float gg[4][4], dU[4][4], dC[R][4];
+            float dga = 0.f, dDp = 0.f;
+            {
+                float Cv[R][4], dyv[R][4];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    ld<T>::v4(Cm + boff(t, r), Cv[r]);
+                    ld<T>::v4(dy + xoff(t, r), dyv[r]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        float v = an * qn[i][jj];
+#pragma unroll
+                        for (int r = 0; r < R; ++r) v += Cv[r][i] * dyv[r][jj];
+                        gg[i][jj] = v;
+                        dU[i][jj] = ga * v + bn * qn[i][jj];
+                        dga += v * uval(Bv, Xv, i, jj);
+                    }
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float c = 0.f;
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) c += hc[i][jj] * dyv[r][jj];
+                        dC[r][i] = c;
+                    }
+                if (pb == 0) {
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) dDp += dyv[r][jj] * Xv[r][jj];
+                }
+            }
+            // (2) q_t = M_t^T g_t; dalpha, dbeta, dtheta (needs h_{t-1} and U_{t-1})
+            float dal = 0.f, dbe = 0.f, dth[2] = {0.f, 0.f};
+            {
+                float Bp[R][4], Xp[R][4];
+                load_bx(t - 1, Bp, Xp);
+                load_state(hc, sH[j], PS);   // hc <- h_{t-1} (h_t is no longer needed)
+#pragma unroll
+                for (int k = 0; k < 2; ++k)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const float g0 = gg[2 * k][jj], g1 = gg[2 * k + 1][jj];
+                        const float q0 = cs[k] * g0 + sn[k] * g1, q1 = -sn[k] * g0 + cs[k] * g1;
+                        qn[2 * k][jj] = q0;
+                        qn[2 * k + 1][jj] = q1;
+                        const float h0v = hc[2 * k][jj], h1v = hc[2 * k + 1][jj];
+                        const float u0 = uval(Bp, Xp, 2 * k, jj), u1 = uval(Bp, Xp, 2 * k + 1, jj);
+                        dal += q0 * h0v + q1 * h1v;
+                        dbe += q0 * u0 + q1 * u1;
+                        const float v0 = al * h0v + be * u0, v1 = al * h1v + be * u1;
+                        dth[k] += q1 * v0 - q0 * v1;
+                    }
+            }
+            // (3) dB_t = dU_t X_t^T, dX_t = B_t^T dU_t
+            float dB[R][4], dX[R][4];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float d = 0.f;
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) d += dU[i][jj] * Xv[r][jj];
+                    dB[r][i] = d;
+                }
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    float v = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v += Bv[r][i] * dU[i][jj];
+                    dX[r][jj] = v;
+                }
+            }
+
+            // sums over columns (the 16 lanes of a row): dB, dC, dtheta
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    dC[r][i] = sum16(dC[r][i]);
+                    dB[r][i] = sum16(dB[r][i]);
+                }
+            dth[0] = sum16(dth[0]);
+            dth[1] = sum16(dth[1]);
+            {
+                const int64_t go = ((static_cast<int64_t>(b) * L + t) * GH + gh) * (R * N);
+                float* dCo = a.per_head ? a.dC_part : a.dC;
+                float* dBo = a.per_head ? a.dB_part : a.dB;
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (((r * 4 + i) & 15) == cb) {
+                            dCo[go + r * N + r0 + i] = dC[r][i];
+                            dBo[go + r * N + r0 + i] = dB[r][i];
+                        }
+                    }
+                float* dTo = a.per_head ? a.dtheta_part : a.dtheta;
+                if (cb < 2) dTo[((static_cast<int64_t>(b) * L + t) * GH + gh) * (N / 2) + 2 * pb + cb] = dth[cb];
+            }
+            // sums over rows: dX within the wave, then across waves through LDS; scalars per wave
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) dX[r][jj] = sum_rows(dX[r][jj]);
+            if (lane < 16) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    *reinterpret_cast<float4*>(&sDX[par][wv][r * P + c0]) = float4{dX[r][0], dX[r][1], dX[r][2], dX[r][3]};
+            }
+            dal = sum64(dal);
+            dbe = sum64(dbe);
+            dga = sum64(dga);
+            dDp = sum64(dDp);
+            if (lane == 63) {
+                sSc[par][wv][0] = dal;
+                sSc[par][wv][1] = dbe;
+                sSc[par][wv][2] = dga;
+                sSc[par][wv][3] = dDp;
+            }
+            __syncthreads();
+            for (int o = tid; o < R * P; o += NT) {
+                float v = 0.f;
+#pragma unroll
+                for (int k = 0; k < NT / 64; ++k) v += sDX[par][k][o];
+                const int64_t xi = ((static_cast<int64_t>(b) * L + t) * H + h) * (R * P) + o;
+                a.dx[xi] = v + Dh * io<T>::load(dy + xi);
+            }
+            if (tid == 0) {
+                float sa = 0.f, sb = 0.f, sg = 0.f, sd = 0.f;
+#pragma unroll
+                for (int k = 0; k < NT / 64; ++k) {
+                    sa += sSc[par][k][0];
+                    sb += sSc[par][k][1];
+                    sg += sSc[par][k][2];
+                    sd += sSc[par][k][3];
+                }
+                const float dtv = a.dt[soff(t)], lv = a.lam[soff(t)];
+                a.ddt[soff(t)] = sa * Ah * al + sb * (1.f - lv) * (al + dtv * Ah * al) + sg * lv;
+                a.dlam[soff(t)] = -sb * dtv * al + sg * dtv;
+                dA_acc += sa * dtv * al + sb * (1.f - lv) * dtv * dtv * al;
+                dD_acc += sd;
+            }
+            an = al;
+            bn = be;
+        }
+    }
+
+    // ---- h_0 and the carried previous input (dU_0 = beta_1 q_1)
+    if (a.dh0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a.dh0[(static_cast<size_t>(bh) * N + r0 + i) * P + c0 + j] = an * qn[i][j];
+    }
+    if (carry && (a.dbl || a.dxl)) {
+        float Bv[R][4], Xv[R][4], dB[R][4], dX[R][4];
+        load_bx(-1, Bv, Xv);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float d = 0.f;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) d += bn * qn[i][jj] * Xv[r][jj];
+                dB[r][i] = sum16(d);
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                float v = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v += Bv[r][i] * bn * qn[i][jj];
+                dX[r][jj] = sum_rows(v);
+            }
+        }
+        if (a.dbl) {
+            float* dBo = a.per_head ? a.dbl_part : a.dbl;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (((r * 4 + i) & 15) == cb) dBo[((static_cast<int64_t>(b) * GH + gh) * R + r) * N + r0 + i] = dB[r][i];
+        }
+        __syncthreads();
+        if (lane < 16) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                *reinterpret_cast<float4*>(&sDX[0][wv][r * P + c0]) = float4{dX[r][0], dX[r][1], dX[r][2], dX[r][3]};
+        }
+        __syncthreads();
+        if (a.dxl) {
+            for (int o = tid; o < R * P; o += NT) {
+                float v = 0.f;
+#pragma unroll
+                for (int k = 0; k < NT / 64; ++k) v += sDX[0][k][o];
+                a.dxl[static_cast<size_t>(bh) * R * P + o] = v;
+            }
+        }
+    } else if (a.dxl) {
+        for (int o = tid; o < R * P; o += NT) a.dxl[static_cast<size_t>(bh) * R * P + o] = 0.f;
+    }
+    if (tid == 0) {
+        a.dA_part[bh] = dA_acc;
+        a.dD_part[bh] = dD_acc;
+    }
+}
+
+// Sums of per-head gradient rows over the heads of each group, and of dA, dD over the batch.
+__global__ __launch_bounds__(256) void bwd_group_sum(const float* __restrict__ part, float* __restrict__ out,
+                                                     int64_t rows, int heads_per_group, int width) {
+    // part: (rows * heads_per_group, width) -> out: (rows, width); rows index (outer, group)
+    const int64_t n = rows * width;
+    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t row = i / width, c = i - row * width;
+        float s = 0.f;
+        for (int k = 0; k < heads_per_group; ++k) s += part[(row * heads_per_group + k) * width + c];
+        out[i] = s;
+    }
+}
+
+__global__ __launch_bounds__(256) void bwd_fill_zero(float* __restrict__ p, int64_t n) {
+    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256) p[i] = 0.f;
+}
+
+__global__ __launch_bounds__(256) void bwd_head_sum(const float* __restrict__ dA_part, const float* __restrict__ dD_part,
+                                                    float* __restrict__ dA, float* __restrict__ dD, int batch, int H) {
+    const int h = blockIdx.x * 256 + threadIdx.x;
+    if (h >= H) return;
+    float sa = 0.f, sd = 0.f;
+    for (int b = 0; b < batch; ++b) {   // fixed order
+        sa += dA_part[b * H + h];
+        sd += dD_part[b * H + h];
+    }
+    dA[h] = sa;
+    dD[h] = sd;
+}
+
+}  // namespace bw
+
+bool backward_supported(const BwdShape& s) {
+    return s.N == bw::N && s.P == bw::P && (s.R == 1 || s.R == 2 || s.R == 4);
+}
+
+// Workspace: checkpoints (batch, H, nseg, N, P) fp32; per-head partials of the
+// group-shared gradients when H > G; dA/dD per (batch, head).
+BwdLayout backward_layout(const BwdShape& s) {
+    BwdLayout l{};
+    auto al = [](size_t v) { return (v + 255) & ~static_cast<size_t>(255); };
+    const int64_t nseg = (s.L + bw::KS - 1) / bw::KS;
+    size_t off = 0;
+    l.ckpt = off;
+    off += al(static_cast<size_t>(s.batch) * s.H * nseg * s.N * s.P * 4);
+    l.per_head = s.H != s.G;
+    if (l.per_head) {
+        l.dB_part = off;
+        off += al(static_cast<size_t>(s.batch) * s.L * s.H * s.R * s.N * 4);
+        l.dC_part = off;
+        off += al(static_cast<size_t>(s.batch) * s.L * s.H * s.R * s.N * 4);
+        l.dtheta_part = off;
+        off += al(static_cast<size_t>(s.batch) * s.L * s.H * (s.N / 2) * 4);
+        l.dbl_part = off;
+        off += al(static_cast<size_t>(s.batch) * s.H * s.R * s.N * 4);
+    }
+    l.dA_part = off;
+    off += al(static_cast<size_t>(s.batch) * s.H * 4);
+    l.dD_part = off;
+    off += al(static_cast<size_t>(s.batch) * s.H * 4);
+    l.bytes = off;
+    return l;
+}
+
+hipError_t launch_backward(BwdArgs a, const BwdLayout& l, hipStream_t st) {
+    uint8_t* ws = static_cast<uint8_t*>(a.workspace);
+    a.ckpt = reinterpret_cast<float*>(ws + l.ckpt);
+    a.per_head = l.per_head;
+    if (l.per_head) {
+        a.dB_part = reinterpret_cast<float*>(ws + l.dB_part);
+        a.dC_part = reinterpret_cast<float*>(ws + l.dC_part);
+        a.dtheta_part = reinterpret_cast<float*>(ws + l.dtheta_part);
+        a.dbl_part = reinterpret_cast<float*>(ws + l.dbl_part);
+    }
+    a.dA_part = reinterpret_cast<float*>(ws + l.dA_part);
+    a.dD_part = reinterpret_cast<float*>(ws + l.dD_part);
+    const dim3 grid(static_cast<unsigned>(a.batch * a.H));
+    if (a.bf16) {
+        if (a.R == 1) bw::bwd_scan<bf16_t, 1><<<grid, bw::NT, 0, st>>>(a);
+        if (a.R == 2) bw::bwd_scan<bf16_t, 2><<<grid, bw::NT, 0, st>>>(a);
+        if (a.R == 4) bw::bwd_scan<bf16_t, 4><<<grid, bw::NT, 0, st>>>(a);
+    } else {
+        if (a.R == 1) bw::bwd_scan<float, 1><<<grid, bw::NT, 0, st>>>(a);
+        if (a.R == 2) bw::bwd_scan<float, 2><<<grid, bw::NT, 0, st>>>(a);
+        if (a.R == 4) bw::bwd_scan<float, 4><<<grid, bw::NT, 0, st>>>(a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (l.per_head) {
+        const int hpg = a.H / a.G;
+        auto sum = [&](const float* part, float* out, int64_t rows, int width) {
+            const int64_t n = rows * width;
+            const unsigned blocks = static_cast<unsigned>(n / 256 + 1 < 65536 ? n / 256 + 1 : 65536);
+            bw::bwd_group_sum<<<blocks, 256, 0, st>>>(part, out, rows, hpg, width);
+        };
+        if (a.L > 0) {
+            sum(a.dB_part, a.dB, a.batch * a.L * a.G, a.R * a.N);
+            sum(a.dC_part, a.dC, a.batch * a.L * a.G, a.R * a.N);
+            sum(a.dtheta_part, a.dtheta, a.batch * a.L * a.G, a.N / 2);
+        }
+        if (a.dbl && a.bl && a.xl) sum(a.dbl_part, a.dbl, a.batch * a.G, a.R * a.N);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (a.dbl && !(a.bl && a.xl)) {   // no carried input: its gradient is zero
+        const int64_t n = a.batch * a.G * a.R * a.N;
+        bw::bwd_fill_zero<<<static_cast<unsigned>(n / 256 + 1 < 4096 ? n / 256 + 1 : 4096), 256, 0, st>>>(a.dbl, n);
+    }
+    bw::bwd_head_sum<<<(a.H + 255) / 256, 256, 0, st>>>(a.dA_part, a.dD_part, a.dA, a.dD, static_cast<int>(a.batch), a.H);
+    return hipGetLastError();
+}
+
+}  // namespace m3

@@ -81,4 +81,57 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, const PrefillPlan& plan, hi
 // Carry-out copy (B and X of the last token), in m3_prefill_generic.hip.
 hipError_t launch_carry_out(const PrefillArgs& a, hipStream_t st);
 
+// Backward pass (m3_backward.hip): N = 128, P = 64, R in {1, 2, 4}, fp32 or bf16 io.
+struct BwdShape {
+    int64_t batch, L;
+    int H, G, N, P, R;
+};
+struct BwdLayout {            // byte offsets into the workspace
+    size_t ckpt, dB_part, dC_part, dtheta_part, dbl_part, dA_part, dD_part, bytes;
+    bool per_head;            // H > G: group-shared gradients are written per head, then summed
+};
+struct BwdArgs {
+    const void* x;
+    const float* dt;
+    const float* A;
+    const float* lam;
+    const float* theta;
+    const void* B;
+    const void* C;
+    const float* D;
+    const void* h0;           // may be null; fp32 or bf16 (state_bf16)
+    const void* bl;           // carried previous input, may be null (with xl)
+    const void* xl;
+    const void* dy;           // io dtype
+    const float* dh_out;      // may be null
+    float* dx;
+    float* ddt;
+    float* dA;
+    float* dlam;
+    float* dtheta;
+    float* dB;
+    float* dC;
+    float* dD;
+    float* dh0;               // may be null
+    float* dbl;               // may be null
+    float* dxl;               // may be null
+    void* workspace;
+    // filled by launch_backward from the layout
+    float* ckpt;
+    float* dB_part;
+    float* dC_part;
+    float* dtheta_part;
+    float* dbl_part;
+    float* dA_part;
+    float* dD_part;
+    int64_t batch, L;
+    int H, G, N, P, R;
+    bool per_head;
+    bool bf16;
+    bool state_bf16;
+};
+bool backward_supported(const BwdShape& s);
+BwdLayout backward_layout(const BwdShape& s);
+hipError_t launch_backward(BwdArgs a, const BwdLayout& l, hipStream_t st);
+
 }  // namespace m3

@@ -37,6 +37,11 @@ class State(ctypes.Structure):
     _fields_ = [("h", ctypes.c_void_p), ("b_last", ctypes.c_void_p), ("x_last", ctypes.c_void_p)]
 
 
+class Grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("dx", "ddt", "dA", "dlambda", "dtheta", "dB", "dC", "dD", "dh0", "db_last", "dx_last")]
+
+
 class M3Error(RuntimeError):
     def __init__(self, where: str, code: int):
         super().__init__(f"{where}: {STATUS.get(code, code)} ({code})")
@@ -69,6 +74,11 @@ def lib(path: str = LIB_PATH):
                                     [ctypes.POINTER(State), ctypes.POINTER(State), vp, vp, sz, vp])
     L.m3_decode_step.restype = ctypes.c_int
     L.m3_decode_step.argtypes = [ctypes.POINTER(Dims)] + [vp] * 13
+    L.m3_backward_workspace_size.restype = ctypes.c_int
+    L.m3_backward_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(sz)]
+    L.m3_backward.restype = ctypes.c_int
+    L.m3_backward.argtypes = ([ctypes.POINTER(Dims)] + [vp] * 8 + [ctypes.POINTER(State), vp, vp,
+                              ctypes.POINTER(Grads), vp, sz, vp])
     _lib = L
     return L
 
@@ -275,3 +285,70 @@ def prefill_varlen(x, dt, A, lam, theta, B, C, D, cu_seqlens, max_seqlen: int, c
     if rc != 0:
         raise M3Error("m3_prefill_varlen", rc)
     return y, st
+
+
+def backward_workspace_size(dims: Dims) -> int:
+    n = ctypes.c_size_t(0)
+    rc = lib().m3_backward_workspace_size(ctypes.byref(dims), ctypes.byref(n))
+    if rc != 0:
+        raise M3Error("m3_backward_workspace_size", rc)
+    return int(n.value)
+
+
+def backward(x, dt, A, lam, theta, B, C, D, dy, dh_out=None, state_in: Optional[DecodeState] = None,
+             want_state_grads: bool = True, workspace: Optional[torch.Tensor] = None,
+             grads: Optional[dict] = None):
+    """Backward pass of the scan: gradients of sum <dy, y> + <dh_out, h_L>.
+
+    Returns a dict of fp32 tensors dx, ddt, dA, dlam, dtheta, dB, dC, dD and, with
+    want_state_grads, dh0 (b,H,N,P), db_last (b,G,R,N), dx_last (b,H,R,P).
+    ``grads`` may hold preallocated output tensors of those names."""
+    b, L, H, R, P = x.shape
+    G, N = B.shape[2], B.shape[4]
+    dev = x.device
+    io = x.dtype
+    if io not in _IO:
+        raise ValueError(f"x dtype {io} not supported (fp32 or bf16)")
+    _check(x, "x", (b, L, H, R, P), io, dev)
+    _check(dy, "dy", (b, L, H, R, P), io, dev)
+    _check(dt, "dt", (b, L, H), torch.float32, dev)
+    _check(lam, "lam", (b, L, H), torch.float32, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(theta, "theta", (b, L, G, N // 2), torch.float32, dev)
+    _check(B, "B", (b, L, G, R, N), io, dev)
+    _check(C, "C", (b, L, G, R, N), io, dev)
+    if dh_out is not None:
+        _check(dh_out, "dh_out", (b, H, N, P), torch.float32, dev)
+    state_dtype = state_in.h.dtype if state_in is not None else torch.float32
+    dims = make_dims(b, L, H, G, P, N, R, 1, _IO[io], _IO[state_dtype])
+    sin = None
+    if state_in is not None:
+        _check(state_in.h, "state_in.h", (b, H, N, P), state_dtype, dev)
+        if state_in.b_last is not None:
+            _check(state_in.b_last, "state_in.b_last", (b, G, R, N), io, dev)
+            _check(state_in.x_last, "state_in.x_last", (b, H, R, P), io, dev)
+        sin = State(state_in.h.data_ptr(),
+                    None if state_in.b_last is None else state_in.b_last.data_ptr(),
+                    None if state_in.x_last is None else state_in.x_last.data_ptr())
+    f32 = dict(dtype=torch.float32, device=dev)
+    shapes = {"dx": (b, L, H, R, P), "ddt": (b, L, H), "dA": (H,), "dlam": (b, L, H),
+              "dtheta": (b, L, G, N // 2), "dB": (b, L, G, R, N), "dC": (b, L, G, R, N), "dD": (H,)}
+    if want_state_grads:
+        shapes.update({"dh0": (b, H, N, P), "db_last": (b, G, R, N), "dx_last": (b, H, R, P)})
+    out = {} if grads is None else dict(grads)
+    for k, shp in shapes.items():
+        if k not in out:
+            out[k] = torch.empty(shp, **f32)
+        _check(out[k], k, shp, torch.float32, dev)
+    gs = Grads(*[out[k].data_ptr() if k in out else None for k in
+                 ("dx", "ddt", "dA", "dlam", "dtheta", "dB", "dC", "dD", "dh0", "db_last", "dx_last")])
+    ws = backward_workspace_size(dims)
+    if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
+        workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+    rc = lib().m3_backward(ctypes.byref(dims), _p(x), _p(dt), _p(A), _p(lam), _p(theta), _p(B), _p(C),
+                           _p(D), None if sin is None else ctypes.byref(sin), _p(dy), _p(dh_out),
+                           ctypes.byref(gs), _p(workspace) if ws > 0 else None, ws, _stream(dev))
+    if rc != 0:
+        raise M3Error("m3_backward", rc)
+    return out

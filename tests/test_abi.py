@@ -28,8 +28,9 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_symbols() == ["m3_decode_step", "m3_prefill_chunked", "m3_prefill_varlen",
-                                  "m3_prefill_workspace_size", "m3_status_string", "m3_version"]
+    assert declared_symbols() == ["m3_backward", "m3_backward_workspace_size", "m3_decode_step",
+                                  "m3_prefill_chunked", "m3_prefill_varlen", "m3_prefill_workspace_size",
+                                  "m3_status_string", "m3_version"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -159,3 +160,45 @@ def test_varlen_rejects_bad_arguments(lib):
     assert lib.m3_prefill_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0 and n.value > 0
     assert lib.m3_prefill_varlen(ctypes.byref(big), FAKE, T, *[FAKE] * 8, None, None, FAKE, FAKE, 16,
                                  None) == -3
+
+
+def _bwd(lib, d, grads, ws=None, nbytes=0, args=None, dy=FAKE, state=None):
+    args = [FAKE] * 8 if args is None else args
+    return lib.m3_backward(ctypes.byref(d), *args, state, dy, None,
+                           None if grads is None else ctypes.byref(grads), ws, nbytes, None)
+
+
+def _grads(**none):
+    names = ("dx", "ddt", "dA", "dlambda", "dtheta", "dB", "dC", "dD", "dh0", "db_last", "dx_last")
+    return m3scan.Grads(*[None if n in none else 0x1000 for n in names])
+
+
+def test_backward_rejects_bad_arguments(lib):
+    big = _dims(headdim=64, dstate=128, rank=4, io_dtype=m3scan.M3_BF16)
+    n = ctypes.c_size_t(0)
+    assert lib.m3_backward_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0 and n.value > 0
+    # unsupported shape (N = 16, P = 16) and rank 3
+    small = _dims()
+    assert lib.m3_backward_workspace_size(ctypes.byref(small), ctypes.byref(n)) == -2
+    assert _bwd(lib, small, _grads()) == -2
+    r3 = _dims(headdim=64, dstate=128, rank=3)
+    assert _bwd(lib, r3, _grads()) == -2
+    # bad dims
+    for kw in BAD_DIMS:
+        bd = _dims(**{"headdim": 64, "dstate": 128, **kw})
+        assert _bwd(lib, bd, _grads()) == -1, kw
+    # missing grads struct, inputs, dy, or a required gradient
+    assert _bwd(lib, big, None) == -1
+    for i in range(8):
+        args = [FAKE] * 8
+        args[i] = None
+        assert _bwd(lib, big, _grads(), args=args) == -1, i
+    assert _bwd(lib, big, _grads(), dy=None) == -1
+    for k in ("dx", "ddt", "dA", "dlambda", "dtheta", "dB", "dC", "dD"):
+        assert _bwd(lib, big, _grads(**{k: 1})) == -1, k
+    # a state without h
+    st = m3scan.State(None, None, None)
+    assert _bwd(lib, big, _grads(), state=ctypes.byref(st)) == -1
+    # workspace too small
+    assert _bwd(lib, big, _grads(), ws=FAKE, nbytes=n.value - 1) == -3
+    assert _bwd(lib, big, _grads(), ws=None, nbytes=0) == -3
