@@ -27,6 +27,8 @@ sys.path.insert(0, ROOT)
 METRIC = "prefill scan tokens/s + decode state GB/s (% roofline), 1.5B-shape layer, 1 GPU"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2516.6        # dense bf16 MFMA: 4096 flop/clk/CU x 256 CU x 2.4 GHz
+FP32_VALU_PEAK_TFLOPS = 157.3    # fp32 vector: 256 CU x 4 SIMD x 16 lanes x 2 (FMA) x 2 (packed) x 2.4 GHz
+BWD_METRIC = "backward scan tokens/s (training step of the scan), 1 GPU"
 
 
 def parse():
@@ -34,8 +36,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="c4", help="c1, c2, c3 (prefill only) or c4 (prefill + decode)")
+    ap.add_argument("--workload", default=None, help="c1, c2, c3 (prefill only) or c4 (prefill + decode); "
+                                                      "default c4, or c1 with --backward")
     ap.add_argument("--decode-steps", type=int, default=None, help="override the decode steps per step")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (m3_backward) of the workload's prefill instead "
+                         "(default workload for it: c1, the nanomamba3 training shape)")
     ap.add_argument("--varlen", action="store_true",
                     help="pack the batch's sequences with seeded lengths uniform in [L/4, L] "
                          "(m3_prefill_varlen) instead of equal lengths L")
@@ -105,6 +111,8 @@ def pmc_traffic(kernel_file, src_names, per_launch_alg):
 
 def main():
     args = parse()
+    if args.workload is None:
+        args.workload = "c1" if args.backward else "c4"
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the scan on a single MI355X "
               "(multi-GPU sharding is a design note, not implemented); use --gpus 1", file=sys.stderr)
@@ -116,6 +124,8 @@ def main():
     from state_space_sequence_scan_amd import CONFIGS, inputs, m3scan
 
     cfg = CONFIGS[args.workload]
+    if args.backward:
+        return run_backward(args, cfg)
     state_dtype = torch.bfloat16 if args.state_dtype == "bf16" else torch.float32
     state_bytes = 2 if args.state_dtype == "bf16" else 4
     steps_dec = cfg.decode_steps if args.decode_steps is None else args.decode_steps
@@ -315,6 +325,145 @@ def main():
         "cpu_baseline": cpu,
         "parity_check": check,
         "input_gen_s": round(t_gen, 2),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def backward_flops(cfg, L):
+    """fp32 arithmetic of the adjoint method per workload: one forward step and one
+    reverse step of the recurrence per (token, head) over the N x P state, counted as
+    14 R + 33 flops per state element (see the backward's section of the design notes)."""
+    return cfg.batch * L * cfg.nheads * cfg.dstate * cfg.headdim * (14 * cfg.rank + 33)
+
+
+def backward_bytes(cfg, L):
+    """Bytes the backward must move: its inputs once (x, dy, dt, lambda per head; B, C,
+    theta per group) and its gradients once (fp32)."""
+    s = 2 if cfg.io_dtype == "bf16" else 4
+    b, H, G, P, N, R = cfg.batch, cfg.nheads, cfg.ngroups, cfg.headdim, cfg.dstate, cfg.rank
+    tok = b * L
+    rd = tok * H * (2 * R * P * s + 8) + tok * G * (2 * N * R * s + 4 * (N // 2))
+    wr = tok * H * (R * P * 4 + 8) + tok * G * (2 * N * R * 4 + 4 * (N // 2))
+    return rd + wr
+
+
+def run_backward(args, cfg):
+    import numpy as np
+    import torch
+
+    from state_space_sequence_scan_amd import inputs, m3scan
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    m3scan.lib()
+    stream = torch.cuda.current_stream(dev)
+    if args.probe_copy:
+        src = torch.empty(2**28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    L = cfg.seqlen
+    names = ("x", "dt", "A", "lam", "theta", "B", "C", "D")
+    d = inputs.draw_config(cfg, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(cfg.seed + 11)
+    dy = torch.randn(d["x"].shape, generator=gen, device=dev).to(d["x"].dtype)
+    dims = m3scan.make_dims(cfg.batch, L, cfg.nheads, cfg.ngroups, cfg.headdim, cfg.dstate, cfg.rank,
+                            1, m3scan.M3_BF16 if cfg.io_dtype == "bf16" else m3scan.M3_F32)
+    ws = torch.empty(m3scan.backward_workspace_size(dims), dtype=torch.uint8, device=dev)
+    grads = m3scan.backward(*[d[k] for k in names], dy, workspace=ws, want_state_grads=False)
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        m3scan.backward(*[d[k] for k in names], dy, workspace=ws, grads=grads, want_state_grads=False)
+    torch.cuda.synchronize()
+    times = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        m3scan.backward(*[d[k] for k in names], dy, workspace=ws, grads=grads, want_state_grads=False)
+        e1.record(stream)
+        times.append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.mean([a.elapsed_time(b) for a, b in times]))
+    step_ms = wall * 1e3 / args.steps
+    tokens = cfg.batch * L
+    flops = backward_flops(cfg, L)
+    nbytes = backward_bytes(cfg, L)
+    tflops = flops / (ms / 1e3) / 1e12
+    traffic = pmc_traffic(f"backward_{args.workload}_hbm_counters.json", ["m3_backward.hip", "m3_common.h"], nbytes)
+    roof = {"kernel": f"bwd_scan<io {cfg.io_dtype}, R{cfg.rank}> + group sums", "bound": "alu",
+            "achieved": round(tflops, 3), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / FP32_VALU_PEAK_TFLOPS, 4), "traffic": traffic,
+            "alg_flops_per_launch": flops, "alg_bytes_per_launch": nbytes,
+            "alg_GB_per_s": round(nbytes / (ms / 1e3) / 1e9, 1), "avg_launch_us": round(ms * 1e3, 1)}
+
+    check = cpu = None
+    if args.check_slices > 0 or not args.no_cpu_baseline:
+        import oracle
+        f = lambda t: t.detach().double().cpu().numpy()
+
+        def slice_inputs(bi, h):
+            g = h // (cfg.nheads // cfg.ngroups)
+            return {"x": f(d["x"][bi:bi + 1, :, h:h + 1]), "dt": f(d["dt"][bi:bi + 1, :, h:h + 1]),
+                    "lam": f(d["lam"][bi:bi + 1, :, h:h + 1]), "theta": f(d["theta"][bi:bi + 1, :, g:g + 1]),
+                    "B": f(d["B"][bi:bi + 1, :, g:g + 1]), "C": f(d["C"][bi:bi + 1, :, g:g + 1]),
+                    "A": f(d["A"][h:h + 1]), "D": f(d["D"][h:h + 1]), "dy": f(dy[bi:bi + 1, :, h:h + 1])}
+
+        if args.check_slices > 0:
+            rng = np.random.default_rng(cfg.seed)
+            errs = []
+            for _ in range(args.check_slices):
+                bi, h = int(rng.integers(cfg.batch)), int(rng.integers(cfg.nheads))
+                si = slice_inputs(bi, h)
+                ref = oracle.scan_backward(*[si[k] for k in names], si["dy"])
+                # per-head gradients (group-shared and batch-summed ones mix other slices)
+                for k, sl in (("dx", (slice(bi, bi + 1), slice(None), slice(h, h + 1))),
+                              ("ddt", (slice(bi, bi + 1), slice(None), slice(h, h + 1))),
+                              ("dlam", (slice(bi, bi + 1), slice(None), slice(h, h + 1)))):
+                    gv = grads[k][sl].double().cpu().numpy()
+                    errs.append(float(np.max(np.abs(gv - ref[k])) / max(np.max(np.abs(ref[k])), 1e-30)))
+            check = {"slices": args.check_slices, "max_rel_err": max(errs), "tolerance": 1e-3,
+                     "compared": "dx, ddt, dlambda of sampled (b, h) slices"}
+        if not args.no_cpu_baseline:
+            threads = oracle.max_threads()
+            si = slice_inputs(0, 0)
+            t1 = time.perf_counter()
+            oracle.scan_backward(*[si[k] for k in names], si["dy"], nthreads=1)
+            one = time.perf_counter() - t1
+            # the oracle parallelises over batch elements: each sampled slice is its own batch element
+            n = int(max(threads, min(cfg.batch * cfg.nheads, args.cpu_seconds * threads / max(one, 1e-6))))
+            n = max(threads, (n // threads) * threads)
+            sl = [slice_inputs(i // cfg.nheads % cfg.batch, i % cfg.nheads) for i in range(n)]
+            st = {k: np.concatenate([s[k] for s in sl], axis=0) for k in ("x", "dt", "lam", "theta", "B", "C", "dy")}
+            t1 = time.perf_counter()
+            # A, D differ per slice's head; the sample uses head 0's values for all (same cost)
+            oracle.scan_backward(st["x"], st["dt"], sl[0]["A"], st["lam"], st["theta"], st["B"], st["C"],
+                                 sl[0]["D"], st["dy"], nthreads=threads)
+            sec = time.perf_counter() - t1
+            cpu = {"value": round(n * L / cfg.nheads / sec, 2), "unit": "tokens/s", "cores": threads,
+                   "kind": "oracle",
+                   "sample": f"{n} (batch, head) slices of the workload, {L} tokens each, backward "
+                             f"(fp64 adjoint loop), {sec:.1f} s; scaled to whole-workload tokens "
+                             f"(1/{cfg.nheads} per slice-token)"}
+
+    out = {
+        "metric": BWD_METRIC, "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic (seeded torch generators on the GPU; distributions of the workload; "
+                "dy ~ N(0,1))",
+        "config": {"workload": cfg.label + "; backward pass (gradients of every input)", "name": cfg.name,
+                   "batch": cfg.batch, "seqlen": L, "heads": cfg.nheads, "groups": cfg.ngroups,
+                   "headdim": cfg.headdim, "dstate": cfg.dstate, "rank": cfg.rank, "io_dtype": cfg.io_dtype},
+        "backward": {"ms": round(ms, 4), "tokens_per_s": round(tokens / (ms / 1e3), 1),
+                     "tflops": round(tflops, 3), "alg_GB_per_s": round(nbytes / (ms / 1e3) / 1e9, 1),
+                     "workspace_GB": round(ws.numel() / 1e9, 3)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity_check": check,
     }
     print(json.dumps(out), flush=True)
 
