@@ -12,7 +12,10 @@
 // every step; they are not stored per token.  A forward sweep keeps h after
 // every KS-th token in a workspace (checkpoints); the reverse sweep takes the
 // segments of KS tokens last to first, recomputes the segment's states into LDS
-// from the previous checkpoint, and walks them backwards.
+// from the previous checkpoint, and walks them backwards.  The inputs of a
+// segment's tokens (and of the token before it) are staged into LDS once per
+// segment by the whole workgroup in 16-byte units, so the per-token steps read
+// their operands from LDS, not from global memory.
 //
 // One workgroup per (batch, head), 512 threads; thread t owns state rows
 // 4 (t >> 4) .. +3 (two rotation pairs) and columns 4 (t & 15) .. +3, of h and of
@@ -71,6 +74,21 @@ __device__ __forceinline__ float sum_rows(float v) {
     return v;
 }
 
+template <typename T> struct lds4;
+template <> struct lds4<float> {
+    __device__ __forceinline__ static void get(const float* p, float* o) {
+        const float4 v = *reinterpret_cast<const float4*>(p);
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    }
+};
+template <> struct lds4<bf16_t> {
+    __device__ __forceinline__ static void get(const bf16_t* p, float* o) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+        o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+    }
+};
+
 template <typename T, int R>
 __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
     const int bh = blockIdx.x;
@@ -87,39 +105,74 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
     const T* dy = static_cast<const T*>(a.dy);
     const T* Bm = static_cast<const T*>(a.B);
     const T* Cm = static_cast<const T*>(a.C);
+    const T* blp = static_cast<const T*>(a.bl);
+    const T* xlp = static_cast<const T*>(a.xl);
     // group-shared gradients go to per-head rows when heads share a group
     const int gh = a.per_head ? h : g, GH = a.per_head ? H : G;
 
     __shared__ __align__(16) float sH[KS][N * PS];              // states h_{t0-1} .. h_{t0+len-2}
     __shared__ __align__(16) float sDX[2][NT / 64][R * P];       // per-wave dX sums, by token parity
     __shared__ float sSc[2][NT / 64][4];                         // per-wave dalpha, dbeta, dgamma, dD
+    // inputs of tokens t0-1 .. t0+KS-1 (slot k holds token t0 - 1 + k)
+    __shared__ __align__(16) T sB[KS + 1][R * N];
+    __shared__ __align__(16) T sC[KS + 1][R * N];
+    __shared__ __align__(16) T sX[KS + 1][R * P];
+    __shared__ __align__(16) T sDY[KS + 1][R * P];
+    __shared__ __align__(16) float sTh[KS + 1][N / 2];
+    __shared__ float sDt[KS + 1], sLam[KS + 1];
 
-    auto xoff = [&](int64_t t, int r) { return ((static_cast<int64_t>(b) * L + t) * H + h) * (R * P) + r * P + c0; };
-    auto boff = [&](int64_t t, int r) { return ((static_cast<int64_t>(b) * L + t) * G + g) * (R * N) + r * N + r0; };
-    auto toff = [&](int64_t t) { return ((static_cast<int64_t>(b) * L + t) * G + g) * (N / 2) + 2 * pb; };
     auto soff = [&](int64_t t) { return (static_cast<int64_t>(b) * L + t) * H + h; };
 
-    // B rows and X columns of token t (t = -1: the carried previous input, or zero)
-    auto load_bx = [&](int64_t t, float (&Bv)[R][4], float (&Xv)[R][4]) {
-        if (t >= 0) {
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                ld<T>::v4(Bm + boff(t, r), Bv[r]);
-                ld<T>::v4(x + xoff(t, r), Xv[r]);
+    // Tokens t0-1 .. t0+len-1 into slots 0 .. len, in 16-byte units spread over the
+    // workgroup; token -1 is the carried previous input (B and X only), or zeros.
+    auto stage = [&](int64_t t0, int len, bool with_cdy) {
+        constexpr int E = 16 / static_cast<int>(sizeof(T));
+        constexpr int uB = R * N / E, uX = R * P / E, uT = (N / 2) / 4;
+        constexpr int upt = 2 * uB + 2 * uX + uT;
+        const int total = upt * (len + 1);
+        for (int u = tid; u < total; u += NT) {
+            const int k = u / upt, w = u - k * upt;
+            const int64_t t = t0 - 1 + k;
+            uint4 v = {0u, 0u, 0u, 0u};
+            void* dst;
+            if (w < uB) {
+                const int o = w * E;
+                dst = &sB[k][o];
+                if (t >= 0) v = *reinterpret_cast<const uint4*>(Bm + ((static_cast<int64_t>(b) * L + t) * G + g) * (R * N) + o);
+                else if (carry) v = *reinterpret_cast<const uint4*>(blp + (static_cast<int64_t>(b) * G + g) * (R * N) + o);
+            } else if (w < 2 * uB) {
+                const int o = (w - uB) * E;
+                dst = &sC[k][o];
+                if (t >= 0 && with_cdy)
+                    v = *reinterpret_cast<const uint4*>(Cm + ((static_cast<int64_t>(b) * L + t) * G + g) * (R * N) + o);
+            } else if (w < 2 * uB + uX) {
+                const int o = (w - 2 * uB) * E;
+                dst = &sX[k][o];
+                if (t >= 0) v = *reinterpret_cast<const uint4*>(x + ((static_cast<int64_t>(b) * L + t) * H + h) * (R * P) + o);
+                else if (carry) v = *reinterpret_cast<const uint4*>(xlp + (static_cast<int64_t>(b) * H + h) * (R * P) + o);
+            } else if (w < 2 * uB + 2 * uX) {
+                const int o = (w - 2 * uB - uX) * E;
+                dst = &sDY[k][o];
+                if (t >= 0 && with_cdy)
+                    v = *reinterpret_cast<const uint4*>(dy + ((static_cast<int64_t>(b) * L + t) * H + h) * (R * P) + o);
+            } else {
+                const int o = (w - 2 * uB - 2 * uX) * 4;
+                dst = &sTh[k][o];
+                if (t >= 0) v = *reinterpret_cast<const uint4*>(a.theta + ((static_cast<int64_t>(b) * L + t) * G + g) * (N / 2) + o);
             }
-        } else if (carry) {
-            const T* bl = static_cast<const T*>(a.bl);
-            const T* xl = static_cast<const T*>(a.xl);
+            *reinterpret_cast<uint4*>(dst) = v;
+        }
+        if (tid <= len) {
+            const int64_t t = t0 - 1 + tid;
+            sDt[tid] = t >= 0 ? a.dt[soff(t)] : 0.f;
+            sLam[tid] = t >= 0 ? a.lam[soff(t)] : 0.f;
+        }
+    };
+    auto slot_bx = [&](int k, float (&Bv)[R][4], float (&Xv)[R][4]) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                ld<T>::v4(bl + ((static_cast<int64_t>(b) * G + g) * R + r) * N + r0, Bv[r]);
-                ld<T>::v4(xl + ((static_cast<int64_t>(b) * H + h) * R + r) * P + c0, Xv[r]);
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Bv[r][i] = Xv[r][i] = 0.f;
+        for (int r = 0; r < R; ++r) {
+            lds4<T>::get(&sB[k][r * N + r0], Bv[r]);
+            lds4<T>::get(&sX[k][r * P + c0], Xv[r]);
         }
     };
     auto uval = [&](const float (&Bv)[R][4], const float (&Xv)[R][4], int i, int j) {
@@ -128,28 +181,29 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
         for (int r = 0; r < R; ++r) u += Bv[r][i] * Xv[r][j];
         return u;
     };
-    auto coeffs = [&](int64_t t, float* al, float* be, float* ga, float* sn, float* cs) {
-        const float dtv = a.dt[soff(t)], lv = a.lam[soff(t)];
+    auto coeffs = [&](int k, float* al, float* be, float* ga, float* sn, float* cs) {
+        const float dtv = sDt[k], lv = sLam[k];
         *al = __expf(dtv * Ah);
         *be = (1.f - lv) * dtv * *al;
         *ga = lv * dtv;
-        const float2 th = *reinterpret_cast<const float2*>(a.theta + toff(t));
-        sincos_acc(th.x, &sn[0], &cs[0]);
-        sincos_acc(th.y, &sn[1], &cs[1]);
+        sincos_acc(sTh[k][2 * pb], &sn[0], &cs[0]);
+        sincos_acc(sTh[k][2 * pb + 1], &sn[1], &cs[1]);
     };
-    // one forward step on hs: h <- M (alpha h + beta U_{t-1}) + gamma U_t
-    auto fwd_step = [&](int64_t t, float (&hs)[4][4], const float (&Bp)[R][4], const float (&Xp)[R][4],
-                        const float (&Bv)[R][4], const float (&Xv)[R][4]) {
+    // one forward step on hs for the token in slot k: h <- M (alpha h + beta U_{t-1}) + gamma U_t
+    auto fwd_step = [&](int k, float (&hs)[4][4]) {
+        float Bp[R][4], Xp[R][4], Bv[R][4], Xv[R][4];
+        slot_bx(k - 1, Bp, Xp);
+        slot_bx(k, Bv, Xv);
         float al, be, ga, sn[2], cs[2];
-        coeffs(t, &al, &be, &ga, sn, cs);
+        coeffs(k, &al, &be, &ga, sn, cs);
 #pragma unroll
-        for (int k = 0; k < 2; ++k)
+        for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float v0 = al * hs[2 * k][j] + be * uval(Bp, Xp, 2 * k, j);
-                const float v1 = al * hs[2 * k + 1][j] + be * uval(Bp, Xp, 2 * k + 1, j);
-                hs[2 * k][j] = cs[k] * v0 - sn[k] * v1 + ga * uval(Bv, Xv, 2 * k, j);
-                hs[2 * k + 1][j] = sn[k] * v0 + cs[k] * v1 + ga * uval(Bv, Xv, 2 * k + 1, j);
+                const float v0 = al * hs[2 * q][j] + be * uval(Bp, Xp, 2 * q, j);
+                const float v1 = al * hs[2 * q + 1][j] + be * uval(Bp, Xp, 2 * q + 1, j);
+                hs[2 * q][j] = cs[q] * v0 - sn[q] * v1 + ga * uval(Bv, Xv, 2 * q, j);
+                hs[2 * q + 1][j] = sn[q] * v0 + cs[q] * v1 + ga * uval(Bv, Xv, 2 * q + 1, j);
             }
     };
     auto load_state = [&](float (&hs)[4][4], const float* src, int stride) {
@@ -176,21 +230,14 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
     // ---- forward sweep: checkpoint after the last token of every segment
     float hc[4][4];
     initial_state(hc);
-    {
-        float Bp[R][4], Xp[R][4], Bv[R][4], Xv[R][4];
-        load_bx(-1, Bp, Xp);
-        for (int64_t t = 0; t < L; ++t) {
-            load_bx(t, Bv, Xv);
-            fwd_step(t, hc, Bp, Xp, Bv, Xv);
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    Bp[r][i] = Bv[r][i];
-                    Xp[r][i] = Xv[r][i];
-                }
-            if ((t + 1) % KS == 0 || t == L - 1) store_state(hc, ck + (t / KS) * N * P, P);
-        }
+    for (int64_t s = 0; s < nseg; ++s) {
+        const int64_t t0 = s * KS;
+        const int len = static_cast<int>(L - t0 < KS ? L - t0 : KS);
+        __syncthreads();   // the previous segment's slots are read
+        stage(t0, len, false);
+        __syncthreads();
+        for (int j = 1; j <= len; ++j) fwd_step(j, hc);
+        store_state(hc, ck + s * N * P, P);
     }
 
     // ---- reverse sweep.  q_{t+1}, alpha_{t+1}, beta_{t+1} belong to the token after; the
@@ -208,23 +255,15 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
     for (int64_t s = nseg - 1; s >= 0; --s) {
         const int64_t t0 = s * KS;
         const int len = static_cast<int>(L - t0 < KS ? L - t0 : KS);
-        __syncthreads();   // the previous segment's readers are done with sH
+        __syncthreads();   // the previous segment's readers are done with sH and the slots
+        stage(t0, len, true);
+        __syncthreads();
         {   // recompute h_{t0-1} .. h_{t0+len-2} into LDS
-            float hr[4][4], Bp[R][4], Xp[R][4], Bv[R][4], Xv[R][4];
+            float hr[4][4];
             if (s == 0) initial_state(hr); else load_state(hr, ck + (s - 1) * N * P, P);
             store_state(hr, sH[0], PS);
-            load_bx(t0 - 1, Bp, Xp);
             for (int j = 1; j < len; ++j) {
-                const int64_t t = t0 + j - 1;
-                load_bx(t, Bv, Xv);
-                fwd_step(t, hr, Bp, Xp, Bv, Xv);
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        Bp[r][i] = Bv[r][i];
-                        Xp[r][i] = Xv[r][i];
-                    }
+                fwd_step(j, hr);
                 store_state(hr, sH[j], PS);
             }
         }
@@ -233,10 +272,11 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
         for (int j = len - 1; j >= 0; --j) {
             const int64_t t = t0 + j;
             const int par = static_cast<int>(t & 1);
+            const int k = j + 1;   // slot of token t (slot j holds token t - 1)
             float al, be, ga, sn[2], cs[2];
-            coeffs(t, &al, &be, &ga, sn, cs);
+            coeffs(k, &al, &be, &ga, sn, cs);
             float Bv[R][4], Xv[R][4];
-            load_bx(t, Bv, Xv);
+            slot_bx(k, Bv, Xv);
 
             // (1) g_t = alpha_{t+1} q_{t+1} + C_t dy_t^T; dU_t; dgamma; dC_t = h_t dy_t; dD
             float gg[4][4], dU[4][4], dC[R][4];
@@ -245,8 +285,8 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
                 float Cv[R][4], dyv[R][4];
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    ld<T>::v4(Cm + boff(t, r), Cv[r]);
-                    ld<T>::v4(dy + xoff(t, r), dyv[r]);
+                    lds4<T>::get(&sC[k][r * N + r0], Cv[r]);
+                    lds4<T>::get(&sDY[k][r * P + c0], dyv[r]);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -279,22 +319,22 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
             float dal = 0.f, dbe = 0.f, dth[2] = {0.f, 0.f};
             {
                 float Bp[R][4], Xp[R][4];
-                load_bx(t - 1, Bp, Xp);
+                slot_bx(k - 1, Bp, Xp);
                 load_state(hc, sH[j], PS);   // hc <- h_{t-1} (h_t is no longer needed)
 #pragma unroll
-                for (int k = 0; k < 2; ++k)
+                for (int q = 0; q < 2; ++q)
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
-                        const float g0 = gg[2 * k][jj], g1 = gg[2 * k + 1][jj];
-                        const float q0 = cs[k] * g0 + sn[k] * g1, q1 = -sn[k] * g0 + cs[k] * g1;
-                        qn[2 * k][jj] = q0;
-                        qn[2 * k + 1][jj] = q1;
-                        const float h0v = hc[2 * k][jj], h1v = hc[2 * k + 1][jj];
-                        const float u0 = uval(Bp, Xp, 2 * k, jj), u1 = uval(Bp, Xp, 2 * k + 1, jj);
+                        const float g0 = gg[2 * q][jj], g1 = gg[2 * q + 1][jj];
+                        const float q0 = cs[q] * g0 + sn[q] * g1, q1 = -sn[q] * g0 + cs[q] * g1;
+                        qn[2 * q][jj] = q0;
+                        qn[2 * q + 1][jj] = q1;
+                        const float h0v = hc[2 * q][jj], h1v = hc[2 * q + 1][jj];
+                        const float u0 = uval(Bp, Xp, 2 * q, jj), u1 = uval(Bp, Xp, 2 * q + 1, jj);
                         dal += q0 * h0v + q1 * h1v;
                         dbe += q0 * u0 + q1 * u1;
                         const float v0 = al * h0v + be * u0, v1 = al * h1v + be * u1;
-                        dth[k] += q1 * v0 - q0 * v1;
+                        dth[q] += q1 * v0 - q0 * v1;
                     }
             }
             // (3) dB_t = dU_t X_t^T, dX_t = B_t^T dU_t
@@ -341,7 +381,7 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
                         }
                     }
                 float* dTo = a.per_head ? a.dtheta_part : a.dtheta;
-                if (cb < 2) dTo[((static_cast<int64_t>(b) * L + t) * GH + gh) * (N / 2) + 2 * pb + cb] = dth[cb];
+                if (cb < 2) dTo[((static_cast<int64_t>(b) * L + t) * GH + gh) * (N / 2) + 2 * pb + cb] = cb ? dth[1] : dth[0];
             }
             // sums over rows: dX within the wave, then across waves through LDS; scalars per wave
 #pragma unroll
@@ -367,20 +407,20 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
             for (int o = tid; o < R * P; o += NT) {
                 float v = 0.f;
 #pragma unroll
-                for (int k = 0; k < NT / 64; ++k) v += sDX[par][k][o];
+                for (int w2 = 0; w2 < NT / 64; ++w2) v += sDX[par][w2][o];
                 const int64_t xi = ((static_cast<int64_t>(b) * L + t) * H + h) * (R * P) + o;
-                a.dx[xi] = v + Dh * io<T>::load(dy + xi);
+                a.dx[xi] = v + Dh * io<T>::load(reinterpret_cast<const T*>(&sDY[k][o]));
             }
             if (tid == 0) {
                 float sa = 0.f, sb = 0.f, sg = 0.f, sd = 0.f;
 #pragma unroll
-                for (int k = 0; k < NT / 64; ++k) {
-                    sa += sSc[par][k][0];
-                    sb += sSc[par][k][1];
-                    sg += sSc[par][k][2];
-                    sd += sSc[par][k][3];
+                for (int w2 = 0; w2 < NT / 64; ++w2) {
+                    sa += sSc[par][w2][0];
+                    sb += sSc[par][w2][1];
+                    sg += sSc[par][w2][2];
+                    sd += sSc[par][w2][3];
                 }
-                const float dtv = a.dt[soff(t)], lv = a.lam[soff(t)];
+                const float dtv = sDt[k], lv = sLam[k];
                 a.ddt[soff(t)] = sa * Ah * al + sb * (1.f - lv) * (al + dtv * Ah * al) + sg * lv;
                 a.dlam[soff(t)] = -sb * dtv * al + sg * dtv;
                 dA_acc += sa * dtv * al + sb * (1.f - lv) * dtv * dtv * al;
@@ -400,7 +440,11 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
     }
     if (carry && (a.dbl || a.dxl)) {
         float Bv[R][4], Xv[R][4], dB[R][4], dX[R][4];
-        load_bx(-1, Bv, Xv);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            ld<T>::v4(blp + ((static_cast<int64_t>(b) * G + g) * R + r) * N + r0, Bv[r]);
+            ld<T>::v4(xlp + ((static_cast<int64_t>(b) * H + h) * R + r) * P + c0, Xv[r]);
+        }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
 #pragma unroll
@@ -437,7 +481,7 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
             for (int o = tid; o < R * P; o += NT) {
                 float v = 0.f;
 #pragma unroll
-                for (int k = 0; k < NT / 64; ++k) v += sDX[0][k][o];
+                for (int w2 = 0; w2 < NT / 64; ++w2) v += sDX[0][w2][o];
                 a.dxl[static_cast<size_t>(bh) * R * P + o] = v;
             }
         }
