@@ -7,6 +7,9 @@ calls it, and it shares no code with the HIP library.
 Contents
   * ``scan``          -- ctypes front end of ``m3_oracle.c``: the sequential
                          fp64 loop over t (the definition written out).
+  * ``scan_fused``    -- the scan with the fused prologue/epilogue of a Mamba-3
+                         layer written out around it: RMSNorm and bias of B and C
+                         (``bc_norm``), per-token A, the output gate (``gate``).
   * ``scan_backward`` -- its reverse-mode derivative (the adjoint loop of
                          ``m3_oracle.c``), pinned by finite differences of ``scan``.
   * ``m3_oracle_np``  -- two independent numpy formulations used to pin it:
@@ -55,6 +58,10 @@ def load(path: str = _LIB):
     f = lib.m3o_scan_rounded
     f.restype = ctypes.c_int
     f.argtypes = [ctypes.POINTER(_Dims)] + [ctypes.c_void_p] * 14 + [ctypes.c_int]
+    f = lib.m3o_scan_ex
+    f.restype = ctypes.c_int
+    f.argtypes = ([ctypes.POINTER(_Dims)] + [ctypes.c_void_p] * 3 + [ctypes.c_int] +
+                  [ctypes.c_void_p] * 11 + [ctypes.c_int])
     f = lib.m3o_scan_backward
     f.restype = ctypes.c_int
     f.argtypes = [ctypes.POINTER(_Dims)] + [ctypes.c_void_p] * 24 + [ctypes.c_int]
@@ -88,7 +95,7 @@ def scan(x, dt, A, lam, theta, B, C, D, state_in=None, nthreads: int = 0, lib_pa
          round_after=None):
     """Sequential fp64 scan.
 
-    Shapes: x (b,L,H,R,P), dt/lam (b,L,H), A/D (H,), theta (b,L,G,N/2),
+    Shapes: x (b,L,H,R,P), dt/lam (b,L,H), A (H,) or per token (b,L,H), D (H,), theta (b,L,G,N/2),
     B/C (b,L,G,R,N).  ``state_in`` is None or a tuple (h0 (b,H,N,P),
     b_last (b,G,R,N), x_last (b,H,R,P)); b_last/x_last may be None.
     ``round_after``: None (full-precision state) or L booleans; after each
@@ -100,7 +107,8 @@ def scan(x, dt, A, lam, theta, B, C, D, state_in=None, nthreads: int = 0, lib_pa
     b, L, H, R, P = x.shape
     G, N = B.shape[2], B.shape[4]
     assert dt.shape == (b, L, H) and lam.shape == (b, L, H)
-    assert A.shape == (H,) and D.shape == (H,)
+    assert (A.shape == (H,) or A.shape == (b, L, H)) and D.shape == (H,)
+    a_tok = int(A.shape != (H,))
     assert theta.shape == (b, L, G, N // 2)
     assert B.shape == (b, L, G, R, N) and C.shape == (b, L, G, R, N)
     h0 = bl = xl = None
@@ -118,17 +126,19 @@ def scan(x, dt, A, lam, theta, B, C, D, state_in=None, nthreads: int = 0, lib_pa
     y = np.empty((b, L, H, R, P), dtype=np.float64)
     h_out = np.empty((b, H, N, P), dtype=np.float64)
     d = _Dims(b, L, H, G, P, N, R)
-    if round_after is None:
+    if round_after is None and not a_tok:
         rc = load(lib_path).m3o_scan(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(lam),
                                      _ptr(theta), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(bl),
                                      _ptr(xl), _ptr(y), _ptr(h_out), int(nthreads))
     else:
-        ra = np.ascontiguousarray(np.asarray(round_after, dtype=bool), dtype=np.uint8)
-        assert ra.shape == (L,)
-        rc = load(lib_path).m3o_scan_rounded(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A),
-                                             _ptr(lam), _ptr(theta), _ptr(B), _ptr(C), _ptr(D),
-                                             _ptr(h0), _ptr(bl), _ptr(xl), _ptr(ra), _ptr(y),
-                                             _ptr(h_out), int(nthreads))
+        ra = None
+        if round_after is not None:
+            ra = np.ascontiguousarray(np.asarray(round_after, dtype=bool), dtype=np.uint8)
+            assert ra.shape == (L,)
+        rc = load(lib_path).m3o_scan_ex(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), a_tok,
+                                        _ptr(lam), _ptr(theta), _ptr(B), _ptr(C), _ptr(D),
+                                        _ptr(h0), _ptr(bl), _ptr(xl), _ptr(ra), _ptr(y),
+                                        _ptr(h_out), int(nthreads))
     if rc != 0:
         raise ValueError(f"m3o_scan failed with code {rc}")
     return y, h_out
@@ -174,3 +184,40 @@ def scan_backward(x, dt, A, lam, theta, B, C, D, dy, dh_out=None, state_in=None,
     if rc != 0:
         raise ValueError(f"m3o_scan_backward failed with code {rc}")
     return out
+
+
+def bc_norm(M, weight=None, bias=None, eps: float = 1e-6):
+    """BCNorm of B or C (b, L, G, R, N): each length-N vector M[b, t, g, r, :] divided by its
+    root mean square (sqrt(mean(M^2) + eps)) and scaled by weight[r, :] when a weight is given,
+    then bias[r, :] added when a bias is given (the bias of B and C follows BCNorm: Mamba-3
+    blog, part 1, "Normalization" and "Removing the short convolution").  fp64."""
+    M = _f64(M)
+    if weight is not None:
+        rms = np.sqrt(np.mean(M * M, axis=-1, keepdims=True) + eps)
+        M = M / rms * _f64(weight)[None, None, None]
+    if bias is not None:
+        M = M + _f64(bias)[None, None, None]
+    return M
+
+
+def gate(y, z):
+    """Output gate y * silu(z), silu(v) = v / (1 + exp(-v)).  fp64."""
+    y, z = _f64(y), _f64(z)
+    return y * z / (1.0 + np.exp(-z))
+
+
+def scan_fused(x, dt, A, lam, theta, B, C, D, b_norm_w=None, c_norm_w=None, b_bias=None,
+               c_bias=None, eps: float = 1e-6, z=None, state_in=None, round_after=None):
+    """``scan`` with the layer's prologue and epilogue around it: B and C through
+    ``bc_norm`` (the carried previous B of state_in as well), A per head (H,) or per token
+    (b,L,H), and y through ``gate`` when z is given.  Returns (y, h_out)."""
+    Bn = bc_norm(B, b_norm_w, b_bias, eps)
+    Cn = bc_norm(C, c_norm_w, c_bias, eps)
+    st = state_in
+    if state_in is not None and state_in[1] is not None:
+        bl = bc_norm(_f64(state_in[1])[:, None], b_norm_w, b_bias, eps)[:, 0]
+        st = (state_in[0], bl, state_in[2])
+    y, h = scan(x, dt, A, lam, theta, Bn, Cn, D, state_in=st, round_after=round_after)
+    if z is not None:
+        y = gate(y, z)
+    return y, h

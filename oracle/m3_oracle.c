@@ -28,6 +28,10 @@
  *           -- output equation y = C h + D x: IBM "What is a Mamba model?",
  *              section on the state and output equations.
  *
+ * Per-token decay rate (m3o_scan_ex with a_per_token): the note writes A_t per
+ * token in the discretisation; with a_per_token set, A is (batch, L, H) and
+ * alpha_t = exp(dt_t * A_t) -- the same recurrence with the per-head A replaced.
+ *
  * Start of a scan: h_0 and the previous input (B_0, X_0) come from the optional
  * state_in; absent, both are zero.  state_out is (h_L, B_L, X_L).
  *
@@ -80,7 +84,7 @@ double m3o_round_bf16(double v) {
 
 /* Scan one (batch b, head h) slice through all L tokens. */
 static void scan_slice(const m3o_dims* dm, int64_t b, int64_t h,
-                       const double* x, const double* dt, const double* A,
+                       const double* x, const double* dt, const double* A, int a_per_token,
                        const double* lam, const double* theta, const double* B,
                        const double* C, const double* D,
                        const double* h0, const double* b_last, const double* x_last,
@@ -106,7 +110,8 @@ static void scan_slice(const m3o_dims* dm, int64_t b, int64_t h,
     for (int64_t t = 0; t < L; ++t) {
         const double dtv = dt[(b * L + t) * H + h];
         const double lv = lam[(b * L + t) * H + h];
-        const double alpha = exp(dtv * A[h]);
+        const double a_th = a_per_token ? A[(b * L + t) * H + h] : A[h];
+        const double alpha = exp(dtv * a_th);
         const double beta = (1.0 - lv) * dtv * alpha;
         const double gamma = lv * dtv;
 
@@ -165,11 +170,11 @@ static void scan_slice(const m3o_dims* dm, int64_t b, int64_t h,
  * (b_last, x_last) are used only when both are non-NULL.  round_after is NULL
  * (full-precision state) or one flag per token (length L, shared by all slices).
  */
-int m3o_scan_rounded(const m3o_dims* dm, const double* x, const double* dt, const double* A,
-                     const double* lam, const double* theta, const double* B, const double* C,
-                     const double* D, const double* h0, const double* b_last,
-                     const double* x_last, const unsigned char* round_after, double* y,
-                     double* h_out, int nthreads) {
+int m3o_scan_ex(const m3o_dims* dm, const double* x, const double* dt, const double* A,
+                int a_per_token, const double* lam, const double* theta, const double* B,
+                const double* C, const double* D, const double* h0, const double* b_last,
+                const double* x_last, const unsigned char* round_after, double* y,
+                double* h_out, int nthreads) {
     if (!dm || !y || dm->batch < 0 || dm->seqlen < 0 || dm->nheads <= 0 || dm->ngroups <= 0 ||
         dm->headdim <= 0 || dm->dstate <= 0 || dm->rank <= 0)
         return -1;
@@ -193,12 +198,22 @@ int m3o_scan_rounded(const m3o_dims* dm, const double* x, const double* dt, cons
         for (int64_t s = 0; s < nslices; ++s) {
             if (!scratch) continue;
             const int64_t b = s / dm->nheads, h = s % dm->nheads;
-            scan_slice(dm, b, h, x, dt, A, lam, theta, B, C, D, h0, b_last, x_last, round_after,
-                       y, h_out, scratch, scratch + NP, scratch + 2 * NP);
+            scan_slice(dm, b, h, x, dt, A, a_per_token, lam, theta, B, C, D, h0, b_last, x_last,
+                       round_after, y, h_out, scratch, scratch + NP, scratch + 2 * NP);
         }
         free(scratch);
     }
     return err;
+}
+
+/* The scan with one decay rate A per head (H), optionally rounding the state. */
+int m3o_scan_rounded(const m3o_dims* dm, const double* x, const double* dt, const double* A,
+                     const double* lam, const double* theta, const double* B, const double* C,
+                     const double* D, const double* h0, const double* b_last,
+                     const double* x_last, const unsigned char* round_after, double* y,
+                     double* h_out, int nthreads) {
+    return m3o_scan_ex(dm, x, dt, A, 0, lam, theta, B, C, D, h0, b_last, x_last, round_after, y,
+                       h_out, nthreads);
 }
 
 /* The scan with a full-precision state (no rounding). */
