@@ -169,6 +169,52 @@ m3_status m3_decode_step(const m3_dims* dims, void* h, const void* b_last,
                          const void* B_t, const void* C_t, const float* D, void* y_t,
                          void* stream);
 
+/*
+ * Fused prologue and epilogue of a Mamba-3 layer around the scan (the pieces of
+ * the layer next to it on the Mamba-3 blog, part 1, "Normalization" and
+ * "Removing the short convolution", and the per-token A of the paper note's
+ * discretisation).  Every pointer may be NULL (that piece is off); fp32 unless
+ * stated.
+ *   A_t:       per-token decay rate replacing A: (batch, L, H) for a prefill,
+ *              (batch, H) for a decode step (A must still be passed; it is not read).
+ *   b_norm_w:  (R, N): B[b,t,g,r,:] is divided by its root mean square
+ *              sqrt(mean(B^2) + norm_eps) and multiplied by b_norm_w[r,:] (BCNorm).
+ *   c_norm_w:  (R, N): the same for C.
+ *   b_bias, c_bias: (R, N) added to B and C after the norm.
+ *              All four act before the rotation, on every B and C the scan reads,
+ *              including a carried previous B: carries stay raw (as given).
+ *   z:         gate, io dtype, laid out as y: y is returned as y * silu(z),
+ *              silu(v) = v / (1 + exp(-v)).
+ *   norm_eps:  > 0 when a norm weight is given.
+ */
+typedef struct {
+    const float* A_t;
+    const float* b_norm_w;
+    const float* c_norm_w;
+    const float* b_bias;
+    const float* c_bias;
+    const void* z;
+    float norm_eps;
+} m3_fusion;
+
+/* m3_prefill_chunked with the fused prologue/epilogue of `fusion` (non-NULL).
+ * Same workspace size (m3_prefill_workspace_size); the other arguments, layouts and
+ * errors as m3_prefill_chunked, plus M3_ERR_INVALID_ARG for a NULL fusion or a norm
+ * weight with norm_eps <= 0. */
+m3_status m3_prefill_fused(const m3_dims* dims, const void* x, const float* dt, const float* A,
+                           const float* lambda, const float* theta, const void* B, const void* C,
+                           const float* D, const m3_fusion* fusion, const m3_state* state_in,
+                           m3_state* state_out, void* y, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* m3_decode_step with the fused prologue/epilogue of `fusion` (non-NULL; z and A_t
+ * have the step's shapes (batch, H, R, P) and (batch, H)).  The carry b_last is the
+ * raw previous B, normalised here like B_t. */
+m3_status m3_decode_step_fused(const m3_dims* dims, void* h, const void* b_last, const void* x_last,
+                               const void* x_t, const float* dt_t, const float* A, const float* lambda_t,
+                               const float* theta_t, const void* B_t, const void* C_t, const float* D,
+                               const m3_fusion* fusion, void* y_t, void* stream);
+
 /* Gradients written by m3_backward; every array is fp32, in the layout of the
  * input it belongs to.  dh0, db_last and dx_last may be NULL (not wanted). */
 typedef struct {

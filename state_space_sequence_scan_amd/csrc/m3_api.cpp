@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int32_t kVersion = 103;  // 0.1.3: backward pass
+constexpr int32_t kVersion = 104;  // 0.1.4: backward pass, fused prologue/epilogue
 constexpr size_t kMaxLds = 160 * 1024;
 
 bool dims_ok(const m3_dims* d, bool prefill) {
@@ -47,10 +47,19 @@ m3::PrefillArgs make_prefill_args(const m3_dims* d) {
 
 namespace m3 {
 
+// Every plan reserves, after the path's own workspace, room for a copy of the
+// carried-in B (batch, G, R, N) in the io dtype: a fused call normalises it there.
+static void add_carry_room(const PrefillArgs& a, PrefillPlan* p) {
+    const size_t al = (p->workspace + 255) & ~static_cast<size_t>(255);
+    p->carry_off = al;
+    p->workspace = al + static_cast<size_t>(a.batch) * a.G * a.R * a.N * (a.bf16 ? 2 : 4);
+}
+
 PrefillPlan plan_prefill(const PrefillArgs& a) {
-    PrefillPlan p{PrefillPath::Unsupported, 1, 0, 0};
+    PrefillPlan p{PrefillPath::Unsupported, 1, 0, 0, 0};
     if (mfma_supported(a)) {
         plan_mfma(a, &p);
+        add_carry_room(a, &p);
         return p;
     }
     if (a.R > kMaxRankGeneric) return p;
@@ -58,12 +67,19 @@ PrefillPlan plan_prefill(const PrefillArgs& a) {
     if (lds <= kMaxLds) {
         p.path = PrefillPath::Generic;
         p.lds = lds;
+        add_carry_room(a, &p);
     }
     return p;
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStream_t st) {
+hipError_t launch_prefill(const PrefillArgs& a0, const PrefillPlan& plan, hipStream_t st) {
     hipError_t e = hipSuccess;
+    PrefillArgs a = a0;   // the scan kernels read the normalised carry; the carry copy-out the raw one
+    if (a.fu.bc() && a.bl_in && a.xl_in) {
+        void* buf = static_cast<uint8_t*>(a.workspace) + plan.carry_off;
+        if ((e = launch_carry_bc(a0, buf, st)) != hipSuccess) return e;
+        a.bl_in = buf;
+    }
     if (plan.path == PrefillPath::Generic) {
         e = launch_prefill_generic(a, st);
     } else if (plan.path == PrefillPath::Mfma) {
@@ -76,7 +92,7 @@ hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStre
         return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
-    if (a.bl_out || a.xl_out) e = launch_carry_out(a, st);
+    if (a0.bl_out || a0.xl_out) e = launch_carry_out(a0, st);
     return e;
 }
 
@@ -112,9 +128,9 @@ namespace {
 
 m3_status prefill_common(const m3_dims* dims, const int64_t* cu, int64_t total_tokens, const void* x,
                          const float* dt, const float* A, const float* lambda, const float* theta,
-                         const void* B, const void* C, const float* D, const m3_state* state_in,
-                         m3_state* state_out, void* y, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+                         const void* B, const void* C, const float* D, const m3_fusion* fu,
+                         const m3_state* state_in, m3_state* state_out, void* y, void* workspace,
+                         size_t workspace_bytes, void* stream) {
     if (!dims_ok(dims, true)) return M3_ERR_INVALID_ARG;
     if (!A || !D) return M3_ERR_INVALID_ARG;
     const int64_t tokens = cu ? total_tokens : dims->batch * dims->seqlen;
@@ -149,6 +165,16 @@ m3_status prefill_common(const m3_dims* dims, const int64_t* cu, int64_t total_t
     }
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
+    if (fu) {
+        a.fu.At = fu->A_t;
+        a.fu.bnw = fu->b_norm_w;
+        a.fu.cnw = fu->c_norm_w;
+        a.fu.bbias = fu->b_bias;
+        a.fu.cbias = fu->c_bias;
+        a.fu.z = fu->z;
+        a.fu.eps = fu->norm_eps;
+        if ((a.fu.bnw || a.fu.cnw) && !(fu->norm_eps > 0.f)) return M3_ERR_INVALID_ARG;
+    }
     const m3::PrefillPlan plan = m3::plan_prefill(a);
     if (plan.path == m3::PrefillPath::Unsupported) return M3_ERR_UNSUPPORTED;
     if (plan.workspace > 0 && (!workspace || workspace_bytes < plan.workspace)) return M3_ERR_WORKSPACE;
@@ -165,8 +191,18 @@ m3_status m3_prefill_chunked(const m3_dims* dims, const void* x, const float* dt
                              const void* B, const void* C, const float* D,
                              const m3_state* state_in, m3_state* state_out, void* y,
                              void* workspace, size_t workspace_bytes, void* stream) {
-    return prefill_common(dims, nullptr, 0, x, dt, A, lambda, theta, B, C, D, state_in, state_out, y,
-                          workspace, workspace_bytes, stream);
+    return prefill_common(dims, nullptr, 0, x, dt, A, lambda, theta, B, C, D, nullptr, state_in, state_out,
+                          y, workspace, workspace_bytes, stream);
+}
+
+m3_status m3_prefill_fused(const m3_dims* dims, const void* x, const float* dt, const float* A,
+                           const float* lambda, const float* theta, const void* B, const void* C,
+                           const float* D, const m3_fusion* fusion, const m3_state* state_in,
+                           m3_state* state_out, void* y, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    if (!fusion) return M3_ERR_INVALID_ARG;
+    return prefill_common(dims, nullptr, 0, x, dt, A, lambda, theta, B, C, D, fusion, state_in, state_out,
+                          y, workspace, workspace_bytes, stream);
 }
 
 m3_status m3_prefill_varlen(const m3_dims* dims, const int64_t* cu_seqlens, int64_t total_tokens,
@@ -175,14 +211,18 @@ m3_status m3_prefill_varlen(const m3_dims* dims, const int64_t* cu_seqlens, int6
                             const m3_state* state_in, m3_state* state_out, void* y, void* workspace,
                             size_t workspace_bytes, void* stream) {
     if (!cu_seqlens || total_tokens < 0) return M3_ERR_INVALID_ARG;
-    return prefill_common(dims, cu_seqlens, total_tokens, x, dt, A, lambda, theta, B, C, D, state_in,
-                          state_out, y, workspace, workspace_bytes, stream);
+    return prefill_common(dims, cu_seqlens, total_tokens, x, dt, A, lambda, theta, B, C, D, nullptr,
+                          state_in, state_out, y, workspace, workspace_bytes, stream);
 }
 
-m3_status m3_decode_step(const m3_dims* dims, void* h, const void* b_last, const void* x_last,
-                         const void* x_t, const float* dt_t, const float* A,
-                         const float* lambda_t, const float* theta_t, const void* B_t,
-                         const void* C_t, const float* D, void* y_t, void* stream) {
+}  // extern "C"
+
+namespace {
+
+m3_status decode_common(const m3_dims* dims, void* h, const void* b_last, const void* x_last,
+                        const void* x_t, const float* dt_t, const float* A, const float* lambda_t,
+                        const float* theta_t, const void* B_t, const void* C_t, const float* D,
+                        const m3_fusion* fu, void* y_t, void* stream) {
     if (!dims_ok(dims, false)) return M3_ERR_INVALID_ARG;
     if (!h || !x_t || !dt_t || !A || !lambda_t || !theta_t || !B_t || !C_t || !D || !y_t)
         return M3_ERR_INVALID_ARG;
@@ -209,10 +249,41 @@ m3_status m3_decode_step(const m3_dims* dims, void* h, const void* b_last, const
     a.has_carry = b_last != nullptr;
     a.bf16 = dims->io_dtype == M3_BF16;
     a.state_bf16 = dims->state_dtype == M3_BF16;
+    if (fu) {
+        a.fu.At = fu->A_t;
+        a.fu.bnw = fu->b_norm_w;
+        a.fu.cnw = fu->c_norm_w;
+        a.fu.bbias = fu->b_bias;
+        a.fu.cbias = fu->c_bias;
+        a.fu.z = fu->z;
+        a.fu.eps = fu->norm_eps;
+        if ((a.fu.bnw || a.fu.cnw) && !(fu->norm_eps > 0.f)) return M3_ERR_INVALID_ARG;
+    }
     if (dims->batch * dims->nheads > 0x7fffffffLL) return M3_ERR_UNSUPPORTED;
     if (!m3::decode_supported(a)) return M3_ERR_UNSUPPORTED;
     const hipError_t e = m3::launch_decode(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+m3_status m3_decode_step(const m3_dims* dims, void* h, const void* b_last, const void* x_last,
+                         const void* x_t, const float* dt_t, const float* A,
+                         const float* lambda_t, const float* theta_t, const void* B_t,
+                         const void* C_t, const float* D, void* y_t, void* stream) {
+    return decode_common(dims, h, b_last, x_last, x_t, dt_t, A, lambda_t, theta_t, B_t, C_t, D, nullptr, y_t,
+                         stream);
+}
+
+m3_status m3_decode_step_fused(const m3_dims* dims, void* h, const void* b_last, const void* x_last,
+                               const void* x_t, const float* dt_t, const float* A, const float* lambda_t,
+                               const float* theta_t, const void* B_t, const void* C_t, const float* D,
+                               const m3_fusion* fusion, void* y_t, void* stream) {
+    if (!fusion) return M3_ERR_INVALID_ARG;
+    return decode_common(dims, h, b_last, x_last, x_t, dt_t, A, lambda_t, theta_t, B_t, C_t, D, fusion, y_t,
+                         stream);
 }
 
 }  // extern "C"

@@ -89,6 +89,16 @@ template <> struct state4<bf16_t> {
     }
 };
 
+// Sum over the 64 lanes of a wave (every lane gets it).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// silu(v) = v / (1 + e^-v), the output gate's nonlinearity.
+__device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
+
 // Accurate sin/cos of an angle of any size (chunk-local angle sums can reach
 // hundreds of radians); the HIP library routine does the range reduction.
 __device__ __forceinline__ void sincos_acc(float a, float* s, float* c) { sincosf(a, s, c); }

@@ -55,6 +55,44 @@ template <> struct state_vec<bf16_t, 8> {
     }
 };
 
+// The fused prologue on the staged per-token operands: each of the R rows of B, C
+// and the previous B (N values in LDS, fp32) through RMSNorm (weight (R, N)) and
+// bias (R, N).  One wave per row at a time; the block has nt threads (one partial
+// wave when nt < 64).  Ends with a barrier.
+__device__ __forceinline__ void fuse_bc(float* sB, float* sC, float* sBp, float* sScale, int R, int N,
+                                        int nt, const Fusion& fu) {
+    const int tid = threadIdx.x, width = nt < 64 ? nt : 64, lane = tid % width, wave = tid / width;
+    const int nwaves = (nt + width - 1) / width;
+    if (fu.bnw || fu.cnw) {
+        for (int row = wave; row < 3 * R; row += nwaves) {
+            const float* src = row < R ? sB + row * N : (row < 2 * R ? sC + (row - R) * N : sBp + (row - 2 * R) * N);
+            float ss = 0.f;
+            for (int n = lane; n < N; n += width) ss += src[n] * src[n];
+            for (int off = 1; off < width; off <<= 1) ss += __shfl_xor(ss, off, width);
+            if (lane == 0) sScale[row] = rsqrtf(ss / N + fu.eps);
+        }
+        __syncthreads();
+    }
+    for (int i = tid; i < R * N; i += nt) {
+        const int r = i / N;
+        float b = sB[i], c = sC[i], bp = sBp[i];
+        if (fu.bnw) {
+            b *= sScale[r] * fu.bnw[i];
+            bp *= sScale[2 * R + r] * fu.bnw[i];
+        }
+        if (fu.cnw) c *= sScale[R + r] * fu.cnw[i];
+        if (fu.bbias) {
+            b += fu.bbias[i];
+            bp += fu.bbias[i];
+        }
+        if (fu.cbias) c += fu.cbias[i];
+        sB[i] = b;
+        sC[i] = c;
+        sBp[i] = bp;
+    }
+    __syncthreads();
+}
+
 // Fast path.  One workgroup of NT threads per (b, h).  Thread tid owns the
 // CW-column block c = tid % PC (PC = P/CW) and the rotation pairs
 // k = kk + TPG * j (kk = tid / PC, j < PPT), i.e. 2 * PPT state rows x CW columns.
@@ -64,7 +102,7 @@ __global__ __launch_bounds__(NT) void decode_fast(
     const T* __restrict__ x_t, const float* __restrict__ dt_t, const float* __restrict__ A,
     const float* __restrict__ lam_t, const float* __restrict__ theta_t,
     const T* __restrict__ B_t, const T* __restrict__ C_t, const float* __restrict__ D,
-    T* __restrict__ y_t, int H, int G, int has_carry) {
+    T* __restrict__ y_t, int H, int G, int has_carry, Fusion fu) {
     constexpr int KP = N / 2;
     constexpr int PC = P / CW;
     constexpr int TPG = NT / PC;
@@ -157,10 +195,14 @@ __global__ __launch_bounds__(NT) void decode_fast(
     }
     const float dtv = dt_t[bh];
     const float lv = lam_t[bh];
-    const float alpha = __expf(dtv * A[hh]);
+    const float alpha = __expf(dtv * (fu.At ? fu.At[bh] : A[hh]));
     const float c1 = (1.f - lv) * dtv;   // (1 - lambda) dt : weight of the carry before the decay
     const float c2 = lv * dtv;           // gamma
     __syncthreads();
+    if (fu.bc()) {   // uniform across the grid
+        __shared__ float sScale[3 * R];
+        fuse_bc(&sB[0][0], &sC[0][0], &sBp[0][0], sScale, R, N, NT, fu);
+    }
 
     fvec xv[R], xpv[R];
 #pragma unroll
@@ -211,11 +253,14 @@ __global__ __launch_bounds__(NT) void decode_fast(
     }
     __syncthreads();
     const float dv = D[hh];
+    const T* zt = static_cast<const T*>(fu.z);
     for (int i = tid; i < R * P; i += NT) {
         float acc = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) acc += (&sY[w][0][0])[i];
-        io<T>::store(y_t + hofs + i, acc + dv * (&sX[0][0])[i]);
+        acc += dv * (&sX[0][0])[i];
+        if (zt) acc *= silu(io<T>::load(zt + hofs + i));
+        io<T>::store(y_t + hofs + i, acc);
     }
 }
 
@@ -227,7 +272,7 @@ __global__ __launch_bounds__(64) void decode_generic(
     const T* __restrict__ x_t, const float* __restrict__ dt_t, const float* __restrict__ A,
     const float* __restrict__ lam_t, const float* __restrict__ theta_t,
     const T* __restrict__ B_t, const T* __restrict__ C_t, const float* __restrict__ D,
-    T* __restrict__ y_t, int H, int G, int N, int P, int R, int has_carry) {
+    T* __restrict__ y_t, int H, int G, int N, int P, int R, int has_carry, Fusion fu) {
     extern __shared__ float smem[];
     const int KP = N / 2;
     float* sB = smem;               // R*N
@@ -237,6 +282,7 @@ __global__ __launch_bounds__(64) void decode_generic(
     float* sXp = sX + R * P;        // R*P
     float* sCs = sXp + R * P;       // KP
     float* sSn = sCs + KP;          // KP
+    float* sScale = sSn + KP;       // 3R
 
     const int bh = blockIdx.x;
     const int b = bh / H, hh = bh - b * H;
@@ -260,8 +306,9 @@ __global__ __launch_bounds__(64) void decode_generic(
         sSn[k] = sn;
     }
     __syncthreads();
+    if (fu.bc()) fuse_bc(sB, sC, sBp, sScale, R, N, blockDim.x, fu);
     const float dtv = dt_t[bh], lv = lam_t[bh];
-    const float alpha = __expf(dtv * A[hh]);
+    const float alpha = __expf(dtv * (fu.At ? fu.At[bh] : A[hh]));
     const float c1 = (1.f - lv) * dtv, c2 = lv * dtv;
     S* hp = h + static_cast<size_t>(bh) * N * P;
     for (int p = tid; p < P; p += blockDim.x) {
@@ -283,8 +330,11 @@ __global__ __launch_bounds__(64) void decode_generic(
             io<S>::store(hp + (2 * k + 1) * P + p, n1);
             for (int r = 0; r < R; ++r) yacc[r] += sC[r * N + 2 * k] * n0 + sC[r * N + 2 * k + 1] * n1;
         }
-        for (int r = 0; r < R; ++r)
-            io<T>::store(y_t + hofs + r * P + p, yacc[r] + D[hh] * sX[r * P + p]);
+        for (int r = 0; r < R; ++r) {
+            float v = yacc[r] + D[hh] * sX[r * P + p];
+            if (fu.z) v *= silu(io<T>::load(static_cast<const T*>(fu.z) + hofs + r * P + p));
+            io<T>::store(y_t + hofs + r * P + p, v);
+        }
     }
 }
 
@@ -298,7 +348,7 @@ static hipError_t launch_fast(const DecodeArgs& a, hipStream_t st) {
                        static_cast<const T*>(a.x_last), static_cast<const T*>(a.x_t), a.dt_t, a.A,
                        a.lam_t, a.theta_t, static_cast<const T*>(a.B_t),
                        static_cast<const T*>(a.C_t), a.D, static_cast<T*>(a.y_t), a.H, a.G,
-                       a.has_carry);
+                       a.has_carry, a.fu);
     return hipGetLastError();
 }
 
@@ -313,19 +363,19 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
         }
     }
     if (a.N == 16 && a.P == 16 && a.R == 1) return launch_fast<T, S, 16, 16, 1, 32>(a, st);
-    const size_t shm = sizeof(float) * (3 * a.R * a.N + 2 * a.R * a.P + a.N);
+    const size_t shm = sizeof(float) * (3 * a.R * a.N + 2 * a.R * a.P + a.N + 3 * a.R);
     hipLaunchKernelGGL((decode_generic<T, S>), dim3(static_cast<unsigned>(a.batch * a.H)), dim3(64),
                        shm, st, static_cast<S*>(a.h), static_cast<const T*>(a.b_last),
                        static_cast<const T*>(a.x_last), static_cast<const T*>(a.x_t), a.dt_t, a.A,
                        a.lam_t, a.theta_t, static_cast<const T*>(a.B_t),
                        static_cast<const T*>(a.C_t), a.D, static_cast<T*>(a.y_t), a.H, a.G,
-                       a.N, a.P, a.R, a.has_carry);
+                       a.N, a.P, a.R, a.has_carry, a.fu);
     return hipGetLastError();
 }
 
 bool decode_supported(const DecodeArgs& a) {
     if (a.R > kMaxRankGeneric) return false;
-    const size_t shm = sizeof(float) * (3 * a.R * a.N + 2 * a.R * a.P + a.N);
+    const size_t shm = sizeof(float) * (3 * a.R * a.N + 2 * a.R * a.P + a.N + 3 * a.R);
     return shm <= 64 * 1024;
 }
 

@@ -9,6 +9,20 @@ namespace m3 {
 
 constexpr int kMaxRankGeneric = 8;
 
+// Fused prologue/epilogue of a Mamba-3 layer around the scan (all optional):
+// per-token decay rates, RMSNorm and bias of B and C before the rotation, and the
+// output gate y * silu(z).
+struct Fusion {
+    const float* At = nullptr;      // per-token A: (b, L, H) prefill / (b, H) decode
+    const float* bnw = nullptr;     // RMSNorm weight of B (R, N)
+    const float* cnw = nullptr;     // RMSNorm weight of C (R, N)
+    const float* bbias = nullptr;   // bias of B (R, N)
+    const float* cbias = nullptr;   // bias of C (R, N)
+    const void* z = nullptr;        // gate input, io dtype, laid out as y
+    float eps = 1e-6f;
+    __host__ __device__ bool bc() const { return bnw || cnw || bbias || cbias; }
+};
+
 struct DecodeArgs {
     void* h;                 // state, fp32 or bf16 (state_bf16)
     const void* b_last;
@@ -26,6 +40,7 @@ struct DecodeArgs {
     int has_carry;
     bool bf16;               // io dtype
     bool state_bf16;         // state dtype
+    Fusion fu;
 };
 
 bool decode_supported(const DecodeArgs& a);
@@ -55,6 +70,7 @@ struct PrefillArgs {
     bool state_bf16;         // state dtype
     const int64_t* cu;       // packed variable-length batch: sequence starts (batch + 1), device; else null
     int64_t T;               // tokens in the packed batch (batch * L without cu)
+    Fusion fu;
 };
 
 // Which kernel family runs a prefill, and the workspace it needs.
@@ -64,6 +80,7 @@ struct PrefillPlan {
     int nseg;                // segments per sequence (1 = one sweep per (b, h))
     size_t workspace;        // bytes
     size_t lds;              // dynamic LDS bytes of the main kernel
+    size_t carry_off;        // workspace offset of the normalised carried-in B (fused calls)
 };
 PrefillPlan plan_prefill(const PrefillArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStream_t st);
@@ -80,6 +97,8 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, const PrefillPlan& plan, hi
 
 // Carry-out copy (B and X of the last token), in m3_prefill_generic.hip.
 hipError_t launch_carry_out(const PrefillArgs& a, hipStream_t st);
+// The carried-in B through the fusion's RMSNorm and bias, into `out` (b, G, R, N) io dtype.
+hipError_t launch_carry_bc(const PrefillArgs& a, void* out, hipStream_t st);
 
 // Backward pass (m3_backward.hip): N = 128, P = 64, R in {1, 2, 4}, fp32 or bf16 io.
 struct BwdShape {

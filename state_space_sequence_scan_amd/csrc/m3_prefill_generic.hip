@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void prefill_generic(
     const T* __restrict__ C, const float* __restrict__ Dv, const void* __restrict__ h_in,
     const T* __restrict__ bl_in, const T* __restrict__ xl_in, T* __restrict__ y,
     void* __restrict__ h_out, int64_t Lmax, int H, int G, int N, int P, int R, int Q, int state_bf16,
-    const int64_t* __restrict__ cu, int64_t Tt) {
+    const int64_t* __restrict__ cu, int64_t Tt, Fusion fu) {
     extern __shared__ float smem[];
     const int KP = N / 2, QR = Q * R;
     float* S = smem;                       // N*P
@@ -44,6 +44,9 @@ __global__ __launch_bounds__(256) void prefill_generic(
     float* wv = cum + Q;                   // Q
     float* gam = wv + Q;                   // Q
     float* sv = gam + Q;                   // Q
+    float* bsc = sv + Q;                   // Q*R: RMSNorm scale of each B row of the chunk
+    float* csc = bsc + QR;                 // Q*R: same for C
+    const T* zg = static_cast<const T*>(fu.z);
 
     const int bh = blockIdx.x;
     const int b = bh / H, h = bh - b * H;
@@ -83,7 +86,7 @@ __global__ __launch_bounds__(256) void prefill_generic(
             if (i < nq) {
                 const int64_t t = t0 + i;
                 const float dtv = dt[(tb + t) * H + h], lv = lam[(tb + t) * H + h];
-                a = dtv * Ah;
+                a = dtv * (fu.At ? fu.At[(tb + t) * H + h] : Ah);
                 gm = lv * dtv;
                 w = gm;
                 if (t + 1 < L) w += (1.f - lam[(tb + t + 1) * H + h]) * dt[(tb + t + 1) * H + h];
@@ -104,6 +107,23 @@ __global__ __launch_bounds__(256) void prefill_generic(
         for (int idx = tid; idx < Q * KP; idx += NT) {
             const int i = idx / KP, k = idx - i * KP;
             phi[idx] = (i < nq) ? theta[((tb + t0 + i) * G + g) * KP + k] : 0.f;
+        }
+        // RMSNorm scales of the chunk's B and C rows (token, rank), when normalised.
+        if (fu.bnw || fu.cnw) {
+            for (int row = tid; row < QR; row += NT) {
+                const int i = row / R, r = row - i * R;
+                float sb = 0.f, sc = 0.f;
+                if (i < nq) {
+                    const size_t o = (((tb + t0 + i) * G + g) * R + r) * static_cast<size_t>(N);
+                    for (int n = 0; n < N; ++n) {
+                        const float bv = io<T>::load(B + o + n), cv = io<T>::load(C + o + n);
+                        sb += bv * bv;
+                        sc += cv * cv;
+                    }
+                }
+                bsc[row] = rsqrtf(sb / N + fu.eps);
+                csc[row] = rsqrtf(sc / N + fu.eps);
+            }
         }
         __syncthreads();
         // Chunk-local angle prefix sums, one pair per thread, within LDS.
@@ -130,8 +150,25 @@ __global__ __launch_bounds__(256) void prefill_generic(
                 const size_t o = (((tb + t0 + i) * G + g) * R + r) * static_cast<size_t>(N) + 2 * k;
                 float sn, cs;
                 sincos_acc(phi[i * KP + k], &sn, &cs);
-                const float bb0 = io<T>::load(B + o), bb1 = io<T>::load(B + o + 1);
-                const float cc0 = io<T>::load(C + o), cc1 = io<T>::load(C + o + 1);
+                float bb0 = io<T>::load(B + o), bb1 = io<T>::load(B + o + 1);
+                float cc0 = io<T>::load(C + o), cc1 = io<T>::load(C + o + 1);
+                const int wi = r * N + 2 * k;
+                if (fu.bnw) {
+                    bb0 *= bsc[i * R + r] * fu.bnw[wi];
+                    bb1 *= bsc[i * R + r] * fu.bnw[wi + 1];
+                }
+                if (fu.cnw) {
+                    cc0 *= csc[i * R + r] * fu.cnw[wi];
+                    cc1 *= csc[i * R + r] * fu.cnw[wi + 1];
+                }
+                if (fu.bbias) {
+                    bb0 += fu.bbias[wi];
+                    bb1 += fu.bbias[wi + 1];
+                }
+                if (fu.cbias) {
+                    cc0 += fu.cbias[wi];
+                    cc1 += fu.cbias[wi + 1];
+                }
                 b0 = cs * bb0 + sn * bb1;
                 b1 = -sn * bb0 + cs * bb1;
                 c0 = cs * cc0 + sn * cc1;
@@ -175,8 +212,9 @@ __global__ __launch_bounds__(256) void prefill_generic(
             float acc = __expf(cum[i]) * st;
             for (int js = 0; js < (i + 1) * R; ++js) acc += Gm[ir * QR + js] * X[js * P + p];
             acc += Dh * X[ir * P + p];
-            io<T>::store(y + ((tb + t0 + i) * H + h) * static_cast<size_t>(R * P) + (ir - i * R) * P + p,
-                         acc);
+            const size_t yi = ((tb + t0 + i) * H + h) * static_cast<size_t>(R * P) + (ir - i * R) * P + p;
+            if (zg) acc *= silu(io<T>::load(zg + yi));
+            io<T>::store(y + yi, acc);
         }
         __syncthreads();
         // State update, one rotation pair x column per thread.
@@ -232,10 +270,44 @@ __global__ void carry_out(const T* __restrict__ x, const T* __restrict__ B,
     }
 }
 
+// The carried previous B through the same RMSNorm and bias as every B (one wave per
+// row (b, g, r) of N values), into a copy the scan kernels read instead.
+template <typename T>
+__global__ __launch_bounds__(64) void carry_bc(const T* __restrict__ bl_in, T* __restrict__ out, int N, int R,
+                                               Fusion fu) {
+    const int64_t row = blockIdx.x;
+    const int r = static_cast<int>(row % R);
+    const int lane = threadIdx.x;
+    const T* src = bl_in + row * N;
+    float ss = 0.f;
+    for (int n = lane; n < N; n += 64) {
+        const float v = io<T>::load(src + n);
+        ss += v * v;
+    }
+    const float sc = fu.bnw ? rsqrtf(wave_sum(ss) / N + fu.eps) : 1.f;
+    for (int n = lane; n < N; n += 64) {
+        float v = io<T>::load(src + n);
+        if (fu.bnw) v *= sc * fu.bnw[r * N + n];
+        if (fu.bbias) v += fu.bbias[r * N + n];
+        io<T>::store(out + row * N + n, v);
+    }
+}
+
+hipError_t launch_carry_bc(const PrefillArgs& a, void* out, hipStream_t st) {
+    const unsigned rows = static_cast<unsigned>(a.batch * a.G * a.R);
+    if (a.bf16)
+        hipLaunchKernelGGL(carry_bc<bf16_t>, dim3(rows), dim3(64), 0, st, static_cast<const bf16_t*>(a.bl_in),
+                           static_cast<bf16_t*>(out), a.N, a.R, a.fu);
+    else
+        hipLaunchKernelGGL(carry_bc<float>, dim3(rows), dim3(64), 0, st, static_cast<const float*>(a.bl_in),
+                           static_cast<float*>(out), a.N, a.R, a.fu);
+    return hipGetLastError();
+}
+
 size_t generic_lds_bytes(const PrefillArgs& a) {
     const size_t QR = static_cast<size_t>(a.Q) * a.R;
     return sizeof(float) * (static_cast<size_t>(a.N) * a.P + 2 * QR * a.N + QR * a.P + QR * QR +
-                            static_cast<size_t>(a.Q) * (a.N / 2) + 4 * static_cast<size_t>(a.Q));
+                            static_cast<size_t>(a.Q) * (a.N / 2) + 4 * static_cast<size_t>(a.Q) + 2 * QR);
 }
 
 template <typename T>
@@ -252,7 +324,7 @@ static hipError_t launch_generic_t(const PrefillArgs& a, hipStream_t st) {
                        static_cast<const T*>(a.B), static_cast<const T*>(a.C), a.D, a.h_in,
                        static_cast<const T*>(a.bl_in), static_cast<const T*>(a.xl_in),
                        static_cast<T*>(a.y), a.h_out, a.L, a.H, a.G, a.N, a.P, a.R, a.Q,
-                       a.state_bf16 ? 1 : 0, a.cu, a.T);
+                       a.state_bf16 ? 1 : 0, a.cu, a.T, a.fu);
     return hipGetLastError();
 }
 

@@ -121,7 +121,7 @@ __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
                                                 const uint16_t* __restrict__ C,
                                                 const float* __restrict__ theta, int64_t L, int G,
                                                 int nchunks, uint8_t* __restrict__ prep,
-                                                const int64_t* __restrict__ cu, int64_t T) {
+                                                const int64_t* __restrict__ cu, int64_t T, Fusion fu) {
     constexpr int QR = Q * R;
     __shared__ float sCos[Q][KP], sSin[Q][KP];
     __shared__ float sPart[4][KP];
@@ -171,6 +171,10 @@ __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
     __syncthreads();
     // One unit = 8 consecutive rows (token, rank) x one rotation pair k:
     // R(-phi) (x0, x1) = (c x0 + s x1, -s x0 + c x1), stored as 4 bytes per row.
+    // With KP = 64 pairs and NT a multiple of 64, the 64 pairs of a row are the 64
+    // lanes of one wave, so a row's RMSNorm (before the rotation) is a wave sum.
+    static_assert(KP == 64 && NT % 64 == 0, "one wave per row");
+    const bool bc = fu.bc();
     for (int u = tid; u < (QR / 8) * KP; u += NT) {
         const int r8 = u / KP, k = u - r8 * KP;
 #pragma unroll
@@ -183,8 +187,29 @@ __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
                 const uint32_t bb = *reinterpret_cast<const uint32_t*>(B + o);
                 const uint32_t cc = *reinterpret_cast<const uint32_t*>(C + o);
                 const float cn = sCos[i][k], sn = sSin[i][k];
-                const float x0 = bits_to_f(bb & 0xffff), x1 = bits_to_f(bb >> 16);
-                const float y0 = bits_to_f(cc & 0xffff), y1 = bits_to_f(cc >> 16);
+                float x0 = bits_to_f(bb & 0xffff), x1 = bits_to_f(bb >> 16);
+                float y0 = bits_to_f(cc & 0xffff), y1 = bits_to_f(cc >> 16);
+                if (bc) {   // uniform: whole waves take this branch (i < nq is uniform per row)
+                    const int wi = r * N + 2 * k;
+                    if (fu.bnw) {
+                        const float sc = rsqrtf(wave_sum(x0 * x0 + x1 * x1) / N + fu.eps);
+                        x0 *= sc * fu.bnw[wi];
+                        x1 *= sc * fu.bnw[wi + 1];
+                    }
+                    if (fu.cnw) {
+                        const float sc = rsqrtf(wave_sum(y0 * y0 + y1 * y1) / N + fu.eps);
+                        y0 *= sc * fu.cnw[wi];
+                        y1 *= sc * fu.cnw[wi + 1];
+                    }
+                    if (fu.bbias) {
+                        x0 += fu.bbias[wi];
+                        x1 += fu.bbias[wi + 1];
+                    }
+                    if (fu.cbias) {
+                        y0 += fu.cbias[wi];
+                        y1 += fu.cbias[wi + 1];
+                    }
+                }
                 b0 = cn * x0 + sn * x1;
                 b1 = -sn * x0 + cn * x1;
                 c0 = cn * y0 + sn * y1;
@@ -221,6 +246,8 @@ struct ScanParams {
     int state_bf16;         // h_in and h_out hold bf16 (else fp32)
     const int64_t* cu;      // packed variable-length batch: sequence starts, or null
     int64_t T;              // tokens in the packed arrays
+    const float* At;        // per-token decay rates (b, L, H) replacing A, or null
+    const uint16_t* z;      // output gate input, laid out as y, or null
 };
 
 // Initial state of segment 0 when no segment pass ran: h_in plus the beta term
@@ -413,7 +440,7 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
     // ---- registers holding the next chunk's inputs (raw loads; validity applied by the consumer)
     u32v<4 * XPT> xr;           // X units tid + NTH*e: row u / 8, columns 8 (u % 8) .. +7
     u32v<4 * BPT> br;           // Bt units tid + NTH*e
-    float pd0 = 0.f, pl0 = 0.f, pd1 = 0.f, pl1 = 0.f, pcs = 0.f;
+    float pd0 = 0.f, pl0 = 0.f, pd1 = 0.f, pl1 = 0.f, pa0 = 0.f, pcs = 0.f;
     int pnq = 0;                // valid tokens of the prefetched chunk
     bfv<32> cf0, cf1;           // Ct fragments (4 k-steps) of the wave's output row blocks a_lo, a_hi
 
@@ -452,6 +479,7 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
             pl0 = lmc[static_cast<uint32_t>(i0 * p.H)];                                                       \
             pd1 = dtc[static_cast<uint32_t>(i1 * p.H)];                                                       \
             pl1 = lmc[static_cast<uint32_t>(i1 * p.H)];                                                       \
+            pa0 = (p.At ? p.At : p.dt)[(tb + t0f) * p.H + h + static_cast<uint32_t>(i0 * p.H)];              \
         }                                                                                                     \
     } while (0)
 
@@ -486,7 +514,7 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
             const bool has1 = valid && (nextpos + lane + 1 < Lb);                                             \
             const float gm = lv * dtv;                                                                        \
             const float wv = gm + (has1 ? (1.f - pl1) * pd1 : 0.f);                                           \
-            float cum = dtv * Ah;                                                                             \
+            float cum = dtv * (p.At ? pa0 : Ah);                                                              \
             _Pragma("unroll") for (int off = 1; off < 64; off <<= 1) {                                        \
                 const float o = __shfl_up(cum, off);                                                          \
                 if (lane >= off) cum += o;                                                                    \
@@ -644,10 +672,24 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
     } while (0)
 
     // Lane (l16, lg) writes columns 16ct + 4lg .. +3 of output row 16a + l16: 8 bytes per tile.
+    // With a gate the row's z values (same place as y; rows past the end read the last
+    // token's) multiply y by silu(z) first.
 #define M3_STORE_Y(yv_, a_)                                                                                   \
     do {                                                                                                      \
         const int i = 16 * (a_) + l16;                                                                        \
         const int tk = i / R, r = i - tk * R;                                                                 \
+        if (p.z) {                                                                                            \
+            const uint16_t* zrow = p.z + ((tb + t0) * p.H + h) * static_cast<int64_t>(R * P) +                \
+                                   (static_cast<uint32_t>(tk < nq ? tk : nq - 1) * HRP +                      \
+                                    static_cast<uint32_t>(r * P + 4 * lg));                                   \
+            _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) {                                                \
+                const uint2 zz = *reinterpret_cast<const uint2*>(zrow + 16 * ct);                             \
+                yv_[ct][0] *= silu(bits_to_f(zz.x & 0xffff));                                                 \
+                yv_[ct][1] *= silu(bits_to_f(zz.x >> 16));                                                    \
+                yv_[ct][2] *= silu(bits_to_f(zz.y & 0xffff));                                                 \
+                yv_[ct][3] *= silu(bits_to_f(zz.y >> 16));                                                    \
+            }                                                                                                 \
+        }                                                                                                     \
         uint16_t* yrow = (tk < nq) ? ych + (static_cast<uint32_t>(tk) * HRP + static_cast<uint32_t>(r * P + 4 * lg)) \
                                    : p.y_sink + lane * 64;                                                    \
         _Pragma("unroll") for (int ct = 0; ct < 4; ++ct)                                                      \
@@ -1056,7 +1098,7 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
 
     hipLaunchKernelGGL((mf::rope_prep<R, Q>), dim3(nchunks, a.G, static_cast<unsigned>(a.batch)), dim3(mf::NT), 0,
                        st, static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.theta, a.L,
-                       a.G, nchunks, base + ws.prep, a.cu, a.T);
+                       a.G, nchunks, base + ws.prep, a.cu, a.T, a.fu);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
@@ -1077,6 +1119,8 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
     p.L = a.L;
     p.cu = a.cu;
     p.T = a.T;
+    p.At = a.fu.At;
+    p.z = static_cast<const uint16_t*>(a.fu.z);
     p.H = a.H;
     p.G = a.G;
     p.nchunks = nchunks;

@@ -42,6 +42,12 @@ class Grads(ctypes.Structure):
                 ("dx", "ddt", "dA", "dlambda", "dtheta", "dB", "dC", "dD", "dh0", "db_last", "dx_last")]
 
 
+class Fusion(ctypes.Structure):
+    _fields_ = [("A_t", ctypes.c_void_p), ("b_norm_w", ctypes.c_void_p), ("c_norm_w", ctypes.c_void_p),
+                ("b_bias", ctypes.c_void_p), ("c_bias", ctypes.c_void_p), ("z", ctypes.c_void_p),
+                ("norm_eps", ctypes.c_float)]
+
+
 class M3Error(RuntimeError):
     def __init__(self, where: str, code: int):
         super().__init__(f"{where}: {STATUS.get(code, code)} ({code})")
@@ -74,6 +80,11 @@ def lib(path: str = LIB_PATH):
                                     [ctypes.POINTER(State), ctypes.POINTER(State), vp, vp, sz, vp])
     L.m3_decode_step.restype = ctypes.c_int
     L.m3_decode_step.argtypes = [ctypes.POINTER(Dims)] + [vp] * 13
+    L.m3_prefill_fused.restype = ctypes.c_int
+    L.m3_prefill_fused.argtypes = ([ctypes.POINTER(Dims)] + [vp] * 8 + [ctypes.POINTER(Fusion)] +
+                                   [ctypes.POINTER(State), ctypes.POINTER(State), vp, vp, sz, vp])
+    L.m3_decode_step_fused.restype = ctypes.c_int
+    L.m3_decode_step_fused.argtypes = [ctypes.POINTER(Dims)] + [vp] * 11 + [ctypes.POINTER(Fusion), vp, vp]
     L.m3_backward_workspace_size.restype = ctypes.c_int
     L.m3_backward_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(sz)]
     L.m3_backward.restype = ctypes.c_int
@@ -352,3 +363,94 @@ def backward(x, dt, A, lam, theta, B, C, D, dy, dh_out=None, state_in: Optional[
     if rc != 0:
         raise M3Error("m3_backward", rc)
     return out
+
+
+def _fusion(dev, shapes, A_t=None, b_norm_w=None, c_norm_w=None, b_bias=None, c_bias=None, z=None,
+            eps: float = 1e-6, io=None):
+    """Checks the fusion tensors against the call's shapes and packs them."""
+    R, N, at_shape, z_shape = shapes
+    for t, name in ((b_norm_w, "b_norm_w"), (c_norm_w, "c_norm_w"), (b_bias, "b_bias"), (c_bias, "c_bias")):
+        if t is not None:
+            _check(t, name, (R, N), torch.float32, dev)
+    if A_t is not None:
+        _check(A_t, "A_t", at_shape, torch.float32, dev)
+    if z is not None:
+        _check(z, "z", z_shape, io, dev)
+    return Fusion(*[None if t is None else t.data_ptr() for t in (A_t, b_norm_w, c_norm_w, b_bias, c_bias, z)],
+                  float(eps))
+
+
+def prefill_fused(x, dt, A, lam, theta, B, C, D, chunk: int, A_t=None, b_norm_w=None, c_norm_w=None,
+                  b_bias=None, c_bias=None, z=None, eps: float = 1e-6,
+                  state_in: Optional[DecodeState] = None, out_state: bool = True,
+                  y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  state_dtype: Optional[torch.dtype] = None):
+    """``prefill`` with the fused layer prologue/epilogue (m3_prefill_fused): per-token A
+    (b,L,H), RMSNorm weights and biases of B and C (R,N), gate z (laid out as y)."""
+    b, L, H, R, P = x.shape
+    G, N = B.shape[2], B.shape[4]
+    dev = x.device
+    io = x.dtype
+    _check(x, "x", (b, L, H, R, P), io, dev)
+    _check(dt, "dt", (b, L, H), torch.float32, dev)
+    _check(lam, "lam", (b, L, H), torch.float32, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(theta, "theta", (b, L, G, N // 2), torch.float32, dev)
+    _check(B, "B", (b, L, G, R, N), io, dev)
+    _check(C, "C", (b, L, G, R, N), io, dev)
+    fu = _fusion(dev, (R, N, (b, L, H), (b, L, H, R, P)), A_t, b_norm_w, c_norm_w, b_bias, c_bias, z, eps, io)
+    if state_dtype is None:
+        state_dtype = state_in.h.dtype if state_in is not None else torch.float32
+    dims = make_dims(b, L, H, G, P, N, R, chunk, _IO[io], _IO[state_dtype])
+    if y is None:
+        y = torch.empty_like(x)
+    sin = None
+    if state_in is not None:
+        _check(state_in.h, "state_in.h", (b, H, N, P), state_dtype, dev)
+        if state_in.b_last is not None:
+            _check(state_in.b_last, "state_in.b_last", (b, G, R, N), io, dev)
+            _check(state_in.x_last, "state_in.x_last", (b, H, R, P), io, dev)
+        sin = State(state_in.h.data_ptr(),
+                    None if state_in.b_last is None else state_in.b_last.data_ptr(),
+                    None if state_in.x_last is None else state_in.x_last.data_ptr())
+    sout = st = None
+    if out_state:
+        st = DecodeState(torch.empty((b, H, N, P), dtype=state_dtype, device=dev),
+                         torch.empty((b, G, R, N), dtype=io, device=dev),
+                         torch.empty((b, H, R, P), dtype=io, device=dev))
+        sout = State(st.h.data_ptr(), st.b_last.data_ptr(), st.x_last.data_ptr())
+    ws = workspace_size(dims)
+    if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
+        workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+    rc = lib().m3_prefill_fused(ctypes.byref(dims), _p(x), _p(dt), _p(A), _p(lam), _p(theta), _p(B), _p(C),
+                                _p(D), ctypes.byref(fu), None if sin is None else ctypes.byref(sin),
+                                None if sout is None else ctypes.byref(sout), _p(y),
+                                _p(workspace) if ws > 0 else None, ws, _stream(dev))
+    if rc != 0:
+        raise M3Error("m3_prefill_fused", rc)
+    return y, st
+
+
+def decode_step_fused(state: DecodeState, x_t, dt_t, A, lam_t, theta_t, B_t, C_t, D, A_t=None,
+                      b_norm_w=None, c_norm_w=None, b_bias=None, c_bias=None, z=None, eps: float = 1e-6,
+                      y_t: Optional[torch.Tensor] = None, advance: bool = True):
+    """``decode_step`` with the fused prologue/epilogue (m3_decode_step_fused): A_t (b,H),
+    norm weights and biases (R,N), gate z (b,H,R,P).  The carry stays raw."""
+    b, H, R, P = x_t.shape
+    G, N = B_t.shape[1], B_t.shape[3]
+    dev = x_t.device
+    io = x_t.dtype
+    _check(state.h, "state.h", (b, H, N, P), state.h.dtype, dev)
+    fu = _fusion(dev, (R, N, (b, H), (b, H, R, P)), A_t, b_norm_w, c_norm_w, b_bias, c_bias, z, eps, io)
+    dims = make_dims(b, 1, H, G, P, N, R, 1, _IO[io], _IO[state.h.dtype])
+    if y_t is None:
+        y_t = torch.empty_like(x_t)
+    rc = lib().m3_decode_step_fused(ctypes.byref(dims), _p(state.h), _p(state.b_last), _p(state.x_last), _p(x_t),
+                                    _p(dt_t), _p(A), _p(lam_t), _p(theta_t), _p(B_t), _p(C_t), _p(D),
+                                    ctypes.byref(fu), _p(y_t), _stream(dev))
+    if rc != 0:
+        raise M3Error("m3_decode_step_fused", rc)
+    if advance:
+        state.b_last, state.x_last = B_t, x_t
+    return y_t

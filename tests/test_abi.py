@@ -29,8 +29,9 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_symbols() == ["m3_backward", "m3_backward_workspace_size", "m3_decode_step",
-                                  "m3_prefill_chunked", "m3_prefill_varlen", "m3_prefill_workspace_size",
-                                  "m3_status_string", "m3_version"]
+                                  "m3_decode_step_fused", "m3_prefill_chunked", "m3_prefill_fused",
+                                  "m3_prefill_varlen", "m3_prefill_workspace_size", "m3_status_string",
+                                  "m3_version"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -202,3 +203,26 @@ def test_backward_rejects_bad_arguments(lib):
     # workspace too small
     assert _bwd(lib, big, _grads(), ws=FAKE, nbytes=n.value - 1) == -3
     assert _bwd(lib, big, _grads(), ws=None, nbytes=0) == -3
+
+
+def test_fused_entry_points_reject_bad_arguments(lib):
+    d = _dims()
+    fu = m3scan.Fusion(None, None, None, None, None, None, 1e-6)
+    # a NULL fusion
+    assert lib.m3_prefill_fused(ctypes.byref(d), *[FAKE] * 8, None, None, None, FAKE, None, 0, None) == -1
+    assert lib.m3_decode_step_fused(ctypes.byref(d), *[FAKE] * 11, None, FAKE, None) == -1
+    # a norm weight with a non-positive epsilon
+    bad = m3scan.Fusion(None, 0x1000, None, None, None, None, 0.0)
+    assert lib.m3_prefill_fused(ctypes.byref(d), *[FAKE] * 8, ctypes.byref(bad), None, None, FAKE, None, 0,
+                                None) == -1
+    assert lib.m3_decode_step_fused(ctypes.byref(d), *[FAKE] * 11, ctypes.byref(bad), FAKE, None) == -1
+    # bad dims, missing inputs: as the plain entry points
+    for kw in BAD_DIMS:
+        bd = _dims(**kw)
+        assert lib.m3_prefill_fused(ctypes.byref(bd), *[FAKE] * 8, ctypes.byref(fu), None, None, FAKE, None, 0,
+                                    None) == -1, kw
+    assert lib.m3_prefill_fused(ctypes.byref(d), *([FAKE] * 7 + [None]), ctypes.byref(fu), None, None, FAKE,
+                                None, 0, None) == -1
+    # the workspace reserves room for the normalised carry: none given is too small
+    assert lib.m3_prefill_fused(ctypes.byref(d), *[FAKE] * 8, ctypes.byref(fu), None, None, FAKE, None, 0,
+                                None) == -3

@@ -1,0 +1,106 @@
+"""GPU parity of the fused prologue/epilogue (m3_prefill_fused, m3_decode_step_fused)
+against the oracle's scan_fused: per-token A, RMSNorm of B and C with weights, their
+biases, and the output gate -- together and one at a time, on the matrix-core and the
+generic prefill paths, from a state with a (raw) carried B, and a fused prefill
+continued by fused decode steps."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, draw, np64, rand_state, say, slice_err
+from state_space_sequence_scan_amd import m3scan
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("x", "dt", "A", "lam", "theta", "B", "C", "D")
+
+
+def _fusion(b, L, H, R, N, P, io, seed, parts):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    tdt = torch.bfloat16 if io == "bf16" else torch.float32
+    f = {}
+    if "A_t" in parts:
+        f["A_t"] = (-torch.exp(torch.rand((b, L, H), generator=g) * np.log(16.0))).cuda()
+    if "norm" in parts:
+        f["b_norm_w"] = (1.0 + 0.3 * torch.randn((R, N), generator=g)).cuda()
+        f["c_norm_w"] = (1.0 + 0.3 * torch.randn((R, N), generator=g)).cuda()
+    if "bias" in parts:
+        f["b_bias"] = (0.02 + 0.05 * torch.randn((R, N), generator=g)).cuda()
+        f["c_bias"] = (0.02 + 0.05 * torch.randn((R, N), generator=g)).cuda()
+    if "gate" in parts:
+        f["z"] = torch.randn((b, L, H, R, P), generator=g).to(tdt).cuda()
+    return f
+
+
+def _oracle(d, f, state_in=None):
+    kw = {k: np64(v) for k, v in f.items() if k != "A_t"}
+    args = [np64(d[k]) for k in NAMES]
+    if "A_t" in f:
+        args[2] = np64(f["A_t"])
+    return oracle.scan_fused(*args, **kw, state_in=state_in)
+
+
+CASES = [
+    # b, L, H, G, P, N, R, Q, io, parts
+    (2, 100, 4, 2, 64, 128, 2, 32, "bf16", ("A_t", "norm", "bias", "gate")),   # matrix cores
+    (1, 70, 2, 1, 64, 128, 4, 64, "bf16", ("norm",)),
+    (1, 70, 2, 1, 64, 128, 4, 64, "bf16", ("bias",)),
+    (1, 70, 2, 1, 64, 128, 1, 64, "bf16", ("gate",)),
+    (1, 70, 2, 1, 64, 128, 1, 64, "bf16", ("A_t",)),
+    (2, 45, 4, 2, 16, 16, 2, 16, "fp32", ("A_t", "norm", "bias", "gate")),      # generic path
+]
+
+
+def _id(c):
+    return "b{}L{}H{}G{}P{}N{}R{}Q{}-{}-{}".format(*c[:9], "+".join(c[9]))
+
+
+@pytest.mark.parametrize("case", CASES, ids=_id)
+def test_prefill_fused_matches_oracle(case):
+    b, L, H, G, P, N, R, Q, io, parts = case
+    say("prefill fused", _id(case))
+    d = draw(b, L, H, G, P, N, R, io, 1.0, seed=L + R)
+    f = _fusion(b, L, H, R, N, P, io, seed=7, parts=parts)
+    st = rand_state(b, H, G, N, P, R, io, seed=3)
+    y, so = m3scan.prefill_fused(*[d[k] for k in NAMES], Q, **f, state_in=st)
+    torch.cuda.synchronize()
+    yr, hr = _oracle(d, f, state_in=(np64(st.h), np64(st.b_last), np64(st.x_last)))
+    ey, eh = slice_err(np64(y), yr, 2), slice_err(np64(so.h), hr, 1)
+    say(f"  y {ey:.2e} h {eh:.2e}")
+    assert ey <= TOL[io] and eh <= TOL[io]
+    # the carry written is the raw last token
+    assert torch.equal(so.b_last, d["B"][:, -1]) and torch.equal(so.x_last, d["x"][:, -1])
+
+
+@pytest.mark.parametrize("R", [2, 4])
+def test_fused_prefill_then_fused_decode(R):
+    b, L, H, G, P, N, Q, steps = 2, 64, 4, 1, 64, 128, 32, 5
+    say("fused prefill + decode", R)
+    d = draw(b, L + steps, H, G, P, N, R, "bf16", 1.0, seed=40 + R)
+    f = _fusion(b, L + steps, H, R, N, P, "bf16", seed=9, parts=("A_t", "norm", "bias", "gate"))
+    cut = lambda t, s: t[:, s].contiguous() if t.dim() > 1 else t
+    pre = {k: cut(v, slice(0, L)) for k, v in d.items()}
+    fpre = {k: (cut(v, slice(0, L)) if k in ("A_t", "z") else v) for k, v in f.items()}
+    y, st = m3scan.prefill_fused(*[pre[k] for k in NAMES], Q, **fpre)
+    ys = [y]
+    for t in range(L, L + steps):
+        tok = {k: (v[:, t].contiguous() if v.dim() > 1 else v) for k, v in d.items()}
+        ft = {k: (v[:, t].contiguous() if k in ("A_t", "z") else v) for k, v in f.items()}
+        ys.append(m3scan.decode_step_fused(st, *[tok[k] for k in NAMES], **ft)[:, None])
+    torch.cuda.synchronize()
+    yr, hr = _oracle(d, f)
+    ey = slice_err(np64(torch.cat(ys, dim=1)), yr, 2)
+    eh = slice_err(np64(st.h), hr, 1)
+    say(f"  y {ey:.2e} h {eh:.2e}")
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+def test_fused_without_parts_is_the_plain_prefill():
+    """An empty fusion gives bit-identical results to m3_prefill_chunked."""
+    b, L, H, G, P, N, R, Q = 1, 80, 2, 1, 64, 128, 2, 32
+    d = draw(b, L, H, G, P, N, R, "bf16", 1.0, seed=5)
+    y0, s0 = m3scan.prefill(*[d[k] for k in NAMES], Q)
+    y1, s1 = m3scan.prefill_fused(*[d[k] for k in NAMES], Q)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(s0.h, s1.h)
