@@ -16,6 +16,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import math
 import json
 import os
 import sys
@@ -42,6 +43,9 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (m3_backward) of the workload's prefill instead "
                          "(default workload for it: c1, the nanomamba3 training shape)")
+    ap.add_argument("--fused", action="store_true",
+                    help="run the fused layer prologue/epilogue (m3_prefill_fused, m3_decode_step_fused): "
+                         "per-token A, RMSNorm and bias of B and C, output gate")
     ap.add_argument("--varlen", action="store_true",
                     help="pack the batch's sequences with seeded lengths uniform in [L/4, L] "
                          "(m3_prefill_varlen) instead of equal lengths L")
@@ -53,6 +57,15 @@ def parse():
     ap.add_argument("--probe-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (known bytes) to calibrate HBM counters")
     return ap.parse_args()
+
+
+def fused_extra_bytes(cfg, L, steps, tokens=None):
+    """Extra bytes of the fused prologue/epilogue: the gate input z (laid out as y) and the
+    per-token A, per (token, head), for the prefill and for one decode step."""
+    s = 2 if cfg.io_dtype == "bf16" else 4
+    tok = cfg.batch * L if tokens is None else tokens
+    per = cfg.nheads * (cfg.rank * cfg.headdim * s + 4)
+    return tok * per, (cfg.batch * per if steps else 0)
 
 
 def algorithmic_bytes(cfg, L, steps, state_bytes=4, tokens=None):
@@ -156,6 +169,23 @@ def main():
     else:
         y = torch.empty_like(d["x"])
     ydec = torch.empty((max(steps_dec, 1),) + tuple(d["x"][:, 0].shape), dtype=d["x"].dtype, device=dev)
+    fz = fzd = None
+    if args.fused:   # seeded fusion inputs: per-token A, norm weights and biases (R, N), gate z
+        if args.varlen:
+            print("--fused is measured on uniform batches only", file=sys.stderr)
+            sys.exit(2)
+        gf = torch.Generator(device=dev).manual_seed(cfg.seed + 23)
+        Rr, Nn = cfg.rank, cfg.dstate
+        fz = {"A_t": -torch.exp(torch.rand(d["dt"].shape, generator=gf, device=dev) * math.log(16.0)),
+              "b_norm_w": 1.0 + 0.3 * torch.randn((Rr, Nn), generator=gf, device=dev),
+              "c_norm_w": 1.0 + 0.3 * torch.randn((Rr, Nn), generator=gf, device=dev),
+              "b_bias": 0.02 + 0.05 * torch.randn((Rr, Nn), generator=gf, device=dev),
+              "c_bias": 0.02 + 0.05 * torch.randn((Rr, Nn), generator=gf, device=dev),
+              "z": torch.randn(d["x"].shape, generator=gf, device=dev).to(d["x"].dtype)}
+        if steps_dec:
+            fzd = {"A_t": -torch.exp(torch.rand((steps_dec,) + tuple(d["dt"][:, 0].shape), generator=gf, device=dev)
+                                     * math.log(16.0)),
+                   "z": torch.randn((steps_dec,) + tuple(d["x"][:, 0].shape), generator=gf, device=dev).to(d["x"].dtype)}
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
 
@@ -167,13 +197,22 @@ def main():
         if args.varlen:
             _, st = m3scan.prefill_varlen(dp["x"], dp["dt"], d["A"], dp["lam"], dp["theta"], dp["B"],
                                           dp["C"], d["D"], cu, L, cfg.chunk, y=y, state_dtype=state_dtype)
+        elif args.fused:
+            _, st = m3scan.prefill_fused(d["x"], d["dt"], d["A"], d["lam"], d["theta"], d["B"], d["C"], d["D"],
+                                         cfg.chunk, **fz, y=y, state_dtype=state_dtype)
         else:
             _, st = m3scan.prefill(d["x"], d["dt"], d["A"], d["lam"], d["theta"], d["B"], d["C"], d["D"],
                                    cfg.chunk, y=y, state_dtype=state_dtype)
         e1.record(stream)
         for t in range(steps_dec):
-            m3scan.decode_step(st, dd["x"][t], dd["dt"][t], d["A"], dd["lam"][t], dd["theta"][t],
-                               dd["B"][t], dd["C"][t], d["D"], y_t=ydec[t])
+            if args.fused:
+                m3scan.decode_step_fused(st, dd["x"][t], dd["dt"][t], d["A"], dd["lam"][t], dd["theta"][t],
+                                         dd["B"][t], dd["C"][t], d["D"], A_t=fzd["A_t"][t],
+                                         b_norm_w=fz["b_norm_w"], c_norm_w=fz["c_norm_w"], b_bias=fz["b_bias"],
+                                         c_bias=fz["c_bias"], z=fzd["z"][t], y_t=ydec[t])
+            else:
+                m3scan.decode_step(st, dd["x"][t], dd["dt"][t], d["A"], dd["lam"][t], dd["theta"][t],
+                                   dd["B"][t], dd["C"][t], d["D"], y_t=ydec[t])
         e2.record(stream)
         if record is not None:
             record.append((e0, e1, e2))
@@ -197,6 +236,10 @@ def main():
     tokens_dec = cfg.batch * steps_dec
     value = (tokens_pre + tokens_dec) / (step_ms / 1e3)
     pre_bytes, dec_bytes = algorithmic_bytes(cfg, L, steps_dec, state_bytes, tokens=tokens_pre)
+    if args.fused:
+        xp, xd = fused_extra_bytes(cfg, L, steps_dec, tokens=tokens_pre)
+        pre_bytes += xp
+        dec_bytes += xd
     pre_tps = tokens_pre / (pre_avg / 1e3)
     pre_gbs = pre_bytes / (pre_avg / 1e3) / 1e9
     dec_launch_ms = dec_avg / max(steps_dec, 1)
@@ -207,7 +250,7 @@ def main():
 
     # Dominant kernel: the one with the larger share of the step.
     if steps_dec and dec_avg >= pre_avg:
-        sfx = "" if args.state_dtype == "fp32" else "_bf16state"
+        sfx = ("" if args.state_dtype == "fp32" else "_bf16state") + ("_fused" if args.fused else "")
         traffic = pmc_traffic(f"decode_{args.workload}{sfx}_hbm_counters.json",
                               ["m3_decode.hip", "m3_common.h"], dec_bytes)
         roof = {"kernel": f"decode_fast<io bf16, state {args.state_dtype}, N128, P64, R4>", "bound": "hbm",
@@ -215,7 +258,8 @@ def main():
                 "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "alg_bytes_per_launch": dec_bytes, "avg_launch_us": round(dec_launch_ms * 1e3, 2)}
     else:
-        traffic = pmc_traffic(f"prefill_{args.workload}{'_varlen' if args.varlen else ''}_hbm_counters.json",
+        traffic = pmc_traffic(f"prefill_{args.workload}{'_varlen' if args.varlen else ''}"
+                              f"{'_fused' if args.fused else ''}_hbm_counters.json",
                               ["m3_prefill_mfma.hip", "m3_common.h"], pre_bytes)
         roof = {"kernel": "prefill (chunked scan)", "bound": "hbm",
                 "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -245,6 +289,12 @@ def main():
                 parts["theta"].append(f(dd["theta"][:, bi:bi + 1, g:g + 1].transpose(0, 1)))
                 parts["B"].append(f(dd["B"][:, bi:bi + 1, g:g + 1].transpose(0, 1)))
                 parts["C"].append(f(dd["C"][:, bi:bi + 1, g:g + 1].transpose(0, 1)))
+            if args.fused:
+                parts["A_t"] = [f(fz["A_t"][bi:bi + 1, :n, h:h + 1])]
+                parts["z"] = [f(fz["z"][bi:bi + 1, :n, h:h + 1])]
+                if with_decode and steps_dec:
+                    parts["A_t"].append(f(fzd["A_t"][:, bi:bi + 1, h:h + 1].transpose(0, 1)))
+                    parts["z"].append(f(fzd["z"][:, bi:bi + 1, h:h + 1].transpose(0, 1)))
             out = {k: np.concatenate(v, axis=1) for k, v in parts.items()}
             out["A"] = f(d["A"][h:h + 1])
             out["D"] = f(d["D"][h:h + 1])
@@ -262,7 +312,16 @@ def main():
                 if args.state_dtype == "bf16":   # state rounded after the prefill and every decode token
                     flags = np.zeros(n + steps_dec, bool)
                     flags[n - 1:] = True
-                yr, hr = oracle.scan(*[si[k] for k in order], round_after=flags)
+                if args.fused:
+                    args_o = [si[k] for k in order]
+                    args_o[2] = si["A_t"]
+                    yr, hr = oracle.scan_fused(*args_o, b_norm_w=fz["b_norm_w"].double().cpu().numpy(),
+                                               c_norm_w=fz["c_norm_w"].double().cpu().numpy(),
+                                               b_bias=fz["b_bias"].double().cpu().numpy(),
+                                               c_bias=fz["c_bias"].double().cpu().numpy(), z=si["z"],
+                                               round_after=flags)
+                else:
+                    yr, hr = oracle.scan(*[si[k] for k in order], round_after=flags)
                 if args.varlen:
                     yg = [y[int(starts[bi]):int(starts[bi + 1]), h:h + 1][None].double().cpu().numpy()]
                 else:
@@ -308,7 +367,8 @@ def main():
         "dtype": "bf16" if cfg.io_dtype == "bf16" else "fp32",
         "data": "synthetic (seeded torch generators on the GPU; distributions of the workload)",
         "config": {"workload": cfg.label + (f"; packed lengths uniform in [{max(L // 4, 1)}, {L}], "
-                                            f"{tokens_pre} tokens" if args.varlen else ""),
+                                            f"{tokens_pre} tokens" if args.varlen else "")
+                               + ("; fused per-token A, BCNorm and bias of B and C, output gate" if args.fused else ""),
                    "name": cfg.name, "batch": cfg.batch, "prefill_len": L,
                    "decode_steps": steps_dec, "heads": cfg.nheads, "groups": cfg.ngroups,
                    "headdim": cfg.headdim, "dstate": cfg.dstate, "rank": cfg.rank, "chunk": cfg.chunk,
