@@ -74,3 +74,55 @@ def test_decode_workload_sampled():
         ey, eh = _err(yg, yr), _err(f64(st.h[bi:bi + 1, h:h + 1]), hr)
         say(f"  slice b={bi} h={h}: y {ey:.2e} state {eh:.2e}")
         assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("name", ["c1", "c3"])
+def test_backward_workload_sampled(name):
+    """The backward at the full size of a training-shaped workload (c1 is the benchmark's
+    default for it): per-head gradients dx, ddt, dlambda of sampled (batch, head) slices
+    against the oracle's adjoint run on that slice alone (group-shared and batch-summed
+    gradients mix slices and are covered by the small-size tests)."""
+    cfg = CONFIGS[name]
+    say("backward workload", name)
+    d = inputs.draw_config(cfg, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(cfg.seed + 11)
+    dy = torch.randn(d["x"].shape, generator=g, device="cuda").to(d["x"].dtype)
+    gr = m3scan.backward(d["x"], d["dt"], d["A"], d["lam"], d["theta"], d["B"], d["C"], d["D"], dy,
+                         want_state_grads=False)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(cfg.seed + 1)
+    for bi, h in [(0, 0), (cfg.batch - 1, cfg.nheads - 1), (int(rng.integers(cfg.batch)), int(rng.integers(cfg.nheads)))]:
+        ref = oracle.scan_backward(*_slice(d, bi, h, cfg.ngroups, cfg.nheads), f64(dy[bi:bi + 1, :, h:h + 1]))
+        for k in ("dx", "ddt", "dlam"):
+            gv = f64(gr[k][bi:bi + 1, :, h:h + 1])
+            e = _err(gv, ref[k])
+            say(f"  ({bi},{h}) {k} {e:.2e}")
+            assert e <= 1e-3, (bi, h, k, e)
+
+
+def test_fused_prefill_workload_sampled():
+    """The fused prologue/epilogue at the full size of the 1.5B-scale SISO layer."""
+    cfg = CONFIGS["c2"]
+    say("fused workload c2")
+    d = inputs.draw_config(cfg, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(cfg.seed + 23)
+    R, N = cfg.rank, cfg.dstate
+    fz = {"A_t": -torch.exp(torch.rand(d["dt"].shape, generator=g, device="cuda") * np.log(16.0)),
+          "b_norm_w": 1.0 + 0.3 * torch.randn((R, N), generator=g, device="cuda"),
+          "c_norm_w": 1.0 + 0.3 * torch.randn((R, N), generator=g, device="cuda"),
+          "b_bias": 0.02 + 0.05 * torch.randn((R, N), generator=g, device="cuda"),
+          "c_bias": 0.02 + 0.05 * torch.randn((R, N), generator=g, device="cuda"),
+          "z": torch.randn(d["x"].shape, generator=g, device="cuda").to(d["x"].dtype)}
+    y, st = m3scan.prefill_fused(d["x"], d["dt"], d["A"], d["lam"], d["theta"], d["B"], d["C"], d["D"],
+                                 cfg.chunk, **fz)
+    torch.cuda.synchronize()
+    for bi, h in [(0, 0), (cfg.batch - 1, cfg.nheads - 1)]:
+        args = _slice(d, bi, h, cfg.ngroups, cfg.nheads)
+        args[2] = f64(fz["A_t"][bi:bi + 1, :, h:h + 1])
+        yr, hr = oracle.scan_fused(*args, b_norm_w=f64(fz["b_norm_w"]), c_norm_w=f64(fz["c_norm_w"]),
+                                   b_bias=f64(fz["b_bias"]), c_bias=f64(fz["c_bias"]),
+                                   z=f64(fz["z"][bi:bi + 1, :, h:h + 1]))
+        ey = _err(f64(y[bi:bi + 1, :, h:h + 1]), yr)
+        eh = _err(f64(st.h[bi:bi + 1, h:h + 1]), hr)
+        say(f"  ({bi},{h}) y {ey:.2e} h {eh:.2e}")
+        assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
