@@ -454,7 +454,10 @@ def run_backward(args, cfg):
     nbytes = backward_bytes(cfg, L)
     tflops = flops / (ms / 1e3) / 1e12
     traffic = pmc_traffic(f"backward_{args.workload}_hbm_counters.json", ["m3_backward.hip", "m3_common.h"], nbytes)
-    roof = {"kernel": f"bwd_scan<io {cfg.io_dtype}, R{cfg.rank}> + group sums", "bound": "alu",
+    parts, tpp = m3scan.backward_parts(dims)
+    passes = "local + combine + " if parts > 1 else ""
+    roof = {"kernel": f"{passes}bwd_scan<io {cfg.io_dtype}, R{cfg.rank}> + group sums "
+                      f"({parts} pieces of {tpp} tokens per (b, h))", "bound": "alu",
             "achieved": round(tflops, 3), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / FP32_VALU_PEAK_TFLOPS, 4), "traffic": traffic,
             "alg_flops_per_launch": flops, "alg_bytes_per_launch": nbytes,

@@ -233,10 +233,19 @@ typedef struct {
 
 /* Bytes of device workspace m3_backward needs for these dims (may be large: the
  * state of every (b, h) after every third token, N * P * 4 bytes each, plus,
- * when H > G, per-head copies of the group-shared gradients).
+ * when H > G, per-head copies of the group-shared gradients, plus, when the
+ * sequences are split (m3_backward_parts), two N * P states per piece).
  * Errors: M3_ERR_INVALID_ARG for bad dims or a NULL `bytes`;
  * M3_ERR_UNSUPPORTED for shapes m3_backward does not handle. */
 m3_status m3_backward_workspace_size(const m3_dims* dims, size_t* bytes);
+
+/* How m3_backward divides the work for these dims: each (b, h) sequence is cut
+ * into *parts pieces of *tokens_per_part tokens (the last may be shorter) that are
+ * processed side by side, after a pass that gives each piece the state and the
+ * adjoint it starts from; *parts is 1 (and *tokens_per_part the length) when the
+ * (b, h) pairs alone fill the GPU.  The choice depends on the dims only, so the
+ * rounding of the gradients does too.  Errors as m3_backward_workspace_size. */
+m3_status m3_backward_parts(const m3_dims* dims, int32_t* parts, int64_t* tokens_per_part);
 
 /*
  * Backward pass of the scan for training: the derivative of
@@ -250,7 +259,8 @@ m3_status m3_backward_workspace_size(const m3_dims* dims, size_t* bytes);
  *
  * Supported: dstate 128, headdim 64, rank 1, 2 or 4; io dtype fp32 or bf16;
  * state_in->h in dims->state_dtype.  dims->chunk is ignored.  All arithmetic
- * is fp32.  Results do not depend on scheduling (no atomics).
+ * is fp32, except the sums of dt*A and theta over the tokens of a piece of a
+ * split sequence (fp64).  Results do not depend on scheduling (no atomics).
  * state_in:  NULL or as for m3_prefill_chunked (h non-NULL; carry optional).
  * dy:        (batch, L, H, R, P) in the io dtype.
  * dh_out:    NULL (zero) or (batch, H, N, P) fp32.

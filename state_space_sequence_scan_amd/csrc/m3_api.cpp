@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int32_t kVersion = 104;  // 0.1.4: backward pass, fused prologue/epilogue
+constexpr int32_t kVersion = 105;  // 0.1.5: sequence-split backward
 constexpr size_t kMaxLds = 160 * 1024;
 
 bool dims_ok(const m3_dims* d, bool prefill) {
@@ -307,6 +307,18 @@ m3_status m3_backward_workspace_size(const m3_dims* dims, size_t* bytes) {
     return M3_OK;
 }
 
+m3_status m3_backward_parts(const m3_dims* dims, int32_t* parts, int64_t* tokens_per_part) {
+    if (!parts || !tokens_per_part || !dims_ok(dims, true)) return M3_ERR_INVALID_ARG;
+    const m3::BwdShape s = bwd_shape(dims);
+    if (!m3::backward_supported(s)) return M3_ERR_UNSUPPORTED;
+    int p = 1;
+    int64_t spp = 0;
+    m3::backward_parts(s, &p, &spp);
+    *parts = p;
+    *tokens_per_part = p > 1 ? spp * 3 : s.L;
+    return M3_OK;
+}
+
 m3_status m3_backward(const m3_dims* dims, const void* x, const float* dt, const float* A,
                       const float* lambda, const float* theta, const void* B, const void* C,
                       const float* D, const m3_state* state_in, const void* dy,
@@ -322,6 +334,7 @@ m3_status m3_backward(const m3_dims* dims, const void* x, const float* dt, const
     const m3::BwdShape s = bwd_shape(dims);
     if (!m3::backward_supported(s)) return M3_ERR_UNSUPPORTED;
     const m3::BwdLayout lay = m3::backward_layout(s);
+    if (s.batch * s.H * lay.parts > 0x7fffffffll) return M3_ERR_UNSUPPORTED;   // one workgroup per (b, h, part)
     if (lay.bytes > 0 && (!workspace || workspace_bytes < lay.bytes)) return M3_ERR_WORKSPACE;
     m3::BwdArgs a{};
     a.x = x;

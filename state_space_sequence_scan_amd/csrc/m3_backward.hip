@@ -17,7 +17,17 @@
 // segment by the whole workgroup in 16-byte units, so the per-token steps read
 // their operands from LDS, not from global memory.
 //
-// One workgroup per (batch, head), 512 threads; thread t owns state rows
+// Sequence split.  Both recurrences are linear: over a piece of the sequence the
+// state maps as h_end = e^{sum dt A} R(sum theta) h_start + (the piece's own end
+// state from a zero start), and the adjoint at the piece's first token is the
+// piece's own (from a zero cotangent) plus a decayed, counter-rotated copy of
+// the adjoint entering from the right.  When few (batch, head) pairs would leave
+// CUs idle, each sequence is cut into pieces of whole segments: a local pass
+// gives every piece its two own terms and its sums of dt A and theta (in fp64,
+// the angles reduced mod 2 pi), a combine pass chains them into the state and the
+// adjoint each piece starts from, and the gradient pass runs every piece at once.
+//
+// One workgroup per (batch, head) and piece, 512 threads; thread t owns state rows
 // 4 (t >> 4) .. +3 (two rotation pairs) and columns 4 (t & 15) .. +3, of h and of
 // the adjoint, in registers.  Sums over columns (dB, dC, dtheta) are taken
 // within the 16 lanes that share rows, by DPP lane exchanges; sums over rows
@@ -89,9 +99,14 @@ template <> struct lds4<bf16_t> {
     }
 };
 
-template <typename T, int R>
+// LOCAL: the first pass of a split sequence (see launch_backward): for one part, the
+// forward sweep from a zero state and the adjoint sweep from a zero cotangent, with
+// the part's sums of dt*A and of theta.  Otherwise the gradient pass over one part
+// (the whole sequence when it is not split).
+template <typename T, int R, bool LOCAL>
 __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
-    const int bh = blockIdx.x;
+    const int64_t BH = a.batch * a.H;
+    const int bh = static_cast<int>(blockIdx.x % BH), part = static_cast<int>(blockIdx.x / BH);
     const int b = bh / a.H, h = bh - b * a.H, g = h / (a.H / a.G);
     const int tid = threadIdx.x, cb = tid & 15, pb = tid >> 4, lane = tid & 63, wv = tid >> 6;
     const int r0 = 4 * pb, c0 = 4 * cb;   // state rows r0 .. r0+3 (two rotation pairs), columns c0 .. c0+3
@@ -99,6 +114,10 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
     const int H = a.H, G = a.G;
     const float Ah = a.A[h], Dh = a.D[h];
     const int64_t nseg = (L + KS - 1) / KS;
+    const int64_t s_lo = part * a.seg_per_part;
+    const int64_t s_hi = s_lo + a.seg_per_part < nseg ? s_lo + a.seg_per_part : nseg;   // segments of this part
+    const bool split = a.parts > 1;
+    const size_t pidx = static_cast<size_t>(bh) * a.parts + part;
     float* ck = a.ckpt + static_cast<size_t>(bh) * nseg * N * P;
     const bool carry = a.bl && a.xl;
     const T* x = static_cast<const T*>(a.x);
@@ -110,8 +129,8 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
     // group-shared gradients go to per-head rows when heads share a group
     const int gh = a.per_head ? h : g, GH = a.per_head ? H : G;
 
-    __shared__ __align__(16) float sH[KS][N * PS];              // states h_{t0-1} .. h_{t0+len-2}
-    __shared__ __align__(16) float sDX[2][NT / 64][R * P];       // per-wave dX sums, by token parity
+    __shared__ __align__(16) float sH[LOCAL ? 1 : KS][LOCAL ? 4 : N * PS];   // states h_{t0-1} .. h_{t0+len-2}
+    __shared__ __align__(16) float sDX[2][NT / 64][LOCAL ? 4 : R * P];       // per-wave dX sums, by token parity
     __shared__ float sSc[2][NT / 64][4];                         // per-wave dalpha, dbeta, dgamma, dD
     // inputs of tokens t0-1 .. t0+KS-1 (slot k holds token t0 - 1 + k)
     __shared__ __align__(16) T sB[KS + 1][R * N];
@@ -125,7 +144,7 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
 
     // Tokens t0-1 .. t0+len-1 into slots 0 .. len, in 16-byte units spread over the
     // workgroup; token -1 is the carried previous input (B and X only), or zeros.
-    auto stage = [&](int64_t t0, int len, bool with_cdy) {
+    auto stage = [&](int64_t t0, int len, bool with_cdy, bool with_bx = true) {
         constexpr int E = 16 / static_cast<int>(sizeof(T));
         constexpr int uB = R * N / E, uX = R * P / E, uT = (N / 2) / 4;
         constexpr int upt = 2 * uB + 2 * uX + uT;
@@ -138,8 +157,8 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
             if (w < uB) {
                 const int o = w * E;
                 dst = &sB[k][o];
-                if (t >= 0) v = *reinterpret_cast<const uint4*>(Bm + ((static_cast<int64_t>(b) * L + t) * G + g) * (R * N) + o);
-                else if (carry) v = *reinterpret_cast<const uint4*>(blp + (static_cast<int64_t>(b) * G + g) * (R * N) + o);
+                if (t >= 0 && with_bx) v = *reinterpret_cast<const uint4*>(Bm + ((static_cast<int64_t>(b) * L + t) * G + g) * (R * N) + o);
+                else if (carry && with_bx) v = *reinterpret_cast<const uint4*>(blp + (static_cast<int64_t>(b) * G + g) * (R * N) + o);
             } else if (w < 2 * uB) {
                 const int o = (w - uB) * E;
                 dst = &sC[k][o];
@@ -148,8 +167,8 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
             } else if (w < 2 * uB + uX) {
                 const int o = (w - 2 * uB) * E;
                 dst = &sX[k][o];
-                if (t >= 0) v = *reinterpret_cast<const uint4*>(x + ((static_cast<int64_t>(b) * L + t) * H + h) * (R * P) + o);
-                else if (carry) v = *reinterpret_cast<const uint4*>(xlp + (static_cast<int64_t>(b) * H + h) * (R * P) + o);
+                if (t >= 0 && with_bx) v = *reinterpret_cast<const uint4*>(x + ((static_cast<int64_t>(b) * L + t) * H + h) * (R * P) + o);
+                else if (carry && with_bx) v = *reinterpret_cast<const uint4*>(xlp + (static_cast<int64_t>(b) * H + h) * (R * P) + o);
             } else if (w < 2 * uB + 2 * uX) {
                 const int o = (w - 2 * uB - uX) * E;
                 dst = &sDY[k][o];
@@ -227,10 +246,82 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
                                 : 0.f;
     };
 
-    // ---- forward sweep: checkpoint after the last token of every segment
+    if constexpr (LOCAL) {
+        // ---- forward sweep of the part from a zero state (the token before the part
+        // still feeds its first update through U_{t-1})
+        float hs[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) hs[i][j] = 0.f;
+        double sum = 0.0;   // thread i < N/2: theta of pair i; thread N/2: dt * A (as the steps round it)
+        for (int64_t s = s_lo; s < s_hi; ++s) {
+            const int64_t t0 = s * KS;
+            const int len = static_cast<int>(L - t0 < KS ? L - t0 : KS);
+            __syncthreads();
+            stage(t0, len, false);
+            __syncthreads();
+            for (int j = 1; j <= len; ++j) fwd_step(j, hs);
+            if (tid < N / 2) {
+                for (int j = 1; j <= len; ++j) sum += static_cast<double>(sTh[j][tid]);
+            } else if (tid == N / 2) {
+                for (int j = 1; j <= len; ++j) sum += static_cast<double>(sDt[j] * Ah);
+            }
+        }
+        store_state(hs, a.hloc + pidx * N * P, P);
+        constexpr double kTwoPi = 6.283185307179586;
+        if (tid < N / 2) a.ang[pidx * (N / 2) + tid] = static_cast<float>(sum - kTwoPi * floor(sum / kTwoPi));
+        else if (tid == N / 2) a.dec[pidx] = sum;
+        // ---- adjoint sweep of the part from a zero cotangent: g_t = C_t dy_t^T + alpha_{t+1} q_{t+1},
+        // q_t = M_t^T g_t; the result is the part's share of q at its first token
+        float qs[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qs[i][j] = 0.f;
+        float an = 0.f;
+        for (int64_t s = s_hi - 1; s >= s_lo; --s) {
+            const int64_t t0 = s * KS;
+            const int len = static_cast<int>(L - t0 < KS ? L - t0 : KS);
+            __syncthreads();
+            stage(t0, len, true, false);
+            __syncthreads();
+            for (int j = len - 1; j >= 0; --j) {
+                const int k = j + 1;
+                float al, be, ga, sn[2], cs[2];
+                coeffs(k, &al, &be, &ga, sn, cs);
+                float Cv[R][4], dyv[R][4];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    lds4<T>::get(&sC[k][r * N + r0], Cv[r]);
+                    lds4<T>::get(&sDY[k][r * P + c0], dyv[r]);
+                }
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        float g0 = an * qs[2 * q][jj], g1 = an * qs[2 * q + 1][jj];
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            g0 += Cv[r][2 * q] * dyv[r][jj];
+                            g1 += Cv[r][2 * q + 1] * dyv[r][jj];
+                        }
+                        qs[2 * q][jj] = cs[q] * g0 + sn[q] * g1;
+                        qs[2 * q + 1][jj] = -sn[q] * g0 + cs[q] * g1;
+                    }
+                an = al;
+            }
+        }
+        store_state(qs, a.qloc + pidx * N * P, P);
+        return;
+    }
+
+    // ---- forward sweep: checkpoint after the last token of every segment.  A part
+    // after the first starts from the state the combine pass left for it.
     float hc[4][4];
-    initial_state(hc);
-    for (int64_t s = 0; s < nseg; ++s) {
+    if (split) load_state(hc, a.hloc + pidx * N * P, P);
+    else initial_state(hc);
+    for (int64_t s = s_lo; s < s_hi; ++s) {
         const int64_t t0 = s * KS;
         const int len = static_cast<int>(L - t0 < KS ? L - t0 : KS);
         __syncthreads();   // the previous segment's slots are read
@@ -242,17 +333,28 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
 
     // ---- reverse sweep.  q_{t+1}, alpha_{t+1}, beta_{t+1} belong to the token after; the
     // final-state cotangent enters as a token after the last one with alpha = 1, beta = 0 and
-    // no rotation.
+    // no rotation.  A part before the last starts from the q of the next part's first
+    // token (left by the combine pass) and that token's alpha and beta.
     float qn[4][4];
+    if (split) {
+        load_state(qn, a.qloc + pidx * N * P, P);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            qn[i][j] = a.dh_out ? a.dh_out[(static_cast<size_t>(bh) * N + r0 + i) * P + c0 + j] : 0.f;
+            for (int j = 0; j < 4; ++j)
+                qn[i][j] = a.dh_out ? a.dh_out[(static_cast<size_t>(bh) * N + r0 + i) * P + c0 + j] : 0.f;
+    }
     float an = 1.f, bn = 0.f;
+    if (s_hi < nseg) {
+        const int64_t tn = s_hi * KS;
+        const float dtv = a.dt[soff(tn)], lv = a.lam[soff(tn)];
+        an = __expf(dtv * Ah);
+        bn = (1.f - lv) * dtv * an;
+    }
     float dA_acc = 0.f, dD_acc = 0.f;   // thread 0
 
-    for (int64_t s = nseg - 1; s >= 0; --s) {
+    for (int64_t s = s_hi - 1; s >= s_lo; --s) {
         const int64_t t0 = s * KS;
         const int len = static_cast<int>(L - t0 < KS ? L - t0 : KS);
         __syncthreads();   // the previous segment's readers are done with sH and the slots
@@ -260,7 +362,9 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
         __syncthreads();
         {   // recompute h_{t0-1} .. h_{t0+len-2} into LDS
             float hr[4][4];
-            if (s == 0) initial_state(hr); else load_state(hr, ck + (s - 1) * N * P, P);
+            if (s > s_lo) load_state(hr, ck + (s - 1) * N * P, P);
+            else if (split) load_state(hr, a.hloc + pidx * N * P, P);
+            else initial_state(hr);
             store_state(hr, sH[0], PS);
             for (int j = 1; j < len; ++j) {
                 fwd_step(j, hr);
@@ -431,14 +535,16 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
         }
     }
 
-    // ---- h_0 and the carried previous input (dU_0 = beta_1 q_1)
-    if (a.dh0) {
+    // ---- h_0 and the carried previous input (dU_0 = beta_1 q_1): the first part only
+    if (part == 0 && a.dh0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) a.dh0[(static_cast<size_t>(bh) * N + r0 + i) * P + c0 + j] = an * qn[i][j];
     }
-    if (carry && (a.dbl || a.dxl)) {
+    if (part != 0) {
+        // nothing before this part
+    } else if (carry && (a.dbl || a.dxl)) {
         float Bv[R][4], Xv[R][4], dB[R][4], dX[R][4];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -489,8 +595,92 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
         for (int o = tid; o < R * P; o += NT) a.dxl[static_cast<size_t>(bh) * R * P + o] = 0.f;
     }
     if (tid == 0) {
-        a.dA_part[bh] = dA_acc;
-        a.dD_part[bh] = dD_acc;
+        a.dA_part[pidx] = dA_acc;
+        a.dD_part[pidx] = dD_acc;
+    }
+}
+
+// Combine pass of a split sequence, one workgroup per (b, h), same element ownership as
+// bwd_scan.  The state after part p is e^{dec_p} R(ang_p) (state before it) plus the
+// part's local end state; the q at the first token of part p is the part's local q plus
+// (product of alpha over tokens T_p+1 .. T_{p+1}) R(-ang_p) (q at T_{p+1}), where the
+// alpha after the last token is 1 and the final-state cotangent is the q there.  Each
+// part's slots of hloc and qloc are overwritten with what it starts from: the state
+// before its first token and the q of the token after its last.
+__global__ __launch_bounds__(NT) void bwd_combine(BwdArgs a) {
+    const int bh = blockIdx.x;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int tid = threadIdx.x, cb = tid & 15, pb = tid >> 4;
+    const int r0 = 4 * pb, c0 = 4 * cb;
+    const int S = a.parts;
+    const float Ah = a.A[h];
+    const int64_t tok_per_part = a.seg_per_part * KS;
+    auto slot = [&](float* base, int p) { return base + ((static_cast<size_t>(bh) * S + p) * N + r0) * P + c0; };
+    auto ld16 = [&](const float* p, float (&v)[4][4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 u = *reinterpret_cast<const float4*>(p + i * P);
+            v[i][0] = u.x; v[i][1] = u.y; v[i][2] = u.z; v[i][3] = u.w;
+        }
+    };
+    auto st16 = [&](float* p, const float (&v)[4][4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<float4*>(p + i * P) = float4{v[i][0], v[i][1], v[i][2], v[i][3]};
+    };
+
+    float st[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            st[i][j] = a.h0 ? state_load(a.h0, (static_cast<size_t>(bh) * N + r0 + i) * P + c0 + j, a.state_bf16) : 0.f;
+    for (int p = 0; p < S; ++p) {
+        float* sp = slot(a.hloc, p);
+        float hl[4][4];
+        ld16(sp, hl);
+        st16(sp, st);
+        if (p + 1 == S) break;
+        const float d = static_cast<float>(exp(a.dec[static_cast<size_t>(bh) * S + p]));
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            float sn, cs;
+            sincos_acc(a.ang[(static_cast<size_t>(bh) * S + p) * (N / 2) + 2 * pb + q], &sn, &cs);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float v0 = st[2 * q][j], v1 = st[2 * q + 1][j];
+                st[2 * q][j] = d * (cs * v0 - sn * v1) + hl[2 * q][j];
+                st[2 * q + 1][j] = d * (sn * v0 + cs * v1) + hl[2 * q + 1][j];
+            }
+        }
+    }
+
+    float qs[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            qs[i][j] = a.dh_out ? a.dh_out[(static_cast<size_t>(bh) * N + r0 + i) * P + c0 + j] : 0.f;
+    for (int p = S - 1; p >= 0; --p) {
+        float* sp = slot(a.qloc, p);
+        float ql[4][4];
+        ld16(sp, ql);
+        st16(sp, qs);
+        if (p == 0) break;
+        const int64_t tp = p * tok_per_part;   // first token of part p
+        double lq = a.dec[static_cast<size_t>(bh) * S + p] - static_cast<double>(a.dt[(static_cast<int64_t>(b) * a.L + tp) * a.H + h] * Ah);
+        if (p + 1 < S) lq += static_cast<double>(a.dt[(static_cast<int64_t>(b) * a.L + tp + tok_per_part) * a.H + h] * Ah);
+        const float d = static_cast<float>(exp(lq));
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            float sn, cs;
+            sincos_acc(a.ang[(static_cast<size_t>(bh) * S + p) * (N / 2) + 2 * pb + q], &sn, &cs);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float g0 = qs[2 * q][j], g1 = qs[2 * q + 1][j];
+                qs[2 * q][j] = ql[2 * q][j] + d * (cs * g0 + sn * g1);
+                qs[2 * q + 1][j] = ql[2 * q + 1][j] + d * (-sn * g0 + cs * g1);
+            }
+        }
     }
 }
 
@@ -512,14 +702,16 @@ __global__ __launch_bounds__(256) void bwd_fill_zero(float* __restrict__ p, int6
 }
 
 __global__ __launch_bounds__(256) void bwd_head_sum(const float* __restrict__ dA_part, const float* __restrict__ dD_part,
-                                                    float* __restrict__ dA, float* __restrict__ dD, int batch, int H) {
+                                                    float* __restrict__ dA, float* __restrict__ dD, int batch, int H,
+                                                    int parts) {
     const int h = blockIdx.x * 256 + threadIdx.x;
     if (h >= H) return;
     float sa = 0.f, sd = 0.f;
-    for (int b = 0; b < batch; ++b) {   // fixed order
-        sa += dA_part[b * H + h];
-        sd += dD_part[b * H + h];
-    }
+    for (int b = 0; b < batch; ++b)   // fixed order
+        for (int p = 0; p < parts; ++p) {
+            sa += dA_part[(static_cast<size_t>(b) * H + h) * parts + p];
+            sd += dD_part[(static_cast<size_t>(b) * H + h) * parts + p];
+        }
     dA[h] = sa;
     dD[h] = sd;
 }
@@ -530,12 +722,45 @@ bool backward_supported(const BwdShape& s) {
     return s.N == bw::N && s.P == bw::P && (s.R == 1 || s.R == 2 || s.R == 4);
 }
 
+// One workgroup per (b, h) and part, one workgroup per CU (its LDS and registers
+// allow no second).  With few (b, h) most CUs would idle, so the sequence is split
+// into S parts of whole segments when that shortens the run: the cost model counts
+// rounds of workgroups over the CUs times the segments of a part, and charges
+// the split its local and combine passes (about a third of the gradient pass).
+// The CU count is MI355X's, fixed, so that the split (and with it the rounding of
+// the results) depends on the shape alone.
+void backward_parts(const BwdShape& s, int* parts, int64_t* seg_per_part) {
+    constexpr int64_t kCUs = 256;
+    constexpr double kSplitCost = 1.3;
+    const int64_t nseg = (s.L + bw::KS - 1) / bw::KS;
+    const int64_t bh = s.batch * s.H;
+    auto rounds = [&](int64_t wgs) { return (wgs + kCUs - 1) / kCUs; };
+    int best_s = 1;
+    int64_t best_per = nseg;
+    double best = static_cast<double>(rounds(bh)) * static_cast<double>(nseg);
+    for (int64_t S = 2; S <= 64 && S <= nseg; ++S) {
+        const int64_t per = (nseg + S - 1) / S;
+        const int64_t used = (nseg + per - 1) / per;   // every part holds at least one segment
+        const double cost = kSplitCost * static_cast<double>(rounds(bh * used)) * static_cast<double>(per);
+        if (cost < 0.95 * best) {
+            best = cost;
+            best_s = static_cast<int>(used);
+            best_per = per;
+        }
+    }
+    *parts = best_s;
+    *seg_per_part = best_per;
+}
+
 // Workspace: checkpoints (batch, H, nseg, N, P) fp32; per-head partials of the
-// group-shared gradients when H > G; dA/dD per (batch, head).
+// group-shared gradients when H > G; dA/dD per (batch, head, part); with a split,
+// each part's local state and adjoint (N, P) and its decay and angle sums.
 BwdLayout backward_layout(const BwdShape& s) {
     BwdLayout l{};
     auto al = [](size_t v) { return (v + 255) & ~static_cast<size_t>(255); };
     const int64_t nseg = (s.L + bw::KS - 1) / bw::KS;
+    backward_parts(s, &l.parts, &l.seg_per_part);
+    const size_t units = static_cast<size_t>(s.batch) * s.H * l.parts;
     size_t off = 0;
     l.ckpt = off;
     off += al(static_cast<size_t>(s.batch) * s.H * nseg * s.N * s.P * 4);
@@ -551,12 +776,37 @@ BwdLayout backward_layout(const BwdShape& s) {
         off += al(static_cast<size_t>(s.batch) * s.H * s.R * s.N * 4);
     }
     l.dA_part = off;
-    off += al(static_cast<size_t>(s.batch) * s.H * 4);
+    off += al(units * 4);
     l.dD_part = off;
-    off += al(static_cast<size_t>(s.batch) * s.H * 4);
+    off += al(units * 4);
+    if (l.parts > 1) {
+        l.hloc = off;
+        off += al(units * s.N * s.P * 4);
+        l.qloc = off;
+        off += al(units * s.N * s.P * 4);
+        l.dec = off;
+        off += al(units * 8);
+        l.ang = off;
+        off += al(units * (s.N / 2) * 4);
+    }
     l.bytes = off;
     return l;
 }
+
+namespace {
+template <bool LOCAL>
+void launch_scan(const BwdArgs& a, dim3 grid, hipStream_t st) {
+    if (a.bf16) {
+        if (a.R == 1) bw::bwd_scan<bf16_t, 1, LOCAL><<<grid, bw::NT, 0, st>>>(a);
+        if (a.R == 2) bw::bwd_scan<bf16_t, 2, LOCAL><<<grid, bw::NT, 0, st>>>(a);
+        if (a.R == 4) bw::bwd_scan<bf16_t, 4, LOCAL><<<grid, bw::NT, 0, st>>>(a);
+    } else {
+        if (a.R == 1) bw::bwd_scan<float, 1, LOCAL><<<grid, bw::NT, 0, st>>>(a);
+        if (a.R == 2) bw::bwd_scan<float, 2, LOCAL><<<grid, bw::NT, 0, st>>>(a);
+        if (a.R == 4) bw::bwd_scan<float, 4, LOCAL><<<grid, bw::NT, 0, st>>>(a);
+    }
+}
+}  // namespace
 
 hipError_t launch_backward(BwdArgs a, const BwdLayout& l, hipStream_t st) {
     uint8_t* ws = static_cast<uint8_t*>(a.workspace);
@@ -570,16 +820,20 @@ hipError_t launch_backward(BwdArgs a, const BwdLayout& l, hipStream_t st) {
     }
     a.dA_part = reinterpret_cast<float*>(ws + l.dA_part);
     a.dD_part = reinterpret_cast<float*>(ws + l.dD_part);
-    const dim3 grid(static_cast<unsigned>(a.batch * a.H));
-    if (a.bf16) {
-        if (a.R == 1) bw::bwd_scan<bf16_t, 1><<<grid, bw::NT, 0, st>>>(a);
-        if (a.R == 2) bw::bwd_scan<bf16_t, 2><<<grid, bw::NT, 0, st>>>(a);
-        if (a.R == 4) bw::bwd_scan<bf16_t, 4><<<grid, bw::NT, 0, st>>>(a);
-    } else {
-        if (a.R == 1) bw::bwd_scan<float, 1><<<grid, bw::NT, 0, st>>>(a);
-        if (a.R == 2) bw::bwd_scan<float, 2><<<grid, bw::NT, 0, st>>>(a);
-        if (a.R == 4) bw::bwd_scan<float, 4><<<grid, bw::NT, 0, st>>>(a);
+    a.parts = l.parts;
+    a.seg_per_part = l.seg_per_part;
+    if (l.parts > 1) {
+        a.hloc = reinterpret_cast<float*>(ws + l.hloc);
+        a.qloc = reinterpret_cast<float*>(ws + l.qloc);
+        a.dec = reinterpret_cast<double*>(ws + l.dec);
+        a.ang = reinterpret_cast<float*>(ws + l.ang);
     }
+    const dim3 grid(static_cast<unsigned>(a.batch * a.H * l.parts));
+    if (l.parts > 1) {   // local pass of every part, then the combine over parts
+        launch_scan<true>(a, grid, st);
+        bw::bwd_combine<<<static_cast<unsigned>(a.batch * a.H), bw::NT, 0, st>>>(a);
+    }
+    launch_scan<false>(a, grid, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (l.per_head) {
@@ -602,7 +856,8 @@ hipError_t launch_backward(BwdArgs a, const BwdLayout& l, hipStream_t st) {
         const int64_t n = a.batch * a.G * a.R * a.N;
         bw::bwd_fill_zero<<<static_cast<unsigned>(n / 256 + 1 < 4096 ? n / 256 + 1 : 4096), 256, 0, st>>>(a.dbl, n);
     }
-    bw::bwd_head_sum<<<(a.H + 255) / 256, 256, 0, st>>>(a.dA_part, a.dD_part, a.dA, a.dD, static_cast<int>(a.batch), a.H);
+    bw::bwd_head_sum<<<(a.H + 255) / 256, 256, 0, st>>>(a.dA_part, a.dD_part, a.dA, a.dD, static_cast<int>(a.batch), a.H,
+                                                      l.parts);
     return hipGetLastError();
 }
 

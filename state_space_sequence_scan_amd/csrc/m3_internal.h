@@ -106,9 +106,14 @@ struct BwdShape {
     int H, G, N, P, R;
 };
 struct BwdLayout {            // byte offsets into the workspace
-    size_t ckpt, dB_part, dC_part, dtheta_part, dbl_part, dA_part, dD_part, bytes;
+    size_t ckpt, dB_part, dC_part, dtheta_part, dbl_part, dA_part, dD_part, hloc, qloc, dec, ang, bytes;
     bool per_head;            // H > G: group-shared gradients are written per head, then summed
+    int parts;                // S: the sequence of each (b, h) is split into S parts (1: no split)
+    int64_t seg_per_part;     // recompute segments per part (the last part may hold fewer)
 };
+// Number of parts the backward splits each sequence into, and the segments of
+// each part: chosen from the shape alone so that results depend on nothing else.
+void backward_parts(const BwdShape& s, int* parts, int64_t* seg_per_part);
 struct BwdArgs {
     const void* x;
     const float* dt;
@@ -143,8 +148,14 @@ struct BwdArgs {
     float* dbl_part;
     float* dA_part;
     float* dD_part;
+    float* hloc;              // (batch*H, S, N, P): local end state of each part, then its entering state
+    float* qloc;              // (batch*H, S, N, P): local adjoint at each part's start, then the entering one
+    double* dec;              // (batch*H, S): sum of dt*A over each part's tokens
+    float* ang;               // (batch*H, S, N/2): sum of theta over each part's tokens, mod 2 pi
+    int64_t seg_per_part;
     int64_t batch, L;
     int H, G, N, P, R;
+    int parts;
     bool per_head;
     bool bf16;
     bool state_bf16;

@@ -87,6 +87,9 @@ def lib(path: str = LIB_PATH):
     L.m3_decode_step_fused.argtypes = [ctypes.POINTER(Dims)] + [vp] * 11 + [ctypes.POINTER(Fusion), vp, vp]
     L.m3_backward_workspace_size.restype = ctypes.c_int
     L.m3_backward_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(sz)]
+    L.m3_backward_parts.restype = ctypes.c_int
+    L.m3_backward_parts.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(ctypes.c_int32),
+                                    ctypes.POINTER(ctypes.c_int64)]
     L.m3_backward.restype = ctypes.c_int
     L.m3_backward.argtypes = ([ctypes.POINTER(Dims)] + [vp] * 8 + [ctypes.POINTER(State), vp, vp,
                               ctypes.POINTER(Grads), vp, sz, vp])
@@ -304,6 +307,16 @@ def backward_workspace_size(dims: Dims) -> int:
     if rc != 0:
         raise M3Error("m3_backward_workspace_size", rc)
     return int(n.value)
+
+
+def backward_parts(dims: Dims):
+    """(parts, tokens_per_part): how m3_backward splits each (b, h) sequence."""
+    n = ctypes.c_int32(0)
+    t = ctypes.c_int64(0)
+    rc = lib().m3_backward_parts(ctypes.byref(dims), ctypes.byref(n), ctypes.byref(t))
+    if rc != 0:
+        raise M3Error("m3_backward_parts", rc)
+    return int(n.value), int(t.value)
 
 
 def backward(x, dt, A, lam, theta, B, C, D, dy, dh_out=None, state_in: Optional[DecodeState] = None,

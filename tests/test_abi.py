@@ -28,7 +28,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_symbols() == ["m3_backward", "m3_backward_workspace_size", "m3_decode_step",
+    assert declared_symbols() == ["m3_backward", "m3_backward_parts", "m3_backward_workspace_size",
+                                  "m3_decode_step",
                                   "m3_decode_step_fused", "m3_prefill_chunked", "m3_prefill_fused",
                                   "m3_prefill_varlen", "m3_prefill_workspace_size", "m3_status_string",
                                   "m3_version"]
@@ -226,3 +227,33 @@ def test_fused_entry_points_reject_bad_arguments(lib):
     # the workspace reserves room for the normalised carry: none given is too small
     assert lib.m3_prefill_fused(ctypes.byref(d), *[FAKE] * 8, ctypes.byref(fu), None, None, FAKE, None, 0,
                                 None) == -3
+
+
+def test_backward_parts(lib):
+    """The split of the backward is a function of the dims: none when the (b, h)
+    pairs fill the CUs or the sequence is a single segment, otherwise pieces of
+    whole 3-token segments that cover the sequence, every piece non-empty; the
+    workspace grows by the pieces' states."""
+    P, N = 64, 128
+    nb = ctypes.c_size_t(0)
+    # 256 (b, h) pairs: no split
+    d = _dims(batch=8, nheads=32, ngroups=8, headdim=P, dstate=N, rank=1, seqlen=40)
+    assert m3scan.backward_parts(d) == (1, 40)
+    # a single segment
+    for L in (0, 1, 3):
+        assert m3scan.backward_parts(_dims(batch=1, nheads=2, headdim=P, dstate=N, seqlen=L)) == (1, L)
+    # few pairs: split
+    for b, H, L in [(4, 24, 2048), (2, 64, 16384), (4, 24, 200), (2, 4, 37), (1, 1, 100000)]:
+        d = _dims(batch=b, nheads=H, ngroups=1, headdim=P, dstate=N, rank=2, seqlen=L)
+        parts, tpp = m3scan.backward_parts(d)
+        assert parts > 1 and tpp % 3 == 0, (b, H, L)
+        assert (parts - 1) * tpp < L <= parts * tpp, (b, H, L, parts, tpp)
+        assert lib.m3_backward_workspace_size(ctypes.byref(d), ctypes.byref(nb)) == 0
+        assert nb.value >= 2 * b * H * parts * N * P * 4
+    n32, n64 = ctypes.c_int32(0), ctypes.c_int64(0)
+    good = _dims(headdim=P, dstate=N)
+    assert lib.m3_backward_parts(ctypes.byref(good), None, ctypes.byref(n64)) == -1
+    assert lib.m3_backward_parts(ctypes.byref(good), ctypes.byref(n32), None) == -1
+    assert lib.m3_backward_parts(ctypes.byref(_dims(batch=0, headdim=P, dstate=N)), ctypes.byref(n32),
+                                 ctypes.byref(n64)) == -1
+    assert lib.m3_backward_parts(ctypes.byref(_dims()), ctypes.byref(n32), ctypes.byref(n64)) == -2

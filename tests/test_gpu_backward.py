@@ -69,6 +69,12 @@ CASES = [
     (1, 64, 4, 1, 4, "fp32", False, True),
     (1, 3, 2, 2, 4, "bf16", True, True),
     (1, 1, 2, 1, 2, "bf16", True, True),
+    # split sequences (m3_backward_parts > 1): pieces of two segments, the last one a
+    # single 2-token segment; and a split with a carried state and final cotangent
+    (4, 200, 24, 1, 2, "bf16", False, True),
+    (2, 150, 4, 2, 4, "fp32", True, True),
+    # 256 (b, h) pairs: no split
+    (8, 40, 32, 8, 1, "bf16", True, False),
 ]
 
 
@@ -79,7 +85,7 @@ def _id(c):
 @pytest.mark.parametrize("case", CASES, ids=_id)
 def test_backward_matches_oracle(case):
     b, L, H, G, R, io, ws, wd = case
-    say("backward", _id(case))
+    say("backward", _id(case), "pieces", m3scan.backward_parts(m3scan.make_dims(b, L, H, G, 64, 128, R, 1, 0)))
     errs = _run_case(b, L, H, G, R, io, seed=L * 7 + R, with_state=ws, with_dh=wd)
     say("  " + " ".join(f"{k} {v:.1e}" for k, v in errs.items()))
     bad = {k: v for k, v in errs.items() if not v <= TOL_BWD}
@@ -110,3 +116,13 @@ def test_backward_is_deterministic():
     torch.cuda.synchronize()
     for k in g1:
         assert torch.equal(g1[k], g2[k]), k
+
+
+def test_cases_cover_split_and_whole_sequences():
+    """The cases above run both the split path (several pieces, some of several
+    segments) and the whole-sequence path beyond a single segment."""
+    plans = [(c, m3scan.backward_parts(m3scan.make_dims(c[0], c[1], c[2], c[3], 64, 128, c[4], 1, 0)))
+             for c in CASES]
+    assert any(p > 1 and t > 3 for _, (p, t) in plans)
+    assert any(p > 1 and c[6] for c, (p, t) in plans)
+    assert any(p == 1 and c[1] > 3 for c, (p, t) in plans)
