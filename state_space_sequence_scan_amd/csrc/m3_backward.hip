@@ -138,6 +138,7 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
     __shared__ __align__(16) T sX[KS + 1][R * P];
     __shared__ __align__(16) T sDY[KS + 1][R * P];
     __shared__ __align__(16) float sTh[KS + 1][N / 2];
+    __shared__ __align__(16) float sRot[KS + 1][N];             // cos, sin of each pair's angle
     __shared__ float sDt[KS + 1], sLam[KS + 1];
 
     auto soff = [&](int64_t t) { return (static_cast<int64_t>(b) * L + t) * H + h; };
@@ -178,6 +179,13 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
                 const int o = (w - 2 * uB - 2 * uX) * 4;
                 dst = &sTh[k][o];
                 if (t >= 0) v = *reinterpret_cast<const uint4*>(a.theta + ((static_cast<int64_t>(b) * L + t) * G + g) * (N / 2) + o);
+                // the rotation of these four pairs, once per token for the whole workgroup
+                const float th[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+                float cs4[4], sn4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sincos_acc(th[e], &sn4[e], &cs4[e]);
+                *reinterpret_cast<float4*>(&sRot[k][2 * o]) = float4{cs4[0], sn4[0], cs4[1], sn4[1]};
+                *reinterpret_cast<float4*>(&sRot[k][2 * o + 4]) = float4{cs4[2], sn4[2], cs4[3], sn4[3]};
             }
             *reinterpret_cast<uint4*>(dst) = v;
         }
@@ -205,8 +213,11 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
         *al = __expf(dtv * Ah);
         *be = (1.f - lv) * dtv * *al;
         *ga = lv * dtv;
-        sincos_acc(sTh[k][2 * pb], &sn[0], &cs[0]);
-        sincos_acc(sTh[k][2 * pb + 1], &sn[1], &cs[1]);
+        const float4 rot = *reinterpret_cast<const float4*>(&sRot[k][4 * pb]);   // pairs 2pb, 2pb+1
+        cs[0] = rot.x;
+        sn[0] = rot.y;
+        cs[1] = rot.z;
+        sn[1] = rot.w;
     };
     // one forward step on hs for the token in slot k: h <- M (alpha h + beta U_{t-1}) + gamma U_t
     auto fwd_step = [&](int k, float (&hs)[4][4]) {
