@@ -88,6 +88,15 @@ __device__ __forceinline__ s16x4 lds_tr4(uint32_t a) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(static_cast<uintptr_t>(a)));
 }
 
+// Global-memory view of a pointer chosen at run time (a select between two
+// pointers hides their address space from the compiler).  Loads through it are
+// global loads; a generic (flat) load would also count as a possible LDS access
+// and make every LDS wait of the loop a full drain.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* global_view(const T* p) {
+    return (const __attribute__((address_space(1))) T*)(p);
+}
+
 __device__ __forceinline__ f32x4 mfma_k32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -479,7 +488,7 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
             pl0 = lmc[static_cast<uint32_t>(i0 * p.H)];                                                       \
             pd1 = dtc[static_cast<uint32_t>(i1 * p.H)];                                                       \
             pl1 = lmc[static_cast<uint32_t>(i1 * p.H)];                                                       \
-            pa0 = (p.At ? p.At : p.dt)[(tb + t0f) * p.H + h + static_cast<uint32_t>(i0 * p.H)];              \
+            pa0 = global_view(p.At ? p.At : p.dt)[(tb + t0f) * p.H + h + static_cast<uint32_t>(i0 * p.H)];  \
         }                                                                                                     \
     } while (0)
 
