@@ -63,6 +63,7 @@ PrefillPlan plan_prefill(const PrefillArgs& a) {
         return p;
     }
     if (a.R > kMaxRankGeneric) return p;
+    if (a.batch * a.H >= (int64_t{1} << 24)) return p;   // 256-thread workgroups per (b, h): under 2^32 work-items
     const size_t lds = generic_lds_bytes(a);
     if (lds <= kMaxLds) {
         p.path = PrefillPath::Generic;
@@ -259,7 +260,8 @@ m3_status decode_common(const m3_dims* dims, void* h, const void* b_last, const 
         a.fu.eps = fu->norm_eps;
         if ((a.fu.bnw || a.fu.cnw) && !(fu->norm_eps > 0.f)) return M3_ERR_INVALID_ARG;
     }
-    if (dims->batch * dims->nheads > 0x7fffffffLL) return M3_ERR_UNSUPPORTED;
+    // one workgroup of at most 256 threads per (b, h): under 2^32 work-items per launch
+    if (dims->batch * dims->nheads >= (int64_t{1} << 24)) return M3_ERR_UNSUPPORTED;
     if (!m3::decode_supported(a)) return M3_ERR_UNSUPPORTED;
     const hipError_t e = m3::launch_decode(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? M3_OK : M3_ERR_HIP;
@@ -334,7 +336,8 @@ m3_status m3_backward(const m3_dims* dims, const void* x, const float* dt, const
     const m3::BwdShape s = bwd_shape(dims);
     if (!m3::backward_supported(s)) return M3_ERR_UNSUPPORTED;
     const m3::BwdLayout lay = m3::backward_layout(s);
-    if (s.batch * s.H * lay.parts > 0x7fffffffll) return M3_ERR_UNSUPPORTED;   // one workgroup per (b, h, part)
+    // one workgroup of 512 threads per (b, h, part): under 2^32 work-items per launch
+    if (s.batch * s.H * lay.parts >= (int64_t{1} << 23)) return M3_ERR_UNSUPPORTED;
     if (lay.bytes > 0 && (!workspace || workspace_bytes < lay.bytes)) return M3_ERR_WORKSPACE;
     m3::BwdArgs a{};
     a.x = x;

@@ -1035,8 +1035,15 @@ __global__ __launch_bounds__(NT) void seg_pass(ScanParams p, float* __restrict__
 bool mfma_supported(const PrefillArgs& a) {
     // per-lane offsets within one chunk of x and y are 32-bit
     const bool offsets_fit = static_cast<int64_t>(a.H) * a.R * a.P * a.Q < (int64_t{1} << 31);
+    // Every launch stays under 2^32 work-items and rope_prep's grid is (chunks, G, batch);
+    // larger shapes take the generic path.  The scan launches at most max(batch * H, 1023)
+    // workgroups of at most 512 threads (segments are added only while batch * H < 512).
+    const int64_t nchunks = (a.L + a.Q - 1) / a.Q;
+    const bool grid_fits = a.batch <= 65535 && a.G <= 65535 &&
+                           nchunks * a.G * a.batch * mf::NT < (int64_t{1} << 32) &&
+                           a.batch * a.H < (int64_t{1} << 23);
     return a.bf16 && a.N == mf::N && a.P == mf::P && (a.R == 1 || a.R == 2 || a.R == 4) &&
-           (a.Q == 32 || a.Q == 64) && offsets_fit;
+           (a.Q == 32 || a.Q == 64) && offsets_fit && grid_fits;
 }
 
 static int choose_nseg(const PrefillArgs& a, int nchunks) {

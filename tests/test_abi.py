@@ -257,3 +257,26 @@ def test_backward_parts(lib):
     assert lib.m3_backward_parts(ctypes.byref(_dims(batch=0, headdim=P, dstate=N)), ctypes.byref(n32),
                                  ctypes.byref(n64)) == -1
     assert lib.m3_backward_parts(ctypes.byref(_dims()), ctypes.byref(n32), ctypes.byref(n64)) == -2
+
+
+def test_launch_size_limits(lib):
+    """Shapes whose launches would exceed 2^32 work-items are refused before anything
+    is launched (M3_ERR_UNSUPPORTED), and a batch too large for the matrix-core
+    prefill's grid falls back to the generic path while that one fits."""
+    P, N = 64, 128
+    n = ctypes.c_size_t(0)
+    # decode: one workgroup per (b, h)
+    d = _dims(batch=1 << 18, nheads=64, ngroups=1, headdim=P, dstate=N, rank=4, io_dtype=m3scan.M3_BF16)
+    args = [FAKE] * 12
+    assert lib.m3_decode_step(ctypes.byref(d), *args, None) == -2
+    # prefill: 2^24 (b, h) pairs fit neither path
+    assert lib.m3_prefill_workspace_size(ctypes.byref(_dims(batch=1 << 18, nheads=64, ngroups=1, headdim=P,
+                                                            dstate=N, rank=1, chunk=64, seqlen=64,
+                                                            io_dtype=m3scan.M3_BF16)), ctypes.byref(n)) == -2
+    # 70000 sequences of one head: past the matrix-core grid, still the generic path
+    small = _dims(batch=70000, nheads=1, ngroups=1, headdim=P, dstate=N, rank=1, chunk=64, seqlen=64,
+                  io_dtype=m3scan.M3_BF16)
+    assert lib.m3_prefill_workspace_size(ctypes.byref(small), ctypes.byref(n)) == 0
+    # backward: one workgroup per (b, h, piece)
+    bd = _dims(batch=1 << 17, nheads=64, ngroups=1, headdim=P, dstate=N, rank=1, seqlen=3)
+    assert _bwd(lib, bd, _grads(), ws=FAKE, nbytes=1 << 62) == -2
