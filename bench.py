@@ -122,6 +122,24 @@ def pmc_traffic(kernel_file, src_names, per_launch_alg):
         return None
 
 
+def mfma_util_rocprof(workload):
+    """MFMA busy fraction (rocprofv3 MfmaUtil) of the workload's output-pass scan kernel from
+    the committed counter summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "prefill_mfma_counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        if rec.get("source_sha") != source_sha(*rec["source_files"]):
+            return None
+        kernels = rec["workloads"][workload]["kernels"]
+        full = next(v for k, v in kernels.items() if k.endswith("true>"))
+        return round(full["mfma_util_percent"] / 100.0, 4)
+    except Exception:
+        return None
+
+
 def main():
     args = parse()
     if args.workload is None:
@@ -376,7 +394,9 @@ def main():
         "prefill": {"ms": round(pre_avg, 4), "tokens_per_s": round(pre_tps, 1),
                     "alg_GB_per_s": round(pre_gbs, 1), "hbm_frac": round(pre_gbs / HBM_PEAK_GBS, 4),
                     "mfma_tflops": round(flops / (pre_avg / 1e3) / 1e12, 2),
-                    "mfma_frac": round(flops / (pre_avg / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+                    "mfma_frac": round(flops / (pre_avg / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                    "mfma_busy_rocprof": (None if (args.fused or args.varlen or args.state_dtype != "fp32")
+                                          else mfma_util_rocprof(args.workload))},
         "decode": ({"ms_total": round(dec_avg, 4), "us_per_step": round(dec_launch_ms * 1e3, 2),
                     "steps_per_s": round(1e3 / dec_launch_ms, 1), "state_GB_per_s": round(state_gbs, 1),
                     "alg_GB_per_s": round(dec_gbs, 1), "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4)}
