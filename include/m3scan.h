@@ -275,6 +275,34 @@ m3_status m3_backward(const m3_dims* dims, const void* x, const float* dt, const
                       const float* dh_out, const m3_grads* grads, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/*
+ * m3_backward for a packed batch of variable-length sequences (the gradients of
+ * m3_prefill_varlen's outputs): sequence s is tokens cu_seqlens[s] ..
+ * cu_seqlens[s+1]-1 and is differentiated as if run alone, from state_in's slice
+ * s (else a zero state and previous input) to its own final state.
+ *
+ * dims:       batch = number of sequences; seqlen = an upper bound on every
+ *             sequence's length; total_tokens <= batch * seqlen (the workspace,
+ *             m3_backward_workspace_size(dims), holds per-token partial sums for
+ *             that many tokens).
+ * cu_seqlens: device array of batch + 1 int64 offsets, non-decreasing, from 0 to
+ *             total_tokens; read only by the kernels and clamped there as in
+ *             m3_prefill_varlen (wrong results for an inconsistent sequence, never
+ *             an access outside the arrays).  Gradient rows of tokens that belong
+ *             to no sequence are left undefined.
+ * Layouts:    x, dy, dx (total_tokens, H, R, P); dt, lambda, ddt, dlambda
+ *             (total_tokens, H); theta, dtheta (total_tokens, G, N/2); B, C, dB, dC
+ *             (total_tokens, G, R, N); dh_out, state_in and the state gradients per
+ *             sequence, as for m3_backward.
+ * Errors:     as m3_backward; also M3_ERR_INVALID_ARG for a NULL cu_seqlens,
+ *             total_tokens < 0 or total_tokens > batch * seqlen.
+ */
+m3_status m3_backward_varlen(const m3_dims* dims, const int64_t* cu_seqlens, int64_t total_tokens,
+                             const void* x, const float* dt, const float* A, const float* lambda,
+                             const float* theta, const void* B, const void* C, const float* D,
+                             const m3_state* state_in, const void* dy, const float* dh_out,
+                             const m3_grads* grads, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* m3_status_string(m3_status status);
 

@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int32_t kVersion = 105;  // 0.1.5: sequence-split backward
+constexpr int32_t kVersion = 106;  // 0.1.6: packed-batch backward
 constexpr size_t kMaxLds = 160 * 1024;
 
 bool dims_ok(const m3_dims* d, bool prefill) {
@@ -321,14 +321,18 @@ m3_status m3_backward_parts(const m3_dims* dims, int32_t* parts, int64_t* tokens
     return M3_OK;
 }
 
-m3_status m3_backward(const m3_dims* dims, const void* x, const float* dt, const float* A,
-                      const float* lambda, const float* theta, const void* B, const void* C,
-                      const float* D, const m3_state* state_in, const void* dy,
-                      const float* dh_out, const m3_grads* grads, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+m3_status backward_common(const m3_dims* dims, const int64_t* cu, int64_t total_tokens, const void* x,
+                          const float* dt, const float* A, const float* lambda, const float* theta,
+                          const void* B, const void* C, const float* D, const m3_state* state_in,
+                          const void* dy, const float* dh_out, const m3_grads* grads, void* workspace,
+                          size_t workspace_bytes, void* stream) {
     if (!dims_ok(dims, true) || !grads) return M3_ERR_INVALID_ARG;
     if (!A || !D || !grads->dA || !grads->dD) return M3_ERR_INVALID_ARG;
-    const bool any_tokens = dims->seqlen > 0;
+    const bool any_tokens = (cu ? total_tokens : dims->batch * dims->seqlen) > 0;
     if (any_tokens && (!x || !dt || !lambda || !theta || !B || !C || !dy || !grads->dx || !grads->ddt ||
                        !grads->dlambda || !grads->dtheta || !grads->dB || !grads->dC))
         return M3_ERR_INVALID_ARG;
@@ -374,8 +378,35 @@ m3_status m3_backward(const m3_dims* dims, const void* x, const float* dt, const
     a.R = s.R;
     a.bf16 = dims->io_dtype == M3_BF16;
     a.state_bf16 = dims->state_dtype == M3_BF16;
+    a.cu = cu;
+    a.T = cu ? total_tokens : s.batch * s.L;
     const hipError_t e = m3::launch_backward(a, lay, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+m3_status m3_backward(const m3_dims* dims, const void* x, const float* dt, const float* A,
+                      const float* lambda, const float* theta, const void* B, const void* C,
+                      const float* D, const m3_state* state_in, const void* dy,
+                      const float* dh_out, const m3_grads* grads, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    return backward_common(dims, nullptr, 0, x, dt, A, lambda, theta, B, C, D, state_in, dy, dh_out, grads,
+                           workspace, workspace_bytes, stream);
+}
+
+m3_status m3_backward_varlen(const m3_dims* dims, const int64_t* cu_seqlens, int64_t total_tokens,
+                             const void* x, const float* dt, const float* A, const float* lambda,
+                             const float* theta, const void* B, const void* C, const float* D,
+                             const m3_state* state_in, const void* dy, const float* dh_out,
+                             const m3_grads* grads, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!cu_seqlens || total_tokens < 0 || !dims) return M3_ERR_INVALID_ARG;
+    // the workspace holds per-token partial gradients for batch * seqlen tokens
+    if (dims->batch > 0 && dims->seqlen >= 0 && total_tokens > dims->batch * dims->seqlen) return M3_ERR_INVALID_ARG;
+    return backward_common(dims, cu_seqlens, total_tokens, x, dt, A, lambda, theta, B, C, D, state_in, dy,
+                           dh_out, grads, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -110,15 +110,19 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
     const int b = bh / a.H, h = bh - b * a.H, g = h / (a.H / a.G);
     const int tid = threadIdx.x, cb = tid & 15, pb = tid >> 4, lane = tid & 63, wv = tid >> 6;
     const int r0 = 4 * pb, c0 = 4 * cb;   // state rows r0 .. r0+3 (two rotation pairs), columns c0 .. c0+3
-    const int64_t L = a.L;
+    // This sequence's tokens: b * L .. + L, or those of packed sequence b (clamped as the
+    // prefill clamps them)
+    const SeqSpan span = seq_span(a.cu, b, a.L, a.T);
+    const int64_t tb = span.start, L = span.len;
     const int H = a.H, G = a.G;
     const float Ah = a.A[h], Dh = a.D[h];
-    const int64_t nseg = (L + KS - 1) / KS;
+    const int64_t nseg = (L + KS - 1) / KS;                    // segments of this sequence
+    const int64_t nseg_max = (a.L + KS - 1) / KS;              // checkpoint slots per (b, h)
     const int64_t s_lo = part * a.seg_per_part;
     const int64_t s_hi = s_lo + a.seg_per_part < nseg ? s_lo + a.seg_per_part : nseg;   // segments of this part
     const bool split = a.parts > 1;
     const size_t pidx = static_cast<size_t>(bh) * a.parts + part;
-    float* ck = a.ckpt + static_cast<size_t>(bh) * nseg * N * P;
+    float* ck = a.ckpt + static_cast<size_t>(bh) * nseg_max * N * P;
     const bool carry = a.bl && a.xl;
     const T* x = static_cast<const T*>(a.x);
     const T* dy = static_cast<const T*>(a.dy);
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
     __shared__ __align__(16) float sRot[KS + 1][N];             // cos, sin of each pair's angle
     __shared__ float sDt[KS + 1], sLam[KS + 1];
 
-    auto soff = [&](int64_t t) { return (static_cast<int64_t>(b) * L + t) * H + h; };
+    auto soff = [&](int64_t t) { return (tb + t) * H + h; };
 
     // Tokens t0-1 .. t0+len-1 into slots 0 .. len, in 16-byte units spread over the
     // workgroup; token -1 is the carried previous input (B and X only), or zeros.
@@ -158,27 +162,27 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
             if (w < uB) {
                 const int o = w * E;
                 dst = &sB[k][o];
-                if (t >= 0 && with_bx) v = *reinterpret_cast<const uint4*>(Bm + ((static_cast<int64_t>(b) * L + t) * G + g) * (R * N) + o);
+                if (t >= 0 && with_bx) v = *reinterpret_cast<const uint4*>(Bm + ((tb + t) * G + g) * (R * N) + o);
                 else if (carry && with_bx) v = *reinterpret_cast<const uint4*>(blp + (static_cast<int64_t>(b) * G + g) * (R * N) + o);
             } else if (w < 2 * uB) {
                 const int o = (w - uB) * E;
                 dst = &sC[k][o];
                 if (t >= 0 && with_cdy)
-                    v = *reinterpret_cast<const uint4*>(Cm + ((static_cast<int64_t>(b) * L + t) * G + g) * (R * N) + o);
+                    v = *reinterpret_cast<const uint4*>(Cm + ((tb + t) * G + g) * (R * N) + o);
             } else if (w < 2 * uB + uX) {
                 const int o = (w - 2 * uB) * E;
                 dst = &sX[k][o];
-                if (t >= 0 && with_bx) v = *reinterpret_cast<const uint4*>(x + ((static_cast<int64_t>(b) * L + t) * H + h) * (R * P) + o);
+                if (t >= 0 && with_bx) v = *reinterpret_cast<const uint4*>(x + ((tb + t) * H + h) * (R * P) + o);
                 else if (carry && with_bx) v = *reinterpret_cast<const uint4*>(xlp + (static_cast<int64_t>(b) * H + h) * (R * P) + o);
             } else if (w < 2 * uB + 2 * uX) {
                 const int o = (w - 2 * uB - uX) * E;
                 dst = &sDY[k][o];
                 if (t >= 0 && with_cdy)
-                    v = *reinterpret_cast<const uint4*>(dy + ((static_cast<int64_t>(b) * L + t) * H + h) * (R * P) + o);
+                    v = *reinterpret_cast<const uint4*>(dy + ((tb + t) * H + h) * (R * P) + o);
             } else {
                 const int o = (w - 2 * uB - 2 * uX) * 4;
                 dst = &sTh[k][o];
-                if (t >= 0) v = *reinterpret_cast<const uint4*>(a.theta + ((static_cast<int64_t>(b) * L + t) * G + g) * (N / 2) + o);
+                if (t >= 0) v = *reinterpret_cast<const uint4*>(a.theta + ((tb + t) * G + g) * (N / 2) + o);
                 // the rotation of these four pairs, once per token for the whole workgroup
                 const float th[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
                 float cs4[4], sn4[4];
@@ -483,7 +487,7 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
             dth[0] = sum16(dth[0]);
             dth[1] = sum16(dth[1]);
             {
-                const int64_t go = ((static_cast<int64_t>(b) * L + t) * GH + gh) * (R * N);
+                const int64_t go = ((tb + t) * GH + gh) * (R * N);
                 float* dCo = a.per_head ? a.dC_part : a.dC;
                 float* dBo = a.per_head ? a.dB_part : a.dB;
 #pragma unroll
@@ -496,7 +500,7 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
                         }
                     }
                 float* dTo = a.per_head ? a.dtheta_part : a.dtheta;
-                if (cb < 2) dTo[((static_cast<int64_t>(b) * L + t) * GH + gh) * (N / 2) + 2 * pb + cb] = cb ? dth[1] : dth[0];
+                if (cb < 2) dTo[((tb + t) * GH + gh) * (N / 2) + 2 * pb + cb] = cb ? dth[1] : dth[0];
             }
             // sums over rows: dX within the wave, then across waves through LDS; scalars per wave
 #pragma unroll
@@ -523,7 +527,7 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
                 float v = 0.f;
 #pragma unroll
                 for (int w2 = 0; w2 < NT / 64; ++w2) v += sDX[par][w2][o];
-                const int64_t xi = ((static_cast<int64_t>(b) * L + t) * H + h) * (R * P) + o;
+                const int64_t xi = ((tb + t) * H + h) * (R * P) + o;
                 a.dx[xi] = v + Dh * io<T>::load(reinterpret_cast<const T*>(&sDY[k][o]));
             }
             if (tid == 0) {
@@ -626,6 +630,10 @@ __global__ __launch_bounds__(NT) void bwd_combine(BwdArgs a) {
     const int S = a.parts;
     const float Ah = a.A[h];
     const int64_t tok_per_part = a.seg_per_part * KS;
+    const SeqSpan span = seq_span(a.cu, b, a.L, a.T);   // a packed sequence may leave trailing parts empty
+    auto dta = [&](int64_t t) {   // dt A at token t of the sequence; 0 (alpha = 1) past its end
+        return t < span.len ? static_cast<double>(a.dt[(span.start + t) * a.H + h] * Ah) : 0.0;
+    };
     auto slot = [&](float* base, int p) { return base + ((static_cast<size_t>(bh) * S + p) * N + r0) * P + c0; };
     auto ld16 = [&](const float* p, float (&v)[4][4]) {
 #pragma unroll
@@ -678,8 +686,7 @@ __global__ __launch_bounds__(NT) void bwd_combine(BwdArgs a) {
         st16(sp, qs);
         if (p == 0) break;
         const int64_t tp = p * tok_per_part;   // first token of part p
-        double lq = a.dec[static_cast<size_t>(bh) * S + p] - static_cast<double>(a.dt[(static_cast<int64_t>(b) * a.L + tp) * a.H + h] * Ah);
-        if (p + 1 < S) lq += static_cast<double>(a.dt[(static_cast<int64_t>(b) * a.L + tp + tok_per_part) * a.H + h] * Ah);
+        const double lq = a.dec[static_cast<size_t>(bh) * S + p] - dta(tp) + dta(tp + tok_per_part);
         const float d = static_cast<float>(exp(lq));
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
@@ -854,10 +861,11 @@ hipError_t launch_backward(BwdArgs a, const BwdLayout& l, hipStream_t st) {
             const unsigned blocks = static_cast<unsigned>(n / 256 + 1 < 65536 ? n / 256 + 1 : 65536);
             bw::bwd_group_sum<<<blocks, 256, 0, st>>>(part, out, rows, hpg, width);
         };
-        if (a.L > 0) {
-            sum(a.dB_part, a.dB, a.batch * a.L * a.G, a.R * a.N);
-            sum(a.dC_part, a.dC, a.batch * a.L * a.G, a.R * a.N);
-            sum(a.dtheta_part, a.dtheta, a.batch * a.L * a.G, a.N / 2);
+        const int64_t tokens = a.cu ? a.T : a.batch * a.L;
+        if (tokens > 0) {
+            sum(a.dB_part, a.dB, tokens * a.G, a.R * a.N);
+            sum(a.dC_part, a.dC, tokens * a.G, a.R * a.N);
+            sum(a.dtheta_part, a.dtheta, tokens * a.G, a.N / 2);
         }
         if (a.dbl && a.bl && a.xl) sum(a.dbl_part, a.dbl, a.batch * a.G, a.R * a.N);
         e = hipGetLastError();

@@ -153,7 +153,9 @@ struct BwdArgs {
     double* dec;              // (batch*H, S): sum of dt*A over each part's tokens
     float* ang;               // (batch*H, S, N/2): sum of theta over each part's tokens, mod 2 pi
     int64_t seg_per_part;
-    int64_t batch, L;
+    int64_t batch, L;         // L: the length, or with cu an upper bound on every sequence's length
+    const int64_t* cu;        // packed sequence starts (batch + 1, device) or null
+    int64_t T;                // tokens of the packed arrays (with cu)
     int H, G, N, P, R;
     int parts;
     bool per_head;

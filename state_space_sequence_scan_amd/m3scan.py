@@ -87,6 +87,9 @@ def lib(path: str = LIB_PATH):
     L.m3_decode_step_fused.argtypes = [ctypes.POINTER(Dims)] + [vp] * 11 + [ctypes.POINTER(Fusion), vp, vp]
     L.m3_backward_workspace_size.restype = ctypes.c_int
     L.m3_backward_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(sz)]
+    L.m3_backward_varlen.restype = ctypes.c_int
+    L.m3_backward_varlen.argtypes = ([ctypes.POINTER(Dims), vp, ctypes.c_int64] + [vp] * 8 +
+                                     [ctypes.POINTER(State), vp, vp, ctypes.POINTER(Grads), vp, sz, vp])
     L.m3_backward_parts.restype = ctypes.c_int
     L.m3_backward_parts.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(ctypes.c_int32),
                                     ctypes.POINTER(ctypes.c_int64)]
@@ -319,6 +322,44 @@ def backward_parts(dims: Dims):
     return int(n.value), int(t.value)
 
 
+def _backward_state(state_in, nb, H, G, N, P, R, io, dev):
+    """The state_in argument of a backward call (nb sequences) and its state dtype."""
+    state_dtype = state_in.h.dtype if state_in is not None else torch.float32
+    if state_in is None:
+        return None, state_dtype
+    _check(state_in.h, "state_in.h", (nb, H, N, P), state_dtype, dev)
+    if state_in.b_last is not None:
+        _check(state_in.b_last, "state_in.b_last", (nb, G, R, N), io, dev)
+        _check(state_in.x_last, "state_in.x_last", (nb, H, R, P), io, dev)
+    return State(state_in.h.data_ptr(),
+                 None if state_in.b_last is None else state_in.b_last.data_ptr(),
+                 None if state_in.x_last is None else state_in.x_last.data_ptr()), state_dtype
+
+
+def _backward_grads(lead, nb, H, G, N, P, R, want_state_grads, grads, dev):
+    """Output tensors of a backward call (per-token ones with leading shape `lead`)."""
+    f32 = dict(dtype=torch.float32, device=dev)
+    shapes = {"dx": lead + (H, R, P), "ddt": lead + (H,), "dA": (H,), "dlam": lead + (H,),
+              "dtheta": lead + (G, N // 2), "dB": lead + (G, R, N), "dC": lead + (G, R, N), "dD": (H,)}
+    if want_state_grads:
+        shapes.update({"dh0": (nb, H, N, P), "db_last": (nb, G, R, N), "dx_last": (nb, H, R, P)})
+    out = {} if grads is None else dict(grads)
+    for k, shp in shapes.items():
+        if k not in out:
+            out[k] = torch.empty(shp, **f32)
+        _check(out[k], k, shp, torch.float32, dev)
+    gs = Grads(*[out[k].data_ptr() if k in out else None for k in
+                 ("dx", "ddt", "dA", "dlam", "dtheta", "dB", "dC", "dD", "dh0", "db_last", "dx_last")])
+    return out, gs
+
+
+def _backward_workspace(dims, workspace, dev):
+    ws = backward_workspace_size(dims)
+    if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
+        workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+    return ws, workspace
+
+
 def backward(x, dt, A, lam, theta, B, C, D, dy, dh_out=None, state_in: Optional[DecodeState] = None,
              want_state_grads: bool = True, workspace: Optional[torch.Tensor] = None,
              grads: Optional[dict] = None):
@@ -344,37 +385,54 @@ def backward(x, dt, A, lam, theta, B, C, D, dy, dh_out=None, state_in: Optional[
     _check(C, "C", (b, L, G, R, N), io, dev)
     if dh_out is not None:
         _check(dh_out, "dh_out", (b, H, N, P), torch.float32, dev)
-    state_dtype = state_in.h.dtype if state_in is not None else torch.float32
+    sin, state_dtype = _backward_state(state_in, b, H, G, N, P, R, io, dev)
     dims = make_dims(b, L, H, G, P, N, R, 1, _IO[io], _IO[state_dtype])
-    sin = None
-    if state_in is not None:
-        _check(state_in.h, "state_in.h", (b, H, N, P), state_dtype, dev)
-        if state_in.b_last is not None:
-            _check(state_in.b_last, "state_in.b_last", (b, G, R, N), io, dev)
-            _check(state_in.x_last, "state_in.x_last", (b, H, R, P), io, dev)
-        sin = State(state_in.h.data_ptr(),
-                    None if state_in.b_last is None else state_in.b_last.data_ptr(),
-                    None if state_in.x_last is None else state_in.x_last.data_ptr())
-    f32 = dict(dtype=torch.float32, device=dev)
-    shapes = {"dx": (b, L, H, R, P), "ddt": (b, L, H), "dA": (H,), "dlam": (b, L, H),
-              "dtheta": (b, L, G, N // 2), "dB": (b, L, G, R, N), "dC": (b, L, G, R, N), "dD": (H,)}
-    if want_state_grads:
-        shapes.update({"dh0": (b, H, N, P), "db_last": (b, G, R, N), "dx_last": (b, H, R, P)})
-    out = {} if grads is None else dict(grads)
-    for k, shp in shapes.items():
-        if k not in out:
-            out[k] = torch.empty(shp, **f32)
-        _check(out[k], k, shp, torch.float32, dev)
-    gs = Grads(*[out[k].data_ptr() if k in out else None for k in
-                 ("dx", "ddt", "dA", "dlam", "dtheta", "dB", "dC", "dD", "dh0", "db_last", "dx_last")])
-    ws = backward_workspace_size(dims)
-    if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
-        workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+    out, gs = _backward_grads((b, L), b, H, G, N, P, R, want_state_grads, grads, dev)
+    ws, workspace = _backward_workspace(dims, workspace, dev)
     rc = lib().m3_backward(ctypes.byref(dims), _p(x), _p(dt), _p(A), _p(lam), _p(theta), _p(B), _p(C),
                            _p(D), None if sin is None else ctypes.byref(sin), _p(dy), _p(dh_out),
                            ctypes.byref(gs), _p(workspace) if ws > 0 else None, ws, _stream(dev))
     if rc != 0:
         raise M3Error("m3_backward", rc)
+    return out
+
+
+def backward_varlen(x, dt, A, lam, theta, B, C, D, dy, cu_seqlens, max_seqlen: int, dh_out=None,
+                    state_in: Optional[DecodeState] = None, want_state_grads: bool = True,
+                    workspace: Optional[torch.Tensor] = None, grads: Optional[dict] = None):
+    """Backward pass of prefill_varlen (m3_backward_varlen): the packed layouts of
+    prefill_varlen for the inputs, dy and the per-token gradients (T, ...), per-sequence
+    dh_out, state_in and state gradients (nseq, ...).  Returns the dict of ``backward``."""
+    T, H, R, P = x.shape
+    G, N = B.shape[1], B.shape[3]
+    nseq = cu_seqlens.shape[0] - 1
+    dev, io = x.device, x.dtype
+    if io not in _IO:
+        raise ValueError(f"x dtype {io} not supported (fp32 or bf16)")
+    if nseq < 1:
+        raise ValueError("cu_seqlens needs at least two entries")
+    _check(cu_seqlens, "cu_seqlens", (nseq + 1,), torch.int64, dev)
+    _check(x, "x", (T, H, R, P), io, dev)
+    _check(dy, "dy", (T, H, R, P), io, dev)
+    _check(dt, "dt", (T, H), torch.float32, dev)
+    _check(lam, "lam", (T, H), torch.float32, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(theta, "theta", (T, G, N // 2), torch.float32, dev)
+    _check(B, "B", (T, G, R, N), io, dev)
+    _check(C, "C", (T, G, R, N), io, dev)
+    if dh_out is not None:
+        _check(dh_out, "dh_out", (nseq, H, N, P), torch.float32, dev)
+    sin, state_dtype = _backward_state(state_in, nseq, H, G, N, P, R, io, dev)
+    dims = make_dims(nseq, max_seqlen, H, G, P, N, R, 1, _IO[io], _IO[state_dtype])
+    out, gs = _backward_grads((T,), nseq, H, G, N, P, R, want_state_grads, grads, dev)
+    ws, workspace = _backward_workspace(dims, workspace, dev)
+    rc = lib().m3_backward_varlen(ctypes.byref(dims), _p(cu_seqlens), T, _p(x), _p(dt), _p(A), _p(lam),
+                                  _p(theta), _p(B), _p(C), _p(D), None if sin is None else ctypes.byref(sin),
+                                  _p(dy), _p(dh_out), ctypes.byref(gs), _p(workspace) if ws > 0 else None, ws,
+                                  _stream(dev))
+    if rc != 0:
+        raise M3Error("m3_backward_varlen", rc)
     return out
 
 

@@ -28,8 +28,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_symbols() == ["m3_backward", "m3_backward_parts", "m3_backward_workspace_size",
-                                  "m3_decode_step",
+    assert declared_symbols() == ["m3_backward", "m3_backward_parts", "m3_backward_varlen",
+                                  "m3_backward_workspace_size", "m3_decode_step",
                                   "m3_decode_step_fused", "m3_prefill_chunked", "m3_prefill_fused",
                                   "m3_prefill_varlen", "m3_prefill_workspace_size", "m3_status_string",
                                   "m3_version"]
@@ -280,3 +280,27 @@ def test_launch_size_limits(lib):
     # backward: one workgroup per (b, h, piece)
     bd = _dims(batch=1 << 17, nheads=64, ngroups=1, headdim=P, dstate=N, rank=1, seqlen=3)
     assert _bwd(lib, bd, _grads(), ws=FAKE, nbytes=1 << 62) == -2
+
+
+def test_backward_varlen_rejects_bad_arguments(lib):
+    """Packed-batch backward: a NULL cu_seqlens, a negative token count or more tokens than
+    batch * seqlen (the workspace's per-token room) are argument errors; everything else is
+    checked as for m3_backward.  No call here reaches a launch."""
+    d = _dims(batch=3, seqlen=10, nheads=4, ngroups=2, headdim=64, dstate=128, rank=2, io_dtype=m3scan.M3_BF16)
+    def call(cu=FAKE, T=20, grads=None, args=None, dy=FAKE):
+        args = [FAKE] * 8 if args is None else args
+        g = _grads() if grads is None else grads
+        return lib.m3_backward_varlen(ctypes.byref(d), cu, T, *args, None, dy, None, ctypes.byref(g),
+                                      None, 0, None)
+    assert call(cu=None) == -1
+    assert call(T=-1) == -1
+    assert call(T=31) == -1                   # 3 sequences of at most 10 tokens
+    assert call(dy=None) == -1
+    assert call(grads=_grads(dx=1)) == -1
+    args = [FAKE] * 8
+    args[5] = None                            # B
+    assert call(args=args) == -1
+    assert call(T=30) == -3                   # valid: the missing workspace is the only error
+    small = _dims(batch=3, seqlen=10)         # N = 16, P = 16: no backward kernel
+    assert lib.m3_backward_varlen(ctypes.byref(small), FAKE, 20, *([FAKE] * 8), None, FAKE, None,
+                                  ctypes.byref(_grads()), None, 0, None) == -2

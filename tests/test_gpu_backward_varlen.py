@@ -1,0 +1,115 @@
+"""GPU parity of the packed variable-length backward (m3_backward_varlen through the
+C ABI): every sequence of the pack against the oracle's adjoint loop run on that
+sequence alone (its own incoming state, carry and final-state cotangent), empty and
+one-token sequences, packs whose sequences are split into pieces with the short ones
+leaving trailing pieces empty, one without a split, and an equal-length pack against
+the uniform-batch backward (same kernels, so bit-identical).  Bar: 1e-3 max relative
+error per gradient, as for the uniform-batch backward."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import draw, np64, say
+from state_space_sequence_scan_amd import m3scan
+
+pytestmark = pytest.mark.gpu
+
+TOL_BWD = 1e-3
+NAMES = ("x", "dt", "A", "lam", "theta", "B", "C", "D")
+P, N = 64, 128
+
+
+def _pack(lengths, H, G, R, io, seed):
+    T = int(sum(lengths))
+    d = draw(1, max(T, 1), H, G, P, N, R, io, 2.0, seed=seed)
+    d = {k: (v[0, :T].contiguous() if v.dim() > 1 else v) for k, v in d.items()}
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int64, device="cuda")
+    return d, cu, T
+
+
+def _rel(g, r):
+    g = np.asarray(g, np.float64)
+    r = np.asarray(r, np.float64)
+    if r.size == 0:
+        return 0.0
+    return float(np.max(np.abs(g - r)) / max(np.max(np.abs(r)), 1e-30))
+
+
+# lengths, H, G, R, io, with state_in, with dh_out
+CASES = [
+    ([130, 0, 64, 17, 300, 1], 4, 1, 2, "bf16", True, True),
+    ([200, 63, 1, 129], 2, 2, 4, "fp32", False, True),
+    ([40, 10, 33, 0], 64, 8, 1, "bf16", True, False),      # 256 (b, h) pairs: no split
+]
+
+
+def _id(c):
+    return "L{}-H{}G{}R{}-{}{}{}".format("_".join(map(str, c[0])), *c[1:5], "-state" if c[5] else "",
+                                       "-dh" if c[6] else "")
+
+
+@pytest.mark.parametrize("case", CASES, ids=_id)
+def test_backward_varlen_each_sequence_matches_oracle(case):
+    lengths, H, G, R, io, with_state, with_dh = case
+    ns, Lmax = len(lengths), max(lengths)
+    d, cu, T = _pack(lengths, H, G, R, io, seed=sum(lengths) + R)
+    tdt = torch.bfloat16 if io == "bf16" else torch.float32
+    gen = torch.Generator(device="cpu").manual_seed(T + 5)
+    dy = torch.randn((T, H, R, P), generator=gen).to(tdt).cuda()
+    dh = torch.randn((ns, H, N, P), generator=gen).cuda() if with_dh else None
+    st = None
+    if with_state:
+        h0 = torch.randn((ns, H, N, P), generator=gen).cuda()
+        bl = torch.randn((ns, G, R, N), generator=gen).to(tdt).cuda()
+        xl = torch.randn((ns, H, R, P), generator=gen).to(tdt).cuda()
+        st = m3scan.DecodeState(h0, bl, xl)
+    parts = m3scan.backward_parts(m3scan.make_dims(ns, Lmax, H, G, P, N, R, 1, 0))
+    say("backward varlen", _id(case), "pieces", parts)
+    gr = m3scan.backward_varlen(*[d[k] for k in NAMES], dy, cu, Lmax, dh_out=dh, state_in=st)
+    torch.cuda.synchronize()
+    c = [0] + list(np.cumsum(lengths))
+    dA = np.zeros(H)
+    dD = np.zeros(H)
+    for s, n in enumerate(lengths):
+        if n == 0:   # nothing to differentiate: h_L = h_0, so dh0 = dh_out; no carry gradient
+            ref_dh0 = np64(dh[s]) if with_dh else np.zeros((H, N, P))
+            assert np.array_equal(np64(gr["dh0"][s]), ref_dh0)
+            assert float(gr["db_last"][s].abs().max()) == 0.0 and float(gr["dx_last"][s].abs().max()) == 0.0
+            continue
+        sl = lambda k: np64(d[k][c[s]:c[s + 1]])[None]
+        st_np = (np64(st.h[s:s + 1]), np64(st.b_last[s:s + 1]), np64(st.x_last[s:s + 1])) if with_state else None
+        ref = oracle.scan_backward(sl("x"), sl("dt"), np64(d["A"]), sl("lam"), sl("theta"), sl("B"), sl("C"),
+                                   np64(d["D"]), np64(dy[c[s]:c[s + 1]])[None],
+                                   dh_out=None if dh is None else np64(dh[s:s + 1]), state_in=st_np)
+        errs = {k: _rel(np64(gr[k][c[s]:c[s + 1]])[None], ref[k])
+                for k in ("dx", "ddt", "dlam", "dtheta", "dB", "dC")}
+        errs["dh0"] = _rel(np64(gr["dh0"][s:s + 1]), ref["dh0"])
+        if with_state:
+            errs["db_last"] = _rel(np64(gr["db_last"][s:s + 1]), ref["db_last"])
+            errs["dx_last"] = _rel(np64(gr["dx_last"][s:s + 1]), ref["dx_last"])
+        dA += ref["dA"]
+        dD += ref["dD"]
+        say(f"  seq {s} (len {n}): " + " ".join(f"{k} {v:.1e}" for k, v in errs.items()))
+        bad = {k: v for k, v in errs.items() if not v <= TOL_BWD}
+        assert not bad, (s, bad)
+    eA, eD = _rel(np64(gr["dA"]), dA), _rel(np64(gr["dD"]), dD)
+    say(f"  dA {eA:.1e} dD {eD:.1e}")
+    assert eA <= TOL_BWD and eD <= TOL_BWD
+
+
+def test_backward_varlen_equal_lengths_match_uniform_batch():
+    """A pack of equal-length sequences runs the uniform batch's kernels on the same
+    tokens: the gradients are bit-identical."""
+    b, L, H, G, R = 3, 50, 4, 2, 2
+    d = draw(b, L, H, G, P, N, R, "bf16", 2.0, seed=91)
+    gen = torch.Generator(device="cpu").manual_seed(4)
+    dy = torch.randn((b, L, H, R, P), generator=gen).to(torch.bfloat16).cuda()
+    dh = torch.randn((b, H, N, P), generator=gen).cuda()
+    g1 = m3scan.backward(*[d[k] for k in NAMES], dy, dh_out=dh)
+    flat = {k: (v.reshape((b * L,) + tuple(v.shape[2:])).contiguous() if v.dim() > 1 else v) for k, v in d.items()}
+    cu = torch.arange(0, b * L + 1, L, dtype=torch.int64, device="cuda")
+    g2 = m3scan.backward_varlen(*[flat[k] for k in NAMES], dy.reshape(b * L, H, R, P), cu, L, dh_out=dh)
+    torch.cuda.synchronize()
+    for k in g1:
+        assert torch.equal(g1[k].reshape(g2[k].shape), g2[k]), k
