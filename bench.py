@@ -48,7 +48,7 @@ def parse():
                          "per-token A, RMSNorm and bias of B and C, output gate")
     ap.add_argument("--varlen", action="store_true",
                     help="pack the batch's sequences with seeded lengths uniform in [L/4, L] "
-                         "(m3_prefill_varlen) instead of equal lengths L")
+                         "(m3_prefill_varlen; with --backward, m3_backward_varlen) instead of equal lengths L")
     ap.add_argument("--state-dtype", default="fp32", choices=("fp32", "bf16"),
                     help="dtype of the state in HBM (bf16: reduced-precision state, fp32 math)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -451,29 +451,44 @@ def run_backward(args, cfg):
     dims = m3scan.make_dims(cfg.batch, L, cfg.nheads, cfg.ngroups, cfg.headdim, cfg.dstate, cfg.rank,
                             1, m3scan.M3_BF16 if cfg.io_dtype == "bf16" else m3scan.M3_F32)
     ws = torch.empty(m3scan.backward_workspace_size(dims), dtype=torch.uint8, device=dev)
-    grads = m3scan.backward(*[d[k] for k in names], dy, workspace=ws, want_state_grads=False)
+    lens = np.full(cfg.batch, L, dtype=np.int64)
+    if args.varlen:   # the prefill's seeded length mix; each sequence keeps its first lens[i] tokens
+        lens = np.random.default_rng(cfg.seed + 7).integers(max(L // 4, 1), L + 1, cfg.batch)
+        starts = np.concatenate([[0], np.cumsum(lens)])
+        cu = torch.tensor(starts, dtype=torch.int64, device=dev)
+        dp = {k: torch.cat([v[i, :int(lens[i])] for i in range(cfg.batch)]).contiguous()
+              for k, v in list(d.items()) + [("dy", dy)] if v.dim() > 1}
+
+        def bwd(g=None):
+            return m3scan.backward_varlen(*[dp[k] if k in dp else d[k] for k in names], dp["dy"], cu, L,
+                                          workspace=ws, grads=g, want_state_grads=False)
+    else:
+        def bwd(g=None):
+            return m3scan.backward(*[d[k] for k in names], dy, workspace=ws, grads=g, want_state_grads=False)
+    grads = bwd()
     torch.cuda.synchronize()
     ev = lambda: torch.cuda.Event(enable_timing=True)
     for _ in range(args.warmup):
-        m3scan.backward(*[d[k] for k in names], dy, workspace=ws, grads=grads, want_state_grads=False)
+        bwd(grads)
     torch.cuda.synchronize()
     times = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
         e0, e1 = ev(), ev()
         e0.record(stream)
-        m3scan.backward(*[d[k] for k in names], dy, workspace=ws, grads=grads, want_state_grads=False)
+        bwd(grads)
         e1.record(stream)
         times.append((e0, e1))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = float(np.mean([a.elapsed_time(b) for a, b in times]))
     step_ms = wall * 1e3 / args.steps
-    tokens = cfg.batch * L
-    flops = backward_flops(cfg, L)
-    nbytes = backward_bytes(cfg, L)
+    tokens = int(lens.sum())
+    flops = backward_flops(cfg, L) * tokens / (cfg.batch * L)
+    nbytes = backward_bytes(cfg, L) * tokens / (cfg.batch * L)
     tflops = flops / (ms / 1e3) / 1e12
-    traffic = pmc_traffic(f"backward_{args.workload}_hbm_counters.json", ["m3_backward.hip", "m3_common.h"], nbytes)
+    traffic = pmc_traffic(f"backward_{args.workload}{'_varlen' if args.varlen else ''}_hbm_counters.json",
+                          ["m3_backward.hip", "m3_common.h"], nbytes)
     parts, tpp = m3scan.backward_parts(dims)
     passes = "local + combine + " if parts > 1 else ""
     roof = {"kernel": f"{passes}bwd_scan<io {cfg.io_dtype}, R{cfg.rank}> + group sums "
@@ -488,8 +503,19 @@ def run_backward(args, cfg):
         import oracle
         f = lambda t: t.detach().double().cpu().numpy()
 
-        def slice_inputs(bi, h):
+        def grad_slice(k, bi, h):   # the per-head gradient k of sequence bi, head h, as (1, len, 1, ...)
+            if args.varlen:
+                return grads[k][int(starts[bi]):int(starts[bi + 1]), h:h + 1][None].double().cpu().numpy()
+            return grads[k][bi:bi + 1, :, h:h + 1].double().cpu().numpy()
+
+        def slice_inputs(bi, h, packed=args.varlen):
             g = h // (cfg.nheads // cfg.ngroups)
+            if packed:
+                s0, s1 = int(starts[bi]), int(starts[bi + 1])
+                return {"x": f(dp["x"][s0:s1, h:h + 1][None]), "dt": f(dp["dt"][s0:s1, h:h + 1][None]),
+                        "lam": f(dp["lam"][s0:s1, h:h + 1][None]), "theta": f(dp["theta"][s0:s1, g:g + 1][None]),
+                        "B": f(dp["B"][s0:s1, g:g + 1][None]), "C": f(dp["C"][s0:s1, g:g + 1][None]),
+                        "A": f(d["A"][h:h + 1]), "D": f(d["D"][h:h + 1]), "dy": f(dp["dy"][s0:s1, h:h + 1][None])}
             return {"x": f(d["x"][bi:bi + 1, :, h:h + 1]), "dt": f(d["dt"][bi:bi + 1, :, h:h + 1]),
                     "lam": f(d["lam"][bi:bi + 1, :, h:h + 1]), "theta": f(d["theta"][bi:bi + 1, :, g:g + 1]),
                     "B": f(d["B"][bi:bi + 1, :, g:g + 1]), "C": f(d["C"][bi:bi + 1, :, g:g + 1]),
@@ -503,23 +529,21 @@ def run_backward(args, cfg):
                 si = slice_inputs(bi, h)
                 ref = oracle.scan_backward(*[si[k] for k in names], si["dy"])
                 # per-head gradients (group-shared and batch-summed ones mix other slices)
-                for k, sl in (("dx", (slice(bi, bi + 1), slice(None), slice(h, h + 1))),
-                              ("ddt", (slice(bi, bi + 1), slice(None), slice(h, h + 1))),
-                              ("dlam", (slice(bi, bi + 1), slice(None), slice(h, h + 1)))):
-                    gv = grads[k][sl].double().cpu().numpy()
+                for k in ("dx", "ddt", "dlam"):
+                    gv = grad_slice(k, bi, h)
                     errs.append(float(np.max(np.abs(gv - ref[k])) / max(np.max(np.abs(ref[k])), 1e-30)))
             check = {"slices": args.check_slices, "max_rel_err": max(errs), "tolerance": 1e-3,
                      "compared": "dx, ddt, dlambda of sampled (b, h) slices"}
         if not args.no_cpu_baseline:
             threads = oracle.max_threads()
-            si = slice_inputs(0, 0)
+            si = slice_inputs(0, 0, packed=False)   # the oracle's rate on whole-length slices
             t1 = time.perf_counter()
             oracle.scan_backward(*[si[k] for k in names], si["dy"], nthreads=1)
             one = time.perf_counter() - t1
             # the oracle parallelises over batch elements: each sampled slice is its own batch element
             n = int(max(threads, min(cfg.batch * cfg.nheads, args.cpu_seconds * threads / max(one, 1e-6))))
             n = max(threads, (n // threads) * threads)
-            sl = [slice_inputs(i // cfg.nheads % cfg.batch, i % cfg.nheads) for i in range(n)]
+            sl = [slice_inputs(i // cfg.nheads % cfg.batch, i % cfg.nheads, packed=False) for i in range(n)]
             st = {k: np.concatenate([s[k] for s in sl], axis=0) for k in ("x", "dt", "lam", "theta", "B", "C", "dy")}
             t1 = time.perf_counter()
             # A, D differ per slice's head; the sample uses head 0's values for all (same cost)
@@ -538,7 +562,9 @@ def run_backward(args, cfg):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
         "data": "synthetic (seeded torch generators on the GPU; distributions of the workload; "
                 "dy ~ N(0,1))",
-        "config": {"workload": cfg.label + "; backward pass (gradients of every input)", "name": cfg.name,
+        "config": {"workload": cfg.label + "; backward pass (gradients of every input)"
+                               + (f"; packed lengths uniform in [{max(L // 4, 1)}, {L}], {tokens} tokens"
+                                  if args.varlen else ""), "name": cfg.name,
                    "batch": cfg.batch, "seqlen": L, "heads": cfg.nheads, "groups": cfg.ngroups,
                    "headdim": cfg.headdim, "dstate": cfg.dstate, "rank": cfg.rank, "io_dtype": cfg.io_dtype},
         "backward": {"ms": round(ms, 4), "tokens_per_s": round(tokens / (ms / 1e3), 1),
