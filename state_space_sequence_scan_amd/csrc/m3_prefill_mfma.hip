@@ -1046,10 +1046,15 @@ bool mfma_supported(const PrefillArgs& a) {
            (a.Q == 32 || a.Q == 64) && offsets_fit && grid_fits;
 }
 
+// Segments per sequence: as many as fill the CUs in one round of workgroups.  A chunk
+// of up to 64 rows (Q * R <= 64) runs 4 waves and fits two workgroups per CU (registers);
+// larger chunks fit one (LDS).  Rounding down keeps the output pass to a single round
+// (rounding up left a second round nearly empty).  The CU count is MI355X's.
 static int choose_nseg(const PrefillArgs& a, int nchunks) {
+    constexpr int64_t kCUs = 256;
     const int64_t slices = a.batch * a.H;
-    const int64_t target = 512;                       // two workgroups per CU
-    int64_t nseg = (target + slices - 1) / slices;
+    const int64_t slots = kCUs * (a.Q * a.R <= 64 ? 2 : 1);
+    int64_t nseg = slots / slices;
     const int64_t max_seg = nchunks / 4 > 0 ? nchunks / 4 : 1;   // at least ~4 chunks per segment
     if (nseg > max_seg) nseg = max_seg;
     if (nseg < 1) nseg = 1;
