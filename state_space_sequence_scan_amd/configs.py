@@ -36,22 +36,22 @@ class ScanConfig:
 
 
 CONFIGS = {
-    "c0": ScanConfig("c0", batch=1, seqlen=256, nheads=4, headdim=16, dstate=16, rank=1,
+    "siso_l256_fp32": ScanConfig("siso_l256_fp32", batch=1, seqlen=256, nheads=4, headdim=16, dstate=16, rank=1,
                      chunk=32, io_dtype="fp32", seed=1000,
                      label="single SISO layer, fp32, L=256, H=4, P=16, N=16, chunk 32"),
-    "c1": ScanConfig("c1", batch=4, seqlen=2048, nheads=24, headdim=64, dstate=128, rank=2,
+    "nanomamba3": ScanConfig("nanomamba3", batch=4, seqlen=2048, nheads=24, headdim=64, dstate=128, rank=2,
                      chunk=32, seed=1001,
                      label="nanomamba3-shaped layer (d_model 768, d_inner 1536): 24 heads x P=64, "
                            "N=128, MIMO R=2, chunk 32, batch 4, L=2048"),
-    "c2": ScanConfig("c2", batch=8, seqlen=8192, nheads=64, headdim=64, dstate=128, rank=1,
+    "siso_l8192": ScanConfig("siso_l8192", batch=8, seqlen=8192, nheads=64, headdim=64, dstate=128, rank=1,
                      chunk=64, seed=1002,
                      label="1.5B-scale SISO layer (d_model 2048): 64 heads x P=64, N=128, R=1, "
                            "chunk 64, batch 8, L=8192"),
-    "c3": ScanConfig("c3", batch=2, seqlen=16384, nheads=64, headdim=64, dstate=128, rank=4,
+    "mimo4_l16384": ScanConfig("mimo4_l16384", batch=2, seqlen=16384, nheads=64, headdim=64, dstate=128, rank=4,
                      chunk=64, theta_scale=4.0, seed=1003,
                      label="1.5B-scale MIMO layer: 64 heads x P=64, N=128, R=4, chunk 64, batch 2, "
                            "L=16384, theta x4"),
-    "c4": ScanConfig("c4", batch=256, seqlen=1024, nheads=64, headdim=64, dstate=128, rank=4,
+    "mimo4_decode_b256": ScanConfig("mimo4_decode_b256", batch=256, seqlen=1024, nheads=64, headdim=64, dstate=128, rank=4,
                      chunk=64, decode_steps=512, seed=1004,
                      label="1.5B-scale MIMO R=4 layer, batch 256: 1024-token chunked prefill, "
                            "then 512 single-token decode steps from its fp32 state"),

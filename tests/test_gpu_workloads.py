@@ -26,7 +26,7 @@ def _err(g, r):
     return float(np.max(np.abs(g - r)) / np.max(np.abs(r)))
 
 
-@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3"])
+@pytest.mark.parametrize("name", ["siso_l256_fp32", "nanomamba3", "siso_l8192", "mimo4_l16384"])
 def test_prefill_workload_sampled(name):
     cfg = CONFIGS[name]
     say("workload", name, cfg.label)
@@ -47,8 +47,8 @@ def test_prefill_workload_sampled(name):
 
 def test_decode_workload_sampled():
     """1.5B MIMO R=4 layer, batch 256: 1024-token prefill, then 512 decode steps."""
-    cfg = CONFIGS["c4"]
-    say("workload c4", cfg.label)
+    cfg = CONFIGS["mimo4_decode_b256"]
+    say("workload mimo4_decode_b256", cfg.label)
     d = inputs.draw_config(cfg, device="cuda")
     dd = inputs.draw_decode(cfg, cfg.decode_steps, device="cuda")
     y, st = m3scan.prefill(d["x"], d["dt"], d["A"], d["lam"], d["theta"], d["B"], d["C"], d["D"],
@@ -76,9 +76,9 @@ def test_decode_workload_sampled():
         assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("name", ["c1", "c3"])
+@pytest.mark.parametrize("name", ["nanomamba3", "mimo4_l16384"])
 def test_backward_workload_sampled(name):
-    """The backward at the full size of a training-shaped workload (c1 is the benchmark's
+    """The backward at the full size of a training-shaped workload (nanomamba3 is the benchmark's
     default for it): per-head gradients dx, ddt, dlambda of sampled (batch, head) slices
     against the oracle's adjoint run on that slice alone (group-shared and batch-summed
     gradients mix slices and are covered by the small-size tests)."""
@@ -102,8 +102,8 @@ def test_backward_workload_sampled(name):
 
 def test_fused_prefill_workload_sampled():
     """The fused prologue/epilogue at the full size of the 1.5B-scale SISO layer."""
-    cfg = CONFIGS["c2"]
-    say("fused workload c2")
+    cfg = CONFIGS["siso_l8192"]
+    say("fused workload siso_l8192")
     d = inputs.draw_config(cfg, device="cuda")
     g = torch.Generator(device="cuda").manual_seed(cfg.seed + 23)
     R, N = cfg.rank, cfg.dstate
