@@ -37,12 +37,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default=None, help="nanomamba3, siso_l8192, mimo4_l16384 (prefill only) or mimo4_decode_b256 (prefill + decode); "
-                                                      "default mimo4_decode_b256, or nanomamba3 with --backward")
+    ap.add_argument("--workload", default=None,
+                    help="siso_l256_fp32, nanomamba3, siso_l8192, mimo4_l16384 (prefill only) or "
+                         "mimo4_decode_b256 (prefill + decode); default mimo4_decode_b256, or nanomamba3 "
+                         "with --backward")
     ap.add_argument("--decode-steps", type=int, default=None, help="override the decode steps per step")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (m3_backward) of the workload's prefill instead "
-                         "(default workload for it: nanomamba3, the nanomamba3 training shape)")
+                         "(default workload for it: nanomamba3, the training shape)")
     ap.add_argument("--fused", action="store_true",
                     help="run the fused layer prologue/epilogue (m3_prefill_fused, m3_decode_step_fused): "
                          "per-token A, RMSNorm and bias of B and C, output gate")
@@ -145,7 +147,7 @@ def main():
     if args.workload is None:
         args.workload = "nanomamba3" if args.backward else "mimo4_decode_b256"
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the scan on a single MI355X "
+        print("bench.py measures one GPU only: the scan runs on a single MI355X "
               "(multi-GPU sharding is a design note, not implemented); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
