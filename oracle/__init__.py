@@ -65,6 +65,10 @@ def load(path: str = _LIB):
     f = lib.m3o_scan_backward
     f.restype = ctypes.c_int
     f.argtypes = [ctypes.POINTER(_Dims)] + [ctypes.c_void_p] * 24 + [ctypes.c_int]
+    f = lib.m3o_scan_backward_ex
+    f.restype = ctypes.c_int
+    f.argtypes = ([ctypes.POINTER(_Dims)] + [ctypes.c_void_p] * 3 + [ctypes.c_int] +
+                  [ctypes.c_void_p] * 21 + [ctypes.c_int])
     lib.m3o_round_bf16.restype = ctypes.c_double
     lib.m3o_round_bf16.argtypes = [ctypes.c_double]
     lib.m3o_max_threads.restype = ctypes.c_int
@@ -152,7 +156,8 @@ def scan_backward(x, dt, A, lam, theta, B, C, D, dy, dh_out=None, state_in=None,
     (optional) that of the final state.  Returns a dict with dx, ddt, dA, dlam, dtheta,
     dB, dC, dD (shapes of the inputs; dB, dC and dtheta summed over the heads of a
     group, dA and dD over batch and tokens), dh0 (b,H,N,P) and, when the state carries
-    a previous input, db_last (b,G,R,N) and dx_last (b,H,R,P).
+    a previous input, db_last (b,G,R,N) and dx_last (b,H,R,P).  A per-token decay rate
+    A (b, L, H) gives dA per token, (b, L, H).
     """
     x, dt, A, lam, theta, B, C, D, dy = map(_f64, (x, dt, A, lam, theta, B, C, D, dy))
     b, L, H, R, P = x.shape
@@ -168,15 +173,18 @@ def scan_backward(x, dt, A, lam, theta, B, C, D, dy, dh_out=None, state_in=None,
     if dho is not None:
         assert dho.shape == (b, H, N, P)
     carry = bl is not None and xl is not None
-    out = {"dx": np.empty_like(x), "ddt": np.empty_like(dt), "dA": np.empty((H,)),
+    a_tok = A.ndim == 3
+    if a_tok:
+        assert A.shape == (b, L, H)
+    out = {"dx": np.empty_like(x), "ddt": np.empty_like(dt), "dA": np.empty((b, L, H) if a_tok else (H,)),
            "dlam": np.empty_like(lam), "dtheta": np.empty_like(theta), "dB": np.empty_like(B),
            "dC": np.empty_like(C), "dD": np.empty((H,)), "dh0": np.empty((b, H, N, P))}
     if carry:
         out["db_last"] = np.empty((b, G, R, N))
         out["dx_last"] = np.empty((b, H, R, P))
     d = _Dims(b, L, H, G, P, N, R)
-    rc = load(lib_path).m3o_scan_backward(
-        ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(lam), _ptr(theta), _ptr(B), _ptr(C),
+    rc = load(lib_path).m3o_scan_backward_ex(
+        ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), int(a_tok), _ptr(lam), _ptr(theta), _ptr(B), _ptr(C),
         _ptr(D), _ptr(h0), _ptr(bl), _ptr(xl), _ptr(dy), _ptr(dho), _ptr(out["dx"]),
         _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dlam"]), _ptr(out["dtheta"]), _ptr(out["dB"]),
         _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dh0"]), _ptr(out.get("db_last")),

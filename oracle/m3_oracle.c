@@ -255,14 +255,18 @@ int m3o_max_threads(void) {
  *   dC_t[:,r] = h_t dy_t[r,:],  dB_t[:,r] = dU_t X_t[r,:],  dX_t[r,:] = D dy_t[r,:] + B_t[:,r]^T dU_t
  *   dD = sum_t <dy_t, X_t>,  dh0 = alpha_1 q_1,  dU_0 = beta_1 q_1 (the carried input)
  * and the chain rule through alpha = exp(dt A), beta = (1 - lambda) dt alpha,
- * gamma = lambda dt for ddt, dlambda and dA.
+ * gamma = lambda dt for ddt, dlambda and dA.  With a per-token decay rate
+ * (a_per_token: A is (batch, L, H), the A_t of the discretisation) A is read at
+ * each token and its gradient is written per token to dA_tok instead of summed
+ * per head.
  *
  * The forward states are recomputed and kept for the whole slice (fp64, L + 1
  * states of N x P), which suits the small sizes it is used at.
  * Returns 0, -1 on a shape error, -2 if memory cannot be allocated.
  */
 static int backward_batch(const m3o_dims* dm, int64_t b,
-                          const double* x, const double* dt, const double* A, const double* lam,
+                          const double* x, const double* dt, const double* A, int a_per_token,
+                          double* dA_tok, const double* lam,
                           const double* theta, const double* B, const double* C, const double* D,
                           const double* h0, const double* b_last, const double* x_last,
                           const double* dy, const double* dh_out,
@@ -296,7 +300,8 @@ static int backward_batch(const m3o_dims* dm, int64_t b,
             }
         for (int64_t t = 0; t < L; ++t) {
             const double dtv = dt[(b * L + t) * H + h], lv = lam[(b * L + t) * H + h];
-            const double alpha = exp(dtv * A[h]), beta = (1.0 - lv) * dtv * alpha, gamma = lv * dtv;
+            const double a_th = a_per_token ? A[(b * L + t) * H + h] : A[h];
+            const double alpha = exp(dtv * a_th), beta = (1.0 - lv) * dtv * alpha, gamma = lv * dtv;
             for (int64_t n = 0; n < N; ++n)
                 for (int64_t p = 0; p < P; ++p) {
                     double u = 0.0;
@@ -325,7 +330,8 @@ static int backward_batch(const m3o_dims* dm, int64_t b,
         double dA_h = 0.0, dD_h = 0.0;
         for (int64_t t = L - 1; t >= 0; --t) {
             const double dtv = dt[(b * L + t) * H + h], lv = lam[(b * L + t) * H + h];
-            const double alpha = exp(dtv * A[h]), beta = (1.0 - lv) * dtv * alpha, gamma = lv * dtv;
+            const double a_th = a_per_token ? A[(b * L + t) * H + h] : A[h];
+            const double alpha = exp(dtv * a_th), beta = (1.0 - lv) * dtv * alpha, gamma = lv * dtv;
             const double* ht = hall + (t + 1) * NP;
             const double* hp = hall + t * NP;
             /* g_t = alpha_{t+1} q_{t+1} + C_t dy_t^T */
@@ -402,9 +408,13 @@ static int backward_batch(const m3o_dims* dm, int64_t b,
                 }
             }
             /* scalars through alpha = exp(dt A), beta = (1 - lambda) dt alpha, gamma = lambda dt */
-            ddt[(b * L + t) * H + h] = dal * A[h] * alpha + dbe * (1.0 - lv) * (alpha + dtv * A[h] * alpha) + dgam * lv;
+            ddt[(b * L + t) * H + h] = dal * a_th * alpha + dbe * (1.0 - lv) * (alpha + dtv * a_th * alpha) + dgam * lv;
             dlam[(b * L + t) * H + h] = -dbe * dtv * alpha + dgam * dtv;
-            dA_h += dal * dtv * alpha + dbe * (1.0 - lv) * dtv * dtv * alpha;
+            const double dA_t = dal * dtv * alpha + dbe * (1.0 - lv) * dtv * dtv * alpha;
+            if (a_per_token)
+                dA_tok[(b * L + t) * H + h] = dA_t;
+            else
+                dA_h += dA_t;
             memcpy(qn, q, sizeof(double) * NP);
             alpha_next = alpha;
             beta_next = beta;
@@ -441,16 +451,17 @@ static int backward_batch(const m3o_dims* dm, int64_t b,
     return 0;
 }
 
-/* Backward of m3o_scan (see backward_batch).  Group-shared gradients (dtheta,
- * dB, dC, db_last) and the per-head sums dA, dD are accumulated, so each batch
- * element is handled by one thread; the outputs are overwritten, not added to.
- * dh_out, dh0, db_last and dx_last may be NULL. */
-int m3o_scan_backward(const m3o_dims* dm, const double* x, const double* dt, const double* A,
-                      const double* lam, const double* theta, const double* B, const double* C,
-                      const double* D, const double* h0, const double* b_last, const double* x_last,
-                      const double* dy, const double* dh_out, double* dx, double* ddt, double* dA,
-                      double* dlam, double* dtheta, double* dB, double* dC, double* dD, double* dh0,
-                      double* db_last, double* dx_last, int nthreads) {
+/* Backward of m3o_scan_ex (see backward_batch).  Group-shared gradients (dtheta,
+ * dB, dC, db_last) and the per-head sums dA (per-head A), dD are accumulated, so
+ * each batch element is handled by one thread; the outputs are overwritten, not
+ * added to.  With a_per_token, A and dA are (batch, L, H).  dh_out, dh0, db_last
+ * and dx_last may be NULL. */
+int m3o_scan_backward_ex(const m3o_dims* dm, const double* x, const double* dt, const double* A,
+                         int a_per_token, const double* lam, const double* theta, const double* B,
+                         const double* C, const double* D, const double* h0, const double* b_last,
+                         const double* x_last, const double* dy, const double* dh_out, double* dx,
+                         double* ddt, double* dA, double* dlam, double* dtheta, double* dB, double* dC,
+                         double* dD, double* dh0, double* db_last, double* dx_last, int nthreads) {
     if (!dm || !dy || !dx || !ddt || !dA || !dlam || !dtheta || !dB || !dC || !dD || dm->batch < 0 ||
         dm->seqlen < 0 || dm->nheads <= 0 || dm->ngroups <= 0 || dm->headdim <= 0 || dm->dstate <= 0 ||
         dm->rank <= 0 || dm->dstate % 2 != 0 || dm->nheads % dm->ngroups != 0)
@@ -471,7 +482,7 @@ int m3o_scan_backward(const m3o_dims* dm, const double* x, const double* dt, con
 #endif
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t b = 0; b < b_; ++b) {
-        const int rc = backward_batch(dm, b, x, dt, A, lam, theta, B, C, D, h0, b_last, x_last, dy,
+        const int rc = backward_batch(dm, b, x, dt, A, a_per_token, dA, lam, theta, B, C, D, h0, b_last, x_last, dy,
                                       dh_out, dx, ddt, partial + b * H, dlam, dtheta, dB, dC,
                                       partial + (b_ + b) * H, dh0, db_last, dx_last);
         if (rc) {
@@ -485,9 +496,20 @@ int m3o_scan_backward(const m3o_dims* dm, const double* x, const double* dt, con
             a += partial[b * H + h];
             d += partial[(b_ + b) * H + h];
         }
-        dA[h] = a;
+        if (!a_per_token) dA[h] = a;
         dD[h] = d;
     }
     free(partial);
     return err;
+}
+
+/* m3o_scan_backward_ex with one decay rate per head. */
+int m3o_scan_backward(const m3o_dims* dm, const double* x, const double* dt, const double* A,
+                      const double* lam, const double* theta, const double* B, const double* C,
+                      const double* D, const double* h0, const double* b_last, const double* x_last,
+                      const double* dy, const double* dh_out, double* dx, double* ddt, double* dA,
+                      double* dlam, double* dtheta, double* dB, double* dC, double* dD, double* dh0,
+                      double* db_last, double* dx_last, int nthreads) {
+    return m3o_scan_backward_ex(dm, x, dt, A, 0, lam, theta, B, C, D, h0, b_last, x_last, dy, dh_out, dx, ddt,
+                                dA, dlam, dtheta, dB, dC, dD, dh0, db_last, dx_last, nthreads);
 }

@@ -23,11 +23,15 @@ def _objective(scan, d, st, dy, dho):
     return float(np.sum(dy * y) + np.sum(dho * h))
 
 
-def fd_check(scan, scan_backward, seed=0, b=2, L=7, H=4, G=2, P=3, N=4, R=2, eps=1e-6, with_state=True):
+def fd_check(scan, scan_backward, seed=0, b=2, L=7, H=4, G=2, P=3, N=4, R=2, eps=1e-6, with_state=True,
+             a_per_token=False):
     """Largest relative mismatch between <grad, v> and the central difference of the
-    objective along v, over every input (and the state, when given) and 3 random v each."""
+    objective along v, over every input (and the state, when given) and 3 random v each.
+    With a_per_token, A is a per-token decay rate (b, L, H) drawn like the per-head one."""
     d = rand_case(b=b, L=L, H=H, G=G, P=P, N=N, R=R, seed=seed, theta_scale=2.0)
     rng = np.random.default_rng(seed + 100)
+    if a_per_token:
+        d["A"] = -np.exp(rng.uniform(0.0, np.log(16.0), (b, L, H)))
     st = rand_state(d, seed=seed + 1) if with_state else None
     dy = rng.standard_normal(d["x"].shape)
     dho = rng.standard_normal((b, H, N, P))
@@ -132,11 +136,11 @@ BWD_MUTANTS = {
     "dtheta_without_beta_input": [("const double v0 = alpha * h0v + beta * u0, v1 = alpha * h1v + beta * u1;",
                                    "const double v0 = alpha * h0v, v1 = alpha * h1v;")],
     "dC_from_previous_state": [("a += ht[n * P + p] * dy[", "a += hp[n * P + p] * dy[")],
-    "ddt_missing_decay_chain": [("dbe * (1.0 - lv) * (alpha + dtv * A[h] * alpha)", "dbe * (1.0 - lv) * alpha")],
+    "ddt_missing_decay_chain": [("dbe * (1.0 - lv) * (alpha + dtv * a_th * alpha)", "dbe * (1.0 - lv) * alpha")],
     "dlam_sign": [("dlam[(b * L + t) * H + h] = -dbe * dtv * alpha + dgam * dtv;",
                    "dlam[(b * L + t) * H + h] = dbe * dtv * alpha + dgam * dtv;")],
-    "dA_drops_beta_path": [("dA_h += dal * dtv * alpha + dbe * (1.0 - lv) * dtv * dtv * alpha;",
-                            "dA_h += dal * dtv * alpha;")],
+    "dA_drops_beta_path": [("const double dA_t = dal * dtv * alpha + dbe * (1.0 - lv) * dtv * dtv * alpha;",
+                            "const double dA_t = dal * dtv * alpha;")],
     "skip_gradient_dropped": [("dx[xi] = D[h] * dy[xi];", "dx[xi] = 0.0;")],
     "carry_gradient_without_beta": [("for (int64_t i = 0; i < NP; ++i) dU[i] = beta_next * qn[i];",
                                      "for (int64_t i = 0; i < NP; ++i) dU[i] = qn[i];")],
@@ -163,3 +167,46 @@ def test_backward_mutant_is_caught(name, tmpdir_mod):
     bwd = functools.partial(oracle.scan_backward, lib_path=lib)
     e = fd_check(oracle.scan, bwd, seed=3)
     assert e > 1e-4, f"mutant {name} passed the finite-difference pin ({e:.2e})"
+
+
+def test_per_token_A_gradients_match_finite_differences():
+    """A per-token decay rate A_t (the discretisation's A_t): every gradient, dA per token
+    included, against central differences of the forward oracle run with the same A_t."""
+    assert fd_check(oracle.scan, oracle.scan_backward, seed=6, a_per_token=True) < 1e-6
+    assert fd_check(oracle.scan, oracle.scan_backward, seed=7, R=1, G=1, H=2, with_state=False,
+                    a_per_token=True) < 1e-6
+
+
+def test_per_token_A_constant_over_tokens_matches_per_head():
+    """A_t equal to A[h] at every token: the same gradients, and dA_t summed over batch and
+    tokens is the per-head dA."""
+    b, L, H, G, P, N, R = 2, 6, 4, 2, 3, 4, 2
+    d = rand_case(b=b, L=L, H=H, G=G, P=P, N=N, R=R, seed=12, theta_scale=2.0)
+    st = rand_state(d, seed=13)
+    rng = np.random.default_rng(3)
+    dy = rng.standard_normal(d["x"].shape)
+    dho = rng.standard_normal((b, H, N, P))
+    g1 = oracle.scan_backward(*_args(d), dy, dh_out=dho, state_in=st)
+    dt_ = dict(d)
+    dt_["A"] = np.broadcast_to(d["A"], (b, L, H)).copy()
+    g2 = oracle.scan_backward(*[dt_[k] for k in NAMES], dy, dh_out=dho, state_in=st)
+    for k in ("dx", "ddt", "dlam", "dtheta", "dB", "dC", "dD", "dh0", "db_last", "dx_last"):
+        np.testing.assert_allclose(g2[k], g1[k], rtol=1e-12, atol=1e-12)
+    assert g2["dA"].shape == (b, L, H)
+    np.testing.assert_allclose(g2["dA"].sum(axis=(0, 1)), g1["dA"], rtol=1e-12, atol=1e-12)
+
+
+def test_per_token_A_mutant_is_caught(tmpdir_mod):
+    """A reverse sweep that reads the per-head slot of A instead of the token's rate."""
+    src = open(SRC).read()
+    old = ("const double a_th = a_per_token ? A[(b * L + t) * H + h] : A[h];\n"
+           "            const double alpha = exp(dtv * a_th), beta = (1.0 - lv) * dtv * alpha, gamma = lv * dtv;\n"
+           "            const double* ht = hall + (t + 1) * NP;")
+    assert src.count(old) == 1
+    src = src.replace(old, old.replace("a_per_token ? A[(b * L + t) * H + h] : A[h]", "A[h]"))
+    path = os.path.join(tmpdir_mod, "a_tok.c")
+    with open(path, "w") as f:
+        f.write(src)
+    lib = oracle.build(force=True, src=path, out=os.path.join(tmpdir_mod, "liba_tok.so"))
+    bwd = functools.partial(oracle.scan_backward, lib_path=lib)
+    assert fd_check(oracle.scan, bwd, seed=6, a_per_token=True) > 1e-4

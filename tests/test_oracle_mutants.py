@@ -38,8 +38,10 @@ MUTANTS = {
                           ("double* h0r = hs + (2 * k) * P;", "double* h0r = hs + (k) * P;")],
     "angle_of_wrong_group": [("const double th = theta[((b * L + t) * G + g) * K + k];",
                               "const double th = theta[((b * L + t) * G + (h % G)) * K + k];")],
-    "decay_of_wrong_head": [("const double a_th = a_per_token ? A[(b * L + t) * H + h] : A[h];",
-                             "const double a_th = a_per_token ? A[(b * L + t) * H + h] : A[g];")],
+    "decay_of_wrong_head": [("const double a_th = a_per_token ? A[(b * L + t) * H + h] : A[h];\n"
+                             "        const double alpha = exp(dtv * a_th);",
+                             "const double a_th = a_per_token ? A[(b * L + t) * H + h] : A[g];\n"
+                             "        const double alpha = exp(dtv * a_th);")],
     "C_transposed_rank": [("acc += C[IDX5(b, t, g, r, n, L, G, R, N)] * hs[n * P + p];",
                            "acc += C[IDX5(b, t, g, (n % R), (r * (N / R) + n / R) % N, L, G, R, N)] * hs[n * P + p];")],
     "B_read_for_C": [("acc += C[IDX5(b, t, g, r, n, L, G, R, N)] * hs[n * P + p];",
