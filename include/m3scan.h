@@ -220,7 +220,7 @@ m3_status m3_decode_step_fused(const m3_dims* dims, void* h, const void* b_last,
 typedef struct {
     float* dx;       /* (batch, L, H, R, P)                                        */
     float* ddt;      /* (batch, L, H)                                              */
-    float* dA;       /* (H): summed over batch and tokens                         */
+    float* dA;       /* (H): summed over batch and tokens (per token: m3_backward_per_token_A) */
     float* dlambda;  /* (batch, L, H)                                              */
     float* dtheta;   /* (batch, L, G, N/2): summed over the heads of each group    */
     float* dB;       /* (batch, L, G, R, N): summed over the heads of each group   */
@@ -302,6 +302,26 @@ m3_status m3_backward_varlen(const m3_dims* dims, const int64_t* cu_seqlens, int
                              const float* theta, const void* B, const void* C, const float* D,
                              const m3_state* state_in, const void* dy, const float* dh_out,
                              const m3_grads* grads, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * m3_backward (cu_seqlens NULL) or m3_backward_varlen (cu_seqlens non-NULL) with a
+ * per-token decay rate A_t in place of the per-head A: the discretisation of the
+ * Mamba-3 paper note ("Solution 1") gives each token its own A_t, so the decay is
+ * exp(dt_t A_t) (as m3_prefill_fused computes with fusion->A_t).
+ *
+ * A_t:       fp32, (batch, L, H), or (total_tokens, H) with cu_seqlens.
+ * grads->dA: per token, in A_t's layout (not summed); with cu_seqlens, rows of
+ *            tokens that belong to no sequence are left undefined.
+ * total_tokens is read only with cu_seqlens.  Every other argument, the workspace
+ * size and the errors as the call it stands for; also M3_ERR_INVALID_ARG for a
+ * NULL A_t.
+ */
+m3_status m3_backward_per_token_A(const m3_dims* dims, const int64_t* cu_seqlens, int64_t total_tokens,
+                                  const void* x, const float* dt, const float* A_t, const float* lambda,
+                                  const float* theta, const void* B, const void* C, const float* D,
+                                  const m3_state* state_in, const void* dy, const float* dh_out,
+                                  const m3_grads* grads, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /* Static text for a status code. */
 const char* m3_status_string(m3_status status);

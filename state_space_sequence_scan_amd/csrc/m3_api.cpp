@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int32_t kVersion = 106;  // 0.1.6: packed-batch backward
+constexpr int32_t kVersion = 107;  // 0.1.7: backward with a per-token decay rate
 constexpr size_t kMaxLds = 160 * 1024;
 
 bool dims_ok(const m3_dims* d, bool prefill) {
@@ -326,12 +326,12 @@ m3_status m3_backward_parts(const m3_dims* dims, int32_t* parts, int64_t* tokens
 namespace {
 
 m3_status backward_common(const m3_dims* dims, const int64_t* cu, int64_t total_tokens, const void* x,
-                          const float* dt, const float* A, const float* lambda, const float* theta,
+                          const float* dt, const float* A, const float* At, const float* lambda, const float* theta,
                           const void* B, const void* C, const float* D, const m3_state* state_in,
                           const void* dy, const float* dh_out, const m3_grads* grads, void* workspace,
                           size_t workspace_bytes, void* stream) {
     if (!dims_ok(dims, true) || !grads) return M3_ERR_INVALID_ARG;
-    if (!A || !D || !grads->dA || !grads->dD) return M3_ERR_INVALID_ARG;
+    if (!(A || At) || !D || !grads->dA || !grads->dD) return M3_ERR_INVALID_ARG;
     const bool any_tokens = (cu ? total_tokens : dims->batch * dims->seqlen) > 0;
     if (any_tokens && (!x || !dt || !lambda || !theta || !B || !C || !dy || !grads->dx || !grads->ddt ||
                        !grads->dlambda || !grads->dtheta || !grads->dB || !grads->dC))
@@ -346,7 +346,8 @@ m3_status backward_common(const m3_dims* dims, const int64_t* cu, int64_t total_
     m3::BwdArgs a{};
     a.x = x;
     a.dt = dt;
-    a.A = A;
+    a.A = At ? nullptr : A;
+    a.At = At;
     a.lam = lambda;
     a.theta = theta;
     a.B = B;
@@ -393,8 +394,8 @@ m3_status m3_backward(const m3_dims* dims, const void* x, const float* dt, const
                       const float* D, const m3_state* state_in, const void* dy,
                       const float* dh_out, const m3_grads* grads, void* workspace,
                       size_t workspace_bytes, void* stream) {
-    return backward_common(dims, nullptr, 0, x, dt, A, lambda, theta, B, C, D, state_in, dy, dh_out, grads,
-                           workspace, workspace_bytes, stream);
+    return backward_common(dims, nullptr, 0, x, dt, A, nullptr, lambda, theta, B, C, D, state_in, dy, dh_out,
+                           grads, workspace, workspace_bytes, stream);
 }
 
 m3_status m3_backward_varlen(const m3_dims* dims, const int64_t* cu_seqlens, int64_t total_tokens,
@@ -405,8 +406,24 @@ m3_status m3_backward_varlen(const m3_dims* dims, const int64_t* cu_seqlens, int
     if (!cu_seqlens || total_tokens < 0 || !dims) return M3_ERR_INVALID_ARG;
     // the workspace holds per-token partial gradients for batch * seqlen tokens
     if (dims->batch > 0 && dims->seqlen >= 0 && total_tokens > dims->batch * dims->seqlen) return M3_ERR_INVALID_ARG;
-    return backward_common(dims, cu_seqlens, total_tokens, x, dt, A, lambda, theta, B, C, D, state_in, dy,
-                           dh_out, grads, workspace, workspace_bytes, stream);
+    return backward_common(dims, cu_seqlens, total_tokens, x, dt, A, nullptr, lambda, theta, B, C, D, state_in,
+                           dy, dh_out, grads, workspace, workspace_bytes, stream);
+}
+
+m3_status m3_backward_per_token_A(const m3_dims* dims, const int64_t* cu_seqlens, int64_t total_tokens,
+                                  const void* x, const float* dt, const float* A_t, const float* lambda,
+                                  const float* theta, const void* B, const void* C, const float* D,
+                                  const m3_state* state_in, const void* dy, const float* dh_out,
+                                  const m3_grads* grads, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    if (!dims || !A_t) return M3_ERR_INVALID_ARG;
+    if (cu_seqlens) {
+        if (total_tokens < 0) return M3_ERR_INVALID_ARG;
+        if (dims->batch > 0 && dims->seqlen >= 0 && total_tokens > dims->batch * dims->seqlen)
+            return M3_ERR_INVALID_ARG;
+    }
+    return backward_common(dims, cu_seqlens, cu_seqlens ? total_tokens : 0, x, dt, nullptr, A_t, lambda, theta, B,
+                           C, D, state_in, dy, dh_out, grads, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

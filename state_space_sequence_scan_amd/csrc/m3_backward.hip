@@ -115,7 +115,7 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
     const SeqSpan span = seq_span(a.cu, b, a.L, a.T);
     const int64_t tb = span.start, L = span.len;
     const int H = a.H, G = a.G;
-    const float Ah = a.A[h], Dh = a.D[h];
+    const float Ah = a.At ? 0.f : a.A[h], Dh = a.D[h];   // Ah: the head's decay rate without At
     const int64_t nseg = (L + KS - 1) / KS;                    // segments of this sequence
     const int64_t nseg_max = (a.L + KS - 1) / KS;              // checkpoint slots per (b, h)
     const int64_t s_lo = part * a.seg_per_part;
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
     __shared__ __align__(16) T sDY[KS + 1][R * P];
     __shared__ __align__(16) float sTh[KS + 1][N / 2];
     __shared__ __align__(16) float sRot[KS + 1][N];             // cos, sin of each pair's angle
-    __shared__ float sDt[KS + 1], sLam[KS + 1];
+    __shared__ float sDt[KS + 1], sLam[KS + 1], sAt[KS + 1];   // sAt: decay rate of each token
 
     auto soff = [&](int64_t t) { return (tb + t) * H + h; };
 
@@ -197,6 +197,7 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
             const int64_t t = t0 - 1 + tid;
             sDt[tid] = t >= 0 ? a.dt[soff(t)] : 0.f;
             sLam[tid] = t >= 0 ? a.lam[soff(t)] : 0.f;
+            sAt[tid] = t >= 0 ? (a.At ? a.At[soff(t)] : Ah) : 0.f;
         }
     };
     auto slot_bx = [&](int k, float (&Bv)[R][4], float (&Xv)[R][4]) {
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
     };
     auto coeffs = [&](int k, float* al, float* be, float* ga, float* sn, float* cs) {
         const float dtv = sDt[k], lv = sLam[k];
-        *al = __expf(dtv * Ah);
+        *al = __expf(dtv * sAt[k]);
         *be = (1.f - lv) * dtv * *al;
         *ga = lv * dtv;
         const float4 rot = *reinterpret_cast<const float4*>(&sRot[k][4 * pb]);   // pairs 2pb, 2pb+1
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
             if (tid < N / 2) {
                 for (int j = 1; j <= len; ++j) sum += static_cast<double>(sTh[j][tid]);
             } else if (tid == N / 2) {
-                for (int j = 1; j <= len; ++j) sum += static_cast<double>(sDt[j] * Ah);
+                for (int j = 1; j <= len; ++j) sum += static_cast<double>(sDt[j] * sAt[j]);
             }
         }
         store_state(hs, a.hloc + pidx * N * P, P);
@@ -364,7 +365,7 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
     if (s_hi < nseg) {
         const int64_t tn = s_hi * KS;
         const float dtv = a.dt[soff(tn)], lv = a.lam[soff(tn)];
-        an = __expf(dtv * Ah);
+        an = __expf(dtv * (a.At ? a.At[soff(tn)] : Ah));
         bn = (1.f - lv) * dtv * an;
     }
     float dA_acc = 0.f, dD_acc = 0.f;   // thread 0
@@ -539,10 +540,12 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
                     sg += sSc[par][w2][2];
                     sd += sSc[par][w2][3];
                 }
-                const float dtv = sDt[k], lv = sLam[k];
-                a.ddt[soff(t)] = sa * Ah * al + sb * (1.f - lv) * (al + dtv * Ah * al) + sg * lv;
+                const float dtv = sDt[k], lv = sLam[k], av = sAt[k];
+                a.ddt[soff(t)] = sa * av * al + sb * (1.f - lv) * (al + dtv * av * al) + sg * lv;
                 a.dlam[soff(t)] = -sb * dtv * al + sg * dtv;
-                dA_acc += sa * dtv * al + sb * (1.f - lv) * dtv * dtv * al;
+                const float dav = sa * dtv * al + sb * (1.f - lv) * dtv * dtv * al;
+                if (a.At) a.dA[soff(t)] = dav;   // per-token rate: its own gradient
+                else dA_acc += dav;
                 dD_acc += sd;
             }
             an = al;
@@ -628,11 +631,13 @@ __global__ __launch_bounds__(NT) void bwd_combine(BwdArgs a) {
     const int tid = threadIdx.x, cb = tid & 15, pb = tid >> 4;
     const int r0 = 4 * pb, c0 = 4 * cb;
     const int S = a.parts;
-    const float Ah = a.A[h];
+    const float Ah = a.At ? 0.f : a.A[h];
     const int64_t tok_per_part = a.seg_per_part * KS;
     const SeqSpan span = seq_span(a.cu, b, a.L, a.T);   // a packed sequence may leave trailing parts empty
     auto dta = [&](int64_t t) {   // dt A at token t of the sequence; 0 (alpha = 1) past its end
-        return t < span.len ? static_cast<double>(a.dt[(span.start + t) * a.H + h] * Ah) : 0.0;
+        if (t >= span.len) return 0.0;
+        const int64_t i = (span.start + t) * a.H + h;
+        return static_cast<double>(a.dt[i] * (a.At ? a.At[i] : Ah));
     };
     auto slot = [&](float* base, int p) { return base + ((static_cast<size_t>(bh) * S + p) * N + r0) * P + c0; };
     auto ld16 = [&](const float* p, float (&v)[4][4]) {
@@ -730,7 +735,7 @@ __global__ __launch_bounds__(256) void bwd_head_sum(const float* __restrict__ dA
             sa += dA_part[(static_cast<size_t>(b) * H + h) * parts + p];
             sd += dD_part[(static_cast<size_t>(b) * H + h) * parts + p];
         }
-    dA[h] = sa;
+    if (dA) dA[h] = sa;   // null with a per-token rate, whose dA the scan writes
     dD[h] = sd;
 }
 
@@ -875,7 +880,7 @@ hipError_t launch_backward(BwdArgs a, const BwdLayout& l, hipStream_t st) {
         const int64_t n = a.batch * a.G * a.R * a.N;
         bw::bwd_fill_zero<<<static_cast<unsigned>(n / 256 + 1 < 4096 ? n / 256 + 1 : 4096), 256, 0, st>>>(a.dbl, n);
     }
-    bw::bwd_head_sum<<<(a.H + 255) / 256, 256, 0, st>>>(a.dA_part, a.dD_part, a.dA, a.dD, static_cast<int>(a.batch), a.H,
+    bw::bwd_head_sum<<<(a.H + 255) / 256, 256, 0, st>>>(a.dA_part, a.dD_part, a.At ? nullptr : a.dA, a.dD, static_cast<int>(a.batch), a.H,
                                                       l.parts);
     return hipGetLastError();
 }

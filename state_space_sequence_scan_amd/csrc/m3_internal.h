@@ -117,7 +117,8 @@ void backward_parts(const BwdShape& s, int* parts, int64_t* seg_per_part);
 struct BwdArgs {
     const void* x;
     const float* dt;
-    const float* A;
+    const float* A;           // per head; unused when At is given
+    const float* At;          // per-token decay rate (tokens, H), or null
     const float* lam;
     const float* theta;
     const void* B;
@@ -130,7 +131,7 @@ struct BwdArgs {
     const float* dh_out;      // may be null
     float* dx;
     float* ddt;
-    float* dA;
+    float* dA;                // (H), or per token (tokens, H) when At is given
     float* dlam;
     float* dtheta;
     float* dB;

@@ -90,6 +90,9 @@ def lib(path: str = LIB_PATH):
     L.m3_backward_varlen.restype = ctypes.c_int
     L.m3_backward_varlen.argtypes = ([ctypes.POINTER(Dims), vp, ctypes.c_int64] + [vp] * 8 +
                                      [ctypes.POINTER(State), vp, vp, ctypes.POINTER(Grads), vp, sz, vp])
+    L.m3_backward_per_token_A.restype = ctypes.c_int
+    L.m3_backward_per_token_A.argtypes = ([ctypes.POINTER(Dims), vp, ctypes.c_int64] + [vp] * 8 +
+                                          [ctypes.POINTER(State), vp, vp, ctypes.POINTER(Grads), vp, sz, vp])
     L.m3_backward_parts.restype = ctypes.c_int
     L.m3_backward_parts.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(ctypes.c_int32),
                                     ctypes.POINTER(ctypes.c_int64)]
@@ -336,10 +339,11 @@ def _backward_state(state_in, nb, H, G, N, P, R, io, dev):
                  None if state_in.x_last is None else state_in.x_last.data_ptr()), state_dtype
 
 
-def _backward_grads(lead, nb, H, G, N, P, R, want_state_grads, grads, dev):
+def _backward_grads(lead, nb, H, G, N, P, R, want_state_grads, grads, dev, dA_per_token=False):
     """Output tensors of a backward call (per-token ones with leading shape `lead`)."""
     f32 = dict(dtype=torch.float32, device=dev)
-    shapes = {"dx": lead + (H, R, P), "ddt": lead + (H,), "dA": (H,), "dlam": lead + (H,),
+    shapes = {"dx": lead + (H, R, P), "ddt": lead + (H,), "dA": lead + (H,) if dA_per_token else (H,),
+              "dlam": lead + (H,),
               "dtheta": lead + (G, N // 2), "dB": lead + (G, R, N), "dC": lead + (G, R, N), "dD": (H,)}
     if want_state_grads:
         shapes.update({"dh0": (nb, H, N, P), "db_last": (nb, G, R, N), "dx_last": (nb, H, R, P)})
@@ -525,3 +529,53 @@ def decode_step_fused(state: DecodeState, x_t, dt_t, A, lam_t, theta_t, B_t, C_t
     if advance:
         state.b_last, state.x_last = B_t, x_t
     return y_t
+
+
+def backward_per_token_A(x, dt, A_t, lam, theta, B, C, D, dy, cu_seqlens=None, max_seqlen: Optional[int] = None,
+                         dh_out=None, state_in: Optional[DecodeState] = None, want_state_grads: bool = True,
+                         workspace: Optional[torch.Tensor] = None, grads: Optional[dict] = None):
+    """Backward pass with a per-token decay rate A_t (m3_backward_per_token_A): the
+    layouts of ``backward`` (cu_seqlens None) or ``backward_varlen`` (cu_seqlens and
+    max_seqlen given), with A_t fp32 shaped like dt; dA is returned per token, shaped
+    like A_t.  Returns the dict of ``backward``."""
+    packed = cu_seqlens is not None
+    lead = tuple(x.shape[:-3])
+    if len(lead) != (1 if packed else 2):
+        raise ValueError(f"x: {x.dim()} dimensions, expected {4 if packed else 5}")
+    H, R, P = x.shape[-3:]
+    G, N = B.shape[-3], B.shape[-1]
+    dev, io = x.device, x.dtype
+    if io not in _IO:
+        raise ValueError(f"x dtype {io} not supported (fp32 or bf16)")
+    if packed:
+        nseq = cu_seqlens.shape[0] - 1
+        if nseq < 1:
+            raise ValueError("cu_seqlens needs at least two entries")
+        if max_seqlen is None:
+            raise ValueError("max_seqlen is needed with cu_seqlens")
+        _check(cu_seqlens, "cu_seqlens", (nseq + 1,), torch.int64, dev)
+        nb, L = nseq, max_seqlen
+    else:
+        nb, L = lead
+    _check(x, "x", lead + (H, R, P), io, dev)
+    _check(dy, "dy", lead + (H, R, P), io, dev)
+    _check(dt, "dt", lead + (H,), torch.float32, dev)
+    _check(A_t, "A_t", lead + (H,), torch.float32, dev)
+    _check(lam, "lam", lead + (H,), torch.float32, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(theta, "theta", lead + (G, N // 2), torch.float32, dev)
+    _check(B, "B", lead + (G, R, N), io, dev)
+    _check(C, "C", lead + (G, R, N), io, dev)
+    if dh_out is not None:
+        _check(dh_out, "dh_out", (nb, H, N, P), torch.float32, dev)
+    sin, state_dtype = _backward_state(state_in, nb, H, G, N, P, R, io, dev)
+    dims = make_dims(nb, L, H, G, P, N, R, 1, _IO[io], _IO[state_dtype])
+    out, gs = _backward_grads(lead, nb, H, G, N, P, R, want_state_grads, grads, dev, dA_per_token=True)
+    ws, workspace = _backward_workspace(dims, workspace, dev)
+    rc = lib().m3_backward_per_token_A(ctypes.byref(dims), _p(cu_seqlens), lead[0] if packed else 0, _p(x),
+                                       _p(dt), _p(A_t), _p(lam), _p(theta), _p(B), _p(C), _p(D),
+                                       None if sin is None else ctypes.byref(sin), _p(dy), _p(dh_out),
+                                       ctypes.byref(gs), _p(workspace) if ws > 0 else None, ws, _stream(dev))
+    if rc != 0:
+        raise M3Error("m3_backward_per_token_A", rc)
+    return out

@@ -28,7 +28,7 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_symbols() == ["m3_backward", "m3_backward_parts", "m3_backward_varlen",
+    assert declared_symbols() == ["m3_backward", "m3_backward_parts", "m3_backward_per_token_A", "m3_backward_varlen",
                                   "m3_backward_workspace_size", "m3_decode_step",
                                   "m3_decode_step_fused", "m3_prefill_chunked", "m3_prefill_fused",
                                   "m3_prefill_varlen", "m3_prefill_workspace_size", "m3_status_string",
@@ -304,3 +304,22 @@ def test_backward_varlen_rejects_bad_arguments(lib):
     small = _dims(batch=3, seqlen=10)         # N = 16, P = 16: no backward kernel
     assert lib.m3_backward_varlen(ctypes.byref(small), FAKE, 20, *([FAKE] * 8), None, FAKE, None,
                                   ctypes.byref(_grads()), None, 0, None) == -2
+
+
+def test_backward_per_token_A_rejects_bad_arguments(lib):
+    """Backward with a per-token decay rate: a NULL A_t is an argument error; without
+    cu_seqlens the token count is ignored, with it the packed-batch bounds apply.  No call
+    here reaches a launch."""
+    d = _dims(batch=3, seqlen=10, nheads=4, ngroups=2, headdim=64, dstate=128, rank=2, io_dtype=m3scan.M3_BF16)
+    def call(cu=FAKE, T=20, args=None):
+        args = [FAKE] * 8 if args is None else args
+        return lib.m3_backward_per_token_A(ctypes.byref(d), cu, T, *args, None, FAKE, None,
+                                           ctypes.byref(_grads()), None, 0, None)
+    args = [FAKE] * 8
+    args[2] = None                            # A_t
+    assert call(args=args) == -1
+    assert call(cu=None, args=args) == -1
+    assert call(T=-1) == -1
+    assert call(T=31) == -1
+    assert call(cu=None, T=-1) == -3          # T unused without cu_seqlens: only the workspace is missing
+    assert call(T=30) == -3
