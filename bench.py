@@ -47,7 +47,8 @@ def parse():
                          "(default workload for it: nanomamba3, the training shape)")
     ap.add_argument("--fused", action="store_true",
                     help="run the fused layer prologue/epilogue (m3_prefill_fused, m3_decode_step_fused): "
-                         "per-token A, RMSNorm and bias of B and C, output gate")
+                         "per-token A, RMSNorm and bias of B and C, output gate; with --backward, the "
+                         "backward with a per-token decay rate A_t (m3_backward_per_token_A)")
     ap.add_argument("--varlen", action="store_true",
                     help="pack the batch's sequences with seeded lengths uniform in [L/4, L] "
                          "(m3_prefill_varlen; with --backward, m3_backward_varlen) instead of equal lengths L")
@@ -450,6 +451,8 @@ def run_backward(args, cfg):
     d = inputs.draw_config(cfg, device=dev)
     gen = torch.Generator(device=dev).manual_seed(cfg.seed + 11)
     dy = torch.randn(d["x"].shape, generator=gen, device=dev).to(d["x"].dtype)
+    if args.fused:   # per-token decay rate A_t, drawn like the per-head rates: -exp(U(0, ln 16))
+        d["At"] = -torch.exp(torch.rand(d["dt"].shape, generator=gen, device=dev) * math.log(16.0))
     dims = m3scan.make_dims(cfg.batch, L, cfg.nheads, cfg.ngroups, cfg.headdim, cfg.dstate, cfg.rank,
                             1, m3scan.M3_BF16 if cfg.io_dtype == "bf16" else m3scan.M3_F32)
     ws = torch.empty(m3scan.backward_workspace_size(dims), dtype=torch.uint8, device=dev)
@@ -462,10 +465,17 @@ def run_backward(args, cfg):
               for k, v in list(d.items()) + [("dy", dy)] if v.dim() > 1}
 
         def bwd(g=None):
+            if args.fused:
+                return m3scan.backward_per_token_A(*[dp["At"] if k == "A" else dp[k] if k in dp else d[k]
+                                                     for k in names], dp["dy"], cu_seqlens=cu, max_seqlen=L,
+                                                   workspace=ws, grads=g, want_state_grads=False)
             return m3scan.backward_varlen(*[dp[k] if k in dp else d[k] for k in names], dp["dy"], cu, L,
                                           workspace=ws, grads=g, want_state_grads=False)
     else:
         def bwd(g=None):
+            if args.fused:
+                return m3scan.backward_per_token_A(*[d["At"] if k == "A" else d[k] for k in names], dy,
+                                                   workspace=ws, grads=g, want_state_grads=False)
             return m3scan.backward(*[d[k] for k in names], dy, workspace=ws, grads=g, want_state_grads=False)
     grads = bwd()
     torch.cuda.synchronize()
@@ -489,11 +499,12 @@ def run_backward(args, cfg):
     flops = backward_flops(cfg, L) * tokens / (cfg.batch * L)
     nbytes = backward_bytes(cfg, L) * tokens / (cfg.batch * L)
     tflops = flops / (ms / 1e3) / 1e12
-    traffic = pmc_traffic(f"backward_{args.workload}{'_varlen' if args.varlen else ''}_hbm_counters.json",
+    traffic = pmc_traffic(f"backward_{args.workload}{'_varlen' if args.varlen else ''}"
+                          f"{'_per_token_A' if args.fused else ''}_hbm_counters.json",
                           ["m3_backward.hip", "m3_common.h"], nbytes)
     parts, tpp = m3scan.backward_parts(dims)
     passes = "local + combine + " if parts > 1 else ""
-    roof = {"kernel": f"{passes}bwd_scan<io {cfg.io_dtype}, R{cfg.rank}> + group sums "
+    roof = {"kernel": f"{passes}bwd_scan<io {cfg.io_dtype}, R{cfg.rank}{', per-token A' if args.fused else ''}> + group sums "
                       f"({parts} pieces of {tpp} tokens per (b, h))", "bound": "alu",
             "achieved": round(tflops, 3), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / FP32_VALU_PEAK_TFLOPS, 4), "traffic": traffic,
@@ -517,11 +528,13 @@ def run_backward(args, cfg):
                 return {"x": f(dp["x"][s0:s1, h:h + 1][None]), "dt": f(dp["dt"][s0:s1, h:h + 1][None]),
                         "lam": f(dp["lam"][s0:s1, h:h + 1][None]), "theta": f(dp["theta"][s0:s1, g:g + 1][None]),
                         "B": f(dp["B"][s0:s1, g:g + 1][None]), "C": f(dp["C"][s0:s1, g:g + 1][None]),
-                        "A": f(d["A"][h:h + 1]), "D": f(d["D"][h:h + 1]), "dy": f(dp["dy"][s0:s1, h:h + 1][None])}
+                        "A": f(dp["At"][s0:s1, h:h + 1][None]) if args.fused else f(d["A"][h:h + 1]),
+                        "D": f(d["D"][h:h + 1]), "dy": f(dp["dy"][s0:s1, h:h + 1][None])}
             return {"x": f(d["x"][bi:bi + 1, :, h:h + 1]), "dt": f(d["dt"][bi:bi + 1, :, h:h + 1]),
                     "lam": f(d["lam"][bi:bi + 1, :, h:h + 1]), "theta": f(d["theta"][bi:bi + 1, :, g:g + 1]),
                     "B": f(d["B"][bi:bi + 1, :, g:g + 1]), "C": f(d["C"][bi:bi + 1, :, g:g + 1]),
-                    "A": f(d["A"][h:h + 1]), "D": f(d["D"][h:h + 1]), "dy": f(dy[bi:bi + 1, :, h:h + 1])}
+                    "A": f(d["At"][bi:bi + 1, :, h:h + 1]) if args.fused else f(d["A"][h:h + 1]),
+                    "D": f(d["D"][h:h + 1]), "dy": f(dy[bi:bi + 1, :, h:h + 1])}
 
         if args.check_slices > 0:
             rng = np.random.default_rng(cfg.seed)
@@ -548,8 +561,10 @@ def run_backward(args, cfg):
             sl = [slice_inputs(i // cfg.nheads % cfg.batch, i % cfg.nheads, packed=False) for i in range(n)]
             st = {k: np.concatenate([s[k] for s in sl], axis=0) for k in ("x", "dt", "lam", "theta", "B", "C", "dy")}
             t1 = time.perf_counter()
-            # A, D differ per slice's head; the sample uses head 0's values for all (same cost)
-            oracle.scan_backward(st["x"], st["dt"], sl[0]["A"], st["lam"], st["theta"], st["B"], st["C"],
+            # A (per head), D differ per slice's head; the sample uses head 0's values for all (same
+            # cost).  A per-token A_t is each slice's own.
+            a_cpu = np.concatenate([s["A"] for s in sl], axis=0) if args.fused else sl[0]["A"]
+            oracle.scan_backward(st["x"], st["dt"], a_cpu, st["lam"], st["theta"], st["B"], st["C"],
                                  sl[0]["D"], st["dy"], nthreads=threads)
             sec = time.perf_counter() - t1
             cpu = {"value": round(n * L / cfg.nheads / sec, 2), "unit": "tokens/s", "cores": threads,
@@ -565,6 +580,7 @@ def run_backward(args, cfg):
         "data": "synthetic (seeded torch generators on the GPU; distributions of the workload; "
                 "dy ~ N(0,1))",
         "config": {"workload": cfg.label + "; backward pass (gradients of every input)"
+                               + ("; per-token decay rate A_t" if args.fused else "")
                                + (f"; packed lengths uniform in [{max(L // 4, 1)}, {L}], {tokens} tokens"
                                   if args.varlen else ""), "name": cfg.name,
                    "batch": cfg.batch, "seqlen": L, "heads": cfg.nheads, "groups": cfg.ngroups,
