@@ -32,8 +32,9 @@
 //              state contraction reads Bt^T straight from the token-major Bt tile
 //              in LDS with the transposing 64-bit LDS read of gfx950.
 //              In state-only mode (segment summaries) only the S update runs.
-//  seg_pass    one workgroup per (b, h): combines the segment summaries into the
-//              state entering each segment (sequential over segments).
+//  seg_pass    one thread per (b, h, rotation pair, column): carries the pair
+//              through the segment summaries, giving the state entering each
+//              segment (sequential over segments).
 #include "m3_common.h"
 #include "m3_internal.h"
 
@@ -1000,30 +1001,45 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
 // ------------------------------------------------------------------------------------
 template <int R>
 __global__ __launch_bounds__(NT) void seg_pass(ScanParams p, float* __restrict__ s_init) {
+    // One thread per (rotation pair k, column): blockIdx.y picks NT of the KP * P of them, so
+    // each thread carries one pair through the segments.  The next segment's summary is
+    // loaded before the current one is applied, keeping a load in flight across the chain.
     const int bh = blockIdx.x;
     const int b = bh / p.H, h = bh - b * p.H, g = h / (p.H / p.G);
+    const int idx = blockIdx.y * NT + threadIdx.x;   // < KP * P: the grid's y extent is KP * P / NT
+    const int k = idx / P, col = idx - k * P;
     const SeqSpan sp = seq_span(p.cu, b, p.L, p.T);
     const float c1 = (sp.len > 0 && p.bl_in && p.xl_in)
                          ? (1.f - p.lam[sp.start * p.H + h]) * p.dt[sp.start * p.H + h]
                          : 0.f;
-    for (int idx = threadIdx.x; idx < KP * P; idx += NT) {
-        const int k = idx / P, col = idx - k * P;
-        float s0 = initial_state<R>(p, b, h, g, 2 * k, col, c1);
-        float s1 = initial_state<R>(p, b, h, g, 2 * k + 1, col, c1);
-        for (int s = 0; s < p.nseg; ++s) {
-            float* out = s_init + ((static_cast<size_t>(bh) * p.nseg + s) * N) * P;
-            out[(2 * k) * P + col] = s0;
-            out[(2 * k + 1) * P + col] = s1;
-            if (s == p.nseg - 1) break;
-            const size_t sidx = static_cast<size_t>(bh) * (p.nseg - 1) + s;
-            const float dec = __expf(p.seg_decay[sidx]);
-            const float cn = p.seg_rot[sidx * KP * 2 + 2 * k], sn = p.seg_rot[sidx * KP * 2 + 2 * k + 1];
-            const float* ds = p.seg_state + sidx * N * P;
-            const float n0 = dec * (cn * s0 - sn * s1) + ds[(2 * k) * P + col];
-            const float n1 = dec * (sn * s0 + cn * s1) + ds[(2 * k + 1) * P + col];
-            s0 = n0;
-            s1 = n1;
-        }
+    const float* __restrict__ seg_state = p.seg_state;
+    const float* __restrict__ seg_rot = p.seg_rot;
+    const float* __restrict__ seg_decay = p.seg_decay;
+    const size_t sbase = static_cast<size_t>(bh) * (p.nseg - 1);
+    auto summary = [&](int s, float* d, float* cn, float* sn, float* ds0, float* ds1) {
+        const size_t sidx = sbase + s;
+        *d = seg_decay[sidx];
+        *cn = seg_rot[sidx * KP * 2 + 2 * k];
+        *sn = seg_rot[sidx * KP * 2 + 2 * k + 1];
+        const float* ds = seg_state + sidx * N * P;
+        *ds0 = ds[(2 * k) * P + col];
+        *ds1 = ds[(2 * k + 1) * P + col];
+    };
+    float s0 = initial_state<R>(p, b, h, g, 2 * k, col, c1);
+    float s1 = initial_state<R>(p, b, h, g, 2 * k + 1, col, c1);
+    float d = 0.f, cn = 1.f, sn = 0.f, ds0 = 0.f, ds1 = 0.f;
+    if (p.nseg > 1) summary(0, &d, &cn, &sn, &ds0, &ds1);
+    for (int s = 0; s < p.nseg; ++s) {
+        float* out = s_init + ((static_cast<size_t>(bh) * p.nseg + s) * N) * P;
+        out[(2 * k) * P + col] = s0;
+        out[(2 * k + 1) * P + col] = s1;
+        if (s == p.nseg - 1) break;
+        const float dec = __expf(d), c = cn, si = sn, a0 = ds0, a1 = ds1;
+        if (s + 1 < p.nseg - 1) summary(s + 1, &d, &cn, &sn, &ds0, &ds1);
+        const float n0 = dec * (c * s0 - si * s1) + a0;
+        const float n1 = dec * (si * s0 + c * s1) + a1;
+        s0 = n0;
+        s1 = n1;
     }
 }
 
@@ -1155,7 +1171,9 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
                            dim3(64 * NW), 0, st, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         float* s_init = reinterpret_cast<float*>(base + ws.s_init);
-        hipLaunchKernelGGL((mf::seg_pass<R>), dim3(static_cast<unsigned>(a.batch * a.H)), dim3(mf::NT), 0, st, p,
+        static_assert((mf::KP * mf::P) % mf::NT == 0, "seg_pass grid");
+        hipLaunchKernelGGL((mf::seg_pass<R>), dim3(static_cast<unsigned>(a.batch * a.H), (mf::KP * mf::P) / mf::NT),
+                           dim3(mf::NT), 0, st, p,
                            s_init);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         p.s_init = s_init;
