@@ -56,7 +56,10 @@ static void add_carry_room(const PrefillArgs& a, PrefillPlan* p) {
 }
 
 PrefillPlan plan_prefill(const PrefillArgs& a) {
-    PrefillPlan p{PrefillPath::Unsupported, 1, 0, 0, 0};
+    PrefillPlan p{};
+    p.path = PrefillPath::Unsupported;
+    p.nseg = 1;
+    p.state_split = 1;
     if (mfma_supported(a)) {
         plan_mfma(a, &p);
         add_carry_room(a, &p);

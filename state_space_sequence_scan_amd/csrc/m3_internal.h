@@ -78,6 +78,8 @@ enum class PrefillPath { Generic, Mfma, Unsupported };
 struct PrefillPlan {
     PrefillPath path;
     int nseg;                // segments per sequence (1 = one sweep per (b, h))
+    int chunks_per_seg;      // chunks of each segment (the last may be shorter)
+    int state_split;         // pieces each summarised segment is cut into for the state-only pass
     size_t workspace;        // bytes
     size_t lds;              // dynamic LDS bytes of the main kernel
     size_t carry_off;        // workspace offset of the normalised carried-in B (fused calls)

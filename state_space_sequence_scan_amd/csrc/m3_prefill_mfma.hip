@@ -243,7 +243,8 @@ struct ScanParams {
     const uint8_t* prep;    // prepared operands, per (b, g, chunk)
     uint16_t* y;            // (b, L, H, R, P) bf16
     uint16_t* y_sink;       // 64 x 64 bf16 scratch: stores of rows past the sequence end land here
-    const float* s_init;    // state entering segment s: (b, H, nseg, N, P) fp32, or null
+    const float* s_init;    // states entering the state-only pieces: (b, H, sinit_stride, N, P) fp32, or null;
+                            // segment s of the output pass starts from entry sinit_step * s
     const void* h_in;       // used when s_init is null (nseg == 1): (b, H, N, P), may be null
     const uint16_t* bl_in;  // carry in (b, G, R, N), may be null
     const uint16_t* xl_in;  // carry in (b, H, R, P), may be null
@@ -253,6 +254,7 @@ struct ScanParams {
     float* seg_rot;         // state-only mode: (b, H, nseg-1, KP, 2)
     int64_t L;              // sequence length (the maximum one with cu)
     int H, G, nchunks, nseg, chunks_per_seg;
+    int sinit_stride, sinit_step;
     int state_bf16;         // h_in and h_out hold bf16 (else fp32)
     const int64_t* cu;      // packed variable-length batch: sequence starts, or null
     int64_t T;              // tokens in the packed arrays
@@ -437,7 +439,8 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
                 for (int i = 0; i < 4; ++i) {
                     const int n = n0 + 16 * rt + 4 * lg + i, col = p0 + 16 * ct + l16;
                     sacc[rt][ct][i] =
-                        p.s_init ? p.s_init[((static_cast<size_t>(b) * p.H + h) * p.nseg + seg) * N * P + n * P + col]
+                        p.s_init ? p.s_init[((static_cast<size_t>(b) * p.H + h) * p.sinit_stride +
+                                             static_cast<size_t>(p.sinit_step) * seg) * N * P + n * P + col]
                                  : initial_state<R>(p, b, h, g, n, col, c1);
                 }
     } else {
@@ -1077,11 +1080,25 @@ static int choose_nseg(const PrefillArgs& a, int nchunks) {
     return static_cast<int>(nseg);
 }
 
+// The state-only pass runs one workgroup per (b, h, summarised segment).  When those leave
+// CUs idle (few (b, h) and few segments), each summarised segment is cut into `split`
+// pieces that are summarised side by side; the segment pass then chains the pieces, and
+// the output pass starts segment s from the state entering piece split * s.  Each piece
+// keeps at least 4 chunks.
+static int choose_state_split(const PrefillArgs& a, int nseg, int cps) {
+    constexpr int64_t kCUs = 256;
+    if (nseg < 2) return 1;
+    const int64_t slots = kCUs * (a.Q * a.R <= 64 ? 2 : 1);
+    int64_t f = slots / ((nseg - 1) * a.batch * a.H);
+    if (f > cps / 4) f = cps / 4;
+    return f < 1 ? 1 : static_cast<int>(f);
+}
+
 struct MfmaWs {
     size_t prep, sink, seg_state, seg_decay, seg_rot, s_init, total;
 };
 
-static MfmaWs mfma_ws(const PrefillArgs& a, int nchunks, int nseg) {
+static MfmaWs mfma_ws(const PrefillArgs& a, int nchunks, int nseg, int split) {
     MfmaWs w{};
     const mf::PrepLayout lay{a.Q * a.R};
     auto al = [](size_t v) { return (v + 255) & ~static_cast<size_t>(255); };
@@ -1092,14 +1109,15 @@ static MfmaWs mfma_ws(const PrefillArgs& a, int nchunks, int nseg) {
     off += al(64 * 64 * sizeof(uint16_t));
     const size_t bh = static_cast<size_t>(a.batch) * a.H;
     if (nseg > 1) {
+        const size_t pieces = static_cast<size_t>(split) * (nseg - 1);   // summarised pieces per (b, h)
         w.seg_state = off;
-        off += al(bh * (nseg - 1) * mf::N * mf::P * sizeof(float));
+        off += al(bh * pieces * mf::N * mf::P * sizeof(float));
         w.seg_decay = off;
-        off += al(bh * (nseg - 1) * sizeof(float));
+        off += al(bh * pieces * sizeof(float));
         w.seg_rot = off;
-        off += al(bh * (nseg - 1) * mf::KP * 2 * sizeof(float));
+        off += al(bh * pieces * mf::KP * 2 * sizeof(float));
         w.s_init = off;
-        off += al(bh * nseg * mf::N * mf::P * sizeof(float));
+        off += al(bh * (pieces + 1) * mf::N * mf::P * sizeof(float));
     }
     w.total = off;
     return w;
@@ -1109,13 +1127,16 @@ void plan_mfma(const PrefillArgs& a, PrefillPlan* plan) {
     const int nchunks = static_cast<int>((a.L + a.Q - 1) / a.Q);
     // packed variable-length batches run each sequence in one sweep
     int nseg = (nchunks > 0 && !a.cu) ? choose_nseg(a, nchunks) : 1;
-    if (nchunks > 0) {                       // no empty trailing segment
-        const int cps = (nchunks + nseg - 1) / nseg;
-        nseg = (nchunks + cps - 1) / cps;
-    }
+    int cps = nchunks > 0 ? (nchunks + nseg - 1) / nseg : 0;
+    int split = choose_state_split(a, nseg, cps);
+    if (split > 1) cps = split * ((cps + split - 1) / split);   // pieces of equal length
+    if (nchunks > 0) nseg = (nchunks + cps - 1) / cps;           // no empty trailing segment
+    if (nseg < 2) split = 1;
     plan->path = PrefillPath::Mfma;
     plan->nseg = nseg;
-    plan->workspace = mfma_ws(a, nchunks, nseg).total;
+    plan->chunks_per_seg = cps;
+    plan->state_split = split;
+    plan->workspace = mfma_ws(a, nchunks, nseg, split).total;
     plan->lds = 0;
 }
 
@@ -1127,10 +1148,10 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
     constexpr int NW = NB > 8 ? NB / 2 : (NB > 4 ? NB : 4);
     const int nchunks = static_cast<int>((a.L + a.Q - 1) / a.Q);
     if (nchunks == 0) return hipSuccess;
-    const int nseg = plan.nseg;
-    const int cps = (nchunks + nseg - 1) / nseg;
-    if (static_cast<int64_t>(nseg) * a.H * a.batch > 0x7fffffffLL) return hipErrorInvalidValue;
-    const MfmaWs ws = mfma_ws(a, nchunks, nseg);
+    const int nseg = plan.nseg, cps = plan.chunks_per_seg, split = plan.state_split;
+    const int pieces = split * (nseg - 1);   // summarised pieces per (b, h)
+    if (static_cast<int64_t>(nseg > pieces ? nseg : pieces) * a.H * a.batch > 0x7fffffffLL) return hipErrorInvalidValue;
+    const MfmaWs ws = mfma_ws(a, nchunks, nseg, split);
     uint8_t* base = static_cast<uint8_t*>(a.workspace);
 
     hipLaunchKernelGGL((mf::rope_prep<R, Q>), dim3(nchunks, a.G, static_cast<unsigned>(a.batch)), dim3(mf::NT), 0,
@@ -1164,19 +1185,25 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
     p.nseg = nseg;
     p.chunks_per_seg = cps;
     if (nseg > 1) {
-        p.seg_state = reinterpret_cast<float*>(base + ws.seg_state);
-        p.seg_decay = reinterpret_cast<float*>(base + ws.seg_decay);
-        p.seg_rot = reinterpret_cast<float*>(base + ws.seg_rot);
-        hipLaunchKernelGGL((mf::scan_mfma<R, Q, NW, false>), dim3(static_cast<unsigned>((nseg - 1) * a.H * a.batch)),
-                           dim3(64 * NW), 0, st, p);
+        // state-only pass and segment pass over the pieces (split per summarised segment)
+        mf::ScanParams ps = p;
+        ps.nseg = pieces + 1;
+        ps.chunks_per_seg = cps / split;
+        ps.seg_state = reinterpret_cast<float*>(base + ws.seg_state);
+        ps.seg_decay = reinterpret_cast<float*>(base + ws.seg_decay);
+        ps.seg_rot = reinterpret_cast<float*>(base + ws.seg_rot);
+        hipLaunchKernelGGL((mf::scan_mfma<R, Q, NW, false>), dim3(static_cast<unsigned>(pieces * a.H * a.batch)),
+                           dim3(64 * NW), 0, st, ps);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         float* s_init = reinterpret_cast<float*>(base + ws.s_init);
         static_assert((mf::KP * mf::P) % mf::NT == 0, "seg_pass grid");
         hipLaunchKernelGGL((mf::seg_pass<R>), dim3(static_cast<unsigned>(a.batch * a.H), (mf::KP * mf::P) / mf::NT),
-                           dim3(mf::NT), 0, st, p,
+                           dim3(mf::NT), 0, st, ps,
                            s_init);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         p.s_init = s_init;
+        p.sinit_stride = pieces + 1;
+        p.sinit_step = split;
     }
     hipLaunchKernelGGL((mf::scan_mfma<R, Q, NW, true>), dim3(static_cast<unsigned>(nseg * a.H * a.batch)),
                        dim3(64 * NW), 0, st, p);

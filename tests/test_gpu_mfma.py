@@ -23,6 +23,10 @@ CASES = [
     (3, 64, 2, 1, 2, 64, 1.0),       # exactly one chunk
     (1, 17, 2, 1, 1, 32, 1.0),       # shorter than a chunk
     (2, 512, 4, 1, 2, 32, 1.0),
+    # two segments whose summarised one is cut into two pieces for the state-only pass
+    # (few (b, h) pairs): the output pass starts segment 1 from the second piece's end
+    (2, 1100, 44, 1, 4, 64, 1.0),
+    (4, 600, 48, 2, 2, 32, 1.0),
 ]
 
 
