@@ -207,6 +207,17 @@ m3_status m3_prefill_fused(const m3_dims* dims, const void* x, const float* dt, 
                            m3_state* state_out, void* y, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* m3_prefill_varlen with the fused prologue/epilogue of `fusion` (non-NULL), on a packed
+ * batch: A_t is (total_tokens, H) and z is laid out as y, (total_tokens, H, R, P); a
+ * carried b_last of state_in (per sequence) is normalised like B.  Same workspace size
+ * (m3_prefill_workspace_size); the other arguments, layouts and errors as
+ * m3_prefill_varlen, plus those of m3_prefill_fused. */
+m3_status m3_prefill_varlen_fused(const m3_dims* dims, const int64_t* cu_seqlens, int64_t total_tokens,
+                                  const void* x, const float* dt, const float* A, const float* lambda,
+                                  const float* theta, const void* B, const void* C, const float* D,
+                                  const m3_fusion* fusion, const m3_state* state_in, m3_state* state_out,
+                                  void* y, void* workspace, size_t workspace_bytes, void* stream);
+
 /* m3_decode_step with the fused prologue/epilogue of `fusion` (non-NULL; z and A_t
  * have the step's shapes (batch, H, R, P) and (batch, H)).  The carry b_last is the
  * raw previous B, normalised here like B_t. */

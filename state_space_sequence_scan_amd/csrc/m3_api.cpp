@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int32_t kVersion = 107;  // 0.1.7: backward with a per-token decay rate
+constexpr int32_t kVersion = 108;  // 0.1.8: fused prologue/epilogue on packed batches
 constexpr size_t kMaxLds = 160 * 1024;
 
 bool dims_ok(const m3_dims* d, bool prefill) {
@@ -216,6 +216,16 @@ m3_status m3_prefill_varlen(const m3_dims* dims, const int64_t* cu_seqlens, int6
                             size_t workspace_bytes, void* stream) {
     if (!cu_seqlens || total_tokens < 0) return M3_ERR_INVALID_ARG;
     return prefill_common(dims, cu_seqlens, total_tokens, x, dt, A, lambda, theta, B, C, D, nullptr,
+                          state_in, state_out, y, workspace, workspace_bytes, stream);
+}
+
+m3_status m3_prefill_varlen_fused(const m3_dims* dims, const int64_t* cu_seqlens, int64_t total_tokens,
+                                  const void* x, const float* dt, const float* A, const float* lambda,
+                                  const float* theta, const void* B, const void* C, const float* D,
+                                  const m3_fusion* fusion, const m3_state* state_in, m3_state* state_out,
+                                  void* y, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!cu_seqlens || total_tokens < 0 || !fusion) return M3_ERR_INVALID_ARG;
+    return prefill_common(dims, cu_seqlens, total_tokens, x, dt, A, lambda, theta, B, C, D, fusion,
                           state_in, state_out, y, workspace, workspace_bytes, stream);
 }
 

@@ -83,6 +83,10 @@ def lib(path: str = LIB_PATH):
     L.m3_prefill_fused.restype = ctypes.c_int
     L.m3_prefill_fused.argtypes = ([ctypes.POINTER(Dims)] + [vp] * 8 + [ctypes.POINTER(Fusion)] +
                                    [ctypes.POINTER(State), ctypes.POINTER(State), vp, vp, sz, vp])
+    L.m3_prefill_varlen_fused.restype = ctypes.c_int
+    L.m3_prefill_varlen_fused.argtypes = ([ctypes.POINTER(Dims), vp, ctypes.c_int64] + [vp] * 8 +
+                                          [ctypes.POINTER(Fusion), ctypes.POINTER(State), ctypes.POINTER(State),
+                                           vp, vp, sz, vp])
     L.m3_decode_step_fused.restype = ctypes.c_int
     L.m3_decode_step_fused.argtypes = [ctypes.POINTER(Dims)] + [vp] * 11 + [ctypes.POINTER(Fusion), vp, vp]
     L.m3_backward_workspace_size.restype = ctypes.c_int
@@ -253,6 +257,26 @@ def prefill_varlen(x, dt, A, lam, theta, B, C, D, cu_seqlens, max_seqlen: int, c
     (cu_seqlens[0] = 0, cu_seqlens[-1] = T); max_seqlen bounds every length.
     Each sequence is scanned from its own state_in slice (else from zero).
     Returns (y (T,H,R,P), DecodeState with (nseq, ...) tensors or None)."""
+    return _prefill_packed(x, dt, A, lam, theta, B, C, D, cu_seqlens, max_seqlen, chunk, state_in, out_state,
+                           y, workspace, state_dtype, None)
+
+
+def prefill_varlen_fused(x, dt, A, lam, theta, B, C, D, cu_seqlens, max_seqlen: int, chunk: int, A_t=None,
+                         b_norm_w=None, c_norm_w=None, b_bias=None, c_bias=None, z=None, eps: float = 1e-6,
+                         state_in: Optional[DecodeState] = None, out_state: bool = True,
+                         y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                         state_dtype: Optional[torch.dtype] = None):
+    """``prefill_varlen`` with the fused layer prologue/epilogue (m3_prefill_varlen_fused):
+    per-token A (T,H), RMSNorm weights and biases of B and C (R,N), gate z (laid out as y)."""
+    T, H, R, P = x.shape
+    N = B.shape[3]
+    fu = _fusion(x.device, (R, N, (T, H), (T, H, R, P)), A_t, b_norm_w, c_norm_w, b_bias, c_bias, z, eps, x.dtype)
+    return _prefill_packed(x, dt, A, lam, theta, B, C, D, cu_seqlens, max_seqlen, chunk, state_in, out_state,
+                           y, workspace, state_dtype, fu)
+
+
+def _prefill_packed(x, dt, A, lam, theta, B, C, D, cu_seqlens, max_seqlen, chunk, state_in, out_state, y,
+                    workspace, state_dtype, fu):
     T, H, R, P = x.shape
     G, N = B.shape[1], B.shape[3]
     nseq = cu_seqlens.shape[0] - 1
@@ -297,13 +321,16 @@ def prefill_varlen(x, dt, A, lam, theta, B, C, D, cu_seqlens, max_seqlen: int, c
     ws = workspace_size(dims)
     if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
         workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
-    rc = lib().m3_prefill_varlen(ctypes.byref(dims), _p(cu_seqlens), ctypes.c_int64(T), _p(x), _p(dt),
-                                 _p(A), _p(lam), _p(theta), _p(B), _p(C), _p(D),
-                                 None if sin is None else ctypes.byref(sin),
-                                 None if sout is None else ctypes.byref(sout), _p(y),
-                                 _p(workspace) if ws > 0 else None, ws, _stream(dev))
+    common = (ctypes.byref(dims), _p(cu_seqlens), ctypes.c_int64(T), _p(x), _p(dt), _p(A), _p(lam), _p(theta),
+              _p(B), _p(C), _p(D))
+    tail = (None if sin is None else ctypes.byref(sin), None if sout is None else ctypes.byref(sout), _p(y),
+            _p(workspace) if ws > 0 else None, ws, _stream(dev))
+    if fu is None:
+        rc, name = lib().m3_prefill_varlen(*common, *tail), "m3_prefill_varlen"
+    else:
+        rc, name = lib().m3_prefill_varlen_fused(*common, ctypes.byref(fu), *tail), "m3_prefill_varlen_fused"
     if rc != 0:
-        raise M3Error("m3_prefill_varlen", rc)
+        raise M3Error(name, rc)
     return y, st
 
 

@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     assert declared_symbols() == ["m3_backward", "m3_backward_parts", "m3_backward_per_token_A", "m3_backward_varlen",
                                   "m3_backward_workspace_size", "m3_decode_step",
                                   "m3_decode_step_fused", "m3_prefill_chunked", "m3_prefill_fused",
-                                  "m3_prefill_varlen", "m3_prefill_workspace_size", "m3_status_string",
+                                  "m3_prefill_varlen", "m3_prefill_varlen_fused", "m3_prefill_workspace_size", "m3_status_string",
                                   "m3_version"]
 
 
