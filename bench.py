@@ -56,7 +56,9 @@ def parse():
                     help="dtype of the state in HBM (bf16: reduced-precision state, fp32 math)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--check-slices", type=int, default=2, help="(b,h) slices checked against the oracle")
+    ap.add_argument("--check-slices", type=int, default=2,
+                    help="(b,h) slices of the run checked against the oracle in the CPU-baseline leg "
+                         "(none with --no-cpu-baseline)")
     ap.add_argument("--probe-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (known bytes) to calibrate HBM counters")
     return ap.parse_args()
@@ -287,10 +289,12 @@ def main():
                 "frac": round(pre_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "alg_bytes_per_launch": pre_bytes, "avg_launch_us": round(pre_avg * 1e3, 2)}
 
-    # Sampled parity of this very run against the oracle, and the CPU baseline.
+    # The CPU-baseline leg, the one place here that runs the oracle: the oracle timed on a
+    # bounded sample of the workload and, in the same leg, sampled slices of this very run
+    # checked against it.
     check = None
     cpu = None
-    if args.check_slices > 0 or not args.no_cpu_baseline:
+    if not args.no_cpu_baseline:
         import oracle
 
         def slice_inputs(bi, h, with_decode=True, n=None):
@@ -355,31 +359,31 @@ def main():
                 errs.append(max(e, eh))
             check = {"slices": args.check_slices, "max_rel_err": float(max(errs)),
                      "tolerance": 2e-2 if cfg.io_dtype == "bf16" else 1e-4}
-        if not args.no_cpu_baseline:
-            threads = oracle.max_threads()
-            si = slice_inputs(0, 0)
-            t1 = time.perf_counter()
-            oracle.scan(*[si[k] for k in order], nthreads=1)
-            one = time.perf_counter() - t1
-            n = int(max(threads, min(cfg.batch * cfg.nheads, args.cpu_seconds * threads / max(one, 1e-6))))
-            n = max(threads, (n // threads) * threads)
-            hs = list(range(n))
-            batch_in = [slice_inputs(i // cfg.nheads % cfg.batch, i % cfg.nheads) for i in hs]
-            # each sampled slice becomes its own head (and group) of one oracle call
-            stack = {k: np.concatenate([s[k] for s in batch_in], axis=2)
-                     for k in ("x", "dt", "lam", "theta", "B", "C")}
-            stack["A"] = np.concatenate([s["A"] for s in batch_in])
-            stack["D"] = np.concatenate([s["D"] for s in batch_in])
-            t1 = time.perf_counter()
-            oracle.scan(*[stack[k] for k in order], nthreads=threads)
-            sec = time.perf_counter() - t1
-            tok_per_slice = L + steps_dec
-            # tokens of the full workload carry all H heads: (slice-tokens / H) per second
-            cpu = {"value": round(n * tok_per_slice / cfg.nheads / sec, 2), "unit": "tokens/s",
-                   "cores": threads, "kind": "oracle",
-                   "sample": f"{n} (batch, head) slices of the workload, {tok_per_slice} tokens each "
-                             f"({L} prefill + {steps_dec} decode), fp64 sequential loop, "
-                             f"{sec:.1f} s; scaled to whole-workload tokens (1/{cfg.nheads} per slice-token)"}
+        # the timed oracle sample
+        threads = oracle.max_threads()
+        si = slice_inputs(0, 0)
+        t1 = time.perf_counter()
+        oracle.scan(*[si[k] for k in order], nthreads=1)
+        one = time.perf_counter() - t1
+        n = int(max(threads, min(cfg.batch * cfg.nheads, args.cpu_seconds * threads / max(one, 1e-6))))
+        n = max(threads, (n // threads) * threads)
+        hs = list(range(n))
+        batch_in = [slice_inputs(i // cfg.nheads % cfg.batch, i % cfg.nheads) for i in hs]
+        # each sampled slice becomes its own head (and group) of one oracle call
+        stack = {k: np.concatenate([s[k] for s in batch_in], axis=2)
+                 for k in ("x", "dt", "lam", "theta", "B", "C")}
+        stack["A"] = np.concatenate([s["A"] for s in batch_in])
+        stack["D"] = np.concatenate([s["D"] for s in batch_in])
+        t1 = time.perf_counter()
+        oracle.scan(*[stack[k] for k in order], nthreads=threads)
+        sec = time.perf_counter() - t1
+        tok_per_slice = L + steps_dec
+        # tokens of the full workload carry all H heads: (slice-tokens / H) per second
+        cpu = {"value": round(n * tok_per_slice / cfg.nheads / sec, 2), "unit": "tokens/s",
+               "cores": threads, "kind": "oracle",
+               "sample": f"{n} (batch, head) slices of the workload, {tok_per_slice} tokens each "
+                         f"({L} prefill + {steps_dec} decode), fp64 sequential loop, "
+                         f"{sec:.1f} s; scaled to whole-workload tokens (1/{cfg.nheads} per slice-token)"}
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -511,8 +515,10 @@ def run_backward(args, cfg):
             "alg_flops_per_launch": flops, "alg_bytes_per_launch": nbytes,
             "alg_GB_per_s": round(nbytes / (ms / 1e3) / 1e9, 1), "avg_launch_us": round(ms * 1e3, 1)}
 
+    # The CPU-baseline leg (the oracle timed on a bounded sample, and sampled slices of this
+    # run checked against it), the one place here that runs the oracle.
     check = cpu = None
-    if args.check_slices > 0 or not args.no_cpu_baseline:
+    if not args.no_cpu_baseline:
         import oracle
         f = lambda t: t.detach().double().cpu().numpy()
 
@@ -549,29 +555,29 @@ def run_backward(args, cfg):
                     errs.append(float(np.max(np.abs(gv - ref[k])) / max(np.max(np.abs(ref[k])), 1e-30)))
             check = {"slices": args.check_slices, "max_rel_err": max(errs), "tolerance": 1e-3,
                      "compared": "dx, ddt, dlambda of sampled (b, h) slices"}
-        if not args.no_cpu_baseline:
-            threads = oracle.max_threads()
-            si = slice_inputs(0, 0, packed=False)   # the oracle's rate on whole-length slices
-            t1 = time.perf_counter()
-            oracle.scan_backward(*[si[k] for k in names], si["dy"], nthreads=1)
-            one = time.perf_counter() - t1
-            # the oracle parallelises over batch elements: each sampled slice is its own batch element
-            n = int(max(threads, min(cfg.batch * cfg.nheads, args.cpu_seconds * threads / max(one, 1e-6))))
-            n = max(threads, (n // threads) * threads)
-            sl = [slice_inputs(i // cfg.nheads % cfg.batch, i % cfg.nheads, packed=False) for i in range(n)]
-            st = {k: np.concatenate([s[k] for s in sl], axis=0) for k in ("x", "dt", "lam", "theta", "B", "C", "dy")}
-            t1 = time.perf_counter()
-            # A (per head), D differ per slice's head; the sample uses head 0's values for all (same
-            # cost).  A per-token A_t is each slice's own.
-            a_cpu = np.concatenate([s["A"] for s in sl], axis=0) if args.fused else sl[0]["A"]
-            oracle.scan_backward(st["x"], st["dt"], a_cpu, st["lam"], st["theta"], st["B"], st["C"],
-                                 sl[0]["D"], st["dy"], nthreads=threads)
-            sec = time.perf_counter() - t1
-            cpu = {"value": round(n * L / cfg.nheads / sec, 2), "unit": "tokens/s", "cores": threads,
-                   "kind": "oracle",
-                   "sample": f"{n} (batch, head) slices of the workload, {L} tokens each, backward "
-                             f"(fp64 adjoint loop), {sec:.1f} s; scaled to whole-workload tokens "
-                             f"(1/{cfg.nheads} per slice-token)"}
+        # the timed oracle sample
+        threads = oracle.max_threads()
+        si = slice_inputs(0, 0, packed=False)   # the oracle's rate on whole-length slices
+        t1 = time.perf_counter()
+        oracle.scan_backward(*[si[k] for k in names], si["dy"], nthreads=1)
+        one = time.perf_counter() - t1
+        # the oracle parallelises over batch elements: each sampled slice is its own batch element
+        n = int(max(threads, min(cfg.batch * cfg.nheads, args.cpu_seconds * threads / max(one, 1e-6))))
+        n = max(threads, (n // threads) * threads)
+        sl = [slice_inputs(i // cfg.nheads % cfg.batch, i % cfg.nheads, packed=False) for i in range(n)]
+        st = {k: np.concatenate([s[k] for s in sl], axis=0) for k in ("x", "dt", "lam", "theta", "B", "C", "dy")}
+        t1 = time.perf_counter()
+        # A (per head), D differ per slice's head; the sample uses head 0's values for all (same
+        # cost).  A per-token A_t is each slice's own.
+        a_cpu = np.concatenate([s["A"] for s in sl], axis=0) if args.fused else sl[0]["A"]
+        oracle.scan_backward(st["x"], st["dt"], a_cpu, st["lam"], st["theta"], st["B"], st["C"],
+                             sl[0]["D"], st["dy"], nthreads=threads)
+        sec = time.perf_counter() - t1
+        cpu = {"value": round(n * L / cfg.nheads / sec, 2), "unit": "tokens/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{n} (batch, head) slices of the workload, {L} tokens each, backward "
+                         f"(fp64 adjoint loop), {sec:.1f} s; scaled to whole-workload tokens "
+                         f"(1/{cfg.nheads} per slice-token)"}
 
     out = {
         "metric": BWD_METRIC, "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
