@@ -194,9 +194,6 @@ def main():
     ydec = torch.empty((max(steps_dec, 1),) + tuple(d["x"][:, 0].shape), dtype=d["x"].dtype, device=dev)
     fz = fzd = None
     if args.fused:   # seeded fusion inputs: per-token A, norm weights and biases (R, N), gate z
-        if args.varlen:
-            print("--fused is measured on uniform batches only", file=sys.stderr)
-            sys.exit(2)
         gf = torch.Generator(device=dev).manual_seed(cfg.seed + 23)
         Rr, Nn = cfg.rank, cfg.dstate
         fz = {"A_t": -torch.exp(torch.rand(d["dt"].shape, generator=gf, device=dev) * math.log(16.0)),
@@ -209,6 +206,10 @@ def main():
             fzd = {"A_t": -torch.exp(torch.rand((steps_dec,) + tuple(d["dt"][:, 0].shape), generator=gf, device=dev)
                                      * math.log(16.0)),
                    "z": torch.randn((steps_dec,) + tuple(d["x"][:, 0].shape), generator=gf, device=dev).to(d["x"].dtype)}
+        if args.varlen:   # the per-token pieces packed like the other inputs
+            dpf = {k: torch.cat([fz[k][i, :int(lens[i])] for i in range(cfg.batch)]).contiguous()
+                   for k in ("A_t", "z")}
+            dpf.update({k: fz[k] for k in ("b_norm_w", "c_norm_w", "b_bias", "c_bias")})
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
 
@@ -217,7 +218,11 @@ def main():
     def one_step(record=None):
         e0, e1, e2 = ev(), ev(), ev()
         e0.record(stream)
-        if args.varlen:
+        if args.varlen and args.fused:
+            _, st = m3scan.prefill_varlen_fused(dp["x"], dp["dt"], d["A"], dp["lam"], dp["theta"], dp["B"],
+                                                dp["C"], d["D"], cu, L, cfg.chunk, **dpf, y=y,
+                                                state_dtype=state_dtype)
+        elif args.varlen:
             _, st = m3scan.prefill_varlen(dp["x"], dp["dt"], d["A"], dp["lam"], dp["theta"], dp["B"],
                                           dp["C"], d["D"], cu, L, cfg.chunk, y=y, state_dtype=state_dtype)
         elif args.fused:
