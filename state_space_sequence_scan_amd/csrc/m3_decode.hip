@@ -62,8 +62,10 @@ template <> struct state_vec<bf16_t, 8> {
 // bias (R, N), then B and the previous B scaled by bscale and bpscale.  One wave
 // per row at a time; the block has nt threads (one partial wave when nt < 64).
 // Ends with a barrier.
-__device__ __forceinline__ void fuse_bc(float* sB, float* sC, float* sBp, float* sScale, int R, int N,
-                                        int nt, const Fusion& fu, float bscale = 1.f, float bpscale = 1.f) {
+// The RMSNorm scales of the 3R staged rows (B, C, previous B) into sScale[3R]; ends
+// with a barrier when a norm weight is given.
+__device__ __forceinline__ void bc_scales(const float* sB, const float* sC, const float* sBp, float* sScale,
+                                          int R, int N, int nt, const Fusion& fu) {
     const int tid = threadIdx.x, width = nt < 64 ? nt : 64, lane = tid % width, wave = tid / width;
     const int nwaves = (nt + width - 1) / width;
     if (fu.bnw || fu.cnw) {
@@ -76,6 +78,12 @@ __device__ __forceinline__ void fuse_bc(float* sB, float* sC, float* sBp, float*
         }
         __syncthreads();
     }
+}
+
+__device__ __forceinline__ void fuse_bc(float* sB, float* sC, float* sBp, float* sScale, int R, int N,
+                                        int nt, const Fusion& fu, float bscale = 1.f, float bpscale = 1.f) {
+    const int tid = threadIdx.x;
+    bc_scales(sB, sC, sBp, sScale, R, N, nt, fu);
     for (int i = tid; i < R * N; i += nt) {
         const int r = i / N;
         float b = sB[i], c = sC[i], bp = sBp[i];
@@ -99,7 +107,9 @@ __device__ __forceinline__ void fuse_bc(float* sB, float* sC, float* sBp, float*
 // Fast path.  One workgroup of NT threads per (b, h).  Thread tid owns the
 // CW-column block c = tid % PC (PC = P/CW) and the rotation pairs
 // k = kk + TPG * j (kk = tid / PC, j < PPT), i.e. 2 * PPT state rows x CW columns.
-template <typename T, typename S, int N, int P, int R, int NT, int CW>
+// FU: the fused prologue/epilogue may be present (its weights, biases and gate input are
+// then loaded with the other small operands, ahead of the state stream).
+template <typename T, typename S, int N, int P, int R, int NT, int CW, bool FU>
 __global__ __launch_bounds__(NT) void decode_fast(
     S* __restrict__ h, const T* __restrict__ b_last, const T* __restrict__ x_last,
     const T* __restrict__ x_t, const float* __restrict__ dt_t, const float* __restrict__ A,
@@ -159,6 +169,26 @@ __global__ __launch_bounds__(NT) void decode_fast(
         const int k = tid + NT * e;
         vth[e] = (k < KP) ? theta_t[(static_cast<size_t>(b) * G + g) * KP + k] : 0.f;
     }
+    // Fused pieces of this thread's elements: norm weights and biases of its B/C entries,
+    // the gate input of its outputs.
+    constexpr int FS = FU ? SPT : 1, FX = FU ? XPT : 1;
+    float wbn[FS], wcn[FS], wbb[FS], wcb[FS], vz[FX];
+    if constexpr (FU) {
+#pragma unroll
+        for (int e = 0; e < SPT; ++e) {
+            const int i = tid + NT * e;
+            const bool in = i < R * N;
+            wbn[e] = (in && fu.bnw) ? fu.bnw[i] : 1.f;
+            wcn[e] = (in && fu.cnw) ? fu.cnw[i] : 1.f;
+            wbb[e] = (in && fu.bbias) ? fu.bbias[i] : 0.f;
+            wcb[e] = (in && fu.cbias) ? fu.cbias[i] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < XPT; ++e) {
+            const int i = tid + NT * e;
+            vz[e] = (fu.z && i < R * P) ? io<T>::load(static_cast<const T*>(fu.z) + hofs + i) : 0.f;
+        }
+    }
 
     // Step scalars.  gamma = lambda dt is folded into the staged B, the carry weight
     // (1 - lambda) dt into the staged previous B (after BCNorm when that is fused:
@@ -170,7 +200,7 @@ __global__ __launch_bounds__(NT) void decode_fast(
     const float alpha = __expf(dtv * (fu.At ? fu.At[bh] : A[hh]));
     const float c1 = (1.f - lv) * dtv;   // (1 - lambda) dt : weight of the carry before the decay
     const float c2 = lv * dtv;           // gamma
-    const bool fuse = fu.bc();           // uniform across the grid
+    const bool fuse = FU && fu.bc();     // uniform across the grid
     const float bsc = fuse ? 1.f : c2, bpsc = fuse ? 1.f : c1;
 
     S* hp = h + static_cast<size_t>(bh) * N * P;
@@ -210,9 +240,27 @@ __global__ __launch_bounds__(NT) void decode_fast(
         }
     }
     __syncthreads();
-    if (fuse) {
-        __shared__ float sScale[3 * R];
-        fuse_bc(&sB[0][0], &sC[0][0], &sBp[0][0], sScale, R, N, NT, fu, c2, c1);
+    if constexpr (FU) {
+        if (fuse) {   // norm and bias of the staged rows with this thread's preloaded weights
+            __shared__ float sScale[3 * R];
+            bc_scales(&sB[0][0], &sC[0][0], &sBp[0][0], sScale, R, N, NT, fu);
+            float* fB = &sB[0][0];
+            float* fC = &sC[0][0];
+            float* fBp = &sBp[0][0];
+#pragma unroll
+            for (int e = 0; e < SPT; ++e) {
+                const int i = tid + NT * e;
+                if (i < R * N) {
+                    const int r = i / N;
+                    const float sb = fu.bnw ? sScale[r] : 1.f, sbp = fu.bnw ? sScale[2 * R + r] : 1.f;
+                    const float sc = fu.cnw ? sScale[R + r] : 1.f;
+                    fB[i] = (fB[i] * (sb * wbn[e]) + wbb[e]) * c2;
+                    fC[i] = fC[i] * (sc * wcn[e]) + wcb[e];
+                    fBp[i] = (fBp[i] * (sbp * wbn[e]) + wbb[e]) * c1;
+                }
+            }
+            __syncthreads();
+        }
     }
 
     fvec xv[R], xpv[R];
@@ -267,14 +315,19 @@ __global__ __launch_bounds__(NT) void decode_fast(
     }
     __syncthreads();
     const float dv = D[hh];
-    const T* zt = static_cast<const T*>(fu.z);
-    for (int i = tid; i < R * P; i += NT) {
-        float acc = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) acc += (&sY[w][0][0])[i];
-        acc += dv * (&sX[0][0])[i];
-        if (zt) acc *= silu(io<T>::load(zt + hofs + i));
-        io<T>::store(y_t + hofs + i, acc);
+    for (int e = 0; e < XPT; ++e) {
+        const int i = tid + NT * e;
+        if (i < R * P) {
+            float acc = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) acc += (&sY[w][0][0])[i];
+            acc += dv * (&sX[0][0])[i];
+            if constexpr (FU) {
+                if (fu.z) acc *= silu(vz[e]);
+            }
+            io<T>::store(y_t + hofs + i, acc);
+        }
     }
 }
 
@@ -357,7 +410,11 @@ __global__ __launch_bounds__(64) void decode_generic(
 // step is limited by its fp32 arithmetic, and fewer rows per thread are in flight.)
 template <typename T, typename S, int N, int P, int R, int NT, int CW = 4>
 static hipError_t launch_fast(const DecodeArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((decode_fast<T, S, N, P, R, NT, CW>), dim3(static_cast<unsigned>(a.batch * a.H)),
+    // the fused variant only when a norm, bias or gate is given (a per-token A alone is one
+    // scalar per workgroup, read by both)
+    const bool fused = a.fu.bc() || a.fu.z;
+    auto kernel = fused ? decode_fast<T, S, N, P, R, NT, CW, true> : decode_fast<T, S, N, P, R, NT, CW, false>;
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(a.batch * a.H)),
                        dim3(NT), 0, st, static_cast<S*>(a.h), static_cast<const T*>(a.b_last),
                        static_cast<const T*>(a.x_last), static_cast<const T*>(a.x_t), a.dt_t, a.A,
                        a.lam_t, a.theta_t, static_cast<const T*>(a.B_t),
