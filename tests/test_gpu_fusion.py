@@ -142,3 +142,37 @@ def test_prefill_varlen_fused_each_sequence_matches_oracle(case):
         say(f"  seq {s} (len {n}): y {ey:.2e} h {eh:.2e}")
         assert ey <= TOL[io] and eh <= TOL[io], (s, ey, eh)
         assert torch.equal(so.b_last[s], d["B"][c[s + 1] - 1]) and torch.equal(so.x_last[s], d["x"][c[s + 1] - 1])
+
+
+@pytest.mark.parametrize("parts", [("gate",), ("A_t",), ("norm",), ("bias",), ("A_t", "norm", "bias", "gate")],
+                         ids=lambda p: "+".join(p))
+@pytest.mark.parametrize("state", ["fp32", "bf16"])
+def test_fused_decode_steps_match_oracle(parts, state):
+    """Three fused decode steps from a random state with a raw carried B, one fused piece at a
+    time and all together (the decode kernel has a variant for norm, bias or gate, and reads
+    a per-token A in both); fp32 and bf16 state (the latter against the oracle rounded
+    after every token)."""
+    b, H, G, P, N, R, steps = 2, 8, 2, 64, 128, 4, 3
+    say("fused decode", "+".join(parts), state)
+    d = draw(b, steps, H, G, P, N, R, "bf16", 1.0, seed=70 + len(parts))
+    f = _fusion(b, steps, H, R, N, P, "bf16", seed=12, parts=parts)
+    st = rand_state(b, H, G, N, P, R, "bf16", seed=14)
+    if state == "bf16":
+        st = m3scan.DecodeState(st.h.to(torch.bfloat16), st.b_last, st.x_last)
+    st0 = (np64(st.h), np64(st.b_last), np64(st.x_last))
+    ys = []
+    for t in range(steps):
+        tok = {k: (v[:, t].contiguous() if v.dim() > 1 else v) for k, v in d.items()}
+        ft = {k: (v[:, t].contiguous() if k in ("A_t", "z") else v) for k, v in f.items()}
+        ys.append(m3scan.decode_step_fused(st, *[tok[k] for k in NAMES], **ft)[:, None])
+    torch.cuda.synchronize()
+    kw = {k: np64(v) for k, v in f.items() if k != "A_t"}
+    args = [np64(d[k]) for k in NAMES]
+    if "A_t" in f:
+        args[2] = np64(f["A_t"])
+    yr, hr = oracle.scan_fused(*args, **kw, state_in=st0,
+                               round_after=np.ones(steps, bool) if state == "bf16" else None)
+    ey = slice_err(np64(torch.cat(ys, dim=1)), yr, 2)
+    eh = slice_err(np64(st.h), hr, 1)
+    say(f"  y {ey:.2e} h {eh:.2e}")
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
