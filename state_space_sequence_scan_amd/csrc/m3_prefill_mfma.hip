@@ -342,7 +342,8 @@ __device__ __forceinline__ void set_oct(bfv<K>& v, int i, bf16x8 o) {
     for (int e = 0; e < 8; ++e) v[8 * i + e] = o[e];
 }
 
-template <int R, int Q, int NW, bool FULL>
+// GATE: the output gate is applied (its input rows are loaded well before the store).
+template <int R, int Q, int NW, bool FULL, bool GATE>
 __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
     constexpr int NTH = 64 * NW;
     constexpr int QR = Q * R;
@@ -687,16 +688,27 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
     // Lane (l16, lg) writes columns 16ct + 4lg .. +3 of output row 16a + l16: 8 bytes per tile.
     // With a gate the row's z values (same place as y; rows past the end read the last
     // token's) multiply y by silu(z) first.
-#define M3_STORE_Y(yv_, a_)                                                                                   \
+    // Gate input of output row 16a_ + l16 into zr_ (rows past the end read the last token's),
+    // loaded a phase ahead of the store that uses it.
+#define M3_LOAD_Z(zr_, a_)                                                                                    \
     do {                                                                                                      \
         const int i = 16 * (a_) + l16;                                                                        \
         const int tk = i / R, r = i - tk * R;                                                                 \
-        if (p.z) {                                                                                            \
-            const uint16_t* zrow = p.z + ((tb + t0) * p.H + h) * static_cast<int64_t>(R * P) +                \
-                                   (static_cast<uint32_t>(tk < nq ? tk : nq - 1) * HRP +                      \
-                                    static_cast<uint32_t>(r * P + 4 * lg));                                   \
+        const uint16_t* zrow = p.z + ((tb + t0) * p.H + h) * static_cast<int64_t>(R * P) +                    \
+                               (static_cast<uint32_t>(tk < nq ? tk : nq - 1) * HRP +                          \
+                                static_cast<uint32_t>(r * P + 4 * lg));                                       \
+        _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) zr_[ct] = *reinterpret_cast<const uint2*>(zrow + 16 * ct); \
+    } while (0)
+
+    // Lane (l16, lg) writes columns 16ct + 4lg .. +3 of output row 16a + l16: 8 bytes per tile.
+    // With the gate, the row's z values (zr_, from M3_LOAD_Z) multiply y by silu(z) first.
+#define M3_STORE_Y(yv_, a_, zr_)                                                                              \
+    do {                                                                                                      \
+        const int i = 16 * (a_) + l16;                                                                        \
+        const int tk = i / R, r = i - tk * R;                                                                 \
+        if constexpr (GATE) {                                                                                 \
             _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) {                                                \
-                const uint2 zz = *reinterpret_cast<const uint2*>(zrow + 16 * ct);                             \
+                const uint2 zz = zr_[ct];                                                                     \
                 yv_[ct][0] *= silu(bits_to_f(zz.x & 0xffff));                                                 \
                 yv_[ct][1] *= silu(bits_to_f(zz.x >> 16));                                                    \
                 yv_[ct][2] *= silu(bits_to_f(zz.y & 0xffff));                                                 \
@@ -762,6 +774,8 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
             s16x4 xfA[4], xfB[4];
             float4 v0A, v1A, v0B, v1B;
             f32x4 y0[4], y1[4];
+            uint2 zr[4];   // gate input of the row block being finished (GATE only)
+            if constexpr (GATE) M3_LOAD_Z(zr, a_lo);
             // (4a) inter-chunk term; with two row blocks the S^T fragments serve both.  The
             // fragments of column tile ct + 1 are read while tile ct is multiplied.
             {
@@ -833,9 +847,10 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
             }
             M3_DIAG(y0, cf0, a_lo, A);
             if (MB == 2) M3_OFFDIAG(y1, cf1, A, v1A);
-            M3_STORE_Y(y0, a_lo);
+            M3_STORE_Y(y0, a_lo, zr);
             M3_LOAD_CF(cf0, cn, a_lo);
             if constexpr (MB == 2) {
+                if constexpr (GATE) M3_LOAD_Z(zr, a_hi);
                 // set B holds block a_lo + 1 (or a_hi when that is the next one)
                 bb = a_lo + 1;
                 for (; bb + 1 < a_hi; bb += 2) {   // blocks bb (set B) and bb + 1 (set A)
@@ -856,7 +871,7 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
                 } else {                           // set B holds block a_hi
                     M3_DIAG(y1, cf1, a_hi, B);
                 }
-                M3_STORE_Y(y1, a_hi);
+                M3_STORE_Y(y1, a_hi, zr);
                 M3_LOAD_CF(cf1, cn, a_hi);
             }
         } else if (FULL) {
@@ -963,6 +978,7 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
 #undef M3_OFFDIAG
 #undef M3_DIAG
 #undef M3_STORE_Y
+#undef M3_LOAD_Z
 #undef M3_INTER_SCALE
 
     // epilogue
@@ -1192,7 +1208,7 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
         ps.seg_state = reinterpret_cast<float*>(base + ws.seg_state);
         ps.seg_decay = reinterpret_cast<float*>(base + ws.seg_decay);
         ps.seg_rot = reinterpret_cast<float*>(base + ws.seg_rot);
-        hipLaunchKernelGGL((mf::scan_mfma<R, Q, NW, false>), dim3(static_cast<unsigned>(pieces * a.H * a.batch)),
+        hipLaunchKernelGGL((mf::scan_mfma<R, Q, NW, false, false>), dim3(static_cast<unsigned>(pieces * a.H * a.batch)),
                            dim3(64 * NW), 0, st, ps);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         float* s_init = reinterpret_cast<float*>(base + ws.s_init);
@@ -1205,7 +1221,8 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
         p.sinit_stride = pieces + 1;
         p.sinit_step = split;
     }
-    hipLaunchKernelGGL((mf::scan_mfma<R, Q, NW, true>), dim3(static_cast<unsigned>(nseg * a.H * a.batch)),
+    auto scan = p.z ? mf::scan_mfma<R, Q, NW, true, true> : mf::scan_mfma<R, Q, NW, true, false>;
+    hipLaunchKernelGGL(scan, dim3(static_cast<unsigned>(nseg * a.H * a.batch)),
                        dim3(64 * NW), 0, st, p);
     return hipGetLastError();
 }
