@@ -207,7 +207,9 @@ m3_status m3_prefill_fused(const m3_dims* dims, const void* x, const float* dt, 
                            m3_state* state_out, void* y, void* workspace, size_t workspace_bytes,
                            void* stream);
 
-/* m3_prefill_varlen with the fused prologue/epilogue of `fusion` (non-NULL), on a packed
+/* m3_prefill_varlen with the fused prologue/epilogue of `fusion` (non-NULL; the pieces of
+ * the layer next to the scan, Mamba-3 blog part 1, "Normalization" and "Removing the short
+ * convolution", and the per-token A of the paper note's "Solution 1"), on a packed
  * batch: A_t is (total_tokens, H) and z is laid out as y, (total_tokens, H, R, P); a
  * carried b_last of state_in (per sequence) is normalised like B.  Same workspace size
  * (m3_prefill_workspace_size); the other arguments, layouts and errors as
