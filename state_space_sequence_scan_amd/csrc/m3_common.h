@@ -96,8 +96,10 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// silu(v) = v / (1 + e^-v), the output gate's nonlinearity.
-__device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
+// silu(v) = v / (1 + e^-v), the output gate's nonlinearity, with the hardware reciprocal
+// (1 ulp) in place of an IEEE division: a dozen fewer instructions per gated output.
+// Large negative v gives e^-v = inf, a reciprocal of 0 and silu = -0.
+__device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.f + __expf(-v)); }
 
 // Accurate sin/cos of an angle of any size (chunk-local angle sums can reach
 // hundreds of radians); the HIP library routine does the range reduction.
