@@ -74,8 +74,8 @@ def fused_extra_bytes(cfg, L, steps, tokens=None):
 
 
 def algorithmic_bytes(cfg, L, steps, state_bytes=4, tokens=None):
-    """Bytes the method must move (see the workload formulas in the design notes);
-    state_bytes is 4 for an fp32 state, 2 for a bf16 state; tokens is the number of
+    """Bytes the method must move: every input read once and every output written once
+    (the terms below); state_bytes is 4 for an fp32 state, 2 for a bf16 state; tokens is the number of
     prefill tokens over all sequences (batch * L unless the lengths vary)."""
     s = 2 if cfg.io_dtype == "bf16" else 4
     b, H, G, P, N, R = cfg.batch, cfg.nheads, cfg.ngroups, cfg.headdim, cfg.dstate, cfg.rank
@@ -424,7 +424,8 @@ def main():
 def backward_flops(cfg, L):
     """fp32 arithmetic of the adjoint method per workload: one forward step and one
     reverse step of the recurrence per (token, head) over the N x P state, counted as
-    14 R + 33 flops per state element (see the backward's section of the design notes)."""
+    14 R + 33 flops per state element: 2 R + 8 for the forward step that recomputes the
+    state and 12 R + 25 for the adjoint step and the gradient contractions."""
     return cfg.batch * L * cfg.nheads * cfg.dstate * cfg.headdim * (14 * cfg.rank + 33)
 
 
