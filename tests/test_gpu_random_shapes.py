@@ -1,4 +1,4 @@
-"""GPU parity over a seeded sweep of shapes, against the oracle: batch, length (1 to 700,
+"""GPU parity over a seeded sweep of 32 shapes, against the oracle: batch, length (1 to 700,
 so ragged last chunks and sequences shorter than a chunk), heads and groups, rank, chunk
 size, io dtype and kernel family (matrix-core bf16 at N=128, P=64; the fp32 path at
 smaller N and P), with and without an incoming state; each case runs a prefill, then
@@ -34,7 +34,7 @@ def _cases(n=16, seed=2024):
     return out
 
 
-CASES = _cases()
+CASES = _cases(32)
 
 
 def _id(c):
