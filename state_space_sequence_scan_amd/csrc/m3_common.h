@@ -89,11 +89,26 @@ template <> struct state4<bf16_t> {
     }
 };
 
-// Sum over the 64 lanes of a wave (every lane gets it).
+// One DPP move of a float between lanes (control C: a quad permutation or a rotation
+// within each row of 16 lanes); every source lane exists for these controls.
+template <int C>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), C, 0xf, 0xf, false));
+}
+
+// Sum over the 64 lanes of a wave, all of them active (every lane gets it): the lanes of
+// each row of 16 are summed with DPP moves (swap neighbours, swap pairs, rotate by 4, by 8),
+// then the four row sums are read into scalars and added.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off);
-    return v;
+    v += dpp_move<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+    v += dpp_move<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+    v += dpp_move<0x124>(v);   // row_ror 4
+    v += dpp_move<0x128>(v);   // row_ror 8
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 // silu(v) = v / (1 + e^-v), the output gate's nonlinearity, with the hardware reciprocal

@@ -73,7 +73,11 @@ __device__ __forceinline__ void bc_scales(const float* sB, const float* sC, cons
             const float* src = row < R ? sB + row * N : (row < 2 * R ? sC + (row - R) * N : sBp + (row - 2 * R) * N);
             float ss = 0.f;
             for (int n = lane; n < N; n += width) ss += src[n] * src[n];
-            for (int off = 1; off < width; off <<= 1) ss += __shfl_xor(ss, off, width);
+            if (width == 64) {
+                ss = wave_sum(ss);
+            } else {
+                for (int off = 1; off < width; off <<= 1) ss += __shfl_xor(ss, off, width);
+            }
             if (lane == 0) sScale[row] = rsqrtf(ss / N + fu.eps);
         }
         __syncthreads();
