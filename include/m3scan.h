@@ -41,8 +41,9 @@
  * Ownership and execution: every pointer is device memory owned by the caller.
  * The library never allocates, frees or synchronises; all work is enqueued on
  * `stream` (a hipStream_t; NULL = the null stream) and the call returns at once.
- * There is no global mutable state: calls on different streams may run from
- * different threads.  Outputs must not alias inputs unless stated.
+ * There is no global mutable state (except the static scratch array of
+ * m3_prefill_chunked_noalloc, see there): calls on different streams may run
+ * from different threads.  Outputs must not alias inputs unless stated.
  *
  * Errors: argument and shape errors are returned before anything is launched.
  * Launch failures return M3_ERR_HIP.  Faults inside a kernel surface at the
@@ -335,6 +336,31 @@ m3_status m3_backward_per_token_A(const m3_dims* dims, const int64_t* cu_seqlens
                                   const m3_state* state_in, const void* dy, const float* dh_out,
                                   const m3_grads* grads, void* workspace, size_t workspace_bytes,
                                   void* stream);
+
+/*
+ * For callers that cannot allocate device memory (work recorded under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): m3_prefill_chunked
+ * without a workspace argument.  The workspace lives in a static device array of
+ * M3_NOALLOC_SCRATCH_BYTES bytes inside this library; every GPU the call runs on
+ * holds its own copy from the first such call until the process ends.  The call
+ * allocates and frees nothing.
+ *
+ * Limit: dims whose m3_prefill_workspace_size exceeds M3_NOALLOC_SCRATCH_BYTES are
+ * rejected with M3_ERR_WORKSPACE before anything is launched (call
+ * m3_prefill_chunked with a workspace of your own for those).
+ * Sharing: all calls on one GPU use that GPU's one array, so calls that can overlap
+ * on one GPU (different streams, or threads without ordering between them) race
+ * on it and must be serialised by the caller.  Nothing in the array needs to start
+ * at zero; it keeps the last call's contents.
+ * Arguments, layouts and the other errors: as m3_prefill_chunked; M3_ERR_HIP also
+ * when the array's device address cannot be obtained.
+ */
+#define M3_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+m3_status m3_prefill_chunked_noalloc(const m3_dims* dims, const void* x, const float* dt,
+                                     const float* A, const float* lambda, const float* theta,
+                                     const void* B, const void* C, const float* D,
+                                     const m3_state* state_in, m3_state* state_out, void* y,
+                                     void* stream);
 
 /* Static text for a status code. */
 const char* m3_status_string(m3_status status);

@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "m3_internal.h"
 
 namespace {
@@ -227,6 +229,54 @@ m3_status m3_prefill_varlen_fused(const m3_dims* dims, const int64_t* cu_seqlens
     if (!cu_seqlens || total_tokens < 0 || !fusion) return M3_ERR_INVALID_ARG;
     return prefill_common(dims, cu_seqlens, total_tokens, x, dt, A, lambda, theta, B, C, D, fusion,
                           state_in, state_out, y, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// Workspace of m3_prefill_chunked_noalloc: one static array per GPU (the runtime gives
+// every device its own copy of a __device__ variable).  Host code never uses the
+// array's name as an address (on the host it names a host-side stand-in); it asks
+// the runtime for each device's address once, with that device current, and keeps it.
+namespace {
+
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[M3_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+m3_status scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return M3_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return M3_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return M3_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return M3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+m3_status m3_prefill_chunked_noalloc(const m3_dims* dims, const void* x, const float* dt,
+                                     const float* A, const float* lambda, const float* theta,
+                                     const void* B, const void* C, const float* D,
+                                     const m3_state* state_in, m3_state* state_out, void* y,
+                                     void* stream) {
+    // the size check comes first: a shape beyond the array is refused before any HIP call
+    size_t need = 0;
+    const m3_status st = m3_prefill_workspace_size(dims, &need);
+    if (st != M3_OK) return st;
+    if (need > M3_NOALLOC_SCRATCH_BYTES) return M3_ERR_WORKSPACE;
+    void* ws = nullptr;
+    const m3_status sc = scratch_of_current_device(&ws);
+    if (sc != M3_OK) return sc;
+    return prefill_common(dims, nullptr, 0, x, dt, A, lambda, theta, B, C, D, nullptr, state_in, state_out,
+                          y, ws, M3_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -75,6 +75,9 @@ def lib(path: str = LIB_PATH):
     L.m3_prefill_chunked.restype = ctypes.c_int
     L.m3_prefill_chunked.argtypes = ([ctypes.POINTER(Dims)] + [vp] * 8 +
                                      [ctypes.POINTER(State), ctypes.POINTER(State), vp, vp, sz, vp])
+    L.m3_prefill_chunked_noalloc.restype = ctypes.c_int
+    L.m3_prefill_chunked_noalloc.argtypes = ([ctypes.POINTER(Dims)] + [vp] * 8 +
+                                             [ctypes.POINTER(State), ctypes.POINTER(State), vp, vp])
     L.m3_prefill_varlen.restype = ctypes.c_int
     L.m3_prefill_varlen.argtypes = ([ctypes.POINTER(Dims), vp, ctypes.c_int64] + [vp] * 8 +
                                     [ctypes.POINTER(State), ctypes.POINTER(State), vp, vp, sz, vp])
@@ -206,6 +209,58 @@ def prefill(x, dt, A, lam, theta, B, C, D, chunk: int, state_in: Optional[Decode
     if rc != 0:
         raise M3Error("m3_prefill_chunked", rc)
     return y, st
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # M3_NOALLOC_SCRATCH_BYTES of include/m3scan.h
+
+
+def prefill_noalloc(x, dt, A, lam, theta, B, C, D, chunk: int, state_in: Optional[DecodeState] = None,
+                    y: Optional[torch.Tensor] = None, state_out: Optional[DecodeState] = None):
+    """``prefill`` through m3_prefill_chunked_noalloc: no workspace argument (the library's
+    static scratch array serves as one).  The caller's y and state_out are used when given
+    (nothing is allocated then); else they are allocated here.  Returns (y, state_out)."""
+    b, L, H, R, P = x.shape
+    G, N = B.shape[2], B.shape[4]
+    dev, io = x.device, x.dtype
+    if io not in _IO:
+        raise ValueError(f"x dtype {io} not supported (fp32 or bf16)")
+    _check(x, "x", (b, L, H, R, P), io, dev)
+    _check(dt, "dt", (b, L, H), torch.float32, dev)
+    _check(lam, "lam", (b, L, H), torch.float32, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(theta, "theta", (b, L, G, N // 2), torch.float32, dev)
+    _check(B, "B", (b, L, G, R, N), io, dev)
+    _check(C, "C", (b, L, G, R, N), io, dev)
+    state_dtype = state_in.h.dtype if state_in is not None else (
+        state_out.h.dtype if state_out is not None else torch.float32)
+    dims = make_dims(b, L, H, G, P, N, R, chunk, _IO[io], _IO[state_dtype])
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", x.shape, io, dev)
+    sin = None
+    if state_in is not None:
+        _check(state_in.h, "state_in.h", (b, H, N, P), state_dtype, dev)
+        if state_in.b_last is not None:
+            _check(state_in.b_last, "state_in.b_last", (b, G, R, N), io, dev)
+            _check(state_in.x_last, "state_in.x_last", (b, H, R, P), io, dev)
+        sin = State(state_in.h.data_ptr(),
+                    None if state_in.b_last is None else state_in.b_last.data_ptr(),
+                    None if state_in.x_last is None else state_in.x_last.data_ptr())
+    if state_out is None:
+        state_out = DecodeState(torch.empty((b, H, N, P), dtype=state_dtype, device=dev),
+                                torch.empty((b, G, R, N), dtype=io, device=dev),
+                                torch.empty((b, H, R, P), dtype=io, device=dev))
+    _check(state_out.h, "state_out.h", (b, H, N, P), state_dtype, dev)
+    sout = State(state_out.h.data_ptr(),
+                 None if state_out.b_last is None else state_out.b_last.data_ptr(),
+                 None if state_out.x_last is None else state_out.x_last.data_ptr())
+    rc = lib().m3_prefill_chunked_noalloc(ctypes.byref(dims), _p(x), _p(dt), _p(A), _p(lam), _p(theta),
+                                          _p(B), _p(C), _p(D), None if sin is None else ctypes.byref(sin),
+                                          ctypes.byref(sout), _p(y), _stream(dev))
+    if rc != 0:
+        raise M3Error("m3_prefill_chunked_noalloc", rc)
+    return y, state_out
 
 
 def decode_step(state: DecodeState, x_t, dt_t, A, lam_t, theta_t, B_t, C_t, D,

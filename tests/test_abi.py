@@ -30,7 +30,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_symbols() == ["m3_backward", "m3_backward_parts", "m3_backward_per_token_A", "m3_backward_varlen",
                                   "m3_backward_workspace_size", "m3_decode_step",
-                                  "m3_decode_step_fused", "m3_prefill_chunked", "m3_prefill_fused",
+                                  "m3_decode_step_fused", "m3_prefill_chunked", "m3_prefill_chunked_noalloc", "m3_prefill_fused",
                                   "m3_prefill_varlen", "m3_prefill_varlen_fused", "m3_prefill_workspace_size", "m3_status_string",
                                   "m3_version"]
 
@@ -323,3 +323,16 @@ def test_backward_per_token_A_rejects_bad_arguments(lib):
     assert call(T=31) == -1
     assert call(cu=None, T=-1) == -3          # T unused without cu_seqlens: only the workspace is missing
     assert call(T=30) == -3
+
+
+def test_noalloc_refuses_shapes_beyond_its_scratch(lib):
+    """m3_prefill_chunked_noalloc checks the workspace its plan needs against its static
+    array before any HIP call: the batch-256 MIMO layer needs about 514 MiB and is refused
+    with M3_ERR_WORKSPACE; bad dims give M3_ERR_INVALID_ARG."""
+    null8 = [None] * 8
+    big = m3scan.make_dims(256, 1024, 64, 1, 64, 128, 4, 64, m3scan.M3_BF16)
+    assert m3scan.workspace_size(big) > m3scan.NOALLOC_SCRATCH_BYTES
+    assert lib.m3_prefill_chunked_noalloc(ctypes.byref(big), *null8, None, None, None, None) == -3
+    bad = _dims(ngroups=3)
+    assert lib.m3_prefill_chunked_noalloc(ctypes.byref(bad), *null8, None, None, None, None) == -1
+    assert lib.m3_prefill_chunked_noalloc(None, *null8, None, None, None, None) == -1
