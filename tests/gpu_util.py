@@ -44,6 +44,25 @@ def slice_err(gpu, ref, head_axis):
     return float(np.max(num / den))
 
 
+def slice_errs(gpu, ref, head_axis):
+    """Per (b, h) slice: the metric of slice_err (max|gpu-ref| / max|ref|), as an array
+    (b, H), and the elementwise diagnostic max |gpu-ref| / (|ref| + 1e-3 max|ref|)
+    over the whole block: it exposes errors on small outputs (early or strongly decayed
+    tokens) that the slice maximum would hide."""
+    g = np.moveaxis(np.asarray(gpu, np.float64), head_axis, 1)
+    r = np.moveaxis(np.asarray(ref, np.float64), head_axis, 1)
+    b, H = g.shape[:2]
+    g = g.reshape(b, H, -1)
+    r = r.reshape(b, H, -1)
+    if g.shape[2] == 0:
+        return np.zeros((b, H)), 0.0
+    d = np.abs(g - r)
+    scale = np.maximum(np.max(np.abs(r), axis=2), 1e-30)
+    per_slice = np.max(d, axis=2) / scale
+    elem = float(np.max(d / (np.abs(r) + 1e-3 * scale[:, :, None])))
+    return per_slice, elem
+
+
 def oracle_args(d):
     return [np64(d[k]) for k in ("x", "dt", "A", "lam", "theta", "B", "C", "D")]
 

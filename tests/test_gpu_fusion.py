@@ -176,3 +176,33 @@ def test_fused_decode_steps_match_oracle(parts, state):
     eh = slice_err(np64(st.h), hr, 1)
     say(f"  y {ey:.2e} h {eh:.2e}")
     assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("carry", [True, False], ids=["carried_B", "no_carry"])
+def test_fused_decode_generic_shape_matches_oracle(carry):
+    """The decode kernel for shapes other than N=128, P=64 (decode_generic) with every fused
+    piece together: per-token A, BCNorm of B and C (its row sums of squares in one wave of
+    64 lanes), biases and the gate, fp32 io, four steps from a random state, with and
+    without a carried previous B."""
+    b, H, G, P, N, R, steps = 2, 6, 3, 12, 24, 3, 4
+    say("fused decode, generic shape", "carry" if carry else "no carry")
+    d = draw(b, steps, H, G, P, N, R, "fp32", 1.0, seed=91)
+    f = _fusion(b, steps, H, R, N, P, "fp32", seed=15, parts=("A_t", "norm", "bias", "gate"))
+    st = rand_state(b, H, G, N, P, R, "fp32", seed=16)
+    if not carry:
+        st = m3scan.DecodeState(st.h, None, None)
+    st0 = (np64(st.h), np64(st.b_last), np64(st.x_last)) if carry else (np64(st.h), None, None)
+    ys = []
+    for t in range(steps):
+        tok = {k: (v[:, t].contiguous() if v.dim() > 1 else v) for k, v in d.items()}
+        ft = {k: (v[:, t].contiguous() if k in ("A_t", "z") else v) for k, v in f.items()}
+        ys.append(m3scan.decode_step_fused(st, *[tok[k] for k in NAMES], **ft)[:, None])
+    torch.cuda.synchronize()
+    kw = {k: np64(v) for k, v in f.items() if k != "A_t"}
+    args = [np64(d[k]) for k in NAMES]
+    args[2] = np64(f["A_t"])
+    yr, hr = oracle.scan_fused(*args, **kw, state_in=st0)
+    ey = slice_err(np64(torch.cat(ys, dim=1)), yr, 2)
+    eh = slice_err(np64(st.h), hr, 1)
+    say(f"  y {ey:.2e} h {eh:.2e}")
+    assert ey <= TOL["fp32"] and eh <= TOL["fp32"]

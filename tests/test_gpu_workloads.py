@@ -1,52 +1,95 @@
 """The workloads at their full sizes, in the launch configuration the benchmark
-times, checked on sampled (batch, head) slices that the oracle computes one by
-one (a full-size oracle run would take hours)."""
+times, checked against the oracle on every (batch, head) slice.
+
+The GPU runs each workload whole (one prefill over all sequences, then the decode
+steps); the oracle then runs block by block (a few batch elements and heads at a
+time, OpenMP over the slices of a block), so host memory stays bounded.  Each
+slice is held to the tolerance of its io dtype with the metric max|gpu - ref| /
+max|ref| over the slice; the elementwise diagnostic max |gpu - ref| / (|ref| +
+1e-3 max|ref|) is printed next to it for every workload."""
+import concurrent.futures
+import os
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_util import TOL, say
+from gpu_util import TOL, say, slice_errs
 from state_space_sequence_scan_amd import CONFIGS, inputs, m3scan
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
 f64 = lambda t: t.detach().double().cpu().numpy()
 
 
-def _slice(d, bi, h, G, H):
-    g = h // (H // G)
-    return [f64(d["x"][bi:bi + 1, :, h:h + 1]), f64(d["dt"][bi:bi + 1, :, h:h + 1]),
-            f64(d["A"][h:h + 1]), f64(d["lam"][bi:bi + 1, :, h:h + 1]),
-            f64(d["theta"][bi:bi + 1, :, g:g + 1]), f64(d["B"][bi:bi + 1, :, g:g + 1]),
-            f64(d["C"][bi:bi + 1, :, g:g + 1]), f64(d["D"][h:h + 1])]
+def _blocks(cfg, heads_per_block):
+    """(batch range, head range) blocks covering every slice; head ranges hold whole groups."""
+    per_group = cfg.nheads // cfg.ngroups
+    if cfg.ngroups == 1:   # one group: any head range sees it whole
+        hb = min(heads_per_block, cfg.nheads)
+    else:
+        hb = max(per_group, (heads_per_block // per_group) * per_group)
+    for b0 in range(cfg.batch):
+        for h0 in range(0, cfg.nheads, hb):
+            yield b0, b0 + 1, h0, min(cfg.nheads, h0 + hb)
 
 
-def _err(g, r):
-    return float(np.max(np.abs(g - r)) / np.max(np.abs(r)))
+def _block_args(d, cfg, b0, b1, h0, h1, At=None):
+    per_group = cfg.nheads // cfg.ngroups
+    g0, g1 = h0 // per_group, (h1 - 1) // per_group + 1
+    return [f64(d["x"][b0:b1, :, h0:h1]), f64(d["dt"][b0:b1, :, h0:h1]),
+            f64(d["A"][h0:h1]) if At is None else f64(At[b0:b1, :, h0:h1]),
+            f64(d["lam"][b0:b1, :, h0:h1]), f64(d["theta"][b0:b1, :, g0:g1]),
+            f64(d["B"][b0:b1, :, g0:g1]), f64(d["C"][b0:b1, :, g0:g1]), f64(d["D"][h0:h1])]
+
+
+class Tally:
+    def __init__(self, name, tol):
+        self.name, self.tol = name, tol
+        self.worst = {}
+        self.elem = 0.0
+        self.slices = 0
+
+    def add(self, what, per_slice, elem, where):
+        w = float(np.max(per_slice)) if per_slice.size else 0.0
+        if w > self.worst.get(what, (-1.0, None))[0]:
+            i = np.unravel_index(int(np.argmax(per_slice)), per_slice.shape) if per_slice.size else ()
+            self.worst[what] = (w, (where, tuple(int(v) for v in i)))
+        self.elem = max(self.elem, elem)
+        assert w <= self.tol, f"{self.name} {what} {where}: slice error {w:.3e} > {self.tol}"
+
+    def report(self):
+        say(f"  {self.name}: {self.slices} slices; worst per-slice error "
+            + ", ".join(f"{k} {v[0]:.2e} at {v[1]}" for k, v in self.worst.items())
+            + f"; elementwise diagnostic max {self.elem:.2e}")
 
 
 @pytest.mark.parametrize("name", ["siso_l256_fp32", "nanomamba3", "siso_l8192", "mimo4_l16384"])
-def test_prefill_workload_sampled(name):
+def test_prefill_workload_every_slice(name):
     cfg = CONFIGS[name]
     say("workload", name, cfg.label)
     d = inputs.draw_config(cfg, device="cuda")
     y, st = m3scan.prefill(d["x"], d["dt"], d["A"], d["lam"], d["theta"], d["B"], d["C"], d["D"],
                            cfg.chunk)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(cfg.seed)
-    picks = [(0, 0), (cfg.batch - 1, cfg.nheads - 1)] + \
-            [(int(rng.integers(cfg.batch)), int(rng.integers(cfg.nheads))) for _ in range(2)]
-    for bi, h in picks:
-        yr, hr = oracle.scan(*_slice(d, bi, h, cfg.ngroups, cfg.nheads))
-        ey = _err(f64(y[bi:bi + 1, :, h:h + 1]), yr)
-        eh = _err(f64(st.h[bi:bi + 1, h:h + 1]), hr)
-        say(f"  slice b={bi} h={h}: y {ey:.2e} state {eh:.2e}")
-        assert ey <= TOL[cfg.io_dtype] and eh <= TOL[cfg.io_dtype]
+    tally = Tally(name, TOL[cfg.io_dtype])
+    for b0, b1, h0, h1 in _blocks(cfg, 16):
+        yr, hr = oracle.scan(*_block_args(d, cfg, b0, b1, h0, h1))
+        tally.add("y", *slice_errs(f64(y[b0:b1, :, h0:h1]), yr, 2), (b0, h0))
+        tally.add("h", *slice_errs(f64(st.h[b0:b1, h0:h1]), hr, 1), (b0, h0))
+        tally.slices += (b1 - b0) * (h1 - h0)
+        say(f"  block b{b0} h{h0}..{h1 - 1} done")
+    assert tally.slices == cfg.batch * cfg.nheads
+    # the carry is a copy of the last token's B and X: bit-exact
+    assert torch.equal(st.b_last, d["B"][:, -1]) and torch.equal(st.x_last, d["x"][:, -1])
+    tally.report()
 
 
-def test_decode_workload_sampled():
-    """1.5B MIMO R=4 layer, batch 256: 1024-token prefill, then 512 decode steps."""
+def test_decode_workload_every_slice():
+    """1.5B MIMO R=4 layer, batch 256: 1024-token prefill, then 512 decode steps; every
+    (batch, head) slice's 1536 outputs and final state against one oracle scan of the
+    1536 tokens."""
     cfg = CONFIGS["mimo4_decode_b256"]
     say("workload mimo4_decode_b256", cfg.label)
     d = inputs.draw_config(cfg, device="cuda")
@@ -58,31 +101,30 @@ def test_decode_workload_sampled():
         m3scan.decode_step(st, dd["x"][t], dd["dt"][t], d["A"], dd["lam"][t], dd["theta"][t],
                            dd["B"][t], dd["C"][t], d["D"], y_t=ydec[t])
     torch.cuda.synchronize()
-    for bi, h in [(0, 0), (255, 63), (137, 21)]:
-        g = h // (cfg.nheads // cfg.ngroups)
-        pre = _slice(d, bi, h, cfg.ngroups, cfg.nheads)
-        dec = [f64(dd["x"][:, bi:bi + 1, h:h + 1].transpose(0, 1)),
-               f64(dd["dt"][:, bi:bi + 1, h:h + 1].transpose(0, 1)), pre[2],
-               f64(dd["lam"][:, bi:bi + 1, h:h + 1].transpose(0, 1)),
-               f64(dd["theta"][:, bi:bi + 1, g:g + 1].transpose(0, 1)),
-               f64(dd["B"][:, bi:bi + 1, g:g + 1].transpose(0, 1)),
-               f64(dd["C"][:, bi:bi + 1, g:g + 1].transpose(0, 1)), pre[7]]
-        full = [np.concatenate([a, c], axis=1) if a.ndim > 1 else a for a, c in zip(pre, dec)]
-        yr, hr = oracle.scan(*full)
-        yg = np.concatenate([f64(y[bi:bi + 1, :, h:h + 1]),
-                             f64(ydec[:, bi:bi + 1, h:h + 1].transpose(0, 1))], axis=1)
-        ey, eh = _err(yg, yr), _err(f64(st.h[bi:bi + 1, h:h + 1]), hr)
-        say(f"  slice b={bi} h={h}: y {ey:.2e} state {eh:.2e}")
-        assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+    tally = Tally("mimo4_decode_b256", TOL["bf16"])
+    nb = 8
+    for b0 in range(0, cfg.batch, nb):
+        b1 = b0 + nb
+        cat = lambda k: np.concatenate([f64(d[k][b0:b1]), f64(dd[k][:, b0:b1].transpose(0, 1))], axis=1)
+        yr, hr = oracle.scan(cat("x"), cat("dt"), f64(d["A"]), cat("lam"), cat("theta"), cat("B"), cat("C"),
+                             f64(d["D"]))
+        yg = np.concatenate([f64(y[b0:b1]), f64(ydec[:, b0:b1].transpose(0, 1))], axis=1)
+        tally.add("y", *slice_errs(yg, yr, 2), (b0, 0))
+        tally.add("h", *slice_errs(f64(st.h[b0:b1]), hr, 1), (b0, 0))
+        tally.slices += nb * cfg.nheads
+        say(f"  batches {b0}..{b1 - 1} done")
+    assert tally.slices == cfg.batch * cfg.nheads
+    tally.report()
 
 
 @pytest.mark.parametrize("name", ["nanomamba3", "mimo4_l16384"])
-def test_backward_workload_sampled(name):
-    """The backward at the full size of a training-shaped workload (nanomamba3 is the benchmark's
-    default for it): per-head gradients dx, ddt, dlambda of sampled (batch, head) slices
-    against the oracle's adjoint run on that slice alone (group-shared and batch-summed
-    gradients mix slices and are covered by the small-size tests)."""
+def test_backward_workload_every_slice(name):
+    """The backward at the full size of a training-shaped workload: every gradient.  The
+    per-head ones (dx, ddt, dlambda) slice by slice; the group-shared ones (dB, dC, dtheta,
+    summed over a group's heads) per batch element, after the head blocks of that element
+    are summed; dA and dD (summed over batch and tokens) over the whole tensor."""
     cfg = CONFIGS[name]
+    assert cfg.ngroups == 1   # the group-shared sums below run over every head
     say("backward workload", name)
     d = inputs.draw_config(cfg, device="cuda")
     g = torch.Generator(device="cuda").manual_seed(cfg.seed + 11)
@@ -90,18 +132,37 @@ def test_backward_workload_sampled(name):
     gr = m3scan.backward(d["x"], d["dt"], d["A"], d["lam"], d["theta"], d["B"], d["C"], d["D"], dy,
                          want_state_grads=False)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(cfg.seed + 1)
-    for bi, h in [(0, 0), (cfg.batch - 1, cfg.nheads - 1), (int(rng.integers(cfg.batch)), int(rng.integers(cfg.nheads)))]:
-        ref = oracle.scan_backward(*_slice(d, bi, h, cfg.ngroups, cfg.nheads), f64(dy[bi:bi + 1, :, h:h + 1]))
-        for k in ("dx", "ddt", "dlam"):
-            gv = f64(gr[k][bi:bi + 1, :, h:h + 1])
-            e = _err(gv, ref[k])
-            say(f"  ({bi},{h}) {k} {e:.2e}")
-            assert e <= 1e-3, (bi, h, k, e)
+    tally = Tally(f"{name} backward", 1e-3)
+    dA = np.zeros(cfg.nheads)
+    dD = np.zeros(cfg.nheads)
+    # The oracle's backward runs its batch elements in parallel; here every call is one
+    # (batch, head) slice, and the slices of a batch element run side by side on host threads
+    # (the C oracle runs outside the interpreter lock).
+    workers = min(16, os.cpu_count() or 1)
+    for b0 in range(cfg.batch):
+        ins = [(_block_args(d, cfg, b0, b0 + 1, h, h + 1), f64(dy[b0:b0 + 1, :, h:h + 1])) for h in range(cfg.nheads)]
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            refs = list(ex.map(lambda a: oracle.scan_backward(*a[0], a[1], nthreads=1), ins))
+        shared = {k: sum(r[k] for r in refs) for k in ("dB", "dC", "dtheta")}   # G = 1: over every head
+        for h, ref in enumerate(refs):
+            for k, ax in (("dx", 2), ("ddt", 2), ("dlam", 2)):
+                tally.add(k, *slice_errs(f64(gr[k][b0:b0 + 1, :, h:h + 1]), ref[k], ax), (b0, h))
+            dA[h] += ref["dA"][0]
+            dD[h] += ref["dD"][0]
+        for k, ax in (("dB", 2), ("dC", 2), ("dtheta", 2)):
+            tally.add(k, *slice_errs(f64(gr[k][b0:b0 + 1]), shared[k], ax), (b0, "groups"))
+        tally.slices += cfg.nheads
+        say(f"  batch element {b0} done")
+    for k, ref in (("dA", dA), ("dD", dD)):
+        e = float(np.max(np.abs(f64(gr[k]) - ref)) / np.max(np.abs(ref)))
+        say(f"  {k}: {e:.2e}")
+        assert e <= 1e-3, (k, e)
+    tally.report()
 
 
-def test_fused_prefill_workload_sampled():
-    """The fused prologue/epilogue at the full size of the 1.5B-scale SISO layer."""
+def test_fused_prefill_workload_every_slice():
+    """The fused prologue/epilogue (per-token A, BCNorm and bias of B and C, gate) at the
+    full size of the 1.5B-scale SISO layer, every slice."""
     cfg = CONFIGS["siso_l8192"]
     say("fused workload siso_l8192")
     d = inputs.draw_config(cfg, device="cuda")
@@ -116,13 +177,14 @@ def test_fused_prefill_workload_sampled():
     y, st = m3scan.prefill_fused(d["x"], d["dt"], d["A"], d["lam"], d["theta"], d["B"], d["C"], d["D"],
                                  cfg.chunk, **fz)
     torch.cuda.synchronize()
-    for bi, h in [(0, 0), (cfg.batch - 1, cfg.nheads - 1)]:
-        args = _slice(d, bi, h, cfg.ngroups, cfg.nheads)
-        args[2] = f64(fz["A_t"][bi:bi + 1, :, h:h + 1])
+    tally = Tally("siso_l8192 fused", TOL["bf16"])
+    for b0, b1, h0, h1 in _blocks(cfg, 64):
+        args = _block_args(d, cfg, b0, b1, h0, h1, At=fz["A_t"])
         yr, hr = oracle.scan_fused(*args, b_norm_w=f64(fz["b_norm_w"]), c_norm_w=f64(fz["c_norm_w"]),
                                    b_bias=f64(fz["b_bias"]), c_bias=f64(fz["c_bias"]),
-                                   z=f64(fz["z"][bi:bi + 1, :, h:h + 1]))
-        ey = _err(f64(y[bi:bi + 1, :, h:h + 1]), yr)
-        eh = _err(f64(st.h[bi:bi + 1, h:h + 1]), hr)
-        say(f"  ({bi},{h}) y {ey:.2e} h {eh:.2e}")
-        assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+                                   z=f64(fz["z"][b0:b1, :, h0:h1]))
+        tally.add("y", *slice_errs(f64(y[b0:b1, :, h0:h1]), yr, 2), (b0, h0))
+        tally.add("h", *slice_errs(f64(st.h[b0:b1, h0:h1]), hr, 1), (b0, h0))
+        tally.slices += (b1 - b0) * (h1 - h0)
+        say(f"  block b{b0} done")
+    tally.report()
