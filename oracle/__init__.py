@@ -9,7 +9,9 @@ Contents
                          fp64 loop over t (the definition written out).
   * ``scan_fused``    -- the scan with the fused prologue/epilogue of a Mamba-3
                          layer written out around it: RMSNorm and bias of B and C
-                         (``bc_norm``), per-token A, the output gate (``gate``).
+                         (``bc_norm``), per-token A, angles per head over shared B and
+                         C (``expand_groups``), the output gate (``gate``) and the
+                         output RMSNorm (``out_norm``).
   * ``scan_backward`` -- its reverse-mode derivative (the adjoint loop of
                          ``m3_oracle.c``), pinned by finite differences of ``scan``.
   * ``m3_oracle_np``  -- two independent numpy formulations used to pin it:
@@ -214,18 +216,53 @@ def gate(y, z):
     return y * z / (1.0 + np.exp(-z))
 
 
+def out_norm(y, weight, eps: float = 1e-6):
+    """RMSNorm of the scan's output before the out-projection (the Mamba-3 paper note,
+    "Architecture": kept in hybrid models): each row y[b, t, h, r, :] of P values divided by
+    its root mean square sqrt(mean(y^2) + eps) and multiplied by weight[h, :] (one weight per
+    channel of the head, shared by its R rows).  fp64."""
+    y = _f64(y)
+    rms = np.sqrt(np.mean(y * y, axis=-1, keepdims=True) + eps)
+    return y / rms * _f64(weight)[None, None, :, None, :]
+
+
+def expand_groups(M, groups: int):
+    """Repeat each group of M (b, L, G, ...) over groups // G consecutive groups: the B or C
+    a finer grouping of heads sees (group j of the finer grouping holds group j // (groups // G))."""
+    G = M.shape[2]
+    assert groups % G == 0
+    return np.repeat(_f64(M), groups // G, axis=2)
+
+
 def scan_fused(x, dt, A, lam, theta, B, C, D, b_norm_w=None, c_norm_w=None, b_bias=None,
-               c_bias=None, eps: float = 1e-6, z=None, state_in=None, round_after=None):
+               c_bias=None, eps: float = 1e-6, z=None, state_in=None, round_after=None,
+               out_norm_w=None):
     """``scan`` with the layer's prologue and epilogue around it: B and C through
     ``bc_norm`` (the carried previous B of state_in as well), A per head (H,) or per token
-    (b,L,H), and y through ``gate`` when z is given.  Returns (y, h_out)."""
+    (b,L,H), y through ``gate`` when z is given and then through ``out_norm`` when
+    out_norm_w (H, P) is given.
+
+    theta (b, L, Gt, N/2) may have more groups than B and C (G): G divides Gt, Gt divides H,
+    head h turns with angle group h // (H/Gt) and reads B, C group h // (H/G); with Gt = H
+    every head has its own angles over shared B and C.  Each head then sees exactly the
+    grouped scan of B and C repeated over the angle groups (``expand_groups``).
+    Returns (y, h_out)."""
     Bn = bc_norm(B, b_norm_w, b_bias, eps)
     Cn = bc_norm(C, c_norm_w, c_bias, eps)
     st = state_in
+    bl = None
     if state_in is not None and state_in[1] is not None:
         bl = bc_norm(_f64(state_in[1])[:, None], b_norm_w, b_bias, eps)[:, 0]
         st = (state_in[0], bl, state_in[2])
+    Gt = theta.shape[2]
+    if Gt != B.shape[2]:
+        Bn = expand_groups(Bn, Gt)
+        Cn = expand_groups(Cn, Gt)
+        if bl is not None:
+            st = (st[0], expand_groups(bl[:, None], Gt)[:, 0], st[2])
     y, h = scan(x, dt, A, lam, theta, Bn, Cn, D, state_in=st, round_after=round_after)
     if z is not None:
         y = gate(y, z)
+    if out_norm_w is not None:
+        y = out_norm(y, out_norm_w, eps)
     return y, h

@@ -97,3 +97,63 @@ def test_fused_split_scan_normalises_the_carry():
         bl, xl = d["B"][:, t], d["x"][:, t]
     np.testing.assert_allclose(np.concatenate(ys, axis=1), y_all, rtol=0, atol=1e-12)
     np.testing.assert_allclose(h, h_all, rtol=0, atol=1e-12)
+
+
+def test_out_norm_matches_torch_rms_norm():
+    """The output RMSNorm against torch's rms_norm over the last axis, head by head with
+    that head's weight."""
+    rng = np.random.default_rng(6)
+    b, L, H, R, P = 2, 3, 4, 2, 8
+    y = rng.standard_normal((b, L, H, R, P)) * 2.0
+    w = rng.standard_normal((H, P))
+    got = oracle.out_norm(y, w, eps=1e-5)
+    t = torch.tensor(y)
+    ref = torch.stack([torch.nn.functional.rms_norm(t[:, :, h], (P,), torch.tensor(w[h]), eps=1e-5)
+                       for h in range(H)], dim=2)
+    np.testing.assert_allclose(got, ref.numpy(), rtol=1e-13, atol=1e-13)
+
+
+def test_out_norm_follows_the_gate():
+    """scan_fused applies the gate, then the norm: equal to out_norm(gate(y, z))."""
+    d = rand_case(b=1, L=5, H=2, G=1, P=4, N=4, R=2, seed=24)
+    rng = np.random.default_rng(7)
+    z = rng.standard_normal(d["x"].shape)
+    w = rng.standard_normal((2, 4))
+    y0, _ = oracle.scan(*_args(d))
+    y1, _ = oracle.scan_fused(*_args(d), z=z, out_norm_w=w, eps=1e-6)
+    np.testing.assert_allclose(y1, oracle.out_norm(oracle.gate(y0, z), w, 1e-6), rtol=1e-14, atol=1e-14)
+
+
+def test_theta_groups_equal_within_a_group_is_the_grouped_scan():
+    """Angles per head that are equal over the heads of each B/C group reproduce the
+    grouped scan bit for bit (state carried in, with a carry, included)."""
+    b, L, H, G, P, N, R = 2, 7, 6, 2, 3, 6, 2
+    d = rand_case(b=b, L=L, H=H, G=G, P=P, N=N, R=R, seed=25)
+    st = rand_state(d, seed=8)
+    y0, h0 = oracle.scan_fused(*_args(d), state_in=st)
+    args = list(_args(d))
+    args[4] = np.repeat(d["theta"], H // G, axis=2)      # (b, L, H, N/2): each head its group's angles
+    y1, h1 = oracle.scan_fused(*args, state_in=st)
+    np.testing.assert_array_equal(y0, y1)
+    np.testing.assert_array_equal(h0, h1)
+
+
+def test_theta_per_head_is_each_head_alone():
+    """Distinct angles per head over shared B and C: every head equals a one-head scan with
+    its own angles and its group's B and C (the head-to-group maps of both groupings)."""
+    b, L, H, G, Gt, P, N, R = 2, 6, 8, 2, 4, 3, 4, 2
+    d = rand_case(b=b, L=L, H=H, G=G, P=P, N=N, R=R, seed=26)
+    rng = np.random.default_rng(9)
+    theta_t = rng.uniform(-np.pi, np.pi, size=(b, L, Gt, N // 2))
+    st = rand_state(d, seed=10)
+    args = list(_args(d))
+    args[4] = theta_t
+    y, hh = oracle.scan_fused(*args, state_in=st)
+    for h in range(H):
+        g, j = h // (H // G), h // (H // Gt)
+        yh, hs = oracle.scan(d["x"][:, :, h:h + 1], d["dt"][:, :, h:h + 1], d["A"][h:h + 1],
+                             d["lam"][:, :, h:h + 1], theta_t[:, :, j:j + 1], d["B"][:, :, g:g + 1],
+                             d["C"][:, :, g:g + 1], d["D"][h:h + 1],
+                             state_in=(st[0][:, h:h + 1], st[1][:, g:g + 1], st[2][:, h:h + 1]))
+        np.testing.assert_allclose(y[:, :, h:h + 1], yh, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(hh[:, h:h + 1], hs, rtol=0, atol=1e-13)
