@@ -173,9 +173,10 @@ m3_status m3_decode_step(const m3_dims* dims, void* h, const void* b_last,
 /*
  * Fused prologue and epilogue of a Mamba-3 layer around the scan (the pieces of
  * the layer next to it on the Mamba-3 blog, part 1, "Normalization" and
- * "Removing the short convolution", and the per-token A of the paper note's
- * discretisation).  Every pointer may be NULL (that piece is off); fp32 unless
- * stated.
+ * "Removing the short convolution", the per-token A of the paper note's
+ * discretisation, the output norm of its "Architecture" section) and the layout
+ * with angles per head.  Every pointer may be NULL (that piece is off); fp32
+ * unless stated.
  *   A_t:       per-token decay rate replacing A: (batch, L, H) for a prefill,
  *              (batch, H) for a decode step (A must still be passed; it is not read).
  *   b_norm_w:  (R, N): B[b,t,g,r,:] is divided by its root mean square
@@ -187,6 +188,16 @@ m3_status m3_decode_step(const m3_dims* dims, void* h, const void* b_last,
  *   z:         gate, io dtype, laid out as y: y is returned as y * silu(z),
  *              silu(v) = v / (1 + exp(-v)).
  *   norm_eps:  > 0 when a norm weight is given.
+ *   out_norm_w: (H, P): RMSNorm of the output before the out-projection (the paper
+ *              note's "Architecture" section: kept in hybrid models): each row
+ *              y[.., h, r, :] of P values is divided by sqrt(mean(y^2) + norm_eps) and
+ *              multiplied by out_norm_w[h, :], after the gate when both are given.
+ *   theta_groups: 0, or the number Gt of angle groups when the angles are grouped more
+ *              finely than B and C (Gt = H: every head turns with its own angles over
+ *              the B and C its group shares).  G divides Gt and Gt divides H; theta is
+ *              then (batch, L, Gt, N/2) ((batch, Gt, N/2) for a decode step,
+ *              (total_tokens, Gt, N/2) for a packed batch) and head h turns with angle
+ *              group h / (H / Gt).  0 means Gt = G (the layout of the plain calls).
  */
 typedef struct {
     const float* A_t;
@@ -196,12 +207,22 @@ typedef struct {
     const float* c_bias;
     const void* z;
     float norm_eps;
+    const float* out_norm_w;
+    int32_t theta_groups;
 } m3_fusion;
 
+/* Bytes of device workspace m3_prefill_fused and m3_prefill_varlen_fused need for these
+ * dims and this fusion (equal to m3_prefill_workspace_size when fusion->theta_groups is 0
+ * or G; angles per head need room for operands prepared per angle group).
+ * Errors: those of m3_prefill_workspace_size, and M3_ERR_INVALID_ARG for a NULL fusion or
+ * bad theta_groups. */
+m3_status m3_prefill_fused_workspace_size(const m3_dims* dims, const m3_fusion* fusion, size_t* bytes);
+
 /* m3_prefill_chunked with the fused prologue/epilogue of `fusion` (non-NULL).
- * Same workspace size (m3_prefill_workspace_size); the other arguments, layouts and
- * errors as m3_prefill_chunked, plus M3_ERR_INVALID_ARG for a NULL fusion or a norm
- * weight with norm_eps <= 0. */
+ * The workspace size depends on fusion->theta_groups: query it with
+ * m3_prefill_fused_workspace_size.  The other arguments, layouts and errors as
+ * m3_prefill_chunked, plus M3_ERR_INVALID_ARG for a NULL fusion, a norm weight with
+ * norm_eps <= 0, or theta_groups not a multiple of G dividing H. */
 m3_status m3_prefill_fused(const m3_dims* dims, const void* x, const float* dt, const float* A,
                            const float* lambda, const float* theta, const void* B, const void* C,
                            const float* D, const m3_fusion* fusion, const m3_state* state_in,
@@ -212,8 +233,8 @@ m3_status m3_prefill_fused(const m3_dims* dims, const void* x, const float* dt, 
  * the layer next to the scan, Mamba-3 blog part 1, "Normalization" and "Removing the short
  * convolution", and the per-token A of the paper note's "Solution 1"), on a packed
  * batch: A_t is (total_tokens, H) and z is laid out as y, (total_tokens, H, R, P); a
- * carried b_last of state_in (per sequence) is normalised like B.  Same workspace size
- * (m3_prefill_workspace_size); the other arguments, layouts and errors as
+ * carried b_last of state_in (per sequence) is normalised like B.  Workspace size:
+ * m3_prefill_fused_workspace_size; the other arguments, layouts and errors as
  * m3_prefill_varlen, plus those of m3_prefill_fused. */
 m3_status m3_prefill_varlen_fused(const m3_dims* dims, const int64_t* cu_seqlens, int64_t total_tokens,
                                   const void* x, const float* dt, const float* A, const float* lambda,

@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int32_t kVersion = 108;  // 0.1.8: fused prologue/epilogue on packed batches
+constexpr int32_t kVersion = 200;  // 0.2.0: output norm, angles per head, allocation-free prefill
 constexpr size_t kMaxLds = 160 * 1024;
 
 bool dims_ok(const m3_dims* d, bool prefill) {
@@ -43,6 +43,24 @@ m3::PrefillArgs make_prefill_args(const m3_dims* d) {
     a.cu = nullptr;
     a.T = d->batch * d->seqlen;
     return a;
+}
+
+// The fused pieces into the kernels' descriptor; false for invalid ones (a norm weight
+// without a positive eps, angle groups that are not a multiple of G dividing H).
+bool copy_fusion(const m3_dims* d, const m3_fusion* f, m3::Fusion* out) {
+    out->At = f->A_t;
+    out->bnw = f->b_norm_w;
+    out->cnw = f->c_norm_w;
+    out->bbias = f->b_bias;
+    out->cbias = f->c_bias;
+    out->z = f->z;
+    out->eps = f->norm_eps;
+    out->onw = f->out_norm_w;
+    out->Gt = f->theta_groups;
+    if ((out->bnw || out->cnw || out->onw) && !(f->norm_eps > 0.f)) return false;
+    if (f->theta_groups < 0) return false;
+    if (f->theta_groups > 0 && (f->theta_groups % d->ngroups != 0 || d->nheads % f->theta_groups != 0)) return false;
+    return true;
 }
 
 }  // namespace
@@ -128,6 +146,16 @@ m3_status m3_prefill_workspace_size(const m3_dims* dims, size_t* bytes) {
     return M3_OK;
 }
 
+m3_status m3_prefill_fused_workspace_size(const m3_dims* dims, const m3_fusion* fusion, size_t* bytes) {
+    if (!bytes || !fusion || !dims_ok(dims, true)) return M3_ERR_INVALID_ARG;
+    m3::PrefillArgs a = make_prefill_args(dims);
+    if (!copy_fusion(dims, fusion, &a.fu)) return M3_ERR_INVALID_ARG;
+    const m3::PrefillPlan plan = m3::plan_prefill(a);
+    if (plan.path == m3::PrefillPath::Unsupported) return M3_ERR_UNSUPPORTED;
+    *bytes = plan.workspace;
+    return M3_OK;
+}
+
 }  // extern "C"
 
 namespace {
@@ -171,16 +199,7 @@ m3_status prefill_common(const m3_dims* dims, const int64_t* cu, int64_t total_t
     }
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
-    if (fu) {
-        a.fu.At = fu->A_t;
-        a.fu.bnw = fu->b_norm_w;
-        a.fu.cnw = fu->c_norm_w;
-        a.fu.bbias = fu->b_bias;
-        a.fu.cbias = fu->c_bias;
-        a.fu.z = fu->z;
-        a.fu.eps = fu->norm_eps;
-        if ((a.fu.bnw || a.fu.cnw) && !(fu->norm_eps > 0.f)) return M3_ERR_INVALID_ARG;
-    }
+    if (fu && !copy_fusion(dims, fu, &a.fu)) return M3_ERR_INVALID_ARG;
     const m3::PrefillPlan plan = m3::plan_prefill(a);
     if (plan.path == m3::PrefillPath::Unsupported) return M3_ERR_UNSUPPORTED;
     if (plan.workspace > 0 && (!workspace || workspace_bytes < plan.workspace)) return M3_ERR_WORKSPACE;
@@ -313,16 +332,7 @@ m3_status decode_common(const m3_dims* dims, void* h, const void* b_last, const 
     a.has_carry = b_last != nullptr;
     a.bf16 = dims->io_dtype == M3_BF16;
     a.state_bf16 = dims->state_dtype == M3_BF16;
-    if (fu) {
-        a.fu.At = fu->A_t;
-        a.fu.bnw = fu->b_norm_w;
-        a.fu.cnw = fu->c_norm_w;
-        a.fu.bbias = fu->b_bias;
-        a.fu.cbias = fu->c_bias;
-        a.fu.z = fu->z;
-        a.fu.eps = fu->norm_eps;
-        if ((a.fu.bnw || a.fu.cnw) && !(fu->norm_eps > 0.f)) return M3_ERR_INVALID_ARG;
-    }
+    if (fu && !copy_fusion(dims, fu, &a.fu)) return M3_ERR_INVALID_ARG;
     // one workgroup of at most 256 threads per (b, h): under 2^32 work-items per launch
     if (dims->batch * dims->nheads >= (int64_t{1} << 24)) return M3_ERR_UNSUPPORTED;
     if (!m3::decode_supported(a)) return M3_ERR_UNSUPPORTED;

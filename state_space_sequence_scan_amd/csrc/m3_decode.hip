@@ -108,6 +108,25 @@ __device__ __forceinline__ void fuse_bc(float* sB, float* sC, float* sBp, float*
     __syncthreads();
 }
 
+// Output RMSNorm scales: rows r < R of P values in sO (LDS, fp32) into
+// sRs[r] = 1 / sqrt(mean(row^2) + eps), one wave (or the whole block when it has fewer
+// than 64 threads) per row at a time.  Ends with a barrier.
+__device__ __forceinline__ void row_rms(const float* sO, float* sRs, int R, int P, int nt, float eps) {
+    const int tid = threadIdx.x, width = nt < 64 ? nt : 64, lane = tid % width, wave = tid / width;
+    const int nwaves = (nt + width - 1) / width;
+    for (int r = wave; r < R; r += nwaves) {
+        float ss = 0.f;
+        for (int q = lane; q < P; q += width) ss += sO[r * P + q] * sO[r * P + q];
+        if (width == 64) {
+            ss = wave_sum(ss);
+        } else {
+            for (int off = 1; off < width; off <<= 1) ss += __shfl_xor(ss, off, width);
+        }
+        if (lane == 0) sRs[r] = rsqrtf(ss / P + eps);
+    }
+    __syncthreads();
+}
+
 // Fast path.  One workgroup of NT threads per (b, h).  Thread tid owns the
 // CW-column block c = tid % PC (PC = P/CW) and the rotation pairs
 // k = kk + TPG * j (kk = tid / PC, j < PPT), i.e. 2 * PPT state rows x CW columns.
@@ -131,6 +150,7 @@ __global__ __launch_bounds__(NT) void decode_fast(
     const int bh = blockIdx.x;
     const int b = bh / H, hh = bh - b * H;
     const int g = hh / (H / G);
+    const int Gt = fu.tgroups(G), gt = hh / (H / Gt);   // angle group
     const int tid = threadIdx.x;
     const int c = tid % PC;
     const int kk = tid / PC;
@@ -171,12 +191,12 @@ __global__ __launch_bounds__(NT) void decode_fast(
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
         const int k = tid + NT * e;
-        vth[e] = (k < KP) ? theta_t[(static_cast<size_t>(b) * G + g) * KP + k] : 0.f;
+        vth[e] = (k < KP) ? theta_t[(static_cast<size_t>(b) * Gt + gt) * KP + k] : 0.f;
     }
     // Fused pieces of this thread's elements: norm weights and biases of its B/C entries,
-    // the gate input of its outputs.
+    // the gate input and output-norm weight of its outputs.
     constexpr int FS = FU ? SPT : 1, FX = FU ? XPT : 1;
-    float wbn[FS], wcn[FS], wbb[FS], wcb[FS], vz[FX];
+    float wbn[FS], wcn[FS], wbb[FS], wcb[FS], vz[FX], won[FX];
     if constexpr (FU) {
 #pragma unroll
         for (int e = 0; e < SPT; ++e) {
@@ -191,6 +211,7 @@ __global__ __launch_bounds__(NT) void decode_fast(
         for (int e = 0; e < XPT; ++e) {
             const int i = tid + NT * e;
             vz[e] = (fu.z && i < R * P) ? io<T>::load(static_cast<const T*>(fu.z) + hofs + i) : 0.f;
+            won[e] = (fu.onw && i < R * P) ? fu.onw[hh * P + i % P] : 1.f;
         }
     }
 
@@ -319,19 +340,43 @@ __global__ __launch_bounds__(NT) void decode_fast(
     }
     __syncthreads();
     const float dv = D[hh];
+    float yo[XPT];
 #pragma unroll
     for (int e = 0; e < XPT; ++e) {
         const int i = tid + NT * e;
+        float acc = 0.f;
         if (i < R * P) {
-            float acc = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) acc += (&sY[w][0][0])[i];
             acc += dv * (&sX[0][0])[i];
             if constexpr (FU) {
                 if (fu.z) acc *= silu(vz[e]);
             }
-            io<T>::store(y_t + hofs + i, acc);
         }
+        yo[e] = acc;
+    }
+    if constexpr (FU) {
+        if (fu.onw) {   // output RMSNorm over each row of P outputs (uniform branch)
+            __shared__ float sO[R * P];
+            __shared__ float sRs[R];
+#pragma unroll
+            for (int e = 0; e < XPT; ++e) {
+                const int i = tid + NT * e;
+                if (i < R * P) sO[i] = yo[e];
+            }
+            __syncthreads();
+            row_rms(sO, sRs, R, P, NT, fu.eps);
+#pragma unroll
+            for (int e = 0; e < XPT; ++e) {
+                const int i = tid + NT * e;
+                if (i < R * P) yo[e] *= sRs[i / P] * won[e];
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < XPT; ++e) {
+        const int i = tid + NT * e;
+        if (i < R * P) io<T>::store(y_t + hofs + i, yo[e]);
     }
 }
 
@@ -354,10 +399,13 @@ __global__ __launch_bounds__(64) void decode_generic(
     float* sCs = sXp + R * P;       // KP
     float* sSn = sCs + KP;          // KP
     float* sScale = sSn + KP;       // 3R
+    float* sO = sScale + 3 * R;     // R*P outputs (output norm only)
+    float* sRs = sO + R * P;        // R
 
     const int bh = blockIdx.x;
     const int b = bh / H, hh = bh - b * H;
     const int g = hh / (H / G);
+    const int Gt = fu.tgroups(G), gt = hh / (H / Gt);   // angle group
     const int tid = threadIdx.x;
     const size_t gofs = (static_cast<size_t>(b) * G + g) * R * N;
     const size_t hofs = static_cast<size_t>(bh) * R * P;
@@ -372,7 +420,7 @@ __global__ __launch_bounds__(64) void decode_generic(
     }
     for (int k = tid; k < KP; k += blockDim.x) {
         float sn, cs;
-        sincos_acc(theta_t[(static_cast<size_t>(b) * G + g) * KP + k], &sn, &cs);
+        sincos_acc(theta_t[(static_cast<size_t>(b) * Gt + gt) * KP + k], &sn, &cs);
         sCs[k] = cs;
         sSn[k] = sn;
     }
@@ -404,9 +452,23 @@ __global__ __launch_bounds__(64) void decode_generic(
         for (int r = 0; r < R; ++r) {
             float v = yacc[r] + D[hh] * sX[r * P + p];
             if (fu.z) v *= silu(io<T>::load(static_cast<const T*>(fu.z) + hofs + r * P + p));
-            io<T>::store(y_t + hofs + r * P + p, v);
+            if (fu.onw)
+                sO[r * P + p] = v;   // stored after the norm below
+            else
+                io<T>::store(y_t + hofs + r * P + p, v);
         }
     }
+    if (fu.onw) {   // output RMSNorm over each row of P outputs
+        __syncthreads();
+        row_rms(sO, sRs, R, P, blockDim.x, fu.eps);
+        for (int i = tid; i < R * P; i += blockDim.x)
+            io<T>::store(y_t + hofs + i, sO[i] * sRs[i / P] * fu.onw[hh * P + i % P]);
+    }
+}
+
+// Dynamic LDS of decode_generic: staged operands, scales, and the outputs of the norm.
+static size_t generic_decode_lds(const DecodeArgs& a) {
+    return sizeof(float) * (3 * a.R * a.N + 2 * a.R * a.P + a.N + 3 * a.R + a.R * a.P + a.R);
 }
 
 // Four columns per thread for either state dtype.  (Eight bf16 columns, for 16-byte
@@ -414,9 +476,9 @@ __global__ __launch_bounds__(64) void decode_generic(
 // step is limited by its fp32 arithmetic, and fewer rows per thread are in flight.)
 template <typename T, typename S, int N, int P, int R, int NT, int CW = 4>
 static hipError_t launch_fast(const DecodeArgs& a, hipStream_t st) {
-    // the fused variant only when a norm, bias or gate is given (a per-token A alone is one
-    // scalar per workgroup, read by both)
-    const bool fused = a.fu.bc() || a.fu.z;
+    // the fused variant only when a norm, bias, gate or output norm is given (a per-token A
+    // or angles per head alone are one scalar or one index per workgroup, read by both)
+    const bool fused = a.fu.bc() || a.fu.z || a.fu.onw;
     auto kernel = fused ? decode_fast<T, S, N, P, R, NT, CW, true> : decode_fast<T, S, N, P, R, NT, CW, false>;
     hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(a.batch * a.H)),
                        dim3(NT), 0, st, static_cast<S*>(a.h), static_cast<const T*>(a.b_last),
@@ -444,7 +506,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
         }
     }
     if (a.N == 16 && a.P == 16 && a.R == 1) return launch_fast<T, S, 16, 16, 1, 32>(a, st);
-    const size_t shm = sizeof(float) * (3 * a.R * a.N + 2 * a.R * a.P + a.N + 3 * a.R);
+    const size_t shm = generic_decode_lds(a);
     hipLaunchKernelGGL((decode_generic<T, S>), dim3(static_cast<unsigned>(a.batch * a.H)), dim3(64),
                        shm, st, static_cast<S*>(a.h), static_cast<const T*>(a.b_last),
                        static_cast<const T*>(a.x_last), static_cast<const T*>(a.x_t), a.dt_t, a.A,
@@ -456,8 +518,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
 
 bool decode_supported(const DecodeArgs& a) {
     if (a.R > kMaxRankGeneric) return false;
-    const size_t shm = sizeof(float) * (3 * a.R * a.N + 2 * a.R * a.P + a.N + 3 * a.R);
-    return shm <= 64 * 1024;
+    return generic_decode_lds(a) <= 64 * 1024;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {

@@ -20,7 +20,10 @@ struct Fusion {
     const float* cbias = nullptr;   // bias of C (R, N)
     const void* z = nullptr;        // gate input, io dtype, laid out as y
     float eps = 1e-6f;
+    const float* onw = nullptr;     // output RMSNorm weight (H, P), applied after the gate
+    int Gt = 0;                     // angle groups (theta (.., Gt, N/2)); 0: the B/C groups
     __host__ __device__ bool bc() const { return bnw || cnw || bbias || cbias; }
+    __host__ __device__ int tgroups(int G) const { return Gt > 0 ? Gt : G; }
 };
 
 struct DecodeArgs {

@@ -44,13 +44,16 @@ __global__ __launch_bounds__(256) void prefill_generic(
     float* wv = cum + Q;                   // Q
     float* gam = wv + Q;                   // Q
     float* sv = gam + Q;                   // Q
-    float* bsc = sv + Q;                   // Q*R: RMSNorm scale of each B row of the chunk
+    float* bsc = sv + Q;                   // Q*R: RMSNorm scale of each B row of the chunk (and,
+                                           // later in the chunk, the output-norm scale of each row)
     float* csc = bsc + QR;                 // Q*R: same for C
+    float* Yb = csc + QR;                  // QR*P: outputs before the output norm (with it only)
     const T* zg = static_cast<const T*>(fu.z);
 
     const int bh = blockIdx.x;
     const int b = bh / H, h = bh - b * H;
     const int g = h / (H / G);
+    const int Gt = fu.tgroups(G), gt = h / (H / Gt);   // angle group
     // this sequence: tokens tb .. tb + L - 1 of the (possibly packed) token axis
     const SeqSpan sp = seq_span(cu, b, Lmax, Tt);
     const int64_t tb = sp.start, L = sp.len;
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(256) void prefill_generic(
         // Angles into LDS, one element per thread (loads in parallel).
         for (int idx = tid; idx < Q * KP; idx += NT) {
             const int i = idx / KP, k = idx - i * KP;
-            phi[idx] = (i < nq) ? theta[((tb + t0 + i) * G + g) * KP + k] : 0.f;
+            phi[idx] = (i < nq) ? theta[((tb + t0 + i) * Gt + gt) * KP + k] : 0.f;
         }
         // RMSNorm scales of the chunk's B and C rows (token, rank), when normalised.
         if (fu.bnw || fu.cnw) {
@@ -214,9 +217,28 @@ __global__ __launch_bounds__(256) void prefill_generic(
             acc += Dh * X[ir * P + p];
             const size_t yi = ((tb + t0 + i) * H + h) * static_cast<size_t>(R * P) + (ir - i * R) * P + p;
             if (zg) acc *= silu(io<T>::load(zg + yi));
-            io<T>::store(y + yi, acc);
+            if (fu.onw)
+                Yb[idx] = acc;   // normalised below
+            else
+                io<T>::store(y + yi, acc);
         }
         __syncthreads();
+        if (fu.onw) {   // output RMSNorm of each row (token, rank) over its P values: a wave per row
+            const int lane = tid & 63, wave = tid >> 6;
+            for (int ir = wave; ir < nq * R; ir += NT / 64) {
+                float ss = 0.f;
+                for (int p = lane; p < P; p += 64) ss += Yb[ir * P + p] * Yb[ir * P + p];
+                ss = wave_sum(ss);
+                if (lane == 0) bsc[ir] = rsqrtf(ss / P + fu.eps);
+            }
+            __syncthreads();
+            for (int idx = tid; idx < nq * R * P; idx += NT) {
+                const int ir = idx / P, p = idx - ir * P;
+                const int i = ir / R;
+                const size_t yi = ((tb + t0 + i) * H + h) * static_cast<size_t>(R * P) + (ir - i * R) * P + p;
+                io<T>::store(y + yi, Yb[idx] * bsc[ir] * fu.onw[h * P + p]);
+            }
+        }
         // State update, one rotation pair x column per thread.
         const float decay = __expf(cend);
         for (int idx = tid; idx < KP * P; idx += NT) {
@@ -307,7 +329,8 @@ hipError_t launch_carry_bc(const PrefillArgs& a, void* out, hipStream_t st) {
 size_t generic_lds_bytes(const PrefillArgs& a) {
     const size_t QR = static_cast<size_t>(a.Q) * a.R;
     return sizeof(float) * (static_cast<size_t>(a.N) * a.P + 2 * QR * a.N + QR * a.P + QR * QR +
-                            static_cast<size_t>(a.Q) * (a.N / 2) + 4 * static_cast<size_t>(a.Q) + 2 * QR);
+                            static_cast<size_t>(a.Q) * (a.N / 2) + 4 * static_cast<size_t>(a.Q) + 2 * QR +
+                            (a.fu.onw ? QR * a.P : 0));
 }
 
 template <typename T>

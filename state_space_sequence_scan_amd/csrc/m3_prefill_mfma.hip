@@ -135,7 +135,12 @@ __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
     constexpr int QR = Q * R;
     __shared__ float sCos[Q][KP], sSin[Q][KP];
     __shared__ float sPart[4][KP];
-    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    // One workgroup per (b, angle group j, chunk).  The angle groups are those of the
+    // B/C groups unless the fusion asks for finer ones (angles per head over shared B, C):
+    // group j then reads B and C of group j / (Gt / G).
+    const int Gt = fu.tgroups(G);
+    const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    const int g = j / (Gt / G);
     const int tid = threadIdx.x;
     const SeqSpan sp = seq_span(cu, b, L, T);
     const int64_t t0 = static_cast<int64_t>(c) * Q;
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
     const int nq = static_cast<int>(sp.len - t0 < Q ? sp.len - t0 : Q);
     const int64_t tg = sp.start + t0;         // first token of the chunk in the packed arrays
     const PrepLayout lay{QR};
-    uint8_t* base = prep + ((static_cast<size_t>(b) * G + g) * nchunks + c) * lay.bytes();
+    uint8_t* base = prep + ((static_cast<size_t>(b) * Gt + j) * nchunks + c) * lay.bytes();
     uint16_t* Bt = reinterpret_cast<uint16_t*>(base + lay.bt());
     uint16_t* Ct = reinterpret_cast<uint16_t*>(base + lay.ct());
     float* cs = reinterpret_cast<float*>(base + lay.cs());
@@ -157,7 +162,7 @@ __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
 #pragma unroll
         for (int e = 0; e < QP; ++e) {
             const int i = part * QP + e;
-            run += (i < nq) ? theta[((tg + i) * G + g) * KP + k] : 0.f;
+            run += (i < nq) ? theta[((tg + i) * Gt + j) * KP + k] : 0.f;
             th[e] = run;
         }
         sPart[part][k] = run;
@@ -260,6 +265,9 @@ struct ScanParams {
     int64_t T;              // tokens in the packed arrays
     const float* At;        // per-token decay rates (b, L, H) replacing A, or null
     const uint16_t* z;      // output gate input, laid out as y, or null
+    const float* onw;       // output RMSNorm weight (H, P), or null
+    float eps;              // its epsilon
+    int Gt;                 // angle groups: the prepared operands are per (b, angle group, chunk)
 };
 
 // Initial state of segment 0 when no segment pass ran: h_in plus the beta term
@@ -343,7 +351,8 @@ __device__ __forceinline__ void set_oct(bfv<K>& v, int i, bf16x8 o) {
 }
 
 // GATE: the output gate is applied (its input rows are loaded well before the store).
-template <int R, int Q, int NW, bool FULL, bool GATE>
+// ONORM: the output RMSNorm follows (after the gate), each output row over its P values.
+template <int R, int Q, int NW, bool FULL, bool GATE, bool ONORM>
 __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
     constexpr int NTH = 64 * NW;
     constexpr int QR = Q * R;
@@ -370,6 +379,7 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
     __shared__ __align__(16) float sCum[2][Q], sSc[2][Q], sW[2][Q], sGam[2][Q];  // by chunk parity
     __shared__ float sCs[2][KP * 2];
     __shared__ float sDec[2];
+    __shared__ __align__(16) float sOW[ONORM ? P : 4];              // output-norm weight of this head
 
     int seg, h, b;
     xcd_decode(blockIdx.x, gridDim.x, p.H, FULL ? p.nseg : p.nseg - 1, &b, &h, &seg);
@@ -387,7 +397,8 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
     const int c_begin = seg * p.chunks_per_seg;
     const int c_end = min(nchunks_b, c_begin + p.chunks_per_seg);
     const bool last_seg = (seg == p.nseg - 1);
-    const size_t gbase = (static_cast<size_t>(b) * p.G + g) * p.nchunks;
+    const size_t gbase = (static_cast<size_t>(b) * p.Gt + h / (p.H / p.Gt)) * p.nchunks;   // angle group's operands
+    if (ONORM && tid < P) sOW[tid] = p.onw[h * P + tid];   // visible after the prologue's barrier
     const uint32_t HRP = static_cast<uint32_t>(p.H) * R * P;   // elements between tokens of x and y
     // Output row block(s) of this wave (uniform).  Waves w, w+4, .. share a SIMD.  With
     // one block per wave the order 0..3, 7..4, 8..11, 15..12 gives every SIMD the same
@@ -713,6 +724,21 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
                 yv_[ct][1] *= silu(bits_to_f(zz.x >> 16));                                                    \
                 yv_[ct][2] *= silu(bits_to_f(zz.y & 0xffff));                                                 \
                 yv_[ct][3] *= silu(bits_to_f(zz.y >> 16));                                                    \
+            }                                                                                                 \
+        }                                                                                                     \
+        if constexpr (ONORM) {   /* row i's 64 values sit in lanes l16, l16 + 16, + 32, + 48 */              \
+            float ss = 0.f;                                                                                   \
+            _Pragma("unroll") for (int ct = 0; ct < 4; ++ct)                                                  \
+                _Pragma("unroll") for (int e = 0; e < 4; ++e) ss += yv_[ct][e] * yv_[ct][e];                  \
+            ss += __shfl_xor(ss, 16);                                                                         \
+            ss += __shfl_xor(ss, 32);                                                                         \
+            const float sc = rsqrtf(ss * (1.f / P) + p.eps);                                                  \
+            _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) {                                                \
+                const float4 wv = *reinterpret_cast<const float4*>(&sOW[16 * ct + 4 * lg]);                  \
+                yv_[ct][0] *= sc * wv.x;                                                                      \
+                yv_[ct][1] *= sc * wv.y;                                                                      \
+                yv_[ct][2] *= sc * wv.z;                                                                      \
+                yv_[ct][3] *= sc * wv.w;                                                                      \
             }                                                                                                 \
         }                                                                                                     \
         uint16_t* yrow = (tk < nq) ? ych + (static_cast<uint32_t>(tk) * HRP + static_cast<uint32_t>(r * P + 4 * lg)) \
@@ -1074,8 +1100,9 @@ bool mfma_supported(const PrefillArgs& a) {
     // larger shapes take the generic path.  The scan launches at most max(batch * H, 1023)
     // workgroups of at most 512 threads (segments are added only while batch * H < 512).
     const int64_t nchunks = (a.L + a.Q - 1) / a.Q;
-    const bool grid_fits = a.batch <= 65535 && a.G <= 65535 &&
-                           nchunks * a.G * a.batch * mf::NT < (int64_t{1} << 32) &&
+    const int64_t Gt = a.fu.tgroups(a.G);
+    const bool grid_fits = a.batch <= 65535 && Gt <= 65535 &&
+                           nchunks * Gt * a.batch * mf::NT < (int64_t{1} << 32) &&
                            a.batch * a.H < (int64_t{1} << 23);
     return a.bf16 && a.N == mf::N && a.P == mf::P && (a.R == 1 || a.R == 2 || a.R == 4) &&
            (a.Q == 32 || a.Q == 64) && offsets_fit && grid_fits;
@@ -1119,8 +1146,8 @@ static MfmaWs mfma_ws(const PrefillArgs& a, int nchunks, int nseg, int split) {
     const mf::PrepLayout lay{a.Q * a.R};
     auto al = [](size_t v) { return (v + 255) & ~static_cast<size_t>(255); };
     size_t off = 0;
-    w.prep = off;
-    off += al(static_cast<size_t>(a.batch) * a.G * nchunks * lay.bytes());
+    w.prep = off;   // prepared operands per (b, angle group, chunk)
+    off += al(static_cast<size_t>(a.batch) * a.fu.tgroups(a.G) * nchunks * lay.bytes());
     w.sink = off;
     off += al(64 * 64 * sizeof(uint16_t));
     const size_t bh = static_cast<size_t>(a.batch) * a.H;
@@ -1170,7 +1197,7 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
     const MfmaWs ws = mfma_ws(a, nchunks, nseg, split);
     uint8_t* base = static_cast<uint8_t*>(a.workspace);
 
-    hipLaunchKernelGGL((mf::rope_prep<R, Q>), dim3(nchunks, a.G, static_cast<unsigned>(a.batch)), dim3(mf::NT), 0,
+    hipLaunchKernelGGL((mf::rope_prep<R, Q>), dim3(nchunks, a.fu.tgroups(a.G), static_cast<unsigned>(a.batch)), dim3(mf::NT), 0,
                        st, static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.theta, a.L,
                        a.G, nchunks, base + ws.prep, a.cu, a.T, a.fu);
     hipError_t e = hipGetLastError();
@@ -1195,6 +1222,9 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
     p.T = a.T;
     p.At = a.fu.At;
     p.z = static_cast<const uint16_t*>(a.fu.z);
+    p.onw = a.fu.onw;
+    p.eps = a.fu.eps;
+    p.Gt = a.fu.tgroups(a.G);
     p.H = a.H;
     p.G = a.G;
     p.nchunks = nchunks;
@@ -1208,7 +1238,7 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
         ps.seg_state = reinterpret_cast<float*>(base + ws.seg_state);
         ps.seg_decay = reinterpret_cast<float*>(base + ws.seg_decay);
         ps.seg_rot = reinterpret_cast<float*>(base + ws.seg_rot);
-        hipLaunchKernelGGL((mf::scan_mfma<R, Q, NW, false, false>), dim3(static_cast<unsigned>(pieces * a.H * a.batch)),
+        hipLaunchKernelGGL((mf::scan_mfma<R, Q, NW, false, false, false>), dim3(static_cast<unsigned>(pieces * a.H * a.batch)),
                            dim3(64 * NW), 0, st, ps);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         float* s_init = reinterpret_cast<float*>(base + ws.s_init);
@@ -1221,7 +1251,8 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
         p.sinit_stride = pieces + 1;
         p.sinit_step = split;
     }
-    auto scan = p.z ? mf::scan_mfma<R, Q, NW, true, true> : mf::scan_mfma<R, Q, NW, true, false>;
+    auto scan = p.onw ? (p.z ? mf::scan_mfma<R, Q, NW, true, true, true> : mf::scan_mfma<R, Q, NW, true, false, true>)
+                      : (p.z ? mf::scan_mfma<R, Q, NW, true, true, false> : mf::scan_mfma<R, Q, NW, true, false, false>);
     hipLaunchKernelGGL(scan, dim3(static_cast<unsigned>(nseg * a.H * a.batch)),
                        dim3(64 * NW), 0, st, p);
     return hipGetLastError();

@@ -45,7 +45,7 @@ class Grads(ctypes.Structure):
 class Fusion(ctypes.Structure):
     _fields_ = [("A_t", ctypes.c_void_p), ("b_norm_w", ctypes.c_void_p), ("c_norm_w", ctypes.c_void_p),
                 ("b_bias", ctypes.c_void_p), ("c_bias", ctypes.c_void_p), ("z", ctypes.c_void_p),
-                ("norm_eps", ctypes.c_float)]
+                ("norm_eps", ctypes.c_float), ("out_norm_w", ctypes.c_void_p), ("theta_groups", ctypes.c_int32)]
 
 
 class M3Error(RuntimeError):
@@ -83,6 +83,8 @@ def lib(path: str = LIB_PATH):
                                     [ctypes.POINTER(State), ctypes.POINTER(State), vp, vp, sz, vp])
     L.m3_decode_step.restype = ctypes.c_int
     L.m3_decode_step.argtypes = [ctypes.POINTER(Dims)] + [vp] * 13
+    L.m3_prefill_fused_workspace_size.restype = ctypes.c_int
+    L.m3_prefill_fused_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Fusion), ctypes.POINTER(sz)]
     L.m3_prefill_fused.restype = ctypes.c_int
     L.m3_prefill_fused.argtypes = ([ctypes.POINTER(Dims)] + [vp] * 8 + [ctypes.POINTER(Fusion)] +
                                    [ctypes.POINTER(State), ctypes.POINTER(State), vp, vp, sz, vp])
@@ -320,12 +322,14 @@ def prefill_varlen_fused(x, dt, A, lam, theta, B, C, D, cu_seqlens, max_seqlen: 
                          b_norm_w=None, c_norm_w=None, b_bias=None, c_bias=None, z=None, eps: float = 1e-6,
                          state_in: Optional[DecodeState] = None, out_state: bool = True,
                          y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                         state_dtype: Optional[torch.dtype] = None):
+                         state_dtype: Optional[torch.dtype] = None, out_norm_w=None):
     """``prefill_varlen`` with the fused layer prologue/epilogue (m3_prefill_varlen_fused):
-    per-token A (T,H), RMSNorm weights and biases of B and C (R,N), gate z (laid out as y)."""
+    per-token A (T,H), RMSNorm weights and biases of B and C (R,N), gate z (laid out as y),
+    output norm weight (H,P); theta may carry finer angle groups (T, Gt, N/2)."""
     T, H, R, P = x.shape
-    N = B.shape[3]
-    fu = _fusion(x.device, (R, N, (T, H), (T, H, R, P)), A_t, b_norm_w, c_norm_w, b_bias, c_bias, z, eps, x.dtype)
+    G, N = B.shape[1], B.shape[3]
+    fu = _fusion(x.device, (R, N, (T, H), (T, H, R, P), (H, P)), A_t, b_norm_w, c_norm_w, b_bias, c_bias, z, eps,
+                 x.dtype, out_norm_w, _theta_groups(theta, 1, G, H))
     return _prefill_packed(x, dt, A, lam, theta, B, C, D, cu_seqlens, max_seqlen, chunk, state_in, out_state,
                            y, workspace, state_dtype, fu)
 
@@ -346,7 +350,8 @@ def _prefill_packed(x, dt, A, lam, theta, B, C, D, cu_seqlens, max_seqlen, chunk
     _check(lam, "lam", (T, H), torch.float32, dev)
     _check(A, "A", (H,), torch.float32, dev)
     _check(D, "D", (H,), torch.float32, dev)
-    _check(theta, "theta", (T, G, N // 2), torch.float32, dev)
+    _check(theta, "theta", (T, fu.theta_groups if fu is not None and fu.theta_groups else G, N // 2),
+           torch.float32, dev)
     _check(B, "B", (T, G, R, N), io, dev)
     _check(C, "C", (T, G, R, N), io, dev)
     if state_dtype is None:
@@ -373,7 +378,7 @@ def _prefill_packed(x, dt, A, lam, theta, B, C, D, cu_seqlens, max_seqlen, chunk
                          torch.empty((nseq, G, R, N), dtype=io, device=dev),
                          torch.empty((nseq, H, R, P), dtype=io, device=dev))
         sout = State(st.h.data_ptr(), st.b_last.data_ptr(), st.x_last.data_ptr())
-    ws = workspace_size(dims)
+    ws = workspace_size(dims) if fu is None else fused_workspace_size(dims, fu)
     if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
         workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
     common = (ctypes.byref(dims), _p(cu_seqlens), ctypes.c_int64(T), _p(x), _p(dt), _p(A), _p(lam), _p(theta),
@@ -523,9 +528,10 @@ def backward_varlen(x, dt, A, lam, theta, B, C, D, dy, cu_seqlens, max_seqlen: i
 
 
 def _fusion(dev, shapes, A_t=None, b_norm_w=None, c_norm_w=None, b_bias=None, c_bias=None, z=None,
-            eps: float = 1e-6, io=None):
-    """Checks the fusion tensors against the call's shapes and packs them."""
-    R, N, at_shape, z_shape = shapes
+            eps: float = 1e-6, io=None, out_norm_w=None, theta_groups: int = 0):
+    """Checks the fusion tensors against the call's shapes and packs them.  shapes is
+    (R, N, A_t shape, z shape, (H, P)); theta_groups is the angle-group count (0: that of B, C)."""
+    R, N, at_shape, z_shape, hp = shapes
     for t, name in ((b_norm_w, "b_norm_w"), (c_norm_w, "c_norm_w"), (b_bias, "b_bias"), (c_bias, "c_bias")):
         if t is not None:
             _check(t, name, (R, N), torch.float32, dev)
@@ -533,30 +539,54 @@ def _fusion(dev, shapes, A_t=None, b_norm_w=None, c_norm_w=None, b_bias=None, c_
         _check(A_t, "A_t", at_shape, torch.float32, dev)
     if z is not None:
         _check(z, "z", z_shape, io, dev)
+    if out_norm_w is not None:
+        _check(out_norm_w, "out_norm_w", hp, torch.float32, dev)
     return Fusion(*[None if t is None else t.data_ptr() for t in (A_t, b_norm_w, c_norm_w, b_bias, c_bias, z)],
-                  float(eps))
+                  float(eps), None if out_norm_w is None else out_norm_w.data_ptr(), int(theta_groups))
+
+
+def _theta_groups(theta, axis, G, H):
+    """Angle groups of a fused call from theta's shape: 0 when they are B and C's G."""
+    Gt = theta.shape[axis]
+    if Gt == G:
+        return 0
+    if Gt % G != 0 or H % Gt != 0:
+        raise ValueError(f"theta has {Gt} angle groups: not a multiple of G={G} dividing H={H}")
+    return Gt
+
+
+def fused_workspace_size(dims: Dims, fu: Fusion) -> int:
+    n = ctypes.c_size_t(0)
+    rc = lib().m3_prefill_fused_workspace_size(ctypes.byref(dims), ctypes.byref(fu), ctypes.byref(n))
+    if rc != 0:
+        raise M3Error("m3_prefill_fused_workspace_size", rc)
+    return int(n.value)
 
 
 def prefill_fused(x, dt, A, lam, theta, B, C, D, chunk: int, A_t=None, b_norm_w=None, c_norm_w=None,
                   b_bias=None, c_bias=None, z=None, eps: float = 1e-6,
                   state_in: Optional[DecodeState] = None, out_state: bool = True,
                   y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                  state_dtype: Optional[torch.dtype] = None):
+                  state_dtype: Optional[torch.dtype] = None, out_norm_w=None):
     """``prefill`` with the fused layer prologue/epilogue (m3_prefill_fused): per-token A
-    (b,L,H), RMSNorm weights and biases of B and C (R,N), gate z (laid out as y)."""
+    (b,L,H), RMSNorm weights and biases of B and C (R,N), gate z (laid out as y), output
+    norm weight (H,P); theta may carry finer angle groups than B and C, (b, L, Gt, N/2)
+    (Gt = H: angles per head)."""
     b, L, H, R, P = x.shape
     G, N = B.shape[2], B.shape[4]
     dev = x.device
     io = x.dtype
+    Gt = _theta_groups(theta, 2, G, H)
     _check(x, "x", (b, L, H, R, P), io, dev)
     _check(dt, "dt", (b, L, H), torch.float32, dev)
     _check(lam, "lam", (b, L, H), torch.float32, dev)
     _check(A, "A", (H,), torch.float32, dev)
     _check(D, "D", (H,), torch.float32, dev)
-    _check(theta, "theta", (b, L, G, N // 2), torch.float32, dev)
+    _check(theta, "theta", (b, L, Gt or G, N // 2), torch.float32, dev)
     _check(B, "B", (b, L, G, R, N), io, dev)
     _check(C, "C", (b, L, G, R, N), io, dev)
-    fu = _fusion(dev, (R, N, (b, L, H), (b, L, H, R, P)), A_t, b_norm_w, c_norm_w, b_bias, c_bias, z, eps, io)
+    fu = _fusion(dev, (R, N, (b, L, H), (b, L, H, R, P), (H, P)), A_t, b_norm_w, c_norm_w, b_bias, c_bias, z, eps,
+                 io, out_norm_w, Gt)
     if state_dtype is None:
         state_dtype = state_in.h.dtype if state_in is not None else torch.float32
     dims = make_dims(b, L, H, G, P, N, R, chunk, _IO[io], _IO[state_dtype])
@@ -577,7 +607,7 @@ def prefill_fused(x, dt, A, lam, theta, B, C, D, chunk: int, A_t=None, b_norm_w=
                          torch.empty((b, G, R, N), dtype=io, device=dev),
                          torch.empty((b, H, R, P), dtype=io, device=dev))
         sout = State(st.h.data_ptr(), st.b_last.data_ptr(), st.x_last.data_ptr())
-    ws = workspace_size(dims)
+    ws = fused_workspace_size(dims, fu)
     if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
         workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
     rc = lib().m3_prefill_fused(ctypes.byref(dims), _p(x), _p(dt), _p(A), _p(lam), _p(theta), _p(B), _p(C),
@@ -591,15 +621,19 @@ def prefill_fused(x, dt, A, lam, theta, B, C, D, chunk: int, A_t=None, b_norm_w=
 
 def decode_step_fused(state: DecodeState, x_t, dt_t, A, lam_t, theta_t, B_t, C_t, D, A_t=None,
                       b_norm_w=None, c_norm_w=None, b_bias=None, c_bias=None, z=None, eps: float = 1e-6,
-                      y_t: Optional[torch.Tensor] = None, advance: bool = True):
+                      y_t: Optional[torch.Tensor] = None, advance: bool = True, out_norm_w=None):
     """``decode_step`` with the fused prologue/epilogue (m3_decode_step_fused): A_t (b,H),
-    norm weights and biases (R,N), gate z (b,H,R,P).  The carry stays raw."""
+    norm weights and biases (R,N), gate z (b,H,R,P), output norm weight (H,P); theta_t may
+    carry finer angle groups (b, Gt, N/2).  The carry stays raw."""
     b, H, R, P = x_t.shape
     G, N = B_t.shape[1], B_t.shape[3]
     dev = x_t.device
     io = x_t.dtype
     _check(state.h, "state.h", (b, H, N, P), state.h.dtype, dev)
-    fu = _fusion(dev, (R, N, (b, H), (b, H, R, P)), A_t, b_norm_w, c_norm_w, b_bias, c_bias, z, eps, io)
+    Gt = _theta_groups(theta_t, 1, G, H)
+    _check(theta_t, "theta_t", (b, Gt or G, N // 2), torch.float32, dev)
+    fu = _fusion(dev, (R, N, (b, H), (b, H, R, P), (H, P)), A_t, b_norm_w, c_norm_w, b_bias, c_bias, z, eps, io,
+                 out_norm_w, Gt)
     dims = make_dims(b, 1, H, G, P, N, R, 1, _IO[io], _IO[state.h.dtype])
     if y_t is None:
         y_t = torch.empty_like(x_t)

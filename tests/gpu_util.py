@@ -63,6 +63,28 @@ def slice_errs(gpu, ref, head_axis):
     return per_slice, elem
 
 
+def onorm_slice_errs(gpu_n, ref_pre, w, eps):
+    """Error of outputs after the output RMSNorm, on the scale of the rows before it.
+
+    The norm divides every row (b, t, h, r, :) by its own root mean square, so it magnifies
+    the absolute error of rows that are small next to the rest of their slice; the bar of
+    the scan output (max|error| / max|ref| per slice) is therefore applied before that
+    division: each normalised row's error is multiplied back by the oracle's row RMS and
+    divided by the head's largest |weight|.  gpu_n (b, L, H, R, P) is the normalised GPU
+    output, ref_pre the oracle's output before the norm, w (H, P) the weight.  Returns
+    (per-slice errors (b, H), max of the plain per-slice error of the normalised outputs)."""
+    pre = np.asarray(ref_pre, np.float64)
+    w = np.asarray(w, np.float64)
+    rms = np.sqrt(np.mean(pre * pre, axis=-1, keepdims=True) + eps)
+    ref_n = pre / rms * w[None, None, :, None, :]
+    d = np.abs(np.asarray(gpu_n, np.float64) - ref_n) * rms / np.max(np.abs(w), axis=1)[None, None, :, None, None]
+    b, L, H = pre.shape[:3]
+    num = np.moveaxis(d, 2, 1).reshape(b, H, -1).max(-1)
+    den = np.maximum(np.moveaxis(np.abs(pre), 2, 1).reshape(b, H, -1).max(-1), 1e-30)
+    plain, _ = slice_errs(gpu_n, ref_n, 2)
+    return num / den, float(np.max(plain))
+
+
 def oracle_args(d):
     return [np64(d[k]) for k in ("x", "dt", "A", "lam", "theta", "B", "C", "D")]
 

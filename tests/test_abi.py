@@ -31,6 +31,7 @@ def test_header_declares_the_entry_points():
     assert declared_symbols() == ["m3_backward", "m3_backward_parts", "m3_backward_per_token_A", "m3_backward_varlen",
                                   "m3_backward_workspace_size", "m3_decode_step",
                                   "m3_decode_step_fused", "m3_prefill_chunked", "m3_prefill_chunked_noalloc", "m3_prefill_fused",
+                                  "m3_prefill_fused_workspace_size",
                                   "m3_prefill_varlen", "m3_prefill_varlen_fused", "m3_prefill_workspace_size", "m3_status_string",
                                   "m3_version"]
 
@@ -208,12 +209,12 @@ def test_backward_rejects_bad_arguments(lib):
 
 def test_fused_entry_points_reject_bad_arguments(lib):
     d = _dims()
-    fu = m3scan.Fusion(None, None, None, None, None, None, 1e-6)
+    fu = m3scan.Fusion(None, None, None, None, None, None, 1e-6, None, 0)
     # a NULL fusion
     assert lib.m3_prefill_fused(ctypes.byref(d), *[FAKE] * 8, None, None, None, FAKE, None, 0, None) == -1
     assert lib.m3_decode_step_fused(ctypes.byref(d), *[FAKE] * 11, None, FAKE, None) == -1
     # a norm weight with a non-positive epsilon
-    bad = m3scan.Fusion(None, 0x1000, None, None, None, None, 0.0)
+    bad = m3scan.Fusion(None, 0x1000, None, None, None, None, 0.0, None, 0)
     assert lib.m3_prefill_fused(ctypes.byref(d), *[FAKE] * 8, ctypes.byref(bad), None, None, FAKE, None, 0,
                                 None) == -1
     assert lib.m3_decode_step_fused(ctypes.byref(d), *[FAKE] * 11, ctypes.byref(bad), FAKE, None) == -1
@@ -227,6 +228,32 @@ def test_fused_entry_points_reject_bad_arguments(lib):
     # the workspace reserves room for the normalised carry: none given is too small
     assert lib.m3_prefill_fused(ctypes.byref(d), *[FAKE] * 8, ctypes.byref(fu), None, None, FAKE, None, 0,
                                 None) == -3
+    # an output-norm weight with a non-positive epsilon
+    bad = m3scan.Fusion(None, None, None, None, None, None, 0.0, 0x1000, 0)
+    assert lib.m3_prefill_fused(ctypes.byref(d), *[FAKE] * 8, ctypes.byref(bad), None, None, FAKE, None, 0,
+                                None) == -1
+    assert lib.m3_decode_step_fused(ctypes.byref(d), *[FAKE] * 11, ctypes.byref(bad), FAKE, None) == -1
+    # angle groups must be a multiple of G (2 here) dividing H (4): 1, 3, 8 and -2 are refused
+    for gt in (1, 3, 8, -2):
+        bad = m3scan.Fusion(None, None, None, None, None, None, 1e-6, None, gt)
+        assert lib.m3_prefill_fused(ctypes.byref(d), *[FAKE] * 8, ctypes.byref(bad), None, None, FAKE, None, 0,
+                                    None) == -1, gt
+        assert lib.m3_decode_step_fused(ctypes.byref(d), *[FAKE] * 11, ctypes.byref(bad), FAKE, None) == -1, gt
+        n = ctypes.c_size_t(0)
+        assert lib.m3_prefill_fused_workspace_size(ctypes.byref(d), ctypes.byref(bad), ctypes.byref(n)) == -1, gt
+
+
+def test_fused_workspace_grows_with_angle_groups(lib):
+    """Angles per head over shared B and C prepare the rotated operands per angle group:
+    the matrix-core path's workspace holds Gt / G times the per-group share; 0 or G angle
+    groups give the plain size."""
+    d = m3scan.make_dims(2, 640, 8, 2, 64, 128, 2, 32, m3scan.M3_BF16)
+    n0, n2, n8 = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    for gt, n in ((0, n0), (2, n2), (8, n8)):
+        fu = m3scan.Fusion(None, None, None, None, None, None, 1e-6, None, gt)
+        assert lib.m3_prefill_fused_workspace_size(ctypes.byref(d), ctypes.byref(fu), ctypes.byref(n)) == 0
+    assert n0.value == n2.value == m3scan.workspace_size(d)
+    assert n8.value > n0.value
 
 
 def test_backward_parts(lib):

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import TOL, say, slice_errs
+from gpu_util import TOL, onorm_slice_errs, say, slice_errs
 from state_space_sequence_scan_amd import CONFIGS, inputs, m3scan
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
@@ -188,3 +188,36 @@ def test_fused_prefill_workload_every_slice():
         tally.slices += (b1 - b0) * (h1 - h0)
         say(f"  block b{b0} done")
     tally.report()
+
+
+def test_theta_per_head_out_norm_workload_every_slice():
+    """The 1.5B-scale SISO layer with angles per head over the shared B and C (64 angle
+    groups: the rotated operands are prepared per head) and the output RMSNorm, at full
+    size, every slice.  The normalised outputs are held to the bar on the scale of the rows
+    before the norm (onorm_slice_errs); the printed elementwise figure is then the plain
+    per-slice error of the normalised outputs, which the norm inflates on small rows."""
+    cfg = CONFIGS["siso_l8192"]
+    say("angles per head + output norm, workload siso_l8192")
+    d = inputs.draw_config(cfg, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(cfg.seed + 29)
+    theta_h = (torch.rand((cfg.batch, cfg.seqlen, cfg.nheads, cfg.dstate // 2), generator=g, device="cuda") * 2 - 1) \
+        * np.pi
+    onw = 1.0 + 0.3 * torch.randn((cfg.nheads, cfg.headdim), generator=g, device="cuda")
+    y, st = m3scan.prefill_fused(d["x"], d["dt"], d["A"], d["lam"], theta_h, d["B"], d["C"], d["D"], cfg.chunk,
+                                 out_norm_w=onw)
+    torch.cuda.synchronize()
+    tally = Tally("siso_l8192 angles per head + output norm", TOL["bf16"])
+    worst_plain = 0.0
+    for b0, b1, h0, h1 in _blocks(cfg, 16):
+        args = _block_args(d, cfg, b0, b1, h0, h1)
+        args[4] = f64(theta_h[b0:b1, :, h0:h1])
+        ypre, hr = oracle.scan_fused(*args)
+        per, plain = onorm_slice_errs(f64(y[b0:b1, :, h0:h1]), ypre, f64(onw[h0:h1]), 1e-6)
+        tally.add("y (normalised, pre-norm scale)", per, 0.0, (b0, h0))
+        worst_plain = max(worst_plain, plain)
+        tally.add("h", *slice_errs(f64(st.h[b0:b1, h0:h1]), hr, 1), (b0, h0))
+        tally.slices += (b1 - b0) * (h1 - h0)
+        say(f"  block b{b0} h{h0}..{h1 - 1} done")
+    assert tally.slices == cfg.batch * cfg.nheads
+    tally.report()
+    say(f"  plain per-slice error of the normalised outputs (inflated on near-zero rows): {worst_plain:.2e}")
