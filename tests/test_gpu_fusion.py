@@ -266,13 +266,14 @@ def _fused_errs(y, h, d, f, state_in=None, y_axis=2):
 
 
 def test_theta_groups_equal_within_a_group_is_the_grouped_prefill():
-    """Angles per head that repeat each group's angles over its heads give bit for bit the
-    plain grouped prefill (the same rotation per (b, group, chunk), now prepared per head)."""
-    b, L, H, G, P, N, R, Q = 2, 150, 4, 2, 64, 128, 4, 64
+    """Angle groups finer than the B/C groups (Gt = 4 over G = 2, two heads per angle group)
+    that repeat each B/C group's angles give bit for bit the plain grouped prefill: the same
+    operands are prepared once per angle group instead of once per B/C group."""
+    b, L, H, G, Gt, P, N, R, Q = 2, 150, 8, 2, 4, 64, 128, 4, 64
     d = draw(b, L, H, G, P, N, R, "bf16", 1.0, seed=55)
     y0, s0 = m3scan.prefill(*[d[k] for k in NAMES], Q)
     d1 = dict(d)
-    d1["theta"] = d["theta"].repeat_interleave(H // G, dim=2).contiguous()
+    d1["theta"] = d["theta"].repeat_interleave(Gt // G, dim=2).contiguous()
     y1, s1 = m3scan.prefill_fused(*[d1[k] for k in NAMES], Q)
     torch.cuda.synchronize()
     assert torch.equal(y0, y1) and torch.equal(s0.h, s1.h)
