@@ -61,7 +61,96 @@ def parse():
                          "(none with --no-cpu-baseline)")
     ap.add_argument("--probe-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (known bytes) to calibrate HBM counters")
+    ap.add_argument("--groups", type=int, default=None,
+                    help="override the workload's B/C/theta group count G (e.g. 64 = G = H: per-head B, C, theta)")
+    ap.add_argument("--no-intra-chunk", action="store_true",
+                    help="skip the single-chunk (L = chunk) measurement of the intra-chunk contractions")
     return ap.parse_args()
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=5):
+    """A plain device-to-device copy of known size timed with HIP events: bytes read plus bytes
+    written per second (the secondary denominator next to the 8 TB/s HBM peak)."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2 * nbytes / (ms / 1e3) / 1e9
+
+
+def intra_chunk_flops(cfg, tokens):
+    """Useful MFMA-shaped flops of single-chunk sequences: the masked block C~B~^T (once per
+    group) and its product with X, and the chunk-state contraction; the inter-chunk term reads
+    a zero state here and is not counted."""
+    G, H, P, N, R, Q = cfg.ngroups, cfg.nheads, cfg.headdim, cfg.dstate, cfg.rank, cfg.chunk
+    return 2 * (tokens * G * R * R * N * (Q + 1) / 2 + tokens * H * (R * R * P * (Q + 1) / 2 + R * N * P))
+
+
+def intra_chunk_counters(name):
+    """Matrix-core figures of the single-chunk workload's scan kernel from the committed rocprofv3
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "intra_chunk_mfma_counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        if rec.get("source_sha") != source_sha(*rec["source_files"]):
+            return None
+        return rec["workloads"][name]
+    except Exception:
+        return None
+
+
+def measure_intra_chunk(torch, dev, name="mimo4_chunk64_b4096", reps=3):
+    """Prefill of the single-chunk workload (every sequence one chunk): time, useful
+    intra-chunk flops against the bf16 peak, algorithmic bytes against HBM."""
+    from state_space_sequence_scan_amd import inputs, m3scan
+    from state_space_sequence_scan_amd.configs import INTRA_CHUNK
+    cfg = INTRA_CHUNK[name]
+    d = inputs.draw_config(cfg, device=dev)
+    args = [d[k] for k in ("x", "dt", "A", "lam", "theta", "B", "C", "D")]
+    y = torch.empty_like(d["x"])
+    _, st = m3scan.prefill(*args, cfg.chunk, y=y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        m3scan.prefill(*args, cfg.chunk, y=y)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tok = cfg.batch * cfg.seqlen
+    flops = intra_chunk_flops(cfg, tok)
+    pre_bytes, _ = algorithmic_bytes(cfg, cfg.seqlen, 0)
+    tflops = flops / (ms / 1e3) / 1e12
+    out = {"workload": cfg.label, "name": name, "ms": round(ms, 4), "tokens_per_s": round(tok / (ms / 1e3), 1),
+           "useful_mfma_tflops": round(tflops, 2), "useful_mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+           "alg_GB_per_s": round(pre_bytes / (ms / 1e3) / 1e9, 1),
+           "hbm_frac": round(pre_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+           "mfma_frac_at_hbm_roofline": round(flops / (pre_bytes / (HBM_PEAK_GBS * 1e9)) / 1e12 / BF16_PEAK_TFLOPS, 4),
+           "counters": intra_chunk_counters(name)}
+    del d, args, y, st
+    return out
 
 
 def fused_extra_bytes(cfg, L, steps, tokens=None):
@@ -157,9 +246,18 @@ def main():
     import numpy as np
     import torch
 
-    from state_space_sequence_scan_amd import CONFIGS, inputs, m3scan
+    import dataclasses
 
-    cfg = CONFIGS[args.workload]
+    from state_space_sequence_scan_amd import CONFIGS, inputs, m3scan
+    from state_space_sequence_scan_amd.configs import INTRA_CHUNK
+
+    cfg = CONFIGS[args.workload] if args.workload in CONFIGS else INTRA_CHUNK[args.workload]
+    if args.groups is not None:
+        if cfg.nheads % args.groups != 0:
+            sys.exit(f"--groups {args.groups} does not divide the {cfg.nheads} heads")
+        cfg = dataclasses.replace(cfg, ngroups=args.groups,
+                                  label=cfg.label + f"; {args.groups} B/C/theta groups"
+                                        + (" (per head)" if args.groups == cfg.nheads else ""))
     if args.backward:
         return run_backward(args, cfg)
     state_dtype = torch.bfloat16 if args.state_dtype == "bf16" else torch.float32
@@ -177,6 +275,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    copy_gbs = copy_bandwidth(torch, dev)
 
     t_gen = time.time()
     d = inputs.draw_config(cfg, device=dev)
@@ -284,7 +383,8 @@ def main():
         roof = {"kernel": f"decode_fast<io bf16, state {args.state_dtype}, N128, P64, R4>", "bound": "hbm",
                 "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "alg_bytes_per_launch": dec_bytes, "avg_launch_us": round(dec_launch_ms * 1e3, 2)}
+                "alg_bytes_per_launch": dec_bytes, "avg_launch_us": round(dec_launch_ms * 1e3, 2),
+                "measured_copy_GB_per_s": round(copy_gbs, 1), "frac_of_measured_copy": round(dec_gbs / copy_gbs, 4)}
     else:
         traffic = pmc_traffic(f"prefill_{args.workload}{'_varlen' if args.varlen else ''}"
                               f"{'_fused' if args.fused else ''}_hbm_counters.json",
@@ -292,7 +392,8 @@ def main():
         roof = {"kernel": "prefill (chunked scan)", "bound": "hbm",
                 "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(pre_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "alg_bytes_per_launch": pre_bytes, "avg_launch_us": round(pre_avg * 1e3, 2)}
+                "alg_bytes_per_launch": pre_bytes, "avg_launch_us": round(pre_avg * 1e3, 2),
+                "measured_copy_GB_per_s": round(copy_gbs, 1), "frac_of_measured_copy": round(pre_gbs / copy_gbs, 4)}
 
     # The CPU-baseline leg, the one place here that runs the oracle: the oracle timed on a
     # bounded sample of the workload and, in the same leg, sampled slices of this very run
@@ -388,7 +489,15 @@ def main():
                "cores": threads, "kind": "oracle",
                "sample": f"{n} (batch, head) slices of the workload, {tok_per_slice} tokens each "
                          f"({L} prefill + {steps_dec} decode), fp64 sequential loop, "
-                         f"{sec:.1f} s; scaled to whole-workload tokens (1/{cfg.nheads} per slice-token)"}
+                         f"{sec:.1f} s; scaled to whole-workload tokens (1/{cfg.nheads} per slice-token)",
+               "cpu_model": cpu_model(), "logical_cpus": os.cpu_count(),
+               "single_thread": oracle_single_thread(oracle, np)}
+
+    intra = None
+    if not args.no_intra_chunk and args.workload == "mimo4_decode_b256":
+        del d, dd, y, ydec, st
+        torch.cuda.empty_cache()
+        intra = measure_intra_chunk(torch, dev)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -414,11 +523,44 @@ def main():
                     "alg_GB_per_s": round(dec_gbs, 1), "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4)}
                    if steps_dec else None),
         "roofline": roof,
+        "intra_chunk": intra,
         "cpu_baseline": cpu,
         "parity_check": check,
         "input_gen_s": round(t_gen, 2),
     }
     print(json.dumps(out), flush=True)
+
+
+def oracle_single_thread(oracle, np):
+    """The oracle on one host thread: the whole single SISO layer workload (b1, L256, H4, fp32),
+    and a sample of nanomamba3 (batch, head) slices (2048 tokens each), as whole-workload
+    tokens per second."""
+    from state_space_sequence_scan_amd import CONFIGS, inputs
+    order = ("x", "dt", "A", "lam", "theta", "B", "C", "D")
+    out = {}
+    c0 = CONFIGS["siso_l256_fp32"]
+    d = {k: v.double().numpy() for k, v in inputs.draw_config(c0, device="cpu").items()}
+    oracle.scan(*[d[k] for k in order], nthreads=1)   # library loaded, pages touched
+    reps, t = 0, time.perf_counter()
+    while reps < 5 or time.perf_counter() - t < 0.5:   # about a millisecond per run: repeat
+        oracle.scan(*[d[k] for k in order], nthreads=1)
+        reps += 1
+    out["siso_l256_fp32"] = {"tokens_per_s": round(reps * c0.tokens / (time.perf_counter() - t), 1),
+                             "sample": f"the whole workload (1 x 256 tokens x 4 heads), {reps} runs"}
+    c1 = CONFIGS["nanomamba3"]
+    ns = 4   # heads 0..3 of batch element 0 (B, C and theta are shared by all heads: G = 1)
+    d = {k: v.double().numpy() for k, v in inputs.draw_config(c1, device="cpu", batch=1).items()}
+    for k in ("x", "dt", "lam"):
+        d[k] = d[k][:, :, :ns]
+    for k in ("A", "D"):
+        d[k] = d[k][:ns]
+    t = time.perf_counter()
+    oracle.scan(*[d[k] for k in order], nthreads=1)
+    sec = time.perf_counter() - t
+    out["nanomamba3"] = {"tokens_per_s": round(ns * c1.seqlen / c1.nheads / sec, 1),
+                         "sample": f"{ns} (batch, head) slices of 2048 tokens, scaled to whole-workload tokens "
+                                   f"(1/{c1.nheads} per slice-token)"}
+    return out
 
 
 def backward_flops(cfg, L):

@@ -58,6 +58,22 @@ CONFIGS = {
 }
 
 
+# Single-chunk sequences (L = Q) at the head shapes of the 1.5B-scale layers: each sequence is
+# exactly one intra-chunk block (the masked C~B~^T product over the chunk) plus its chunk-state
+# contraction, with no state passed between chunks.  They measure the intra-chunk contractions
+# on their own; they are measurement workloads, not layers of the pages' models.
+INTRA_CHUNK = {
+    "mimo4_chunk64_b4096": ScanConfig("mimo4_chunk64_b4096", batch=4096, seqlen=64, nheads=64, headdim=64,
+                                      dstate=128, rank=4, chunk=64, seed=1005,
+                                      label="single-chunk sequences at the 1.5B MIMO head shape: 64 heads x P=64, "
+                                            "N=128, R=4, L = chunk = 64, batch 4096"),
+    "siso_chunk64_b4096": ScanConfig("siso_chunk64_b4096", batch=4096, seqlen=64, nheads=64, headdim=64,
+                                     dstate=128, rank=1, chunk=64, seed=1006,
+                                     label="single-chunk sequences at the 1.5B SISO head shape: 64 heads x P=64, "
+                                           "N=128, R=1, L = chunk = 64, batch 4096"),
+}
+
+
 def scaled(cfg: ScanConfig, **kw) -> ScanConfig:
     """A copy with some fields replaced (smaller parity-test variants)."""
     return dataclasses.replace(cfg, **kw)

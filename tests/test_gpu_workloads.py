@@ -221,3 +221,26 @@ def test_theta_per_head_out_norm_workload_every_slice():
     assert tally.slices == cfg.batch * cfg.nheads
     tally.report()
     say(f"  plain per-slice error of the normalised outputs (inflated on near-zero rows): {worst_plain:.2e}")
+
+
+@pytest.mark.parametrize("name", ["mimo4_chunk64_b4096", "siso_chunk64_b4096"])
+def test_intra_chunk_workload(name):
+    """Single-chunk sequences (L = chunk = 64, batch 4096) at the 1.5B head shapes: one launch
+    as the benchmark times it; every head of the first and the last 256 batch elements against
+    the oracle (each sequence is one intra-chunk block plus its chunk state)."""
+    from state_space_sequence_scan_amd.configs import INTRA_CHUNK
+    cfg = INTRA_CHUNK[name]
+    say("intra-chunk workload", name, cfg.label)
+    d = inputs.draw_config(cfg, device="cuda")
+    y, st = m3scan.prefill(d["x"], d["dt"], d["A"], d["lam"], d["theta"], d["B"], d["C"], d["D"], cfg.chunk)
+    torch.cuda.synchronize()
+    tally = Tally(name, TOL[cfg.io_dtype])
+    for b0 in list(range(0, 256, 64)) + list(range(cfg.batch - 256, cfg.batch, 64)):
+        b1 = b0 + 64
+        yr, hr = oracle.scan(*[f64(d[k][b0:b1] if d[k].dim() > 1 else d[k]) for k in
+                               ("x", "dt", "A", "lam", "theta", "B", "C", "D")])
+        tally.add("y", *slice_errs(f64(y[b0:b1]), yr, 2), (b0, 0))
+        tally.add("h", *slice_errs(f64(st.h[b0:b1]), hr, 1), (b0, 0))
+        tally.slices += (b1 - b0) * cfg.nheads
+        say(f"  batches {b0}..{b1 - 1} done")
+    tally.report()
