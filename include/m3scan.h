@@ -114,6 +114,10 @@ m3_status m3_prefill_workspace_size(const m3_dims* dims, size_t* bytes);
  * workspace: device memory of at least m3_prefill_workspace_size bytes
  *            (NULL allowed when that size is 0); contents on entry ignored.
  * Partial last chunks (L not a multiple of `chunk`) and L = 0 are allowed.
+ * chunk:     the block size of the chunked form.  The result does not depend on it
+ *            beyond rounding; the matrix-core kernels (bf16 io, N = 128, P = 64,
+ *            R in {1, 2, 4}, chunk 32 or 64) use it as given, the fp32 vector
+ *            kernels split a chunk whose arrays exceed LDS into halves (quarters, ..).
  */
 m3_status m3_prefill_chunked(const m3_dims* dims, const void* x, const float* dt,
                              const float* A, const float* lambda, const float* theta,

@@ -86,11 +86,17 @@ PrefillPlan plan_prefill(const PrefillArgs& a) {
         return p;
     }
     if (a.R > kMaxRankGeneric) return p;
-    if (a.batch * a.H >= (int64_t{1} << 24)) return p;   // 256-thread workgroups per (b, h): under 2^32 work-items
-    const size_t lds = generic_lds_bytes(a);
+    if (a.batch * a.H >= (int64_t{1} << 22)) return p;   // 1024-thread workgroups per (b, h): under 2^32 work-items
+    // The chunked form gives the same result for any block size (up to rounding): a chunk
+    // whose arrays do not fit in LDS is processed as consecutive blocks of half, a quarter, ..
+    // of its tokens.
+    PrefillArgs ab = a;
+    while (generic_lds_bytes(ab) > kMaxLds && ab.Q > 1) ab.Q = (ab.Q + 1) / 2;
+    const size_t lds = generic_lds_bytes(ab);
     if (lds <= kMaxLds) {
         p.path = PrefillPath::Generic;
         p.lds = lds;
+        p.q_block = ab.Q;
         add_carry_room(a, &p);
     }
     return p;
@@ -105,7 +111,9 @@ hipError_t launch_prefill(const PrefillArgs& a0, const PrefillPlan& plan, hipStr
         a.bl_in = buf;
     }
     if (plan.path == PrefillPath::Generic) {
-        e = launch_prefill_generic(a, st);
+        PrefillArgs ab = a;
+        ab.Q = plan.q_block;
+        e = launch_prefill_generic(ab, st);
     } else if (plan.path == PrefillPath::Mfma) {
         if (a.L == 0) {
             e = launch_prefill_generic(a, st);   // no chunks: passes the state through

@@ -86,6 +86,8 @@ struct PrefillPlan {
     size_t workspace;        // bytes
     size_t lds;              // dynamic LDS bytes of the main kernel
     size_t carry_off;        // workspace offset of the normalised carried-in B (fused calls)
+    int q_block;             // generic path: the chunk is processed in blocks of this many
+                             // tokens (the caller's chunk unless it does not fit in LDS)
 };
 PrefillPlan plan_prefill(const PrefillArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStream_t st);

@@ -24,14 +24,18 @@
 
 namespace m3 {
 
+// One workgroup of kThreads threads per (b, h): four waves per SIMD, so that the LDS
+// latency of one wave's loop is covered by the others.
+constexpr int kThreads = 1024;
+
 template <typename T>
-__global__ __launch_bounds__(256) void prefill_generic(
+__global__ __launch_bounds__(kThreads) void prefill_generic(
     const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
     const float* __restrict__ lam, const float* __restrict__ theta, const T* __restrict__ B,
     const T* __restrict__ C, const float* __restrict__ Dv, const void* __restrict__ h_in,
     const T* __restrict__ bl_in, const T* __restrict__ xl_in, T* __restrict__ y,
     void* __restrict__ h_out, int64_t Lmax, int H, int G, int N, int P, int R, int Q, int state_bf16,
-    const int64_t* __restrict__ cu, int64_t Tt, Fusion fu) {
+    const int64_t* __restrict__ cu, int64_t Tt, Fusion fu, int resident) {
     extern __shared__ float smem[];
     const int KP = N / 2, QR = Q * R;
     float* S = smem;                       // N*P
@@ -59,6 +63,56 @@ __global__ __launch_bounds__(256) void prefill_generic(
     const int64_t tb = sp.start, L = sp.len;
     const int tid = threadIdx.x, NT = blockDim.x;
     const float Ah = A[h], Dh = Dv[h];
+
+    // Resident mode (short sequences, decided by the host): every input of this (b, h)
+    // sequence is copied into LDS once, in one sweep of loads, and the chunks read their
+    // operands from there instead of paying a round trip to memory per chunk and phase.
+    float* rX = (fu.onw ? Yb + QR * P : Yb);   // [Lmax][R*P]
+    float* rB = rX + Lmax * R * P;             // [Lmax][R*N]
+    float* rC = rB + Lmax * R * N;             // [Lmax][R*N]
+    float* rTh = rC + Lmax * R * N;            // [Lmax][KP]
+    float* rDt = rTh + Lmax * KP;              // [Lmax]
+    float* rLam = rDt + Lmax;                  // [Lmax]
+    float* rAt = rLam + Lmax;                  // [Lmax]
+    float* rZ = rAt + Lmax;                    // [Lmax][R*P] (gate only)
+    if (resident) {
+        for (int64_t u = tid; u < L * R * P; u += NT) {
+            const int64_t t = u / (R * P), e = u - t * (R * P);
+            rX[u] = io<T>::load(x + ((tb + t) * H + h) * static_cast<size_t>(R * P) + e);
+            if (zg) rZ[u] = io<T>::load(zg + ((tb + t) * H + h) * static_cast<size_t>(R * P) + e);
+        }
+        for (int64_t u = tid; u < L * R * N; u += NT) {
+            const int64_t t = u / (R * N), e = u - t * (R * N);
+            rB[u] = io<T>::load(B + ((tb + t) * G + g) * static_cast<size_t>(R * N) + e);
+            rC[u] = io<T>::load(C + ((tb + t) * G + g) * static_cast<size_t>(R * N) + e);
+        }
+        for (int64_t u = tid; u < L * KP; u += NT) {
+            const int64_t t = u / KP, k = u - t * KP;
+            rTh[u] = theta[((tb + t) * Gt + gt) * KP + k];
+        }
+        for (int64_t t = tid; t < L; t += NT) {
+            rDt[t] = dt[(tb + t) * H + h];
+            rLam[t] = lam[(tb + t) * H + h];
+            rAt[t] = fu.At ? fu.At[(tb + t) * H + h] : Ah;
+        }
+    }
+    // operand reads by token t of the sequence (0-based): LDS in resident mode, else memory
+    auto DT = [&](int64_t t) { return resident ? rDt[t] : dt[(tb + t) * H + h]; };
+    auto LAM = [&](int64_t t) { return resident ? rLam[t] : lam[(tb + t) * H + h]; };
+    auto AT = [&](int64_t t) { return resident ? rAt[t] : (fu.At ? fu.At[(tb + t) * H + h] : Ah); };
+    auto TH = [&](int64_t t, int k) { return resident ? rTh[t * KP + k] : theta[((tb + t) * Gt + gt) * KP + k]; };
+    auto BV = [&](int64_t t, int r, int n) {
+        return resident ? rB[(t * R + r) * N + n] : io<T>::load(B + (((tb + t) * G + g) * R + r) * static_cast<size_t>(N) + n);
+    };
+    auto CV = [&](int64_t t, int r, int n) {
+        return resident ? rC[(t * R + r) * N + n] : io<T>::load(C + (((tb + t) * G + g) * R + r) * static_cast<size_t>(N) + n);
+    };
+    auto XV = [&](int64_t t, int e) {   // e < R * P
+        return resident ? rX[t * R * P + e] : io<T>::load(x + ((tb + t) * H + h) * static_cast<size_t>(R * P) + e);
+    };
+    auto ZV = [&](int64_t t, int e) {
+        return resident ? rZ[t * R * P + e] : io<T>::load(zg + ((tb + t) * H + h) * static_cast<size_t>(R * P) + e);
+    };
 
     // Incoming state: h_in plus the beta term of the first token for the carry.
     const bool carry = (bl_in != nullptr) && (xl_in != nullptr) && L > 0;
@@ -88,11 +142,11 @@ __global__ __launch_bounds__(256) void prefill_generic(
             float a = 0.f, gm = 0.f, w = 0.f;
             if (i < nq) {
                 const int64_t t = t0 + i;
-                const float dtv = dt[(tb + t) * H + h], lv = lam[(tb + t) * H + h];
-                a = dtv * (fu.At ? fu.At[(tb + t) * H + h] : Ah);
+                const float dtv = DT(t), lv = LAM(t);
+                a = dtv * AT(t);
                 gm = lv * dtv;
                 w = gm;
-                if (t + 1 < L) w += (1.f - lam[(tb + t + 1) * H + h]) * dt[(tb + t + 1) * H + h];
+                if (t + 1 < L) w += (1.f - LAM(t + 1)) * DT(t + 1);
             }
             if (Q <= 64) {   // i == lane of wave 0
                 for (int off = 1; off < 64; off <<= 1) {
@@ -106,10 +160,25 @@ __global__ __launch_bounds__(256) void prefill_generic(
                 wv[i] = w;
             }
         }
-        // Angles into LDS, one element per thread (loads in parallel).
-        for (int idx = tid; idx < Q * KP; idx += NT) {
-            const int i = idx / KP, k = idx - i * KP;
-            phi[idx] = (i < nq) ? theta[((tb + t0 + i) * Gt + gt) * KP + k] : 0.f;
+        // Angles into LDS.  Up to 64 tokens per chunk, each pair's chunk-local prefix sum is
+        // taken right here with lane shuffles over W lanes (W the power of two >= Q: tokens
+        // i of pair k on lanes k W + i); longer chunks sum serially below.
+        if (Q <= 64) {
+            const int W = Q <= 1 ? 1 : 1 << (32 - __clz(Q - 1));
+            for (int base = 0; base < KP * W; base += NT) {   // every lane of a wave takes the shuffles
+                const int u = base + tid, k = u / W, i = u - k * W;
+                float v = (u < KP * W && i < nq) ? TH(t0 + i, k) : 0.f;
+                for (int off = 1; off < W; off <<= 1) {
+                    const float o = __shfl_up(v, off, W);
+                    if (i >= off) v += o;
+                }
+                if (u < KP * W && i < Q) phi[i * KP + k] = v;
+            }
+        } else {
+            for (int idx = tid; idx < Q * KP; idx += NT) {
+                const int i = idx / KP, k = idx - i * KP;
+                phi[idx] = (i < nq) ? TH(t0 + i, k) : 0.f;
+            }
         }
         // RMSNorm scales of the chunk's B and C rows (token, rank), when normalised.
         if (fu.bnw || fu.cnw) {
@@ -117,9 +186,8 @@ __global__ __launch_bounds__(256) void prefill_generic(
                 const int i = row / R, r = row - i * R;
                 float sb = 0.f, sc = 0.f;
                 if (i < nq) {
-                    const size_t o = (((tb + t0 + i) * G + g) * R + r) * static_cast<size_t>(N);
                     for (int n = 0; n < N; ++n) {
-                        const float bv = io<T>::load(B + o + n), cv = io<T>::load(C + o + n);
+                        const float bv = BV(t0 + i, r, n), cv = CV(t0 + i, r, n);
                         sb += bv * bv;
                         sc += cv * cv;
                     }
@@ -129,12 +197,14 @@ __global__ __launch_bounds__(256) void prefill_generic(
             }
         }
         __syncthreads();
-        // Chunk-local angle prefix sums, one pair per thread, within LDS.
-        for (int k = tid; k < KP; k += NT) {
-            float acc = 0.f;
-            for (int i = 0; i < Q; ++i) {
-                acc += phi[i * KP + k];
-                phi[i * KP + k] = acc;
+        // Chunk-local angle prefix sums of longer chunks, one pair per thread, within LDS.
+        if (Q > 64) {
+            for (int k = tid; k < KP; k += NT) {
+                float acc = 0.f;
+                for (int i = 0; i < Q; ++i) {
+                    acc += phi[i * KP + k];
+                    phi[i * KP + k] = acc;
+                }
             }
         }
         if (Q > 64 && tid == 0) {
@@ -150,11 +220,10 @@ __global__ __launch_bounds__(256) void prefill_generic(
             const int i = idx / (R * KP), rem = idx - i * R * KP, r = rem / KP, k = rem - r * KP;
             float b0 = 0.f, b1 = 0.f, c0 = 0.f, c1 = 0.f;
             if (i < nq) {
-                const size_t o = (((tb + t0 + i) * G + g) * R + r) * static_cast<size_t>(N) + 2 * k;
                 float sn, cs;
                 sincos_acc(phi[i * KP + k], &sn, &cs);
-                float bb0 = io<T>::load(B + o), bb1 = io<T>::load(B + o + 1);
-                float cc0 = io<T>::load(C + o), cc1 = io<T>::load(C + o + 1);
+                float bb0 = BV(t0 + i, r, 2 * k), bb1 = BV(t0 + i, r, 2 * k + 1);
+                float cc0 = CV(t0 + i, r, 2 * k), cc1 = CV(t0 + i, r, 2 * k + 1);
                 const int wi = r * N + 2 * k;
                 if (fu.bnw) {
                     bb0 *= bsc[i * R + r] * fu.bnw[wi];
@@ -184,9 +253,7 @@ __global__ __launch_bounds__(256) void prefill_generic(
         }
         for (int idx = tid; idx < QR * P; idx += NT) {
             const int i = idx / (R * P);
-            X[idx] = (i < nq) ? io<T>::load(x + ((tb + t0 + i) * H + h) * static_cast<size_t>(R * P) +
-                                            (idx - i * R * P))
-                              : 0.f;
+            X[idx] = (i < nq) ? XV(t0 + i, idx - i * R * P) : 0.f;
         }
         __syncthreads();
         const float cend = cum[Q - 1];
@@ -198,6 +265,7 @@ __global__ __launch_bounds__(256) void prefill_generic(
             float v = 0.f;
             if (j <= i) {
                 float dot = 0.f;
+#pragma unroll 4
                 for (int n = 0; n < N; ++n) dot += Ct[ir * N + n] * Bt[js * N + n];
                 const float m = (j < i) ? __expf(cum[i] - cum[j]) * wv[j] : gam[i];
                 v = m * dot;
@@ -211,12 +279,14 @@ __global__ __launch_bounds__(256) void prefill_generic(
             const int i = ir / R;
             if (i >= nq) continue;
             float st = 0.f;
+#pragma unroll 4
             for (int n = 0; n < N; ++n) st += Ct[ir * N + n] * S[n * P + p];
             float acc = __expf(cum[i]) * st;
+#pragma unroll 4
             for (int js = 0; js < (i + 1) * R; ++js) acc += Gm[ir * QR + js] * X[js * P + p];
             acc += Dh * X[ir * P + p];
             const size_t yi = ((tb + t0 + i) * H + h) * static_cast<size_t>(R * P) + (ir - i * R) * P + p;
-            if (zg) acc *= silu(io<T>::load(zg + yi));
+            if (zg) acc *= silu(ZV(t0 + i, (ir - i * R) * P + p));
             if (fu.onw)
                 Yb[idx] = acc;   // normalised below
             else
@@ -244,6 +314,7 @@ __global__ __launch_bounds__(256) void prefill_generic(
         for (int idx = tid; idx < KP * P; idx += NT) {
             const int k = idx / P, p = idx - k * P;
             float s0 = decay * S[(2 * k) * P + p], s1 = decay * S[(2 * k + 1) * P + p];
+#pragma unroll 4
             for (int js = 0; js < QR; ++js) {
                 const float xs = sv[js / R] * X[js * P + p];
                 s0 += Bt[js * N + 2 * k] * xs;
@@ -333,21 +404,31 @@ size_t generic_lds_bytes(const PrefillArgs& a) {
                             (a.fu.onw ? QR * a.P : 0));
 }
 
+// LDS of one whole sequence's inputs (resident mode): x (and the gate input), B, C, the
+// angles, dt, lambda and the decay rate of every token, fp32.
+static size_t resident_lds_bytes(const PrefillArgs& a) {
+    const size_t per_token = static_cast<size_t>(a.R) * a.P * (a.fu.z ? 2 : 1) + 2 * static_cast<size_t>(a.R) * a.N +
+                             a.N / 2 + 3;
+    return sizeof(float) * per_token * static_cast<size_t>(a.L);
+}
+
 template <typename T>
 static hipError_t launch_generic_t(const PrefillArgs& a, hipStream_t st) {
-    const size_t shm = generic_lds_bytes(a);
+    // resident mode when the sequence's inputs fit in LDS beside the chunk arrays
+    const bool resident = generic_lds_bytes(a) + resident_lds_bytes(a) <= 160 * 1024;
+    const size_t shm = generic_lds_bytes(a) + (resident ? resident_lds_bytes(a) : 0);
     if (shm > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_generic<T>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  static_cast<int>(shm));
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(prefill_generic<T>, dim3(static_cast<unsigned>(a.batch * a.H)), dim3(256), shm,
+    hipLaunchKernelGGL(prefill_generic<T>, dim3(static_cast<unsigned>(a.batch * a.H)), dim3(kThreads), shm,
                        st, static_cast<const T*>(a.x), a.dt, a.A, a.lam, a.theta,
                        static_cast<const T*>(a.B), static_cast<const T*>(a.C), a.D, a.h_in,
                        static_cast<const T*>(a.bl_in), static_cast<const T*>(a.xl_in),
                        static_cast<T*>(a.y), a.h_out, a.L, a.H, a.G, a.N, a.P, a.R, a.Q,
-                       a.state_bf16 ? 1 : 0, a.cu, a.T, a.fu);
+                       a.state_bf16 ? 1 : 0, a.cu, a.T, a.fu, resident ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -113,6 +113,20 @@ def test_prefill_rejects_unsupported(lib):
     n = ctypes.c_size_t(0)
     assert lib.m3_prefill_workspace_size(ctypes.byref(d), ctypes.byref(n)) == -2
     assert lib.m3_prefill_chunked(ctypes.byref(d), *[FAKE] * 8, None, None, FAKE, None, 0, None) == -2
+    # a state too large for LDS whatever the block size
+    d = _dims(rank=1, dstate=512, headdim=512, chunk=1)
+    assert lib.m3_prefill_workspace_size(ctypes.byref(d), ctypes.byref(n)) == -2
+
+
+@pytest.mark.parametrize("R,Q", [(4, 64), (2, 64), (4, 128)])
+def test_fp32_chunks_larger_than_lds_are_split(lib, R, Q):
+    """fp32 io at the 1.5B head shape (N=128, P=64): chunks whose arrays exceed LDS run as
+    smaller blocks instead of being refused (the chunked result does not depend on the block
+    size beyond rounding); only the carry room is asked for as workspace."""
+    d = m3scan.make_dims(2, 300, 4, 1, 64, 128, R, Q, m3scan.M3_F32)
+    n = ctypes.c_size_t(0)
+    assert lib.m3_prefill_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    assert n.value == 2 * 1 * R * 128 * 4   # batch x G x R x N fp32: the normalised carried B
 
 
 @pytest.mark.parametrize("kw", [k for k in BAD_DIMS if "seqlen" not in k and "chunk" not in k],
