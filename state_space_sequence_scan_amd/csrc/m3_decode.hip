@@ -13,6 +13,7 @@
 // (2k, 2k+1) inside one thread.  decode_stream (N = 128, P = 64) keeps the R x P
 // read-out reduction inside each wave; decode_fast (small N) reduces across
 // waves through LDS; decode_generic handles any other shape.
+#include <algorithm>
 #include <type_traits>
 
 #include "m3_common.h"
@@ -21,18 +22,32 @@
 namespace m3 {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // CW consecutive state values of one row: 16 bytes for CW = 4 fp32 or CW = 8 bf16
 // (8 bytes for CW = 4 bf16), streamed with non-temporal accesses.
 template <typename S, int CW> struct state_vec;
+// Raw is the loaded form (kept in registers by the prefetching variant) and widen()
+// turns it into fp32.
 template <> struct state_vec<float, 4> {
     typedef float V __attribute__((ext_vector_type(4)));
+    typedef V Raw;
     __device__ __forceinline__ static V load(const float* p) { return state4<float>::load(p); }
+    __device__ __forceinline__ static Raw load_raw(const float* p) { return state4<float>::load(p); }
+    __device__ __forceinline__ static V widen(Raw w) { return w; }
     __device__ __forceinline__ static void store(float* p, V v) { state4<float>::store(p, v); }
 };
 template <> struct state_vec<bf16_t, 4> {
     typedef float V __attribute__((ext_vector_type(4)));
+    typedef u32x2_t Raw;
     __device__ __forceinline__ static V load(const bf16_t* p) { return state4<bf16_t>::load(p); }
+    __device__ __forceinline__ static Raw load_raw(const bf16_t* p) {
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    }
+    __device__ __forceinline__ static V widen(Raw w) {
+        return V{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                 __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+    }
     __device__ __forceinline__ static void store(bf16_t* p, V v) { state4<bf16_t>::store(p, v); }
 };
 template <> struct state_vec<bf16_t, 8> {
@@ -54,6 +69,73 @@ template <> struct state_vec<bf16_t, 8> {
         const W w = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
                      __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
         __builtin_nontemporal_store(w, reinterpret_cast<W*>(p));
+    }
+};
+
+// n consecutive values of T from p into fp32, with loads of up to 16 bytes, and the
+// reverse.  (Global accesses need not be aligned to their width on this hardware; the
+// callers' runs start at multiples of their own length.)
+template <typename T, int n> struct run;
+template <int n> struct run<bf16_t, n> {
+    __device__ __forceinline__ static void load(const bf16_t* p, float* out) {
+        if constexpr (n % 8 == 0) {
+#pragma unroll
+            for (int k = 0; k < n / 8; ++k) {
+                const u32x4_t w = *reinterpret_cast<const u32x4_t*>(p + 8 * k);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    out[8 * k + 2 * j] = __uint_as_float(w[j] << 16);
+                    out[8 * k + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+                }
+            }
+        } else if constexpr (n == 4) {
+            const u32x2_t w = *reinterpret_cast<const u32x2_t*>(p);
+            out[0] = __uint_as_float(w.x << 16);
+            out[1] = __uint_as_float(w.x & 0xffff0000u);
+            out[2] = __uint_as_float(w.y << 16);
+            out[3] = __uint_as_float(w.y & 0xffff0000u);
+        } else {
+#pragma unroll
+            for (int k = 0; k < n; ++k) out[k] = io<bf16_t>::load(p + k);
+        }
+    }
+    __device__ __forceinline__ static void store(bf16_t* p, const float* v) {
+        if constexpr (n % 4 == 0) {
+#pragma unroll
+            for (int k = 0; k < n / 4; ++k) {
+                const u32x2_t w = {f32_to_bf16(v[4 * k]) | (static_cast<uint32_t>(f32_to_bf16(v[4 * k + 1])) << 16),
+                                   f32_to_bf16(v[4 * k + 2]) | (static_cast<uint32_t>(f32_to_bf16(v[4 * k + 3])) << 16)};
+                *reinterpret_cast<u32x2_t*>(p + 4 * k) = w;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < n; ++k) io<bf16_t>::store(p + k, v[k]);
+        }
+    }
+};
+template <int n> struct run<float, n> {
+    __device__ __forceinline__ static void load(const float* p, float* out) {
+        if constexpr (n % 4 == 0) {
+#pragma unroll
+            for (int k = 0; k < n / 4; ++k) {
+                const f32x4_t w = *reinterpret_cast<const f32x4_t*>(p + 4 * k);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) out[4 * k + j] = w[j];
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < n; ++k) out[k] = p[k];
+        }
+    }
+    __device__ __forceinline__ static void store(float* p, const float* v) {
+        if constexpr (n % 4 == 0) {
+#pragma unroll
+            for (int k = 0; k < n / 4; ++k)
+                *reinterpret_cast<f32x4_t*>(p + 4 * k) = f32x4_t{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
+        } else {
+#pragma unroll
+            for (int k = 0; k < n; ++k) p[k] = v[k];
+        }
     }
 };
 
@@ -132,7 +214,19 @@ __device__ __forceinline__ void row_rms(const float* sO, float* sRs, int R, int 
 // k = kk + TPG * j (kk = tid / PC, j < PPT), i.e. 2 * PPT state rows x CW columns.
 // FU: the fused prologue/epilogue may be present (its weights, biases and gate input are
 // then loaded with the other small operands, ahead of the state stream).
-template <typename T, typename S, int N, int P, int R, int NT, int CW, bool FU>
+// PACED: the per-token operands are loaded and staged in LDS in three dependent
+// groups (B, C and the previous B; X and the previous X; the angles), and the state
+// loads are issued after the last.  Measured at N = 128, P = 64, R = 4 with an fp32
+// state (169 us per step at batch 256, H = 64), this is 4% faster than issuing the
+// state loads right behind all the operand loads, and the variants that start the
+// fp32 state stream earlier still (the operands staged in one group: 3% slower; the
+// state loads first: 7% slower) lose too: the state streams of the resident workgroups
+// are spread in time.  Without PACED the operands are loaded in one or two wide
+// unconditional loads per array and the state loads issued right behind them, their
+// staging under the state stream: with a bf16 state, whose single-wave workgroups
+// carry more arithmetic per byte, that is 7% faster than operand loads that complete
+// one after another (97 against 103 us).
+template <typename T, typename S, int N, int P, int R, int NT, int CW, bool FU, bool PACED>
 __global__ __launch_bounds__(NT) void decode_fast(
     S* __restrict__ h, const T* __restrict__ b_last, const T* __restrict__ x_last,
     const T* __restrict__ x_t, const float* __restrict__ dt_t, const float* __restrict__ A,
@@ -145,73 +239,96 @@ __global__ __launch_bounds__(NT) void decode_fast(
     constexpr int PPT = KP / TPG;
     constexpr int NW = (NT + 63) / 64;
     static_assert(P % CW == 0 && NT % PC == 0 && KP % TPG == 0 && PPT >= 1, "decode tiling");
-    typedef typename state_vec<S, CW>::V fvec;
+    typedef state_vec<S, CW> SV;
+    typedef typename SV::V fvec;
+    typedef typename SV::Raw raw;
 
-    const int bh = blockIdx.x;
-    const int b = bh / H, hh = bh - b * H;
-    const int g = hh / (H / G);
-    const int Gt = fu.tgroups(G), gt = hh / (H / Gt);   // angle group
     const int tid = threadIdx.x;
+    __builtin_assume(tid < NT);   // lets the element guards below fold away
     const int c = tid % PC;
     const int kk = tid / PC;
 
     __shared__ float sB[R][N], sC[R][N], sBp[R][N];
     __shared__ __align__(32) float sX[R][P];
     __shared__ __align__(32) float sXp[R][P];
-    __shared__ float sCs[KP], sSn[KP];
+    __shared__ float sCs[KP + 1], sSn[KP + 1];   // + a slot that threads past KP write
+    __shared__ __align__(32) float sY[NW][R][P];
 
-    // The small per-token operands are loaded into registers first and written to
-    // LDS after the state loads have been issued: their staging then overlaps the
-    // state stream instead of delaying it.
     constexpr int SPT = (R * N + NT - 1) / NT;
     constexpr int XPT = (R * P + NT - 1) / NT;
     constexpr int KPT = (KP + NT - 1) / NT;
+    constexpr bool SRUN = !PACED && (R * N) % NT == 0, XRUN = !PACED && (R * P) % NT == 0;
+    auto sidx = [&](int e) { return SRUN ? tid * SPT + e : tid + NT * e; };   // element of B/C
+    auto xidx = [&](int e) { return XRUN ? tid * XPT + e : tid + NT * e; };   // element of X/Y
+
+    const int bh = blockIdx.x;
+    const int b = bh / H, hh = bh - b * H;
+    const int g = hh / (H / G);
+    const int Gt = fu.tgroups(G), gt = hh / (H / Gt);   // angle group
+
+    // Without PACED the small per-token operands are loaded into registers here, the
+    // state loads are issued, and then the operands are staged in LDS.  A thread's
+    // elements are consecutive when the threads tile the array exactly (SRUN, XRUN: one
+    // or two wide loads each), else strided, and every load is unconditional (a clamped
+    // index or a valid stand-in array; unwanted values are dropped at staging), so that
+    // the compiler has no branch join at which to wait for them.
     const size_t gofs = (static_cast<size_t>(b) * G + g) * R * N;
     const size_t hofs = static_cast<size_t>(bh) * R * P;
-    float vb[SPT], vc[SPT], vbp[SPT], vx[XPT], vxp[XPT], vth[KPT];
+    const T* bl = has_carry ? b_last : B_t;   // without a carry its values are dropped
+    const T* xl = has_carry ? x_last : x_t;
+    constexpr int SR = PACED ? 1 : SPT, XR = PACED ? 1 : XPT, KR = PACED ? 1 : KPT;
+    float vb[SR], vc[SR], vbp[SR], vx[XR], vxp[XR], vth[KR];
+    if constexpr (!PACED) {
+        if constexpr (SRUN) {
+            run<T, SPT>::load(B_t + gofs + tid * SPT, vb);
+            run<T, SPT>::load(C_t + gofs + tid * SPT, vc);
+            run<T, SPT>::load(bl + gofs + tid * SPT, vbp);
+        } else {
 #pragma unroll
-    for (int e = 0; e < SPT; ++e) {
-        const int i = tid + NT * e;
-        vb[e] = vc[e] = vbp[e] = 0.f;
-        if (i < R * N) {
-            vb[e] = io<T>::load(B_t + gofs + i);
-            vc[e] = io<T>::load(C_t + gofs + i);
-            if (has_carry) vbp[e] = io<T>::load(b_last + gofs + i);
+            for (int e = 0; e < SPT; ++e) {
+                const int i = sidx(e), ic = i < R * N ? i : 0;
+                vb[e] = io<T>::load(B_t + gofs + ic);
+                vc[e] = io<T>::load(C_t + gofs + ic);
+                vbp[e] = io<T>::load(bl + gofs + ic);
+            }
         }
-    }
+        if constexpr (XRUN) {
+            run<T, XPT>::load(x_t + hofs + tid * XPT, vx);
+            run<T, XPT>::load(xl + hofs + tid * XPT, vxp);
+        } else {
 #pragma unroll
-    for (int e = 0; e < XPT; ++e) {
-        const int i = tid + NT * e;
-        vx[e] = vxp[e] = 0.f;
-        if (i < R * P) {
-            vx[e] = io<T>::load(x_t + hofs + i);
-            if (has_carry) vxp[e] = io<T>::load(x_last + hofs + i);
+            for (int e = 0; e < XPT; ++e) {
+                const int i = xidx(e), ic = i < R * P ? i : 0;
+                vx[e] = io<T>::load(x_t + hofs + ic);
+                vxp[e] = io<T>::load(xl + hofs + ic);
+            }
         }
-    }
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-        const int k = tid + NT * e;
-        vth[e] = (k < KP) ? theta_t[(static_cast<size_t>(b) * Gt + gt) * KP + k] : 0.f;
+        for (int e = 0; e < KPT; ++e) {
+            const int k = tid + NT * e;
+            vth[e] = theta_t[(static_cast<size_t>(b) * Gt + gt) * KP + (k < KP ? k : 0)];
+        }
     }
     // Fused pieces of this thread's elements: norm weights and biases of its B/C entries,
-    // the gate input and output-norm weight of its outputs.
+    // the gate input and output-norm weight of its outputs (absent ones read a stand-in
+    // and are replaced by their neutral value at use).
     constexpr int FS = FU ? SPT : 1, FX = FU ? XPT : 1;
     float wbn[FS], wcn[FS], wbb[FS], wcb[FS], vz[FX], won[FX];
     if constexpr (FU) {
+        const float* one = dt_t + bh;   // any valid element
 #pragma unroll
         for (int e = 0; e < SPT; ++e) {
-            const int i = tid + NT * e;
-            const bool in = i < R * N;
-            wbn[e] = (in && fu.bnw) ? fu.bnw[i] : 1.f;
-            wcn[e] = (in && fu.cnw) ? fu.cnw[i] : 1.f;
-            wbb[e] = (in && fu.bbias) ? fu.bbias[i] : 0.f;
-            wcb[e] = (in && fu.cbias) ? fu.cbias[i] : 0.f;
+            const int i = sidx(e), ic = i < R * N ? i : 0;
+            wbn[e] = *(fu.bnw ? fu.bnw + ic : one);
+            wcn[e] = *(fu.cnw ? fu.cnw + ic : one);
+            wbb[e] = *(fu.bbias ? fu.bbias + ic : one);
+            wcb[e] = *(fu.cbias ? fu.cbias + ic : one);
         }
 #pragma unroll
         for (int e = 0; e < XPT; ++e) {
-            const int i = tid + NT * e;
-            vz[e] = (fu.z && i < R * P) ? io<T>::load(static_cast<const T*>(fu.z) + hofs + i) : 0.f;
-            won[e] = (fu.onw && i < R * P) ? fu.onw[hh * P + i % P] : 1.f;
+            const int i = xidx(e), ic = i < R * P ? i : 0;
+            vz[e] = io<T>::load((fu.z ? static_cast<const T*>(fu.z) : x_t) + hofs + ic);
+            won[e] = *(fu.onw ? fu.onw + hh * P + ic % P : one);
         }
     }
 
@@ -229,39 +346,81 @@ __global__ __launch_bounds__(NT) void decode_fast(
     const float bsc = fuse ? 1.f : c2, bpsc = fuse ? 1.f : c1;
 
     S* hp = h + static_cast<size_t>(bh) * N * P;
-    fvec s0[PPT], s1[PPT];
+    raw s0[PPT], s1[PPT];
+    auto load_state = [&]() {
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-        const int k = kk + TPG * j;
-        s0[j] = state_vec<S, CW>::load(hp + (2 * k) * P + CW * c);
-        s1[j] = state_vec<S, CW>::load(hp + (2 * k + 1) * P + CW * c);
-    }
-
-#pragma unroll
-    for (int e = 0; e < SPT; ++e) {
-        const int i = tid + NT * e;
-        if (i < R * N) {
-            (&sB[0][0])[i] = vb[e] * bsc;
-            (&sC[0][0])[i] = vc[e];
-            (&sBp[0][0])[i] = vbp[e] * bpsc;
+        for (int j = 0; j < PPT; ++j) {
+            const int k = kk + TPG * j;
+            s0[j] = SV::load_raw(hp + (2 * k) * P + CW * c);
+            s1[j] = SV::load_raw(hp + (2 * k + 1) * P + CW * c);
         }
-    }
+    };
+    if constexpr (PACED) {
+        // Three dependent groups: each is staged before the next is issued (the
+        // scheduling barriers keep the later loads behind the earlier LDS writes).
 #pragma unroll
-    for (int e = 0; e < XPT; ++e) {
-        const int i = tid + NT * e;
-        if (i < R * P) {
-            (&sX[0][0])[i] = vx[e];
-            (&sXp[0][0])[i] = vxp[e];
+        for (int e = 0; e < SPT; ++e) {
+            const int i = sidx(e), ic = i < R * N ? i : 0;
+            const float vbe = io<T>::load(B_t + gofs + ic), vce = io<T>::load(C_t + gofs + ic);
+            const float vbpe = io<T>::load(bl + gofs + ic);
+            if (i < R * N) {
+                (&sB[0][0])[i] = vbe * bsc;
+                (&sC[0][0])[i] = vce;
+                (&sBp[0][0])[i] = has_carry ? vbpe * bpsc : 0.f;
+            }
         }
-    }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-        const int k = tid + NT * e;
-        if (k < KP) {
+        for (int e = 0; e < XPT; ++e) {
+            const int i = xidx(e), ic = i < R * P ? i : 0;
+            const float vxe = io<T>::load(x_t + hofs + ic), vxpe = io<T>::load(xl + hofs + ic);
+            if (i < R * P) {
+                (&sX[0][0])[i] = vxe;
+                (&sXp[0][0])[i] = has_carry ? vxpe : 0.f;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const int k = tid + NT * e, kw = k < KP ? k : KP;   // threads past KP write the spare slot
+            float sn, cs;
+            sincos_acc(theta_t[(static_cast<size_t>(b) * Gt + gt) * KP + (k < KP ? k : 0)], &sn, &cs);
+            sCs[kw] = alpha * cs;
+            sSn[kw] = alpha * sn;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        load_state();
+    } else {
+        load_state();
+        // Keep the staging below behind the state loads (the scheduler would otherwise
+        // hoist it, and with it the wait for the small loads, ahead of them).
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int e = 0; e < SPT; ++e) {
+            const int i = sidx(e);
+            if (i < R * N) {
+                (&sB[0][0])[i] = vb[e] * bsc;
+                (&sC[0][0])[i] = vc[e];
+                (&sBp[0][0])[i] = has_carry ? vbp[e] * bpsc : 0.f;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < XPT; ++e) {
+            const int i = xidx(e);
+            if (i < R * P) {
+                (&sX[0][0])[i] = vx[e];
+                (&sXp[0][0])[i] = has_carry ? vxp[e] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            // every thread, without a branch, so that the angle load is not moved behind
+            // the state loads; threads past KP write the spare slot
+            const int k = tid + NT * e, kw = k < KP ? k : KP;
             float sn, cs;
             sincos_acc(vth[e], &sn, &cs);
-            sCs[k] = alpha * cs;
-            sSn[k] = alpha * sn;
+            sCs[kw] = alpha * cs;
+            sSn[kw] = alpha * sn;
         }
     }
     __syncthreads();
@@ -274,14 +433,16 @@ __global__ __launch_bounds__(NT) void decode_fast(
             float* fBp = &sBp[0][0];
 #pragma unroll
             for (int e = 0; e < SPT; ++e) {
-                const int i = tid + NT * e;
+                const int i = sidx(e);
                 if (i < R * N) {
                     const int r = i / N;
                     const float sb = fu.bnw ? sScale[r] : 1.f, sbp = fu.bnw ? sScale[2 * R + r] : 1.f;
                     const float sc = fu.cnw ? sScale[R + r] : 1.f;
-                    fB[i] = (fB[i] * (sb * wbn[e]) + wbb[e]) * c2;
-                    fC[i] = fC[i] * (sc * wcn[e]) + wcb[e];
-                    fBp[i] = (fBp[i] * (sbp * wbn[e]) + wbb[e]) * c1;
+                    const float wb = fu.bnw ? wbn[e] : 1.f, wc = fu.cnw ? wcn[e] : 1.f;
+                    const float bb = fu.bbias ? wbb[e] : 0.f, cb = fu.cbias ? wcb[e] : 0.f;
+                    fB[i] = (fB[i] * (sb * wb) + bb) * c2;
+                    fC[i] = fC[i] * (sc * wc) + cb;
+                    fBp[i] = has_carry ? (fBp[i] * (sbp * wb) + bb) * c1 : 0.f;
                 }
             }
             __syncthreads();
@@ -302,7 +463,7 @@ __global__ __launch_bounds__(NT) void decode_fast(
     for (int j = 0; j < PPT; ++j) {
         const int k = kk + TPG * j;
         const float cs = sCs[k], sn = sSn[k];   // alpha cos, alpha sin
-        fvec v0 = s0[j], v1 = s1[j], n0 = fvec(0.f), n1 = n0;
+        fvec v0 = SV::widen(s0[j]), v1 = SV::widen(s1[j]), n0 = fvec(0.f), n1 = n0;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             v0 += sBp[r][2 * k] * xpv[r];       // h + (1 - lambda) dt U_prev
@@ -314,8 +475,8 @@ __global__ __launch_bounds__(NT) void decode_fast(
         n0 -= sn * v1;
         n1 += sn * v0;
         n1 += cs * v1;
-        state_vec<S, CW>::store(hp + (2 * k) * P + CW * c, n0);
-        state_vec<S, CW>::store(hp + (2 * k + 1) * P + CW * c, n1);
+        SV::store(hp + (2 * k) * P + CW * c, n0);
+        SV::store(hp + (2 * k + 1) * P + CW * c, n1);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             yacc[r] += sC[r][2 * k] * n0;
@@ -332,7 +493,6 @@ __global__ __launch_bounds__(NT) void decode_fast(
 #pragma unroll
             for (int q = 0; q < CW; ++q) yacc[r][q] += __shfl_xor(yacc[r][q], off);
     }
-    __shared__ __align__(32) float sY[NW][R][P];
     const int lane = tid & 63, wave = tid >> 6;
     if (lane < PC) {
 #pragma unroll
@@ -343,7 +503,7 @@ __global__ __launch_bounds__(NT) void decode_fast(
     float yo[XPT];
 #pragma unroll
     for (int e = 0; e < XPT; ++e) {
-        const int i = tid + NT * e;
+        const int i = xidx(e);
         float acc = 0.f;
         if (i < R * P) {
 #pragma unroll
@@ -361,22 +521,26 @@ __global__ __launch_bounds__(NT) void decode_fast(
             __shared__ float sRs[R];
 #pragma unroll
             for (int e = 0; e < XPT; ++e) {
-                const int i = tid + NT * e;
+                const int i = xidx(e);
                 if (i < R * P) sO[i] = yo[e];
             }
             __syncthreads();
             row_rms(sO, sRs, R, P, NT, fu.eps);
 #pragma unroll
             for (int e = 0; e < XPT; ++e) {
-                const int i = tid + NT * e;
+                const int i = xidx(e);
                 if (i < R * P) yo[e] *= sRs[i / P] * won[e];
             }
         }
     }
+    if constexpr (XRUN) {
+        run<T, XPT>::store(y_t + hofs + tid * XPT, yo);
+    } else {
 #pragma unroll
-    for (int e = 0; e < XPT; ++e) {
-        const int i = tid + NT * e;
-        if (i < R * P) io<T>::store(y_t + hofs + i, yo[e]);
+        for (int e = 0; e < XPT; ++e) {
+            const int i = xidx(e);
+            if (i < R * P) io<T>::store(y_t + hofs + i, yo[e]);
+        }
     }
 }
 
@@ -479,7 +643,8 @@ static hipError_t launch_fast(const DecodeArgs& a, hipStream_t st) {
     // the fused variant only when a norm, bias, gate or output norm is given (a per-token A
     // or angles per head alone are one scalar or one index per workgroup, read by both)
     const bool fused = a.fu.bc() || a.fu.z || a.fu.onw;
-    auto kernel = fused ? decode_fast<T, S, N, P, R, NT, CW, true> : decode_fast<T, S, N, P, R, NT, CW, false>;
+    constexpr bool PACED = std::is_same<S, float>::value;
+    auto kernel = fused ? decode_fast<T, S, N, P, R, NT, CW, true, PACED> : decode_fast<T, S, N, P, R, NT, CW, false, PACED>;
     hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(a.batch * a.H)),
                        dim3(NT), 0, st, static_cast<S*>(a.h), static_cast<const T*>(a.b_last),
                        static_cast<const T*>(a.x_last), static_cast<const T*>(a.x_t), a.dt_t, a.A,
