@@ -158,7 +158,12 @@ m3_status m3_prefill_varlen(const m3_dims* dims, const int64_t* cu_seqlens, int6
  * One decode step for every (b, h): reads the state h (dims->state_dtype) in
  * place, applies one token in fp32 and writes the new state back to h, and
  * writes y_t (batch, H, R, P).  y_t reads the new state before it is rounded to
- * a bf16 state.
+ * a bf16 state.  This is the single-token recurrence step of the paper note's
+ * "Problem definition" (its third problem: each generated token reads and writes
+ * the whole state for little arithmetic, so the step is bound by memory
+ * bandwidth) with the rank-R update of "Solution 3: MIMO", which raises the
+ * arithmetic per state byte.  Its equations are those at the top of this file
+ * at L = 1.
  *
  * b_last, x_last: B and X of the previous token (the trapezoid carry), in the
  *            io dtype; both NULL means a zero previous input.  They are only

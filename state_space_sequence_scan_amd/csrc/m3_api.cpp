@@ -85,6 +85,11 @@ PrefillPlan plan_prefill(const PrefillArgs& a) {
         add_carry_room(a, &p);
         return p;
     }
+    if (serial_supported(a)) {   // small states: the tokens one by one
+        p.path = PrefillPath::Serial;
+        add_carry_room(a, &p);
+        return p;
+    }
     if (a.R > kMaxRankGeneric) return p;
     if (a.batch * a.H >= (int64_t{1} << 22)) return p;   // 1024-thread workgroups per (b, h): under 2^32 work-items
     // The chunked form gives the same result for any block size (up to rounding): a chunk
@@ -114,6 +119,8 @@ hipError_t launch_prefill(const PrefillArgs& a0, const PrefillPlan& plan, hipStr
         PrefillArgs ab = a;
         ab.Q = plan.q_block;
         e = launch_prefill_generic(ab, st);
+    } else if (plan.path == PrefillPath::Serial) {
+        e = launch_prefill_serial(a, st);
     } else if (plan.path == PrefillPath::Mfma) {
         if (a.L == 0) {
             e = launch_prefill_generic(a, st);   // no chunks: passes the state through

@@ -77,7 +77,7 @@ struct PrefillArgs {
 };
 
 // Which kernel family runs a prefill, and the workspace it needs.
-enum class PrefillPath { Generic, Mfma, Unsupported };
+enum class PrefillPath { Generic, Mfma, Serial, Unsupported };
 struct PrefillPlan {
     PrefillPath path;
     int nseg;                // segments per sequence (1 = one sweep per (b, h))
@@ -95,6 +95,12 @@ hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStre
 // Generic family (any shape whose chunk fits in LDS), in m3_prefill_generic.hip.
 size_t generic_lds_bytes(const PrefillArgs& a);
 hipError_t launch_prefill_generic(const PrefillArgs& a, hipStream_t st);
+
+// Token-serial kernel for small states (N/2 a power of two, N/2 * P <= 256, no fused
+// norm, bias, gate or output norm), in m3_prefill_serial.hip.
+bool serial_supported(const PrefillArgs& a);
+size_t serial_lds_bytes(const PrefillArgs& a);
+hipError_t launch_prefill_serial(const PrefillArgs& a, hipStream_t st);
 
 // Matrix-core family (bf16, N = 128, P = 64, R in {1, 2, 4}, Q in {32, 64}),
 // in m3_prefill_mfma.hip.
