@@ -117,7 +117,10 @@ m3_status m3_prefill_workspace_size(const m3_dims* dims, size_t* bytes);
  * chunk:     the block size of the chunked form.  The result does not depend on it
  *            beyond rounding; the matrix-core kernels (bf16 io, N = 128, P = 64,
  *            R in {1, 2, 4}, chunk 32 or 64) use it as given, the fp32 vector
- *            kernels split a chunk whose arrays exceed LDS into halves (quarters, ..).
+ *            kernels split a chunk whose arrays exceed LDS into halves (quarters, ..),
+ *            and small states (N/2 a power of two, N/2 * P <= 256, no fused B/C
+ *            norm, bias, gate or output norm) are scanned token by token, without
+ *            chunks.
  */
 m3_status m3_prefill_chunked(const m3_dims* dims, const void* x, const float* dt,
                              const float* A, const float* lambda, const float* theta,
@@ -275,11 +278,16 @@ typedef struct {
     float* dx_last;  /* (batch, H, R, P): of state_in->x_last (zero without a carry) */
 } m3_grads;
 
-/* Bytes of device workspace m3_backward needs for these dims (may be large: the
- * state of every (b, h) after every third token, N * P * 4 bytes each, plus,
- * when H > G, per-head copies of the group-shared gradients, plus, when the
- * sequences are split (m3_backward_parts), two N * P states per piece).
- * Errors: M3_ERR_INVALID_ARG for bad dims or a NULL `bytes`;
+/* Bytes of device workspace m3_backward needs for these dims: checkpointed states
+ * (N * P * 4 bytes each) of every (b, h) -- one after every third token while
+ * those fit in a budget of 4 GiB, else two levels of about sqrt(L / 3) states
+ * each (one after every group of segments, and one group's states recomputed into
+ * a scratch), for one more forward pass -- plus, when H > G, per-head copies of
+ * the group-shared gradients, plus, when the sequences are split
+ * (m3_backward_parts), two N * P states per piece.  The environment variable
+ * M3_BACKWARD_CHECKPOINT_BYTES, read at each call, replaces the budget (a
+ * caller short of memory lowers it); the gradients are the same bits for any
+ * budget.  Errors: M3_ERR_INVALID_ARG for bad dims or a NULL `bytes`;
  * M3_ERR_UNSUPPORTED for shapes m3_backward does not handle. */
 m3_status m3_backward_workspace_size(const m3_dims* dims, size_t* bytes);
 

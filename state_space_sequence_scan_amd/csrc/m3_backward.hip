@@ -9,13 +9,19 @@
 //   dU_t = gamma_t g_t + beta_{t+1} q_{t+1}           (U_t = B_t X_t feeds h_t and h_{t+1})
 // and every input gradient is a contraction of g_t, q_t, dU_t with the forward
 // quantities (see m3_backward below).  The adjoint needs h_{t-1} and h_t at
-// every step; they are not stored per token.  A forward sweep keeps h after
-// every KS-th token in a workspace (checkpoints); the reverse sweep takes the
-// segments of KS tokens last to first, recomputes the segment's states into LDS
-// from the previous checkpoint, and walks them backwards.  The inputs of a
-// segment's tokens (and of the token before it) are staged into LDS once per
-// segment by the whole workgroup in 16-byte units, so the per-token steps read
-// their operands from LDS, not from global memory.
+// every step; they are not stored per token.  The reverse sweep takes segments of
+// KS tokens last to first, recomputes each segment's states into LDS from the state
+// before it, and walks them backwards.  The states before the segments come from
+// checkpoints in two levels: a forward sweep keeps h after every group of `grp`
+// segments in the workspace, and before a group is reversed the states after each
+// of its segments are recomputed from the group's checkpoint into a per-workgroup
+// scratch.  With grp = 1 (whenever a checkpoint after every segment fits the
+// workspace budget) there is no second level; otherwise grp is about the square root
+// of the segments of a part, which keeps the workspace near 2 sqrt(L / KS) states per
+// (b, h) for one more forward pass.  The inputs of a segment's tokens (and of the
+// token before it) are staged into LDS once per segment by the whole workgroup in
+// 16-byte units, so the per-token steps read their operands from LDS, not from
+// global memory.
 //
 // Sequence split.  Both recurrences are linear: over a piece of the sequence the
 // state maps as h_end = e^{sum dt A} R(sum theta) h_start + (the piece's own end
@@ -35,6 +41,9 @@
 // barrier per token.  Gradients of inputs shared by the heads of a group (B, C,
 // theta, the carried B) are written per head and summed by a second kernel in a
 // fixed order, so results do not depend on scheduling.  All gradients are fp32.
+#include <cmath>
+#include <cstdlib>
+
 #include "m3_common.h"
 #include "m3_internal.h"
 
@@ -117,12 +126,13 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
     const int H = a.H, G = a.G;
     const float Ah = a.At ? 0.f : a.A[h], Dh = a.D[h];   // Ah: the head's decay rate without At
     const int64_t nseg = (L + KS - 1) / KS;                    // segments of this sequence
-    const int64_t nseg_max = (a.L + KS - 1) / KS;              // checkpoint slots per (b, h)
     const int64_t s_lo = part * a.seg_per_part;
     const int64_t s_hi = s_lo + a.seg_per_part < nseg ? s_lo + a.seg_per_part : nseg;   // segments of this part
     const bool split = a.parts > 1;
     const size_t pidx = static_cast<size_t>(bh) * a.parts + part;
-    float* ck = a.ckpt + static_cast<size_t>(bh) * nseg_max * N * P;
+    const int64_t grp = a.grp, gpp = (a.seg_per_part + grp - 1) / grp;   // groups per part
+    float* ck = a.ckpt + pidx * gpp * N * P;         // state after group u of this part: ck[u]
+    float* scr = a.scratch + pidx * grp * N * P;     // state after segment i of the group being reversed
     const bool carry = a.bl && a.xl;
     const T* x = static_cast<const T*>(a.x);
     const T* dy = static_cast<const T*>(a.dy);
@@ -332,20 +342,32 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
         return;
     }
 
-    // ---- forward sweep: checkpoint after the last token of every segment.  A part
-    // after the first starts from the state the combine pass left for it.
+    // ---- forward sweep: checkpoint after the last segment of every group (the last group's
+    // end is never a starting point).  A part after the first starts from the state the
+    // combine pass left for it.
     float hc[4][4];
-    if (split) load_state(hc, a.hloc + pidx * N * P, P);
-    else initial_state(hc);
-    for (int64_t s = s_lo; s < s_hi; ++s) {
-        const int64_t t0 = s * KS;
-        const int len = static_cast<int>(L - t0 < KS ? L - t0 : KS);
-        __syncthreads();   // the previous segment's slots are read
-        stage(t0, len, false);
-        __syncthreads();
-        for (int j = 1; j <= len; ++j) fwd_step(j, hc);
-        store_state(hc, ck + s * N * P, P);
-    }
+    auto part_start = [&](float (&hs)[4][4]) {
+        if (split) load_state(hs, a.hloc + pidx * N * P, P);
+        else initial_state(hs);
+    };
+    part_start(hc);
+    // forward steps of segments s0 .. s1-1 on hs; with `dst`, the state after segment s is
+    // stored at dst[(s - s0 - 1 + off) ...] as described at the call
+    auto sweep = [&](float (&hs)[4][4], int64_t s0, int64_t s1, auto&& after) {
+        for (int64_t s = s0; s < s1; ++s) {
+            const int64_t t0 = s * KS;
+            const int len = static_cast<int>(L - t0 < KS ? L - t0 : KS);
+            __syncthreads();   // the previous segment's slots are read
+            stage(t0, len, false);
+            __syncthreads();
+            for (int j = 1; j <= len; ++j) fwd_step(j, hs);
+            after(s, hs);
+        }
+    };
+    sweep(hc, s_lo, s_hi, [&](int64_t s, const float (&hs)[4][4]) {
+        const int64_t i = s - s_lo;
+        if (i % grp == grp - 1 && s + 1 < s_hi) store_state(hs, ck + (i / grp) * N * P, P);
+    });
 
     // ---- reverse sweep.  q_{t+1}, alpha_{t+1}, beta_{t+1} belong to the token after; the
     // final-state cotangent enters as a token after the last one with alpha = 1, beta = 0 and
@@ -370,7 +392,19 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
     }
     float dA_acc = 0.f, dD_acc = 0.f;   // thread 0
 
-    for (int64_t s = s_hi - 1; s >= s_lo; --s) {
+    const int64_t ngrp = (s_hi - s_lo + grp - 1) / grp;
+    for (int64_t u = ngrp - 1; u >= 0; --u) {
+    const int64_t g_lo = s_lo + u * grp, g_hi = g_lo + grp < s_hi ? g_lo + grp : s_hi;
+    auto group_start = [&](float (&hs)[4][4]) {
+        if (u > 0) load_state(hs, ck + (u - 1) * N * P, P);
+        else part_start(hs);
+    };
+    if (g_hi - g_lo > 1) {   // the states after segments g_lo .. g_hi-2, into the scratch
+        float hg[4][4];
+        group_start(hg);
+        sweep(hg, g_lo, g_hi - 1, [&](int64_t s, const float (&hs)[4][4]) { store_state(hs, scr + (s - g_lo) * N * P, P); });
+    }
+    for (int64_t s = g_hi - 1; s >= g_lo; --s) {
         const int64_t t0 = s * KS;
         const int len = static_cast<int>(L - t0 < KS ? L - t0 : KS);
         __syncthreads();   // the previous segment's readers are done with sH and the slots
@@ -378,9 +412,8 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
         __syncthreads();
         {   // recompute h_{t0-1} .. h_{t0+len-2} into LDS
             float hr[4][4];
-            if (s > s_lo) load_state(hr, ck + (s - 1) * N * P, P);
-            else if (split) load_state(hr, a.hloc + pidx * N * P, P);
-            else initial_state(hr);
+            if (s > g_lo) load_state(hr, scr + (s - 1 - g_lo) * N * P, P);
+            else group_start(hr);
             store_state(hr, sH[0], PS);
             for (int j = 1; j < len; ++j) {
                 fwd_step(j, hr);
@@ -551,6 +584,7 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
             an = al;
             bn = be;
         }
+    }
     }
 
     // ---- h_0 and the carried previous input (dU_0 = beta_1 q_1): the first part only
@@ -775,18 +809,37 @@ void backward_parts(const BwdShape& s, int* parts, int64_t* seg_per_part) {
     *seg_per_part = best_per;
 }
 
-// Workspace: checkpoints (batch, H, nseg, N, P) fp32; per-head partials of the
-// group-shared gradients when H > G; dA/dD per (batch, head, part); with a split,
-// each part's local state and adjoint (N, P) and its decay and angle sums.
+// Segments per checkpoint group: 1 while a checkpoint after every segment fits the
+// budget (4 GiB, or the byte count in the environment variable
+// M3_BACKWARD_CHECKPOINT_BYTES), else the square root of the segments of a part
+// (rounded up), which minimises checkpoints plus scratch (groups per part + segments
+// per group states).  The grouping changes where states are kept, not how they are
+// computed: the gradients are the same bits for every group size.
+static int64_t checkpoint_group(const BwdShape& s, int parts, int64_t seg_per_part) {
+    double budget = 4.0 * (1ull << 30);
+    if (const char* e = std::getenv("M3_BACKWARD_CHECKPOINT_BYTES")) budget = std::strtod(e, nullptr);
+    const double one_level = static_cast<double>(s.batch) * s.H * parts * seg_per_part * s.N * s.P * 4;
+    if (one_level <= budget) return 1;
+    int64_t g = static_cast<int64_t>(std::ceil(std::sqrt(static_cast<double>(seg_per_part))));
+    return g < 1 ? 1 : g;
+}
+
+// Workspace: checkpoints (batch, H, parts, groups per part, N, P) fp32 and, with groups of
+// more than one segment, a scratch of one group's states per (batch, head, part); per-head
+// partials of the group-shared gradients when H > G; dA/dD per (batch, head, part); with a
+// split, each part's local state and adjoint (N, P) and its decay and angle sums.
 BwdLayout backward_layout(const BwdShape& s) {
     BwdLayout l{};
     auto al = [](size_t v) { return (v + 255) & ~static_cast<size_t>(255); };
-    const int64_t nseg = (s.L + bw::KS - 1) / bw::KS;
     backward_parts(s, &l.parts, &l.seg_per_part);
+    l.grp = checkpoint_group(s, l.parts, l.seg_per_part);
     const size_t units = static_cast<size_t>(s.batch) * s.H * l.parts;
+    const size_t gpp = static_cast<size_t>((l.seg_per_part + l.grp - 1) / l.grp);
     size_t off = 0;
     l.ckpt = off;
-    off += al(static_cast<size_t>(s.batch) * s.H * nseg * s.N * s.P * 4);
+    off += al(units * gpp * s.N * s.P * 4);
+    l.scratch = off;
+    if (l.grp > 1) off += al(units * static_cast<size_t>(l.grp) * s.N * s.P * 4);
     l.per_head = s.H != s.G;
     if (l.per_head) {
         l.dB_part = off;
@@ -834,6 +887,8 @@ void launch_scan(const BwdArgs& a, dim3 grid, hipStream_t st) {
 hipError_t launch_backward(BwdArgs a, const BwdLayout& l, hipStream_t st) {
     uint8_t* ws = static_cast<uint8_t*>(a.workspace);
     a.ckpt = reinterpret_cast<float*>(ws + l.ckpt);
+    a.scratch = reinterpret_cast<float*>(ws + l.scratch);
+    a.grp = l.grp;
     a.per_head = l.per_head;
     if (l.per_head) {
         a.dB_part = reinterpret_cast<float*>(ws + l.dB_part);

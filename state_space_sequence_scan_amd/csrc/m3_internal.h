@@ -119,10 +119,11 @@ struct BwdShape {
     int H, G, N, P, R;
 };
 struct BwdLayout {            // byte offsets into the workspace
-    size_t ckpt, dB_part, dC_part, dtheta_part, dbl_part, dA_part, dD_part, hloc, qloc, dec, ang, bytes;
+    size_t ckpt, scratch, dB_part, dC_part, dtheta_part, dbl_part, dA_part, dD_part, hloc, qloc, dec, ang, bytes;
     bool per_head;            // H > G: group-shared gradients are written per head, then summed
     int parts;                // S: the sequence of each (b, h) is split into S parts (1: no split)
     int64_t seg_per_part;     // recompute segments per part (the last part may hold fewer)
+    int64_t grp;              // segments per checkpoint group (1: a checkpoint after every segment)
 };
 // Number of parts the backward splits each sequence into, and the segments of
 // each part: chosen from the shape alone so that results depend on nothing else.
@@ -155,7 +156,8 @@ struct BwdArgs {
     float* dxl;               // may be null
     void* workspace;
     // filled by launch_backward from the layout
-    float* ckpt;
+    float* ckpt;              // the state after each checkpoint group of each part
+    float* scratch;           // (batch*H, S, grp, N, P): the states inside the group being reversed
     float* dB_part;
     float* dC_part;
     float* dtheta_part;
@@ -167,6 +169,7 @@ struct BwdArgs {
     double* dec;              // (batch*H, S): sum of dt*A over each part's tokens
     float* ang;               // (batch*H, S, N/2): sum of theta over each part's tokens, mod 2 pi
     int64_t seg_per_part;
+    int64_t grp;              // segments per checkpoint group
     int64_t batch, L;         // L: the length, or with cu an upper bound on every sequence's length
     const int64_t* cu;        // packed sequence starts (batch + 1, device) or null
     int64_t T;                // tokens of the packed arrays (with cu)

@@ -126,3 +126,45 @@ def test_cases_cover_split_and_whole_sequences():
     assert any(p > 1 and t > 3 for _, (p, t) in plans)
     assert any(p > 1 and c[6] for c, (p, t) in plans)
     assert any(p == 1 and c[1] > 3 for c, (p, t) in plans)
+
+
+def _grads(d, dy, dh=None, st=None):
+    g = m3scan.backward(*[d[k] for k in NAMES], dy, dh_out=dh, state_in=st)
+    torch.cuda.synchronize()
+    return g
+
+
+@pytest.mark.parametrize("case", [
+    (4, 200, 24, 1, 2, "bf16", False, True),    # split into pieces
+    (2, 150, 4, 2, 4, "fp32", True, True),      # split, carried state, final cotangent
+    (8, 40, 32, 8, 1, "bf16", True, False),     # whole sequences
+    (1, 100, 4, 1, 4, "fp32", True, True),      # groups of 6 segments, the last one of 4
+], ids=_id)
+def test_checkpoint_groups_give_the_same_bits(case, monkeypatch):
+    """With a checkpoint budget too small for one state per segment, the states inside each
+    group of segments are recomputed from the group's checkpoint: the same forward steps in
+    the same order, so every gradient is bit-identical to the one-level run."""
+    b, L, H, G, R, io, ws, wd = case
+    d = draw(b, L, H, G, 64, 128, R, io, 2.0, seed=L + 5)
+    gen = torch.Generator(device="cpu").manual_seed(L)
+    tdt = torch.bfloat16 if io == "bf16" else torch.float32
+    dy = torch.randn((b, L, H, R, 64), generator=gen).to(tdt).cuda()
+    dh = torch.randn((b, H, 128, 64), generator=gen).cuda() if wd else None
+    st = None
+    if ws:
+        st = m3scan.DecodeState(torch.randn((b, H, 128, 64), generator=gen).cuda(),
+                                torch.randn((b, G, R, 128), generator=gen).to(tdt).cuda(),
+                                torch.randn((b, H, R, 64), generator=gen).to(tdt).cuda())
+    dims = m3scan.make_dims(b, L, H, G, 64, 128, R, 1, 0)
+    monkeypatch.delenv("M3_BACKWARD_CHECKPOINT_BYTES", raising=False)
+    ws1 = m3scan.backward_workspace_size(dims)
+    g1 = _grads(d, dy, dh, st)
+    monkeypatch.setenv("M3_BACKWARD_CHECKPOINT_BYTES", "1")
+    ws2 = m3scan.backward_workspace_size(dims)
+    g2 = _grads(d, dy, dh, st)
+    parts, tpp = m3scan.backward_parts(dims)
+    say(f"checkpoint groups {_id(case)}: {parts} pieces of {tpp} tokens, workspace {ws1} -> {ws2} bytes")
+    if parts == 1:   # one piece of L/3 segments: sqrt-sized groups hold fewer states
+        assert ws2 < ws1
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), k

@@ -113,3 +113,30 @@ def test_backward_varlen_equal_lengths_match_uniform_batch():
     torch.cuda.synchronize()
     for k in g1:
         assert torch.equal(g1[k].reshape(g2[k].shape), g2[k]), k
+
+
+@pytest.mark.parametrize("case", CASES, ids=_id)
+def test_backward_varlen_checkpoint_groups_give_the_same_bits(case, monkeypatch):
+    """Checkpoint groups (forced by a one-byte budget) in a packed batch: short sequences end
+    inside or before a group; every gradient is bit-identical to the one-level run."""
+    lengths, H, G, R, io, with_state, with_dh = case
+    ns, Lmax = len(lengths), max(lengths)
+    d, cu, T = _pack(lengths, H, G, R, io, seed=sum(lengths) + 2 * R)
+    tdt = torch.bfloat16 if io == "bf16" else torch.float32
+    gen = torch.Generator(device="cpu").manual_seed(T + 9)
+    dy = torch.randn((T, H, R, P), generator=gen).to(tdt).cuda()
+    dh = torch.randn((ns, H, N, P), generator=gen).cuda() if with_dh else None
+    st = None
+    if with_state:
+        st = m3scan.DecodeState(torch.randn((ns, H, N, P), generator=gen).cuda(),
+                                torch.randn((ns, G, R, N), generator=gen).to(tdt).cuda(),
+                                torch.randn((ns, H, R, P), generator=gen).to(tdt).cuda())
+    monkeypatch.delenv("M3_BACKWARD_CHECKPOINT_BYTES", raising=False)
+    g1 = m3scan.backward_varlen(*[d[k] for k in NAMES], dy, cu, Lmax, dh_out=dh, state_in=st)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("M3_BACKWARD_CHECKPOINT_BYTES", "1")
+    g2 = m3scan.backward_varlen(*[d[k] for k in NAMES], dy, cu, Lmax, dh_out=dh, state_in=st)
+    torch.cuda.synchronize()
+    say("backward varlen checkpoint groups", _id(case))
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), k
