@@ -228,7 +228,7 @@ def mfma_util_rocprof(workload):
         if rec.get("source_sha") != source_sha(*rec["source_files"]):
             return None
         kernels = rec["workloads"][workload]["kernels"]
-        full = next(v for k, v in kernels.items() if k.endswith("true, false>"))   # the output pass, no gate
+        full = next(v for k, v in kernels.items() if k.endswith("true, false, false>"))   # output pass, no gate or norm
         return round(full["mfma_util_percent"] / 100.0, 4)
     except Exception:
         return None
@@ -388,8 +388,8 @@ def main():
     else:
         traffic = pmc_traffic(f"prefill_{args.workload}{'_varlen' if args.varlen else ''}"
                               f"{'_fused' if args.fused else ''}_hbm_counters.json",
-                              ["m3_prefill_mfma.hip", "m3_common.h"], pre_bytes)
-        roof = {"kernel": "prefill (chunked scan)", "bound": "hbm",
+                              ["m3_prefill_mfma.hip", "m3_mfma_common.h", "m3_common.h"], pre_bytes)
+        roof = {"kernel": "prefill (all kernels of one call)", "bound": "hbm",
                 "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(pre_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "alg_bytes_per_launch": pre_bytes, "avg_launch_us": round(pre_avg * 1e3, 2),
