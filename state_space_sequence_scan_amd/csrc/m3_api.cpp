@@ -67,9 +67,10 @@ bool copy_fusion(const m3_dims* d, const m3_fusion* f, m3::Fusion* out) {
 
 namespace m3 {
 
-// Every plan reserves, after the path's own workspace, room for a copy of the
-// carried-in B (batch, G, R, N) in the io dtype: a fused call normalises it there.
+// A fused call with a B/C norm or bias reserves, after the path's own workspace, room
+// for a copy of the carried-in B (batch, G, R, N) in the io dtype: it normalises it there.
 static void add_carry_room(const PrefillArgs& a, PrefillPlan* p) {
+    if (!a.fu.bc()) return;   // only a fused norm or bias rewrites the carried B
     const size_t al = (p->workspace + 255) & ~static_cast<size_t>(255);
     p->carry_off = al;
     p->workspace = al + static_cast<size_t>(a.batch) * a.G * a.R * a.N * (a.bf16 ? 2 : 4);

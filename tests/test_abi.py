@@ -122,10 +122,14 @@ def test_prefill_rejects_unsupported(lib):
 def test_fp32_chunks_larger_than_lds_are_split(lib, R, Q):
     """fp32 io at the 1.5B head shape (N=128, P=64): chunks whose arrays exceed LDS run as
     smaller blocks instead of being refused (the chunked result does not depend on the block
-    size beyond rounding); only the carry room is asked for as workspace."""
+    size beyond rounding); no workspace is asked for, except by a fused call with a B norm
+    or bias, which normalises the carried B into it."""
     d = m3scan.make_dims(2, 300, 4, 1, 64, 128, R, Q, m3scan.M3_F32)
-    n = ctypes.c_size_t(0)
+    n = ctypes.c_size_t(1)
     assert lib.m3_prefill_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    assert n.value == 0
+    fu = m3scan.Fusion(None, 0x1000, None, None, None, None, 1e-6, None, 0)   # a B norm weight
+    assert lib.m3_prefill_fused_workspace_size(ctypes.byref(d), ctypes.byref(fu), ctypes.byref(n)) == 0
     assert n.value == 2 * 1 * R * 128 * 4   # batch x G x R x N fp32: the normalised carried B
 
 
@@ -239,8 +243,10 @@ def test_fused_entry_points_reject_bad_arguments(lib):
                                     None) == -1, kw
     assert lib.m3_prefill_fused(ctypes.byref(d), *([FAKE] * 7 + [None]), ctypes.byref(fu), None, None, FAKE,
                                 None, 0, None) == -1
-    # the workspace reserves room for the normalised carry: none given is too small
-    assert lib.m3_prefill_fused(ctypes.byref(d), *[FAKE] * 8, ctypes.byref(fu), None, None, FAKE, None, 0,
+    # with a norm weight the workspace reserves room for the normalised carry: none given is
+    # too small
+    fn = m3scan.Fusion(None, 0x1000, None, None, None, None, 1e-6, None, 0)
+    assert lib.m3_prefill_fused(ctypes.byref(d), *[FAKE] * 8, ctypes.byref(fn), None, None, FAKE, None, 0,
                                 None) == -3
     # an output-norm weight with a non-positive epsilon
     bad = m3scan.Fusion(None, None, None, None, None, None, 0.0, 0x1000, 0)
@@ -377,3 +383,56 @@ def test_noalloc_refuses_shapes_beyond_its_scratch(lib):
     bad = _dims(ngroups=3)
     assert lib.m3_prefill_chunked_noalloc(ctypes.byref(bad), *null8, None, None, None, None) == -1
     assert lib.m3_prefill_chunked_noalloc(None, *null8, None, None, None, None) == -1
+
+
+def _bwd_ws(lib, d):
+    n = ctypes.c_size_t(0)
+    assert lib.m3_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    return n.value
+
+
+def test_backward_checkpoint_budget(lib, monkeypatch):
+    """Checkpoints stay one per 3-token segment while they fit the budget (4 GiB by default,
+    or M3_BACKWARD_CHECKPOINT_BYTES); above it the workspace holds about 2 sqrt(L/3) states
+    per (b, h) instead of L/3 -- checked against the sizes that layout implies."""
+    P, N, state = 64, 128, 64 * 128 * 4
+    monkeypatch.delenv("M3_BACKWARD_CHECKPOINT_BYTES", raising=False)
+    # nanomamba3-shaped: 2.15 GB of checkpoints, under the budget: one level
+    d = _dims(batch=4, nheads=24, ngroups=1, headdim=P, dstate=N, rank=2, seqlen=2048)
+    parts, tpp = m3scan.backward_parts(d)
+    one = _bwd_ws(lib, d)
+    assert one >= 4 * 24 * parts * (tpp // 3) * state
+    # a budget below that: groups of ceil(sqrt(segments per piece)) segments
+    monkeypatch.setenv("M3_BACKWARD_CHECKPOINT_BYTES", str(1 << 20))
+    two = _bwd_ws(lib, d)
+    segs = tpp // 3
+    g = -(-segs // 1)
+    import math
+    g = math.ceil(math.sqrt(segs))
+    ck_one = 4 * 24 * parts * segs * state
+    ck_two = 4 * 24 * parts * (-(-segs // g) + g) * state
+    assert one - two == ck_one - ck_two, (one, two, ck_one, ck_two)
+    # the 1.5B SISO layer (44.8 GB of one-level checkpoints) is grouped by default
+    monkeypatch.delenv("M3_BACKWARD_CHECKPOINT_BYTES")
+    d = _dims(batch=8, nheads=64, ngroups=1, headdim=P, dstate=N, rank=1, seqlen=8192)
+    assert m3scan.backward_parts(d) == (1, 8192)
+    segs = -(-8192 // 3)
+    g = math.ceil(math.sqrt(segs))
+    ws = _bwd_ws(lib, d)
+    partials = 8 * 8192 * 64 * (2 * 1 * N + N // 2) * 4 + 8 * 64 * 1 * N * 4
+    assert ws < 8 * 64 * segs * state
+    assert ws >= 8 * 64 * (-(-segs // g) + g) * state + partials
+    # a budget above it restores one level
+    monkeypatch.setenv("M3_BACKWARD_CHECKPOINT_BYTES", str(64 << 30))
+    assert _bwd_ws(lib, d) >= 8 * 64 * segs * state
+
+
+def test_serial_prefill_needs_no_workspace(lib):
+    """Small states are scanned token by token: no workspace (the chunked paths need one
+    only for their prepared operands and segment states)."""
+    n = ctypes.c_size_t(1)
+    for N, P, R, io in [(16, 16, 1, m3scan.M3_F32), (2, 4, 6, m3scan.M3_F32), (32, 16, 4, m3scan.M3_BF16),
+                        (128, 2, 8, m3scan.M3_F32)]:
+        d = m3scan.make_dims(2, 300, 4, 2, P, N, R, 32, io)
+        assert lib.m3_prefill_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+        assert n.value == 0, (N, P, R)
