@@ -42,8 +42,12 @@
  * The library never allocates, frees or synchronises; all work is enqueued on
  * `stream` (a hipStream_t; NULL = the null stream) and the call returns at once.
  * There is no global mutable state (except the static scratch array of
- * m3_prefill_chunked_noalloc, see there): calls on different streams may run
- * from different threads.  Outputs must not alias inputs unless stated.
+ * m3_prefill_chunked_noalloc, see there, and a mutex-guarded host-side record of
+ * the kernels whose LDS limit has been raised on each device): calls on different
+ * streams may run from different threads.  Outputs must not alias inputs unless
+ * stated.  After a first call of a given shape on a device, a call enqueues kernel
+ * launches only (no allocation, memset, synchronisation or attribute change), so it
+ * can be captured in a HIP graph.
  *
  * Errors: argument and shape errors are returned before anything is launched.
  * Launch failures return M3_ERR_HIP.  Faults inside a kernel surface at the

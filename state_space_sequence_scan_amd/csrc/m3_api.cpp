@@ -4,7 +4,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "m3_internal.h"
 
@@ -66,6 +68,22 @@ bool copy_fusion(const m3_dims* d, const m3_fusion* f, m3::Fusion* out) {
 }  // namespace
 
 namespace m3 {
+
+hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes) {
+    if (bytes <= 64 * 1024) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    static std::mutex mu;
+    static std::map<std::pair<int, const void*>, size_t> raised;   // (device, kernel) -> limit set
+    std::lock_guard<std::mutex> lock(mu);
+    size_t& cur = raised[{dev, kernel}];
+    if (bytes <= cur) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+    if (e == hipSuccess) cur = bytes;
+    return e;
+}
+
 
 // A fused call with a B/C norm or bias reserves, after the path's own workspace, room
 // for a copy of the carried-in B (batch, G, R, N) in the io dtype: it normalises it there.

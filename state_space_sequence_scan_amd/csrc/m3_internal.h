@@ -9,6 +9,13 @@ namespace m3 {
 
 constexpr int kMaxRankGeneric = 8;
 
+// Lets `kernel` launch with `bytes` of dynamic LDS on the current device: raises its limit
+// with hipFuncSetAttribute the first time a size above 64 KB (or above what was set before)
+// is asked for on a device, and does nothing on later calls, so that launches after the
+// first enqueue nothing but the kernel (a caller may capture them in a graph).  In
+// m3_api.cpp.
+hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes);
+
 // Fused prologue/epilogue of a Mamba-3 layer around the scan (all optional):
 // per-token decay rates, RMSNorm and bias of B and C before the rotation, and the
 // output gate y * silu(z).

@@ -417,12 +417,8 @@ static hipError_t launch_generic_t(const PrefillArgs& a, hipStream_t st) {
     // resident mode when the sequence's inputs fit in LDS beside the chunk arrays
     const bool resident = generic_lds_bytes(a) + resident_lds_bytes(a) <= 160 * 1024;
     const size_t shm = generic_lds_bytes(a) + (resident ? resident_lds_bytes(a) : 0);
-    if (shm > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_generic<T>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 static_cast<int>(shm));
-        if (e != hipSuccess) return e;
-    }
+    const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&prefill_generic<T>), shm);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(prefill_generic<T>, dim3(static_cast<unsigned>(a.batch * a.H)), dim3(kThreads), shm,
                        st, static_cast<const T*>(a.x), a.dt, a.A, a.lam, a.theta,
                        static_cast<const T*>(a.B), static_cast<const T*>(a.C), a.D, a.h_in,

@@ -328,11 +328,8 @@ static hipError_t launch_serial_t(const PrefillArgs& a, hipStream_t st) {
         default: return hipErrorInvalidValue;
     }
     const size_t shm = serial_lds_bytes(a);
-    if (shm > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm));
-        if (e != hipSuccess) return e;
-    }
+    const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kernel), shm);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(a.batch * a.H)), dim3(serial_threads(a)), shm, st, q);
     return hipGetLastError();
 }

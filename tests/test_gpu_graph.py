@@ -1,9 +1,10 @@
 """HIP graph capture of the scan (torch.cuda.graph, which captures the stream the binding
 launches on): a prefill through the allocation-free entry point followed by decode steps
-continuing it, captured once and replayed several times with new inputs copied into the
-captured buffers between replays, with eager work and synchronisations in between.  Every
-replay must give the bits of an eager run of the same calls on the same inputs: the path
-records kernel launches only (no allocation, memset or host synchronisation inside)."""
+continuing it, on each prefill kernel family, captured once after an eager warm-up call and
+replayed several times with new inputs copied into the captured buffers between replays,
+with eager work and synchronisations in between.  Every replay must give the bits of an
+eager run of the same calls on the same inputs: after a first call the path records kernel
+launches only (no allocation, memset, host synchronisation or attribute change)."""
 import pytest
 import torch
 
@@ -41,11 +42,23 @@ def _buffers(pre, toks, state_dtype):
     return y, st, ydec
 
 
-@pytest.mark.parametrize("state_dtype", [torch.float32, torch.bfloat16], ids=["fp32-state", "bf16-state"])
-def test_graph_replays_match_eager(state_dtype):
-    b, L, H, G, P, N, R, Q, steps = 2, 200, 4, 1, 64, 128, 2, 32, 3
-    say("graph capture", L, steps, state_dtype)
-    pre, toks = _split(draw(b, L + steps, H, G, P, N, R, "bf16", 1.0, seed=77), L, steps)
+# (b, L, H, G, P, N, R, Q, io, state dtype): the matrix-core prefill with an fp32 and a bf16
+# state, the token-serial fp32 prefill (66.5 KB of LDS: its limit is raised by the warm-up
+# call, before the capture) and the chunked fp32 prefill
+CASES = [
+    (2, 200, 4, 1, 64, 128, 2, 32, "bf16", torch.float32),
+    (2, 200, 4, 1, 64, 128, 2, 32, "bf16", torch.bfloat16),
+    (1, 256, 4, 1, 16, 16, 1, 32, "fp32", torch.float32),
+    (2, 100, 4, 2, 32, 32, 2, 16, "fp32", torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "P{}N{}R{}-{}-{}".format(c[4], c[5], c[6], c[8], str(c[9])[6:]))
+def test_graph_replays_match_eager(case):
+    b, L, H, G, P, N, R, Q, io, state_dtype = case
+    steps = 3
+    say("graph capture", case)
+    pre, toks = _split(draw(b, L + steps, H, G, P, N, R, io, 1.0, seed=77), L, steps)
     y, st, ydec = _buffers(pre, toks, state_dtype)
 
     # warm-up on a side stream (the binding and kernels loaded before capture)
@@ -63,7 +76,7 @@ def test_graph_replays_match_eager(state_dtype):
     torch.cuda.synchronize()
 
     for rep in range(3):
-        new_pre, new_toks = _split(draw(b, L + steps, H, G, P, N, R, "bf16", 1.0, seed=100 + rep), L, steps)
+        new_pre, new_toks = _split(draw(b, L + steps, H, G, P, N, R, io, 1.0, seed=100 + rep), L, steps)
         for k in NAMES:   # new inputs into the captured buffers (eager copies)
             pre[k].copy_(new_pre[k])
             for t in range(steps):
