@@ -116,7 +116,11 @@ def intra_chunk_counters(name):
             rec = json.load(f)
         if rec.get("source_sha") != source_sha(*rec["source_files"]):
             return None
-        return rec["workloads"][name]
+        k = next(iter(rec["workloads"][name]["kernels"].values()))
+        return {"mfma_busy_rocprof": round(k["mfma_util_percent"] / 100.0, 4),
+                "executed_frac_of_peak": round(k["executed_frac_of_peak"], 4),
+                "executed_over_useful": round(k["executed_over_useful"], 3),
+                "source": "profiles/intra_chunk_mfma_counters.json"}
     except Exception:
         return None
 
