@@ -7,13 +7,12 @@
 // exponential-trapezoidal step of the Mamba-3 paper note, "Solution 1", with the
 // rotation of "Solution 2" and the rank-R input/read-out of "Solution 3").
 //
-// The step reads and writes the whole fp32 state and does little arithmetic per
-// byte: it is bound by HBM bandwidth.  The kernels stream each (b, h) state slice
-// once with 16-byte non-temporal loads and stores and keep every rotation pair
-// (2k, 2k+1) inside one thread.  decode_stream (N = 128, P = 64) keeps the R x P
-// read-out reduction inside each wave; decode_fast (small N) reduces across
-// waves through LDS; decode_generic handles any other shape.
-#include <algorithm>
+// The step reads and writes the whole state (fp32 or bf16) and does little arithmetic
+// per byte: it is bound by HBM bandwidth.  decode_fast (N = 128, P = 64 at R = 1, 2, 4,
+// and N = P = 16 at R = 1) streams each (b, h) state slice once with non-temporal loads
+// and stores, keeps every rotation pair (2k, 2k+1) inside one thread, and reduces the
+// R x P read-out across lanes and then across waves through LDS; decode_generic handles
+// any other shape.
 #include <type_traits>
 
 #include "m3_common.h"
