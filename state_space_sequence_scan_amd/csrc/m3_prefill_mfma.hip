@@ -13,8 +13,9 @@
 //              token-major ([Q*R][N]), and cos/sin of the chunk's total angle
 //              phi_end.  B, C and theta are shared by the H/G heads of a group, so
 //              this work is done once per group, not once per head.
-//  scan_mfma   one workgroup per (b, h, segment of chunks), one wave per 16-row
-//              block of the chunk (at least 4).  The N x P state lives in MFMA
+//  scan_mfma   one workgroup per (b, h, segment of chunks), 4 waves up to 64 rows
+//              per chunk (Q * R), one or two 16-row blocks of the chunk per wave
+//              (8 waves at 256 rows).  The N x P state lives in MFMA
 //              accumulators, split over the waves in 16 x 16 tiles.  Per chunk:
 //                Y      = diag(e^cum) Ct S  +  (M o Ct Bt^T) X  +  D X
 //                S     <- R(phi_end) [ e^{cum_end} S  +  Bt^T diag(s) X ]
@@ -168,10 +169,24 @@ __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
 // ------------------------------------------------------------------------------------
 // GATE: the output gate is applied (its input rows are loaded well before the store).
 // ONORM: the output RMSNorm follows (after the gate), each output row over its P values.
+//
+// A chunk of 128 rows (R = 4 at Q = 32, R = 2 at Q = 64) runs on 4 waves, two row blocks
+// each, and keeps no s X tile: the state contraction scales the Bt^T fragments by s
+// instead.  That brings the output pass to 72 KB of LDS, and with at most 256 registers
+// per lane two workgroups share a CU, so one workgroup's loads, barriers and state
+// update overlap the other's matrix work (measured 14% faster than one 8-wave
+// workgroup per CU).
+template <int R, int Q>
+constexpr bool kTwoPerCu = (Q * R == 128);
+template <int R, int Q, bool FULL>
+constexpr int kWavesPerSimd = (FULL && kTwoPerCu<R, Q>) ? 2 : 1;
+
 template <int R, int Q, int NW, bool FULL, bool GATE, bool ONORM>
-__global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<R, Q, FULL>)))
+void scan_mfma(ScanParams p) {
     constexpr int NTH = 64 * NW;
     constexpr int QR = Q * R;
+    constexpr bool NOXS = FULL && kTwoPerCu<R, Q>;   // state contraction scales Bt^T, reads X
     constexpr int NB = QR / 16;          // 16-row blocks of the chunk
     constexpr int BS = N + 8;            // row stride of sBt and sST
     constexpr int MB = NB > NW ? 2 : 1;  // output row blocks per wave
@@ -187,7 +202,7 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
                       NW % 4 == 0,
                   "tiling");
 
-    __shared__ __align__(16) uint16_t sXs[QR * P];                 // s_j X_j, row-major, swizzled
+    __shared__ __align__(16) uint16_t sXs[NOXS ? 8 : QR * P];      // s_j X_j, row-major, swizzled
     __shared__ __align__(16) uint16_t sX[FULL ? QR * P : 8];       // X, row-major, swizzled
     __shared__ __align__(16) uint16_t sBt[QR * BS];                // Bt token-major
     __shared__ __align__(16) uint16_t sST[FULL ? P * BS : 8];      // S^T (bf16): [p][n]
@@ -227,13 +242,13 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
     const uint32_t aBtRow = lds_addr(&sBt[l16 * BS + 8 * lg]);                          // Bt tiles, A operand
     const uint32_t aBtTr = lds_addr(&sBt[(4 * lg + (l16 >> 2)) * BS + n0 + 4 * (l16 & 3)]);   // Bt^T, transposed
     const uint32_t aBtW = lds_addr(&sBt[(tid >> 4) * BS + 8 * (tid & 15)]);             // Bt staging
-    uint32_t aXTr[4], aXsTr[CT];   // X^T and (sX)^T, transposed: one base per 16-column tile
+    uint32_t aXTr[4], aXsTr[CT];   // X^T and (s X)^T (X^T when NOXS), transposed: one base per 16-column tile
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
         aXTr[ct] = FULL ? lds_addr(&sX[xoff(4 * lg + (l16 >> 2), 16 * ct + 4 * (l16 & 3))]) : 0u;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
-        aXsTr[ct] = lds_addr(&sXs[xoff(4 * lg + (l16 >> 2), p0 + 16 * ct + 4 * (l16 & 3))]);
+        aXsTr[ct] = lds_addr(&(NOXS ? sX : sXs)[xoff(4 * lg + (l16 >> 2), p0 + 16 * ct + 4 * (l16 & 3))]);
     const uint32_t aXW = FULL ? lds_addr(&sX[xoff(tid >> 3, 8 * (tid & 7))]) : 0u;      // X staging
     const uint32_t aXsW = lds_addr(&sXs[xoff(tid >> 3, 8 * (tid & 7))]);               // sX staging
     const uint32_t aST = FULL ? lds_addr(&sST[l16 * BS + 8 * lg]) : 0u;                 // S^T, A operand
@@ -379,14 +394,16 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
         _Pragma("unroll") for (int e = 0; e < XPT; ++e) {                                                     \
             const int u = tid + NTH * e, row = u >> 3;                                                        \
             const int tok = row / R;                                                                          \
-            const float sc = sSc[q_][tok];                                                                    \
             const uint4 xq = (tok < pnq) ? quad(xr, e) : uint4{0u, 0u, 0u, 0u};                               \
             if (FULL) lds_st(aXW + e * (NTH / 8) * P * 2, xq);                                         \
-            const uint32_t wq[4] = {xq.x, xq.y, xq.z, xq.w};                                                  \
-            uint32_t sq[4];                                                                                   \
-            _Pragma("unroll") for (int k = 0; k < 4; ++k)                                                     \
-                sq[k] = pack_bf16x2(bits_to_f(wq[k] & 0xffff) * sc, bits_to_f(wq[k] >> 16) * sc);             \
-            lds_st(aXsW + e * (NTH / 8) * P * 2, uint4{sq[0], sq[1], sq[2], sq[3]});                   \
+            if (!NOXS) {                                                                                      \
+                const float sc = sSc[q_][tok];                                                                \
+                const uint32_t wq[4] = {xq.x, xq.y, xq.z, xq.w};                                              \
+                uint32_t sq[4];                                                                               \
+                _Pragma("unroll") for (int k = 0; k < 4; ++k)                                                 \
+                    sq[k] = pack_bf16x2(bits_to_f(wq[k] & 0xffff) * sc, bits_to_f(wq[k] >> 16) * sc);         \
+                lds_st(aXsW + e * (NTH / 8) * P * 2, uint4{sq[0], sq[1], sq[2], sq[3]});               \
+            }                                                                                                 \
         }                                                                                                     \
         _Pragma("unroll") for (int e = 0; e < BPT; ++e) lds_st(aBtW + e * (NTH / 16) * BS * 2, quad(br, e)); \
         if (FULL) {                                                                                           \
@@ -745,8 +762,26 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
             // on the bank-conflict-free permutation).
             //   A operand: Bt^T rows n0 + 16rt + l16, read transposed
             //   B operand: (s X)^T column p = p0 + 16ct + l16, read transposed
+            // Without the s X tile (NOXS) the B operand is X^T and the A operand is scaled by
+            // s_j of its contraction rows in registers just before the products.
             bf16x8 bta[2][RT], bxs[2][CT];
+            float4 ssv[2][2];   // NOXS: s of contraction rows 32ks + 4lg + (0..3) and 32ks + 16 + 4lg + (0..3)
             auto load_step = [&](int ks, int slot) __attribute__((always_inline)) {
+                if constexpr (NOXS) {
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int r0 = 32 * ks + 16 * hh + 4 * lg;   // rows r0 .. r0 + 3 of token r0 / R ..
+                        if constexpr (R == 4) {
+                            const float v = sSc[q][r0 / 4];
+                            ssv[slot][hh] = float4{v, v, v, v};
+                        } else if constexpr (R == 2) {
+                            const float2 v = *reinterpret_cast<const float2*>(&sSc[q][r0 / 2]);
+                            ssv[slot][hh] = float4{v.x, v.x, v.y, v.y};
+                        } else {
+                            ssv[slot][hh] = *reinterpret_cast<const float4*>(&sSc[q][r0]);
+                        }
+                    }
+                }
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
                     const uint32_t src = aBtTr + (32 * ks * BS + 16 * rt) * 2;
@@ -765,6 +800,17 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma(ScanParams p) {
             for (int ks = 0; ks < KS; ++ks) {
                 if (ks + 1 < KS) load_step(ks + 1, (ks + 1) & 1);
                 __builtin_amdgcn_sched_barrier(0);
+                if constexpr (NOXS) {
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) {
+                        bf16x8 v = bta[ks & 1][rt];
+                        const float4 s0 = ssv[ks & 1][0], s1 = ssv[ks & 1][1];
+                        const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] = to_bf(from_bf(v[e]) * sc[e]);
+                        bta[ks & 1][rt] = v;
+                    }
+                }
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -924,15 +970,19 @@ bool mfma_supported(const PrefillArgs& a) {
            (a.Q == 32 || a.Q == 64) && offsets_fit && grid_fits;
 }
 
-// Segments per sequence: as many as fill the CUs in one round of workgroups.  A chunk
-// of up to 64 rows (Q * R <= 64) runs 4 waves and fits two workgroups per CU (registers);
-// larger chunks fit one (LDS).  Rounding down keeps the output pass to a single round
-// (rounding up left a second round nearly empty).  The CU count is MI355X's.
-static int choose_nseg(const PrefillArgs& a, int nchunks) {
+// Workgroups of the output pass that one CU holds at once: two for chunks of up to 128 rows
+// (4 waves; registers, and LDS at 128 rows), one for 256 rows (LDS).  The CU count is MI355X's.
+static int64_t scan_slots(const PrefillArgs& a) {
     constexpr int64_t kCUs = 256;
+    return kCUs * (a.Q * a.R <= 128 ? 2 : 1);
+}
+
+// Segments per sequence: as many as fill the CUs in one round of workgroups.  Rounding
+// down keeps the output pass to a single round (rounding up left a second round nearly
+// empty).
+static int choose_nseg(const PrefillArgs& a, int nchunks) {
     const int64_t slices = a.batch * a.H;
-    const int64_t slots = kCUs * (a.Q * a.R <= 64 ? 2 : 1);
-    int64_t nseg = slots / slices;
+    int64_t nseg = scan_slots(a) / slices;
     const int64_t max_seg = nchunks / 4 > 0 ? nchunks / 4 : 1;   // at least ~4 chunks per segment
     if (nseg > max_seg) nseg = max_seg;
     if (nseg < 1) nseg = 1;
@@ -945,10 +995,8 @@ static int choose_nseg(const PrefillArgs& a, int nchunks) {
 // the output pass starts segment s from the state entering piece split * s.  Each piece
 // keeps at least 4 chunks.
 static int choose_state_split(const PrefillArgs& a, int nseg, int cps) {
-    constexpr int64_t kCUs = 256;
     if (nseg < 2) return 1;
-    const int64_t slots = kCUs * (a.Q * a.R <= 64 ? 2 : 1);
-    int64_t f = slots / ((nseg - 1) * a.batch * a.H);
+    int64_t f = scan_slots(a) / ((nseg - 1) * a.batch * a.H);
     if (f > cps / 4) f = cps / 4;
     return f < 1 ? 1 : static_cast<int>(f);
 }
@@ -1002,10 +1050,11 @@ void plan_mfma(const PrefillArgs& a, PrefillPlan* plan) {
 
 template <int R, int Q>
 static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, hipStream_t st) {
-    // waves per workgroup: one per 16-row block of the chunk, at least 4; 16 blocks
-    // go two to a wave (8 waves), which shares their Bt and X tile reads
+    // waves per workgroup: one per 16-row block of the chunk, at least 4; 16 blocks go two
+    // to a wave (8 waves), which shares their Bt and X tile reads, and so do 8 blocks (4
+    // waves, two workgroups per CU)
     constexpr int NB = Q * R / 16;
-    constexpr int NW = NB > 8 ? NB / 2 : (NB > 4 ? NB : 4);
+    constexpr int NW = NB > 4 ? NB / 2 : 4;
     const int nchunks = static_cast<int>((a.L + a.Q - 1) / a.Q);
     if (nchunks == 0) return hipSuccess;
     const int nseg = plan.nseg, cps = plan.chunks_per_seg, split = plan.state_split;

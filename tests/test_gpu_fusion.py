@@ -59,6 +59,8 @@ CASES = [
     (1, 70, 2, 1, 64, 128, 4, 64, "bf16", ("bias",)),
     (1, 70, 2, 1, 64, 128, 1, 64, "bf16", ("gate",)),
     (1, 70, 2, 1, 64, 128, 1, 64, "bf16", ("A_t",)),
+    (1, 90, 2, 1, 64, 128, 4, 32, "bf16", ("A_t", "norm", "bias", "gate")),    # chunks of 128 rows
+    (2, 150, 4, 2, 64, 128, 2, 64, "bf16", ("gate",)),
     (2, 45, 4, 2, 16, 16, 2, 16, "fp32", ("A_t", "norm", "bias", "gate")),      # generic path
 ]
 
@@ -227,6 +229,8 @@ THETA_ONORM_CASES = [
     (2, 130, 8, 2, 4, 64, 128, 4, 64, "bf16", ("theta",)),
     (1, 200, 4, 1, 4, 64, 128, 1, 64, "bf16", ("theta", "onorm")),
     (2, 100, 8, 2, 8, 64, 128, 2, 32, "bf16", ("A_t", "norm", "bias", "gate", "theta", "onorm")),
+    (2, 100, 4, 1, 4, 64, 128, 4, 32, "bf16", ("A_t", "norm", "bias", "gate", "theta", "onorm")),
+    (1, 150, 4, 2, 4, 64, 128, 2, 64, "bf16", ("onorm",)),
     (2, 45, 4, 2, 4, 16, 16, 2, 16, "fp32", ("onorm",)),                             # generic path
     (2, 45, 6, 1, 6, 16, 16, 2, 16, "fp32", ("A_t", "norm", "bias", "gate", "theta", "onorm")),
 ]

@@ -27,6 +27,12 @@ CASES = [
     # (few (b, h) pairs): the output pass starts segment 1 from the second piece's end
     (2, 1100, 44, 1, 4, 64, 1.0),
     (4, 600, 48, 2, 2, 32, 1.0),
+    # chunks of 128 rows (4 waves, two workgroups per CU, no s X tile): R = 4 at Q = 32 and
+    # R = 2 at Q = 64, ragged, several segments (cut into pieces at few (b, h)), G = H
+    (1, 1500, 2, 1, 4, 32, 4.0),
+    (1, 400, 4, 4, 4, 32, 1.0),
+    (2, 1100, 100, 1, 2, 64, 1.0),   # two segments, the summarised one in two pieces
+    (2, 300, 4, 2, 2, 64, 1.0),
 ]
 
 
@@ -48,7 +54,7 @@ def test_mfma_prefill_matches_oracle(case):
     assert torch.equal(st.b_last, d["B"][:, -1]) and torch.equal(st.x_last, d["x"][:, -1])
 
 
-@pytest.mark.parametrize("L,R,Q", [(1000, 2, 32), (200, 4, 64), (64, 1, 64)])
+@pytest.mark.parametrize("L,R,Q", [(1000, 2, 32), (200, 4, 64), (64, 1, 64), (300, 4, 32), (500, 2, 64)])
 def test_mfma_prefill_from_state(L, R, Q):
     b, H, G = 1, 2, 1
     say("mfma prefill from state", L, R, Q)

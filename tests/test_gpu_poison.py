@@ -30,8 +30,9 @@ def _args(d):
     return [d[k] for k in ("x", "dt", "A", "lam", "theta", "B", "C", "D")]
 
 
-# (b, L, H, G, R, Q): several segments; one summarised segment cut into two pieces; G = H groups
-PREFILL = [(1, 1000, 2, 1, 2, 32), (2, 1100, 44, 1, 4, 64), (1, 777, 2, 2, 4, 64)]
+# (b, L, H, G, R, Q): several segments; one summarised segment cut into two pieces; G = H groups;
+# segments of 128-row chunks (4-wave workgroups)
+PREFILL = [(1, 1000, 2, 1, 2, 32), (2, 1100, 44, 1, 4, 64), (1, 777, 2, 2, 4, 64), (1, 1500, 2, 1, 4, 32)]
 
 
 @pytest.mark.parametrize("case", PREFILL, ids=lambda c: "b{}L{}H{}G{}R{}Q{}".format(*c))
