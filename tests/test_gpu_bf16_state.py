@@ -20,6 +20,7 @@ TOL_BF16_STATE = 2e-2
 CASES = [
     (2, 130, 12, 4, 1, 64, 128, 4, 64, "bf16"),
     (1, 1000, 6, 2, 1, 64, 128, 2, 32, "bf16"),      # several segments
+    (2, 300, 8, 4, 1, 64, 128, 4, 32, "bf16"),       # 128-row chunks (4-wave prefill)
     (1, 96, 10, 4, 1, 16, 16, 1, 32, "fp32"),
     (2, 40, 8, 2, 2, 8, 12, 3, 16, "fp32"),
 ]
@@ -53,7 +54,7 @@ def test_prefill_then_decode_bf16_state(case):
     assert ey <= TOL_BF16_STATE and eh <= TOL_BF16_STATE
 
 
-@pytest.mark.parametrize("L,R,Q", [(200, 4, 64), (1000, 2, 32), (50, 1, 32)])
+@pytest.mark.parametrize("L,R,Q", [(200, 4, 64), (1000, 2, 32), (50, 1, 32), (700, 4, 32)])
 def test_prefill_from_bf16_state(L, R, Q):
     """state_in in bf16 (values exact in bf16), state_out in bf16."""
     b, H, G, P, N = 1, 2, 1, 64, 128

@@ -37,6 +37,8 @@ def _run(d, cu, Lmax, Q, state_in=None, state_dtype=None):
 CASES = [
     ([130, 0, 64, 17, 300, 1], 4, 1, 64, 128, 2, 32, "bf16"),     # matrix-core path
     ([200, 63, 1, 129], 2, 2, 64, 128, 4, 64, "bf16"),
+    ([257, 0, 31, 96, 1000], 3, 1, 64, 128, 4, 32, "bf16"),         # 128-row chunks (4 waves)
+    ([64, 190, 7], 2, 1, 64, 128, 2, 64, "bf16"),
     ([100, 0, 37, 64, 5], 4, 1, 16, 16, 1, 32, "fp32"),            # generic path
 ]
 
