@@ -283,10 +283,12 @@ typedef struct {
 } m3_grads;
 
 /* Bytes of device workspace m3_backward needs for these dims: checkpointed states
- * (N * P * 4 bytes each) of every (b, h) -- one after every third token while
- * those fit in a budget of 4 GiB, else two levels of about sqrt(L / 3) states
- * each (one after every group of segments, and one group's states recomputed into
- * a scratch), for one more forward pass -- plus, when H > G, per-head copies of
+ * (N * P * 4 bytes each) of every (b, h) -- at N = 128, P = 64 one after every
+ * third token while those fit in a budget of 4 GiB, else two levels of about
+ * sqrt(L / 3) states each (one after every group of segments, and one group's
+ * states recomputed into a scratch), for one more forward pass; at other shapes
+ * one before every 16-token segment plus one segment's 17 states, or segments of
+ * ceil(sqrt(L)) tokens above the budget -- plus, when H > G, per-head copies of
  * the group-shared gradients, plus, when the sequences are split
  * (m3_backward_parts), two N * P states per piece.  The environment variable
  * M3_BACKWARD_CHECKPOINT_BYTES, read at each call, replaces the budget (a
@@ -299,7 +301,8 @@ m3_status m3_backward_workspace_size(const m3_dims* dims, size_t* bytes);
  * into *parts pieces of *tokens_per_part tokens (the last may be shorter) that are
  * processed side by side, after a pass that gives each piece the state and the
  * adjoint it starts from; *parts is 1 (and *tokens_per_part the length) when the
- * (b, h) pairs alone fill the GPU.  The choice depends on the dims only, so the
+ * (b, h) pairs alone fill the GPU, and always off the fast kernel's shape (N = 128,
+ * P = 64).  The choice depends on the dims only, so the
  * rounding of the gradients does too.  Errors as m3_backward_workspace_size. */
 m3_status m3_backward_parts(const m3_dims* dims, int32_t* parts, int64_t* tokens_per_part);
 
@@ -313,7 +316,10 @@ m3_status m3_backward_parts(const m3_dims* dims, int32_t* parts, int64_t* tokens
  * recomputed from checkpoints in the workspace; nothing from a previous
  * prefill call is needed.
  *
- * Supported: dstate 128, headdim 64, rank 1, 2 or 4; io dtype fp32 or bf16;
+ * Supported: dstate 128, headdim 64, rank 1, 2 or 4 (the fast kernel: sequences
+ * split into pieces when the (b, h) pairs leave the GPU idle); any other even
+ * dstate N and headdim P up to 256 with N / 2 * P at most 4096 and rank 1 to 8
+ * (one workgroup per (b, h), token by token, never split); io dtype fp32 or bf16;
  * state_in->h in dims->state_dtype.  dims->chunk is ignored.  All arithmetic
  * is fp32, except the sums of dt*A and theta over the tokens of a piece of a
  * split sequence (fp64).  Results do not depend on scheduling (no atomics).

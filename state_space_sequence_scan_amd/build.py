@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libm3scan.so")
 ARCH = "gfx950"
 
 SOURCES = ["m3_api.cpp", "m3_decode.hip", "m3_prefill_generic.hip", "m3_prefill_serial.hip", "m3_prefill_mfma.hip",
-           "m3_backward.hip"]
+           "m3_backward.hip", "m3_backward_generic.hip"]
 
 FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
          "-Wall", "-Wno-unused-function",

@@ -404,6 +404,14 @@ m3::BwdShape bwd_shape(const m3_dims* d) {
                         static_cast<int>(d->dstate), static_cast<int>(d->headdim), static_cast<int>(d->rank)};
 }
 
+// The fast kernel for its shape, else the generic one within its limits.
+bool bwd_any_supported(const m3::BwdShape& s) {
+    return m3::backward_supported(s) || m3::backward_generic_supported(s);
+}
+m3::BwdLayout bwd_any_layout(const m3::BwdShape& s) {
+    return m3::backward_supported(s) ? m3::backward_layout(s) : m3::backward_generic_layout(s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -411,18 +419,18 @@ extern "C" {
 m3_status m3_backward_workspace_size(const m3_dims* dims, size_t* bytes) {
     if (!bytes || !dims_ok(dims, true)) return M3_ERR_INVALID_ARG;
     const m3::BwdShape s = bwd_shape(dims);
-    if (!m3::backward_supported(s)) return M3_ERR_UNSUPPORTED;
-    *bytes = m3::backward_layout(s).bytes;
+    if (!bwd_any_supported(s)) return M3_ERR_UNSUPPORTED;
+    *bytes = bwd_any_layout(s).bytes;
     return M3_OK;
 }
 
 m3_status m3_backward_parts(const m3_dims* dims, int32_t* parts, int64_t* tokens_per_part) {
     if (!parts || !tokens_per_part || !dims_ok(dims, true)) return M3_ERR_INVALID_ARG;
     const m3::BwdShape s = bwd_shape(dims);
-    if (!m3::backward_supported(s)) return M3_ERR_UNSUPPORTED;
+    if (!bwd_any_supported(s)) return M3_ERR_UNSUPPORTED;
     int p = 1;
     int64_t spp = 0;
-    m3::backward_parts(s, &p, &spp);
+    if (m3::backward_supported(s)) m3::backward_parts(s, &p, &spp);   // the generic kernel never splits
     *parts = p;
     *tokens_per_part = p > 1 ? spp * 3 : s.L;
     return M3_OK;
@@ -445,9 +453,9 @@ m3_status backward_common(const m3_dims* dims, const int64_t* cu, int64_t total_
         return M3_ERR_INVALID_ARG;
     if (state_in && !state_in->h) return M3_ERR_INVALID_ARG;
     const m3::BwdShape s = bwd_shape(dims);
-    if (!m3::backward_supported(s)) return M3_ERR_UNSUPPORTED;
-    const m3::BwdLayout lay = m3::backward_layout(s);
-    // one workgroup of 512 threads per (b, h, part): under 2^32 work-items per launch
+    if (!bwd_any_supported(s)) return M3_ERR_UNSUPPORTED;
+    const m3::BwdLayout lay = bwd_any_layout(s);
+    // one workgroup of at most 512 threads per (b, h, part): under 2^32 work-items per launch
     if (s.batch * s.H * lay.parts >= (int64_t{1} << 23)) return M3_ERR_UNSUPPORTED;
     if (lay.bytes > 0 && (!workspace || workspace_bytes < lay.bytes)) return M3_ERR_WORKSPACE;
     m3::BwdArgs a{};
@@ -488,7 +496,8 @@ m3_status backward_common(const m3_dims* dims, const int64_t* cu, int64_t total_
     a.state_bf16 = dims->state_dtype == M3_BF16;
     a.cu = cu;
     a.T = cu ? total_tokens : s.batch * s.L;
-    const hipError_t e = m3::launch_backward(a, lay, static_cast<hipStream_t>(stream));
+    const hipError_t e = lay.generic ? m3::launch_backward_generic(a, lay, static_cast<hipStream_t>(stream))
+                                     : m3::launch_backward(a, lay, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? M3_OK : M3_ERR_HIP;
 }
 

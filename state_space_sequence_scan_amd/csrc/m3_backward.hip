@@ -912,8 +912,13 @@ hipError_t launch_backward(BwdArgs a, const BwdLayout& l, hipStream_t st) {
         bw::bwd_combine<<<static_cast<unsigned>(a.batch * a.H), bw::NT, 0, st>>>(a);
     }
     launch_scan<false>(a, grid, st);
-    hipError_t e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    return launch_backward_sums(a, l, st);
+}
+
+hipError_t launch_backward_sums(const BwdArgs& a, const BwdLayout& l, hipStream_t st) {
+    hipError_t e;
     if (l.per_head) {
         const int hpg = a.H / a.G;
         auto sum = [&](const float* part, float* out, int64_t rows, int width) {

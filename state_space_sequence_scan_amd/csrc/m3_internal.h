@@ -131,6 +131,8 @@ struct BwdLayout {            // byte offsets into the workspace
     int parts;                // S: the sequence of each (b, h) is split into S parts (1: no split)
     int64_t seg_per_part;     // recompute segments per part (the last part may hold fewer)
     int64_t grp;              // segments per checkpoint group (1: a checkpoint after every segment)
+    bool generic;             // the generic kernel (any shape within its limits): parts 1, grp 1
+    int64_t ks;               // generic kernel: tokens per recompute segment
 };
 // Number of parts the backward splits each sequence into, and the segments of
 // each part: chosen from the shape alone so that results depend on nothing else.
@@ -189,5 +191,13 @@ struct BwdArgs {
 bool backward_supported(const BwdShape& s);
 BwdLayout backward_layout(const BwdShape& s);
 hipError_t launch_backward(BwdArgs a, const BwdLayout& l, hipStream_t st);
+// After the scan kernels: sums of the per-head partial gradients of group-shared inputs,
+// the zero carry gradient when there is no carry, and dA, dD over batch (and parts).
+hipError_t launch_backward_sums(const BwdArgs& a, const BwdLayout& l, hipStream_t st);
+// Any other shape with N even, N and P at most 256, N / 2 * P at most 4096 and rank 1..8
+// (m3_backward_generic.hip): one workgroup per (b, h), token-serial.
+bool backward_generic_supported(const BwdShape& s);
+BwdLayout backward_generic_layout(const BwdShape& s);
+hipError_t launch_backward_generic(BwdArgs a, const BwdLayout& l, hipStream_t st);
 
 }  // namespace m3

@@ -198,12 +198,18 @@ def test_backward_rejects_bad_arguments(lib):
     big = _dims(headdim=64, dstate=128, rank=4, io_dtype=m3scan.M3_BF16)
     n = ctypes.c_size_t(0)
     assert lib.m3_backward_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0 and n.value > 0
-    # unsupported shape (N = 16, P = 16) and rank 3
-    small = _dims()
-    assert lib.m3_backward_workspace_size(ctypes.byref(small), ctypes.byref(n)) == -2
-    assert _bwd(lib, small, _grads()) == -2
-    r3 = _dims(headdim=64, dstate=128, rank=3)
-    assert _bwd(lib, r3, _grads()) == -2
+    # shapes no backward kernel takes: P above 256, rank 9, N / 2 * P above 4096 off the
+    # fast kernel's shape
+    for kw in (dict(headdim=300), dict(rank=9), dict(headdim=64, dstate=256)):
+        un = _dims(**kw)
+        assert lib.m3_backward_workspace_size(ctypes.byref(un), ctypes.byref(n)) == -2, kw
+        assert _bwd(lib, un, _grads()) == -2, kw
+    # the generic kernel's shapes (N = P = 16; rank 3 at N = 128, P = 64): valid calls whose
+    # only error is the missing workspace
+    for kw in (dict(), dict(headdim=64, dstate=128, rank=3)):
+        gen = _dims(**kw)
+        assert lib.m3_backward_workspace_size(ctypes.byref(gen), ctypes.byref(n)) == 0 and n.value > 0, kw
+        assert _bwd(lib, gen, _grads()) == -3, kw
     # bad dims
     for kw in BAD_DIMS:
         bd = _dims(**{"headdim": 64, "dstate": 128, **kw})
@@ -303,7 +309,10 @@ def test_backward_parts(lib):
     assert lib.m3_backward_parts(ctypes.byref(good), ctypes.byref(n32), None) == -1
     assert lib.m3_backward_parts(ctypes.byref(_dims(batch=0, headdim=P, dstate=N)), ctypes.byref(n32),
                                  ctypes.byref(n64)) == -1
-    assert lib.m3_backward_parts(ctypes.byref(_dims()), ctypes.byref(n32), ctypes.byref(n64)) == -2
+    assert lib.m3_backward_parts(ctypes.byref(_dims(headdim=300)), ctypes.byref(n32), ctypes.byref(n64)) == -2
+    # the generic kernel (off the fast shape) never splits
+    for L in (0, 5, 5000):
+        assert m3scan.backward_parts(_dims(batch=1, nheads=2, seqlen=L)) == (1, L)
 
 
 def test_launch_size_limits(lib):
@@ -348,8 +357,8 @@ def test_backward_varlen_rejects_bad_arguments(lib):
     args[5] = None                            # B
     assert call(args=args) == -1
     assert call(T=30) == -3                   # valid: the missing workspace is the only error
-    small = _dims(batch=3, seqlen=10)         # N = 16, P = 16: no backward kernel
-    assert lib.m3_backward_varlen(ctypes.byref(small), FAKE, 20, *([FAKE] * 8), None, FAKE, None,
+    un = _dims(batch=3, seqlen=10, headdim=300)   # P above 256: no backward kernel
+    assert lib.m3_backward_varlen(ctypes.byref(un), FAKE, 20, *([FAKE] * 8), None, FAKE, None,
                                   ctypes.byref(_grads()), None, 0, None) == -2
 
 
@@ -436,3 +445,26 @@ def test_serial_prefill_needs_no_workspace(lib):
         d = m3scan.make_dims(2, 300, 4, 2, P, N, R, 32, io)
         assert lib.m3_prefill_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
         assert n.value == 0, (N, P, R)
+
+
+def test_generic_backward_workspace(lib, monkeypatch):
+    """Off the fast kernel's shape the backward keeps the state before every 16-token segment
+    plus one segment's 17 states per (b, h) while those fit the checkpoint budget, else
+    segments of ceil(sqrt(L)) tokens (fewer bytes, the same gradients); per-head copies of
+    the group-shared gradients are added when H > G."""
+    import math
+    monkeypatch.delenv("M3_BACKWARD_CHECKPOINT_BYTES", raising=False)
+    b, H, N, P, R, L = 2, 4, 24, 12, 3, 1000
+    state = N * P * 4
+    d1 = _dims(batch=b, nheads=H, ngroups=H, headdim=P, dstate=N, rank=R, seqlen=L)
+    w16 = _bwd_ws(lib, d1)
+    assert w16 >= b * H * (math.ceil(L / 16) + 17) * state
+    assert w16 < b * H * (math.ceil(L / 16) + 17) * state + 4 * 256 + 2 * b * H * 4 + 1024
+    monkeypatch.setenv("M3_BACKWARD_CHECKPOINT_BYTES", "1")
+    ks = math.ceil(math.sqrt(L))
+    wsq = _bwd_ws(lib, d1)
+    assert wsq >= b * H * (math.ceil(L / ks) + ks + 1) * state and wsq < w16
+    monkeypatch.delenv("M3_BACKWARD_CHECKPOINT_BYTES")
+    d2 = _dims(batch=b, nheads=H, ngroups=1, headdim=P, dstate=N, rank=R, seqlen=L)
+    per_head = b * L * H * (2 * R * N + N // 2) * 4 + b * H * R * N * 4
+    assert _bwd_ws(lib, d2) >= w16 + per_head
