@@ -288,7 +288,8 @@ typedef struct {
  * sqrt(L / 3) states each (one after every group of segments, and one group's
  * states recomputed into a scratch), for one more forward pass; at other shapes
  * one before every 16-token segment plus one segment's 17 states, or segments of
- * ceil(sqrt(L)) tokens above the budget -- plus, when H > G, per-head copies of
+ * ceil(sqrt(L)) tokens rounded up to a multiple of 16 above the budget -- plus,
+ * when H > G, per-head copies of
  * the group-shared gradients, plus, when the sequences are split
  * (m3_backward_parts), two N * P states per piece.  The environment variable
  * M3_BACKWARD_CHECKPOINT_BYTES, read at each call, replaces the budget (a

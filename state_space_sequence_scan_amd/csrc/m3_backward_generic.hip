@@ -20,8 +20,11 @@
 // whole state (dalpha, dbeta, dgamma, dD) are taken from LDS copies of h_t, dU_t and the
 // per-pair angle terms in a fixed order, so results do not depend on scheduling.  Group-
 // shared gradients are written per head when H > G and summed afterwards, as in the fast
-// kernel.  Staging each token's inputs costs two barriers per token: this path is for the
-// small and unusual shapes; N = 128, P = 64 run the fast kernel.
+// kernel.  The inputs of up to 16 tokens are staged into LDS at once (as many as 128 KB
+// of LDS holds beside the sums' buffers).  The sums take two barriers per token in the
+// reverse sweep; a barrier also waits for the workgroup's outstanding global stores, so
+// each token's gradients are kept in LDS and the block's are written out together.  This
+// path is for the small and unusual shapes; N = 128, P = 64 run the fast kernel.
 #include <cmath>
 #include <cstdlib>
 
@@ -36,23 +39,26 @@ constexpr int kMaxR = 8;
 constexpr int kMaxEPT = 16;      // element pairs per thread: (N / 2) * P <= NT * kMaxEPT
 constexpr int kMaxDim = 256;
 
-// Dynamic LDS layout (floats), sized for this launch's N, P, R.
+// Dynamic LDS layout (floats), sized for this launch's N, P, R and TB tokens per staged
+// block.  Slot j of B and X holds token t0 - 1 + j (slot 0: the token before the block, the
+// carry, or zeros); slot j of the others holds token t0 + j.
 struct Lds {
-    int bp, xp, b, x, c, dy, cs, sn, hL, dUL, thc, red, total;
-    __host__ __device__ Lds(int N, int P, int R) {
+    int b, x, c, dy, cs, sn, sc, hL, dUL, thc, red, ob, ow, total;
+    __host__ __device__ Lds(int N, int P, int R, int TB) {
         int o = 0;
-        bp = o; o += R * N;        // B of the previous token (or the carry, or zeros)
-        xp = o; o += R * P;        // X of the previous token
-        b = o;  o += R * N;        // B of this token
-        x = o;  o += R * P;
-        c = o;  o += R * N;
-        dy = o; o += R * P;
-        cs = o; o += N / 2;        // cos, sin of this token's pair angles
-        sn = o; o += N / 2;
-        hL = o; o += N * P;        // h_t, (n, p) row-major
-        dUL = o; o += N * P;       // dU_t
-        thc = o; o += (N / 2) * P; // per (pair, column) terms of dtheta
-        red = o; o += 3 * NT;      // per-thread partial sums of dalpha, dbeta, dgamma
+        b = o;  o += (TB + 1) * R * N;
+        x = o;  o += (TB + 1) * R * P;
+        c = o;  o += TB * R * N;
+        dy = o; o += TB * R * P;
+        cs = o; o += TB * (N / 2);    // cos, sin of each token's pair angles
+        sn = o; o += TB * (N / 2);
+        sc = o; o += TB * 4;          // dt, lambda, decay rate of each token
+        hL = o; o += N * P;           // h_t, (n, p) row-major
+        dUL = o; o += N * P;          // dU_t
+        thc = o; o += (N / 2) * P;    // per (pair, column) terms of dtheta
+        red = o; o += 3 * NT;         // per-thread partial sums of dalpha, dbeta, dgamma
+        ow = 2 * R * N + N / 2 + R * P + 4;   // one token's outputs: dC, dB, dtheta, dx, ddt, dlambda, dA
+        ob = o; o += TB * ow;         // the block's outputs, written out once per block
         total = o;
     }
 };
@@ -60,35 +66,40 @@ struct Lds {
 template <typename T>
 __device__ __forceinline__ float ldv(const T* p, int64_t i) { return io<T>::load(p + i); }
 
-// Sum over the 64 lanes of a wave in a fixed butterfly order; every lane gets it.
-__device__ __forceinline__ float wave_sum_fixed(float v) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
-    return v;
+// floor(u / d) for 0 <= u < 8192 and 1 <= d <= 256, from inv = 1/d in fp32: (u + 1/2) / d
+// lies at least 1/512 from an integer, and the two roundings move it by at most
+// u * 2^-23 < 2^-10, so the truncation is exact.
+__device__ __forceinline__ int fdiv(int u, float inv) {
+    return static_cast<int>((static_cast<float>(u) + 0.5f) * inv);
 }
 
-template <typename T>
-__global__ __launch_bounds__(NT) void bwd_generic(BwdArgs a, int64_t ks) {
+// ks: tokens per recompute segment, a multiple of TB (tokens staged per block).  EPT:
+// element pairs per thread, the smallest power of two that covers N / 2 * P.
+template <typename T, int EPT>
+__global__ __launch_bounds__(NT) void bwd_generic(BwdArgs a, int64_t ks, int TB) {
     extern __shared__ __align__(16) float lds[];
-    const int N = a.N, P = a.P, R = a.R, KP = N / 2, E = KP * P;
-    const Lds lay(N, P, R);
-    float* sBp = lds + lay.bp;
-    float* sXp = lds + lay.xp;
+    const int N = a.N, P = a.P, R = a.R, KP = N / 2, E = KP * P, RN = R * N, RP = R * P;
+    const float invN = 1.f / N, invP = 1.f / P;   // for the task indices (fdiv)
+    const Lds lay(N, P, R, TB);
     float* sB = lds + lay.b;
     float* sX = lds + lay.x;
     float* sC = lds + lay.c;
     float* sDY = lds + lay.dy;
     float* sCs = lds + lay.cs;
     float* sSn = lds + lay.sn;
+    float* sSc = lds + lay.sc;
     float* sHL = lds + lay.hL;
     float* sDU = lds + lay.dUL;
     float* sTh = lds + lay.thc;
     float* sRed = lds + lay.red;
-    __shared__ float sScal[8];   // dt, lambda, decay rate of this token; reduced dalpha, dbeta, dgamma, dD
+    float* sOut = lds + lay.ob;
+    const int OW = lay.ow;
+    __shared__ float kOne;   // the stride-0 operand of the dtheta sums (set before the first barrier)
 
     const int bh = blockIdx.x;
     const int b = bh / a.H, h = bh - b * a.H, g = h / (a.H / a.G);
     const int tid = threadIdx.x, lane = tid & 63;
+    if (tid == 0) kOne = 1.f;
     const int H = a.H, G = a.G;
     const SeqSpan span = seq_span(a.cu, b, a.L, a.T);
     const int64_t tb = span.start, L = span.len;
@@ -107,42 +118,61 @@ __global__ __launch_bounds__(NT) void bwd_generic(BwdArgs a, int64_t ks) {
     float2* ck = reinterpret_cast<float2*>(a.ckpt) + static_cast<size_t>(bh) * a.seg_per_part * E;
     float2* scr = reinterpret_cast<float2*>(a.scratch) + static_cast<size_t>(bh) * (ks + 1) * E;
 
-    const int EPT = (E + NT - 1) / NT;
+    // the thread's element pairs: pair kk[i], column pp[i] (kk = -1: none)
+    int kk[EPT], pp[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int e = tid + NT * i;
+        kk[i] = e < E ? e / P : -1;
+        pp[i] = e < E ? e - kk[i] * P : 0;
+    }
     auto soff = [&](int64_t t) { return (tb + t) * H + h; };
 
-    // Inputs of token t (and B, X of token t - 1) into LDS; with_cdy also C_t, dy_t.
-    auto stage = [&](int64_t t, bool with_cdy) {
-        __syncthreads();   // the previous step's readers are done
-        for (int i = tid; i < R * N; i += NT) {
-            sB[i] = ldv(Bm, ((tb + t) * G + g) * static_cast<int64_t>(R * N) + i);
-            sBp[i] = t > 0 ? ldv(Bm, ((tb + t - 1) * G + g) * static_cast<int64_t>(R * N) + i)
-                           : (carry ? ldv(blp, (static_cast<int64_t>(b) * G + g) * (R * N) + i) : 0.f);
-            if (with_cdy) sC[i] = ldv(Cm, ((tb + t) * G + g) * static_cast<int64_t>(R * N) + i);
+    // Tokens t0 .. t0+nt-1 (B and X also of token t0 - 1) into the slots; with_cdy also
+    // their C and dy.
+    auto stage = [&](int64_t t0, int nt, bool with_cdy) {
+        __syncthreads();   // the previous block's readers are done
+        for (int i = tid; i < (nt + 1) * RN; i += NT) {
+            const int j = i / RN, o = i - j * RN;
+            const int64_t t = t0 - 1 + j;
+            sB[i] = t >= 0 ? ldv(Bm, ((tb + t) * G + g) * static_cast<int64_t>(RN) + o)
+                           : (carry ? ldv(blp, (static_cast<int64_t>(b) * G + g) * RN + o) : 0.f);
         }
-        for (int i = tid; i < R * P; i += NT) {
-            sX[i] = ldv(x, ((tb + t) * H + h) * static_cast<int64_t>(R * P) + i);
-            sXp[i] = t > 0 ? ldv(x, ((tb + t - 1) * H + h) * static_cast<int64_t>(R * P) + i)
-                           : (carry ? ldv(xlp, (static_cast<int64_t>(b) * H + h) * (R * P) + i) : 0.f);
-            if (with_cdy) sDY[i] = ldv(dy, ((tb + t) * H + h) * static_cast<int64_t>(R * P) + i);
+        for (int i = tid; i < (nt + 1) * RP; i += NT) {
+            const int j = i / RP, o = i - j * RP;
+            const int64_t t = t0 - 1 + j;
+            sX[i] = t >= 0 ? ldv(x, ((tb + t) * H + h) * static_cast<int64_t>(RP) + o)
+                           : (carry ? ldv(xlp, (static_cast<int64_t>(b) * H + h) * RP + o) : 0.f);
         }
-        for (int k = tid; k < KP; k += NT) {
-            float s, c;
-            sincos_acc(a.theta[((tb + t) * G + g) * KP + k], &s, &c);
-            sCs[k] = c;
-            sSn[k] = s;
+        if (with_cdy) {
+            for (int i = tid; i < nt * RN; i += NT) {
+                const int j = i / RN, o = i - j * RN;
+                sC[i] = ldv(Cm, ((tb + t0 + j) * G + g) * static_cast<int64_t>(RN) + o);
+            }
+            for (int i = tid; i < nt * RP; i += NT) {
+                const int j = i / RP, o = i - j * RP;
+                sDY[i] = ldv(dy, ((tb + t0 + j) * H + h) * static_cast<int64_t>(RP) + o);
+            }
         }
-        if (tid == 0) {
-            sScal[0] = a.dt[soff(t)];
-            sScal[1] = a.lam[soff(t)];
-            sScal[2] = a.At ? a.At[soff(t)] : Ah;
+        for (int i = tid; i < nt * KP; i += NT) {
+            const int j = i / KP, k = i - j * KP;
+            float sv, cv;
+            sincos_acc(a.theta[((tb + t0 + j) * G + g) * KP + k], &sv, &cv);
+            sCs[i] = cv;
+            sSn[i] = sv;
+        }
+        for (int j = tid; j < nt; j += NT) {
+            sSc[4 * j] = a.dt[soff(t0 + j)];
+            sSc[4 * j + 1] = a.lam[soff(t0 + j)];
+            sSc[4 * j + 2] = a.At ? a.At[soff(t0 + j)] : Ah;
         }
         __syncthreads();
     };
-    // U of rows (2k, 2k+1) at column p from the B, X rows in LDS.  The forward step is
-    // inlined at two places (the sweep that stores checkpoints and the recompute of a
-    // segment); its multiply-adds are written out as fused operations with contraction
-    // off, so that both places compute the same bits and the gradients do not depend on
-    // where the checkpoints fall.
+    // U of rows (2k, 2k+1) at column p from B, X rows in LDS.  The forward step is inlined
+    // at two places (the sweep that stores checkpoints and the recompute of a segment); its
+    // multiply-adds are written out as fused operations with contraction off, so that both
+    // places compute the same bits and the gradients do not depend on where the
+    // checkpoints fall.
     auto uval = [&](const float* Bs, const float* Xs, int k, int p, float* u0, float* u1) {
 #pragma clang fp contract(off)
         float s0 = 0.f, s1 = 0.f;
@@ -154,204 +184,256 @@ __global__ __launch_bounds__(NT) void bwd_generic(BwdArgs a, int64_t ks) {
         *u0 = s0;
         *u1 = s1;
     };
-    auto coeffs = [&](float* al, float* be, float* ga) {
+    auto coeffs = [&](int j, float* al, float* be, float* ga) {
 #pragma clang fp contract(off)
-        const float dtv = sScal[0], lv = sScal[1];
-        *al = __expf(dtv * sScal[2]);
+        const float dtv = sSc[4 * j], lv = sSc[4 * j + 1];
+        *al = __expf(dtv * sSc[4 * j + 2]);
         *be = (1.f - lv) * dtv * *al;
         *ga = lv * dtv;
     };
-    // one forward step of the staged token on the thread's pairs
-    auto fwd_step = [&](float2 (&hs)[kMaxEPT]) {
+    // one forward step of the token in slot j on the thread's pairs
+    auto fwd_step = [&](int j, float2 (&hs)[EPT]) {
 #pragma clang fp contract(off)
         float al, be, ga;
-        coeffs(&al, &be, &ga);
+        coeffs(j, &al, &be, &ga);
+        const float* Bp = sB + j * RN;
+        const float* Xp = sX + j * RP;
 #pragma unroll
-        for (int i = 0; i < kMaxEPT; ++i) {
+        for (int i = 0; i < EPT; ++i) {
             const int e = tid + NT * i;
-            if (i < EPT && e < E) {
-                const int k = e / P, p = e - k * P;
+            if (kk[i] >= 0) {
+                const int k = kk[i], p = pp[i];
                 float up0, up1, u0, u1;
-                uval(sBp, sXp, k, p, &up0, &up1);
-                uval(sB, sX, k, p, &u0, &u1);
+                uval(Bp, Xp, k, p, &up0, &up1);
+                uval(Bp + RN, Xp + RP, k, p, &u0, &u1);
                 const float v0 = __builtin_fmaf(al, hs[i].x, be * up0);
                 const float v1 = __builtin_fmaf(al, hs[i].y, be * up1);
-                const float c = sCs[k], s = sSn[k];
+                const float c = sCs[j * KP + k], s = sSn[j * KP + k];
                 hs[i].x = __builtin_fmaf(c, v0, __builtin_fmaf(-s, v1, ga * u0));
                 hs[i].y = __builtin_fmaf(s, v0, __builtin_fmaf(c, v1, ga * u1));
             }
         }
     };
-    auto store = [&](float2* dst, const float2 (&hs)[kMaxEPT]) {
+    auto store = [&](float2* dst, const float2 (&hs)[EPT]) {
 #pragma unroll
-        for (int i = 0; i < kMaxEPT; ++i) {
+        for (int i = 0; i < EPT; ++i) {
             const int e = tid + NT * i;
-            if (i < EPT && e < E) {
-                dst[e] = hs[i];
-            }
+            if (kk[i] >= 0) dst[e] = hs[i];
         }
     };
-    auto load = [&](const float2* src, float2 (&hs)[kMaxEPT]) {
+    auto load = [&](const float2* src, float2 (&hs)[EPT]) {
 #pragma unroll
-        for (int i = 0; i < kMaxEPT; ++i) {
+        for (int i = 0; i < EPT; ++i) {
             const int e = tid + NT * i;
-            if (i < EPT && e < E) {
-                hs[i] = src[e];
-            }
+            if (kk[i] >= 0) hs[i] = src[e];
         }
     };
 
     // ---- forward sweep: the state before every segment
-    float2 hs[kMaxEPT];
+    float2 hs[EPT];
 #pragma unroll
-    for (int i = 0; i < kMaxEPT; ++i) {
+    for (int i = 0; i < EPT; ++i) {
         const int e = tid + NT * i;
         hs[i] = float2{0.f, 0.f};
-        if (i < EPT && e < E && a.h0) {
-            const int k = e / P, p = e - k * P;
+        if (kk[i] >= 0 && a.h0) {
+            const int k = kk[i], p = pp[i];
             const size_t base = static_cast<size_t>(bh) * N * P;
             hs[i].x = state_load(a.h0, base + static_cast<size_t>(2 * k) * P + p, a.state_bf16);
             hs[i].y = state_load(a.h0, base + static_cast<size_t>(2 * k + 1) * P + p, a.state_bf16);
         }
     }
-    for (int64_t t = 0; t < L; ++t) {
-        if (t % ks == 0) store(ck + (t / ks) * E, hs);
-        stage(t, false);
-        fwd_step(hs);
+    for (int64_t t0 = 0; t0 < L; t0 += TB) {
+        const int nt = static_cast<int>(L - t0 < TB ? L - t0 : TB);
+        stage(t0, nt, false);
+        for (int j = 0; j < nt; ++j) {
+            if ((t0 + j) % ks == 0) store(ck + ((t0 + j) / ks) * E, hs);
+            fwd_step(j, hs);
+        }
     }
 
     // ---- reverse sweep.  q_{t+1}, alpha_{t+1}, beta_{t+1} belong to the token after; the
     // final-state cotangent enters as a token after the last with alpha = 1, beta = 0.
-    float2 qn[kMaxEPT];
+    float2 qn[EPT];
 #pragma unroll
-    for (int i = 0; i < kMaxEPT; ++i) {
+    for (int i = 0; i < EPT; ++i) {
         const int e = tid + NT * i;
         qn[i] = float2{0.f, 0.f};
-        if (i < EPT && e < E && a.dh_out) {
-            const int k = e / P, p = e - k * P;
+        if (kk[i] >= 0 && a.dh_out) {
+            const int k = kk[i], p = pp[i];
             const size_t base = static_cast<size_t>(bh) * N * P;
             qn[i].x = a.dh_out[base + static_cast<size_t>(2 * k) * P + p];
             qn[i].y = a.dh_out[base + static_cast<size_t>(2 * k + 1) * P + p];
         }
     }
     float an = 1.f, bn = 0.f;
-    float dA_acc = 0.f, dD_acc = 0.f;   // thread 0
+    float dA_acc = 0.f, dD_acc = 0.f;   // thread NT - 64
 
     for (int64_t s = nseg - 1; s >= 0; --s) {
         const int64_t t0 = s * ks;
         const int len = static_cast<int>(L - t0 < ks ? L - t0 : ks);
         {   // h_{t0-1} .. h_{t0+len-1} into the scratch
-            float2 hr[kMaxEPT];
+            float2 hr[EPT];
             load(ck + s * E, hr);
             store(scr, hr);
-            for (int j = 0; j < len; ++j) {
-                stage(t0 + j, false);
-                fwd_step(hr);
-                store(scr + (j + 1) * E, hr);
+            for (int bt = 0; bt < len; bt += TB) {
+                const int nt = len - bt < TB ? len - bt : TB;
+                stage(t0 + bt, nt, false);
+                for (int j = 0; j < nt; ++j) {
+                    fwd_step(j, hr);
+                    store(scr + (bt + j + 1) * E, hr);
+                }
             }
         }
-        for (int j = len - 1; j >= 0; --j) {
-            const int64_t t = t0 + j;
-            stage(t, true);
-            float al, be, ga;
-            coeffs(&al, &be, &ga);
-            float dal = 0.f, dbe = 0.f, dga = 0.f;
+        // h_t and h_{t-1} of the token being reversed, in registers; h_{t-2} is loaded a
+        // token ahead, so the scratch's latency is off the chain of the sums
+        float2 hcur[EPT], hpv[EPT];
+        load(scr + len * E, hcur);
+        load(scr + (len - 1) * E, hpv);
+        for (int bt = ((len - 1) / TB) * TB; bt >= 0; bt -= TB) {
+            const int nt = len - bt < TB ? len - bt : TB;
+            stage(t0 + bt, nt, true);
+            for (int j = nt - 1; j >= 0; --j) {
+                const int js = bt + j;   // token index within the segment
+                float2 hnx[EPT];
 #pragma unroll
-            for (int i = 0; i < kMaxEPT; ++i) {
-                const int e = tid + NT * i;
-                if (i < EPT && e < E) {
-                    const int k = e / P, p = e - k * P;
-                    const float2 ht = scr[(j + 1) * E + e], hp = scr[j * E + e];
-                    float g0 = an * qn[i].x, g1 = an * qn[i].y;
-                    for (int r = 0; r < R; ++r) {
-                        const float dv = sDY[r * P + p];
-                        g0 += sC[r * N + 2 * k] * dv;
-                        g1 += sC[r * N + 2 * k + 1] * dv;
+                for (int i = 0; i < EPT; ++i) hnx[i] = float2{0.f, 0.f};
+                if (js > 0) load(scr + (js - 1) * E, hnx);
+                float al, be, ga;
+                coeffs(j, &al, &be, &ga);
+                const float* Bp = sB + j * RN;
+                const float* Xp = sX + j * RP;
+                const float* Bc = Bp + RN;
+                const float* Xc = Xp + RP;
+                const float* Cc = sC + j * RN;
+                const float* Dc = sDY + j * RP;
+                float dal = 0.f, dbe = 0.f, dga = 0.f;
+#pragma unroll
+                for (int i = 0; i < EPT; ++i) {
+                    const int e = tid + NT * i;
+                    if (kk[i] >= 0) {
+                        const int k = kk[i], p = pp[i];
+                        const float2 ht = hcur[i], hp = hpv[i];
+                        float g0 = an * qn[i].x, g1 = an * qn[i].y;
+                        for (int r = 0; r < R; ++r) {
+                            const float dv = Dc[r * P + p];
+                            g0 += Cc[r * N + 2 * k] * dv;
+                            g1 += Cc[r * N + 2 * k + 1] * dv;
+                        }
+                        float u0, u1, up0, up1;
+                        uval(Bc, Xc, k, p, &u0, &u1);
+                        uval(Bp, Xp, k, p, &up0, &up1);
+                        dga += g0 * u0 + g1 * u1;
+                        const float c = sCs[j * KP + k], sn = sSn[j * KP + k];
+                        const float q0 = c * g0 + sn * g1, q1 = -sn * g0 + c * g1;
+                        dal += q0 * hp.x + q1 * hp.y;
+                        dbe += q0 * up0 + q1 * up1;
+                        const float v0 = al * hp.x + be * up0, v1 = al * hp.y + be * up1;
+                        sTh[e] = q1 * v0 - q0 * v1;
+                        const int n0 = (2 * k) * P + p;
+                        sHL[n0] = ht.x;
+                        sHL[n0 + P] = ht.y;
+                        sDU[n0] = ga * g0 + bn * qn[i].x;
+                        sDU[n0 + P] = ga * g1 + bn * qn[i].y;
+                        qn[i] = float2{q0, q1};
                     }
-                    float u0, u1, up0, up1;
-                    uval(sB, sX, k, p, &u0, &u1);
-                    uval(sBp, sXp, k, p, &up0, &up1);
-                    dga += g0 * u0 + g1 * u1;
-                    const float c = sCs[k], sn = sSn[k];
-                    const float q0 = c * g0 + sn * g1, q1 = -sn * g0 + c * g1;
-                    dal += q0 * hp.x + q1 * hp.y;
-                    dbe += q0 * up0 + q1 * up1;
-                    const float v0 = al * hp.x + be * up0, v1 = al * hp.y + be * up1;
-                    sTh[e] = q1 * v0 - q0 * v1;
-                    const int n0 = (2 * k) * P + p;
-                    sHL[n0] = ht.x;
-                    sHL[n0 + P] = ht.y;
-                    sDU[n0] = ga * g0 + bn * qn[i].x;
-                    sDU[n0 + P] = ga * g1 + bn * qn[i].y;
-                    qn[i] = float2{q0, q1};
+                }
+                sRed[tid] = dal;
+                sRed[NT + tid] = dbe;
+                sRed[2 * NT + tid] = dga;
+                __syncthreads();
+                // The token's sums as one list of dot products, spread over the threads so
+                // that they run side by side (one loop shape for all, no divergence inside):
+                //   dC[r][n] = sum_p h_t[n][p] dy[r][p]      (RN tasks)
+                //   dB[r][n] = sum_p dU[n][p] X[r][p]        (RN)
+                //   dtheta[k] = sum_p (angle term)[k][p]     (KP; times a stride-0 one)
+                //   dX[r][p] = sum_n B[r][n] dU[n][p]        (RP; plus D dy afterwards)
+                const int ntask = 2 * RN + KP + RP;
+                for (int o = tid; o < ntask; o += NT) {
+                    const float* pa;
+                    const float* pb;
+                    int sa = 1, sb = 1, m = P, kind;
+                    if (o < RN) {
+                        const int r = fdiv(o, invN), n = o - r * N;
+                        pa = sHL + n * P; pb = Dc + r * P; kind = 0;
+                    } else if (o < 2 * RN) {
+                        const int r = fdiv(o - RN, invN), n = (o - RN) - r * N;
+                        pa = sDU + n * P; pb = Xc + r * P; kind = 1;
+                    } else if (o < 2 * RN + KP) {
+                        pa = sTh + (o - 2 * RN) * P; pb = &kOne; sb = 0; kind = 2;
+                    } else {
+                        const int q = o - 2 * RN - KP, r = fdiv(q, invP), p = q - r * P;
+                        pa = Bc + r * N; pb = sDU + p; sb = P; m = N; kind = 3;
+                    }
+                    float v = 0.f;
+#pragma unroll 4
+                    for (int i = 0; i < m; ++i) v += pa[i * sa] * pb[i * sb];
+                    if (kind == 3) v += Dh * Dc[o - 2 * RN - KP];
+                    sOut[j * OW + o] = v;   // in the order dC, dB, dtheta, dx
+                }
+                // whole-state sums, in a fixed order by the last wave
+                if (tid >= NT - 64) {
+                    float sa = 0.f, sb = 0.f, sg = 0.f, sd = 0.f;
+                    for (int w = 0; w < NT / 64; ++w) {
+                        sa += sRed[w * 64 + lane];
+                        sb += sRed[NT + w * 64 + lane];
+                        sg += sRed[2 * NT + w * 64 + lane];
+                    }
+                    for (int o = lane; o < RP; o += 64) sd += Dc[o] * Xc[o];
+                    sa = wave_sum(sa);   // DPP, fixed order, all 64 lanes of this wave active
+                    sb = wave_sum(sb);
+                    sg = wave_sum(sg);
+                    sd = wave_sum(sd);
+                    if (tid == NT - 64) {
+                        const float dtv = sSc[4 * j], lv = sSc[4 * j + 1], av = sSc[4 * j + 2];
+                        float* so = sOut + j * OW + ntask;
+                        so[0] = sa * av * al + sb * (1.f - lv) * (al + dtv * av * al) + sg * lv;
+                        so[1] = -sb * dtv * al + sg * dtv;
+                        const float dav = sa * dtv * al + sb * (1.f - lv) * dtv * dtv * al;
+                        so[2] = dav;
+                        if (!a.At) dA_acc += dav;
+                        dD_acc += sd;
+                    }
+                }
+                __syncthreads();   // the sums are read before the next token overwrites them
+                an = al;
+                bn = be;
+#pragma unroll
+                for (int i = 0; i < EPT; ++i) {
+                    hcur[i] = hpv[i];
+                    hpv[i] = hnx[i];
                 }
             }
-            sRed[tid] = dal;
-            sRed[NT + tid] = dbe;
-            sRed[2 * NT + tid] = dga;
-            __syncthreads();
-            // column sums: dC = h_t dy^T, dB = dU X^T (per head when the group is shared)
-            const int64_t go = ((tb + t) * GH + gh) * static_cast<int64_t>(R * N);
-            float* dCo = a.per_head ? a.dC_part : a.dC;
-            float* dBo = a.per_head ? a.dB_part : a.dB;
-            for (int o = tid; o < R * N; o += NT) {
-                const int r = o / N, n = o - r * N;
-                float dc = 0.f, db = 0.f;
-                for (int p = 0; p < P; ++p) {
-                    dc += sHL[n * P + p] * sDY[r * P + p];
-                    db += sDU[n * P + p] * sX[r * P + p];
-                }
-                dCo[go + o] = dc;
-                dBo[go + o] = db;
+            // the block's outputs (visible after the last token's barrier), once per block
+            const int64_t tf = tb + t0 + bt;   // first token of the block in the packed arrays
+            for (int i = tid; i < nt * RN; i += NT) {
+                const int j = i / RN, o = i - j * RN;
+                (a.per_head ? a.dC_part : a.dC)[((tf + j) * GH + gh) * static_cast<int64_t>(RN) + o] = sOut[j * OW + o];
+                (a.per_head ? a.dB_part : a.dB)[((tf + j) * GH + gh) * static_cast<int64_t>(RN) + o] = sOut[j * OW + RN + o];
             }
-            float* dTo = a.per_head ? a.dtheta_part : a.dtheta;
-            for (int k = tid; k < KP; k += NT) {
-                float v = 0.f;
-                for (int p = 0; p < P; ++p) v += sTh[k * P + p];
-                dTo[((tb + t) * GH + gh) * KP + k] = v;
+            for (int i = tid; i < nt * KP; i += NT) {
+                const int j = i / KP, k = i - j * KP;
+                (a.per_head ? a.dtheta_part : a.dtheta)[((tf + j) * GH + gh) * KP + k] = sOut[j * OW + 2 * RN + k];
             }
-            // row sums: dX = B^T dU + D dy
-            for (int o = tid; o < R * P; o += NT) {
-                const int r = o / P, p = o - r * P;
-                float v = 0.f;
-                for (int n = 0; n < N; ++n) v += sB[r * N + n] * sDU[n * P + p];
-                a.dx[((tb + t) * H + h) * static_cast<int64_t>(R * P) + o] = v + Dh * sDY[o];
+            for (int i = tid; i < nt * RP; i += NT) {
+                const int j = i / RP, o = i - j * RP;
+                a.dx[((tf + j) * H + h) * static_cast<int64_t>(RP) + o] = sOut[j * OW + 2 * RN + KP + o];
             }
-            // whole-state sums, in a fixed order by wave 0
-            if (tid < 64) {
-                float sa = 0.f, sb = 0.f, sg = 0.f, sd = 0.f;
-                for (int w = 0; w < NT / 64; ++w) {
-                    sa += sRed[w * 64 + lane];
-                    sb += sRed[NT + w * 64 + lane];
-                    sg += sRed[2 * NT + w * 64 + lane];
-                }
-                for (int o = lane; o < R * P; o += 64) sd += sDY[o] * sX[o];
-                sa = wave_sum_fixed(sa);
-                sb = wave_sum_fixed(sb);
-                sg = wave_sum_fixed(sg);
-                sd = wave_sum_fixed(sd);
-                if (tid == 0) {
-                    const float dtv = sScal[0], lv = sScal[1], av = sScal[2];
-                    a.ddt[soff(t)] = sa * av * al + sb * (1.f - lv) * (al + dtv * av * al) + sg * lv;
-                    a.dlam[soff(t)] = -sb * dtv * al + sg * dtv;
-                    const float dav = sa * dtv * al + sb * (1.f - lv) * dtv * dtv * al;
-                    if (a.At) a.dA[soff(t)] = dav;
-                    else dA_acc += dav;
-                    dD_acc += sd;
-                }
+            for (int j = tid; j < nt; j += NT) {
+                const float* so = sOut + j * OW + 2 * RN + KP + RP;
+                a.ddt[(tf + j) * H + h] = so[0];
+                a.dlam[(tf + j) * H + h] = so[1];
+                if (a.At) a.dA[(tf + j) * H + h] = so[2];
             }
-            an = al;
-            bn = be;
         }
     }
 
     // ---- h_0 and the carried previous input (its cotangent beta_1 q_1)
     if (a.dh0) {
 #pragma unroll
-        for (int i = 0; i < kMaxEPT; ++i) {
+        for (int i = 0; i < EPT; ++i) {
             const int e = tid + NT * i;
-            if (i < EPT && e < E) {
-                const int k = e / P, p = e - k * P;
+            if (kk[i] >= 0) {
+                const int k = kk[i], p = pp[i];
                 const size_t base = static_cast<size_t>(bh) * N * P;
                 a.dh0[base + static_cast<size_t>(2 * k) * P + p] = an * qn[i].x;
                 a.dh0[base + static_cast<size_t>(2 * k + 1) * P + p] = an * qn[i].y;
@@ -360,13 +442,13 @@ __global__ __launch_bounds__(NT) void bwd_generic(BwdArgs a, int64_t ks) {
     }
     if (carry && (a.dbl || a.dxl)) {
         __syncthreads();
-        for (int i = tid; i < R * N; i += NT) sBp[i] = ldv(blp, (static_cast<int64_t>(b) * G + g) * (R * N) + i);
-        for (int i = tid; i < R * P; i += NT) sXp[i] = ldv(xlp, (static_cast<int64_t>(b) * H + h) * (R * P) + i);
+        for (int i = tid; i < RN; i += NT) sB[i] = ldv(blp, (static_cast<int64_t>(b) * G + g) * RN + i);
+        for (int i = tid; i < RP; i += NT) sX[i] = ldv(xlp, (static_cast<int64_t>(b) * H + h) * RP + i);
 #pragma unroll
-        for (int i = 0; i < kMaxEPT; ++i) {
+        for (int i = 0; i < EPT; ++i) {
             const int e = tid + NT * i;
-            if (i < EPT && e < E) {
-                const int k = e / P, p = e - k * P;
+            if (kk[i] >= 0) {
+                const int k = kk[i], p = pp[i];
                 sDU[(2 * k) * P + p] = bn * qn[i].x;
                 sDU[(2 * k + 1) * P + p] = bn * qn[i].y;
             }
@@ -374,25 +456,25 @@ __global__ __launch_bounds__(NT) void bwd_generic(BwdArgs a, int64_t ks) {
         __syncthreads();
         if (a.dbl) {
             float* dBo = a.per_head ? a.dbl_part : a.dbl;
-            for (int o = tid; o < R * N; o += NT) {
+            for (int o = tid; o < RN; o += NT) {
                 const int r = o / N, n = o - r * N;
                 float v = 0.f;
-                for (int p = 0; p < P; ++p) v += sDU[n * P + p] * sXp[r * P + p];
-                dBo[(static_cast<int64_t>(b) * GH + gh) * (R * N) + o] = v;
+                for (int p = 0; p < P; ++p) v += sDU[n * P + p] * sX[r * P + p];
+                dBo[(static_cast<int64_t>(b) * GH + gh) * RN + o] = v;
             }
         }
         if (a.dxl) {
-            for (int o = tid; o < R * P; o += NT) {
+            for (int o = tid; o < RP; o += NT) {
                 const int r = o / P, p = o - r * P;
                 float v = 0.f;
-                for (int n = 0; n < N; ++n) v += sBp[r * N + n] * sDU[n * P + p];
-                a.dxl[static_cast<size_t>(bh) * R * P + o] = v;
+                for (int n = 0; n < N; ++n) v += sB[r * N + n] * sDU[n * P + p];
+                a.dxl[static_cast<size_t>(bh) * RP + o] = v;
             }
         }
     } else if (a.dxl) {
-        for (int o = tid; o < R * P; o += NT) a.dxl[static_cast<size_t>(bh) * R * P + o] = 0.f;
+        for (int o = tid; o < RP; o += NT) a.dxl[static_cast<size_t>(bh) * RP + o] = 0.f;
     }
-    if (tid == 0) {
+    if (tid == NT - 64) {
         a.dA_part[bh] = dA_acc;
         a.dD_part[bh] = dD_acc;
     }
@@ -405,13 +487,22 @@ bool backward_generic_supported(const BwdShape& s) {
            (s.N / 2) * s.P <= bg::NT * bg::kMaxEPT && s.R >= 1 && s.R <= bg::kMaxR;
 }
 
+// Tokens staged per block: the most of 16, 8, 4, 2 whose LDS stays within 128 KB (a
+// workgroup holds a CU alone: its registers allow no second), else 1.
+int backward_generic_tb(const BwdShape& s) {
+    for (int tb = 16; tb > 1; tb /= 2)
+        if (static_cast<size_t>(bg::Lds(s.N, s.P, s.R, tb).total) * sizeof(float) <= 128 * 1024) return tb;
+    return 1;
+}
+
 size_t backward_generic_lds(const BwdShape& s) {
-    return static_cast<size_t>(bg::Lds(s.N, s.P, s.R).total) * sizeof(float);
+    return static_cast<size_t>(bg::Lds(s.N, s.P, s.R, backward_generic_tb(s)).total) * sizeof(float);
 }
 
 // Tokens per recompute segment: 16 while a state before every segment fits the
 // checkpoint budget (as for the fast kernel: 4 GiB, or M3_BACKWARD_CHECKPOINT_BYTES),
-// else about sqrt(L), which minimises checkpoints plus the segment scratch.  The
+// else sqrt(L) rounded up to a multiple of 16, which about minimises checkpoints plus the
+// segment scratch (a multiple of 16 so that staged blocks never straddle a segment).  The
 // segment length changes where states are kept, not how they are computed.
 int64_t backward_generic_ks(const BwdShape& s) {
     double budget = 4.0 * (1ull << 30);
@@ -421,7 +512,7 @@ int64_t backward_generic_ks(const BwdShape& s) {
     const int64_t ks = 16;
     if (per_state * static_cast<double>((L + ks - 1) / ks + ks + 1) <= budget) return ks;
     const int64_t r = static_cast<int64_t>(std::ceil(std::sqrt(static_cast<double>(L))));
-    return r > ks ? r : ks;
+    return ((r + ks - 1) / ks) * ks;
 }
 
 BwdLayout backward_generic_layout(const BwdShape& s) {
@@ -458,6 +549,26 @@ BwdLayout backward_generic_layout(const BwdShape& s) {
     return l;
 }
 
+template <typename T, int EPT>
+static hipError_t launch_generic_e(const BwdArgs& a, const BwdLayout& l, int tb, size_t lds, dim3 grid, hipStream_t st) {
+    const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&bg::bwd_generic<T, EPT>), lds);
+    if (e != hipSuccess) return e;
+    bg::bwd_generic<T, EPT><<<grid, bg::NT, lds, st>>>(a, l.ks, tb);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_generic_t(const BwdArgs& a, const BwdLayout& l, int ept, int tb, size_t lds, dim3 grid,
+                                   hipStream_t st) {
+    switch (ept) {
+        case 1: return launch_generic_e<T, 1>(a, l, tb, lds, grid, st);
+        case 2: return launch_generic_e<T, 2>(a, l, tb, lds, grid, st);
+        case 4: return launch_generic_e<T, 4>(a, l, tb, lds, grid, st);
+        case 8: return launch_generic_e<T, 8>(a, l, tb, lds, grid, st);
+        default: return launch_generic_e<T, 16>(a, l, tb, lds, grid, st);
+    }
+}
+
 hipError_t launch_backward_generic(BwdArgs a, const BwdLayout& l, hipStream_t st) {
     uint8_t* ws = static_cast<uint8_t*>(a.workspace);
     a.ckpt = reinterpret_cast<float*>(ws + l.ckpt);
@@ -474,17 +585,15 @@ hipError_t launch_backward_generic(BwdArgs a, const BwdLayout& l, hipStream_t st
     a.parts = 1;
     a.seg_per_part = l.seg_per_part;
     const BwdShape s{a.batch, a.L, a.H, a.G, a.N, a.P, a.R};
+    const int tb = backward_generic_tb(s);
     const size_t lds = backward_generic_lds(s);
     const dim3 grid(static_cast<unsigned>(a.batch * a.H));
     hipError_t e;
-    if (a.bf16) {
-        if ((e = ensure_dynamic_lds(reinterpret_cast<const void*>(&bg::bwd_generic<bf16_t>), lds)) != hipSuccess) return e;
-        bg::bwd_generic<bf16_t><<<grid, bg::NT, lds, st>>>(a, l.ks);
-    } else {
-        if ((e = ensure_dynamic_lds(reinterpret_cast<const void*>(&bg::bwd_generic<float>), lds)) != hipSuccess) return e;
-        bg::bwd_generic<float><<<grid, bg::NT, lds, st>>>(a, l.ks);
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int pairs = (a.N / 2) * a.P;
+    const int ept = pairs <= bg::NT ? 1 : pairs <= 2 * bg::NT ? 2 : pairs <= 4 * bg::NT ? 4 : pairs <= 8 * bg::NT ? 8 : 16;
+    if ((e = a.bf16 ? launch_generic_t<bf16_t>(a, l, ept, tb, lds, grid, st)
+                    : launch_generic_t<float>(a, l, ept, tb, lds, grid, st)) != hipSuccess)
+        return e;
     return launch_backward_sums(a, l, st);
 }
 

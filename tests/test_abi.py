@@ -450,7 +450,8 @@ def test_serial_prefill_needs_no_workspace(lib):
 def test_generic_backward_workspace(lib, monkeypatch):
     """Off the fast kernel's shape the backward keeps the state before every 16-token segment
     plus one segment's 17 states per (b, h) while those fit the checkpoint budget, else
-    segments of ceil(sqrt(L)) tokens (fewer bytes, the same gradients); per-head copies of
+    segments of ceil(sqrt(L)) tokens rounded up to a multiple of 16 (fewer bytes, the same
+    gradients); per-head copies of
     the group-shared gradients are added when H > G."""
     import math
     monkeypatch.delenv("M3_BACKWARD_CHECKPOINT_BYTES", raising=False)
@@ -461,7 +462,7 @@ def test_generic_backward_workspace(lib, monkeypatch):
     assert w16 >= b * H * (math.ceil(L / 16) + 17) * state
     assert w16 < b * H * (math.ceil(L / 16) + 17) * state + 4 * 256 + 2 * b * H * 4 + 1024
     monkeypatch.setenv("M3_BACKWARD_CHECKPOINT_BYTES", "1")
-    ks = math.ceil(math.sqrt(L))
+    ks = 16 * math.ceil(math.ceil(math.sqrt(L)) / 16)
     wsq = _bwd_ws(lib, d1)
     assert wsq >= b * H * (math.ceil(L / ks) + ks + 1) * state and wsq < w16
     monkeypatch.delenv("M3_BACKWARD_CHECKPOINT_BYTES")

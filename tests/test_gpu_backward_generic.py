@@ -53,7 +53,8 @@ CASES = [
     (1, 256, 4, 1, 16, 16, 1, "fp32", False, True),    # the small fp32 SISO layer's shape
     (2, 37, 4, 2, 12, 24, 3, "fp32", True, True),
     (1, 50, 2, 2, 32, 64, 8, "bf16", True, False),
-    (2, 33, 2, 1, 128, 64, 2, "bf16", False, True),    # 4096 element pairs: 16 per thread
+    (2, 33, 2, 1, 128, 64, 2, "bf16", False, True),    # 4096 element pairs: 16 per thread; 8-token blocks
+    (1, 21, 2, 1, 128, 64, 8, "fp32", True, True),     # 2-token blocks (LDS)
     (1, 1, 2, 1, 8, 4, 1, "fp32", True, True),
     (1, 100, 2, 1, 4, 2, 5, "fp32", False, False),     # N = 2: one rotation pair
     (1, 40, 2, 1, 256, 32, 1, "bf16", True, True),     # P = 256
