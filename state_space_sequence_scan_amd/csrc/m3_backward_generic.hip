@@ -22,9 +22,9 @@
 // shared gradients are written per head when H > G and summed afterwards, as in the fast
 // kernel.  The inputs of up to 16 tokens are staged into LDS at once (as many as 128 KB
 // of LDS holds beside the sums' buffers).  The sums take two barriers per token in the
-// reverse sweep; a barrier also waits for the workgroup's outstanding global stores, so
-// each token's gradients are kept in LDS and the block's are written out together.  This
-// path is for the small and unusual shapes; N = 128, P = 64 run the fast kernel.
+// reverse sweep; each token's gradients are collected in LDS and a block's are written out
+// together by the whole workgroup, in coalesced runs.  This path is for the small and
+// unusual shapes; N = 128, P = 64 run the fast kernel.
 #include <cmath>
 #include <cstdlib>
 
