@@ -332,33 +332,34 @@ __global__ __launch_bounds__(kThreads) void prefill_generic(
             state_store(h_out, static_cast<size_t>(bh) * N * P + idx, S[idx], state_bf16);
 }
 
-// state_out carry: B and X of the last token (or the incoming carry when L == 0).
-template <typename T>
-__global__ void carry_out(const T* __restrict__ x, const T* __restrict__ B,
-                          const T* __restrict__ bl_in, const T* __restrict__ xl_in,
-                          T* __restrict__ bl_out, T* __restrict__ xl_out, int64_t batch,
-                          int64_t Lmax, int H, int G, int N, int P, int R, const int64_t* __restrict__ cu,
-                          int64_t Tt) {
-    const int64_t nb = batch * G * R * N, nx = batch * H * R * P;
-    for (int64_t idx = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; idx < nb + nx;
-         idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        if (idx < nb) {
-            if (!bl_out) continue;
-            const int64_t bb = idx / (G * R * N), rem = idx - bb * G * R * N;
-            const SeqSpan sp = seq_span(cu, bb, Lmax, Tt);
-            T v{};
-            if (sp.len > 0) v = B[(sp.start + sp.len - 1) * G * R * N + rem];
-            else if (bl_in && xl_in) v = bl_in[idx];
-            bl_out[idx] = v;
-        } else {
-            if (!xl_out) continue;
-            const int64_t i2 = idx - nb;
-            const int64_t bb = i2 / (H * R * P), rem = i2 - bb * H * R * P;
-            const SeqSpan sp = seq_span(cu, bb, Lmax, Tt);
-            T v{};
-            if (sp.len > 0) v = x[(sp.start + sp.len - 1) * H * R * P + rem];
-            else if (bl_in && xl_in) v = xl_in[i2];
-            xl_out[i2] = v;
+// state_out carry: B and X of the last token (or the incoming carry when L == 0).  The grid's
+// y index walks the sequences (the span is found once per workgroup), its x index the
+// sequence's G R N carried B values followed by its H R P carried X values, in units of U
+// (16 bytes when every row and pointer is 16-byte aligned, else one element).
+template <typename T, typename U>
+__global__ __launch_bounds__(256) void carry_out(const T* __restrict__ x, const T* __restrict__ B,
+                                                 const T* __restrict__ bl_in, const T* __restrict__ xl_in,
+                                                 T* __restrict__ bl_out, T* __restrict__ xl_out, int64_t batch,
+                                                 int64_t Lmax, int H, int G, int N, int P, int R,
+                                                 const int64_t* __restrict__ cu, int64_t Tt) {
+    constexpr int E = static_cast<int>(sizeof(U) / sizeof(T));   // elements per unit
+    const int64_t nb = static_cast<int64_t>(G) * R * N, nx = static_cast<int64_t>(H) * R * P;
+    const int64_t ub = nb / E, ux = nx / E;
+    for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
+        const SeqSpan sp = seq_span(cu, b, Lmax, Tt);
+        const bool keep = bl_in && xl_in;   // an empty sequence passes the incoming carry on
+        const U* sb = reinterpret_cast<const U*>(sp.len > 0 ? B + (sp.start + sp.len - 1) * nb
+                                                            : (keep ? bl_in + b * nb : nullptr));
+        const U* sx = reinterpret_cast<const U*>(sp.len > 0 ? x + (sp.start + sp.len - 1) * nx
+                                                            : (keep ? xl_in + b * nx : nullptr));
+        U* db = reinterpret_cast<U*>(bl_out ? bl_out + b * nb : nullptr);
+        U* dx = reinterpret_cast<U*>(xl_out ? xl_out + b * nx : nullptr);
+        for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < ub + ux; i += static_cast<int64_t>(gridDim.x) * 256) {
+            if (i < ub) {
+                if (db) db[i] = sb ? sb[i] : U{};
+            } else if (dx) {
+                dx[i - ub] = sx ? sx[i - ub] : U{};
+            }
         }
     }
 }
@@ -434,11 +435,18 @@ hipError_t launch_prefill_generic(const PrefillArgs& a, hipStream_t st) {
 
 template <typename T>
 static hipError_t launch_carry_t(const PrefillArgs& a, hipStream_t st) {
-    const int64_t n = a.batch * (static_cast<int64_t>(a.G) * a.R * a.N + static_cast<int64_t>(a.H) * a.R * a.P);
-    int64_t blocks = (n + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(carry_out<T>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+    const int64_t nb = static_cast<int64_t>(a.G) * a.R * a.N, nx = static_cast<int64_t>(a.H) * a.R * a.P;
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    const bool vec = (nb * sizeof(T)) % 16 == 0 && (nx * sizeof(T)) % 16 == 0 && al16(a.x) && al16(a.B) &&
+                     al16(a.bl_in) && al16(a.xl_in) && al16(a.bl_out) && al16(a.xl_out);
+    const int64_t units = vec ? (nb + nx) * static_cast<int64_t>(sizeof(T)) / 16 : nb + nx;
+    int64_t bx = (units + 255) / 256, by = a.batch;
+    if (bx > 64) bx = 64;
+    if (by > 65535) by = 65535;
+    if (bx < 1) bx = 1;
+    if (by < 1) by = 1;
+    auto kern = vec ? carry_out<T, uint4> : carry_out<T, T>;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(bx), static_cast<unsigned>(by)), dim3(256), 0, st,
                        static_cast<const T*>(a.x), static_cast<const T*>(a.B),
                        static_cast<const T*>(a.bl_in), static_cast<const T*>(a.xl_in),
                        static_cast<T*>(a.bl_out), static_cast<T*>(a.xl_out), a.batch, a.L, a.H,
