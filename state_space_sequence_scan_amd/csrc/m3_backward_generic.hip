@@ -12,10 +12,12 @@
 //
 // One workgroup of 256 threads per (b, h); thread t owns the element pairs
 // e = t + 256 i (rotation pair k = e / P, column p = e % P) of h and of the adjoint, in
-// registers, for the whole sequence.  A forward sweep keeps the state before every
-// segment of `ks` tokens in the workspace; the reverse sweep takes the segments last to
-// first, recomputes a segment's states into a per-(b, h) scratch (each thread its own
-// pairs, so no synchronisation is needed for them), and walks its tokens backwards.
+// registers, for the whole sequence.  While they fit the checkpoint budget, the forward
+// sweep keeps every state in the workspace and the reverse sweep reads them back; else it
+// keeps the state before every segment of `ks` tokens, and the reverse sweep takes the
+// segments last to first, recomputes a segment's states into a per-(b, h) scratch (each
+// thread its own pairs, so no synchronisation is needed for them) and walks its tokens
+// backwards.
 // Per token, the sums over columns (dB, dC, dtheta), over state rows (dX) and over the
 // whole state (dalpha, dbeta, dgamma, dD) are taken from LDS copies of h_t, dU_t and the
 // per-pair angle terms in a fixed order, so results do not depend on scheduling.  Group-
@@ -80,6 +82,14 @@ __global__ __launch_bounds__(NT) void bwd_generic(BwdArgs a, int64_t ks, int TB)
     extern __shared__ __align__(16) float lds[];
     const int N = a.N, P = a.P, R = a.R, KP = N / 2, E = KP * P, RN = R * N, RP = R * P;
     const float invN = 1.f / N, invP = 1.f / P;   // for the task indices (fdiv)
+    // the per-token sums as tasks of 4 lanes each, each kind from a multiple of 16 tasks (a
+    // wave): dC (RN), dB (RN), dtheta (KP), dX (RP); ntask: the tasks' count (and the offset
+    // of the scalars in a token's outputs).  The whole-state sums go to the wave where the
+    // dtheta tasks (the fewest) start.
+    auto up16 = [](int v) { return (v + 15) & ~15; };
+    const int t1 = up16(RN), t2 = t1 + up16(RN), t3 = t2 + up16(KP), tspan = t3 + up16(RP);
+    const int ntask = 2 * RN + KP + RP;
+    const int sw = ((t2 * 4) / 64) % (NT / 64);   // the scalar wave
     const Lds lay(N, P, R, TB);
     float* sB = lds + lay.b;
     float* sX = lds + lay.x;
@@ -242,12 +252,17 @@ __global__ __launch_bounds__(NT) void bwd_generic(BwdArgs a, int64_t ks, int TB)
             hs[i].y = state_load(a.h0, base + static_cast<size_t>(2 * k + 1) * P + p, a.state_bf16);
         }
     }
+    // With one segment for the longest sequence (ks >= a.L) the scratch holds every state of
+    // the sequence: the sweep stores them there and the reverse sweep recomputes nothing.
+    const bool keep_all = ks >= a.L;
+    if (keep_all) store(scr, hs);
     for (int64_t t0 = 0; t0 < L; t0 += TB) {
         const int nt = static_cast<int>(L - t0 < TB ? L - t0 : TB);
         stage(t0, nt, false);
         for (int j = 0; j < nt; ++j) {
-            if ((t0 + j) % ks == 0) store(ck + ((t0 + j) / ks) * E, hs);
+            if (!keep_all && (t0 + j) % ks == 0) store(ck + ((t0 + j) / ks) * E, hs);
             fwd_step(j, hs);
+            if (keep_all) store(scr + (t0 + j + 1) * E, hs);
         }
     }
 
@@ -266,12 +281,12 @@ __global__ __launch_bounds__(NT) void bwd_generic(BwdArgs a, int64_t ks, int TB)
         }
     }
     float an = 1.f, bn = 0.f;
-    float dA_acc = 0.f, dD_acc = 0.f;   // thread NT - 64
+    float dA_acc = 0.f, dD_acc = 0.f;   // thread sw * 64
 
     for (int64_t s = nseg - 1; s >= 0; --s) {
         const int64_t t0 = s * ks;
         const int len = static_cast<int>(L - t0 < ks ? L - t0 : ks);
-        {   // h_{t0-1} .. h_{t0+len-1} into the scratch
+        if (!keep_all) {   // h_{t0-1} .. h_{t0+len-1} into the scratch
             float2 hr[EPT];
             load(ck + s * E, hr);
             store(scr, hr);
@@ -347,31 +362,38 @@ __global__ __launch_bounds__(NT) void bwd_generic(BwdArgs a, int64_t ks, int TB)
                 //   dB[r][n] = sum_p dU[n][p] X[r][p]        (RN)
                 //   dtheta[k] = sum_p (angle term)[k][p]     (KP; times a stride-0 one)
                 //   dX[r][p] = sum_n B[r][n] dU[n][p]        (RP; plus D dy afterwards)
-                const int ntask = 2 * RN + KP + RP;
-                for (int o = tid; o < ntask; o += NT) {
+                // A wave runs one kind; the 4 lanes of a task take every 4th term and add
+                // their parts by two DPP moves within the quad.
+                const int sub = tid & 3;
+                for (int o = tid >> 2; o < tspan; o += NT / 4) {
+                    const int kind = o < t1 ? 0 : o < t2 ? 1 : o < t3 ? 2 : 3;
+                    const int q = o - (kind == 0 ? 0 : kind == 1 ? t1 : kind == 2 ? t2 : t3);
+                    if (q >= (kind < 2 ? RN : kind == 2 ? KP : RP)) continue;   // whole quads
                     const float* pa;
                     const float* pb;
-                    int sa = 1, sb = 1, m = P, kind;
-                    if (o < RN) {
-                        const int r = fdiv(o, invN), n = o - r * N;
-                        pa = sHL + n * P; pb = Dc + r * P; kind = 0;
-                    } else if (o < 2 * RN) {
-                        const int r = fdiv(o - RN, invN), n = (o - RN) - r * N;
-                        pa = sDU + n * P; pb = Xc + r * P; kind = 1;
-                    } else if (o < 2 * RN + KP) {
-                        pa = sTh + (o - 2 * RN) * P; pb = &kOne; sb = 0; kind = 2;
+                    int sb = 1, m = P;
+                    if (kind < 2) {
+                        const int r = fdiv(q, invN), n = q - r * N;
+                        pa = (kind == 0 ? sHL : sDU) + n * P;
+                        pb = (kind == 0 ? Dc : Xc) + r * P;
+                    } else if (kind == 2) {
+                        pa = sTh + q * P; pb = &kOne; sb = 0;
                     } else {
-                        const int q = o - 2 * RN - KP, r = fdiv(q, invP), p = q - r * P;
-                        pa = Bc + r * N; pb = sDU + p; sb = P; m = N; kind = 3;
+                        const int r = fdiv(q, invP), p = q - r * P;
+                        pa = Bc + r * N; pb = sDU + p; sb = P; m = N;
                     }
                     float v = 0.f;
 #pragma unroll 4
-                    for (int i = 0; i < m; ++i) v += pa[i * sa] * pb[i * sb];
-                    if (kind == 3) v += Dh * Dc[o - 2 * RN - KP];
-                    sOut[j * OW + o] = v;   // in the order dC, dB, dtheta, dx
+                    for (int i = sub; i < m; i += 4) v += pa[i] * pb[i * sb];
+                    v += dpp_move<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+                    v += dpp_move<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+                    if (sub == 0) {
+                        if (kind == 3) v += Dh * Dc[q];
+                        sOut[j * OW + (kind == 0 ? 0 : kind == 1 ? RN : kind == 2 ? 2 * RN : 2 * RN + KP) + q] = v;
+                    }
                 }
-                // whole-state sums, in a fixed order by the last wave
-                if (tid >= NT - 64) {
+                // whole-state sums, in a fixed order by the scalar wave
+                if ((tid >> 6) == sw) {
                     float sa = 0.f, sb = 0.f, sg = 0.f, sd = 0.f;
                     for (int w = 0; w < NT / 64; ++w) {
                         sa += sRed[w * 64 + lane];
@@ -383,7 +405,7 @@ __global__ __launch_bounds__(NT) void bwd_generic(BwdArgs a, int64_t ks, int TB)
                     sb = wave_sum(sb);
                     sg = wave_sum(sg);
                     sd = wave_sum(sd);
-                    if (tid == NT - 64) {
+                    if (tid == sw * 64) {
                         const float dtv = sSc[4 * j], lv = sSc[4 * j + 1], av = sSc[4 * j + 2];
                         float* so = sOut + j * OW + ntask;
                         so[0] = sa * av * al + sb * (1.f - lv) * (al + dtv * av * al) + sg * lv;
@@ -474,7 +496,7 @@ __global__ __launch_bounds__(NT) void bwd_generic(BwdArgs a, int64_t ks, int TB)
     } else if (a.dxl) {
         for (int o = tid; o < RP; o += NT) a.dxl[static_cast<size_t>(bh) * RP + o] = 0.f;
     }
-    if (tid == NT - 64) {
+    if (tid == sw * 64) {
         a.dA_part[bh] = dA_acc;
         a.dD_part[bh] = dD_acc;
     }
@@ -499,17 +521,20 @@ size_t backward_generic_lds(const BwdShape& s) {
     return static_cast<size_t>(bg::Lds(s.N, s.P, s.R, backward_generic_tb(s)).total) * sizeof(float);
 }
 
-// Tokens per recompute segment: 16 while a state before every segment fits the
-// checkpoint budget (as for the fast kernel: 4 GiB, or M3_BACKWARD_CHECKPOINT_BYTES),
-// else sqrt(L) rounded up to a multiple of 16, which about minimises checkpoints plus the
-// segment scratch (a multiple of 16 so that staged blocks never straddle a segment).  The
-// segment length changes where states are kept, not how they are computed.
+// Tokens per recompute segment: the whole sequence (every state kept, nothing recomputed)
+// while its L + 2 states per (b, h) fit the checkpoint budget (as for the fast kernel: 4 GiB,
+// or M3_BACKWARD_CHECKPOINT_BYTES); else 16 while a state before every segment fits it; else
+// sqrt(L); each rounded up to a multiple of 16, so that staged blocks never straddle a
+// segment (and the two last choices about minimise checkpoints plus the segment scratch).
+// The segment length changes where states are kept, not how they are computed.
 int64_t backward_generic_ks(const BwdShape& s) {
     double budget = 4.0 * (1ull << 30);
     if (const char* e = std::getenv("M3_BACKWARD_CHECKPOINT_BYTES")) budget = std::strtod(e, nullptr);
     const int64_t L = s.L > 0 ? s.L : 1;
     const double per_state = static_cast<double>(s.batch) * s.H * s.N * s.P * 4;
     const int64_t ks = 16;
+    // every state kept (one segment): no recompute pass
+    if (per_state * static_cast<double>(L + 2) <= budget) return ((L + ks - 1) / ks) * ks;
     if (per_state * static_cast<double>((L + ks - 1) / ks + ks + 1) <= budget) return ks;
     const int64_t r = static_cast<int64_t>(std::ceil(std::sqrt(static_cast<double>(L))));
     return ((r + ks - 1) / ks) * ks;

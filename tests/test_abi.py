@@ -448,24 +448,30 @@ def test_serial_prefill_needs_no_workspace(lib):
 
 
 def test_generic_backward_workspace(lib, monkeypatch):
-    """Off the fast kernel's shape the backward keeps the state before every 16-token segment
-    plus one segment's 17 states per (b, h) while those fit the checkpoint budget, else
-    segments of ceil(sqrt(L)) tokens rounded up to a multiple of 16 (fewer bytes, the same
-    gradients); per-head copies of
-    the group-shared gradients are added when H > G."""
+    """Off the fast kernel's shape the backward keeps every state of the sequence (one
+    segment: L rounded up to 16, plus 2 states per (b, h)) while those fit the checkpoint
+    budget; else the state before every 16-token segment plus one segment's 17 states; else
+    segments of ceil(sqrt(L)) tokens rounded up to a multiple of 16 (fewer bytes each time,
+    the same gradients); per-head copies of the group-shared gradients are added when H > G."""
     import math
     monkeypatch.delenv("M3_BACKWARD_CHECKPOINT_BYTES", raising=False)
     b, H, N, P, R, L = 2, 4, 24, 12, 3, 1000
     state = N * P * 4
+    slack = 4 * 256 + 2 * b * H * 4 + 1024
     d1 = _dims(batch=b, nheads=H, ngroups=H, headdim=P, dstate=N, rank=R, seqlen=L)
+    wall = _bwd_ws(lib, d1)
+    keep = 16 * math.ceil(L / 16) + 2
+    assert b * H * keep * state <= wall < b * H * keep * state + slack
+    # below every state, above 16-token segments
+    monkeypatch.setenv("M3_BACKWARD_CHECKPOINT_BYTES", str(2 << 20))
     w16 = _bwd_ws(lib, d1)
-    assert w16 >= b * H * (math.ceil(L / 16) + 17) * state
-    assert w16 < b * H * (math.ceil(L / 16) + 17) * state + 4 * 256 + 2 * b * H * 4 + 1024
+    seg16 = math.ceil(L / 16) + 17
+    assert b * H * seg16 * state <= w16 < b * H * seg16 * state + slack
     monkeypatch.setenv("M3_BACKWARD_CHECKPOINT_BYTES", "1")
     ks = 16 * math.ceil(math.ceil(math.sqrt(L)) / 16)
     wsq = _bwd_ws(lib, d1)
-    assert wsq >= b * H * (math.ceil(L / ks) + ks + 1) * state and wsq < w16
+    assert wsq >= b * H * (math.ceil(L / ks) + ks + 1) * state and wsq < w16 < wall
     monkeypatch.delenv("M3_BACKWARD_CHECKPOINT_BYTES")
     d2 = _dims(batch=b, nheads=H, ngroups=1, headdim=P, dstate=N, rank=R, seqlen=L)
     per_head = b * L * H * (2 * R * N + N // 2) * 4 + b * H * R * N * 4
-    assert _bwd_ws(lib, d2) >= w16 + per_head
+    assert _bwd_ws(lib, d2) >= wall + per_head

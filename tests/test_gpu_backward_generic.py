@@ -100,24 +100,29 @@ def test_generic_backward_empty_sequence():
 
 
 def test_generic_backward_is_deterministic_and_budget_independent(monkeypatch):
-    """Two calls give the same bits, and so does a segment length forced to about sqrt(L)
-    by a one-byte checkpoint budget (the states are recomputed by the same steps)."""
-    b, L, H, G, P, N, R = 2, 1000, 2, 1, 16, 32, 2   # 16-token segments: 80 states; 32-token: 65
+    """Two calls give the same bits, and so do 16-token segments and segments of about
+    sqrt(L) tokens, forced by smaller checkpoint budgets, against every state kept (the
+    default here): the recomputed states come from the same steps."""
+    b, L, H, G, P, N, R = 2, 1000, 2, 1, 16, 32, 2   # every state: 1010 states; 16-token segments: 80; 32: 65
     d, dy, dh, st = _inputs(b, L, H, G, P, N, R, "fp32", 61, True, True)
     monkeypatch.delenv("M3_BACKWARD_CHECKPOINT_BYTES", raising=False)
     dims = m3scan.make_dims(b, L, H, G, P, N, R, 1, 0)
     w16 = m3scan.backward_workspace_size(dims)
     g1 = m3scan.backward(*[d[k] for k in NAMES], dy, dh_out=dh, state_in=st)
     g2 = m3scan.backward(*[d[k] for k in NAMES], dy, dh_out=dh, state_in=st)
+    monkeypatch.setenv("M3_BACKWARD_CHECKPOINT_BYTES", str(4 << 20))
+    wseg = m3scan.backward_workspace_size(dims)
+    g4 = m3scan.backward(*[d[k] for k in NAMES], dy, dh_out=dh, state_in=st)
     monkeypatch.setenv("M3_BACKWARD_CHECKPOINT_BYTES", "1")
     wsq = m3scan.backward_workspace_size(dims)
     g3 = m3scan.backward(*[d[k] for k in NAMES], dy, dh_out=dh, state_in=st)
     torch.cuda.synchronize()
-    say(f"generic backward workspace: {w16} bytes (16-token segments), {wsq} (sqrt(L))")
-    assert wsq < w16
+    say(f"generic backward workspace: {w16} bytes (every state), {wseg} (16-token segments), {wsq} (sqrt(L))")
+    assert wsq < wseg < w16
     for k in g1:
         assert torch.equal(g1[k], g2[k]), k
         assert torch.equal(g1[k], g3[k]), k
+        assert torch.equal(g1[k], g4[k]), k
 
 
 @pytest.mark.parametrize("io", ["fp32", "bf16"])
