@@ -210,6 +210,90 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
             sAt[tid] = t >= 0 ? (a.At ? a.At[soff(t)] : Ah) : 0.f;
         }
     };
+    // The staging of the forward sweeps (B, X and theta; C and dy are not read there) split
+    // in two: fetch issues a segment's loads into registers, commit writes them to the
+    // slots.  A sweep fetches the next segment before stepping through the current one, so
+    // the loads are in flight during its steps.  Every load is unconditional (an index
+    // clamped into the sequence; `use` says whether the value counts), so the compiler has
+    // no branch join at which to wait for it.
+    constexpr int kE = 16 / static_cast<int>(sizeof(T));
+    constexpr int kuB = R * N / kE, kuX = R * P / kE, kuT = (N / 2) / 4;
+    constexpr int kUF = kuB + kuX + kuT;                   // units per token
+    constexpr int kUnits = (kUF * (KS + 1) + NT - 1) / NT; // units per thread
+    struct Pref {
+        uint4 v[kUnits];
+        unsigned use;     // bit e: unit e holds a value (else zeros are staged)
+        float dt, lam, at;
+    };
+    auto fetch = [&](int64_t t0, int len, Pref& pf) {
+        const int total = kUF * (len + 1);
+        pf.use = 0;
+#pragma unroll
+        for (int e = 0; e < kUnits; ++e) {
+            const int u = tid + NT * e;
+            const int uc = u < total ? u : 0;
+            const int k = uc / kUF, w = uc - k * kUF;
+            const int64_t t = t0 - 1 + k;
+            const int64_t tc = t >= 0 ? t : 0;   // a token of this sequence (len >= 1)
+            const bool from_carry = t < 0 && carry;
+            const uint4* src;
+            bool use;
+            if (w < kuB) {
+                const int o = w * kE;
+                src = reinterpret_cast<const uint4*>(from_carry ? blp + (static_cast<int64_t>(b) * G + g) * (R * N) + o
+                                                                : Bm + ((tb + tc) * G + g) * (R * N) + o);
+                use = t >= 0 || carry;
+            } else if (w < kuB + kuX) {
+                const int o = (w - kuB) * kE;
+                src = reinterpret_cast<const uint4*>(from_carry ? xlp + (static_cast<int64_t>(b) * H + h) * (R * P) + o
+                                                                : x + ((tb + tc) * H + h) * (R * P) + o);
+                use = t >= 0 || carry;
+            } else {
+                const int o = (w - kuB - kuX) * 4;
+                src = reinterpret_cast<const uint4*>(a.theta + ((tb + tc) * G + g) * (N / 2) + o);
+                use = t >= 0;
+            }
+            pf.v[e] = *src;
+            if (use && u < total) pf.use |= 1u << e;
+        }
+        const int64_t t = t0 - 1 + (tid <= len ? tid : 0);
+        const int64_t tc = t >= 0 ? t : 0;
+        pf.dt = a.dt[soff(tc)];
+        pf.lam = a.lam[soff(tc)];
+        pf.at = a.At ? a.At[soff(tc)] : Ah;
+        if (t < 0) pf.dt = pf.lam = pf.at = 0.f;
+    };
+    auto commit = [&](int len, const Pref& pf) {
+        const int total = kUF * (len + 1);
+#pragma unroll
+        for (int e = 0; e < kUnits; ++e) {
+            const int u = tid + NT * e;
+            if (u >= total) continue;
+            const int k = u / kUF, w = u - k * kUF;
+            const uint4 v = (pf.use >> e) & 1u ? pf.v[e] : uint4{0u, 0u, 0u, 0u};
+            void* dst;
+            if (w < kuB) {
+                dst = &sB[k][w * kE];
+            } else if (w < kuB + kuX) {
+                dst = &sX[k][(w - kuB) * kE];
+            } else {
+                const int o = (w - kuB - kuX) * 4;
+                dst = &sTh[k][o];
+                const float th[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+                float cs4[4], sn4[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sincos_acc(th[q], &sn4[q], &cs4[q]);
+                *reinterpret_cast<float4*>(&sRot[k][2 * o]) = float4{cs4[0], sn4[0], cs4[1], sn4[1]};
+                *reinterpret_cast<float4*>(&sRot[k][2 * o + 4]) = float4{cs4[2], sn4[2], cs4[3], sn4[3]};
+            }
+            *reinterpret_cast<uint4*>(dst) = v;
+        }
+        if (tid <= len) {
+            sDt[tid] = pf.dt;
+            sLam[tid] = pf.lam;
+            sAt[tid] = pf.at;
+        }
+    };
     auto slot_bx = [&](int k, float (&Bv)[R][4], float (&Xv)[R][4]) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -281,12 +365,15 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) hs[i][j] = 0.f;
         double sum = 0.0;   // thread i < N/2: theta of pair i; thread N/2: dt * A (as the steps round it)
+        auto seg_len = [&](int64_t s) { return static_cast<int>(L - s * KS < KS ? L - s * KS : KS); };
+        Pref pf;
+        if (s_lo < s_hi) fetch(s_lo * KS, seg_len(s_lo), pf);
         for (int64_t s = s_lo; s < s_hi; ++s) {
-            const int64_t t0 = s * KS;
-            const int len = static_cast<int>(L - t0 < KS ? L - t0 : KS);
+            const int len = seg_len(s);
             __syncthreads();
-            stage(t0, len, false);
+            commit(len, pf);
             __syncthreads();
+            if (s + 1 < s_hi) fetch((s + 1) * KS, seg_len(s + 1), pf);   // in flight during the steps
             for (int j = 1; j <= len; ++j) fwd_step(j, hs);
             if (tid < N / 2) {
                 for (int j = 1; j <= len; ++j) sum += static_cast<double>(sTh[j][tid]);
@@ -353,13 +440,16 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
     part_start(hc);
     // forward steps of segments s0 .. s1-1 on hs; with `dst`, the state after segment s is
     // stored at dst[(s - s0 - 1 + off) ...] as described at the call
+    auto seg_len = [&](int64_t s) { return static_cast<int>(L - s * KS < KS ? L - s * KS : KS); };
     auto sweep = [&](float (&hs)[4][4], int64_t s0, int64_t s1, auto&& after) {
+        Pref pf;
+        if (s0 < s1) fetch(s0 * KS, seg_len(s0), pf);
         for (int64_t s = s0; s < s1; ++s) {
-            const int64_t t0 = s * KS;
-            const int len = static_cast<int>(L - t0 < KS ? L - t0 : KS);
+            const int len = seg_len(s);
             __syncthreads();   // the previous segment's slots are read
-            stage(t0, len, false);
+            commit(len, pf);
             __syncthreads();
+            if (s + 1 < s1) fetch((s + 1) * KS, seg_len(s + 1), pf);   // in flight during the steps
             for (int j = 1; j <= len; ++j) fwd_step(j, hs);
             after(s, hs);
         }
