@@ -282,21 +282,28 @@ typedef struct {
     float* dx_last;  /* (batch, H, R, P): of state_in->x_last (zero without a carry) */
 } m3_grads;
 
-/* Bytes of device workspace m3_backward needs for these dims: checkpointed states
- * (N * P * 4 bytes each) of every (b, h) -- at N = 128, P = 64 one after every
- * third token while those fit in a budget of 4 GiB, else two levels of about
- * sqrt(L / 3) states each (one after every group of segments, and one group's
- * states recomputed into a scratch), for one more forward pass; at other shapes
- * one before every 16-token segment plus one segment's 17 states, or segments of
- * ceil(sqrt(L)) tokens rounded up to a multiple of 16 above the budget -- plus,
- * when H > G, per-head copies of
- * the group-shared gradients, plus, when the sequences are split
- * (m3_backward_parts), two N * P states per piece.  The environment variable
- * M3_BACKWARD_CHECKPOINT_BYTES, read at each call, replaces the budget (a
- * caller short of memory lowers it); the gradients are the same bits for any
- * budget.  Errors: M3_ERR_INVALID_ARG for bad dims or a NULL `bytes`;
+/* Bytes of device workspace m3_backward needs for these dims with a checkpoint
+ * budget of 4 GiB (m3_backward_workspace_size_budget with checkpoint_bytes =
+ * 2^32).  Errors: M3_ERR_INVALID_ARG for bad dims or a NULL `bytes`;
  * M3_ERR_UNSUPPORTED for shapes m3_backward does not handle. */
 m3_status m3_backward_workspace_size(const m3_dims* dims, size_t* bytes);
+
+/* Bytes of device workspace m3_backward needs for these dims when the states it
+ * keeps for the reverse sweep may take at most `checkpoint_bytes` (a caller short
+ * of memory passes less than the default 4 GiB, one with memory to spare more).
+ * The states (N * P * 4 bytes each, per (b, h)) are kept at one of a few levels,
+ * the first whose states fit the budget, else the level with the smallest
+ * workspace: at dstate 128, headdim 64 (level 0) one after every third token,
+ * (level 1) two levels of about sqrt(L / 3) states each (one after every group of
+ * segments, and one group's states recomputed into a scratch) for one more
+ * forward pass; at other shapes (level 0) every state, (level 1) one before every
+ * 16-token segment plus one segment's 17 states, (level 2) segments of
+ * ceil(sqrt(L)) tokens rounded up to a multiple of 16.  The workspace also holds,
+ * when H > G, per-head copies of the group-shared gradients and, when the
+ * sequences are split (m3_backward_parts), two N * P states per piece.  The
+ * gradients are the same bits at every level.  Errors as
+ * m3_backward_workspace_size. */
+m3_status m3_backward_workspace_size_budget(const m3_dims* dims, size_t checkpoint_bytes, size_t* bytes);
 
 /* How m3_backward divides the work for these dims: each (b, h) sequence is cut
  * into *parts pieces of *tokens_per_part tokens (the last may be shorter) that are
@@ -328,9 +335,13 @@ m3_status m3_backward_parts(const m3_dims* dims, int32_t* parts, int64_t* tokens
  * dy:        (batch, L, H, R, P) in the io dtype.
  * dh_out:    NULL (zero) or (batch, H, N, P) fp32.
  * grads:     every pointer of m3_grads except dh0, db_last, dx_last non-NULL.
- * workspace: at least m3_backward_workspace_size bytes; contents ignored.
+ * workspace: workspace_bytes of device memory, contents ignored: at least what
+ *            m3_backward_workspace_size or m3_backward_workspace_size_budget
+ *            returns for these dims; the call keeps states at the first level
+ *            (the fewest recomputed) whose workspace fits workspace_bytes.
  * Errors:    M3_ERR_INVALID_ARG (NULL pointers, bad dims), M3_ERR_UNSUPPORTED,
- *            M3_ERR_WORKSPACE, M3_ERR_HIP -- all before any launch except the last.
+ *            M3_ERR_WORKSPACE (no level fits workspace_bytes), M3_ERR_HIP -- all
+ *            before any launch except the last.
  */
 m3_status m3_backward(const m3_dims* dims, const void* x, const float* dt, const float* A,
                       const float* lambda, const float* theta, const void* B, const void* C,

@@ -408,20 +408,54 @@ m3::BwdShape bwd_shape(const m3_dims* d) {
 bool bwd_any_supported(const m3::BwdShape& s) {
     return m3::backward_supported(s) || m3::backward_generic_supported(s);
 }
-m3::BwdLayout bwd_any_layout(const m3::BwdShape& s) {
-    return m3::backward_supported(s) ? m3::backward_layout(s) : m3::backward_generic_layout(s);
+int bwd_levels(const m3::BwdShape& s) {
+    return m3::backward_supported(s) ? m3::kBackwardLevels : m3::kBackwardGenericLevels;
 }
+m3::BwdLayout bwd_level(const m3::BwdShape& s, int level) {
+    return m3::backward_supported(s) ? m3::backward_layout(s, level) : m3::backward_generic_layout(s, level);
+}
+
+// The layout a checkpoint budget asks for: the first level whose kept states fit it, else
+// the level with the smallest workspace.
+m3::BwdLayout bwd_layout_for_budget(const m3::BwdShape& s, size_t budget) {
+    m3::BwdLayout best = bwd_level(s, 0);
+    for (int lv = 0; lv < bwd_levels(s); ++lv) {
+        const m3::BwdLayout l = bwd_level(s, lv);
+        if (l.kept_bytes <= budget) return l;
+        if (l.bytes < best.bytes) best = l;
+    }
+    return best;
+}
+
+// The layout a backward call runs with: the first level (the fewest recomputed states)
+// whose workspace fits the one passed.  False when none does.
+bool bwd_layout_for_workspace(const m3::BwdShape& s, size_t workspace_bytes, m3::BwdLayout* out) {
+    for (int lv = 0; lv < bwd_levels(s); ++lv) {
+        const m3::BwdLayout l = bwd_level(s, lv);
+        if (l.bytes <= workspace_bytes) {
+            *out = l;
+            return true;
+        }
+    }
+    return false;
+}
+
+constexpr size_t kDefaultCheckpointBudget = size_t{4} << 30;
 
 }  // namespace
 
 extern "C" {
 
-m3_status m3_backward_workspace_size(const m3_dims* dims, size_t* bytes) {
+m3_status m3_backward_workspace_size_budget(const m3_dims* dims, size_t checkpoint_bytes, size_t* bytes) {
     if (!bytes || !dims_ok(dims, true)) return M3_ERR_INVALID_ARG;
     const m3::BwdShape s = bwd_shape(dims);
     if (!bwd_any_supported(s)) return M3_ERR_UNSUPPORTED;
-    *bytes = bwd_any_layout(s).bytes;
+    *bytes = bwd_layout_for_budget(s, checkpoint_bytes).bytes;
     return M3_OK;
+}
+
+m3_status m3_backward_workspace_size(const m3_dims* dims, size_t* bytes) {
+    return m3_backward_workspace_size_budget(dims, kDefaultCheckpointBudget, bytes);
 }
 
 m3_status m3_backward_parts(const m3_dims* dims, int32_t* parts, int64_t* tokens_per_part) {
@@ -454,10 +488,11 @@ m3_status backward_common(const m3_dims* dims, const int64_t* cu, int64_t total_
     if (state_in && !state_in->h) return M3_ERR_INVALID_ARG;
     const m3::BwdShape s = bwd_shape(dims);
     if (!bwd_any_supported(s)) return M3_ERR_UNSUPPORTED;
-    const m3::BwdLayout lay = bwd_any_layout(s);
     // one workgroup of at most 512 threads per (b, h, part): under 2^32 work-items per launch
-    if (s.batch * s.H * lay.parts >= (int64_t{1} << 23)) return M3_ERR_UNSUPPORTED;
-    if (lay.bytes > 0 && (!workspace || workspace_bytes < lay.bytes)) return M3_ERR_WORKSPACE;
+    // (the split into parts is the same at every level)
+    if (s.batch * s.H * bwd_level(s, 0).parts >= (int64_t{1} << 23)) return M3_ERR_UNSUPPORTED;
+    m3::BwdLayout lay{};
+    if (!bwd_layout_for_workspace(s, workspace ? workspace_bytes : 0, &lay)) return M3_ERR_WORKSPACE;
     m3::BwdArgs a{};
     a.x = x;
     a.dt = dt;

@@ -42,7 +42,6 @@
 // theta, the carried B) are written per head and summed by a second kernel in a
 // fixed order, so results do not depend on scheduling.  All gradients are fp32.
 #include <cmath>
-#include <cstdlib>
 
 #include "m3_common.h"
 #include "m3_internal.h"
@@ -899,17 +898,13 @@ void backward_parts(const BwdShape& s, int* parts, int64_t* seg_per_part) {
     *seg_per_part = best_per;
 }
 
-// Segments per checkpoint group: 1 while a checkpoint after every segment fits the
-// budget (4 GiB, or the byte count in the environment variable
-// M3_BACKWARD_CHECKPOINT_BYTES), else the square root of the segments of a part
-// (rounded up), which minimises checkpoints plus scratch (groups per part + segments
-// per group states).  The grouping changes where states are kept, not how they are
-// computed: the gradients are the same bits for every group size.
-static int64_t checkpoint_group(const BwdShape& s, int parts, int64_t seg_per_part) {
-    double budget = 4.0 * (1ull << 30);
-    if (const char* e = std::getenv("M3_BACKWARD_CHECKPOINT_BYTES")) budget = std::strtod(e, nullptr);
-    const double one_level = static_cast<double>(s.batch) * s.H * parts * seg_per_part * s.N * s.P * 4;
-    if (one_level <= budget) return 1;
+// Segments per checkpoint group at each checkpoint level: level 0 keeps a checkpoint after
+// every segment; level 1 groups ceil(sqrt(segments of a part)) segments, which minimises
+// checkpoints plus scratch (groups per part + segments per group states).  The grouping
+// changes where states are kept, not how they are computed: the gradients are the same bits
+// for every group size.
+static int64_t checkpoint_group(int level, int64_t seg_per_part) {
+    if (level == 0) return 1;
     int64_t g = static_cast<int64_t>(std::ceil(std::sqrt(static_cast<double>(seg_per_part))));
     return g < 1 ? 1 : g;
 }
@@ -918,11 +913,11 @@ static int64_t checkpoint_group(const BwdShape& s, int parts, int64_t seg_per_pa
 // more than one segment, a scratch of one group's states per (batch, head, part); per-head
 // partials of the group-shared gradients when H > G; dA/dD per (batch, head, part); with a
 // split, each part's local state and adjoint (N, P) and its decay and angle sums.
-BwdLayout backward_layout(const BwdShape& s) {
+BwdLayout backward_layout(const BwdShape& s, int level) {
     BwdLayout l{};
     auto al = [](size_t v) { return (v + 255) & ~static_cast<size_t>(255); };
     backward_parts(s, &l.parts, &l.seg_per_part);
-    l.grp = checkpoint_group(s, l.parts, l.seg_per_part);
+    l.grp = checkpoint_group(level, l.seg_per_part);
     const size_t units = static_cast<size_t>(s.batch) * s.H * l.parts;
     const size_t gpp = static_cast<size_t>((l.seg_per_part + l.grp - 1) / l.grp);
     size_t off = 0;
@@ -930,6 +925,7 @@ BwdLayout backward_layout(const BwdShape& s) {
     off += al(units * gpp * s.N * s.P * 4);
     l.scratch = off;
     if (l.grp > 1) off += al(units * static_cast<size_t>(l.grp) * s.N * s.P * 4);
+    l.kept_bytes = off;
     l.per_head = s.H != s.G;
     if (l.per_head) {
         l.dB_part = off;

@@ -28,7 +28,6 @@
 // together by the whole workgroup, in coalesced runs.  This path is for the small and
 // unusual shapes; N = 128, P = 64 run the fast kernel.
 #include <cmath>
-#include <cstdlib>
 
 #include "m3_common.h"
 #include "m3_internal.h"
@@ -521,31 +520,25 @@ size_t backward_generic_lds(const BwdShape& s) {
     return static_cast<size_t>(bg::Lds(s.N, s.P, s.R, backward_generic_tb(s)).total) * sizeof(float);
 }
 
-// Tokens per recompute segment: the whole sequence (every state kept, nothing recomputed)
-// while its L + 2 states per (b, h) fit the checkpoint budget (as for the fast kernel: 4 GiB,
-// or M3_BACKWARD_CHECKPOINT_BYTES); else 16 while a state before every segment fits it; else
-// sqrt(L); each rounded up to a multiple of 16, so that staged blocks never straddle a
-// segment (and the two last choices about minimise checkpoints plus the segment scratch).
-// The segment length changes where states are kept, not how they are computed.
-int64_t backward_generic_ks(const BwdShape& s) {
-    double budget = 4.0 * (1ull << 30);
-    if (const char* e = std::getenv("M3_BACKWARD_CHECKPOINT_BYTES")) budget = std::strtod(e, nullptr);
+// Tokens per recompute segment at each checkpoint level: level 0 the whole sequence (every
+// state kept, no recompute pass), level 1 16 tokens (a state before every segment), level 2
+// ceil(sqrt(L)) (about minimising checkpoints plus the segment scratch); each rounded up to a
+// multiple of 16, so that staged blocks never straddle a segment.  The segment length changes
+// where states are kept, not how they are computed.
+static int64_t backward_generic_ks(const BwdShape& s, int level) {
     const int64_t L = s.L > 0 ? s.L : 1;
-    const double per_state = static_cast<double>(s.batch) * s.H * s.N * s.P * 4;
     const int64_t ks = 16;
-    // every state kept (one segment): no recompute pass
-    if (per_state * static_cast<double>(L + 2) <= budget) return ((L + ks - 1) / ks) * ks;
-    if (per_state * static_cast<double>((L + ks - 1) / ks + ks + 1) <= budget) return ks;
-    const int64_t r = static_cast<int64_t>(std::ceil(std::sqrt(static_cast<double>(L))));
+    if (level == 1) return ks;
+    const int64_t r = level == 0 ? L : static_cast<int64_t>(std::ceil(std::sqrt(static_cast<double>(L))));
     return ((r + ks - 1) / ks) * ks;
 }
 
-BwdLayout backward_generic_layout(const BwdShape& s) {
+BwdLayout backward_generic_layout(const BwdShape& s, int level) {
     BwdLayout l{};
     auto al = [](size_t v) { return (v + 255) & ~static_cast<size_t>(255); };
     l.generic = true;
     l.parts = 1;
-    l.ks = backward_generic_ks(s);
+    l.ks = backward_generic_ks(s, level);
     l.seg_per_part = (s.L + l.ks - 1) / l.ks;
     l.grp = 1;
     const size_t bh = static_cast<size_t>(s.batch) * s.H;
@@ -555,6 +548,7 @@ BwdLayout backward_generic_layout(const BwdShape& s) {
     off += al(bh * static_cast<size_t>(l.seg_per_part > 0 ? l.seg_per_part : 1) * state);
     l.scratch = off;
     off += al(bh * static_cast<size_t>(l.ks + 1) * state);
+    l.kept_bytes = off;
     l.per_head = s.H != s.G;
     if (l.per_head) {
         l.dB_part = off;

@@ -133,6 +133,7 @@ struct BwdLayout {            // byte offsets into the workspace
     int64_t grp;              // segments per checkpoint group (1: a checkpoint after every segment)
     bool generic;             // the generic kernel (any shape within its limits): parts 1, grp 1
     int64_t ks;               // generic kernel: tokens per recompute segment
+    size_t kept_bytes;        // the checkpointed states and the recompute scratch together
 };
 // Number of parts the backward splits each sequence into, and the segments of
 // each part: chosen from the shape alone so that results depend on nothing else.
@@ -189,7 +190,10 @@ struct BwdArgs {
     bool state_bf16;
 };
 bool backward_supported(const BwdShape& s);
-BwdLayout backward_layout(const BwdShape& s);
+// Checkpoint levels, level 0 keeping the most states (and recomputing the fewest); every
+// level gives the same gradient bits.
+constexpr int kBackwardLevels = 2;
+BwdLayout backward_layout(const BwdShape& s, int level);
 hipError_t launch_backward(BwdArgs a, const BwdLayout& l, hipStream_t st);
 // After the scan kernels: sums of the per-head partial gradients of group-shared inputs,
 // the zero carry gradient when there is no carry, and dA, dD over batch (and parts).
@@ -197,7 +201,8 @@ hipError_t launch_backward_sums(const BwdArgs& a, const BwdLayout& l, hipStream_
 // Any other shape with N even, N and P at most 256, N / 2 * P at most 4096 and rank 1..8
 // (m3_backward_generic.hip): one workgroup per (b, h), token-serial.
 bool backward_generic_supported(const BwdShape& s);
-BwdLayout backward_generic_layout(const BwdShape& s);
+constexpr int kBackwardGenericLevels = 3;
+BwdLayout backward_generic_layout(const BwdShape& s, int level);
 hipError_t launch_backward_generic(BwdArgs a, const BwdLayout& l, hipStream_t st);
 
 }  // namespace m3

@@ -96,6 +96,8 @@ def lib(path: str = LIB_PATH):
     L.m3_decode_step_fused.argtypes = [ctypes.POINTER(Dims)] + [vp] * 11 + [ctypes.POINTER(Fusion), vp, vp]
     L.m3_backward_workspace_size.restype = ctypes.c_int
     L.m3_backward_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(sz)]
+    L.m3_backward_workspace_size_budget.restype = ctypes.c_int
+    L.m3_backward_workspace_size_budget.argtypes = [ctypes.POINTER(Dims), ctypes.c_size_t, ctypes.POINTER(sz)]
     L.m3_backward_varlen.restype = ctypes.c_int
     L.m3_backward_varlen.argtypes = ([ctypes.POINTER(Dims), vp, ctypes.c_int64] + [vp] * 8 +
                                      [ctypes.POINTER(State), vp, vp, ctypes.POINTER(Grads), vp, sz, vp])
@@ -394,9 +396,15 @@ def _prefill_packed(x, dt, A, lam, theta, B, C, D, cu_seqlens, max_seqlen, chunk
     return y, st
 
 
-def backward_workspace_size(dims: Dims) -> int:
+def backward_workspace_size(dims: Dims, checkpoint_bytes: Optional[int] = None) -> int:
+    """Workspace bytes of the backward calls: for the default checkpoint budget
+    (m3_backward_workspace_size), or for ``checkpoint_bytes`` of kept states
+    (m3_backward_workspace_size_budget)."""
     n = ctypes.c_size_t(0)
-    rc = lib().m3_backward_workspace_size(ctypes.byref(dims), ctypes.byref(n))
+    if checkpoint_bytes is None:
+        rc = lib().m3_backward_workspace_size(ctypes.byref(dims), ctypes.byref(n))
+    else:
+        rc = lib().m3_backward_workspace_size_budget(ctypes.byref(dims), int(checkpoint_bytes), ctypes.byref(n))
     if rc != 0:
         raise M3Error("m3_backward_workspace_size", rc)
     return int(n.value)
@@ -444,21 +452,26 @@ def _backward_grads(lead, nb, H, G, N, P, R, want_state_grads, grads, dev, dA_pe
     return out, gs
 
 
-def _backward_workspace(dims, workspace, dev):
-    ws = backward_workspace_size(dims)
-    if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
+def _backward_workspace(dims, workspace, dev, checkpoint_bytes):
+    """(bytes, tensor): a caller's workspace whole when it holds what the budget needs (the
+    call keeps as many states as it allows), else a new one of that size."""
+    ws = backward_workspace_size(dims, checkpoint_bytes)
+    if workspace is not None and workspace.numel() * workspace.element_size() >= ws:
+        return workspace.numel() * workspace.element_size(), workspace
+    if ws > 0:
         workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
     return ws, workspace
 
 
 def backward(x, dt, A, lam, theta, B, C, D, dy, dh_out=None, state_in: Optional[DecodeState] = None,
              want_state_grads: bool = True, workspace: Optional[torch.Tensor] = None,
-             grads: Optional[dict] = None):
+             grads: Optional[dict] = None, checkpoint_bytes: Optional[int] = None):
     """Backward pass of the scan: gradients of sum <dy, y> + <dh_out, h_L>.
 
     Returns a dict of fp32 tensors dx, ddt, dA, dlam, dtheta, dB, dC, dD and, with
     want_state_grads, dh0 (b,H,N,P), db_last (b,G,R,N), dx_last (b,H,R,P).
-    ``grads`` may hold preallocated output tensors of those names."""
+    ``grads`` may hold preallocated output tensors of those names; ``checkpoint_bytes``
+    bounds the states kept for the reverse sweep (default 4 GiB)."""
     b, L, H, R, P = x.shape
     G, N = B.shape[2], B.shape[4]
     dev = x.device
@@ -479,7 +492,7 @@ def backward(x, dt, A, lam, theta, B, C, D, dy, dh_out=None, state_in: Optional[
     sin, state_dtype = _backward_state(state_in, b, H, G, N, P, R, io, dev)
     dims = make_dims(b, L, H, G, P, N, R, 1, _IO[io], _IO[state_dtype])
     out, gs = _backward_grads((b, L), b, H, G, N, P, R, want_state_grads, grads, dev)
-    ws, workspace = _backward_workspace(dims, workspace, dev)
+    ws, workspace = _backward_workspace(dims, workspace, dev, checkpoint_bytes)
     rc = lib().m3_backward(ctypes.byref(dims), _p(x), _p(dt), _p(A), _p(lam), _p(theta), _p(B), _p(C),
                            _p(D), None if sin is None else ctypes.byref(sin), _p(dy), _p(dh_out),
                            ctypes.byref(gs), _p(workspace) if ws > 0 else None, ws, _stream(dev))
@@ -490,7 +503,8 @@ def backward(x, dt, A, lam, theta, B, C, D, dy, dh_out=None, state_in: Optional[
 
 def backward_varlen(x, dt, A, lam, theta, B, C, D, dy, cu_seqlens, max_seqlen: int, dh_out=None,
                     state_in: Optional[DecodeState] = None, want_state_grads: bool = True,
-                    workspace: Optional[torch.Tensor] = None, grads: Optional[dict] = None):
+                    workspace: Optional[torch.Tensor] = None, grads: Optional[dict] = None,
+                    checkpoint_bytes: Optional[int] = None):
     """Backward pass of prefill_varlen (m3_backward_varlen): the packed layouts of
     prefill_varlen for the inputs, dy and the per-token gradients (T, ...), per-sequence
     dh_out, state_in and state gradients (nseq, ...).  Returns the dict of ``backward``."""
@@ -517,7 +531,7 @@ def backward_varlen(x, dt, A, lam, theta, B, C, D, dy, cu_seqlens, max_seqlen: i
     sin, state_dtype = _backward_state(state_in, nseq, H, G, N, P, R, io, dev)
     dims = make_dims(nseq, max_seqlen, H, G, P, N, R, 1, _IO[io], _IO[state_dtype])
     out, gs = _backward_grads((T,), nseq, H, G, N, P, R, want_state_grads, grads, dev)
-    ws, workspace = _backward_workspace(dims, workspace, dev)
+    ws, workspace = _backward_workspace(dims, workspace, dev, checkpoint_bytes)
     rc = lib().m3_backward_varlen(ctypes.byref(dims), _p(cu_seqlens), T, _p(x), _p(dt), _p(A), _p(lam),
                                   _p(theta), _p(B), _p(C), _p(D), None if sin is None else ctypes.byref(sin),
                                   _p(dy), _p(dh_out), ctypes.byref(gs), _p(workspace) if ws > 0 else None, ws,
@@ -649,7 +663,8 @@ def decode_step_fused(state: DecodeState, x_t, dt_t, A, lam_t, theta_t, B_t, C_t
 
 def backward_per_token_A(x, dt, A_t, lam, theta, B, C, D, dy, cu_seqlens=None, max_seqlen: Optional[int] = None,
                          dh_out=None, state_in: Optional[DecodeState] = None, want_state_grads: bool = True,
-                         workspace: Optional[torch.Tensor] = None, grads: Optional[dict] = None):
+                         workspace: Optional[torch.Tensor] = None, grads: Optional[dict] = None,
+                         checkpoint_bytes: Optional[int] = None):
     """Backward pass with a per-token decay rate A_t (m3_backward_per_token_A): the
     layouts of ``backward`` (cu_seqlens None) or ``backward_varlen`` (cu_seqlens and
     max_seqlen given), with A_t fp32 shaped like dt; dA is returned per token, shaped
@@ -687,7 +702,7 @@ def backward_per_token_A(x, dt, A_t, lam, theta, B, C, D, dy, cu_seqlens=None, m
     sin, state_dtype = _backward_state(state_in, nb, H, G, N, P, R, io, dev)
     dims = make_dims(nb, L, H, G, P, N, R, 1, _IO[io], _IO[state_dtype])
     out, gs = _backward_grads(lead, nb, H, G, N, P, R, want_state_grads, grads, dev, dA_per_token=True)
-    ws, workspace = _backward_workspace(dims, workspace, dev)
+    ws, workspace = _backward_workspace(dims, workspace, dev, checkpoint_bytes)
     rc = lib().m3_backward_per_token_A(ctypes.byref(dims), _p(cu_seqlens), lead[0] if packed else 0, _p(x),
                                        _p(dt), _p(A_t), _p(lam), _p(theta), _p(B), _p(C), _p(D),
                                        None if sin is None else ctypes.byref(sin), _p(dy), _p(dh_out),

@@ -29,7 +29,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_symbols() == ["m3_backward", "m3_backward_parts", "m3_backward_per_token_A", "m3_backward_varlen",
-                                  "m3_backward_workspace_size", "m3_decode_step",
+                                  "m3_backward_workspace_size", "m3_backward_workspace_size_budget", "m3_decode_step",
                                   "m3_decode_step_fused", "m3_prefill_chunked", "m3_prefill_chunked_noalloc", "m3_prefill_fused",
                                   "m3_prefill_fused_workspace_size",
                                   "m3_prefill_varlen", "m3_prefill_varlen_fused", "m3_prefill_workspace_size", "m3_status_string",
@@ -394,26 +394,29 @@ def test_noalloc_refuses_shapes_beyond_its_scratch(lib):
     assert lib.m3_prefill_chunked_noalloc(None, *null8, None, None, None, None) == -1
 
 
-def _bwd_ws(lib, d):
+def _bwd_ws(lib, d, budget=None):
     n = ctypes.c_size_t(0)
-    assert lib.m3_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    if budget is None:
+        assert lib.m3_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    else:
+        assert lib.m3_backward_workspace_size_budget(ctypes.byref(d), ctypes.c_size_t(budget), ctypes.byref(n)) == 0
     return n.value
 
 
-def test_backward_checkpoint_budget(lib, monkeypatch):
+def test_backward_checkpoint_budget(lib):
     """Checkpoints stay one per 3-token segment while they fit the budget (4 GiB by default,
-    or M3_BACKWARD_CHECKPOINT_BYTES); above it the workspace holds about 2 sqrt(L/3) states
-    per (b, h) instead of L/3 -- checked against the sizes that layout implies."""
+    else the one passed to m3_backward_workspace_size_budget); above it the workspace holds
+    about 2 sqrt(L/3) states per (b, h) instead of L/3 -- checked against the sizes that
+    layout implies."""
     P, N, state = 64, 128, 64 * 128 * 4
-    monkeypatch.delenv("M3_BACKWARD_CHECKPOINT_BYTES", raising=False)
     # nanomamba3-shaped: 2.15 GB of checkpoints, under the budget: one level
     d = _dims(batch=4, nheads=24, ngroups=1, headdim=P, dstate=N, rank=2, seqlen=2048)
     parts, tpp = m3scan.backward_parts(d)
     one = _bwd_ws(lib, d)
     assert one >= 4 * 24 * parts * (tpp // 3) * state
+    assert _bwd_ws(lib, d, 4 << 30) == one
     # a budget below that: groups of ceil(sqrt(segments per piece)) segments
-    monkeypatch.setenv("M3_BACKWARD_CHECKPOINT_BYTES", str(1 << 20))
-    two = _bwd_ws(lib, d)
+    two = _bwd_ws(lib, d, 1 << 20)
     segs = tpp // 3
     g = -(-segs // 1)
     import math
@@ -422,7 +425,6 @@ def test_backward_checkpoint_budget(lib, monkeypatch):
     ck_two = 4 * 24 * parts * (-(-segs // g) + g) * state
     assert one - two == ck_one - ck_two, (one, two, ck_one, ck_two)
     # the 1.5B SISO layer (44.8 GB of one-level checkpoints) is grouped by default
-    monkeypatch.delenv("M3_BACKWARD_CHECKPOINT_BYTES")
     d = _dims(batch=8, nheads=64, ngroups=1, headdim=P, dstate=N, rank=1, seqlen=8192)
     assert m3scan.backward_parts(d) == (1, 8192)
     segs = -(-8192 // 3)
@@ -432,8 +434,7 @@ def test_backward_checkpoint_budget(lib, monkeypatch):
     assert ws < 8 * 64 * segs * state
     assert ws >= 8 * 64 * (-(-segs // g) + g) * state + partials
     # a budget above it restores one level
-    monkeypatch.setenv("M3_BACKWARD_CHECKPOINT_BYTES", str(64 << 30))
-    assert _bwd_ws(lib, d) >= 8 * 64 * segs * state
+    assert _bwd_ws(lib, d, 64 << 30) >= 8 * 64 * segs * state
 
 
 def test_serial_prefill_needs_no_workspace(lib):
@@ -447,14 +448,31 @@ def test_serial_prefill_needs_no_workspace(lib):
         assert n.value == 0, (N, P, R)
 
 
-def test_generic_backward_workspace(lib, monkeypatch):
+@pytest.mark.parametrize("shape", [dict(headdim=64, dstate=128, rank=2), dict(headdim=12, dstate=24, rank=3)],
+                         ids=["fast", "generic"])
+def test_backward_workspace_below_every_level_is_refused(lib, shape):
+    """The backward keeps states at the first level whose workspace fits the bytes passed;
+    below the smallest level (the size a budget of one byte asks for) it returns
+    M3_ERR_WORKSPACE before any launch, and the budgeted sizes shrink with the budget."""
+    d = _dims(batch=2, seqlen=1000, nheads=4, ngroups=1, io_dtype=m3scan.M3_BF16, **shape)
+    smallest = _bwd_ws(lib, d, 1)
+    assert 0 < smallest <= _bwd_ws(lib, d, 1 << 20) <= _bwd_ws(lib, d) <= _bwd_ws(lib, d, 1 << 62)
+    assert _bwd(lib, d, _grads(), ws=FAKE, nbytes=smallest - 1) == -3
+    assert _bwd(lib, d, _grads(), ws=None, nbytes=smallest) == -3
+    n = ctypes.c_size_t(0)
+    assert lib.m3_backward_workspace_size_budget(ctypes.byref(d), 1, None) == -1
+    assert lib.m3_backward_workspace_size_budget(None, 1, ctypes.byref(n)) == -1
+    un = _dims(batch=2, seqlen=10, headdim=300)
+    assert lib.m3_backward_workspace_size_budget(ctypes.byref(un), 1, ctypes.byref(n)) == -2
+
+
+def test_generic_backward_workspace(lib):
     """Off the fast kernel's shape the backward keeps every state of the sequence (one
     segment: L rounded up to 16, plus 2 states per (b, h)) while those fit the checkpoint
     budget; else the state before every 16-token segment plus one segment's 17 states; else
     segments of ceil(sqrt(L)) tokens rounded up to a multiple of 16 (fewer bytes each time,
     the same gradients); per-head copies of the group-shared gradients are added when H > G."""
     import math
-    monkeypatch.delenv("M3_BACKWARD_CHECKPOINT_BYTES", raising=False)
     b, H, N, P, R, L = 2, 4, 24, 12, 3, 1000
     state = N * P * 4
     slack = 4 * 256 + 2 * b * H * 4 + 1024
@@ -463,15 +481,12 @@ def test_generic_backward_workspace(lib, monkeypatch):
     keep = 16 * math.ceil(L / 16) + 2
     assert b * H * keep * state <= wall < b * H * keep * state + slack
     # below every state, above 16-token segments
-    monkeypatch.setenv("M3_BACKWARD_CHECKPOINT_BYTES", str(2 << 20))
-    w16 = _bwd_ws(lib, d1)
+    w16 = _bwd_ws(lib, d1, 2 << 20)
     seg16 = math.ceil(L / 16) + 17
     assert b * H * seg16 * state <= w16 < b * H * seg16 * state + slack
-    monkeypatch.setenv("M3_BACKWARD_CHECKPOINT_BYTES", "1")
     ks = 16 * math.ceil(math.ceil(math.sqrt(L)) / 16)
-    wsq = _bwd_ws(lib, d1)
+    wsq = _bwd_ws(lib, d1, 1)
     assert wsq >= b * H * (math.ceil(L / ks) + ks + 1) * state and wsq < w16 < wall
-    monkeypatch.delenv("M3_BACKWARD_CHECKPOINT_BYTES")
     d2 = _dims(batch=b, nheads=H, ngroups=1, headdim=P, dstate=N, rank=R, seqlen=L)
     per_head = b * L * H * (2 * R * N + N // 2) * 4 + b * H * R * N * 4
     assert _bwd_ws(lib, d2) >= wall + per_head

@@ -128,8 +128,8 @@ def test_cases_cover_split_and_whole_sequences():
     assert any(p == 1 and c[1] > 3 for c, (p, t) in plans)
 
 
-def _grads(d, dy, dh=None, st=None):
-    g = m3scan.backward(*[d[k] for k in NAMES], dy, dh_out=dh, state_in=st)
+def _grads(d, dy, dh=None, st=None, checkpoint_bytes=None):
+    g = m3scan.backward(*[d[k] for k in NAMES], dy, dh_out=dh, state_in=st, checkpoint_bytes=checkpoint_bytes)
     torch.cuda.synchronize()
     return g
 
@@ -140,7 +140,7 @@ def _grads(d, dy, dh=None, st=None):
     (8, 40, 32, 8, 1, "bf16", True, False),     # whole sequences
     (1, 100, 4, 1, 4, "fp32", True, True),      # groups of 6 segments, the last one of 4
 ], ids=_id)
-def test_checkpoint_groups_give_the_same_bits(case, monkeypatch):
+def test_checkpoint_groups_give_the_same_bits(case):
     """With a checkpoint budget too small for one state per segment, the states inside each
     group of segments are recomputed from the group's checkpoint: the same forward steps in
     the same order, so every gradient is bit-identical to the one-level run."""
@@ -156,12 +156,10 @@ def test_checkpoint_groups_give_the_same_bits(case, monkeypatch):
                                 torch.randn((b, G, R, 128), generator=gen).to(tdt).cuda(),
                                 torch.randn((b, H, R, 64), generator=gen).to(tdt).cuda())
     dims = m3scan.make_dims(b, L, H, G, 64, 128, R, 1, 0)
-    monkeypatch.delenv("M3_BACKWARD_CHECKPOINT_BYTES", raising=False)
     ws1 = m3scan.backward_workspace_size(dims)
     g1 = _grads(d, dy, dh, st)
-    monkeypatch.setenv("M3_BACKWARD_CHECKPOINT_BYTES", "1")
-    ws2 = m3scan.backward_workspace_size(dims)
-    g2 = _grads(d, dy, dh, st)
+    ws2 = m3scan.backward_workspace_size(dims, 1)
+    g2 = _grads(d, dy, dh, st, checkpoint_bytes=1)
     parts, tpp = m3scan.backward_parts(dims)
     say(f"checkpoint groups {_id(case)}: {parts} pieces of {tpp} tokens, workspace {ws1} -> {ws2} bytes")
     if parts == 1:   # one piece of L/3 segments: sqrt-sized groups hold fewer states

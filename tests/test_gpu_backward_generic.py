@@ -99,23 +99,22 @@ def test_generic_backward_empty_sequence():
     assert float(gr["dA"].abs().max()) == 0.0 and float(gr["dD"].abs().max()) == 0.0
 
 
-def test_generic_backward_is_deterministic_and_budget_independent(monkeypatch):
+def test_generic_backward_is_deterministic_and_budget_independent():
     """Two calls give the same bits, and so do 16-token segments and segments of about
     sqrt(L) tokens, forced by smaller checkpoint budgets, against every state kept (the
-    default here): the recomputed states come from the same steps."""
+    default here): the recomputed states come from the same steps.  A workspace of exactly
+    the smaller size is passed each time, so the call must pick that level to fit it."""
     b, L, H, G, P, N, R = 2, 1000, 2, 1, 16, 32, 2   # every state: 1010 states; 16-token segments: 80; 32: 65
     d, dy, dh, st = _inputs(b, L, H, G, P, N, R, "fp32", 61, True, True)
-    monkeypatch.delenv("M3_BACKWARD_CHECKPOINT_BYTES", raising=False)
     dims = m3scan.make_dims(b, L, H, G, P, N, R, 1, 0)
     w16 = m3scan.backward_workspace_size(dims)
     g1 = m3scan.backward(*[d[k] for k in NAMES], dy, dh_out=dh, state_in=st)
     g2 = m3scan.backward(*[d[k] for k in NAMES], dy, dh_out=dh, state_in=st)
-    monkeypatch.setenv("M3_BACKWARD_CHECKPOINT_BYTES", str(4 << 20))
-    wseg = m3scan.backward_workspace_size(dims)
-    g4 = m3scan.backward(*[d[k] for k in NAMES], dy, dh_out=dh, state_in=st)
-    monkeypatch.setenv("M3_BACKWARD_CHECKPOINT_BYTES", "1")
-    wsq = m3scan.backward_workspace_size(dims)
-    g3 = m3scan.backward(*[d[k] for k in NAMES], dy, dh_out=dh, state_in=st)
+    wseg = m3scan.backward_workspace_size(dims, 4 << 20)
+    g4 = m3scan.backward(*[d[k] for k in NAMES], dy, dh_out=dh, state_in=st,
+                         workspace=torch.empty(wseg, dtype=torch.uint8, device="cuda"))
+    wsq = m3scan.backward_workspace_size(dims, 1)
+    g3 = m3scan.backward(*[d[k] for k in NAMES], dy, dh_out=dh, state_in=st, checkpoint_bytes=1)
     torch.cuda.synchronize()
     say(f"generic backward workspace: {w16} bytes (every state), {wseg} (16-token segments), {wsq} (sqrt(L))")
     assert wsq < wseg < w16

@@ -116,7 +116,7 @@ def test_backward_varlen_equal_lengths_match_uniform_batch():
 
 
 @pytest.mark.parametrize("case", CASES, ids=_id)
-def test_backward_varlen_checkpoint_groups_give_the_same_bits(case, monkeypatch):
+def test_backward_varlen_checkpoint_groups_give_the_same_bits(case):
     """Checkpoint groups (forced by a one-byte budget) in a packed batch: short sequences end
     inside or before a group; every gradient is bit-identical to the one-level run."""
     lengths, H, G, R, io, with_state, with_dh = case
@@ -131,11 +131,9 @@ def test_backward_varlen_checkpoint_groups_give_the_same_bits(case, monkeypatch)
         st = m3scan.DecodeState(torch.randn((ns, H, N, P), generator=gen).cuda(),
                                 torch.randn((ns, G, R, N), generator=gen).to(tdt).cuda(),
                                 torch.randn((ns, H, R, P), generator=gen).to(tdt).cuda())
-    monkeypatch.delenv("M3_BACKWARD_CHECKPOINT_BYTES", raising=False)
     g1 = m3scan.backward_varlen(*[d[k] for k in NAMES], dy, cu, Lmax, dh_out=dh, state_in=st)
     torch.cuda.synchronize()
-    monkeypatch.setenv("M3_BACKWARD_CHECKPOINT_BYTES", "1")
-    g2 = m3scan.backward_varlen(*[d[k] for k in NAMES], dy, cu, Lmax, dh_out=dh, state_in=st)
+    g2 = m3scan.backward_varlen(*[d[k] for k in NAMES], dy, cu, Lmax, dh_out=dh, state_in=st, checkpoint_bytes=1)
     torch.cuda.synchronize()
     say("backward varlen checkpoint groups", _id(case))
     for k in g1:
