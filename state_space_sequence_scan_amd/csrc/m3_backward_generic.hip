@@ -22,10 +22,13 @@
 // whole state (dalpha, dbeta, dgamma, dD) are taken from LDS copies of h_t, dU_t and the
 // per-pair angle terms in a fixed order, so results do not depend on scheduling.  Group-
 // shared gradients are written per head when H > G and summed afterwards, as in the fast
-// kernel.  The inputs of up to 16 tokens are staged into LDS at once (as many as 128 KB
-// of LDS holds beside the sums' buffers).  The sums take two barriers per token in the
-// reverse sweep; each token's gradients are collected in LDS and a block's are written out
-// together by the whole workgroup, in coalesced runs.  This path is for the small and
+// kernel.  The inputs of up to 16 tokens are staged into LDS at once.  The adjoint of a
+// pair needs nothing from other threads, so in the reverse sweep each thread steps its
+// pairs through a batch of up to 16 staged tokens before one barrier, and the batch's sums
+// follow together: two barriers per batch.  The block and batch sizes are those with the
+// fewest barriers per token whose LDS fits in 128 KB.  Each token's gradients are
+// collected in LDS and a block's are written out together by the whole workgroup, in
+// coalesced runs.  This path is for the small and
 // unusual shapes; N = 128, P = 64 run the fast kernel.
 #include <cmath>
 
@@ -40,12 +43,12 @@ constexpr int kMaxR = 8;
 constexpr int kMaxEPT = 16;      // element pairs per thread: (N / 2) * P <= NT * kMaxEPT
 constexpr int kMaxDim = 256;
 
-// Dynamic LDS layout (floats), sized for this launch's N, P, R and TB tokens per staged
-// block.  Slot j of B and X holds token t0 - 1 + j (slot 0: the token before the block, the
-// carry, or zeros); slot j of the others holds token t0 + j.
+// Dynamic LDS layout (floats), sized for this launch's N, P, R, TB tokens per staged block
+// and TS tokens per batch of sums.  Slot j of B and X holds token t0 - 1 + j (slot 0: the
+// token before the block, the carry, or zeros); slot j of the others holds token t0 + j.
 struct Lds {
     int b, x, c, dy, cs, sn, sc, hL, dUL, thc, red, ob, ow, total;
-    __host__ __device__ Lds(int N, int P, int R, int TB) {
+    __host__ __device__ Lds(int N, int P, int R, int TB, int TS) {
         int o = 0;
         b = o;  o += (TB + 1) * R * N;
         x = o;  o += (TB + 1) * R * P;
@@ -54,10 +57,10 @@ struct Lds {
         cs = o; o += TB * (N / 2);    // cos, sin of each token's pair angles
         sn = o; o += TB * (N / 2);
         sc = o; o += TB * 4;          // dt, lambda, decay rate of each token
-        hL = o; o += N * P;           // h_t, (n, p) row-major
-        dUL = o; o += N * P;          // dU_t
-        thc = o; o += (N / 2) * P;    // per (pair, column) terms of dtheta
-        red = o; o += 3 * NT;         // per-thread partial sums of dalpha, dbeta, dgamma
+        hL = o; o += (TS + 1) * N * P;   // h_t of each token of a batch and h_{t-1} of its last, (n, p) row-major
+        dUL = o; o += TS * N * P;     // dU_t
+        thc = o; o += TS * (N / 2) * P;   // per (pair, column) terms of dtheta
+        red = o; o += TS * 3 * (NT / 64);   // per-wave sums of dalpha, dbeta, dgamma
         ow = 2 * R * N + N / 2 + R * P + 4;   // one token's outputs: dC, dB, dtheta, dx, ddt, dlambda, dA
         ob = o; o += TB * ow;         // the block's outputs, written out once per block
         total = o;
@@ -74,10 +77,11 @@ __device__ __forceinline__ int fdiv(int u, float inv) {
     return static_cast<int>((static_cast<float>(u) + 0.5f) * inv);
 }
 
-// ks: tokens per recompute segment, a multiple of TB (tokens staged per block).  EPT:
-// element pairs per thread, the smallest power of two that covers N / 2 * P.
+// ks: tokens per recompute segment, a multiple of TB (tokens staged per block); TS: tokens
+// per batch of sums, dividing TB.  EPT: element pairs per thread, the smallest power of two
+// that covers N / 2 * P.
 template <typename T, int EPT>
-__global__ __launch_bounds__(NT) void bwd_generic(BwdArgs a, int64_t ks, int TB) {
+__global__ __launch_bounds__(NT) void bwd_generic(BwdArgs a, int64_t ks, int TB, int TS) {
     extern __shared__ __align__(16) float lds[];
     const int N = a.N, P = a.P, R = a.R, KP = N / 2, E = KP * P, RN = R * N, RP = R * P;
     const float invN = 1.f / N, invP = 1.f / P;   // for the task indices (fdiv)
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(NT) void bwd_generic(BwdArgs a, int64_t ks, int TB)
     const int t1 = up16(RN), t2 = t1 + up16(RN), t3 = t2 + up16(KP), tspan = t3 + up16(RP);
     const int ntask = 2 * RN + KP + RP;
     const int sw = ((t2 * 4) / 64) % (NT / 64);   // the scalar wave
-    const Lds lay(N, P, R, TB);
+    const Lds lay(N, P, R, TB, TS);
     float* sB = lds + lay.b;
     float* sX = lds + lay.x;
     float* sC = lds + lay.c;
@@ -127,53 +131,118 @@ __global__ __launch_bounds__(NT) void bwd_generic(BwdArgs a, int64_t ks, int TB)
     float2* ck = reinterpret_cast<float2*>(a.ckpt) + static_cast<size_t>(bh) * a.seg_per_part * E;
     float2* scr = reinterpret_cast<float2*>(a.scratch) + static_cast<size_t>(bh) * (ks + 1) * E;
 
-    // the thread's element pairs: pair kk[i], column pp[i] (kk = -1: none)
-    int kk[EPT], pp[EPT];
+    // the thread's element pairs: pair kk[i], column pp[i] (kk = -1: none); ec[i] the pair,
+    // clamped to the last, for loads that every thread issues
+    int kk[EPT], pp[EPT], ec[EPT];
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
         const int e = tid + NT * i;
         kk[i] = e < E ? e / P : -1;
         pp[i] = e < E ? e - kk[i] * P : 0;
+        ec[i] = e < E ? e : E - 1;
     }
+    constexpr int KH = EPT <= 2 ? 8 : EPT <= 4 ? 4 : 2;   // states loaded together
     auto soff = [&](int64_t t) { return (tb + t) * H + h; };
 
     // Tokens t0 .. t0+nt-1 (B and X also of token t0 - 1) into the slots; with_cdy also
     // their C and dy.
     auto stage = [&](int64_t t0, int nt, bool with_cdy) {
         __syncthreads();   // the previous block's readers are done
-        for (int i = tid; i < (nt + 1) * RN; i += NT) {
+        const int nB = (nt + 1) * RN, nX = (nt + 1) * RP, nC = nt * RN, nD = nt * RP, nT = nt * KP;
+        auto b_src = [&](int i, bool* zero) {   // B of unit i (token t0 - 1 + i / RN)
             const int j = i / RN, o = i - j * RN;
             const int64_t t = t0 - 1 + j;
-            sB[i] = t >= 0 ? ldv(Bm, ((tb + t) * G + g) * static_cast<int64_t>(RN) + o)
-                           : (carry ? ldv(blp, (static_cast<int64_t>(b) * G + g) * RN + o) : 0.f);
-        }
-        for (int i = tid; i < (nt + 1) * RP; i += NT) {
+            *zero = t < 0 && !carry;
+            return t >= 0 ? Bm + ((tb + t) * G + g) * static_cast<int64_t>(RN) + o
+                          : carry ? blp + (static_cast<int64_t>(b) * G + g) * RN + o
+                                  : Bm + ((tb + t0) * G + g) * static_cast<int64_t>(RN) + o;
+        };
+        auto x_src = [&](int i, bool* zero) {
             const int j = i / RP, o = i - j * RP;
             const int64_t t = t0 - 1 + j;
-            sX[i] = t >= 0 ? ldv(x, ((tb + t) * H + h) * static_cast<int64_t>(RP) + o)
-                           : (carry ? ldv(xlp, (static_cast<int64_t>(b) * H + h) * RP + o) : 0.f);
+            *zero = t < 0 && !carry;
+            return t >= 0 ? x + ((tb + t) * H + h) * static_cast<int64_t>(RP) + o
+                          : carry ? xlp + (static_cast<int64_t>(b) * H + h) * RP + o
+                                  : x + ((tb + t0) * H + h) * static_cast<int64_t>(RP) + o;
+        };
+        auto c_src = [&](int i) {
+            const int j = i / RN, o = i - j * RN;
+            return Cm + ((tb + t0 + j) * G + g) * static_cast<int64_t>(RN) + o;
+        };
+        auto d_src = [&](int i) {
+            const int j = i / RP, o = i - j * RP;
+            return dy + ((tb + t0 + j) * H + h) * static_cast<int64_t>(RP) + o;
+        };
+        auto th_src = [&](int i) {
+            const int j = i / KP, k = i - j * KP;
+            return a.theta + ((tb + t0 + j) * G + g) * KP + k;
+        };
+        // Each thread's first two units of every array: the loads are issued together
+        // (unconditionally, at clamped indices), then converted and stored, so that their
+        // latencies overlap; the units past those (larger shapes) follow one by one.
+        constexpr int K = 2;
+        float vb[K], vx[K], vc[K], vd[K], vt[K], vs[3];
+#pragma unroll
+        for (int m = 0; m < K; ++m) {
+            const int i = tid + m * NT;
+            bool zb, zx;
+            const T* pb = b_src(i < nB ? i : nB - 1, &zb);
+            const T* px = x_src(i < nX ? i : nX - 1, &zx);
+            const float lb = io<T>::load(pb), lx = io<T>::load(px);
+            vb[m] = zb ? 0.f : lb;
+            vx[m] = zx ? 0.f : lx;
+            if (with_cdy) {
+                vc[m] = io<T>::load(c_src(i < nC ? i : nC - 1));
+                vd[m] = io<T>::load(d_src(i < nD ? i : nD - 1));
+            }
+            vt[m] = *th_src(i < nT ? i : nT - 1);
+        }
+        {
+            const int j = tid < nt ? tid : nt - 1;
+            vs[0] = a.dt[soff(t0 + j)];
+            vs[1] = a.lam[soff(t0 + j)];
+            vs[2] = a.At ? a.At[soff(t0 + j)] : Ah;
+        }
+#pragma unroll
+        for (int m = 0; m < K; ++m) {
+            const int i = tid + m * NT;
+            if (i < nB) sB[i] = vb[m];
+            if (i < nX) sX[i] = vx[m];
+            if (with_cdy) {
+                if (i < nC) sC[i] = vc[m];
+                if (i < nD) sDY[i] = vd[m];
+            }
+            if (i < nT) {
+                float sv, cv;
+                sincos_acc(vt[m], &sv, &cv);
+                sCs[i] = cv;
+                sSn[i] = sv;
+            }
+        }
+        if (tid < nt) {   // nt <= 16 < NT
+            sSc[4 * tid] = vs[0];
+            sSc[4 * tid + 1] = vs[1];
+            sSc[4 * tid + 2] = vs[2];
+        }
+        for (int i = tid + K * NT; i < nB; i += NT) {
+            bool z;
+            const T* p = b_src(i, &z);
+            sB[i] = z ? 0.f : io<T>::load(p);
+        }
+        for (int i = tid + K * NT; i < nX; i += NT) {
+            bool z;
+            const T* p = x_src(i, &z);
+            sX[i] = z ? 0.f : io<T>::load(p);
         }
         if (with_cdy) {
-            for (int i = tid; i < nt * RN; i += NT) {
-                const int j = i / RN, o = i - j * RN;
-                sC[i] = ldv(Cm, ((tb + t0 + j) * G + g) * static_cast<int64_t>(RN) + o);
-            }
-            for (int i = tid; i < nt * RP; i += NT) {
-                const int j = i / RP, o = i - j * RP;
-                sDY[i] = ldv(dy, ((tb + t0 + j) * H + h) * static_cast<int64_t>(RP) + o);
-            }
+            for (int i = tid + K * NT; i < nC; i += NT) sC[i] = io<T>::load(c_src(i));
+            for (int i = tid + K * NT; i < nD; i += NT) sDY[i] = io<T>::load(d_src(i));
         }
-        for (int i = tid; i < nt * KP; i += NT) {
-            const int j = i / KP, k = i - j * KP;
+        for (int i = tid + K * NT; i < nT; i += NT) {
             float sv, cv;
-            sincos_acc(a.theta[((tb + t0 + j) * G + g) * KP + k], &sv, &cv);
+            sincos_acc(*th_src(i), &sv, &cv);
             sCs[i] = cv;
             sSn[i] = sv;
-        }
-        for (int j = tid; j < nt; j += NT) {
-            sSc[4 * j] = a.dt[soff(t0 + j)];
-            sSc[4 * j + 1] = a.lam[soff(t0 + j)];
-            sSc[4 * j + 2] = a.At ? a.At[soff(t0 + j)] : Ah;
         }
         __syncthreads();
     };
@@ -209,7 +278,6 @@ __global__ __launch_bounds__(NT) void bwd_generic(BwdArgs a, int64_t ks, int TB)
         const float* Xp = sX + j * RP;
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
-            const int e = tid + NT * i;
             if (kk[i] >= 0) {
                 const int k = kk[i], p = pp[i];
                 float up0, up1, u0, u1;
@@ -300,62 +368,108 @@ __global__ __launch_bounds__(NT) void bwd_generic(BwdArgs a, int64_t ks, int TB)
         }
         // h_t and h_{t-1} of the token being reversed, in registers; h_{t-2} is loaded a
         // token ahead, so the scratch's latency is off the chain of the sums
-        float2 hcur[EPT], hpv[EPT];
-        load(scr + len * E, hcur);
-        load(scr + (len - 1) * E, hpv);
         for (int bt = ((len - 1) / TB) * TB; bt >= 0; bt -= TB) {
             const int nt = len - bt < TB ? len - bt : TB;
             stage(t0 + bt, nt, true);
-            for (int j = nt - 1; j >= 0; --j) {
-                const int js = bt + j;   // token index within the segment
-                float2 hnx[EPT];
+            // Tokens nt-1 .. 0 in batches of TS: each thread steps its own pairs through the
+            // batch's tokens (the adjoint is elementwise), leaving h_t, dU_t, the angle terms
+            // and per-wave partial sums of each token in LDS; after one barrier the batch's
+            // sums over columns, rows and the whole state run side by side.
+            for (int jb = nt - 1; jb >= 0; jb -= TS) {
+                const int nb = jb + 1 < TS ? jb + 1 : TS;
+                // The batch's states into LDS, each thread its own pairs (no barrier): slot u
+                // holds h_t of token jb - u, slot nb h_{t-1} of the last.  Their loads are
+                // issued KH at a time, unconditionally (clamped indices), so that their
+                // latencies overlap.
+                for (int u0 = 0; u0 <= nb; u0 += KH) {
+                    float2 hb[KH][EPT];
 #pragma unroll
-                for (int i = 0; i < EPT; ++i) hnx[i] = float2{0.f, 0.f};
-                if (js > 0) load(scr + (js - 1) * E, hnx);
-                float al, be, ga;
-                coeffs(j, &al, &be, &ga);
-                const float* Bp = sB + j * RN;
-                const float* Xp = sX + j * RP;
-                const float* Bc = Bp + RN;
-                const float* Xc = Xp + RP;
-                const float* Cc = sC + j * RN;
-                const float* Dc = sDY + j * RP;
-                float dal = 0.f, dbe = 0.f, dga = 0.f;
+                    for (int d = 0; d < KH; ++d) {
+                        const int u = u0 + d < nb ? u0 + d : nb;
+                        const float2* src = scr + static_cast<int64_t>(bt + jb - u + 1) * E;
 #pragma unroll
-                for (int i = 0; i < EPT; ++i) {
-                    const int e = tid + NT * i;
-                    if (kk[i] >= 0) {
-                        const int k = kk[i], p = pp[i];
-                        const float2 ht = hcur[i], hp = hpv[i];
-                        float g0 = an * qn[i].x, g1 = an * qn[i].y;
-                        for (int r = 0; r < R; ++r) {
-                            const float dv = Dc[r * P + p];
-                            g0 += Cc[r * N + 2 * k] * dv;
-                            g1 += Cc[r * N + 2 * k + 1] * dv;
+                        for (int i = 0; i < EPT; ++i) hb[d][i] = src[ec[i]];
+                    }
+#pragma unroll
+                    for (int d = 0; d < KH; ++d) {
+                        if (u0 + d <= nb) {
+                            float* dst = sHL + (u0 + d) * N * P;
+#pragma unroll
+                            for (int i = 0; i < EPT; ++i) {
+                                if (kk[i] >= 0) {
+                                    const int n0 = (2 * kk[i]) * P + pp[i];
+                                    dst[n0] = hb[d][i].x;
+                                    dst[n0 + P] = hb[d][i].y;
+                                }
+                            }
                         }
-                        float u0, u1, up0, up1;
-                        uval(Bc, Xc, k, p, &u0, &u1);
-                        uval(Bp, Xp, k, p, &up0, &up1);
-                        dga += g0 * u0 + g1 * u1;
-                        const float c = sCs[j * KP + k], sn = sSn[j * KP + k];
-                        const float q0 = c * g0 + sn * g1, q1 = -sn * g0 + c * g1;
-                        dal += q0 * hp.x + q1 * hp.y;
-                        dbe += q0 * up0 + q1 * up1;
-                        const float v0 = al * hp.x + be * up0, v1 = al * hp.y + be * up1;
-                        sTh[e] = q1 * v0 - q0 * v1;
-                        const int n0 = (2 * k) * P + p;
-                        sHL[n0] = ht.x;
-                        sHL[n0 + P] = ht.y;
-                        sDU[n0] = ga * g0 + bn * qn[i].x;
-                        sDU[n0 + P] = ga * g1 + bn * qn[i].y;
-                        qn[i] = float2{q0, q1};
                     }
                 }
-                sRed[tid] = dal;
-                sRed[NT + tid] = dbe;
-                sRed[2 * NT + tid] = dga;
+                // U_t of the token being reversed: computed for the batch's first token, then
+                // taken from the U_{t-1} of the token before (the same slot, the same bits)
+                float2 uc[EPT];
+#pragma unroll
+                for (int i = 0; i < EPT; ++i) {
+                    uc[i] = float2{0.f, 0.f};
+                    if (kk[i] >= 0) uval(sB + (jb + 1) * RN, sX + (jb + 1) * RP, kk[i], pp[i], &uc[i].x, &uc[i].y);
+                }
+                for (int u = 0; u < nb; ++u) {
+                    const int j = jb - u;
+                    float al, be, ga;
+                    coeffs(j, &al, &be, &ga);
+                    const float* Bp = sB + j * RN;
+                    const float* Xp = sX + j * RP;
+                    const float* Cc = sC + j * RN;
+                    const float* Dc = sDY + j * RP;
+                    const float* uHL = sHL + u * N * P;
+                    const float* uHP = uHL + N * P;
+                    float* uDU = sDU + u * N * P;
+                    float* uTh = sTh + u * E;
+                    float dal = 0.f, dbe = 0.f, dga = 0.f;
+#pragma unroll
+                    for (int i = 0; i < EPT; ++i) {
+                        const int e = tid + NT * i;
+                        if (kk[i] >= 0) {
+                            const int k = kk[i], p = pp[i];
+                            const int n0 = (2 * k) * P + p;
+                            const float2 hp = float2{uHP[n0], uHP[n0 + P]};
+                            float g0 = an * qn[i].x, g1 = an * qn[i].y;
+                            for (int r = 0; r < R; ++r) {
+                                const float dv = Dc[r * P + p];
+                                g0 += Cc[r * N + 2 * k] * dv;
+                                g1 += Cc[r * N + 2 * k + 1] * dv;
+                            }
+                            const float u0 = uc[i].x, u1 = uc[i].y;
+                            float up0, up1;
+                            uval(Bp, Xp, k, p, &up0, &up1);
+                            uc[i] = float2{up0, up1};
+                            dga += g0 * u0 + g1 * u1;
+                            const float c = sCs[j * KP + k], sn = sSn[j * KP + k];
+                            const float q0 = c * g0 + sn * g1, q1 = -sn * g0 + c * g1;
+                            dal += q0 * hp.x + q1 * hp.y;
+                            dbe += q0 * up0 + q1 * up1;
+                            const float v0 = al * hp.x + be * up0, v1 = al * hp.y + be * up1;
+                            uTh[e] = q1 * v0 - q0 * v1;
+                            uDU[n0] = ga * g0 + bn * qn[i].x;
+                            uDU[n0 + P] = ga * g1 + bn * qn[i].y;
+                            qn[i] = float2{q0, q1};
+                        }
+                    }
+                    // DPP, fixed order, all 64 lanes of every wave active
+                    dal = wave_sum(dal);
+                    dbe = wave_sum(dbe);
+                    dga = wave_sum(dga);
+                    if (lane == 0) {
+                        float* rd = sRed + u * 3 * (NT / 64) + (tid >> 6);
+                        rd[0] = dal;
+                        rd[NT / 64] = dbe;
+                        rd[2 * (NT / 64)] = dga;
+                    }
+                    an = al;
+                    bn = be;
+                }
                 __syncthreads();
-                // The token's sums as one list of dot products, spread over the threads so
+                // Each token's sums as one list of dot products, spread over the threads so
                 // that they run side by side (one loop shape for all, no divergence inside):
                 //   dC[r][n] = sum_p h_t[n][p] dy[r][p]      (RN tasks)
                 //   dB[r][n] = sum_p dU[n][p] X[r][p]        (RN)
@@ -363,66 +477,89 @@ __global__ __launch_bounds__(NT) void bwd_generic(BwdArgs a, int64_t ks, int TB)
                 //   dX[r][p] = sum_n B[r][n] dU[n][p]        (RP; plus D dy afterwards)
                 // A wave runs one kind; the 4 lanes of a task take every 4th term and add
                 // their parts by two DPP moves within the quad.
+                // Four tokens at a time per task, their loads issued together.
                 const int sub = tid & 3;
                 for (int o = tid >> 2; o < tspan; o += NT / 4) {
                     const int kind = o < t1 ? 0 : o < t2 ? 1 : o < t3 ? 2 : 3;
                     const int q = o - (kind == 0 ? 0 : kind == 1 ? t1 : kind == 2 ? t2 : t3);
                     if (q >= (kind < 2 ? RN : kind == 2 ? KP : RP)) continue;   // whole quads
-                    const float* pa;
-                    const float* pb;
-                    int sb = 1, m = P;
+                    // operand a: slot-relative (h_t, dU or angle terms of the token's batch
+                    // slot) or token-relative (B); operand b likewise (dy, X; dU; a constant)
+                    int a_off, b_off, sb = 1, m = P;
+                    const float* a_base;
+                    const float* b_base;
+                    int a_step, b_step, a_slot, b_slot;   // per token: slot stride or token stride
                     if (kind < 2) {
                         const int r = fdiv(q, invN), n = q - r * N;
-                        pa = (kind == 0 ? sHL : sDU) + n * P;
-                        pb = (kind == 0 ? Dc : Xc) + r * P;
+                        a_base = kind == 0 ? sHL : sDU; a_off = n * P; a_slot = N * P; a_step = 0;
+                        b_base = kind == 0 ? sDY : sX + RP; b_off = r * P; b_slot = 0; b_step = RP;
                     } else if (kind == 2) {
-                        pa = sTh + q * P; pb = &kOne; sb = 0;
+                        a_base = sTh; a_off = q * P; a_slot = E; a_step = 0;
+                        b_base = &kOne; b_off = 0; b_slot = 0; b_step = 0; sb = 0;
                     } else {
                         const int r = fdiv(q, invP), p = q - r * P;
-                        pa = Bc + r * N; pb = sDU + p; sb = P; m = N;
+                        a_base = sB + RN; a_off = r * N; a_slot = 0; a_step = RN;
+                        b_base = sDU; b_off = p; b_slot = N * P; b_step = 0; sb = P; m = N;
                     }
-                    float v = 0.f;
+                    const int o_out = (kind == 0 ? 0 : kind == 1 ? RN : kind == 2 ? 2 * RN : 2 * RN + KP) + q;
+                    for (int u0 = 0; u0 < nb; u0 += 4) {
+                        float v[4];
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            const int u = u0 + d < nb ? u0 + d : nb - 1;   // clamped: computed, not stored
+                            const int j = jb - u;
+                            const float* pa = a_base + a_off + u * a_slot + j * a_step;
+                            const float* pb = b_base + b_off + u * b_slot + j * b_step;
+                            float acc = 0.f;
 #pragma unroll 4
-                    for (int i = sub; i < m; i += 4) v += pa[i] * pb[i * sb];
-                    v += dpp_move<0xB1>(v);   // quad_perm [1, 0, 3, 2]
-                    v += dpp_move<0x4E>(v);   // quad_perm [2, 3, 0, 1]
-                    if (sub == 0) {
-                        if (kind == 3) v += Dh * Dc[q];
-                        sOut[j * OW + (kind == 0 ? 0 : kind == 1 ? RN : kind == 2 ? 2 * RN : 2 * RN + KP) + q] = v;
+                            for (int i = sub; i < m; i += 4) acc += pa[i] * pb[i * sb];
+                            v[d] = acc;
+                        }
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            v[d] += dpp_move<0xB1>(v[d]);   // quad_perm [1, 0, 3, 2]
+                            v[d] += dpp_move<0x4E>(v[d]);   // quad_perm [2, 3, 0, 1]
+                        }
+                        if (sub == 0) {
+#pragma unroll
+                            for (int d = 0; d < 4; ++d) {
+                                if (u0 + d < nb) {
+                                    const int j = jb - u0 - d;
+                                    sOut[j * OW + o_out] = kind == 3 ? v[d] + Dh * sDY[j * RP + q] : v[d];
+                                }
+                            }
+                        }
                     }
                 }
-                // whole-state sums, in a fixed order by the scalar wave
-                if ((tid >> 6) == sw) {
-                    float sa = 0.f, sb = 0.f, sg = 0.f, sd = 0.f;
-                    for (int w = 0; w < NT / 64; ++w) {
-                        sa += sRed[w * 64 + lane];
-                        sb += sRed[NT + w * 64 + lane];
-                        sg += sRed[2 * NT + w * 64 + lane];
-                    }
+                // whole-state sums of token u on wave u mod 4: the per-wave partials of
+                // dalpha, dbeta, dgamma and the sum for dD; dA and dD are accumulated over the
+                // tokens when the block is written out
+                for (int u = tid >> 6; u < nb; u += NT / 64) {
+                    const int j = jb - u;
+                    const float* Xc = sX + (j + 1) * RP;
+                    const float* Dc = sDY + j * RP;
+                    const float* rd = sRed + u * 3 * (NT / 64);
+                    float sd = 0.f;
                     for (int o = lane; o < RP; o += 64) sd += Dc[o] * Xc[o];
-                    sa = wave_sum(sa);   // DPP, fixed order, all 64 lanes of this wave active
-                    sb = wave_sum(sb);
-                    sg = wave_sum(sg);
-                    sd = wave_sum(sd);
-                    if (tid == sw * 64) {
+                    sd = wave_sum(sd);   // DPP, fixed order, all 64 lanes of this wave active
+                    if (lane == 0) {
+                        float sa = 0.f, sbt = 0.f, sg = 0.f;
+                        for (int w = 0; w < NT / 64; ++w) {
+                            sa += rd[w];
+                            sbt += rd[NT / 64 + w];
+                            sg += rd[2 * (NT / 64) + w];
+                        }
+                        float al, be, ga;
+                        coeffs(j, &al, &be, &ga);
                         const float dtv = sSc[4 * j], lv = sSc[4 * j + 1], av = sSc[4 * j + 2];
                         float* so = sOut + j * OW + ntask;
-                        so[0] = sa * av * al + sb * (1.f - lv) * (al + dtv * av * al) + sg * lv;
-                        so[1] = -sb * dtv * al + sg * dtv;
-                        const float dav = sa * dtv * al + sb * (1.f - lv) * dtv * dtv * al;
-                        so[2] = dav;
-                        if (!a.At) dA_acc += dav;
-                        dD_acc += sd;
+                        so[0] = sa * av * al + sbt * (1.f - lv) * (al + dtv * av * al) + sg * lv;
+                        so[1] = -sbt * dtv * al + sg * dtv;
+                        so[2] = sa * dtv * al + sbt * (1.f - lv) * dtv * dtv * al;
+                        so[3] = sd;
                     }
                 }
-                __syncthreads();   // the sums are read before the next token overwrites them
-                an = al;
-                bn = be;
-#pragma unroll
-                for (int i = 0; i < EPT; ++i) {
-                    hcur[i] = hpv[i];
-                    hpv[i] = hnx[i];
-                }
+                __syncthreads();   // the sums are read before the next batch overwrites them
             }
             // the block's outputs (visible after the last token's barrier), once per block
             const int64_t tf = tb + t0 + bt;   // first token of the block in the packed arrays
@@ -444,6 +581,13 @@ __global__ __launch_bounds__(NT) void bwd_generic(BwdArgs a, int64_t ks, int TB)
                 a.ddt[(tf + j) * H + h] = so[0];
                 a.dlam[(tf + j) * H + h] = so[1];
                 if (a.At) a.dA[(tf + j) * H + h] = so[2];
+            }
+            if (tid == sw * 64) {   // tokens last to first, as they were reversed
+                for (int j = nt - 1; j >= 0; --j) {
+                    const float* so = sOut + j * OW + 2 * RN + KP + RP;
+                    if (!a.At) dA_acc += so[2];
+                    dD_acc += so[3];
+                }
             }
         }
     }
@@ -508,16 +652,31 @@ bool backward_generic_supported(const BwdShape& s) {
            (s.N / 2) * s.P <= bg::NT * bg::kMaxEPT && s.R >= 1 && s.R <= bg::kMaxR;
 }
 
-// Tokens staged per block: the most of 16, 8, 4, 2 whose LDS stays within 128 KB (a
-// workgroup holds a CU alone: its registers allow no second), else 1.
-int backward_generic_tb(const BwdShape& s) {
-    for (int tb = 16; tb > 1; tb /= 2)
-        if (static_cast<size_t>(bg::Lds(s.N, s.P, s.R, tb).total) * sizeof(float) <= 128 * 1024) return tb;
-    return 1;
+// Tokens staged per block (TB, a power of two up to 16) and tokens per batch of sums (TS, a
+// power of two up to TB): the pair with the fewest barriers per token (2 / TB + 2 / TS)
+// whose LDS stays within 128 KB (a workgroup holds a CU alone: its registers allow no
+// second), the larger TB on a tie.
+static void backward_generic_blocks(const BwdShape& s, int* tb_out, int* ts_out) {
+    int best_tb = 1, best_ts = 1;
+    double best = 3.0;
+    for (int tb = 16; tb >= 1; tb /= 2)
+        for (int ts = tb; ts >= 1; ts /= 2) {
+            const double cost = 1.0 / tb + 1.0 / ts;
+            if (static_cast<size_t>(bg::Lds(s.N, s.P, s.R, tb, ts).total) * sizeof(float) <= 128 * 1024 &&
+                cost < best - 1e-9) {
+                best = cost;
+                best_tb = tb;
+                best_ts = ts;
+            }
+        }
+    *tb_out = best_tb;
+    *ts_out = best_ts;
 }
 
 size_t backward_generic_lds(const BwdShape& s) {
-    return static_cast<size_t>(bg::Lds(s.N, s.P, s.R, backward_generic_tb(s)).total) * sizeof(float);
+    int tb, ts;
+    backward_generic_blocks(s, &tb, &ts);
+    return static_cast<size_t>(bg::Lds(s.N, s.P, s.R, tb, ts).total) * sizeof(float);
 }
 
 // Tokens per recompute segment at each checkpoint level: level 0 the whole sequence (every
@@ -569,22 +728,23 @@ BwdLayout backward_generic_layout(const BwdShape& s, int level) {
 }
 
 template <typename T, int EPT>
-static hipError_t launch_generic_e(const BwdArgs& a, const BwdLayout& l, int tb, size_t lds, dim3 grid, hipStream_t st) {
+static hipError_t launch_generic_e(const BwdArgs& a, const BwdLayout& l, int tb, int ts, size_t lds, dim3 grid,
+                                   hipStream_t st) {
     const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&bg::bwd_generic<T, EPT>), lds);
     if (e != hipSuccess) return e;
-    bg::bwd_generic<T, EPT><<<grid, bg::NT, lds, st>>>(a, l.ks, tb);
+    bg::bwd_generic<T, EPT><<<grid, bg::NT, lds, st>>>(a, l.ks, tb, ts);
     return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t launch_generic_t(const BwdArgs& a, const BwdLayout& l, int ept, int tb, size_t lds, dim3 grid,
-                                   hipStream_t st) {
+static hipError_t launch_generic_t(const BwdArgs& a, const BwdLayout& l, int ept, int tb, int ts, size_t lds,
+                                   dim3 grid, hipStream_t st) {
     switch (ept) {
-        case 1: return launch_generic_e<T, 1>(a, l, tb, lds, grid, st);
-        case 2: return launch_generic_e<T, 2>(a, l, tb, lds, grid, st);
-        case 4: return launch_generic_e<T, 4>(a, l, tb, lds, grid, st);
-        case 8: return launch_generic_e<T, 8>(a, l, tb, lds, grid, st);
-        default: return launch_generic_e<T, 16>(a, l, tb, lds, grid, st);
+        case 1: return launch_generic_e<T, 1>(a, l, tb, ts, lds, grid, st);
+        case 2: return launch_generic_e<T, 2>(a, l, tb, ts, lds, grid, st);
+        case 4: return launch_generic_e<T, 4>(a, l, tb, ts, lds, grid, st);
+        case 8: return launch_generic_e<T, 8>(a, l, tb, ts, lds, grid, st);
+        default: return launch_generic_e<T, 16>(a, l, tb, ts, lds, grid, st);
     }
 }
 
@@ -604,14 +764,15 @@ hipError_t launch_backward_generic(BwdArgs a, const BwdLayout& l, hipStream_t st
     a.parts = 1;
     a.seg_per_part = l.seg_per_part;
     const BwdShape s{a.batch, a.L, a.H, a.G, a.N, a.P, a.R};
-    const int tb = backward_generic_tb(s);
+    int tb, ts;
+    backward_generic_blocks(s, &tb, &ts);
     const size_t lds = backward_generic_lds(s);
     const dim3 grid(static_cast<unsigned>(a.batch * a.H));
     hipError_t e;
     const int pairs = (a.N / 2) * a.P;
     const int ept = pairs <= bg::NT ? 1 : pairs <= 2 * bg::NT ? 2 : pairs <= 4 * bg::NT ? 4 : pairs <= 8 * bg::NT ? 8 : 16;
-    if ((e = a.bf16 ? launch_generic_t<bf16_t>(a, l, ept, tb, lds, grid, st)
-                    : launch_generic_t<float>(a, l, ept, tb, lds, grid, st)) != hipSuccess)
+    if ((e = a.bf16 ? launch_generic_t<bf16_t>(a, l, ept, tb, ts, lds, grid, st)
+                    : launch_generic_t<float>(a, l, ept, tb, ts, lds, grid, st)) != hipSuccess)
         return e;
     return launch_backward_sums(a, l, st);
 }

@@ -7,7 +7,8 @@ and columns the kernel takes (N = 256; P = 256), rank up to 8, groups shared by 
 heads and one head per group, fp32 and bf16 io, a state and carry passed in, a final-state
 cotangent, a single token and none; packed variable-length batches (per sequence), a
 per-token decay rate, and the checkpoint budget (bit-identical gradients for any segment
-length).  Bar: 1e-3 max relative error per gradient tensor, as for the fast kernel."""
+length), with the reverse sweep's sums taken in batches of 1 to 16 tokens (full and ragged).
+Bar: 1e-3 max relative error per gradient tensor, as for the fast kernel."""
 import numpy as np
 import pytest
 import torch
@@ -59,6 +60,7 @@ CASES = [
     (1, 100, 2, 1, 4, 2, 5, "fp32", False, False),     # N = 2: one rotation pair
     (1, 40, 2, 1, 256, 32, 1, "bf16", True, True),     # P = 256
     (1, 45, 3, 3, 16, 256, 2, "fp32", True, True),     # N = 256
+    (2, 45, 2, 1, 64, 32, 2, "fp32", True, True),      # 16-token blocks, sums in batches of 4 (ragged: 13 = 4+4+4+1)
 ]
 
 
