@@ -115,10 +115,15 @@ def test_backward_varlen_equal_lengths_match_uniform_batch():
         assert torch.equal(g1[k].reshape(g2[k].shape), g2[k]), k
 
 
-@pytest.mark.parametrize("case", CASES, ids=_id)
+# packed batches whose grouped checkpoint level needs less workspace than one level (the
+# level a one-byte budget selects): split into pieces of 30 and 39 tokens, and no split
+GROUP_CASES = [CASES[0], ([1200, 63, 1, 500], 2, 2, 4, "fp32", False, True), CASES[2]]
+
+
+@pytest.mark.parametrize("case", GROUP_CASES, ids=_id)
 def test_backward_varlen_checkpoint_groups_give_the_same_bits(case):
-    """Checkpoint groups (forced by a one-byte budget) in a packed batch: short sequences end
-    inside or before a group; every gradient is bit-identical to the one-level run."""
+    """Checkpoint groups (selected by a one-byte budget) in a packed batch: short sequences
+    end inside or before a group; every gradient is bit-identical to the one-level run."""
     lengths, H, G, R, io, with_state, with_dh = case
     ns, Lmax = len(lengths), max(lengths)
     d, cu, T = _pack(lengths, H, G, R, io, seed=sum(lengths) + 2 * R)
@@ -133,6 +138,8 @@ def test_backward_varlen_checkpoint_groups_give_the_same_bits(case):
                                 torch.randn((ns, H, R, P), generator=gen).to(tdt).cuda())
     g1 = m3scan.backward_varlen(*[d[k] for k in NAMES], dy, cu, Lmax, dh_out=dh, state_in=st)
     torch.cuda.synchronize()
+    dims = m3scan.make_dims(ns, Lmax, H, G, P, N, R, 1, 0 if io == "fp32" else 1)
+    assert m3scan.backward_workspace_size(dims, 1) < m3scan.backward_workspace_size(dims)   # grouped
     g2 = m3scan.backward_varlen(*[d[k] for k in NAMES], dy, cu, Lmax, dh_out=dh, state_in=st, checkpoint_bytes=1)
     torch.cuda.synchronize()
     say("backward varlen checkpoint groups", _id(case))
