@@ -490,3 +490,21 @@ def test_generic_backward_workspace(lib):
     d2 = _dims(batch=b, nheads=H, ngroups=1, headdim=P, dstate=N, rank=R, seqlen=L)
     per_head = b * L * H * (2 * R * N + N // 2) * 4 + b * H * R * N * 4
     assert _bwd_ws(lib, d2) >= wall + per_head
+
+
+def test_binding_backward_workspace_choice(lib):
+    """The binding's backward workspace (host-side marshalling, CPU tensors here): a new one
+    of the size the budget asks for; a caller's larger one whole (the call then keeps as many
+    states as it holds); a caller's smaller one replaced."""
+    import torch
+    d = _dims(batch=2, seqlen=1000, nheads=4, ngroups=1, headdim=12, dstate=24, rank=3)
+    need = m3scan.backward_workspace_size(d, 1)
+    n, ws = m3scan._backward_workspace(d, None, "cpu", 1)
+    assert n == need and ws.numel() == need and ws.dtype == torch.uint8
+    big = torch.empty(need * 3, dtype=torch.uint8)
+    n, ws = m3scan._backward_workspace(d, big, "cpu", 1)
+    assert n == need * 3 and ws is big
+    small = torch.empty(need - 1, dtype=torch.uint8)
+    n, ws = m3scan._backward_workspace(d, small, "cpu", 1)
+    assert n == need and ws is not small and ws.numel() == need
+    assert m3scan.backward_workspace_size(d) == m3scan.backward_workspace_size(d, 4 << 30)
