@@ -232,7 +232,8 @@ def mfma_util_rocprof(workload):
         if rec.get("source_sha") != source_sha(*rec["source_files"]):
             return None
         kernels = rec["workloads"][workload]["kernels"]
-        full = next(v for k, v in kernels.items() if k.endswith("true, false, false>"))   # output pass, no gate or norm
+        # output pass, no gate or norm, one sequence per workgroup
+        full = next(v for k, v in kernels.items() if k.endswith("true, false, false, false>"))
         return round(full["mfma_util_percent"] / 100.0, 4)
     except Exception:
         return None

@@ -104,6 +104,18 @@ typedef struct {
  * Errors: M3_ERR_INVALID_ARG for bad dims or a NULL `bytes`. */
 m3_status m3_prefill_workspace_size(const m3_dims* dims, size_t* bytes);
 
+/* How many sequences of the batch one workgroup of the chunked prefill sweeps, one
+ * after another, for these dims (m3_prefill_chunked without fusion).  A single
+ * short sequence leaves its workgroup waiting on its own loads; batches of many
+ * equal-length sequences of one to four whole chunks (the hardware-aware scan of
+ * IBM's "What is a Mamba model?", parallel over sequences and heads) are therefore
+ * swept several to a workgroup, the next sequence's first chunk fetched while the
+ * current one computes, its state reset at the boundary.  1 means one sequence
+ * per workgroup.  The choice depends on the dims only and does not change any
+ * result bit.  Errors as m3_prefill_workspace_size, and M3_ERR_UNSUPPORTED for
+ * dims no prefill kernel takes. */
+m3_status m3_prefill_sequences_per_workgroup(const m3_dims* dims, int32_t* seqs);
+
 /*
  * Chunked prefill: the whole sequence of `seqlen` tokens for every (b, h).
  * Computes y (batch, L, H, R, P) in the io dtype, rounded to nearest even from

@@ -180,6 +180,15 @@ m3_status m3_prefill_workspace_size(const m3_dims* dims, size_t* bytes) {
     return M3_OK;
 }
 
+m3_status m3_prefill_sequences_per_workgroup(const m3_dims* dims, int32_t* seqs) {
+    if (!seqs || !dims_ok(dims, true)) return M3_ERR_INVALID_ARG;
+    const m3::PrefillArgs a = make_prefill_args(dims);
+    const m3::PrefillPlan plan = m3::plan_prefill(a);
+    if (plan.path == m3::PrefillPath::Unsupported) return M3_ERR_UNSUPPORTED;
+    *seqs = (plan.path == m3::PrefillPath::Mfma && plan.seqs > 1) ? plan.seqs : 1;
+    return M3_OK;
+}
+
 m3_status m3_prefill_fused_workspace_size(const m3_dims* dims, const m3_fusion* fusion, size_t* bytes) {
     if (!bytes || !fusion || !dims_ok(dims, true)) return M3_ERR_INVALID_ARG;
     m3::PrefillArgs a = make_prefill_args(dims);

@@ -90,6 +90,7 @@ struct PrefillPlan {
     int nseg;                // segments per sequence (1 = one sweep per (b, h))
     int chunks_per_seg;      // chunks of each segment (the last may be shorter)
     int state_split;         // pieces each summarised segment is cut into for the state-only pass
+    int seqs;                // matrix-core path: sequences swept one after another per workgroup
     size_t workspace;        // bytes
     size_t lds;              // dynamic LDS bytes of the main kernel
     size_t carry_off;        // workspace offset of the normalised carried-in B (fused calls)

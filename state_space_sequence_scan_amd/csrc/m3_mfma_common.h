@@ -112,6 +112,9 @@ struct ScanParams {
     const float* onw;       // output RMSNorm weight (H, P), or null
     float eps;              // its epsilon
     int Gt;                 // angle groups: the prepared operands are per (b, angle group, chunk)
+    int seqs;               // sequences per workgroup of the output pass (equal lengths, whole chunks,
+                            // one angle group, one segment): seqs * w .. + seqs - 1, one after another
+    int batch;              // sequences in the batch
 };
 
 // Initial state of segment 0 when no segment pass ran: h_in plus the beta term

@@ -181,7 +181,7 @@ constexpr bool kTwoPerCu = (Q * R == 128);
 template <int R, int Q, bool FULL>
 constexpr int kWavesPerSimd = (FULL && kTwoPerCu<R, Q>) ? 2 : 1;
 
-template <int R, int Q, int NW, bool FULL, bool GATE, bool ONORM>
+template <int R, int Q, int NW, bool FULL, bool GATE, bool ONORM, bool MULTI = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<R, Q, FULL>)))
 void scan_mfma(ScanParams p) {
     constexpr int NTH = 64 * NW;
@@ -214,6 +214,13 @@ void scan_mfma(ScanParams p) {
 
     int seg, h, b;
     xcd_decode(blockIdx.x, gridDim.x, p.H, FULL ? p.nseg : p.nseg - 1, &b, &h, &seg);
+    // MULTI: several short sequences per workgroup.  Sequences b .. b + nseq - 1 of head h
+    // are swept as one run of chunks (they are adjacent in the token axis and each holds a
+    // whole number of chunks), so each one's first chunk is fetched while the previous one
+    // computes.  Where a sequence ends its look-ahead weight stops, its state is written out
+    // and the state is reset to the next sequence's initial one.
+    if (MULTI) b *= p.seqs;
+    const int nseq = MULTI ? min(p.seqs, p.batch - b) : 1;
     const int g = h / (p.H / p.G);
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
@@ -223,7 +230,7 @@ void scan_mfma(ScanParams p) {
     const PrepLayout lay{QR};
     const float Ah = p.A[h];
     const SeqSpan sp = seq_span(p.cu, b, p.L, p.T);
-    const int64_t tb = sp.start, Lb = sp.len;    // this sequence's first token and length
+    const int64_t tb = sp.start, Lb = sp.len * nseq;   // first token and length of the sweep
     const int nchunks_b = static_cast<int>((Lb + Q - 1) / Q);
     const int c_begin = seg * p.chunks_per_seg;
     const int c_end = min(nchunks_b, c_begin + p.chunks_per_seg);
@@ -270,10 +277,22 @@ void scan_mfma(ScanParams p) {
 
     // ---- state accumulators: rows n = n0 + 16rt + 4lg + i, columns p = p0 + 16ct + l16
     f32x4 sacc[RT][CT];
-    if (FULL) {
+    // initial state of sequence bs (first token tok0) when no segment pass ran
+    auto init_state = [&](int bs, int64_t tok0) __attribute__((always_inline)) {
         const float c1 = (Lb > 0 && p.bl_in && p.xl_in)
-                             ? (1.f - p.lam[tb * p.H + h]) * p.dt[tb * p.H + h]
+                             ? (1.f - p.lam[tok0 * p.H + h]) * p.dt[tok0 * p.H + h]
                              : 0.f;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sacc[rt][ct][i] = initial_state<R>(p, bs, h, g, n0 + 16 * rt + 4 * lg + i, p0 + 16 * ct + l16, c1);
+    };
+    // final state of sequence bs
+    auto store_state = [&](int bs) __attribute__((always_inline)) {
+        const size_t ho = (static_cast<size_t>(bs) * p.H + h) * N * P;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -281,11 +300,24 @@ void scan_mfma(ScanParams p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int n = n0 + 16 * rt + 4 * lg + i, col = p0 + 16 * ct + l16;
-                    sacc[rt][ct][i] =
-                        p.s_init ? p.s_init[((static_cast<size_t>(b) * p.H + h) * p.sinit_stride +
-                                             static_cast<size_t>(p.sinit_step) * seg) * N * P + n * P + col]
-                                 : initial_state<R>(p, b, h, g, n, col, c1);
+                    state_store(p.h_out, ho + n * P + col, sacc[rt][ct][i], p.state_bf16);
                 }
+    };
+    if (FULL) {
+        if (p.s_init) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int n = n0 + 16 * rt + 4 * lg + i, col = p0 + 16 * ct + l16;
+                        sacc[rt][ct][i] = p.s_init[((static_cast<size_t>(b) * p.H + h) * p.sinit_stride +
+                                                    static_cast<size_t>(p.sinit_step) * seg) * N * P + n * P + col];
+                    }
+        } else {
+            init_state(b, tb);
+        }
     } else {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -298,6 +330,7 @@ void scan_mfma(ScanParams p) {
     u32v<4 * BPT> br;           // Bt units tid + NTH*e
     float pd0 = 0.f, pl0 = 0.f, pd1 = 0.f, pl1 = 0.f, pa0 = 0.f, pcs = 0.f;
     int pnq = 0;                // valid tokens of the prefetched chunk
+    bool pend = false;          // the prefetched chunk closes a sequence of a multi-sequence sweep
     bfv<32> cf0, cf1;           // Ct fragments (4 k-steps) of the wave's output row blocks a_lo, a_hi
 
     // Per-workgroup base pointers are uniform (scalar registers); per-lane offsets
@@ -309,13 +342,22 @@ void scan_mfma(ScanParams p) {
     // and the compiler places its waits for the fewest operations any path issues
     // after a load; with equal sequences the wait for this chunk's operands never
     // drains the prefetch of the chunk after next.
-#define M3_PREP(c_) (p.prep + (gbase + (c_)) * lay.bytes())
+    // prepared operands of chunk c of the sweep (with MULTI: chunk c % nchunks of sequence b + c / nchunks)
+    const int gq = h / (p.H / p.Gt);
+    auto prep_index = [&](int c) __attribute__((always_inline)) -> size_t {
+        if constexpr (MULTI)
+            return (static_cast<size_t>(b + c / p.nchunks) * p.Gt + gq) * p.nchunks + c % p.nchunks;
+        else
+            return gbase + c;
+    };
+#define M3_PREP(c_) (p.prep + prep_index(c_) * lay.bytes())
 
 #define M3_FETCH_X(c_)                                                                                        \
     do {                                                                                                      \
         const int64_t t0f = static_cast<int64_t>(c_) * Q;                                                     \
         const int nqf = static_cast<int>(Lb - t0f < Q ? Lb - t0f : Q);                                        \
         pnq = nqf;                                                                                            \
+        pend = MULTI && ((c_) + 1) % p.nchunks == 0;                                                          \
         {                                                                                                     \
             const uint16_t* xch = p.x + ((tb + t0f) * p.H + h) * static_cast<int64_t>(R * P);                 \
             _Pragma("unroll") for (int e = 0; e < XPT; ++e) {                                                 \
@@ -367,7 +409,7 @@ void scan_mfma(ScanParams p) {
         if (w == 0) {                                                                                         \
             const bool valid = lane < pnq;                                                                    \
             const float dtv = valid ? pd0 : 0.f, lv = valid ? pl0 : 0.f;                                      \
-            const bool has1 = valid && (nextpos + lane + 1 < Lb);                                             \
+            const bool has1 = valid && (nextpos + lane + 1 < Lb) && !(pend && lane == Q - 1);                 \
             const float gm = lv * dtv;                                                                        \
             const float wv = gm + (has1 ? (1.f - pl1) * pd1 : 0.f);                                           \
             float cum = dtv * (p.At ? pa0 : Ah);                                                              \
@@ -611,6 +653,9 @@ void scan_mfma(ScanParams p) {
     if (FULL) M3_WRITE_SST();
     __syncthreads();
 
+    // the state entering the current chunk is exactly zero (uniform): no incoming state
+    const bool zero_init = !p.s_init && !p.h_in && !(p.bl_in && p.xl_in);
+    bool zero_in = MULTI && zero_init;
     float dec_total = 0.f;                 // state-only: sum of chunk log-decays
     float rot_c = 1.f, rot_s = 0.f;        // state-only: total rotation of pair tid (tid < KP)
 
@@ -636,8 +681,18 @@ void scan_mfma(ScanParams p) {
             uint2 zr[4];   // gate input of the row block being finished (GATE only)
             if constexpr (GATE) M3_LOAD_Z(zr, a_lo);
             // (4a) inter-chunk term; with two row blocks the S^T fragments serve both.  The
-            // fragments of column tile ct + 1 are read while tile ct is multiplied.
-            {
+            // fragments of column tile ct + 1 are read while tile ct is multiplied.  In a
+            // multi-sequence sweep a state known to be zero (a sequence's first chunk without
+            // an incoming state) adds nothing, and the products are skipped (not in the
+            // one-sequence kernels: there it would save one chunk's term per sequence, and
+            // the branch costs the waits of every other chunk).
+            if (MULTI && zero_in) {
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    y0[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    y1[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            } else {
                 bf16x8 sf[2][4];
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) sf[0][ks] = lds_ld<bf16x8>(aST + (32 * ks) * 2);
@@ -657,9 +712,9 @@ void scan_mfma(ScanParams p) {
                         if (MB == 2) y1[ct] = mfma_k32(sf[ct & 1][ks], oct(cf1, ks), y1[ct]);
                     }
                 }
+                M3_INTER_SCALE(y0, a_lo);
+                if (MB == 2) M3_INTER_SCALE(y1, a_hi);
             }
-            M3_INTER_SCALE(y0, a_lo);
-            if (MB == 2) M3_INTER_SCALE(y1, a_hi);
             // (4b) intra-chunk tiles, column blocks in order; the diagonal tile closes a row block.
             // Two register sets: the operands of the next column block are read from LDS
             // while the current block is multiplied.
@@ -842,8 +897,16 @@ void scan_mfma(ScanParams p) {
         if (has_next) M3_STAGE_SCALARS(q ^ 1);   // the other parity slot: nobody reads it now
         __syncthreads();   // this chunk's tiles, S_{c-1} and the column factors no longer read;
                            // next chunk's scalars visible
-        if (FULL) M3_WRITE_SST();
+        const bool seq_end = MULTI && has_next && (c + 1) % p.nchunks == 0;   // uniform
+        if (FULL && !seq_end) M3_WRITE_SST();
         if (has_next) M3_STAGE_TILES(q ^ 1);
+        zero_in = MULTI && seq_end && zero_init;
+        if (MULTI && seq_end) {   // after the staging, when the prefetch registers are free
+            const int bs = b + c / p.nchunks;
+            if (p.h_out) store_state(bs);
+            init_state(bs + 1, tb + static_cast<int64_t>(c + 1) * Q);
+            M3_WRITE_SST();
+        }
         if (!FULL) {   // state-only mode has no output phase to hide the loads behind: a chunk further ahead
             const int cf = c + 2 < c_end ? c + 2 : c_end - 1;
             M3_FETCH(cf);
@@ -871,18 +934,7 @@ void scan_mfma(ScanParams p) {
 
     // epilogue
     if (FULL) {
-        if (last_seg && p.h_out) {
-            const size_t ho = (static_cast<size_t>(b) * p.H + h) * N * P;
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int n = n0 + 16 * rt + 4 * lg + i, col = p0 + 16 * ct + l16;
-                        state_store(p.h_out, ho + n * P + col, sacc[rt][ct][i], p.state_bf16);
-                    }
-        }
+        if (last_seg && p.h_out) store_state(b + nseq - 1);
     } else {
         const size_t sidx = (static_cast<size_t>(b) * p.H + h) * (p.nseg - 1) + seg;
         float* so = p.seg_state + sidx * N * P;
@@ -1031,6 +1083,21 @@ static MfmaWs mfma_ws(const PrefillArgs& a, int nchunks, int nseg, int split) {
     return w;
 }
 
+// Sequences per workgroup of the output pass.  A workgroup that sweeps one short sequence
+// pays its whole load latency up front: nothing of the next chunk is in flight while the
+// first one computes.  Equal-length batches whose sequences hold a few whole chunks each
+// and whose (b, h) pairs fill at least four rounds of workgroups therefore give each
+// workgroup several sequences of one head (about 16 chunks in all), swept one after another
+// (plain calls only: no gate, no output norm).
+static int choose_seqs(const PrefillArgs& a, int nchunks, int nseg) {
+    if (a.cu || nseg != 1 || nchunks < 1 || nchunks > 4 || a.L % a.Q != 0 || a.fu.z || a.fu.onw) return 1;
+    int64_t s = (16 + nchunks - 1) / nchunks;
+    const int64_t cap = a.batch * a.H / (4 * scan_slots(a));
+    if (s > cap) s = cap;
+    if (s > a.batch) s = a.batch;
+    return s < 2 ? 1 : static_cast<int>(s);
+}
+
 void plan_mfma(const PrefillArgs& a, PrefillPlan* plan) {
     const int nchunks = static_cast<int>((a.L + a.Q - 1) / a.Q);
     // packed variable-length batches run each sequence in one sweep
@@ -1040,10 +1107,13 @@ void plan_mfma(const PrefillArgs& a, PrefillPlan* plan) {
     if (split > 1) cps = split * ((cps + split - 1) / split);   // pieces of equal length
     if (nchunks > 0) nseg = (nchunks + cps - 1) / cps;           // no empty trailing segment
     if (nseg < 2) split = 1;
+    const int seqs = choose_seqs(a, nchunks, nseg);
+    if (seqs > 1) cps = seqs * nchunks;                          // one sweep over all of them
     plan->path = PrefillPath::Mfma;
     plan->nseg = nseg;
     plan->chunks_per_seg = cps;
     plan->state_split = split;
+    plan->seqs = seqs;
     plan->workspace = mfma_ws(a, nchunks, nseg, split).total;
     plan->lds = 0;
 }
@@ -1096,6 +1166,8 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
     p.nchunks = nchunks;
     p.nseg = nseg;
     p.chunks_per_seg = cps;
+    p.seqs = plan.seqs;
+    p.batch = static_cast<int>(a.batch);
     if (nseg > 1) {
         // state-only pass and segment pass over the pieces (split per summarised segment)
         mf::ScanParams ps = p;
@@ -1116,6 +1188,12 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
         p.s_init = s_init;
         p.sinit_stride = pieces + 1;
         p.sinit_step = split;
+    }
+    if (plan.seqs > 1) {   // plain calls only (choose_seqs)
+        const int64_t groups = (a.batch + plan.seqs - 1) / plan.seqs;
+        hipLaunchKernelGGL((mf::scan_mfma<R, Q, NW, true, false, false, true>),
+                           dim3(static_cast<unsigned>(groups * a.H)), dim3(64 * NW), 0, st, p);
+        return hipGetLastError();
     }
     auto scan = p.onw ? (p.z ? mf::scan_mfma<R, Q, NW, true, true, true> : mf::scan_mfma<R, Q, NW, true, false, true>)
                       : (p.z ? mf::scan_mfma<R, Q, NW, true, true, false> : mf::scan_mfma<R, Q, NW, true, false, false>);

@@ -104,6 +104,8 @@ def lib(path: str = LIB_PATH):
     L.m3_backward_per_token_A.restype = ctypes.c_int
     L.m3_backward_per_token_A.argtypes = ([ctypes.POINTER(Dims), vp, ctypes.c_int64] + [vp] * 8 +
                                           [ctypes.POINTER(State), vp, vp, ctypes.POINTER(Grads), vp, sz, vp])
+    L.m3_prefill_sequences_per_workgroup.restype = ctypes.c_int
+    L.m3_prefill_sequences_per_workgroup.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(ctypes.c_int32)]
     L.m3_backward_parts.restype = ctypes.c_int
     L.m3_backward_parts.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(ctypes.c_int32),
                                     ctypes.POINTER(ctypes.c_int64)]
@@ -407,6 +409,15 @@ def backward_workspace_size(dims: Dims, checkpoint_bytes: Optional[int] = None) 
         rc = lib().m3_backward_workspace_size_budget(ctypes.byref(dims), int(checkpoint_bytes), ctypes.byref(n))
     if rc != 0:
         raise M3Error("m3_backward_workspace_size", rc)
+    return int(n.value)
+
+
+def prefill_sequences_per_workgroup(dims: Dims) -> int:
+    """How many sequences one workgroup of m3_prefill_chunked sweeps one after another."""
+    n = ctypes.c_int32(0)
+    rc = lib().m3_prefill_sequences_per_workgroup(ctypes.byref(dims), ctypes.byref(n))
+    if rc != 0:
+        raise M3Error("m3_prefill_sequences_per_workgroup", rc)
     return int(n.value)
 
 

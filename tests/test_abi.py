@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     assert declared_symbols() == ["m3_backward", "m3_backward_parts", "m3_backward_per_token_A", "m3_backward_varlen",
                                   "m3_backward_workspace_size", "m3_backward_workspace_size_budget", "m3_decode_step",
                                   "m3_decode_step_fused", "m3_prefill_chunked", "m3_prefill_chunked_noalloc", "m3_prefill_fused",
-                                  "m3_prefill_fused_workspace_size",
+                                  "m3_prefill_fused_workspace_size", "m3_prefill_sequences_per_workgroup",
                                   "m3_prefill_varlen", "m3_prefill_varlen_fused", "m3_prefill_workspace_size", "m3_status_string",
                                   "m3_version"]
 
@@ -313,6 +313,32 @@ def test_backward_parts(lib):
     # the generic kernel (off the fast shape) never splits
     for L in (0, 5, 5000):
         assert m3scan.backward_parts(_dims(batch=1, nheads=2, seqlen=L)) == (1, L)
+
+
+def test_prefill_sequences_per_workgroup(lib):
+    """The matrix-core prefill sweeps several sequences per workgroup only for equal-length
+    batches of one to four whole chunks whose (b, h) pairs fill at least eight rounds of
+    workgroups (two sequences each, four rounds), about 16 chunks per workgroup, never more
+    than the batch; everything else runs one sequence per workgroup."""
+    def seqs(**kw):
+        base = dict(batch=4096, seqlen=64, nheads=64, ngroups=1, headdim=64, dstate=128, rank=4, chunk=64,
+                    io_dtype=m3scan.M3_BF16)
+        base.update(kw)
+        return m3scan.prefill_sequences_per_workgroup(m3scan.Dims(**base))
+    assert seqs() == 16                                   # one chunk each: 16 per workgroup
+    assert seqs(seqlen=128) == 8 and seqs(seqlen=256) == 4
+    assert seqs(seqlen=320) == 1                          # five chunks
+    assert seqs(seqlen=100) == 1                          # a partial chunk
+    assert seqs(batch=32) == 2                            # 2048 pairs at one workgroup per CU: 8 rounds
+    assert seqs(batch=31) == 1
+    assert seqs(rank=1, batch=64) == 2                    # two workgroups per CU at 64 rows: 512 slots
+    assert seqs(rank=1, batch=63) == 1
+    assert seqs(ngroups=8) == 16                          # groups of heads sharing B and C
+    assert seqs(headdim=16, dstate=16, io_dtype=m3scan.M3_F32) == 1   # not the matrix-core path
+    n = ctypes.c_int32(0)
+    good = _dims()
+    assert lib.m3_prefill_sequences_per_workgroup(ctypes.byref(good), None) == -1
+    assert lib.m3_prefill_sequences_per_workgroup(ctypes.byref(_dims(batch=0)), ctypes.byref(n)) == -1
 
 
 def test_launch_size_limits(lib):
