@@ -151,6 +151,17 @@ __device__ __forceinline__ float swap_adjacent(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
 }
 
+// Sum over each 16-lane row of a wave (DPP quad swaps, then rotations within the row, the
+// first steps of wave_sum); every lane gets its row's sum.  The 16 lanes of a row must all
+// be active.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_move<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+    v += dpp_move<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+    v += dpp_move<0x124>(v);   // row_ror 4
+    v += dpp_move<0x128>(v);   // row_ror 8
+    return v;
+}
+
 // Workgroups are dispatched to the 8 XCDs round-robin by linear id, and each
 // XCD has its own L2.  The heads of one (batch, segment) group read the same
 // prepared Bt/Ct, so the linear id is permuted to place a group's heads on one

@@ -112,55 +112,71 @@ __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
         }
     }
     __syncthreads();
-    // One unit = 8 consecutive rows (token, rank) x one rotation pair k:
-    // R(-phi) (x0, x1) = (c x0 + s x1, -s x0 + c x1), stored as 4 bytes per row.
-    // With KP = 64 pairs and NT a multiple of 64, the 64 pairs of a row are the 64
-    // lanes of one wave, so a row's RMSNorm (before the rotation) is a wave sum.
-    static_assert(KP == 64 && NT % 64 == 0, "one wave per row");
+    // One unit = one row (token, rank) x 4 consecutive rotation pairs k0 .. k0 + 3: 16 bytes
+    // of B and of C per lane, a row on 16 lanes (so a row's RMSNorm before the rotation is
+    // a sum over 16 lanes).  R(-phi) (x0, x1) = (c x0 + s x1, -s x0 + c x1).  Rows past the
+    // sequence end read the last token's operands and store zeros, so every lane of a row
+    // takes the same path.
+    static_assert(KP == 64 && N == 128, "16 lanes per row");
     const bool bc = fu.bc();
-    for (int u = tid; u < (QR / 8) * KP; u += NT) {
-        const int r8 = u / KP, k = u - r8 * KP;
+    for (int u = tid; u < QR * 16; u += NT) {
+        const int row = u >> 4, q4 = u & 15, k0 = 4 * q4;
+        const int i = row / R, r = row - i * R;
+        const int ic = i < nq ? i : nq - 1;
+        const size_t o = (((tg + ic) * G + g) * R + r) * static_cast<size_t>(N) + 8 * q4;
+        const uint4 bb = *reinterpret_cast<const uint4*>(B + o);
+        const uint4 cc = *reinterpret_cast<const uint4*>(C + o);
+        const float4 cn4 = *reinterpret_cast<const float4*>(&sCos[ic][k0]);
+        const float4 sn4 = *reinterpret_cast<const float4*>(&sSin[ic][k0]);
+        const uint32_t bw[4] = {bb.x, bb.y, bb.z, bb.w}, cw[4] = {cc.x, cc.y, cc.z, cc.w};
+        float x[8], y[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int row = 8 * r8 + e;
-            const int i = row / R, r = row - i * R;
-            float b0 = 0.f, b1 = 0.f, c0 = 0.f, c1 = 0.f;
-            if (i < nq) {
-                const size_t o = (((tg + i) * G + g) * R + r) * static_cast<size_t>(N) + 2 * k;
-                const uint32_t bb = *reinterpret_cast<const uint32_t*>(B + o);
-                const uint32_t cc = *reinterpret_cast<const uint32_t*>(C + o);
-                const float cn = sCos[i][k], sn = sSin[i][k];
-                float x0 = bits_to_f(bb & 0xffff), x1 = bits_to_f(bb >> 16);
-                float y0 = bits_to_f(cc & 0xffff), y1 = bits_to_f(cc >> 16);
-                if (bc) {   // uniform: whole waves take this branch (i < nq is uniform per row)
-                    const int wi = r * N + 2 * k;
-                    if (fu.bnw) {
-                        const float sc = rsqrtf(wave_sum(x0 * x0 + x1 * x1) / N + fu.eps);
-                        x0 *= sc * fu.bnw[wi];
-                        x1 *= sc * fu.bnw[wi + 1];
-                    }
-                    if (fu.cnw) {
-                        const float sc = rsqrtf(wave_sum(y0 * y0 + y1 * y1) / N + fu.eps);
-                        y0 *= sc * fu.cnw[wi];
-                        y1 *= sc * fu.cnw[wi + 1];
-                    }
-                    if (fu.bbias) {
-                        x0 += fu.bbias[wi];
-                        x1 += fu.bbias[wi + 1];
-                    }
-                    if (fu.cbias) {
-                        y0 += fu.cbias[wi];
-                        y1 += fu.cbias[wi + 1];
-                    }
-                }
-                b0 = cn * x0 + sn * x1;
-                b1 = -sn * x0 + cn * x1;
-                c0 = cn * y0 + sn * y1;
-                c1 = -sn * y0 + cn * y1;
-            }
-            *reinterpret_cast<uint32_t*>(Bt + static_cast<size_t>(row) * N + 2 * k) = pack_bf16x2(b0, b1);
-            *reinterpret_cast<uint32_t*>(Ct + static_cast<size_t>(row) * N + 2 * k) = pack_bf16x2(c0, c1);
+        for (int e = 0; e < 4; ++e) {
+            x[2 * e] = bits_to_f(bw[e] & 0xffff);
+            x[2 * e + 1] = bits_to_f(bw[e] >> 16);
+            y[2 * e] = bits_to_f(cw[e] & 0xffff);
+            y[2 * e + 1] = bits_to_f(cw[e] >> 16);
         }
+        if (bc) {   // uniform
+            const int wi = r * N + 8 * q4;
+            if (fu.bnw) {
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+                const float sc = rsqrtf(row16_sum(ss) / N + fu.eps);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] *= sc * fu.bnw[wi + e];
+            }
+            if (fu.cnw) {
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss += y[e] * y[e];
+                const float sc = rsqrtf(row16_sum(ss) / N + fu.eps);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] *= sc * fu.cnw[wi + e];
+            }
+            if (fu.bbias) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] += fu.bbias[wi + e];
+            }
+            if (fu.cbias) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] += fu.cbias[wi + e];
+            }
+        }
+        const float cn[4] = {cn4.x, cn4.y, cn4.z, cn4.w}, sn[4] = {sn4.x, sn4.y, sn4.z, sn4.w};
+        uint32_t bo[4], co[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x0 = x[2 * e], x1 = x[2 * e + 1], y0 = y[2 * e], y1 = y[2 * e + 1];
+            bo[e] = pack_bf16x2(cn[e] * x0 + sn[e] * x1, -sn[e] * x0 + cn[e] * x1);
+            co[e] = pack_bf16x2(cn[e] * y0 + sn[e] * y1, -sn[e] * y0 + cn[e] * y1);
+        }
+        const bool live = i < nq;
+        *reinterpret_cast<uint4*>(Bt + static_cast<size_t>(row) * N + 8 * q4) =
+            live ? uint4{bo[0], bo[1], bo[2], bo[3]} : uint4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<uint4*>(Ct + static_cast<size_t>(row) * N + 8 * q4) =
+            live ? uint4{co[0], co[1], co[2], co[3]} : uint4{0u, 0u, 0u, 0u};
     }
 }
 
