@@ -81,6 +81,28 @@ __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
     uint16_t* Ct = reinterpret_cast<uint16_t*>(base + lay.ct());
     float* cs = reinterpret_cast<float*>(base + lay.cs());
 
+    // One unit = one row (token, rank) x 4 consecutive rotation pairs k0 .. k0 + 3: 16 bytes
+    // of B and of C per lane, a row on 16 lanes (so a row's RMSNorm before the rotation is
+    // a sum over 16 lanes).  Rows past the sequence end read the last token's operands and
+    // store zeros, so every lane of a row takes the same path.  The first units' operands
+    // are loaded before the angle sums, so that their latency overlaps that phase.
+    static_assert(KP == 64 && N == 128 && (QR * 16) % NT == 0, "16 lanes per row");
+    constexpr int UPT = QR * 16 / NT;        // units per thread
+    constexpr int PF = UPT < 4 ? UPT : 4;    // of which loaded ahead
+    auto unit_src = [&](int e) __attribute__((always_inline)) -> size_t {
+        const int u = tid + NT * e, row = u >> 4;
+        const int i = row / R, r = row - i * R;
+        const int ic = i < nq ? i : nq - 1;
+        return (((tg + ic) * G + g) * R + r) * static_cast<size_t>(N) + 8 * (u & 15);
+    };
+    uint4 pb[PF], pc[PF];
+#pragma unroll
+    for (int e = 0; e < PF; ++e) {
+        const size_t o = unit_src(e);
+        pb[e] = *reinterpret_cast<const uint4*>(B + o);
+        pc[e] = *reinterpret_cast<const uint4*>(C + o);
+    }
+
     // Chunk-local inclusive angle sums: 4 threads per pair, Q/4 tokens each.
     {
         constexpr int QP = Q / 4;
@@ -112,20 +134,23 @@ __global__ __launch_bounds__(NT) void rope_prep(const uint16_t* __restrict__ B,
         }
     }
     __syncthreads();
-    // One unit = one row (token, rank) x 4 consecutive rotation pairs k0 .. k0 + 3: 16 bytes
-    // of B and of C per lane, a row on 16 lanes (so a row's RMSNorm before the rotation is
-    // a sum over 16 lanes).  R(-phi) (x0, x1) = (c x0 + s x1, -s x0 + c x1).  Rows past the
-    // sequence end read the last token's operands and store zeros, so every lane of a row
-    // takes the same path.
-    static_assert(KP == 64 && N == 128, "16 lanes per row");
+    // The rotation, R(-phi) (x0, x1) = (c x0 + s x1, -s x0 + c x1), unit by unit.
     const bool bc = fu.bc();
-    for (int u = tid; u < QR * 16; u += NT) {
+#pragma unroll
+    for (int e8 = 0; e8 < UPT; ++e8) {
+        const int u = tid + NT * e8;
         const int row = u >> 4, q4 = u & 15, k0 = 4 * q4;
         const int i = row / R, r = row - i * R;
         const int ic = i < nq ? i : nq - 1;
-        const size_t o = (((tg + ic) * G + g) * R + r) * static_cast<size_t>(N) + 8 * q4;
-        const uint4 bb = *reinterpret_cast<const uint4*>(B + o);
-        const uint4 cc = *reinterpret_cast<const uint4*>(C + o);
+        uint4 bb, cc;
+        if (e8 < PF) {
+            bb = pb[e8];
+            cc = pc[e8];
+        } else {
+            const size_t o = unit_src(e8);
+            bb = *reinterpret_cast<const uint4*>(B + o);
+            cc = *reinterpret_cast<const uint4*>(C + o);
+        }
         const float4 cn4 = *reinterpret_cast<const float4*>(&sCos[ic][k0]);
         const float4 sn4 = *reinterpret_cast<const float4*>(&sSin[ic][k0]);
         const uint32_t bw[4] = {bb.x, bb.y, bb.z, bb.w}, cw[4] = {cc.x, cc.y, cc.z, cc.w};
