@@ -226,21 +226,27 @@ def test_theta_per_head_out_norm_workload_every_slice():
 @pytest.mark.parametrize("name", ["mimo4_chunk64_b4096", "siso_chunk64_b4096"])
 def test_intra_chunk_workload(name):
     """Single-chunk sequences (L = chunk = 64, batch 4096) at the 1.5B head shapes: one launch
-    as the benchmark times it; every head of the first and the last 256 batch elements against
-    the oracle (each sequence is one intra-chunk block plus its chunk state)."""
+    as the benchmark times it (16 sequences of a head per workgroup, swept one after
+    another); every (batch, head) slice against the oracle (each sequence is one intra-chunk
+    block plus its chunk state), 128 batch elements at a time."""
     from state_space_sequence_scan_amd.configs import INTRA_CHUNK
     cfg = INTRA_CHUNK[name]
     say("intra-chunk workload", name, cfg.label)
+    dims = m3scan.make_dims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.ngroups, cfg.headdim, cfg.dstate, cfg.rank,
+                            cfg.chunk, m3scan.M3_BF16)
+    assert m3scan.prefill_sequences_per_workgroup(dims) == 16
     d = inputs.draw_config(cfg, device="cuda")
     y, st = m3scan.prefill(d["x"], d["dt"], d["A"], d["lam"], d["theta"], d["B"], d["C"], d["D"], cfg.chunk)
     torch.cuda.synchronize()
     tally = Tally(name, TOL[cfg.io_dtype])
-    for b0 in list(range(0, 256, 64)) + list(range(cfg.batch - 256, cfg.batch, 64)):
-        b1 = b0 + 64
+    for b0 in range(0, cfg.batch, 128):
+        b1 = b0 + 128
         yr, hr = oracle.scan(*[f64(d[k][b0:b1] if d[k].dim() > 1 else d[k]) for k in
                                ("x", "dt", "A", "lam", "theta", "B", "C", "D")])
         tally.add("y", *slice_errs(f64(y[b0:b1]), yr, 2), (b0, 0))
         tally.add("h", *slice_errs(f64(st.h[b0:b1]), hr, 1), (b0, 0))
         tally.slices += (b1 - b0) * cfg.nheads
         say(f"  batches {b0}..{b1 - 1} done")
+    assert tally.slices == cfg.batch * cfg.nheads
+    assert torch.equal(st.b_last, d["B"][:, -1]) and torch.equal(st.x_last, d["x"][:, -1])
     tally.report()
