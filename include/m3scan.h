@@ -110,7 +110,8 @@ m3_status m3_prefill_workspace_size(const m3_dims* dims, size_t* bytes);
  * equal-length sequences of one to four whole chunks (the hardware-aware scan of
  * IBM's "What is a Mamba model?", parallel over sequences and heads) are therefore
  * swept several to a workgroup, the next sequence's first chunk fetched while the
- * current one computes, its state reset at the boundary.  1 means one sequence
+ * current one computes, its state reset at the boundary (not at 128 rows per chunk,
+ * chunk * rank, where two workgroups already share a compute unit).  1 means one sequence
  * per workgroup.  The choice depends on the dims only and does not change any
  * result bit.  Errors as m3_prefill_workspace_size, and M3_ERR_UNSUPPORTED for
  * dims no prefill kernel takes. */

@@ -1129,9 +1129,15 @@ static MfmaWs mfma_ws(const PrefillArgs& a, int nchunks, int nseg, int split) {
 // first one computes.  Equal-length batches whose sequences hold a few whole chunks each
 // and whose (b, h) pairs fill at least four rounds of workgroups therefore give each
 // workgroup several sequences of one head (about 16 chunks in all), swept one after another
-// (plain calls only: no gate, no output norm).
+// (plain calls only: no gate, no output norm).  Not at 128 rows per chunk: there two
+// workgroups already share a CU and cover one another's loads, and the variant spills
+// registers (measured 20-25% slower than one sequence per workgroup).
+static bool multi_rows(int QR) { return QR != 128; }
+
 static int choose_seqs(const PrefillArgs& a, int nchunks, int nseg) {
-    if (a.cu || nseg != 1 || nchunks < 1 || nchunks > 4 || a.L % a.Q != 0 || a.fu.z || a.fu.onw) return 1;
+    if (a.cu || nseg != 1 || nchunks < 1 || nchunks > 4 || a.L % a.Q != 0 || a.fu.z || a.fu.onw ||
+        !multi_rows(a.Q * a.R))
+        return 1;
     int64_t s = (16 + nchunks - 1) / nchunks;
     const int64_t cap = a.batch * a.H / (4 * scan_slots(a));
     if (s > cap) s = cap;
@@ -1230,11 +1236,13 @@ static hipError_t launch_mfma_rq(const PrefillArgs& a, const PrefillPlan& plan, 
         p.sinit_stride = pieces + 1;
         p.sinit_step = split;
     }
-    if (plan.seqs > 1) {   // plain calls only (choose_seqs)
-        const int64_t groups = (a.batch + plan.seqs - 1) / plan.seqs;
-        hipLaunchKernelGGL((mf::scan_mfma<R, Q, NW, true, false, false, true>),
-                           dim3(static_cast<unsigned>(groups * a.H)), dim3(64 * NW), 0, st, p);
-        return hipGetLastError();
+    if constexpr (Q * R != 128) {   // multi_rows
+        if (plan.seqs > 1) {   // plain calls only (choose_seqs)
+            const int64_t groups = (a.batch + plan.seqs - 1) / plan.seqs;
+            hipLaunchKernelGGL((mf::scan_mfma<R, Q, NW, true, false, false, true>),
+                               dim3(static_cast<unsigned>(groups * a.H)), dim3(64 * NW), 0, st, p);
+            return hipGetLastError();
+        }
     }
     auto scan = p.onw ? (p.z ? mf::scan_mfma<R, Q, NW, true, true, true> : mf::scan_mfma<R, Q, NW, true, false, true>)
                       : (p.z ? mf::scan_mfma<R, Q, NW, true, true, false> : mf::scan_mfma<R, Q, NW, true, false, false>);

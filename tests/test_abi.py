@@ -317,9 +317,10 @@ def test_backward_parts(lib):
 
 def test_prefill_sequences_per_workgroup(lib):
     """The matrix-core prefill sweeps several sequences per workgroup only for equal-length
-    batches of one to four whole chunks whose (b, h) pairs fill at least eight rounds of
-    workgroups (two sequences each, four rounds), about 16 chunks per workgroup, never more
-    than the batch; everything else runs one sequence per workgroup."""
+    batches of one to four whole chunks, at 64 or 256 rows per chunk, whose (b, h) pairs fill
+    at least eight rounds of workgroups (two sequences each, four rounds), about 16 chunks
+    per workgroup, never more than the batch; everything else runs one sequence per
+    workgroup."""
     def seqs(**kw):
         base = dict(batch=4096, seqlen=64, nheads=64, ngroups=1, headdim=64, dstate=128, rank=4, chunk=64,
                     io_dtype=m3scan.M3_BF16)
@@ -334,6 +335,8 @@ def test_prefill_sequences_per_workgroup(lib):
     assert seqs(rank=1, batch=64) == 2                    # two workgroups per CU at 64 rows: 512 slots
     assert seqs(rank=1, batch=63) == 1
     assert seqs(ngroups=8) == 16                          # groups of heads sharing B and C
+    assert seqs(chunk=32) == 1 and seqs(rank=2) == 1      # 128-row chunks: two workgroups per CU already
+    assert seqs(rank=2, chunk=32, batch=128) == 4 and seqs(rank=1, chunk=32) == 8   # two chunks each
     assert seqs(headdim=16, dstate=16, io_dtype=m3scan.M3_F32) == 1   # not the matrix-core path
     n = ctypes.c_int32(0)
     good = _dims()

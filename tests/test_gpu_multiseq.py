@@ -27,8 +27,8 @@ CASES = [
     (37, 64, 64, 1, 4, 64, None, 1.0),       # one chunk per sequence, two per workgroup
     (600, 64, 64, 1, 4, 64, None, 4.0),      # sixteen per workgroup
     (301, 256, 64, 1, 1, 64, "fp32", 1.0),   # four chunks each, from a state with carries
-    (200, 128, 64, 8, 2, 64, "bf16", 1.0),   # groups of heads, bf16 state
-    (265, 64, 64, 2, 4, 32, None, 1.0),      # 128-row chunks, two chunks each
+    (201, 128, 64, 8, 2, 32, "bf16", 1.0),   # groups of heads, bf16 state, four chunks each
+    (265, 64, 64, 2, 1, 32, None, 1.0),      # 32-row chunks, two chunks each
     (100, 96, 64, 1, 2, 32, "fp32", 1.0),    # three chunks each
 ]
 
