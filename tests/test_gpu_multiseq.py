@@ -8,6 +8,7 @@ outputs, final states and carries must be the same bits (the sweep changes which
 workgroup computes a sequence, not its arithmetic).  The sequences on both sides
 of the sweep's boundaries (the last of one workgroup, the first of the next, the
 ragged last group) are also checked against the fp64 oracle at the bf16 bar."""
+import ctypes
 import zlib
 
 import pytest
@@ -86,3 +87,29 @@ def test_multi_sequence_sweep(case):
     ey, eh = slice_err(np64(y[picks]), yr, 2), slice_err(np64(st.h[picks]), hr, 1)
     say(f"  oracle on batch entries {picks}: y err {ey:.2e}  h err {eh:.2e}")
     assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+def test_multi_sequence_sweep_in_place():
+    """state_in may alias state_out in the sweep too: each sequence's incoming state is read
+    before its own final state is written, and the carries are copied after the scan.  The
+    in-place call gives the same bits as separate buffers."""
+    b, L, H, G, R, Q = 70, 64, 64, 1, 4, 64
+    seqs = m3scan.prefill_sequences_per_workgroup(m3scan.make_dims(b, L, H, G, P, N, R, Q, m3scan.M3_BF16))
+    assert seqs > 1
+    d = draw(b, L, H, G, P, N, R, "bf16", 1.0, seed=4242)
+    sin = rand_state(b, H, G, N, P, R, "bf16", seed=13)
+    args = [d[k] for k in ("x", "dt", "A", "lam", "theta", "B", "C", "D")]
+    y_ref, st_ref = m3scan.prefill(*args, Q, state_in=sin)
+    buf = m3scan.DecodeState(sin.h.clone(), sin.b_last.clone(), sin.x_last.clone())
+    dims = m3scan.make_dims(b, L, H, G, P, N, R, Q, m3scan.M3_BF16)
+    ws = torch.empty(max(m3scan.workspace_size(dims), 1), dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(d["x"])
+    s = m3scan.State(buf.h.data_ptr(), buf.b_last.data_ptr(), buf.x_last.data_ptr())
+    rc = m3scan.lib().m3_prefill_chunked(ctypes.byref(dims), *[m3scan._p(t) for t in args],
+                                         ctypes.byref(s), ctypes.byref(s), m3scan._p(y), m3scan._p(ws),
+                                         ws.numel(), m3scan._stream(torch.device("cuda")))
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+    assert torch.equal(buf.h, st_ref.h)
+    assert torch.equal(buf.b_last, st_ref.b_last) and torch.equal(buf.x_last, st_ref.x_last)
