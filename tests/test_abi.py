@@ -113,6 +113,8 @@ def test_prefill_rejects_unsupported(lib):
     n = ctypes.c_size_t(0)
     assert lib.m3_prefill_workspace_size(ctypes.byref(d), ctypes.byref(n)) == -2
     assert lib.m3_prefill_chunked(ctypes.byref(d), *[FAKE] * 8, None, None, FAKE, None, 0, None) == -2
+    s = ctypes.c_int32(0)
+    assert lib.m3_prefill_sequences_per_workgroup(ctypes.byref(d), ctypes.byref(s)) == -2
     # a state too large for LDS whatever the block size
     d = _dims(rank=1, dstate=512, headdim=512, chunk=1)
     assert lib.m3_prefill_workspace_size(ctypes.byref(d), ctypes.byref(n)) == -2
